@@ -1,0 +1,166 @@
+/* spec_verify.h -- batched speculative-sampling verification on AMD Instinct MI355X (gfx950).
+ *
+ * One speculative round per request: the draft proposed y_1..y_g from q_1..q_g, the target
+ * scored p_1..p_{g+1} in one forward pass.  The library turns the logit rows into the
+ * tempered, top-k/top-p-filtered distributions, accepts y_i with probability
+ * min(1, p_i(y_i)/q_i(y_i)) (or by argmax equality when greedy), stops at the first
+ * rejection, draws the correction token from the residual [p_i - q_i]_+ / sum [p_i - q_i]_+
+ * or a bonus token from p_{g+1}, and emits per-position draft entropy, draft max-probability
+ * and 1 - TV(p, q).
+ *
+ * Sources: the guide page "5.1 投机解码核心原理" (speculative decoding: core principles),
+ * sections 2.1-2.2 (inputs), 3.1 (greedy rule), 3.2 (acceptance ratio, residual formula),
+ * 3.3 (token-only drafts), 4.1-4.3 (beta = sum [p-q]_+ = 1 - A, A = 1 - TV), 5.1-5.2 (first
+ * rejection, bonus token); the page "SpecKV: Adaptive Speculative Decoding with
+ * Compression-Aware Gamma Selection", section on draft-model signals (entropy in bits,
+ * max probability, their mean / max / min over the draft block).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument is DEVICE memory owned by the caller, except `uniforms` in
+ *    spec_residual_sample (device too) and the by-value structs.  The library allocates
+ *    nothing, keeps no state between calls and writes only the outputs and the workspace.
+ *  - Calls are asynchronous and ordered on `hip_stream` (a hipStream_t; NULL = the null
+ *    stream).  They are re-entrant when concurrent calls use different workspaces.
+ *  - Logit rows are dense, row-major, `ld` ELEMENTS apart (ld >= V).  dtype SPEC_BF16 rows
+ *    hold bf16 bit patterns, SPEC_F32 rows hold floats.  A 16-byte aligned base with a
+ *    16-byte multiple row stride takes the vector path; anything else takes a scalar path
+ *    with identical results.  -inf logits are allowed (masked tokens).
+ *  - Return codes are synchronous argument / launch checks; per-request problems found on
+ *    the device are reported in `out_status` bit flags.
+ *  - Randomness is Philox4x64-10 with key (seed, step); see each entry point for its
+ *    counters.  A uniform is (word >> 11) * 2^-53.  Equal inputs give bitwise equal outputs.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define SPEC_OK 0
+#define SPEC_ERR_INVALID (-1)     /* null / inconsistent argument, bad size, bad parameter */
+#define SPEC_ERR_UNSUPPORTED (-2) /* a valid combination this build does not implement     */
+#define SPEC_ERR_WORKSPACE (-3)   /* workspace smaller than the *_workspace_bytes figure    */
+#define SPEC_ERR_LAUNCH (-4)      /* a HIP launch failed                                    */
+
+/* per-request / per-row status bits written to out_status on the device */
+#define SPEC_STATUS_NONFINITE 1        /* NaN or +inf logit, or a row with no finite logit:
+                                          0 accepted, tokens -1                             */
+#define SPEC_STATUS_BAD_TOKEN 2        /* draft token outside [0, V): rejected there        */
+#define SPEC_STATUS_ZERO_Q 4           /* q(y) = 0 after filtering: rejected there          */
+#define SPEC_STATUS_RESIDUAL_EMPTY 8   /* residual mass 0 after a rejection: drawn from p   */
+#define SPEC_STATUS_TIMEOUT 16         /* reserved: a bounded wait expired                  */
+#define SPEC_STATUS_FILTER_OVERFLOW 32 /* a filtered row kept more tokens than the sparse
+                                          path holds: 0 accepted, tokens -1                 */
+#define SPEC_STATUS_BAD_GAMMA 64       /* cu_draft inconsistent for this request: nothing
+                                          read, 0 accepted, tokens -1                        */
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+/* Sampling parameters applied identically to target and draft rows (guide §2.1: p and q are
+ * the distributions actually sampled from).  temperature 0 = greedy (argmax).  top_k <= 0 or
+ * >= V = off; otherwise every logit >= the k-th largest is kept (ties kept).  top_p >= 1 =
+ * off; otherwise the smallest set of largest values whose mass over the top-k set reaches
+ * top_p is kept (a boundary value is kept with all its ties).  Order: temperature, top-k,
+ * top-p.  Filtering needs 1 <= top_k <= 256 in this build (top-p alone: SPEC_ERR_UNSUPPORTED). */
+typedef struct {
+  float temperature;
+  int top_k;
+  float top_p;
+} spec_sampling_params;
+
+/* Optional per-position outputs of spec_verify_batch; each pointer may be NULL.
+ * Draft-side arrays have one float per draft row (sum gamma_b, laid out like draft rows);
+ * target-side arrays one per target row (sum (gamma_b + 1)).  Values are fp32. */
+typedef struct {
+  float* p_y;                 /* p_i(y_i); NaN if y_i is not a token                      */
+  float* q_y;                 /* q_i(y_i); 1 for a token-only draft                       */
+  float* one_minus_tv;        /* sum_x min(p_i, q_i) = 1 - TV(p_i, q_i)   (guide §4.3)     */
+  float* draft_entropy_bits;  /* H(q_i) in bits (SpecKV signals); NaN when greedy          */
+  float* draft_max_prob;      /* max_x q_i(x); NaN when greedy                             */
+  float* target_entropy_bits; /* H(p_i) in bits, i = 1..gamma_b+1; 0 when greedy           */
+  float* target_max_prob;     /* max_x p_i(x); 1 when greedy                               */
+} spec_pos_stats;
+
+/* spec_verify_batch -- verify one speculative round for B ragged requests.
+ *
+ * Request b has gamma_b = cu_draft[b+1] - cu_draft[b] draft tokens (0 <= gamma_b <=
+ * gamma_max).  Its target rows are target_logits rows cu_draft[b] + b + i, i = 0..gamma_b
+ * (gamma_b + 1 rows, the last one for the bonus token); its draft rows and tokens are rows
+ * cu_draft[b] + i, i = 0..gamma_b-1.  n_draft_rows must equal cu_draft[B] (the sum of the
+ * gamma_b): it bounds every row index the device forms, so the target allocation must hold
+ * n_draft_rows + B rows and the draft allocation n_draft_rows rows.
+ *
+ *  draft_logits NULL = token-only draft (one-hot q at y_i, guide §3.3); with temperature 0
+ *  the draft logits are never read.  Outputs:
+ *   out_tokens        [B, gamma_max + 1] int32: accepted draft tokens, then the correction or
+ *                     bonus token, then -1 padding.
+ *   out_num_accepted  [B] int32 in [0, gamma_b]; the request advances num_accepted + 1 tokens.
+ *   pos_stats         optional per-position signals (see spec_pos_stats).
+ *   out_req_stats     optional [B, 4] fp32: mean H(q_i), mean max q_i, max H(q_i), min max q_i
+ *                     over i = 1..gamma_b (NaN when gamma_b = 0 or greedy).
+ *   out_status        [B] int32 status bits (SPEC_STATUS_*).
+ *  Randomness: Philox counter (b, i, 0, 0) for 1-based position i: word 0 is the accept draw
+ *  at i, words 1..3 drive the three sampler levels when the emitted token is drawn at i.
+ *  The sampler is a fixed-order inverse CDF in three levels (chunks of 4096 tokens, groups of
+ *  64, tokens) with one uniform per level; its law is exactly the residual (or p_{g+1}).
+ *  workspace: spec_verify_workspace_bytes(B, V, gamma_max, dt, sp) bytes of device memory,
+ *  256-byte aligned; its contents need no initialisation and are scratch after the call. */
+int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt,
+                      const void* target_logits, int64_t target_ld,
+                      const void* draft_logits, int64_t draft_ld,
+                      const int32_t* draft_tokens, const int32_t* cu_draft, int n_draft_rows,
+                      spec_sampling_params sp, uint64_t seed, uint64_t step,
+                      int32_t* out_tokens, int32_t* out_num_accepted,
+                      spec_pos_stats pos_stats, float* out_req_stats, int32_t* out_status,
+                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
+size_t spec_verify_workspace_bytes(int B, int V, int gamma_max, spec_dtype dt,
+                                   spec_sampling_params sp);
+
+/* spec_row_stats -- per-row statistics of R filtered, tempered logit rows (the signals of the
+ * SpecKV page, computed on the distribution actually sampled from).  Each output is [R] and
+ * may be NULL: max_logit, argmax (lowest index of the maximum), log_z = ln sum_kept
+ * exp(l/T), entropy_bits, max_prob, kept_count (kept tokens with a finite logit).  With
+ * temperature 0 the row is one-hot at the argmax: entropy 0, max_prob 1, kept 1, log_z NaN.
+ * A row with a NaN / +inf logit or no finite logit gives argmax -1 and NaN statistics. */
+int spec_row_stats(int R, int V, spec_dtype dt, const void* logits, int64_t ld,
+                   spec_sampling_params sp,
+                   float* max_logit, int32_t* argmax, float* log_z, float* entropy_bits,
+                   float* max_prob, int32_t* kept_count,
+                   void* workspace, size_t workspace_bytes, void* hip_stream);
+
+size_t spec_row_stats_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling_params sp);
+
+/* spec_residual_sample -- one draw per row from r(x) = [p(x) - q(x)]_+ / sum [p - q]_+
+ * (guide §3.2), or from p when q_logits is NULL, with the same three-level sampler.
+ *  uniforms: [R, 3] fp64 in [0, 1) on the device, or NULL for Philox counter (r, 0, 1, 0),
+ *  words 1..3.  Outputs [R]: out_token, out_mass (beta = sum [p - q]_+, or 1 without q; NaN
+ *  for non-finite rows), out_status (NONFINITE, RESIDUAL_EMPTY: beta = 0, drawn from p). */
+int spec_residual_sample(int R, int V, spec_dtype dt,
+                         const void* p_logits, int64_t p_ld, const void* q_logits, int64_t q_ld,
+                         spec_sampling_params sp, const double* uniforms,
+                         uint64_t seed, uint64_t step,
+                         int32_t* out_token, double* out_mass, int32_t* out_status,
+                         void* workspace, size_t workspace_bytes, void* hip_stream);
+
+size_t spec_residual_sample_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling_params sp);
+
+/* Benchmark instrumentation.  With two hipEvent_t handles set, every later spec_verify_batch
+ * call records `start_event` on its stream right before its dominant streaming kernel (the
+ * pass that reads every needed logit row) and `stop_event` right after it, so a benchmark can
+ * time that kernel alone.  NULL, NULL switches it off.  Process-wide and not thread-safe;
+ * the events stay owned by the caller.  Returns SPEC_ERR_INVALID if only one is NULL. */
+int spec_set_profile_events(void* start_event, void* stop_event);
+
+/* Human-readable text for a return code (negative) or a single status bit (positive). */
+const char* spec_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,242 @@
+"""Batched speculative-sampling verification for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libspecverify.so`` (the C ABI in ``include/spec_verify.h``).
+Functions keep the C names; they only marshal torch tensors (device memory, strides, the
+current HIP stream) into the C calls.  Every step of the computation runs in the library's
+HIP kernels: there is no Python or CPU fallback, and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "SPEC_F32", "SPEC_BF16", "STATUS", "load_library", "library_path",
+    "spec_verify_batch", "spec_row_stats", "spec_residual_sample", "spec_status_string",
+    "spec_verify_workspace_bytes", "spec_row_stats_workspace_bytes",
+    "spec_residual_sample_workspace_bytes",
+]
+
+SPEC_F32 = 0
+SPEC_BF16 = 1
+STATUS = {
+    "NONFINITE": 1, "BAD_TOKEN": 2, "ZERO_Q": 4, "RESIDUAL_EMPTY": 8, "TIMEOUT": 16,
+    "FILTER_OVERFLOW": 32, "BAD_GAMMA": 64,
+}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class SamplingParams(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int), ("top_p", ctypes.c_float)]
+
+
+class PosStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "p_y", "q_y", "one_minus_tv", "draft_entropy_bits", "draft_max_prob",
+        "target_entropy_bits", "target_max_prob")]
+
+
+def library_path() -> str:
+    return os.environ.get("SPEC_VERIFY_LIB", os.path.join(_HERE, "libspecverify.so"))
+
+
+def load_library():
+    """Load libspecverify.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m lossless_draft_verification_row_amd.build`")
+    lib = ctypes.CDLL(path)
+    i32, i64, u64, sz, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p
+    lib.spec_verify_batch.restype = i32
+    lib.spec_verify_batch.argtypes = [i32, i32, i32, i32, vp, i64, vp, i64, vp, vp, i32, SamplingParams,
+                                      u64, u64, vp, vp, PosStats, vp, vp, vp, sz, vp]
+    lib.spec_verify_workspace_bytes.restype = sz
+    lib.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, i32, SamplingParams]
+    lib.spec_row_stats.restype = i32
+    lib.spec_row_stats.argtypes = [i32, i32, i32, vp, i64, SamplingParams, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_row_stats_workspace_bytes.restype = sz
+    lib.spec_row_stats_workspace_bytes.argtypes = [i32, i32, i32, SamplingParams]
+    lib.spec_residual_sample.restype = i32
+    lib.spec_residual_sample.argtypes = [i32, i32, i32, vp, i64, vp, i64, SamplingParams, vp, u64, u64,
+                                         vp, vp, vp, vp, sz, vp]
+    lib.spec_residual_sample_workspace_bytes.restype = sz
+    lib.spec_residual_sample_workspace_bytes.argtypes = [i32, i32, i32, SamplingParams]
+    lib.spec_set_profile_events.restype = i32
+    lib.spec_set_profile_events.argtypes = [vp, vp]
+    lib.spec_status_string.restype = ctypes.c_char_p
+    lib.spec_status_string.argtypes = [i32]
+    _LIB = lib
+    return lib
+
+
+def spec_status_string(code: int) -> str:
+    return load_library().spec_status_string(int(code)).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise RuntimeError(f"{what} failed: {rc} ({spec_status_string(rc)})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _rows(t: torch.Tensor, name: str):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    return t.data_ptr(), t.stride(0)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _sp(temperature, top_k, top_p):
+    return SamplingParams(float(temperature), int(top_k), float(top_p))
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                             f"{nbytes} needed")
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _workspace.keep = ws  # keep alive until the next call; torch's allocator orders reuse on the stream
+    return ws.data_ptr(), nbytes
+
+
+def spec_verify_workspace_bytes(B, V, gamma_max, dtype, temperature, top_k=0, top_p=1.0) -> int:
+    return int(load_library().spec_verify_workspace_bytes(B, V, gamma_max, dtype, _sp(temperature, top_k, top_p)))
+
+
+def spec_row_stats_workspace_bytes(R, V, dtype, temperature, top_k=0, top_p=1.0) -> int:
+    return int(load_library().spec_row_stats_workspace_bytes(R, V, dtype, _sp(temperature, top_k, top_p)))
+
+
+def spec_residual_sample_workspace_bytes(R, V, dtype, temperature, top_k=0, top_p=1.0) -> int:
+    return int(load_library().spec_residual_sample_workspace_bytes(R, V, dtype, _sp(temperature, top_k, top_p)))
+
+
+def spec_verify_batch(target_logits, draft_logits, draft_tokens, cu_draft, gamma_max, *,
+                      temperature=1.0, top_k=0, top_p=1.0, seed=0, step=0, pos_stats=True,
+                      req_stats=True, workspace=None, out=None, stream=None):
+    """Verify one speculative round for B ragged requests (see spec_verify_batch in the header).
+
+    target_logits [sum(g_b + 1), V] and draft_logits [sum g_b, V] (or None: token-only draft)
+    are bf16 or fp32 CUDA tensors; draft_tokens [sum g_b] and cu_draft [B + 1] are int32 CUDA
+    tensors.  Returns a dict of CUDA tensors: tokens [B, gamma_max + 1], num_accepted [B],
+    status [B], and, when requested, the per-position and per-request statistics.
+    """
+    lib = load_library()
+    dev = target_logits.device
+    B = cu_draft.numel() - 1
+    V = target_logits.shape[1]
+    dt = _dtype_code(target_logits)
+    tp, tld = _rows(target_logits, "target_logits")
+    dp, dld = (None, 0) if draft_logits is None else _rows(draft_logits, "draft_logits")
+    if draft_logits is not None and (draft_logits.dtype != target_logits.dtype or draft_logits.shape[1] != V):
+        raise ValueError("draft_logits must match target_logits in dtype and vocabulary")
+    for t, n in ((draft_tokens, "draft_tokens"), (cu_draft, "cu_draft")):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 CUDA tensor")
+    Rd = draft_tokens.numel()
+    sp = _sp(temperature, top_k, top_p)
+    o = out if out is not None else {}
+    if "tokens" not in o:
+        o["tokens"] = torch.empty((B, gamma_max + 1), dtype=torch.int32, device=dev)
+        o["num_accepted"] = torch.empty(B, dtype=torch.int32, device=dev)
+        o["status"] = torch.empty(B, dtype=torch.int32, device=dev)
+        if pos_stats:
+            for k in ("p_y", "q_y", "one_minus_tv", "draft_entropy_bits", "draft_max_prob"):
+                o[k] = torch.empty(Rd, dtype=torch.float32, device=dev)
+            for k in ("target_entropy_bits", "target_max_prob"):
+                o[k] = torch.empty(Rd + B, dtype=torch.float32, device=dev)
+        if req_stats:
+            o["req_stats"] = torch.empty((B, 4), dtype=torch.float32, device=dev)
+    ps = PosStats(*[_ptr(o.get(k)) for k in (
+        "p_y", "q_y", "one_minus_tv", "draft_entropy_bits", "draft_max_prob",
+        "target_entropy_bits", "target_max_prob")])
+    need = lib.spec_verify_workspace_bytes(B, V, gamma_max, dt, sp)
+    wp, wn = _workspace(need, dev, workspace)
+    rc = lib.spec_verify_batch(B, V, gamma_max, dt, tp, tld, dp, dld, _ptr(draft_tokens), _ptr(cu_draft), Rd,
+                               sp, int(seed) & (2**64 - 1), int(step) & (2**64 - 1),
+                               _ptr(o["tokens"]), _ptr(o["num_accepted"]), ps, _ptr(o.get("req_stats")),
+                               _ptr(o["status"]), wp, wn, _stream(stream))
+    _check(rc, "spec_verify_batch")
+    return o
+
+
+def spec_row_stats(logits, *, temperature=1.0, top_k=0, top_p=1.0, workspace=None, stream=None):
+    """Per-row statistics of filtered, tempered logit rows.  Returns a dict of [R] tensors:
+    max_logit, argmax, log_z, entropy_bits, max_prob, kept_count."""
+    lib = load_library()
+    dev = logits.device
+    R, V = logits.shape
+    dt = _dtype_code(logits)
+    lp, ld = _rows(logits, "logits")
+    sp = _sp(temperature, top_k, top_p)
+    o = {
+        "max_logit": torch.empty(R, dtype=torch.float32, device=dev),
+        "argmax": torch.empty(R, dtype=torch.int32, device=dev),
+        "log_z": torch.empty(R, dtype=torch.float32, device=dev),
+        "entropy_bits": torch.empty(R, dtype=torch.float32, device=dev),
+        "max_prob": torch.empty(R, dtype=torch.float32, device=dev),
+        "kept_count": torch.empty(R, dtype=torch.int32, device=dev),
+    }
+    need = lib.spec_row_stats_workspace_bytes(R, V, dt, sp)
+    wp, wn = _workspace(need, dev, workspace)
+    rc = lib.spec_row_stats(R, V, dt, lp, ld, sp, *[_ptr(o[k]) for k in (
+        "max_logit", "argmax", "log_z", "entropy_bits", "max_prob", "kept_count")], wp, wn, _stream(stream))
+    _check(rc, "spec_row_stats")
+    return o
+
+
+def spec_residual_sample(p_logits, q_logits=None, *, temperature=1.0, top_k=0, top_p=1.0, uniforms=None,
+                         seed=0, step=0, workspace=None, stream=None):
+    """One draw per row from [p - q]_+ (or p when q_logits is None).  Returns a dict of [R]
+    tensors: token (int32), mass (fp64: beta, or 1 without q), status (int32)."""
+    lib = load_library()
+    dev = p_logits.device
+    R, V = p_logits.shape
+    dt = _dtype_code(p_logits)
+    pp, pld = _rows(p_logits, "p_logits")
+    qp, qld = (None, 0) if q_logits is None else _rows(q_logits, "q_logits")
+    if uniforms is not None:
+        if uniforms.dtype != torch.float64 or tuple(uniforms.shape) != (R, 3) or not uniforms.is_contiguous():
+            raise ValueError("uniforms must be a contiguous float64 tensor of shape [R, 3]")
+    sp = _sp(temperature, top_k, top_p)
+    o = {
+        "token": torch.empty(R, dtype=torch.int32, device=dev),
+        "mass": torch.empty(R, dtype=torch.float64, device=dev),
+        "status": torch.empty(R, dtype=torch.int32, device=dev),
+    }
+    need = lib.spec_residual_sample_workspace_bytes(R, V, dt, sp)
+    wp, wn = _workspace(need, dev, workspace)
+    rc = lib.spec_residual_sample(R, V, dt, pp, pld, qp, qld, sp, _ptr(uniforms), int(seed) & (2**64 - 1),
+                                  int(step) & (2**64 - 1), _ptr(o["token"]), _ptr(o["mass"]), _ptr(o["status"]),
+                                  wp, wn, _stream(stream))
+    _check(rc, "spec_residual_sample")
+    return o

@@ -1,0 +1,315 @@
+// spec_api.hip -- the C ABI of libspecverify: argument checks, workspace carving, launches.
+// Declarations and their documentation are in include/spec_verify.h.
+#include <math.h>
+#include <string.h>
+
+#include "spec_device.h"
+#include "spec_internal.h"
+#include "spec_verify.h"
+
+using namespace specv;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+// Benchmark instrumentation (spec_set_profile_events): process-wide, not thread-safe.
+hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int n_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+
+bool filter_on(int V, const spec_sampling_params& sp) {
+  return sp.temperature > 0.f && ((sp.top_k > 0 && sp.top_k < V) || sp.top_p < 1.f);
+}
+
+// Sampling parameters: temperature finite and >= 0, top_p > 0 (NaN rejected).
+int check_params(const spec_sampling_params& sp) {
+  if (!(sp.temperature >= 0.f) || !isfinite(sp.temperature)) return SPEC_ERR_INVALID;
+  if (!(sp.top_p > 0.f)) return SPEC_ERR_INVALID;
+  return SPEC_OK;
+}
+
+int elem_bytes(spec_dtype dt) { return dt == SPEC_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p, int64_t ld, spec_dtype dt) {
+  return p == nullptr || (((uintptr_t)p % 16) == 0 && ((ld * elem_bytes(dt)) % 16) == 0);
+}
+
+struct Carve {
+  char* base;
+  size_t off;
+  template <typename T>
+  T* take(size_t bytes) {
+    T* p = (T*)(base + off);
+    off += align_up(bytes);
+    return p;
+  }
+};
+
+// Workspace of the dense path for n_slots slots (2 logical rows each).
+size_t dense_bytes(int64_t n_slots, int V) {
+  const int64_t n_lr = 2 * n_slots;
+  const int64_t ns = n_chunks(V);
+  return align_up((size_t)(n_lr * ns) * slice_part_bytes()) + align_up((size_t)n_lr * row_stat_bytes()) +
+         align_up((size_t)(n_slots * ns) * sizeof(double));
+}
+
+float exp2_scale(const spec_sampling_params& sp) {
+  return sp.temperature > 0.f ? (float)(1.4426950408889634 / (double)sp.temperature) : 0.f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_status_string(int code) {
+  switch (code) {
+    case SPEC_OK: return "ok";
+    case SPEC_ERR_INVALID: return "invalid argument";
+    case SPEC_ERR_UNSUPPORTED: return "unsupported combination";
+    case SPEC_ERR_WORKSPACE: return "workspace too small";
+    case SPEC_ERR_LAUNCH: return "HIP launch failed";
+    case SPEC_STATUS_NONFINITE: return "non-finite logits";
+    case SPEC_STATUS_BAD_TOKEN: return "draft token out of range";
+    case SPEC_STATUS_ZERO_Q: return "draft probability of the draft token is zero";
+    case SPEC_STATUS_RESIDUAL_EMPTY: return "empty residual, drawn from p";
+    case SPEC_STATUS_TIMEOUT: return "bounded wait expired";
+    case SPEC_STATUS_FILTER_OVERFLOW: return "filtered row too large for the sparse path";
+    case SPEC_STATUS_BAD_GAMMA: return "inconsistent draft offsets";
+    default: return "unknown code";
+  }
+}
+
+int spec_set_profile_events(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return SPEC_ERR_INVALID;
+  g_prof_start = (hipEvent_t)start_event;
+  g_prof_stop = (hipEvent_t)stop_event;
+  return SPEC_OK;
+}
+
+size_t spec_verify_workspace_bytes(int B, int V, int gamma_max, spec_dtype dt, spec_sampling_params sp) {
+  (void)dt;
+  if (B <= 0 || V <= 0 || gamma_max < 0) return 0;
+  if (filter_on(V, sp)) return 0;
+  return dense_bytes((int64_t)B * (gamma_max + 1), V);
+}
+
+size_t spec_row_stats_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling_params sp) {
+  (void)dt;
+  if (R <= 0 || V <= 0) return 0;
+  if (filter_on(V, sp)) return 0;
+  return dense_bytes(R, V);
+}
+
+size_t spec_residual_sample_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling_params sp) {
+  (void)dt;
+  if (R <= 0 || V <= 0) return 0;
+  if (filter_on(V, sp)) return 0;
+  return dense_bytes(R, V);
+}
+
+int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* target_logits,
+                      int64_t target_ld, const void* draft_logits, int64_t draft_ld,
+                      const int32_t* draft_tokens, const int32_t* cu_draft, int n_draft_rows,
+                      spec_sampling_params sp, uint64_t seed, uint64_t step, int32_t* out_tokens,
+                      int32_t* out_num_accepted, spec_pos_stats pos_stats, float* out_req_stats,
+                      int32_t* out_status, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (B < 0 || V <= 0 || gamma_max < 0 || gamma_max > kMaxGamma) return SPEC_ERR_INVALID;
+  if (dt != SPEC_F32 && dt != SPEC_BF16) return SPEC_ERR_INVALID;
+  if (V > kMaxChunks * kChunk) return SPEC_ERR_UNSUPPORTED;
+  if (check_params(sp) != SPEC_OK) return SPEC_ERR_INVALID;
+  if (B == 0) return SPEC_OK;
+  if (n_draft_rows < 0 || (int64_t)n_draft_rows > (int64_t)B * gamma_max) return SPEC_ERR_INVALID;
+  if (!target_logits || target_ld < V || !cu_draft || !out_tokens || !out_num_accepted || !out_status)
+    return SPEC_ERR_INVALID;
+  if (n_draft_rows > 0 && !draft_tokens) return SPEC_ERR_INVALID;
+  if (draft_logits && draft_ld < V) return SPEC_ERR_INVALID;
+  if ((int64_t)B * (gamma_max + 1) * 2 > (int64_t)INT32_MAX / 2) return SPEC_ERR_INVALID;
+  const bool greedy = sp.temperature == 0.f;
+  if (filter_on(V, sp)) return SPEC_ERR_UNSUPPORTED;
+  const size_t need = spec_verify_workspace_bytes(B, V, gamma_max, dt, sp);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SPEC_ERR_WORKSPACE;
+  if (((uintptr_t)workspace % kAlign) != 0) return SPEC_ERR_INVALID;
+
+  const hipStream_t st = (hipStream_t)hip_stream;
+  const int n_slots = B * (gamma_max + 1);
+  const int ns = n_chunks(V);
+  const void* drf = greedy ? nullptr : draft_logits;
+
+  RowMap map;
+  map.tgt = target_logits;
+  map.tgt_ld = target_ld;
+  map.drf = drf;
+  map.drf_ld = draft_ld;
+  map.cu = cu_draft;
+  map.B = B;
+  map.G = gamma_max;
+  map.n_draft_rows = n_draft_rows;
+
+  Carve cv{(char*)workspace, 0};
+  DenseLaunch L;
+  memset(&L, 0, sizeof(L));
+  L.map = map;
+  L.dt = dt == SPEC_BF16 ? kDtBF16 : kDtF32;
+  L.V = V;
+  L.n_slices = ns;
+  L.n_slots = n_slots;
+  L.c = exp2_scale(sp);
+  L.greedy = greedy;
+  L.want_argmax = 0;
+  L.pair = (!greedy && drf != nullptr) ? 1 : 0;
+  L.vec = aligned16(target_logits, target_ld, dt) && aligned16(drf, draft_ld, dt);
+  L.part = cv.take<SlicePart>((size_t)(2 * n_slots) * ns * slice_part_bytes());
+  L.rs = cv.take<RowStat>((size_t)(2 * n_slots) * row_stat_bytes());
+  L.smass = cv.take<double>((size_t)n_slots * ns * sizeof(double));
+  L.rso.enabled = 0;
+  L.ev_start = g_prof_start;
+  L.ev_stop = g_prof_stop;
+  if (launch_dense(L, st) != hipSuccess) return SPEC_ERR_LAUNCH;
+
+  FinalizeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.map = map;
+  a.V = V;
+  a.n_slices = ns;
+  a.greedy = greedy;
+  a.c = L.c;
+  a.seed = seed;
+  a.step = step;
+  a.tokens = draft_tokens;
+  a.rs = L.rs;
+  a.part = L.part;
+  a.smass = L.smass;
+  a.out_tokens = out_tokens;
+  a.out_num_accepted = out_num_accepted;
+  a.out_req_stats = out_req_stats;
+  a.out_status = out_status;
+  a.st.p_y = pos_stats.p_y;
+  a.st.q_y = pos_stats.q_y;
+  a.st.one_minus_tv = pos_stats.one_minus_tv;
+  a.st.draft_entropy_bits = pos_stats.draft_entropy_bits;
+  a.st.draft_max_prob = pos_stats.draft_max_prob;
+  a.st.target_entropy_bits = pos_stats.target_entropy_bits;
+  a.st.target_max_prob = pos_stats.target_max_prob;
+  if (launch_finalize(a, L.dt, st) != hipSuccess) return SPEC_ERR_LAUNCH;
+  return SPEC_OK;
+}
+
+int spec_row_stats(int R, int V, spec_dtype dt, const void* logits, int64_t ld, spec_sampling_params sp,
+                   float* max_logit, int32_t* argmax, float* log_z, float* entropy_bits, float* max_prob,
+                   int32_t* kept_count, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (R < 0 || V <= 0) return SPEC_ERR_INVALID;
+  if (dt != SPEC_F32 && dt != SPEC_BF16) return SPEC_ERR_INVALID;
+  if (V > kMaxChunks * kChunk) return SPEC_ERR_UNSUPPORTED;
+  if (check_params(sp) != SPEC_OK) return SPEC_ERR_INVALID;
+  if (R == 0) return SPEC_OK;
+  if (!logits || ld < V) return SPEC_ERR_INVALID;
+  if ((int64_t)R * 2 > (int64_t)INT32_MAX / 2) return SPEC_ERR_INVALID;
+  if (filter_on(V, sp)) return SPEC_ERR_UNSUPPORTED;
+  const size_t need = spec_row_stats_workspace_bytes(R, V, dt, sp);
+  if (!workspace || workspace_bytes < need) return SPEC_ERR_WORKSPACE;
+  if (((uintptr_t)workspace % kAlign) != 0) return SPEC_ERR_INVALID;
+  const bool greedy = sp.temperature == 0.f;
+  const int ns = n_chunks(V);
+
+  RowMap map;
+  memset(&map, 0, sizeof(map));
+  map.tgt = logits;
+  map.tgt_ld = ld;
+  map.B = R;
+  Carve cv{(char*)workspace, 0};
+  DenseLaunch L;
+  memset(&L, 0, sizeof(L));
+  L.map = map;
+  L.dt = dt == SPEC_BF16 ? kDtBF16 : kDtF32;
+  L.V = V;
+  L.n_slices = ns;
+  L.n_slots = R;
+  L.c = exp2_scale(sp);
+  L.greedy = greedy;
+  L.want_argmax = 1;
+  L.pair = 0;
+  L.vec = aligned16(logits, ld, dt);
+  L.part = cv.take<SlicePart>((size_t)(2 * R) * ns * slice_part_bytes());
+  L.rs = cv.take<RowStat>((size_t)(2 * R) * row_stat_bytes());
+  L.smass = cv.take<double>((size_t)R * ns * sizeof(double));
+  L.rso.enabled = 1;
+  L.rso.max_logit = max_logit;
+  L.rso.argmax = argmax;
+  L.rso.log_z = log_z;
+  L.rso.entropy_bits = entropy_bits;
+  L.rso.max_prob = max_prob;
+  L.rso.kept_count = kept_count;
+  if (launch_dense(L, (hipStream_t)hip_stream) != hipSuccess) return SPEC_ERR_LAUNCH;
+  return SPEC_OK;
+}
+
+int spec_residual_sample(int R, int V, spec_dtype dt, const void* p_logits, int64_t p_ld, const void* q_logits,
+                         int64_t q_ld, spec_sampling_params sp, const double* uniforms, uint64_t seed,
+                         uint64_t step, int32_t* out_token, double* out_mass, int32_t* out_status,
+                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (R < 0 || V <= 0) return SPEC_ERR_INVALID;
+  if (dt != SPEC_F32 && dt != SPEC_BF16) return SPEC_ERR_INVALID;
+  if (V > kMaxChunks * kChunk) return SPEC_ERR_UNSUPPORTED;
+  if (check_params(sp) != SPEC_OK) return SPEC_ERR_INVALID;
+  if (R == 0) return SPEC_OK;
+  if (!p_logits || p_ld < V || !out_token || !out_status) return SPEC_ERR_INVALID;
+  if (q_logits && q_ld < V) return SPEC_ERR_INVALID;
+  if ((int64_t)R * 2 > (int64_t)INT32_MAX / 2) return SPEC_ERR_INVALID;
+  if (filter_on(V, sp)) return SPEC_ERR_UNSUPPORTED;
+  const size_t need = spec_residual_sample_workspace_bytes(R, V, dt, sp);
+  if (!workspace || workspace_bytes < need) return SPEC_ERR_WORKSPACE;
+  if (((uintptr_t)workspace % kAlign) != 0) return SPEC_ERR_INVALID;
+  const bool greedy = sp.temperature == 0.f;
+  const int ns = n_chunks(V);
+  const hipStream_t st = (hipStream_t)hip_stream;
+
+  RowMap map;
+  memset(&map, 0, sizeof(map));
+  map.tgt = p_logits;
+  map.tgt_ld = p_ld;
+  map.drf = q_logits;
+  map.drf_ld = q_ld;
+  map.B = R;
+  Carve cv{(char*)workspace, 0};
+  DenseLaunch L;
+  memset(&L, 0, sizeof(L));
+  L.map = map;
+  L.dt = dt == SPEC_BF16 ? kDtBF16 : kDtF32;
+  L.V = V;
+  L.n_slices = ns;
+  L.n_slots = R;
+  L.c = exp2_scale(sp);
+  L.greedy = greedy;
+  L.want_argmax = 0;
+  L.pair = (!greedy && q_logits != nullptr) ? 1 : 0;
+  L.vec = aligned16(p_logits, p_ld, dt) && aligned16(q_logits, q_ld, dt);
+  L.part = cv.take<SlicePart>((size_t)(2 * R) * ns * slice_part_bytes());
+  L.rs = cv.take<RowStat>((size_t)(2 * R) * row_stat_bytes());
+  L.smass = cv.take<double>((size_t)R * ns * sizeof(double));
+  L.rso.enabled = 0;
+  if (launch_dense(L, st) != hipSuccess) return SPEC_ERR_LAUNCH;
+
+  ResidualArgs a;
+  memset(&a, 0, sizeof(a));
+  a.map = map;
+  a.V = V;
+  a.n_slices = ns;
+  a.greedy = greedy;
+  a.c = L.c;
+  a.seed = seed;
+  a.step = step;
+  a.uniforms = uniforms;
+  a.rs = L.rs;
+  a.part = L.part;
+  a.smass = L.smass;
+  a.out_token = out_token;
+  a.out_mass = out_mass;
+  a.out_status = out_status;
+  if (launch_residual_finalize(a, L.dt, st) != hipSuccess) return SPEC_ERR_LAUNCH;
+  return SPEC_OK;
+}
+
+}  // extern "C"

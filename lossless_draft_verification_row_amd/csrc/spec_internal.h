@@ -1,0 +1,100 @@
+// spec_internal.h -- launch descriptors shared by the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace specv {
+
+constexpr int kModeSoftmax = 0;
+constexpr int kModeArgmax = 1;
+constexpr int kMaxChunks = 512;   // V <= 512 * 4096 logits
+constexpr int kMaxGamma = 64;     // gamma_max bound (one finalize thread per position)
+
+// How a logical row index maps onto the caller's arrays (see resolve_row).
+struct RowMap {
+  const void* tgt;
+  int64_t tgt_ld;
+  const void* drf;          // nullptr: no draft / q rows
+  int64_t drf_ld;
+  const int32_t* cu;        // request mode: [B + 1] draft-row offsets; nullptr: plain rows
+  int B;                    // requests, or rows in plain-row mode
+  int G;                    // gamma_max (request mode)
+  int n_draft_rows;         // cu[B] as stated by the caller (request mode)
+};
+
+// spec_row_stats outputs written by the combine kernel (plain-row mode).
+struct RowStatsOut {
+  int enabled;
+  float* max_logit;
+  int32_t* argmax;
+  float* log_z;
+  float* entropy_bits;
+  float* max_prob;
+  int32_t* kept_count;
+};
+
+struct SlicePart;
+struct RowStat;
+
+struct DenseLaunch {
+  RowMap map;
+  int dt, V, n_slices, n_slots;
+  float c;                  // log2(e) / T (0 when greedy)
+  int greedy, want_argmax, pair, vec;
+  SlicePart* part;
+  RowStat* rs;
+  double* smass;
+  RowStatsOut rso;
+  hipEvent_t ev_start, ev_stop;   // optional: bracket the streaming pass (benchmark timing)
+};
+
+struct PosStatsOut {
+  float* p_y;
+  float* q_y;
+  float* one_minus_tv;
+  float* draft_entropy_bits;
+  float* draft_max_prob;
+  float* target_entropy_bits;
+  float* target_max_prob;
+};
+
+struct FinalizeArgs {
+  RowMap map;
+  int V, n_slices, greedy;
+  float c;
+  uint64_t seed, step;
+  const int32_t* tokens;
+  const RowStat* rs;
+  const SlicePart* part;
+  const double* smass;
+  int32_t* out_tokens;
+  int32_t* out_num_accepted;
+  float* out_req_stats;
+  int32_t* out_status;
+  PosStatsOut st;
+};
+
+struct ResidualArgs {
+  RowMap map;               // plain-row mode, B = R
+  int V, n_slices, greedy;
+  float c;
+  uint64_t seed, step;
+  const double* uniforms;
+  const RowStat* rs;
+  const SlicePart* part;
+  const double* smass;
+  int32_t* out_token;
+  double* out_mass;
+  int32_t* out_status;
+};
+
+hipError_t launch_dense(const DenseLaunch& L, hipStream_t st);
+hipError_t launch_finalize(const FinalizeArgs& a, int dt, hipStream_t st);
+hipError_t launch_residual_finalize(const ResidualArgs& a, int dt, hipStream_t st);
+
+size_t slice_part_bytes();
+size_t row_stat_bytes();
+
+}  // namespace specv

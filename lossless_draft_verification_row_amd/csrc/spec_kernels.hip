@@ -1,0 +1,672 @@
+// spec_kernels.hip -- gfx950 kernels of batched speculative-sampling verification.
+//
+// The verification round follows the guide page "5.1 投机解码核心原理" (speculative decoding:
+// core principles): §3.1 greedy rule, §3.2 acceptance ratio min(1, p/q) and residual
+// [p - q]_+ / sum [p - q]_+, §3.3 token-only drafts, §4.1 beta = sum [p - q]_+ = 1 - A,
+// §4.3 A = 1 - TV, §5.1 stop at the first rejection, §5.2 bonus token from p_{g+1}.  The
+// per-position signals are those of the SpecKV page (draft-model signals section): entropy
+// in bits and max probability of each draft distribution, with mean / max / min.
+//
+// Dense path (no top-k / top-p), all HBM-bound streaming over 4096-logit slices:
+//   pass1    one workgroup per (row, slice): slice max, sum exp2((l - m) c), entropy term,
+//            optional argmax / kept count.                       reads every needed row once
+//   combine  one wave per row: fixed-order fp64 merge of the slice partials.
+//   pair     one workgroup per (position, slice): residual mass of the slice,
+//            sum [p - q]_+, from the target and draft rows.      re-reads the paired rows
+//   finalize one workgroup per request: accept scan, three-level sampler (re-reads one
+//            chunk), outputs.
+// Greedy needs pass1 (argmax) + combine + finalize over the target rows only.
+#include "spec_device.h"
+#include "spec_internal.h"
+
+namespace specv {
+
+// ---------------------------------------------------------------- row addressing
+
+__device__ __forceinline__ bool request_rows(const RowMap& m, int b, int& g, int& c0) {
+  c0 = m.cu[b];
+  const int c1 = m.cu[b + 1];
+  g = c1 - c0;
+  return c0 >= 0 && g >= 0 && g <= m.G && c1 <= m.n_draft_rows;
+}
+
+// Logical row lr = 2 * slot + kind (kind 0: target / p row, 1: draft / q row).  In request
+// mode slot = b * (G + 1) + i; in plain-row mode slot = r.  Returns nullptr for rows that do
+// not exist (i beyond gamma_b, no draft, or an inconsistent request).
+template <int DT>
+__device__ __forceinline__ const void* resolve_row(const RowMap& m, int lr) {
+  const int slot = lr >> 1, kind = lr & 1;
+  if (m.cu == nullptr) {
+    if (slot >= m.B) return nullptr;
+    if (kind == 0) return row_ptr<DT>(m.tgt, m.tgt_ld, slot);
+    return m.drf ? row_ptr<DT>(m.drf, m.drf_ld, slot) : nullptr;
+  }
+  const int b = slot / (m.G + 1), i = slot - b * (m.G + 1);
+  int g, c0;
+  if (b >= m.B || !request_rows(m, b, g, c0)) return nullptr;
+  if (kind == 0) return i <= g ? row_ptr<DT>(m.tgt, m.tgt_ld, (int64_t)c0 + b + i) : nullptr;
+  return (m.drf && i < g) ? row_ptr<DT>(m.drf, m.drf_ld, (int64_t)c0 + i) : nullptr;
+}
+
+// ---------------------------------------------------------------- pass 1
+
+// MODE_SOFTMAX: slice max, sum of exp2((l - m) c) and the entropy numerator; argmax and kept
+// count on request.  MODE_ARGMAX (greedy): slice max, argmax and a NaN / +inf flag.
+template <int DT, bool VEC, int MODE>
+__global__ __launch_bounds__(kThreads) void k_pass1(RowMap m, int V, int n_slices, float c,
+                                                     int want_argmax, SlicePart* __restrict__ part) {
+  const int lr = blockIdx.x, sl = blockIdx.y;
+  const void* row = resolve_row<DT>(m, lr);
+  if (row == nullptr) return;
+  __shared__ float redf[kWaves];
+  __shared__ int redi[kWaves];
+  __shared__ double redd[kWaves];
+  const int base = sl * kChunk;
+  float v[kPerThread];
+  load_slice<DT, VEC>(row, V, base, v);
+
+  float mt = v[0];
+#pragma unroll
+  for (int j = 1; j < kPerThread; ++j) mt = fmaxf(mt, v[j]);
+  const float mw = block_max(mt, redf);
+
+  SlicePart out;
+  out.m = mw;
+  out.s = 0.f;
+  out.w = 0.f;
+  out.amax = -1;
+  out.cnt = 0;
+  if (MODE == kModeArgmax || want_argmax) {
+    int idx = INT_MAX;
+    if (mw > -INFINITY) {
+#pragma unroll
+      for (int j = kPerThread - 1; j >= 0; --j)
+        if (v[j] == mw) idx = slice_index<DT>(base, threadIdx.x, j);
+    }
+    idx = block_min_i(idx, redi);
+    out.amax = (idx == INT_MAX) ? -1 : idx;
+  }
+  if (MODE == kModeArgmax) {
+    int bad = 0;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) bad |= __builtin_amdgcn_class(v[j], 0x203) ? 1 : 0;  // NaN, +inf
+    bad = block_or(bad, redi);
+    if (bad) out.amax = -2;
+  } else {
+    // e = exp2((l - m) c) relative to the slice max; -inf logits give e = 0 and, through the
+    // clamp, a zero entropy term.  A NaN or +inf logit makes s NaN.
+    const float ref = (mw == -INFINITY) ? 0.f : mw;
+    float s = 0.f, w = 0.f;
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const float t = (v[j] - ref) * c;
+      const float e = __builtin_amdgcn_exp2f(t);
+      s += e;
+      w = fmaf(e, fmaxf(t, -256.f), w);
+      if (want_argmax) cnt += (v[j] > -INFINITY) ? 1 : 0;
+    }
+    out.s = (float)block_sum_d((double)s, redd);
+    out.w = (float)block_sum_d((double)w, redd);
+    if (want_argmax) out.cnt = (int)block_sum_d((double)cnt, redd);
+  }
+  if (threadIdx.x == 0) part[(int64_t)lr * n_slices + sl] = out;
+}
+
+// ---------------------------------------------------------------- combine
+
+// One wave per logical row: fixed-order fp64 merge of the slice partials into RowStat.
+// Optionally writes the spec_row_stats outputs (plain-row mode, kind 0 rows only).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_combine(RowMap m, int n_lr, int n_slices, float c,
+                                                       int greedy, const SlicePart* __restrict__ part,
+                                                       RowStat* __restrict__ rs, RowStatsOut out) {
+  const int lane = threadIdx.x & 63;
+  const int lr = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (lr >= n_lr) return;
+  if (resolve_row<DT>(m, lr) == nullptr) return;
+  const SlicePart* p = part + (int64_t)lr * n_slices;
+
+  float mloc = -INFINITY;
+  int bad = 0;
+  for (int s = lane; s < n_slices; s += 64) {
+    const SlicePart q = p[s];
+    mloc = fmaxf(mloc, q.m);
+    if (q.amax == -2 || q.m == INFINITY || (!greedy && !(q.s == q.s && q.s < INFINITY))) bad = 1;
+  }
+  const float mrow = wave_max(mloc);
+  bad = wave_or(bad);
+
+  double z = 0.0, wsum = 0.0;
+  int amax = INT_MAX, cnt = 0;
+  const double cd = (double)c;
+  for (int s = lane; s < n_slices; s += 64) {
+    const SlicePart q = p[s];
+    if (q.m == mrow && q.amax >= 0) amax = min(amax, q.amax);
+    cnt += q.cnt;
+    if (!greedy && q.s > 0.f) {
+      const double d = ((double)q.m - (double)mrow) * cd;  // <= 0
+      const double f = exp2(d);
+      z += (double)q.s * f;
+      wsum += f * ((double)q.w + (double)q.s * d);
+    }
+  }
+  z = wave_sum_d(z);
+  wsum = wave_sum_d(wsum);
+  amax = wave_min_i(amax);
+  cnt = (int)wave_sum_d((double)cnt);
+
+  if (lane != 0) return;
+  RowStat r;
+  r.m = mrow;
+  r.amax = (amax == INT_MAX) ? -1 : amax;
+  r.flags = (bad || !(mrow > -INFINITY)) ? kStNonfinite : 0;
+  r.tau = -INFINITY;
+  r.kept = cnt;
+  if (greedy) {
+    r.z = 1.0; r.log2z = 0.0; r.inv_z = 1.f; r.h_bits = 0.f; r.maxp = 1.f; r.kept = 1;
+  } else {
+    r.z = z;
+    r.log2z = log2(z);
+    r.inv_z = (float)(1.0 / z);
+    r.h_bits = (float)(r.log2z - wsum / z);
+    r.maxp = (float)(1.0 / z);
+  }
+  if (r.flags) r.amax = -1;
+  rs[lr] = r;
+
+  if (out.enabled && (lr & 1) == 0) {
+    const int row = lr >> 1;
+    const float nan = __int_as_float(0x7fc00000);
+    const bool ok = r.flags == 0;
+    if (out.max_logit) out.max_logit[row] = ok ? r.m : nan;
+    if (out.argmax) out.argmax[row] = ok ? r.amax : -1;
+    if (out.log_z) out.log_z[row] = (!ok || greedy) ? nan : (float)(((double)r.m * cd + r.log2z) * 0.6931471805599453);
+    if (out.entropy_bits) out.entropy_bits[row] = ok ? r.h_bits : nan;
+    if (out.max_prob) out.max_prob[row] = ok ? r.maxp : nan;
+    if (out.kept_count) out.kept_count[row] = ok ? r.kept : 0;
+  }
+}
+
+// ---------------------------------------------------------------- pair pass
+
+// Residual mass of one slice of one (target, draft) row pair: sum_x [p(x) - q(x)]_+ with
+// p(x) = exp2((l_x - m) c) / z evaluated in fp32 exactly as the finalize pass does.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_pair(RowMap m, int V, int n_slices, float c,
+                                                    const RowStat* __restrict__ rs,
+                                                    double* __restrict__ smass) {
+  const int slot = blockIdx.x, sl = blockIdx.y;
+  const void* prow = resolve_row<DT>(m, 2 * slot);
+  const void* qrow = resolve_row<DT>(m, 2 * slot + 1);
+  if (prow == nullptr || qrow == nullptr) return;
+  __shared__ double redd[kWaves];
+  const RowStat P = rs[2 * slot], Q = rs[2 * slot + 1];
+  if ((P.flags | Q.flags) != 0) {
+    if (threadIdx.x == 0) smass[(int64_t)slot * n_slices + sl] = 0.0;
+    return;
+  }
+  const int base = sl * kChunk;
+  float lp[kPerThread], lq[kPerThread];
+  load_slice<DT, VEC>(prow, V, base, lp);
+  load_slice<DT, VEC>(qrow, V, base, lq);
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const float p = __builtin_amdgcn_exp2f((lp[j] - P.m) * c) * P.inv_z;
+    const float q = __builtin_amdgcn_exp2f((lq[j] - Q.m) * c) * Q.inv_z;
+    acc += fmaxf(p - q, 0.f);
+  }
+  const double tot = block_sum_d((double)acc, redd);
+  if (threadIdx.x == 0) smass[(int64_t)slot * n_slices + sl] = tot;
+}
+
+// ---------------------------------------------------------------- sampler
+
+// Mass of chunk k of row `lr` under p: sum_x exp2((l - m) c) / z from the slice partial.
+__device__ __forceinline__ double chunk_p_mass(const SlicePart* part, int lr, int n_slices, int k,
+                                               const RowStat& P, double cd) {
+  const SlicePart q = part[(int64_t)lr * n_slices + k];
+  if (!(q.s > 0.f)) return 0.0;
+  return (double)q.s * exp2(((double)q.m - (double)P.m) * cd) / P.z;
+}
+
+// first c with prefix(c) > target; if rounding leaves none, the last c with positive mass
+struct LevelPick {
+  int idx;
+  double total;
+};
+
+// Levels 2 and 3 of the sampler inside chunk k: every thread evaluates 16 weights of the
+// chunk (4 threads per 64-token group), group masses are fp64 sums, the scans are sequential
+// in fp64.  wkind: 0 = p only, 1 = [p - q]_+, 2 = p with token y removed.
+template <int DT>
+__device__ int sample_in_chunk(const void* prow, const void* qrow, int V, int k, float c,
+                               const RowStat& P, const RowStat& Q, int wkind, int y,
+                               double u2, double u3, float* wbuf, double* gmass) {
+  const int t = threadIdx.x;
+  const int grp = t >> 2, quarter = t & 3;
+  const int x0 = k * kChunk + grp * kGroup + quarter * 16;
+  double part = 0.0;
+#pragma unroll 4
+  for (int e = 0; e < 16; ++e) {
+    const int x = x0 + e;
+    float w = 0.f;
+    if (x < V) {
+      const float p = __builtin_amdgcn_exp2f((logit_at<DT>(prow, x) - P.m) * c) * P.inv_z;
+      if (wkind == 1) {
+        const float q = __builtin_amdgcn_exp2f((logit_at<DT>(qrow, x) - Q.m) * c) * Q.inv_z;
+        w = fmaxf(p - q, 0.f);
+      } else if (wkind == 2) {
+        w = (x == y) ? 0.f : p;
+      } else {
+        w = p;
+      }
+    }
+    wbuf[x0 - k * kChunk + e] = w;
+    part += (double)w;
+  }
+  part += __shfl_xor(part, 1, 64);
+  part += __shfl_xor(part, 2, 64);
+  if (quarter == 0) gmass[grp] = part;
+  __syncthreads();
+  __shared__ int pick;
+  if (t == 0) {
+    const int n_in = min(kChunk, V - k * kChunk);
+    const int n_groups = (n_in + kGroup - 1) / kGroup;
+    double tot = 0.0;
+    for (int g = 0; g < n_groups; ++g) tot += gmass[g];
+    double target = u2 * tot, cum = 0.0;
+    int gsel = -1, glast = -1;
+    for (int g = 0; g < n_groups; ++g) {
+      cum += gmass[g];
+      if (gmass[g] > 0.0) glast = g;
+      if (cum > target) { gsel = g; break; }
+    }
+    if (gsel < 0) gsel = glast;
+    int xsel = -1;
+    if (gsel >= 0) {
+      const int lo = gsel * kGroup, hi = min(lo + kGroup, n_in);
+      const double gm = gmass[gsel];
+      target = u3 * gm;
+      cum = 0.0;
+      int xlast = -1;
+      for (int x = lo; x < hi; ++x) {
+        cum += (double)wbuf[x];
+        if (wbuf[x] > 0.f) xlast = x;
+        if (cum > target) { xsel = x; break; }
+      }
+      if (xsel < 0) xsel = xlast;
+      if (xsel >= 0) xsel += k * kChunk;
+    }
+    pick = xsel;
+  }
+  __syncthreads();
+  return pick;
+}
+
+// Level 1 over chunk masses (sequential fp64).  Returns -1 if every mass is zero.
+__device__ __forceinline__ int pick_chunk(const double* mass, int n, double u1, double* total_out) {
+  double tot = 0.0;
+  for (int k = 0; k < n; ++k) tot += mass[k];
+  *total_out = tot;
+  if (!(tot > 0.0)) return -1;
+  const double target = u1 * tot;
+  double cum = 0.0;
+  int last = -1;
+  for (int k = 0; k < n; ++k) {
+    cum += mass[k];
+    if (mass[k] > 0.0) last = k;
+    if (cum > target) return k;
+  }
+  return last;
+}
+
+// p(x) in fp64 from the row statistics: exp2((l_x - m) c) / z.
+template <int DT>
+__device__ __forceinline__ double p_of(const void* row, int x, const RowStat& P, double cd) {
+  const double l = (double)logit_at<DT>(row, x);
+  return exp2((l - (double)P.m) * cd) / P.z;
+}
+
+// ---------------------------------------------------------------- finalize (requests)
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
+  const RowMap& m = a.map;
+  const int b = blockIdx.x;
+  const int G1 = m.G + 1;
+  __shared__ float wbuf[kChunk];
+  __shared__ double gmass[kChunk / kGroup];
+  __shared__ double cmass[kMaxChunks];
+  __shared__ int sh_k, sh_wkind, sh_row, sh_y, sh_emit;
+  __shared__ double sh_u2, sh_u3;
+
+  int g, c0;
+  const bool ok_req = request_rows(m, b, g, c0);
+  const float nan = __int_as_float(0x7fc00000);
+  const double cd = (double)a.c;
+  const bool greedy = a.greedy != 0;
+  const bool token_only = greedy || m.drf == nullptr;
+
+  if (!ok_req) {
+    if (threadIdx.x <= m.G) a.out_tokens[(int64_t)b * G1 + threadIdx.x] = -1;
+    if (threadIdx.x == 0) {
+      a.out_num_accepted[b] = 0;
+      a.out_status[b] = kStBadGamma;
+      if (a.out_req_stats)
+        for (int q = 0; q < 4; ++q) a.out_req_stats[(int64_t)b * 4 + q] = nan;
+    }
+    return;
+  }
+
+  // per-position statistics (one thread per position) and the non-finite check
+  int flags = 0;
+  for (int i = 0; i <= g; ++i) {
+    flags |= a.rs[2 * (b * G1 + i)].flags;
+    if (!token_only && i < g) flags |= a.rs[2 * (b * G1 + i) + 1].flags;
+  }
+  const int t = threadIdx.x;
+  if (t <= g) {
+    const RowStat P = a.rs[2 * (b * G1 + t)];
+    const int64_t trow = (int64_t)c0 + b + t;
+    const bool okp = P.flags == 0;
+    if (a.st.target_entropy_bits) a.st.target_entropy_bits[trow] = okp ? P.h_bits : nan;
+    if (a.st.target_max_prob) a.st.target_max_prob[trow] = okp ? P.maxp : nan;
+    if (t < g) {
+      const int64_t drow = (int64_t)c0 + t;
+      const int y = a.tokens[drow];
+      const bool yv = y >= 0 && y < a.V;
+      const void* prow = row_ptr<DT>(m.tgt, m.tgt_ld, trow);
+      float py = nan, qy = nan, ovl = nan, dh = nan, dm = nan;
+      if (greedy) {
+        py = (okp && yv) ? (y == P.amax ? 1.f : 0.f) : nan;
+        qy = yv ? 1.f : nan;
+        ovl = okp ? (yv ? py : 0.f) : nan;
+      } else if (token_only) {
+        const double p = (okp && yv) ? p_of<DT>(prow, y, P, cd) : 0.0;
+        py = (okp && yv) ? (float)p : nan;
+        qy = yv ? 1.f : nan;
+        ovl = okp ? (yv ? (float)p : 0.f) : nan;
+        dh = yv ? 0.f : nan;
+        dm = yv ? 1.f : nan;
+      } else {
+        const RowStat Q = a.rs[2 * (b * G1 + t) + 1];
+        const bool okq = Q.flags == 0;
+        const void* qrow = row_ptr<DT>(m.drf, m.drf_ld, drow);
+        py = (okp && yv) ? (float)p_of<DT>(prow, y, P, cd) : nan;
+        qy = (okq && yv) ? (float)p_of<DT>(qrow, y, Q, cd) : nan;
+        if (okp && okq) {
+          double beta = 0.0;
+          for (int k = 0; k < a.n_slices; ++k) beta += a.smass[(int64_t)(b * G1 + t) * a.n_slices + k];
+          ovl = (float)(1.0 - beta);
+        }
+        dh = okq ? Q.h_bits : nan;
+        dm = okq ? Q.maxp : nan;
+      }
+      if (a.st.p_y) a.st.p_y[drow] = py;
+      if (a.st.q_y) a.st.q_y[drow] = qy;
+      if (a.st.one_minus_tv) a.st.one_minus_tv[drow] = ovl;
+      if (a.st.draft_entropy_bits) a.st.draft_entropy_bits[drow] = dh;
+      if (a.st.draft_max_prob) a.st.draft_max_prob[drow] = dm;
+      wbuf[2 * t] = dh;
+      wbuf[2 * t + 1] = dm;
+    }
+  }
+  __syncthreads();
+  if (t == 0 && a.out_req_stats) {
+    float r[4] = {nan, nan, nan, nan};
+    if (g > 0 && !greedy) {
+      double hs = 0.0, cs = 0.0;
+      float hmax = -INFINITY, cmin = INFINITY;
+      bool anynan = false;
+      for (int i = 0; i < g; ++i) {
+        const float h = wbuf[2 * i], cm = wbuf[2 * i + 1];
+        if (!(h == h) || !(cm == cm)) anynan = true;
+        hs += h; cs += cm;
+        hmax = fmaxf(hmax, h); cmin = fminf(cmin, cm);
+      }
+      if (!anynan) { r[0] = (float)(hs / g); r[1] = (float)(cs / g); r[2] = hmax; r[3] = cmin; }
+    }
+    for (int q = 0; q < 4; ++q) a.out_req_stats[(int64_t)b * 4 + q] = r[q];
+  }
+
+  if (flags & kStNonfinite) {
+    if (t <= m.G) a.out_tokens[(int64_t)b * G1 + t] = -1;
+    if (t == 0) { a.out_num_accepted[b] = 0; a.out_status[b] = kStNonfinite; }
+    return;
+  }
+
+  // accept scan (one thread; at most gamma_max steps)
+  if (t == 0) {
+    int status = 0, j = -1;
+    for (int i = 0; i < g; ++i) {
+      const int y = a.tokens[(int64_t)c0 + i];
+      if (y < 0 || y >= a.V) { status |= kStBadToken; j = i; break; }
+      const RowStat P = a.rs[2 * (b * G1 + i)];
+      if (greedy) {
+        if (y == P.amax) continue;
+        j = i;
+        break;
+      }
+      const void* prow = row_ptr<DT>(m.tgt, m.tgt_ld, (int64_t)c0 + b + i);
+      const double py = p_of<DT>(prow, y, P, cd);
+      double qy = 1.0;
+      if (!token_only) {
+        const RowStat Q = a.rs[2 * (b * G1 + i) + 1];
+        qy = p_of<DT>(row_ptr<DT>(m.drf, m.drf_ld, (int64_t)c0 + i), y, Q, cd);
+      }
+      if (!(qy > 0.0)) { status |= kStZeroQ; j = i; break; }
+      const double acc = fmin(1.0, py / qy);
+      uint64_t w[4];
+      philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(i + 1), 0, 0, w);
+      if (!(u53(w[0]) < acc)) { j = i; break; }
+    }
+    const int n_acc = j < 0 ? g : j;
+    const int pos = j < 0 ? g : j;  // 0-based position whose distribution emits the token
+    uint64_t w[4];
+    philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(pos + 1), 0, 0, w);
+    sh_u2 = u53(w[2]);
+    sh_u3 = u53(w[3]);
+    sh_row = pos;
+    sh_emit = n_acc;
+    const RowStat P = a.rs[2 * (b * G1 + pos)];
+    int k = -1, wkind = 0, y = -1;
+    if (greedy) {
+      k = -2;  // no sampling: emit the argmax
+      sh_y = P.amax;
+    } else {
+      const int lr_p = 2 * (b * G1 + pos);
+      if (j >= 0) {
+        y = a.tokens[(int64_t)c0 + j];
+        if (!token_only) {
+          wkind = 1;
+          for (int q = 0; q < a.n_slices; ++q) cmass[q] = a.smass[(int64_t)(b * G1 + pos) * a.n_slices + q];
+        } else {
+          wkind = 2;
+          const bool yv = y >= 0 && y < a.V;
+          const double py = yv ? p_of<DT>(row_ptr<DT>(m.tgt, m.tgt_ld, (int64_t)c0 + b + pos), y, P, cd) : 0.0;
+          for (int q = 0; q < a.n_slices; ++q) {
+            double pm = chunk_p_mass(a.part, lr_p, a.n_slices, q, P, cd);
+            if (yv && y / kChunk == q) pm = fmax(pm - py, 0.0);
+            cmass[q] = pm;
+          }
+        }
+      } else {
+        wkind = 0;
+        for (int q = 0; q < a.n_slices; ++q) cmass[q] = chunk_p_mass(a.part, lr_p, a.n_slices, q, P, cd);
+      }
+      double tot;
+      k = pick_chunk(cmass, a.n_slices, u53(w[1]), &tot);
+      if (k < 0) {  // empty residual: draw from p instead
+        status |= kStResidualEmpty;
+        wkind = 0;
+        for (int q = 0; q < a.n_slices; ++q) cmass[q] = chunk_p_mass(a.part, lr_p, a.n_slices, q, P, cd);
+        k = pick_chunk(cmass, a.n_slices, u53(w[1]), &tot);
+      }
+      sh_y = y;
+    }
+    sh_k = k;
+    sh_wkind = wkind;
+    a.out_status[b] = status;
+  }
+  __syncthreads();
+  const int k = sh_k, pos = sh_row, n_acc = sh_emit;
+  int x;
+  if (k == -2) {
+    x = sh_y;
+  } else if (k < 0) {
+    x = -1;
+  } else {
+    const RowStat P = a.rs[2 * (b * G1 + pos)];
+    const void* prow = row_ptr<DT>(m.tgt, m.tgt_ld, (int64_t)c0 + b + pos);
+    const void* qrow = nullptr;
+    RowStat Q = P;
+    if (sh_wkind == 1) {
+      Q = a.rs[2 * (b * G1 + pos) + 1];
+      qrow = row_ptr<DT>(m.drf, m.drf_ld, (int64_t)c0 + pos);
+    }
+    x = sample_in_chunk<DT>(prow, qrow, a.V, k, a.c, P, Q, sh_wkind, sh_y, sh_u2, sh_u3, wbuf, gmass);
+  }
+  if (t <= m.G) {
+    int tok = -1;
+    if (t < n_acc) tok = a.tokens[(int64_t)c0 + t];
+    else if (t == n_acc) tok = x;
+    a.out_tokens[(int64_t)b * G1 + t] = tok;
+  }
+  if (t == 0) a.out_num_accepted[b] = n_acc;
+}
+
+// ---------------------------------------------------------------- finalize (plain rows)
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_residual_finalize(ResidualArgs a) {
+  const RowMap& m = a.map;
+  const int r = blockIdx.x;
+  __shared__ float wbuf[kChunk];
+  __shared__ double gmass[kChunk / kGroup];
+  __shared__ double cmass[kMaxChunks];
+  __shared__ int sh_k, sh_wkind, sh_tok;
+  __shared__ double sh_u2, sh_u3;
+  const double cd = (double)a.c;
+  const RowStat P = a.rs[2 * r];
+  const bool has_q = m.drf != nullptr;
+  const RowStat Q = has_q ? a.rs[2 * r + 1] : P;
+  const int t = threadIdx.x;
+  if (P.flags || (has_q && Q.flags)) {
+    if (t == 0) {
+      a.out_token[r] = -1;
+      if (a.out_mass) a.out_mass[r] = __longlong_as_double(0x7ff8000000000000ll);
+      a.out_status[r] = kStNonfinite;
+    }
+    return;
+  }
+  if (t == 0) {
+    double u1, u2, u3;
+    if (a.uniforms) {
+      u1 = a.uniforms[(int64_t)r * 3 + 0];
+      u2 = a.uniforms[(int64_t)r * 3 + 1];
+      u3 = a.uniforms[(int64_t)r * 3 + 2];
+    } else {
+      uint64_t w[4];
+      philox4x64_10(a.seed, a.step, (uint64_t)r, 0, 1, 0, w);
+      u1 = u53(w[1]); u2 = u53(w[2]); u3 = u53(w[3]);
+    }
+    sh_u2 = u2;
+    sh_u3 = u3;
+    int status = 0, k, wkind;
+    double mass;
+    if (a.greedy) {
+      k = -2;
+      sh_tok = P.amax;
+      mass = (!has_q || P.amax != Q.amax) ? 1.0 : 0.0;
+      if (!(mass > 0.0)) status |= kStResidualEmpty;
+      wkind = 0;
+    } else {
+      if (has_q) {
+        wkind = 1;
+        for (int q = 0; q < a.n_slices; ++q) cmass[q] = a.smass[(int64_t)r * a.n_slices + q];
+      } else {
+        wkind = 0;
+        for (int q = 0; q < a.n_slices; ++q) cmass[q] = chunk_p_mass(a.part, 2 * r, a.n_slices, q, P, cd);
+      }
+      double tot;
+      k = pick_chunk(cmass, a.n_slices, u1, &tot);
+      mass = has_q ? tot : 1.0;
+      if (k < 0) {
+        status |= kStResidualEmpty;
+        wkind = 0;
+        for (int q = 0; q < a.n_slices; ++q) cmass[q] = chunk_p_mass(a.part, 2 * r, a.n_slices, q, P, cd);
+        k = pick_chunk(cmass, a.n_slices, u1, &tot);
+      }
+    }
+    sh_k = k;
+    sh_wkind = wkind;
+    if (a.out_mass) a.out_mass[r] = mass;
+    a.out_status[r] = status;
+  }
+  __syncthreads();
+  const int k = sh_k;
+  int x;
+  if (k == -2) x = sh_tok;
+  else if (k < 0) x = -1;
+  else {
+    const void* prow = row_ptr<DT>(m.tgt, m.tgt_ld, r);
+    const void* qrow = has_q ? row_ptr<DT>(m.drf, m.drf_ld, r) : nullptr;
+    x = sample_in_chunk<DT>(prow, qrow, a.V, k, a.c, P, Q, sh_wkind, -1, sh_u2, sh_u3, wbuf, gmass);
+  }
+  if (t == 0) a.out_token[r] = x;
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <int DT>
+static hipError_t launch_dense_t(const DenseLaunch& L, hipStream_t st) {
+  const dim3 blk(kThreads);
+  const RowMap& m = L.map;
+  const int n_lr = 2 * L.n_slots;
+  const dim3 g1(n_lr, L.n_slices);
+  if (L.ev_start) hipEventRecord(L.ev_start, st);
+  if (L.greedy) {
+    if (L.vec) hipLaunchKernelGGL((k_pass1<DT, true, kModeArgmax>), g1, blk, 0, st, m, L.V, L.n_slices, L.c, 1, L.part);
+    else hipLaunchKernelGGL((k_pass1<DT, false, kModeArgmax>), g1, blk, 0, st, m, L.V, L.n_slices, L.c, 1, L.part);
+  } else {
+    if (L.vec) hipLaunchKernelGGL((k_pass1<DT, true, kModeSoftmax>), g1, blk, 0, st, m, L.V, L.n_slices, L.c, L.want_argmax, L.part);
+    else hipLaunchKernelGGL((k_pass1<DT, false, kModeSoftmax>), g1, blk, 0, st, m, L.V, L.n_slices, L.c, L.want_argmax, L.part);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (L.ev_stop) hipEventRecord(L.ev_stop, st);
+  hipLaunchKernelGGL((k_combine<DT>), dim3((n_lr + kWaves - 1) / kWaves), blk, 0, st, m, n_lr, L.n_slices, L.c,
+                     L.greedy, L.part, L.rs, L.rso);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (L.pair) {
+    const dim3 g3(L.n_slots, L.n_slices);
+    if (L.vec) hipLaunchKernelGGL((k_pair<DT, true>), g3, blk, 0, st, m, L.V, L.n_slices, L.c, L.rs, L.smass);
+    else hipLaunchKernelGGL((k_pair<DT, false>), g3, blk, 0, st, m, L.V, L.n_slices, L.c, L.rs, L.smass);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+size_t slice_part_bytes() { return sizeof(SlicePart); }
+size_t row_stat_bytes() { return sizeof(RowStat); }
+
+hipError_t launch_dense(const DenseLaunch& L, hipStream_t st) {
+  return L.dt == kDtBF16 ? launch_dense_t<kDtBF16>(L, st) : launch_dense_t<kDtF32>(L, st);
+}
+
+hipError_t launch_finalize(const FinalizeArgs& a, int dt, hipStream_t st) {
+  if (dt == kDtBF16) hipLaunchKernelGGL((k_finalize<kDtBF16>), dim3(a.map.B), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((k_finalize<kDtF32>), dim3(a.map.B), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_finalize(const ResidualArgs& a, int dt, hipStream_t st) {
+  if (dt == kDtBF16) hipLaunchKernelGGL((k_residual_finalize<kDtBF16>), dim3(a.map.B), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((k_residual_finalize<kDtF32>), dim3(a.map.B), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace specv

@@ -1,0 +1,75 @@
+"""CPU checks of the C-ABI library: it loads and exports every symbol the header declares,
+and the argument checks that need no GPU reject bad calls.  No compute call is made."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import lossless_draft_verification_row_amd as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(spec_\w+)\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["spec_verify_batch", "spec_row_stats", "spec_residual_sample", "spec_status_string",
+              "spec_verify_workspace_bytes", "spec_row_stats_workspace_bytes",
+              "spec_residual_sample_workspace_bytes"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load_library()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", L.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (spec_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings():
+    assert L.spec_status_string(0) == "ok"
+    assert "workspace" in L.spec_status_string(-3)
+    for name, bit in L.STATUS.items():
+        assert L.spec_status_string(bit) != "unknown code", name
+
+
+def test_workspace_sizes():
+    w2 = L.spec_verify_workspace_bytes(64, 151936, 7, L.SPEC_BF16, 1.0)
+    assert 0 < w2 < 8 << 20
+    assert L.spec_verify_workspace_bytes(0, 151936, 7, L.SPEC_BF16, 1.0) == 0
+    assert L.spec_row_stats_workspace_bytes(10, 8, L.SPEC_F32, 1.0) > 0
+    assert L.spec_residual_sample_workspace_bytes(10, 8, L.SPEC_F32, 0.0) > 0
+
+
+def test_argument_checks_without_gpu():
+    lib = L.load_library()
+    sp = L.SamplingParams(1.0, 0, 1.0)
+    ps = L.PosStats()
+    # null target pointer, bad vocabulary, bad gamma, bad temperature: rejected before any launch
+    assert lib.spec_verify_batch(2, 100, 3, 1, None, 100, None, 0, None, None, 0, sp, 0, 0,
+                                 None, None, ps, None, None, None, 0, None) == -1
+    assert lib.spec_verify_batch(2, 0, 3, 1, 16, 100, None, 0, None, None, 0, sp, 0, 0,
+                                 None, None, ps, None, None, None, 0, None) == -1
+    assert lib.spec_verify_batch(2, 100, 99999, 1, 16, 100, None, 0, None, None, 0, sp, 0, 0,
+                                 None, None, ps, None, None, None, 0, None) == -1
+    bad_t = L.SamplingParams(-1.0, 0, 1.0)
+    assert lib.spec_row_stats(4, 100, 1, 16, 100, bad_t, *([None] * 6), None, 0, None) == -1
+    bad_p = L.SamplingParams(1.0, 0, 0.0)
+    assert lib.spec_row_stats(4, 100, 1, 16, 100, bad_p, *([None] * 6), None, 0, None) == -1
+    # undersized workspace is reported before any launch
+    assert lib.spec_row_stats(4, 100, 1, 256, 100, sp, *([None] * 6), None, 0, None) == -3
+    # top-p without top-k is not implemented by this build
+    only_p = L.SamplingParams(1.0, 0, 0.9)
+    assert lib.spec_row_stats(4, 100, 1, 256, 100, only_p, *([None] * 6), 256, 1 << 20, None) == -2
+    # B = 0 is a no-op
+    assert lib.spec_verify_batch(0, 100, 3, 1, None, 100, None, 0, None, None, 0, sp, 0, 0,
+                                 None, None, ps, None, None, None, 0, None) == 0
