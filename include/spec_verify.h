@@ -16,11 +16,13 @@
  * max probability, their mean / max / min over the draft block).
  *
  * Conventions shared by every entry point
- *  - Every pointer argument is DEVICE memory owned by the caller, except `uniforms` in
- *    spec_residual_sample (device too) and the by-value structs.  The library allocates
- *    nothing, keeps no state between calls and writes only the outputs and the workspace.
+ *  - Every pointer argument is DEVICE memory owned by the caller; structs are by value.
+ *    The library allocates nothing and writes only the outputs and the workspace.
  *  - Calls are asynchronous and ordered on `hip_stream` (a hipStream_t; NULL = the null
  *    stream).  They are re-entrant when concurrent calls use different workspaces.
+ *  - Workspaces: zero-fill once before first use; sizes come from the *_workspace_bytes
+ *    functions.  The only state the library keeps is a process-wide call sequence number
+ *    that tags the records a call writes into its workspace.
  *  - Logit rows are dense, row-major, `ld` ELEMENTS apart (ld >= V).  dtype SPEC_BF16 rows
  *    hold bf16 bit patterns, SPEC_F32 rows hold floats.  A 16-byte aligned base with a
  *    16-byte multiple row stride takes the vector path; anything else takes a scalar path
@@ -108,8 +110,12 @@ typedef struct {
  *  at i, words 1..3 drive the three sampler levels when the emitted token is drawn at i.
  *  The sampler is a fixed-order inverse CDF in three levels (chunks of 4096 tokens, groups of
  *  64, tokens) with one uniform per level; its law is exactly the residual (or p_{g+1}).
+ *  If cu_draft is not an exclusive prefix (cu_draft[0] = 0, 0 <= gamma_b <= gamma_max,
+ *  cu_draft[B] = n_draft_rows) no row is read and every request reports SPEC_STATUS_BAD_GAMMA.
  *  workspace: spec_verify_workspace_bytes(B, V, gamma_max, dt, sp) bytes of device memory,
- *  256-byte aligned; its contents need no initialisation and are scratch after the call. */
+ *  256-byte aligned, ZERO-FILLED once before its first use with this library (workgroups of
+ *  one call exchange records in it, tagged with a per-call sequence number that a zero-filled
+ *  workspace never matches).  A workspace serves one call at a time. */
 int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt,
                       const void* target_logits, int64_t target_ld,
                       const void* draft_logits, int64_t draft_ld,
@@ -156,6 +162,11 @@ size_t spec_residual_sample_workspace_bytes(int R, int V, spec_dtype dt, spec_sa
  * time that kernel alone.  NULL, NULL switches it off.  Process-wide and not thread-safe;
  * the events stay owned by the caller.  Returns SPEC_ERR_INVALID if only one is NULL. */
 int spec_set_profile_events(void* start_event, void* stop_event);
+
+/* Test hook: the fused kernel's bounded wait for a team gives up after `polls` polls and
+ * reports SPEC_STATUS_TIMEOUT for the request (0 = give up at the first incomplete poll).
+ * Process-wide; the default is 262144. */
+int spec_set_spin_limit(unsigned polls);
 
 /* Human-readable text for a return code (negative) or a single status bit (positive). */
 const char* spec_status_string(int code);

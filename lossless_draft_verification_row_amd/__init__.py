@@ -28,6 +28,7 @@ STATUS = {
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
+_WS_CACHE = {}   # per-device zero-initialised workspace reused by calls that pass none
 
 
 class SamplingParams(ctypes.Structure):
@@ -69,6 +70,8 @@ def load_library():
                                          vp, vp, vp, vp, sz, vp]
     lib.spec_residual_sample_workspace_bytes.restype = sz
     lib.spec_residual_sample_workspace_bytes.argtypes = [i32, i32, i32, SamplingParams]
+    lib.spec_set_spin_limit.restype = i32
+    lib.spec_set_spin_limit.argtypes = [ctypes.c_uint]
     lib.spec_set_profile_events.restype = i32
     lib.spec_set_profile_events.argtypes = [vp, vp]
     lib.spec_status_string.restype = ctypes.c_char_p
@@ -115,7 +118,15 @@ def _sp(temperature, top_k, top_p):
     return SamplingParams(float(temperature), int(top_k), float(top_p))
 
 
+def new_workspace(nbytes, device="cuda"):
+    """A workspace for the library: zero-filled device bytes (the counter header must start at
+    zero; every completed call leaves it zero)."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
 def _workspace(nbytes, device, workspace):
+    """Caller's workspace, or a cached per-device one.  The cached workspace is shared by calls
+    on the same device, so calls that pass none must be ordered on one stream."""
     if nbytes == 0:
         return None, 0
     if workspace is not None:
@@ -123,9 +134,11 @@ def _workspace(nbytes, device, workspace):
             raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
                              f"{nbytes} needed")
         return workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    _workspace.keep = ws  # keep alive until the next call; torch's allocator orders reuse on the stream
-    return ws.data_ptr(), nbytes
+    cache = _WS_CACHE.get(device)
+    if cache is None or cache.numel() < nbytes:
+        cache = torch.zeros(nbytes, dtype=torch.uint8, device=device)   # zero once: counter header
+        _WS_CACHE[device] = cache
+    return cache.data_ptr(), cache.numel()
 
 
 def spec_verify_workspace_bytes(B, V, gamma_max, dtype, temperature, top_k=0, top_p=1.0) -> int:

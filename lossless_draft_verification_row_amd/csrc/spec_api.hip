@@ -1,7 +1,10 @@
 // spec_api.hip -- the C ABI of libspecverify: argument checks, workspace carving, launches.
 // Declarations and their documentation are in include/spec_verify.h.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <atomic>
 
 #include "spec_device.h"
 #include "spec_internal.h"
@@ -15,8 +18,15 @@ constexpr size_t kAlign = 256;
 
 // Benchmark instrumentation (spec_set_profile_events): process-wide, not thread-safe.
 hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+// Bound of the fused kernel's team wait, in polls (spec_set_spin_limit).
+unsigned g_spin_limit = 1u << 18;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool getenv_flag(const char* name) {
+  const char* v = getenv(name);
+  return v != nullptr && v[0] != '\0' && v[0] != '0';
+}
 
 int n_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
@@ -39,7 +49,7 @@ bool aligned16(const void* p, int64_t ld, spec_dtype dt) {
 
 struct Carve {
   char* base;
-  size_t off;
+  size_t off = kHeaderBytes;
   template <typename T>
   T* take(size_t bytes) {
     T* p = (T*)(base + off);
@@ -48,12 +58,34 @@ struct Carve {
   }
 };
 
-// Workspace of the dense path for n_slots slots (2 logical rows each).
+// Workspace of the multi-kernel path for n_slots slots (2 logical rows each), after the header.
 size_t dense_bytes(int64_t n_slots, int V) {
   const int64_t n_lr = 2 * n_slots;
   const int64_t ns = n_chunks(V);
-  return align_up((size_t)(n_lr * ns) * slice_part_bytes()) + align_up((size_t)n_lr * row_stat_bytes()) +
-         align_up((size_t)(n_slots * ns) * sizeof(double));
+  return kHeaderBytes + align_up((size_t)(n_lr * ns) * slice_part_bytes()) +
+         align_up((size_t)n_lr * row_stat_bytes()) + align_up((size_t)(n_slots * ns) * sizeof(double));
+}
+
+// Workspace of the fused path for n_teams target rows, after the header.
+size_t fused_bytes(int64_t n_teams, int V) {
+  const int64_t ns = n_chunks(V);
+  return kHeaderBytes + align_up((size_t)(n_teams * ns * 2) * fused_record_bytes()) +
+         align_up((size_t)(n_teams * ns) * sizeof(uint64_t));
+}
+
+// Tags of the fused kernel's workspace records: one per call, unique within the process,
+// never 0 (a zero-filled workspace holds no valid record).
+std::atomic<uint32_t> g_call_seq{0};
+uint32_t next_tag() {
+  uint32_t t;
+  do { t = g_call_seq.fetch_add(1, std::memory_order_relaxed) + 1; } while (t == 0);
+  return t;
+}
+
+// The fused single-kernel path covers these shapes; the rest takes the multi-kernel path.
+bool fused_ok(int B, int V, int gamma_max) {
+  return B <= kMaxReqFused && (int64_t)B * (gamma_max + 1) <= kMaxTeamsFused && n_chunks(V) <= kMaxSlicesFused &&
+         !getenv_flag("SPEC_VERIFY_NO_FUSED");
 }
 
 float exp2_scale(const spec_sampling_params& sp) {
@@ -82,6 +114,11 @@ const char* spec_status_string(int code) {
   }
 }
 
+int spec_set_spin_limit(unsigned polls) {
+  g_spin_limit = polls;
+  return SPEC_OK;
+}
+
 int spec_set_profile_events(void* start_event, void* stop_event) {
   if ((start_event == nullptr) != (stop_event == nullptr)) return SPEC_ERR_INVALID;
   g_prof_start = (hipEvent_t)start_event;
@@ -93,7 +130,9 @@ size_t spec_verify_workspace_bytes(int B, int V, int gamma_max, spec_dtype dt, s
   (void)dt;
   if (B <= 0 || V <= 0 || gamma_max < 0) return 0;
   if (filter_on(V, sp)) return 0;
-  return dense_bytes((int64_t)B * (gamma_max + 1), V);
+  const size_t dense = dense_bytes((int64_t)B * (gamma_max + 1), V);
+  const size_t fused = fused_bytes((int64_t)B * (gamma_max + 1), V);
+  return dense > fused ? dense : fused;
 }
 
 size_t spec_row_stats_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling_params sp) {
@@ -139,6 +178,7 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   const void* drf = greedy ? nullptr : draft_logits;
 
   RowMap map;
+  memset(&map, 0, sizeof(map));
   map.tgt = target_logits;
   map.tgt_ld = target_ld;
   map.drf = drf;
@@ -148,11 +188,60 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   map.G = gamma_max;
   map.n_draft_rows = n_draft_rows;
 
-  Carve cv{(char*)workspace, 0};
+  char* ws = (char*)workspace;
+  const int dtc = dt == SPEC_BF16 ? kDtBF16 : kDtF32;
+  const bool vec = aligned16(target_logits, target_ld, dt) && aligned16(drf, draft_ld, dt);
+  if (fused_ok(B, V, gamma_max)) {
+    FusedArgs f;
+    memset(&f, 0, sizeof(f));
+    f.tgt = target_logits;
+    f.tgt_ld = target_ld;
+    f.drf = drf;
+    f.drf_ld = draft_ld;
+    f.cu = cu_draft;
+    f.tokens = draft_tokens;
+    f.B = B;
+    f.G = gamma_max;
+    f.V = V;
+    f.n_s = ns;
+    f.n_draft_rows = n_draft_rows;
+    f.n_teams = n_draft_rows + B;
+    f.n_tickets = f.n_teams * ns;
+    f.mode = greedy ? kFuGreedy : (drf ? kFuSample : kFuTokenOnly);
+    f.want_t_ent = pos_stats.target_entropy_bits != nullptr;
+    f.spin_limit = g_spin_limit;
+    f.c = exp2_scale(sp);
+    f.seed = seed;
+    f.step = step;
+    f.tag = next_tag();
+    Carve cv{ws};
+    f.part = cv.take<uint64_t>((size_t)f.n_teams * ns * 2 * fused_record_bytes());
+    f.smass = cv.take<uint64_t>((size_t)f.n_teams * ns * sizeof(uint64_t));
+    f.out_tokens = out_tokens;
+    f.out_num_accepted = out_num_accepted;
+    f.out_req_stats = out_req_stats;
+    f.out_status = out_status;
+    f.st.p_y = pos_stats.p_y;
+    f.st.q_y = pos_stats.q_y;
+    f.st.one_minus_tv = pos_stats.one_minus_tv;
+    f.st.draft_entropy_bits = pos_stats.draft_entropy_bits;
+    f.st.draft_max_prob = pos_stats.draft_max_prob;
+    f.st.target_entropy_bits = pos_stats.target_entropy_bits;
+    f.st.target_max_prob = pos_stats.target_max_prob;
+    if (g_prof_start) hipEventRecord(g_prof_start, st);
+    const hipError_t e = launch_fused(f, dtc, vec, st);
+    if (g_prof_stop) hipEventRecord(g_prof_stop, st);
+    return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
+  }
+
+  int* cu_bad = (int*)(ws + kHdrCuBad);
+  if (launch_check_cu(cu_draft, B, gamma_max, n_draft_rows, cu_bad, st) != hipSuccess) return SPEC_ERR_LAUNCH;
+  map.cu_bad = cu_bad;
+  Carve cv{ws};
   DenseLaunch L;
   memset(&L, 0, sizeof(L));
   L.map = map;
-  L.dt = dt == SPEC_BF16 ? kDtBF16 : kDtF32;
+  L.dt = dtc;
   L.V = V;
   L.n_slices = ns;
   L.n_slots = n_slots;
@@ -160,7 +249,7 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   L.greedy = greedy;
   L.want_argmax = 0;
   L.pair = (!greedy && drf != nullptr) ? 1 : 0;
-  L.vec = aligned16(target_logits, target_ld, dt) && aligned16(drf, draft_ld, dt);
+  L.vec = vec;
   L.part = cv.take<SlicePart>((size_t)(2 * n_slots) * ns * slice_part_bytes());
   L.rs = cv.take<RowStat>((size_t)(2 * n_slots) * row_stat_bytes());
   L.smass = cv.take<double>((size_t)n_slots * ns * sizeof(double));
@@ -219,7 +308,7 @@ int spec_row_stats(int R, int V, spec_dtype dt, const void* logits, int64_t ld, 
   map.tgt = logits;
   map.tgt_ld = ld;
   map.B = R;
-  Carve cv{(char*)workspace, 0};
+  Carve cv{(char*)workspace};
   DenseLaunch L;
   memset(&L, 0, sizeof(L));
   L.map = map;
@@ -273,7 +362,7 @@ int spec_residual_sample(int R, int V, spec_dtype dt, const void* p_logits, int6
   map.drf = q_logits;
   map.drf_ld = q_ld;
   map.B = R;
-  Carve cv{(char*)workspace, 0};
+  Carve cv{(char*)workspace};
   DenseLaunch L;
   memset(&L, 0, sizeof(L));
   L.map = map;

@@ -19,6 +19,7 @@ constexpr int kStNonfinite = 1;
 constexpr int kStBadToken = 2;
 constexpr int kStZeroQ = 4;
 constexpr int kStResidualEmpty = 8;
+constexpr int kStTimeout = 16;
 constexpr int kStFilterOverflow = 32;
 constexpr int kStBadGamma = 64;
 
@@ -86,6 +87,62 @@ __device__ __forceinline__ void load_slice(const void* row, int V, int base, flo
   }
 }
 
+// Raw words of one thread's 16 logits of a slice (bf16 pairs or floats), so that the loads of
+// the next slice can be in flight while the current one is processed.
+template <int DT>
+struct RawSlice {
+  static constexpr int kWords = DT == kDtBF16 ? kPerThread / 2 : kPerThread;
+  uint32_t w[kWords];
+};
+
+// Issue the loads of this thread's 16 logits; indices >= V read as -inf.
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_raw(const void* row, int V, int base, RawSlice<DT>& r) {
+  const int t = threadIdx.x;
+  if constexpr (DT == kDtBF16) {
+    const uint16_t* p = (const uint16_t*)row;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e0 = base + 8 * (t + kThreads * k);
+      if (VEC && e0 + 8 <= V) {
+        const uint4 x = *(const uint4*)(p + e0);
+        r.w[4 * k + 0] = x.x; r.w[4 * k + 1] = x.y; r.w[4 * k + 2] = x.z; r.w[4 * k + 3] = x.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = (e0 + 2 * e < V) ? p[e0 + 2 * e] : 0xff80u;
+          const uint32_t hi = (e0 + 2 * e + 1 < V) ? p[e0 + 2 * e + 1] : 0xff80u;
+          r.w[4 * k + e] = lo | (hi << 16);
+        }
+      }
+    }
+  } else {
+    const float* p = (const float*)row;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e0 = base + 4 * (t + kThreads * k);
+      if (VEC && e0 + 4 <= V) {
+        const uint4 x = *(const uint4*)(p + e0);
+        r.w[4 * k + 0] = x.x; r.w[4 * k + 1] = x.y; r.w[4 * k + 2] = x.z; r.w[4 * k + 3] = x.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r.w[4 * k + e] = (e0 + e < V) ? __float_as_uint(p[e0 + e]) : 0xff800000u;
+      }
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack_raw(const RawSlice<DT>& r, float (&v)[kPerThread]) {
+  if constexpr (DT == kDtBF16) {
+#pragma unroll
+    for (int k = 0; k < kPerThread / 2; ++k) { v[2 * k] = bf16_lo(r.w[k]); v[2 * k + 1] = bf16_hi(r.w[k]); }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) v[k] = __uint_as_float(r.w[k]);
+  }
+}
+
 // ---------------------------------------------------------------- reductions (wave64)
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -112,6 +169,31 @@ __device__ __forceinline__ int wave_or(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
   return v;
+}
+
+// DPP wave reductions (gfx9 row broadcasts): the result is valid in lane 63 and is returned
+// to every lane through v_readlane.
+#define SPEC_DPP(old, v, ctrl, rmask) \
+  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, (old)), \
+                                                        __builtin_bit_cast(int, (v)), (ctrl), (rmask), 0xf, false))
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += SPEC_DPP(0.f, v, 0xb1, 0xf);   // quad_perm [1,0,3,2]
+  v += SPEC_DPP(0.f, v, 0x4e, 0xf);   // quad_perm [2,3,0,1]
+  v += SPEC_DPP(0.f, v, 0x124, 0xf);  // row_ror:4
+  v += SPEC_DPP(0.f, v, 0x128, 0xf);  // row_ror:8
+  v += SPEC_DPP(0.f, v, 0x142, 0xa);  // row_bcast:15
+  v += SPEC_DPP(0.f, v, 0x143, 0xc);  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  const float ninf = -INFINITY;
+  v = fmaxf(v, SPEC_DPP(ninf, v, 0xb1, 0xf));
+  v = fmaxf(v, SPEC_DPP(ninf, v, 0x4e, 0xf));
+  v = fmaxf(v, SPEC_DPP(ninf, v, 0x124, 0xf));
+  v = fmaxf(v, SPEC_DPP(ninf, v, 0x128, 0xf));
+  v = fmaxf(v, SPEC_DPP(ninf, v, 0x142, 0xa));
+  v = fmaxf(v, SPEC_DPP(ninf, v, 0x143, 0xc));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // Workgroup reductions; every thread gets the result.  `red` is 2*kWaves floats of LDS.
@@ -161,6 +243,26 @@ __device__ __forceinline__ double block_sum_d(double v, double* red) {
   return r;
 }
 
+// ---------------------------------------------------------------- light fp64 transcendentals
+
+// 2^x as a double with ~1.5e-7 relative error: the integer part is applied exactly with
+// ldexp, the fraction in [0, 1) goes through the hardware exp2.  Keeps fp64 library code
+// (and its registers) out of the kernels.  NaN propagates; x below -1074 gives 0.
+__device__ __forceinline__ double exp2_split(double x) {
+  if (!(x > -1074.0)) return (x != x) ? x : 0.0;
+  const double n = floor(x);
+  const float f = (float)(x - n);
+  return ldexp((double)__builtin_amdgcn_exp2f(f), (int)n);
+}
+
+// log2(z) for z > 0 with ~1e-7 absolute error: exact exponent plus the hardware log2 of the
+// mantissa in [0.5, 1).
+__device__ __forceinline__ double log2_split(double z) {
+  int e;
+  const double mant = frexp(z, &e);
+  return (double)e + (double)__builtin_amdgcn_logf((float)mant);
+}
+
 // ---------------------------------------------------------------- Philox4x64-10
 
 // Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds, each two 64x64 -> 128-bit
@@ -207,5 +309,91 @@ struct RowStat {
   int kept;       // kept tokens with a finite logit
   float tau;      // filter threshold (kept iff l >= tau); -inf when unfiltered
 };
+
+// Slice partial of the fused kernel: e = exp2(l c - ref) with ref = slice max * c.
+struct alignas(16) Part4 {
+  float ref;   // slice reference in base-2 units (greedy: the slice max logit)
+  float s;     // sum e
+  float w;     // sum e * (l c - ref), clamped below at -200 (entropy numerator)
+  int amax;    // greedy: lowest index of the slice maximum, -1 none, -2 NaN / +inf seen
+};
+
+// ---------------------------------------------------------------- cross-workgroup exchange
+//
+// Data shared between workgroups of one launch travel through relaxed agent-scope atomic
+// loads and stores (coherent "sc1" accesses that bypass the per-XCD L2), ordered against
+// the counters by waiting for their completion.  No acquire / release fence is used: on a
+// multi-XCD device those write back and invalidate the whole L2 at every use.
+__device__ __forceinline__ void st_coh(void* p, uint64_t v) {
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_coh(const void* p) {
+  return __hip_atomic_load((uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every vector memory access issued so far has completed (s_waitcnt vmcnt(0)).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ unsigned ctr_add(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned ctr_load(const unsigned* p) {
+  return __hip_atomic_load((unsigned*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t pack2(float a, float b) {
+  return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+}
+__device__ __forceinline__ uint64_t pack2(float a, int b) {
+  return (uint64_t)__float_as_uint(a) | ((uint64_t)(uint32_t)b << 32);
+}
+__device__ __forceinline__ uint64_t pack2(int a, int b) {
+  return (uint64_t)(uint32_t)a | ((uint64_t)(uint32_t)b << 32);
+}
+__device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float((uint32_t)v); }
+__device__ __forceinline__ float hi_f(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
+__device__ __forceinline__ int lo_i(uint64_t v) { return (int)(uint32_t)v; }
+__device__ __forceinline__ int hi_i(uint64_t v) { return (int)(uint32_t)(v >> 32); }
+
+constexpr int kTeamBadP = 1;
+constexpr int kTeamBadQ = 2;
+
+// Statistics of one team (a target row and, for a paired position, its draft row).
+struct TeamStat {
+  double z[2];    // sum over the row of exp2(l c - M)
+  double beta;    // sum_x [p - q]_+ of a paired position
+  float M[2];     // row reference in base-2 units (greedy: the max logit)
+  float h[2];     // entropy in bits
+  int amax;       // greedy: argmax of the target row
+  int flags;      // kTeamBadP / kTeamBadQ: a row with NaN / +inf or without a finite logit
+};
+
+__device__ __forceinline__ void store_part(Part4* p, const Part4& v) {
+  st_coh(p, pack2(v.ref, v.s));
+  st_coh((char*)p + 8, pack2(v.w, v.amax));
+}
+__device__ __forceinline__ Part4 load_part(const Part4* p) {
+  const uint64_t a = ld_coh(p), b = ld_coh((const char*)p + 8);
+  Part4 v;
+  v.ref = lo_f(a); v.s = hi_f(a); v.w = lo_f(b); v.amax = hi_i(b);
+  return v;
+}
+__device__ __forceinline__ void store_double(double* p, double v) { st_coh(p, (uint64_t)__double_as_longlong(v)); }
+__device__ __forceinline__ double load_double(const double* p) { return __longlong_as_double((long long)ld_coh(p)); }
+__device__ __forceinline__ void store_team(TeamStat* p, const TeamStat& v) {
+  st_coh(&p->z[0], (uint64_t)__double_as_longlong(v.z[0]));
+  st_coh(&p->z[1], (uint64_t)__double_as_longlong(v.z[1]));
+  st_coh(&p->beta, (uint64_t)__double_as_longlong(v.beta));
+  st_coh(&p->M[0], pack2(v.M[0], v.M[1]));
+  st_coh(&p->h[0], pack2(v.h[0], v.h[1]));
+  st_coh(&p->amax, pack2(v.amax, v.flags));
+}
+__device__ __forceinline__ TeamStat load_team(const TeamStat* p) {
+  TeamStat v;
+  v.z[0] = __longlong_as_double((long long)ld_coh(&p->z[0]));
+  v.z[1] = __longlong_as_double((long long)ld_coh(&p->z[1]));
+  v.beta = __longlong_as_double((long long)ld_coh(&p->beta));
+  uint64_t m = ld_coh(&p->M[0]), h = ld_coh(&p->h[0]), ai = ld_coh(&p->amax);
+  v.M[0] = lo_f(m); v.M[1] = hi_f(m); v.h[0] = lo_f(h); v.h[1] = hi_f(h);
+  v.amax = lo_i(ai); v.flags = hi_i(ai);
+  return v;
+}
 
 }  // namespace specv

@@ -12,6 +12,18 @@ constexpr int kModeArgmax = 1;
 constexpr int kMaxChunks = 512;   // V <= 512 * 4096 logits
 constexpr int kMaxGamma = 64;     // gamma_max bound (one finalize thread per position)
 
+// fused single-kernel path limits (larger problems take the multi-kernel path)
+constexpr int kMaxSlicesFused = 64;    // V <= 64 * 4096
+constexpr int kMaxTeamsFused = 4096;   // target rows
+constexpr int kMaxReqFused = 1024;     // requests
+constexpr int kFuSample = 0;           // draft logits, temperature > 0
+constexpr int kFuTokenOnly = 1;        // token-only draft, temperature > 0
+constexpr int kFuGreedy = 2;           // temperature 0
+
+// Header at the start of every workspace (the multi-kernel path's offset-check flag).
+constexpr size_t kHeaderBytes = 256;
+constexpr size_t kHdrCuBad = 0;                                     // i32
+
 // How a logical row index maps onto the caller's arrays (see resolve_row).
 struct RowMap {
   const void* tgt;
@@ -22,6 +34,7 @@ struct RowMap {
   int B;                    // requests, or rows in plain-row mode
   int G;                    // gamma_max (request mode)
   int n_draft_rows;         // cu[B] as stated by the caller (request mode)
+  const int* cu_bad;        // request mode: set when cu is not a valid exclusive prefix
 };
 
 // spec_row_stats outputs written by the combine kernel (plain-row mode).
@@ -37,6 +50,8 @@ struct RowStatsOut {
 
 struct SlicePart;
 struct RowStat;
+struct Part4;
+struct TeamStat;
 
 struct DenseLaunch {
   RowMap map;
@@ -89,6 +104,32 @@ struct ResidualArgs {
   double* out_mass;
   int32_t* out_status;
 };
+
+struct FusedArgs {
+  const void* tgt;
+  int64_t tgt_ld;
+  const void* drf;
+  int64_t drf_ld;
+  const int32_t* cu;
+  const int32_t* tokens;
+  int B, G, V, n_s, n_draft_rows, n_teams, n_tickets, mode, want_t_ent;
+  int n_fin;            // finalizer workgroups (set at launch)
+  unsigned spin_limit;
+  uint32_t tag;         // this call's record tag (never 0)
+  float c;
+  uint64_t seed, step;
+  uint64_t* part;       // [n_teams][n_s][2 rows][3 words] tagged slice records
+  uint64_t* smass;      // [n_teams][n_s] tagged residual masses
+  int32_t* out_tokens;
+  int32_t* out_num_accepted;
+  float* out_req_stats;
+  int32_t* out_status;
+  PosStatsOut st;
+};
+
+hipError_t launch_fused(const FusedArgs& a, int dt, int vec, hipStream_t st);
+hipError_t launch_check_cu(const int32_t* cu, int B, int G, int n_draft_rows, int* cu_bad, hipStream_t st);
+size_t fused_record_bytes();
 
 hipError_t launch_dense(const DenseLaunch& L, hipStream_t st);
 hipError_t launch_finalize(const FinalizeArgs& a, int dt, hipStream_t st);

@@ -23,11 +23,33 @@ namespace specv {
 
 // ---------------------------------------------------------------- row addressing
 
+// Request b's rows.  The offsets were checked as one exclusive prefix before any kernel
+// reads a row (k_check_cu); if that check failed every request is reported, none is read.
 __device__ __forceinline__ bool request_rows(const RowMap& m, int b, int& g, int& c0) {
+  if (*m.cu_bad) return false;
   c0 = m.cu[b];
   const int c1 = m.cu[b + 1];
   g = c1 - c0;
   return c0 >= 0 && g >= 0 && g <= m.G && c1 <= m.n_draft_rows;
+}
+
+// cu must be an exclusive prefix: cu[0] = 0, 0 <= cu[b+1] - cu[b] <= G, cu[B] = n_draft_rows.
+__global__ __launch_bounds__(kThreads) void k_check_cu(const int32_t* __restrict__ cu, int B, int G,
+                                                        int n_draft_rows, int* cu_bad) {
+  __shared__ int red[kWaves];
+  int bad = 0;
+  for (int b = threadIdx.x; b < B; b += kThreads) {
+    const int g = cu[b + 1] - cu[b];
+    if (g < 0 || g > G) bad = 1;
+  }
+  if (threadIdx.x == 0 && (cu[0] != 0 || cu[B] != n_draft_rows)) bad = 1;
+  bad = block_or(bad, red);
+  if (threadIdx.x == 0) *cu_bad = bad;
+}
+
+hipError_t launch_check_cu(const int32_t* cu, int B, int G, int n_draft_rows, int* cu_bad, hipStream_t st) {
+  hipLaunchKernelGGL(k_check_cu, dim3(1), dim3(kThreads), 0, st, cu, B, G, n_draft_rows, cu_bad);
+  return hipGetLastError();
 }
 
 // Logical row lr = 2 * slot + kind (kind 0: target / p row, 1: draft / q row).  In request

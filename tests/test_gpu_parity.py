@@ -5,6 +5,7 @@ loads, partial chunks, ragged draft lengths) is exercised, while the oracle stil
 seconds.  The comparison rule is in tests/harness.py.
 """
 import math
+import os
 import sys
 
 import numpy as np
@@ -59,19 +60,40 @@ def custom_inputs(B, V, gammas, dtype="bf16", sigma=3.0, tau=1.0, T=1.0, seed=7,
     return W.Inputs(wl, gammas, cu, target, None if token_only else draft, toks.astype(np.int32), seed)
 
 
-def run_gpu(inp, sp, seed, step, gamma_max=None):
+class path_env:
+    """Select the single-kernel (fused) or the multi-kernel path of spec_verify_batch."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        self.old = os.environ.get("SPEC_VERIFY_NO_FUSED")
+        if self.path == "multi":
+            os.environ["SPEC_VERIFY_NO_FUSED"] = "1"
+        else:
+            os.environ.pop("SPEC_VERIFY_NO_FUSED", None)
+
+    def __exit__(self, *exc):
+        if self.old is None:
+            os.environ.pop("SPEC_VERIFY_NO_FUSED", None)
+        else:
+            os.environ["SPEC_VERIFY_NO_FUSED"] = self.old
+
+
+def run_gpu(inp, sp, seed, step, gamma_max=None, path="fused"):
     d = H.to_device(inp)
     G = int(inp.gammas.max()) if gamma_max is None else gamma_max
-    res = L.spec_verify_batch(d["target"], d["draft"], d["tokens"], d["cu"], G,
-                              temperature=sp.temperature, top_k=sp.top_k, top_p=sp.top_p, seed=seed, step=step)
-    torch.cuda.synchronize()
+    with path_env(path):
+        res = L.spec_verify_batch(d["target"], d["draft"], d["tokens"], d["cu"], G,
+                                  temperature=sp.temperature, top_k=sp.top_k, top_p=sp.top_p, seed=seed, step=step)
+        torch.cuda.synchronize()
     return H.gpu_to_numpy(res)
 
 
-def check(inp, sp, seed=1234, step=5, requests=None, gamma_max=None):
+def check(inp, sp, seed=1234, step=5, requests=None, gamma_max=None, path="fused"):
     note(f"case B={len(inp.gammas)} V={inp.target.shape[1]} dtype={inp.wl.dtype} T={sp.temperature} "
-         f"k={sp.top_k} p={sp.top_p} token_only={inp.draft is None}")
-    gpu = run_gpu(inp, sp, seed, step, gamma_max)
+         f"k={sp.top_k} p={sp.top_p} token_only={inp.draft is None} path={path}")
+    gpu = run_gpu(inp, sp, seed, step, gamma_max, path)
     reqs = range(len(inp.gammas)) if requests is None else requests
     refs = H.oracle_requests(inp, sp, seed, step, reqs)
     rep = H.compare_requests(gpu, refs, inp, H.Report())
@@ -83,27 +105,34 @@ def check(inp, sp, seed=1234, step=5, requests=None, gamma_max=None):
 # ----------------------------------------------------------------------------- dense sampling
 
 
+PATHS = ["fused", "multi"]
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("V", [4096 * 3 + 72, 8192, 4097, 1000])
-def test_dense_bf16_ragged(V):
+def test_dense_bf16_ragged(V, path):
     inp = custom_inputs(7, V, [0, 1, 3, 5, 2, 7, 4], T=1.0, seed=V)
-    check(inp, O.SamplingParams(1.0))
+    check(inp, O.SamplingParams(1.0), path=path)
 
 
-def test_dense_bf16_temperature():
+@pytest.mark.parametrize("path", PATHS)
+def test_dense_bf16_temperature(path):
     inp = custom_inputs(6, 3 * 4096 + 300, [2, 4, 6, 8, 1, 3], tau=1.5, T=0.7, seed=3)
-    check(inp, O.SamplingParams(0.7))
+    check(inp, O.SamplingParams(0.7), path=path)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("V", [8, 3000, 4096 * 2 + 5])
-def test_dense_fp32(V):
+def test_dense_fp32(V, path):
     inp = custom_inputs(5, V, [4, 0, 2, 3, 1], dtype="f32", sigma=2.0, tau=1.0, T=1.3, seed=V + 1)
-    check(inp, O.SamplingParams(1.3))
+    check(inp, O.SamplingParams(1.3), path=path)
 
 
-def test_unaligned_rows_take_the_scalar_path():
+@pytest.mark.parametrize("path", PATHS)
+def test_unaligned_rows_take_the_scalar_path(path):
     """bf16 rows with an odd stride (not a 16-byte multiple): same results as the oracle."""
     inp = custom_inputs(4, 4099, [3, 2, 0, 4], seed=11)
-    check(inp, O.SamplingParams(1.0))
+    check(inp, O.SamplingParams(1.0), path=path)
 
 
 def test_worked_example_v3():
@@ -130,8 +159,9 @@ def test_worked_example_v3():
 # ----------------------------------------------------------------------------- greedy / token-only
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("V", [4096 * 3 + 72, 4096 + 77, 1000])
-def test_greedy(V):
+def test_greedy(V, path):
     inp = custom_inputs(9, V, [7, 7, 0, 3, 7, 1, 7, 5, 2], T=0.0, seed=V + 2, token_only=True)
     # make about half of the draft tokens the target argmax so long accepted prefixes occur
     tv = W.bf16_bits_to_f32(inp.target)
@@ -140,18 +170,19 @@ def test_greedy(V):
         for i in range(int(inp.gammas[b])):
             if rng.random() < 0.7:
                 inp.tokens[inp.cu_draft[b] + i] = int(np.argmax(tv[inp.cu_draft[b] + b + i]))
-    gpu, refs, rep = check(inp, O.SamplingParams(0.0))
+    gpu, refs, rep = check(inp, O.SamplingParams(0.0), path=path)
     assert gpu["num_accepted"].max() >= 3
 
 
-def test_token_only_stochastic():
+@pytest.mark.parametrize("path", PATHS)
+def test_token_only_stochastic(path):
     inp = custom_inputs(6, 2 * 4096 + 11, [1, 3, 0, 5, 2, 4], T=1.0, seed=21, token_only=True)
     rng = np.random.default_rng(2)
     tv = W.bf16_bits_to_f32(inp.target)
     for b in range(6):
         for i in range(int(inp.gammas[b])):
             inp.tokens[inp.cu_draft[b] + i] = int(np.argmax(tv[inp.cu_draft[b] + b + i] + rng.gumbel(size=tv.shape[1])))
-    check(inp, O.SamplingParams(1.0))
+    check(inp, O.SamplingParams(1.0), path=path)
 
 
 # ----------------------------------------------------------------------------- edge cases
@@ -168,7 +199,8 @@ def test_draft_equals_target_always_accepts():
     np.testing.assert_allclose(gpu["one_minus_tv"], 1.0, atol=2e-6)
 
 
-def test_error_statuses_on_gpu():
+@pytest.mark.parametrize("path", PATHS)
+def test_error_statuses_on_gpu(path):
     """NaN / +inf rows, -inf masked logits, out-of-range tokens, q(y) = 0, gamma 0."""
     inp = custom_inputs(8, 4096 + 100, [2, 2, 2, 2, 2, 0, 3, 2], seed=13)
     bf = lambda x: int(W.bf16_bits_from_f32(np.array([x], np.float32))[0])
@@ -181,22 +213,59 @@ def test_error_statuses_on_gpu():
     inp.target[cu[4] + 4 + 0, :300] = bf(-np.inf)            # request 4: masked logits
     inp.draft[cu[4] + 0, 100:200] = bf(-np.inf)
     inp.tokens[cu[6] + 1] = -5                               # request 6: negative token
-    gpu, refs, _ = check(inp, O.SamplingParams(1.0))
+    gpu, refs, _ = check(inp, O.SamplingParams(1.0), path=path)
     assert gpu["status"][0] & L.STATUS["NONFINITE"] and gpu["status"][1] & L.STATUS["NONFINITE"]
     assert gpu["status"][2] & L.STATUS["BAD_TOKEN"] and gpu["status"][3] & L.STATUS["ZERO_Q"]
     assert gpu["num_accepted"][5] == 0 and gpu["tokens"][5, 0] >= 0
 
 
-def test_bad_offsets_are_reported_not_read():
+@pytest.mark.parametrize("path", PATHS)
+def test_bad_offsets_are_reported_not_read(path):
+    """Offsets that are not an exclusive prefix: every request reports BAD_GAMMA, none is read."""
     inp = custom_inputs(3, 2000, [2, 3, 1], seed=17)
     d = H.to_device(inp)
-    cu = torch.tensor([0, 2, 9, 6], dtype=torch.int32, device=DEV)  # request 1 claims 7 > gamma_max
-    res = L.spec_verify_batch(d["target"], d["draft"], d["tokens"], cu, 3, temperature=1.0, seed=1)
-    torch.cuda.synchronize()
-    st = res["status"].cpu().numpy()
-    assert st[1] == L.STATUS["BAD_GAMMA"] and st[2] == L.STATUS["BAD_GAMMA"]
-    assert st[0] & L.STATUS["BAD_GAMMA"] == 0
-    assert (res["tokens"][1:].cpu().numpy() == -1).all()
+    for cu_bad in ([0, 2, 9, 6], [1, 3, 6, 7], [0, 2, 5, 5]):   # gamma > max, cu[0] != 0, cu[B] != rows
+        cu = torch.tensor(cu_bad, dtype=torch.int32, device=DEV)
+        with path_env(path):
+            res = L.spec_verify_batch(d["target"], d["draft"], d["tokens"], cu, 3, temperature=1.0, seed=1)
+            torch.cuda.synchronize()
+        st = res["status"].cpu().numpy()
+        assert (st == L.STATUS["BAD_GAMMA"]).all(), (cu_bad, st)
+        assert (res["tokens"].cpu().numpy() == -1).all()
+        assert (res["num_accepted"].cpu().numpy() == 0).all()
+    # a valid call right after still verifies correctly (the counters were left clean)
+    check(inp, O.SamplingParams(1.0), path=path)
+
+
+def test_forced_timeout_then_clean_call():
+    """A zero wait bound forces the team wait to give up: the affected requests report TIMEOUT
+    with no tokens, the others still match the oracle, and the next call is exact again."""
+    inp = custom_inputs(6, 6 * 4096 + 10, [5, 4, 3, 5, 2, 6], seed=29)
+    sp = O.SamplingParams(1.0)
+    lib = L.load_library()
+    lib.spec_set_spin_limit(0)
+    try:
+        gpu = run_gpu(inp, sp, 5, 6)
+    finally:
+        lib.spec_set_spin_limit(1 << 18)
+    refs = H.oracle_requests(inp, sp, 5, 6, range(6))
+    timed = (gpu["status"] & L.STATUS["TIMEOUT"]) != 0
+    note(f"timed-out requests: {np.nonzero(timed)[0].tolist()}")
+    assert (gpu["tokens"][timed] == -1).all() and (gpu["num_accepted"][timed] == 0).all()
+    keep = {b: refs[b] for b in range(6) if not timed[b]}
+    rep = H.compare_requests(gpu, keep, inp, H.Report(), stats=False)
+    assert rep.ok(), rep
+    check(inp, sp, seed=5, step=6)
+
+
+def test_repeated_calls_identical():
+    """Back-to-back calls on one workspace give bitwise equal outputs (counters reset)."""
+    inp = custom_inputs(5, 3 * 4096 + 8, [7, 7, 7, 7, 7], seed=37)
+    sp = O.SamplingParams(1.0)
+    outs = [run_gpu(inp, sp, 9, 9) for _ in range(3)]
+    for o in outs[1:]:
+        for k in o:
+            assert np.array_equal(o[k], outs[0][k], equal_nan=True), k
 
 
 def test_all_equal_logits():
