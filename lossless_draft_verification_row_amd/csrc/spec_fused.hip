@@ -67,6 +67,17 @@ struct Lds {
   float red[8 * kWaves];
   float f[8];
   int i[8];
+  // one buffer per reduction of a ticket, so that consecutive reductions need no protecting
+  // barrier between them
+  float wp[2][kWaves][3];   // per-wave {ref, sum e, sum e t} of the target and draft rows
+  float rres[kWaves];
+  float cmb[4];
+  int cst;
+};
+
+struct LdsFin {
+  int cu[kMaxReqFused + 1];
+  int i[8];
   FinScratch fin;
 };
 
@@ -77,19 +88,43 @@ __device__ __forceinline__ uint64_t tagged(float v, uint32_t tag) {
 }
 __device__ __forceinline__ uint32_t tag_of(uint64_t w) { return (uint32_t)(w >> 32); }
 
-// slice record of one row: 3 words {ref|tag}, {s|tag}, {w|tag}
-__device__ __forceinline__ uint64_t* rec_ptr(uint64_t* part, int n_s, int r, int s, int row) {
-  return part + (((int64_t)r * n_s + s) * 2 + row) * 3;
+// Slice records: 16 bytes {ref, sum e, sum e t, check}, stored and loaded whole through a
+// buffer resource over the record array with agent-scope coherence (sc1).  check = tag ^
+// mix(ref, s, w): a reader accepts a record only if the check matches this call's tag, so a
+// record of an earlier call, or one read while it was being written, is never taken.
+// Layout: [team][row: 0 target, 1 draft][slice].
+__device__ __forceinline__ uint32_t rec_mix(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t h = a * 0x9E3779B1u;
+  h ^= ((b << 11) | (b >> 21)) * 0x85EBCA77u;
+  h ^= ((c << 22) | (c >> 10)) * 0xC2B2AE3Du;
+  return h ^ (h >> 15);
 }
-__device__ __forceinline__ void store_rec(uint64_t* p, float ref, float s, float w, uint32_t tag) {
-  st_coh(p, tagged(ref, tag));
-  st_coh(p + 1, tagged(s, tag));
-  st_coh(p + 2, tagged(w, tag));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const FusedArgs& a) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)a.part, (short)0, (int)((size_t)a.n_teams * 2 * a.n_s * 16),
+                                           0x00020000);
 }
-__device__ __forceinline__ bool load_rec(const uint64_t* p, uint32_t tag, float& ref, float& s, float& w) {
-  const uint64_t a = ld_coh(p), b = ld_coh(p + 1), c = ld_coh(p + 2);
-  ref = lo_f(a); s = lo_f(b); w = lo_f(c);
-  return tag_of(a) == tag && tag_of(b) == tag && tag_of(c) == tag;
+__device__ __forceinline__ uint32_t rec_off(int n_s, int r, int s, int row) {
+  return (uint32_t)(((r * 2 + row) * n_s + s) * 16);
+}
+__device__ __forceinline__ void store_rec(__amdgpu_buffer_rsrc_t rs, uint32_t off, float ref, float s, float w,
+                                          uint32_t tag) {
+  const uint32_t x = __float_as_uint(ref), y = __float_as_uint(s), z = __float_as_uint(w);
+  const __attribute__((ext_vector_type(4))) uint32_t v = {x, y, z, tag ^ rec_mix(x, y, z)};
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0x10);
+}
+struct Rec {
+  uint32_t x, y, z, c;
+};
+__device__ __forceinline__ Rec load_rec_raw(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0x10);
+  return Rec{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ bool rec_ok(const Rec& q, uint32_t tag) { return (q.c ^ rec_mix(q.x, q.y, q.z)) == tag; }
+__device__ __forceinline__ bool load_rec(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t tag, float& ref, float& s,
+                                         float& w) {
+  const Rec q = load_rec_raw(rs, off);
+  ref = __uint_as_float(q.x); s = __uint_as_float(q.y); w = __uint_as_float(q.z);
+  return rec_ok(q, tag);
 }
 
 __device__ __forceinline__ bool wave_all(bool v) { return __ballot(!v) == 0ull; }
@@ -196,7 +231,7 @@ __device__ __forceinline__ void load_run16(const void* row, int V, int x0, float
 }
 
 template <int DT, bool VEC, int MODE>
-__device__ void finalize_request(const FusedArgs& a, Lds& L, int b) {
+__device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   FinScratch& F = L.fin;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int c0 = L.cu[b], g = L.cu[b + 1] - c0;
@@ -205,6 +240,7 @@ __device__ void finalize_request(const FusedArgs& a, Lds& L, int b) {
   const uint32_t tag = a.tag;
   const float nan = __int_as_float(0x7fc00000);
   const double cd = (double)a.c;
+  const __amdgpu_buffer_rsrc_t rrs = rec_rsrc(a);
   if (t == 0) { F.flags = 0; F.status = 0; }
   // the draft tokens and their logits do not depend on any record: fetch them first
   float ly_p = 0.f, ly_q = 0.f;
@@ -227,9 +263,9 @@ __device__ void finalize_request(const FusedArgs& a, Lds& L, int b) {
     for (unsigned spins = 0;; ++spins) {
       bool ok = true;
       if (in) {
-        ok = load_rec(rec_ptr(a.part, n_s, r, lane, 0), tag, pr, ps, pw);
+        ok = load_rec(rrs, rec_off(n_s, r, lane, 0), tag, pr, ps, pw);
         if (pair) {
-          ok = load_rec(rec_ptr(a.part, n_s, r, lane, 1), tag, qr, qs, qw) && ok;
+          ok = load_rec(rrs, rec_off(n_s, r, lane, 1), tag, qr, qs, qw) && ok;
           const uint64_t m = ld_coh(a.smass + (int64_t)r * n_s + lane);
           sm = lo_f(m);
           ok = ok && tag_of(m) == tag;
@@ -395,7 +431,7 @@ __device__ void finalize_request(const FusedArgs& a, Lds& L, int b) {
             m = (double)lo_f(ld_coh(a.smass + (int64_t)r * n_s + k));
           } else {
             float ref, s, w;
-            load_rec(rec_ptr(a.part, n_s, r, k, 0), tag, ref, s, w);
+            load_rec(rrs, rec_off(n_s, r, k, 0), tag, ref, s, w);
             m = s > 0.f ? (double)s * exp2_split((double)ref - (double)T.M[0]) / T.z[0] : 0.0;
             if (wkind == 2) {
               const int y = F.y;
@@ -434,10 +470,10 @@ __device__ void finalize_request(const FusedArgs& a, Lds& L, int b) {
       // only) or max(e_p * r - e_q, 0) with r = alpha_p / alpha_q, exactly as streamed.
       const int wkind = F.wkind;
       float refp, sp_, wp_, refq = 0.f, rr = 0.f;
-      load_rec(rec_ptr(a.part, n_s, r, k, 0), tag, refp, sp_, wp_);
+      load_rec(rrs, rec_off(n_s, r, k, 0), tag, refp, sp_, wp_);
       if (wkind == 1) {
         float sq_, wq_;
-        load_rec(rec_ptr(a.part, n_s, r, k, 1), tag, refq, sq_, wq_);
+        load_rec(rrs, rec_off(n_s, r, k, 1), tag, refq, sq_, wq_);
         const double alp = exp2_split((double)refp - (double)T.M[0]) / T.z[0];
         const double alq = exp2_split((double)refq - (double)T.M[1]) / T.z[1];
         rr = (float)(alp / alq);
@@ -533,19 +569,94 @@ __device__ void finalize_request(const FusedArgs& a, Lds& L, int b) {
 
 // ---------------------------------------------------------------- streaming phases
 
-// Per-workgroup decode of a ticket.
+// One ticket; every field is uniform over the workgroup.
 struct Ticket {
   int r, s, b, c0, g, i;
   bool pair;
 };
 
-// Phase 1 of a ticket: slice maxima, e = exp2(l c - ref) in place, sums, records published.
+// The lane that publishes a workgroup's records: lane 0 of the last wave.  Wave 0 polls the
+// team records; keeping every store out of wave 0 means that, in wave 0, only the ticket loads
+// issued after a poll stand between the poll and its use (vector memory counters retire in
+// issue order).
+constexpr int kStorer = kThreads - 64;
+
+// 64-bit DPP move of both halves (rows outside RMASK read 0).
+template <int CTRL, int RMASK>
+__device__ __forceinline__ double dpp_d(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, RMASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, RMASK, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+// fp64 sum over the wave in a fixed order (row reductions, then row broadcasts); every lane
+// gets lane 63's total.
+__device__ __forceinline__ double wave_sum_dpp_d(double v) {
+  v += dpp_d<0xb1, 0xf>(v);
+  v += dpp_d<0x4e, 0xf>(v);
+  v += dpp_d<0x124, 0xf>(v);
+  v += dpp_d<0x128, 0xf>(v);
+  v += dpp_d<0x142, 0xa>(v);
+  v += dpp_d<0x143, 0xc>(v);
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, 63), hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Bounds-checked row loads: a buffer resource over the row's bytes.  16-byte loads past the
+// end return zeros and touch no memory (num_records 0 turns every load off).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, nbytes, 0x00020000);
+}
+template <int DT>
+__device__ __forceinline__ void load_raw_buf(__amdgpu_buffer_rsrc_t rs, int base, RawSlice<DT>& r) {
+  const int t = threadIdx.x;
+  constexpr int kEl = DT == kDtBF16 ? 8 : 4;      // elements per 16-byte vector
+  constexpr int kEsz = DT == kDtBF16 ? 2 : 4;
+#pragma unroll
+  for (int k = 0; k < kPerThread / kEl; ++k) {
+    const int e0 = base + kEl * (t + kThreads * k);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, e0 * kEsz, 0, 0);
+    r.w[4 * k + 0] = x[0]; r.w[4 * k + 1] = x[1]; r.w[4 * k + 2] = x[2]; r.w[4 * k + 3] = x[3];
+  }
+}
+// Logits at indices >= V (zeros from the bounds check) become -inf.
+template <int DT>
+__device__ __forceinline__ void mask_tail(int V, int base, float (&v)[kPerThread]) {
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    if (slice_index<DT>(base, threadIdx.x, j) >= V) v[j] = -INFINITY;
+}
+
+// Fold per-wave partials {ref_w, s_w, w_w} of one row's slice (ref_w = -inf for a wave that
+// holds no finite logit) into one record relative to ref = max_w ref_w:
+// s = sum_w s_w 2^(ref_w - ref), w = sum_w 2^(ref_w - ref) (w_w + s_w (ref_w - ref)).
+__device__ __forceinline__ void fold_waves(const float (*pw)[3], float& ref, float& s, float& w) {
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) M = fmaxf(M, pw[k][0]);
+  ref = 0.f; s = 0.f; w = 0.f;
+  if (!(M > -INFINITY)) return;
+  ref = M;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    if (!(pw[k][0] > -INFINITY)) continue;
+    const float d = pw[k][0] - M;
+    const float f = __builtin_amdgcn_exp2f(d);
+    s = fmaf(pw[k][1], f, s);
+    w = fmaf(f, fmaf(pw[k][1], d, pw[k][2]), w);
+  }
+}
+
+// Phase 1 of a ticket: per-wave maxima, e = exp2(l c - ref_w) in place, sums, one record per
+// row.  Returns each wave's references (0 for a wave with no finite logit).
 template <int DT, int MODE>
 __device__ __forceinline__ void phase1(const FusedArgs& a, Lds& L, const Ticket& T, float (&vp)[kPerThread],
                                        float (&vq)[kPerThread], float& refp, float& refq) {
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const uint32_t tag = a.tag;
   const int base = T.s * kChunk;
+  const __amdgpu_buffer_rsrc_t rrs = rec_rsrc(a);
   if (MODE == kFuGreedy) {
     float mv[1];
     mv[0] = vp[0];
@@ -564,23 +675,22 @@ __device__ __forceinline__ void phase1(const FusedArgs& a, Lds& L, const Ticket&
     __syncthreads();
     idx = block_min_i(idx, L.i);
     badv = block_or(badv, L.i);
-    if (t == 0)
-      store_rec(rec_ptr(a.part, a.n_s, T.r, T.s, 0), mv[0],
-                __int_as_float(badv ? -2 : (idx == INT_MAX ? -1 : idx)), 0.f, tag);
+    if (t == kStorer)
+      store_rec(rrs, rec_off(a.n_s, T.r, T.s, 0), mv[0], __int_as_float(badv ? -2 : (idx == INT_MAX ? -1 : idx)),
+                0.f, tag);
     return;
   }
-  float mv[2];
-  mv[0] = vp[0];
-  mv[1] = T.pair ? vq[0] : -INFINITY;
+  float mp = vp[0], mq = T.pair ? vq[0] : -INFINITY;
 #pragma unroll
-  for (int j = 1; j < kPerThread; ++j) mv[0] = fmaxf(mv[0], vp[j]);
+  for (int j = 1; j < kPerThread; ++j) mp = fmaxf(mp, vp[j]);
   if (T.pair) {
 #pragma unroll
-    for (int j = 1; j < kPerThread; ++j) mv[1] = fmaxf(mv[1], vq[j]);
+    for (int j = 1; j < kPerThread; ++j) mq = fmaxf(mq, vq[j]);
   }
-  block_max_f<2>(mv, L.red);
-  refp = mv[0] > -INFINITY ? mv[0] * a.c : 0.f;
-  refq = mv[1] > -INFINITY ? mv[1] * a.c : 0.f;
+  mp = wave_max_dpp(mp);
+  if (T.pair) mq = wave_max_dpp(mq);
+  refp = mp > -INFINITY ? mp * a.c : 0.f;
+  refq = mq > -INFINITY ? mq * a.c : 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   if (a.want_t_ent) {
 #pragma unroll
@@ -609,155 +719,209 @@ __device__ __forceinline__ void phase1(const FusedArgs& a, Lds& L, const Ticket&
       vq[j] = e;
     }
   }
-  __syncthreads();
-  block_sum_f<4>(acc, L.red);
-  if (t == 0) {
-    store_rec(rec_ptr(a.part, a.n_s, T.r, T.s, 0), refp, acc[0], acc[1], tag);
-    if (T.pair) store_rec(rec_ptr(a.part, a.n_s, T.r, T.s, 1), refq, acc[2], acc[3], tag);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc[k] = wave_sum_dpp(acc[k]);
+  if (lane == 0) {
+    L.wp[0][wave][0] = mp > -INFINITY ? refp : -INFINITY;
+    L.wp[0][wave][1] = acc[0];
+    L.wp[0][wave][2] = acc[1];
+    L.wp[1][wave][0] = mq > -INFINITY ? refq : -INFINITY;
+    L.wp[1][wave][1] = acc[2];
+    L.wp[1][wave][2] = acc[3];
   }
   __syncthreads();
+  if (t == kStorer) {
+    float ref, sm, wm;
+    fold_waves(L.wp[0], ref, sm, wm);
+    store_rec(rrs, rec_off(a.n_s, T.r, T.s, 0), ref, sm, wm, tag);
+    if (T.pair) {
+      fold_waves(L.wp[1], ref, sm, wm);
+      store_rec(rrs, rec_off(a.n_s, T.r, T.s, 1), ref, sm, wm, tag);
+    }
+  }
+  if (!(mp > -INFINITY)) refp = -INFINITY;
+  if (!(mq > -INFINITY)) refq = -INFINITY;
 }
 
-// Phase 2 of a paired ticket: wait for the team's records, normalisers, residual mass of the
-// slice from the e-values kept in registers.
-__device__ __forceinline__ void phase2(const FusedArgs& a, Lds& L, int r, int s, float refp, float refq,
-                                       const float (&ep)[kPerThread], const float (&eq)[kPerThread]) {
-  const int t = threadIdx.x, lane = t & 63;
+// Phase 2 of a paired ticket: wave 0 polls the team's records (one slice per lane; lanes past
+// the last slice read it again) and forms the normalisers; then every wave turns its kept
+// e-values into the slice's residual mass sum [p - q]_+ (guide page "5.1 投机解码核心原理",
+// §3.2 / §4.1: beta = sum [p - q]_+).  Returns the tagged mass word; the caller stores it.
+__device__ __forceinline__ uint64_t phase2(const FusedArgs& a, Lds& L, int r, float refp, float refq,
+                                           const float (&ep)[kPerThread], const float (&eq)[kPerThread]) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const uint32_t tag = a.tag;
-  const int n_s = a.n_s;
-  if (t < 64) {
+  if (wave == 0) {
+    const int n_s = a.n_s;
     const bool in = lane < n_s;
-    float pr = -INFINITY, ps = 0.f, pw = 0.f, qr = -INFINITY, qs = 0.f, qw = 0.f;
+    const int sl = min(lane, n_s - 1);
+    const __amdgpu_buffer_rsrc_t rrs = rec_rsrc(a);
+    Rec P = load_rec_raw(rrs, rec_off(n_s, r, sl, 0)), Q = load_rec_raw(rrs, rec_off(n_s, r, sl, 1));
     bool timed_out = false;
-    for (unsigned spins = 0;; ++spins) {
-      bool ok = true;
-      if (in) {
-        ok = load_rec(rec_ptr(a.part, n_s, r, lane, 0), tag, pr, ps, pw);
-        ok = load_rec(rec_ptr(a.part, n_s, r, lane, 1), tag, qr, qs, qw) && ok;
+    if (!wave_all(rec_ok(P, tag) && rec_ok(Q, tag))) {
+      for (unsigned spins = 0;; ++spins) {
+        if (spins >= a.spin_limit) { timed_out = true; break; }
+        __builtin_amdgcn_s_sleep(1);
+        P = load_rec_raw(rrs, rec_off(n_s, r, sl, 0));
+        Q = load_rec_raw(rrs, rec_off(n_s, r, sl, 1));
+        if (wave_all(rec_ok(P, tag) && rec_ok(Q, tag))) break;
       }
-      if (wave_all(ok)) break;
-      if (spins >= a.spin_limit) { timed_out = true; break; }
-      __builtin_amdgcn_s_sleep(1);
     }
-    const RowComb P = combine_lanes(pr, ps, pw, in);
-    const RowComb Q = combine_lanes(qr, qs, qw, in);
+    const float pr = __uint_as_float(P.x), ps = __uint_as_float(P.y);
+    const float qr = __uint_as_float(Q.x), qs = __uint_as_float(Q.y);
+    const bool bad = in && (!(ps == ps) || !(ps < INFINITY) || pr == INFINITY || !(qs == qs) ||
+                            !(qs < INFINITY) || qr == INFINITY);
+    const float Mp = wave_max_dpp(in ? pr : -INFINITY), Mq = wave_max_dpp(in ? qr : -INFINITY);
+    // Z = sum_s s_s 2^(ref_s - M): the difference is exact near the maximum, the product exact
+    // in fp64, the sum fp64
+    const double zp = wave_sum_dpp_d((in && ps > 0.f) ? (double)ps * (double)__builtin_amdgcn_exp2f(pr - Mp) : 0.0);
+    const double zq = wave_sum_dpp_d((in && qs > 0.f) ? (double)qs * (double)__builtin_amdgcn_exp2f(qr - Mq) : 0.0);
+    const bool all_good = wave_all(!bad);
     if (lane == 0) {
-      const double alp = exp2_split((double)refp - (double)P.M) / P.z;
-      const double alq = exp2_split((double)refq - (double)Q.M) / Q.z;
-      L.i[5] = timed_out ? 2 : ((P.ok && Q.ok) ? 0 : 1);
-      L.f[2] = (float)(alp / alq);
-      L.f[3] = (float)alq;
+      const bool ok = !timed_out && all_good && zp > 0.0 && zq > 0.0 && Mp > -INFINITY && Mq > -INFINITY;
+      L.cst = timed_out ? 2 : (ok ? 0 : 1);
+      L.cmb[0] = Mp;
+      L.cmb[1] = Mq;
+      L.cmb[2] = (float)(1.0 / zp);
+      L.cmb[3] = (float)(1.0 / zq);
     }
   }
   __syncthreads();
-  const int st = L.i[5];
-  const float rr = L.f[2], alq = L.f[3];
-  float sres[1] = {0.f};
+  const int st = L.cst;
+  float wmass = 0.f;
   if (st == 0) {
-    // sum_x [p - q]_+ = alpha_q * sum_x max(e_p r - e_q, 0)
+    // this wave's alpha = 2^(ref_w - M) / Z of each row; p = e_p alpha_p, q = e_q alpha_q
+    const float ap = refp > -INFINITY ? __builtin_amdgcn_exp2f(refp - L.cmb[0]) * L.cmb[2] : 0.f;
+    const float aq = refq > -INFINITY ? __builtin_amdgcn_exp2f(refq - L.cmb[1]) * L.cmb[3] : 0.f;
+    float sres = 0.f;
+    if (aq > 0.f) {
+      // sum_x [p - q]_+ = alpha_q sum_x max(e_p r - e_q, 0), r = alpha_p / alpha_q
+      const float rr = ap / aq;
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) sres[0] += fmaxf(fmaf(ep[j], rr, -eq[j]), 0.f);
+      for (int j = 0; j < kPerThread; ++j) sres += fmaxf(fmaf(ep[j], rr, -eq[j]), 0.f);
+      wmass = wave_sum_dpp(sres) * aq;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j) sres += ep[j];
+      wmass = wave_sum_dpp(sres) * ap;
+    }
   }
+  if (lane == 0) L.rres[wave] = wmass;
   __syncthreads();
-  block_sum_f<1>(sres, L.red);
-  if (t == 0) {
+  float mass = 0.f;
+  if (t == kStorer) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mass += L.rres[w];
     // NaN marks a slice whose wait gave up; 0 when a row is non-finite
-    const float mass = st == 2 ? __int_as_float(0x7fc00000) : (st == 1 ? 0.f : sres[0] * alq);
-    st_coh(a.smass + (int64_t)r * n_s + s, tagged(mass, tag));
+    mass = st == 2 ? __int_as_float(0x7fc00000) : (st == 1 ? 0.f : mass);
   }
-  __syncthreads();
+  return tagged(mass, tag);
 }
 
 // ---------------------------------------------------------------- the kernel
+
+// Stage the draft offsets in LDS and check them as one exclusive prefix (every request is
+// refused when any offset is out of order).
+__device__ __forceinline__ bool stage_cu(const FusedArgs& a, int* cu, int* red) {
+  const int t = threadIdx.x;
+  for (int k = t; k <= a.B; k += kThreads) cu[k] = a.cu[k];
+  __syncthreads();
+  int bad = 0;
+  for (int k = t; k < a.B; k += kThreads) {
+    const int g = cu[k + 1] - cu[k];
+    if (g < 0 || g > a.G) bad = 1;
+  }
+  if (t == 0 && (cu[0] != 0 || cu[a.B] != a.n_draft_rows)) bad = 1;
+  return block_or(bad, red) != 0;
+}
 
 template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
   __shared__ Lds L;
   const int t = threadIdx.x;
-
-  // stage the draft offsets, check them as one exclusive prefix, build team -> request
-  for (int k = t; k <= a.B; k += kThreads) L.cu[k] = a.cu[k];
-  __syncthreads();
-  int bad = 0;
-  for (int k = t; k < a.B; k += kThreads) {
-    const int g = L.cu[k + 1] - L.cu[k];
-    if (g < 0 || g > a.G) bad = 1;
-  }
-  if (t == 0 && (L.cu[0] != 0 || L.cu[a.B] != a.n_draft_rows)) bad = 1;
-  bad = block_or(bad, L.i);
-  if (bad) {
-    for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
-      if (t <= a.G) a.out_tokens[(int64_t)b * (a.G + 1) + t] = -1;
-      if (t == 0) {
-        a.out_num_accepted[b] = 0;
-        a.out_status[b] = kStBadGamma;
-        if (a.out_req_stats)
-          for (int q = 0; q < 4; ++q) a.out_req_stats[(int64_t)b * 4 + q] = __int_as_float(0x7fc00000);
-      }
-    }
-    return;
-  }
+  if (stage_cu(a, L.cu, L.i)) return;   // the finalize kernel reports it
   for (int b = t; b < a.B; b += kThreads) {
     const int c0 = L.cu[b], g = L.cu[b + 1] - c0;
     for (int i = 0; i <= g; ++i) L.team_req[c0 + b + i] = (uint16_t)b;
   }
   __syncthreads();
 
-  // the first n_fin workgroups finalize requests as they complete; the rest stream
-  if ((int)blockIdx.x < a.n_fin) {
-    for (int b = blockIdx.x; b < a.B; b += a.n_fin) finalize_request<DT, VEC, MODE>(a, L, b);
-    return;
-  }
-  const int w0 = blockIdx.x - a.n_fin, stride = gridDim.x - a.n_fin;
+  const int w0 = blockIdx.x, stride = gridDim.x;
   const int n_s = a.n_s;
+  constexpr int kEsz = DT == kDtBF16 ? 2 : 4;
+  const bool ragged = (a.V % kChunk) != 0;
   auto decode = [&](int xt) {
     Ticket T;
     T.r = xt / n_s;
     T.s = xt - T.r * n_s;
-    T.b = L.team_req[T.r];
-    T.c0 = L.cu[T.b];
-    T.g = L.cu[T.b + 1] - T.c0;
+    T.b = __builtin_amdgcn_readfirstlane((int)L.team_req[T.r]);
+    T.c0 = __builtin_amdgcn_readfirstlane(L.cu[T.b]);
+    T.g = __builtin_amdgcn_readfirstlane(L.cu[T.b + 1]) - T.c0;
     T.i = T.r - T.c0 - T.b;
     T.pair = (MODE == kFuSample) && (T.i < T.g);
     return T;
   };
   RawSlice<DT> nxp, nxq;
-  auto issue = [&](const Ticket& T) {
-    load_raw<DT, VEC>(row_ptr<DT>(a.tgt, a.tgt_ld, T.r), a.V, T.s * kChunk, nxp);
-    if (T.pair) load_raw<DT, VEC>(row_ptr<DT>(a.drf, a.drf_ld, T.c0 + T.i), a.V, T.s * kChunk, nxq);
+  // the ticket's loads: the draft row's always go out (no memory is touched when the ticket has
+  // no draft row), so that the number of loads after a poll does not depend on the ticket
+  auto issue = [&](const Ticket& T, bool live) {
+    if (VEC) {
+      load_raw_buf<DT>(row_rsrc(row_ptr<DT>(a.tgt, a.tgt_ld, T.r), live ? a.V * kEsz : 0), T.s * kChunk, nxp);
+      if (MODE == kFuSample)
+        load_raw_buf<DT>(row_rsrc(T.pair ? row_ptr<DT>(a.drf, a.drf_ld, T.c0 + T.i) : a.tgt,
+                                  (live && T.pair) ? a.V * kEsz : 0),
+                         T.s * kChunk, nxq);
+    } else if (live) {
+      load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, T.r), a.V, T.s * kChunk, nxp);
+      if (T.pair) load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, T.c0 + T.i), a.V, T.s * kChunk, nxq);
+    }
   };
 
-  // two-stage pipeline: phase 1 of ticket k, then phase 2 (team wait) of ticket k - 1, while
-  // the loads of ticket k + 1 are in flight
-  float ep[kPerThread], eq[kPerThread];
-  int pend_r = -1, pend_s = 0;
-  float pend_refp = 0.f, pend_refq = 0.f;
-  if (w0 < a.n_tickets) issue(decode(w0));
-  for (int xt = w0;; xt += stride) {
-    const bool have = xt < a.n_tickets;
-    Ticket T;
-    T.pair = false;
+  // One ticket at a time: its loads were issued one ticket earlier; after the unpack the loads
+  // of the next ticket go out, then phase 1, the team wait and phase 2.  Residual masses are
+  // stored one ticket late so that no store completion is waited for at the next unpack.
+  uint64_t* mass_ptr = nullptr;
+  uint64_t mass_word = 0;
+  if (w0 < a.n_tickets) issue(decode(w0), true);
+  for (int xt = w0; xt < a.n_tickets; xt += stride) {
+    const Ticket T = decode(xt);
     float vp[kPerThread], vq[kPerThread];
     float refp = 0.f, refq = 0.f;
-    if (have) {
-      T = decode(xt);
-      unpack_raw<DT>(nxp, vp);
-      if (T.pair) unpack_raw<DT>(nxq, vq);
-      if (xt + stride < a.n_tickets) issue(decode(xt + stride));
-      phase1<DT, MODE>(a, L, T, vp, vq, refp, refq);
+    unpack_raw<DT>(nxp, vp);
+    if (T.pair) unpack_raw<DT>(nxq, vq);
+    if (VEC && ragged && T.s == n_s - 1) {
+      mask_tail<DT>(a.V, T.s * kChunk, vp);
+      if (T.pair) mask_tail<DT>(a.V, T.s * kChunk, vq);
     }
-    if (MODE == kFuSample && pend_r >= 0) phase2(a, L, pend_r, pend_s, pend_refp, pend_refq, ep, eq);
-    if (!have) break;
-    pend_r = -1;
-    if (T.pair) {
-      pend_r = T.r;
-      pend_s = T.s;
-      pend_refp = refp;
-      pend_refq = refq;
-#pragma unroll
-      for (int j = 0; j < kPerThread; ++j) { ep[j] = vp[j]; eq[j] = vq[j]; }
+    if (mass_ptr != nullptr && t == kStorer) st_coh(mass_ptr, mass_word);
+    mass_ptr = nullptr;
+    const bool more = xt + stride < a.n_tickets;
+    issue(decode(more ? xt + stride : xt), more);
+    phase1<DT, MODE>(a, L, T, vp, vq, refp, refq);
+    if (MODE == kFuSample && T.pair) {
+      mass_word = phase2(a, L, T.r, refp, refq, vp, vq);
+      mass_ptr = a.smass + (int64_t)T.r * n_s + T.s;
     }
   }
+  if (mass_ptr != nullptr && t == kStorer) st_coh(mass_ptr, mass_word);
+}
+
+// One workgroup per request, after the streaming kernel: every record is in place.
+template <int DT, bool VEC, int MODE>
+__global__ __launch_bounds__(kThreads) void k_fused_finalize(FusedArgs a) {
+  __shared__ LdsFin L;
+  const int t = threadIdx.x, b = blockIdx.x;
+  if (stage_cu(a, L.cu, L.i)) {
+    if (t <= a.G) a.out_tokens[(int64_t)b * (a.G + 1) + t] = -1;
+    if (t == 0) {
+      a.out_num_accepted[b] = 0;
+      a.out_status[b] = kStBadGamma;
+      if (a.out_req_stats)
+        for (int q = 0; q < 4; ++q) a.out_req_stats[(int64_t)b * 4 + q] = __int_as_float(0x7fc00000);
+    }
+    return;
+  }
+  finalize_request<DT, VEC, MODE>(a, L, b);
 }
 
 // ---------------------------------------------------------------- launch
@@ -784,17 +948,17 @@ static hipError_t launch_fused_t(FusedArgs a, hipStream_t st) {
     const int want = atoi(g);
     if (want > 0 && want < grid) grid = want;
   }
-  if (grid > a.n_tickets + 128) grid = a.n_tickets + 128;
-  if (grid < 2) return hipErrorInvalidConfiguration;
-  // finalizer workgroups: enough that finalizing keeps pace with the requests completing
-  a.n_fin = a.B < grid / 4 ? a.B : grid / 4;
-  if (a.n_fin > 128) a.n_fin = 128;
-  if (grid - a.n_fin < 1) return hipErrorInvalidConfiguration;
+  if (grid > a.n_tickets) grid = a.n_tickets;
+  if (grid < 1) return hipErrorInvalidConfiguration;
+  a.n_fin = 0;
   if (getenv("SPEC_VERIFY_DEBUG"))
-    fprintf(stderr, "[specverify] fused grid %d (resident capacity %d, finalizers %d) tickets %d slices %d mode %d\n",
-            grid, cached_grid, a.n_fin, a.n_tickets, a.n_s, a.mode);
+    fprintf(stderr, "[specverify] fused grid %d (resident capacity %d) tickets %d slices %d mode %d\n", grid,
+            cached_grid, a.n_tickets, a.n_s, a.mode);
   void* args[] = {&a};
-  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, st);
+  e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_fused_finalize<DT, VEC, MODE>), dim3(a.B), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_fused(const FusedArgs& a, int dt, int vec, hipStream_t st) {
@@ -808,6 +972,6 @@ hipError_t launch_fused(const FusedArgs& a, int dt, int vec, hipStream_t st) {
   return vec ? launch_fused_t<kDtF32, true, kFuGreedy>(a, st) : launch_fused_t<kDtF32, false, kFuGreedy>(a, st);
 }
 
-size_t fused_record_bytes() { return 3 * sizeof(uint64_t); }
+size_t fused_record_bytes() { return 16; }
 
 }  // namespace specv
