@@ -130,7 +130,8 @@ def load_traffic(kernel):
         with open(path) as f:
             rec = json.load(f)
         import hashlib
-        src = os.path.join(ROOT, "lossless_draft_verification_row_amd", "csrc", "spec_kernels.hip")
+        src = os.path.join(ROOT, "lossless_draft_verification_row_amd", "csrc",
+                           "spec_fused.hip" if kernel == "k_fused" else "spec_kernels.hip")
         h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
         if rec.get("kernel_source_sha") != h:
             return None
@@ -214,7 +215,7 @@ def main():
     kern_avg_s = float(np.mean(kernel_ms)) / 1e3
     achieved = alg_bytes / kern_avg_s / 1e9
     fused = not os.environ.get("SPEC_VERIFY_NO_FUSED")
-    kernel_name = ("k_fused (the whole round: every needed logit read once)" if fused
+    kernel_name = ("k_fused (streaming kernel: every needed logit read once, both phases)" if fused
                    else "k_pass1 (streaming pass over every needed logit)")
     traffic = load_traffic("k_fused" if fused else "k_pass1")
     line = {

@@ -111,7 +111,9 @@ typedef struct {
  *  The sampler is a fixed-order inverse CDF in three levels (chunks of 4096 tokens, groups of
  *  64, tokens) with one uniform per level; its law is exactly the residual (or p_{g+1}).
  *  If cu_draft is not an exclusive prefix (cu_draft[0] = 0, 0 <= gamma_b <= gamma_max,
- *  cu_draft[B] = n_draft_rows) no row is read and every request reports SPEC_STATUS_BAD_GAMMA.
+ *  cu_draft[B] = n_draft_rows) every request reports SPEC_STATUS_BAD_GAMMA; rows may still be
+ *  read, but only inside the declared allocations (target rows < n_draft_rows + B, draft rows
+ *  < n_draft_rows).
  *  workspace: spec_verify_workspace_bytes(B, V, gamma_max, dt, sp) bytes of device memory,
  *  256-byte aligned, ZERO-FILLED once before its first use with this library (workgroups of
  *  one call exchange records in it, tagged with a per-call sequence number that a zero-filled

@@ -185,6 +185,15 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   v += SPEC_DPP(0.f, v, 0x143, 0xc);  // row_bcast:31
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xb1, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4e, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
+  return __builtin_amdgcn_readlane(v, 63);
+}
 __device__ __forceinline__ float wave_max_dpp(float v) {
   const float ninf = -INFINITY;
   v = fmaxf(v, SPEC_DPP(ninf, v, 0xb1, 0xf));

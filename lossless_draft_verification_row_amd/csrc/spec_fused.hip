@@ -53,17 +53,14 @@ struct FinScratch {
   TeamL team[kMaxGamma + 1];
   double py[kMaxGamma], qy[kMaxGamma], u0[kMaxGamma];
   int ytok[kMaxGamma];
-  double mass[kMaxSlicesFused];
   double gm[kChunk / kGroup];
   float dh[kMaxGamma], dm[kMaxGamma];
   float wsel[kGroup];
   double u[3];
-  int flags, status, n_acc, pos, wkind, y, kpick, gpick, xpick, pass;
+  int flags, status, n_acc, pos, wkind, y, kpick, gpick, xpick;
 };
 
 struct Lds {
-  uint16_t team_req[kMaxTeamsFused];
-  int cu[kMaxReqFused + 1];
   float red[8 * kWaves];
   float f[8];
   int i[8];
@@ -80,6 +77,13 @@ struct LdsFin {
   int i[8];
   FinScratch fin;
 };
+
+// A uniform 32-bit load through the scalar data cache (read-only data of the call).
+__device__ __forceinline__ int sload_i32(const int32_t* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
 
 // ---------------------------------------------------------------- tagged records
 
@@ -171,20 +175,70 @@ __device__ __forceinline__ void block_max_f(float (&v)[N], float* red) {
   }
 }
 
-// ---------------------------------------------------------------- combining slice records
+// ---------------------------------------------------------------- wave-wide fp64 helpers
+
+// 64-bit DPP move of both halves (lanes whose source is outside the row, or rows outside
+// RMASK, read 0).
+template <int CTRL, int RMASK>
+__device__ __forceinline__ double dpp_d(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, RMASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, RMASK, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, lane), hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+// fp64 sum over the wave in a fixed order (row reductions, then row broadcasts); every lane
+// gets lane 63's total.
+__device__ __forceinline__ double wave_sum_dpp_d(double v) {
+  v += dpp_d<0xb1, 0xf>(v);
+  v += dpp_d<0x4e, 0xf>(v);
+  v += dpp_d<0x124, 0xf>(v);
+  v += dpp_d<0x128, 0xf>(v);
+  v += dpp_d<0x142, 0xa>(v);
+  v += dpp_d<0x143, 0xc>(v);
+  return readlane_d(v, 63);
+}
+// Inclusive fp64 prefix sum over the wave's lanes (row shifts, then row broadcasts).
+__device__ __forceinline__ double wave_scan_dpp_d(double v) {
+  v += dpp_d<0x111, 0xf>(v);   // row_shr:1
+  v += dpp_d<0x112, 0xf>(v);   // row_shr:2
+  v += dpp_d<0x114, 0xf>(v);   // row_shr:4
+  v += dpp_d<0x118, 0xf>(v);   // row_shr:8
+  v += dpp_d<0x142, 0xa>(v);   // row_bcast:15
+  v += dpp_d<0x143, 0xc>(v);   // row_bcast:31
+  return v;
+}
+// Inverse-CDF pick over the masses held one per lane (lanes >= n hold 0): the first index
+// whose prefix sum exceeds u * total; if rounding leaves none, the last index with positive
+// mass; -1 when the total is not positive.  Returns the pick; `total` gets the sum.
+__device__ __forceinline__ int wave_pick(double m, int n, double u, double& total) {
+  const int lane = threadIdx.x & 63;
+  const bool in = lane < n;
+  const double cum = wave_scan_dpp_d(in ? m : 0.0);
+  total = readlane_d(cum, 63);
+  if (!(total > 0.0)) return -1;
+  const double target = u * total;
+  const unsigned long long over = __ballot(in && cum > target);
+  if (over) return __builtin_ctzll(over);
+  const unsigned long long pos = __ballot(in && m > 0.0);
+  return pos ? 63 - __builtin_clzll(pos) : -1;
+}
 
 // Fixed-order fp64 combine of one row's slice records held one per lane (lanes >= n_s hold
-// ref = -inf, s = 0).  Every lane gets the result.
+// ref = -inf, s = 0): M = max ref, z = sum s 2^(ref - M), w = sum 2^(ref - M) (w_s + s_s (ref - M)).
 struct RowComb {
   double z, w;
   float M;
   bool ok;
 };
-
 __device__ __forceinline__ RowComb combine_lanes(float ref, float s, float w, bool in_range) {
   RowComb rc;
   const bool bad = in_range && (!(s == s) || !(s < INFINITY) || ref == INFINITY);
-  const float M = wave_max(in_range ? ref : -INFINITY);
+  const float M = wave_max_dpp(in_range ? ref : -INFINITY);
   double z = 0.0, ww = 0.0;
   if (in_range && s > 0.f) {
     const double d = (double)ref - (double)M;
@@ -192,8 +246,8 @@ __device__ __forceinline__ RowComb combine_lanes(float ref, float s, float w, bo
     z = (double)s * f;
     ww = f * ((double)w + (double)s * d);
   }
-  rc.z = wave_sum_d(z);
-  rc.w = wave_sum_d(ww);
+  rc.z = wave_sum_dpp_d(z);
+  rc.w = wave_sum_dpp_d(ww);
   rc.M = M;
   rc.ok = wave_all(!bad) && rc.z > 0.0 && M > -INFINITY;
   return rc;
@@ -230,6 +284,11 @@ __device__ __forceinline__ void load_run16(const void* row, int V, int x0, float
   }
 }
 
+// One request: combine its teams' records (normaliser, entropy in bits and max probability as
+// in the SpecKV page's signals, beta = sum [p - q]_+), run the accept scan (guide page
+// "5.1 投机解码核心原理" §3.1 / §3.2, stop at the first rejection §5.1) and the three-level
+// sampler over the residual or p_{g+1} (§5.2), and write the outputs.  Scans over chunk,
+// group and element masses are wave-wide fp64 prefix sums.
 template <int DT, bool VEC, int MODE>
 __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   FinScratch& F = L.fin;
@@ -241,7 +300,6 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   const float nan = __int_as_float(0x7fc00000);
   const double cd = (double)a.c;
   const __amdgpu_buffer_rsrc_t rrs = rec_rsrc(a);
-  if (t == 0) { F.flags = 0; F.status = 0; }
   // the draft tokens and their logits do not depend on any record: fetch them first
   float ly_p = 0.f, ly_q = 0.f;
   int ytok = -1;
@@ -253,36 +311,31 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
     }
   }
 
-  // A. wait for the request's records and combine each team (one wave per team)
+  // A. combine each team's records (one wave per team); the streaming kernel has finished
   for (int ti = wave; ti <= g; ti += kWaves) {
     const int r = c0 + b + ti;
     const bool pair = (MODE == kFuSample) && ti < g;
     const bool in = lane < n_s;
     float pr = -INFINITY, ps = 0.f, pw = 0.f, qr = -INFINITY, qs = 0.f, qw = 0.f, sm = 0.f;
-    bool timed_out = false;
-    for (unsigned spins = 0;; ++spins) {
-      bool ok = true;
-      if (in) {
-        ok = load_rec(rrs, rec_off(n_s, r, lane, 0), tag, pr, ps, pw);
-        if (pair) {
-          ok = load_rec(rrs, rec_off(n_s, r, lane, 1), tag, qr, qs, qw) && ok;
-          const uint64_t m = ld_coh(a.smass + (int64_t)r * n_s + lane);
-          sm = lo_f(m);
-          ok = ok && tag_of(m) == tag;
-        }
+    bool ok = true;
+    if (in) {
+      ok = load_rec(rrs, rec_off(n_s, r, lane, 0), tag, pr, ps, pw);
+      if (pair) {
+        ok = load_rec(rrs, rec_off(n_s, r, lane, 1), tag, qr, qs, qw) && ok;
+        const uint64_t m = ld_coh(a.smass + (int64_t)r * n_s + lane);
+        sm = lo_f(m);
+        ok = ok && tag_of(m) == tag;
       }
-      if (wave_all(ok)) break;
-      if (spins >= a.spin_limit) { timed_out = true; break; }
-      __builtin_amdgcn_s_sleep(2);
     }
+    const bool missing = !wave_all(ok);
     TeamL T;
     T.z[0] = T.z[1] = 1.0; T.w[0] = T.w[1] = 0.0; T.beta = 0.0; T.M[0] = T.M[1] = 0.f;
     T.amax = -1;
-    T.flags = timed_out ? kTeamTimeout : 0;
+    T.flags = missing ? kTeamTimeout : 0;
     if (MODE == kFuGreedy) {
       const int qa = __float_as_int(ps);
       const bool bad = in && (qa == -2 || pr == INFINITY);
-      const float M = wave_max(in ? pr : -INFINITY);
+      const float M = wave_max_dpp(in ? pr : -INFINITY);
       const int idx = wave_min_i((in && pr == M && qa >= 0) ? qa : INT_MAX);
       T.M[0] = M;
       T.amax = idx == INT_MAX ? -1 : idx;
@@ -295,9 +348,9 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
         const RowComb Q = combine_lanes(qr, qs, qw, in);
         T.z[1] = Q.z; T.w[1] = Q.w; T.M[1] = Q.M;
         if (!Q.ok) T.flags |= kTeamBadQ;
-        // a slice that gave up its own wait marked its residual mass NaN
+        // a slice whose team wait gave up marked its residual mass NaN
         if (!wave_all(!(in && !(sm == sm)))) T.flags |= kTeamTimeout;
-        T.beta = wave_sum_d(in ? (double)sm : 0.0);
+        T.beta = wave_sum_dpp_d(in ? (double)sm : 0.0);
       }
     }
     if (lane == 0) F.team[ti] = T;
@@ -305,10 +358,11 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   __syncthreads();
 
   // B. per position: statistics, p(y), q(y), the accept draw
+  bool rej = false;
+  int why = 0;
   if (t <= g) {
     const int r = c0 + b + t;
     const TeamL T = F.team[t];
-    if (T.flags) atomicOr(&F.flags, T.flags);
     const bool okp = (T.flags & (kTeamBadP | kTeamTimeout)) == 0;
     const float hp = (float)(log2_split(T.z[0]) - T.w[0] / T.z[0]);
     if (a.st.target_entropy_bits) a.st.target_entropy_bits[r] = okp ? (MODE == kFuGreedy ? 0.f : hp) : nan;
@@ -355,61 +409,62 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       F.ytok[t] = y;
       F.py[t] = pyd;
       F.qy[t] = qyd;
-      uint64_t w[4];
-      philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(t + 1), 0, 0, w);
-      F.u0[t] = u53(w[0]);
+      // the accept test of position t (evaluated for every position; the scan takes the first)
+      if (!yv) { rej = true; why = kStBadToken; }
+      else if (MODE == kFuGreedy) rej = y != T.amax;
+      else if (!(qyd > 0.0)) { rej = true; why = kStZeroQ; }
+      else {
+        uint64_t w[4];
+        philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(t + 1), 0, 0, w);
+        rej = !(u53(w[0]) < fmin(1.0, pyd / qyd));
+      }
     }
   }
-  __syncthreads();
-
-  // C. request statistics, accept scan, choice of the sampled row (one thread)
-  if (t == 0) {
-    if (a.out_req_stats) {
-      float rq[4] = {nan, nan, nan, nan};
-      if (g > 0 && MODE != kFuGreedy) {
-        double hs = 0.0, cs = 0.0;
-        float hmax = -INFINITY, cmin = INFINITY;
-        bool anynan = false;
-        for (int i = 0; i < g; ++i) {
-          const float h = F.dh[i], cm = F.dm[i];
-          if (!(h == h) || !(cm == cm)) anynan = true;
-          hs += h; cs += cm;
-          hmax = fmaxf(hmax, h); cmin = fminf(cmin, cm);
+  // C. request flags and the first rejection (wave 0 covers positions 0..63)
+  if (wave == 0) {
+    // flags of every team (positions 0..g; wave 0 holds 0..63, lane 0 adds position 64)
+    int fl = lane <= g ? F.team[lane].flags : 0;
+    if (lane == 0 && g >= 64) fl |= F.team[64].flags;
+    fl = wave_or(fl);
+    const unsigned long long rm = __ballot(rej);
+    const int j = rm ? __builtin_ctzll(rm) : -1;
+    const int whyj = j >= 0 ? __builtin_amdgcn_readlane(why, j) : 0;
+    if (lane == 0) {
+      int status = 0;
+      if (fl & kTeamTimeout) status = kStTimeout;
+      else if (fl) status = kStNonfinite;
+      else status = whyj;
+      const bool stop = (status & (kStTimeout | kStNonfinite)) != 0;
+      const int jj = stop ? -1 : j;
+      F.n_acc = jj < 0 ? g : jj;
+      F.pos = jj < 0 ? g : jj;
+      F.y = jj >= 0 ? F.ytok[jj] : -1;
+      // wkind: 0 = p of the row, 1 = [p - q]_+, 2 = p without token y
+      F.wkind = (jj < 0) ? 0 : (MODE == kFuSample ? 1 : 2);
+      uint64_t w[4];
+      philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(F.pos + 1), 0, 0, w);
+      F.u[0] = u53(w[1]);
+      F.u[1] = u53(w[2]);
+      F.u[2] = u53(w[3]);
+      F.status = status;
+      F.kpick = -1;
+      if (a.out_req_stats) {
+        float rq[4] = {nan, nan, nan, nan};
+        if (g > 0 && MODE != kFuGreedy) {
+          double hs = 0.0, cs = 0.0;
+          float hmax = -INFINITY, cmin = INFINITY;
+          bool anynan = false;
+          for (int i = 0; i < g; ++i) {
+            const float h = F.dh[i], cm = F.dm[i];
+            if (!(h == h) || !(cm == cm)) anynan = true;
+            hs += h; cs += cm;
+            hmax = fmaxf(hmax, h); cmin = fminf(cmin, cm);
+          }
+          if (!anynan) { rq[0] = (float)(hs / g); rq[1] = (float)(cs / g); rq[2] = hmax; rq[3] = cmin; }
         }
-        if (!anynan) { rq[0] = (float)(hs / g); rq[1] = (float)(cs / g); rq[2] = hmax; rq[3] = cmin; }
-      }
-      for (int q = 0; q < 4; ++q) a.out_req_stats[(int64_t)b * 4 + q] = rq[q];
-    }
-    int status = 0, j = -1;
-    if (F.flags & kTeamTimeout) status = kStTimeout;
-    else if (F.flags) status = kStNonfinite;
-    else {
-      for (int i = 0; i < g; ++i) {
-        const int y = F.ytok[i];
-        if (y < 0 || y >= a.V) { status |= kStBadToken; j = i; break; }
-        if (MODE == kFuGreedy) {
-          if (y == F.team[i].amax) continue;
-          j = i;
-          break;
-        }
-        const double qy = F.qy[i];
-        if (!(qy > 0.0)) { status |= kStZeroQ; j = i; break; }
-        const double acc = fmin(1.0, F.py[i] / qy);
-        if (!(F.u0[i] < acc)) { j = i; break; }
+        for (int q = 0; q < 4; ++q) a.out_req_stats[(int64_t)b * 4 + q] = rq[q];
       }
     }
-    F.n_acc = j < 0 ? g : j;
-    F.pos = j < 0 ? g : j;
-    F.y = j >= 0 ? F.ytok[j] : -1;
-    // wkind: 0 = p of the row, 1 = [p - q]_+, 2 = p without token y
-    F.wkind = (j < 0) ? 0 : (MODE == kFuSample ? 1 : 2);
-    uint64_t w[4];
-    philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(F.pos + 1), 0, 0, w);
-    F.u[0] = u53(w[1]);
-    F.u[1] = u53(w[2]);
-    F.u[2] = u53(w[3]);
-    F.status = status;
-    F.kpick = -1;
   }
   __syncthreads();
 
@@ -421,53 +476,38 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   } else {
     const int r = c0 + b + F.pos;
     const TeamL T = F.team[F.pos];
-    // D. level 1 over chunk masses (a second pass only if the residual turned out empty)
-    for (int pass = 0; pass < 2; ++pass) {
-      const int wkind = F.wkind;
-      if (t < 64) {
-        for (int k = lane; k < n_s; k += 64) {
-          double m;
+    // D. level 1 over the chunk masses (p's masses again if the residual turned out empty)
+    if (wave == 0) {
+      int wkind = F.wkind;
+      int pick = -1;
+      for (int pass = 0; pass < 2; ++pass) {
+        double m = 0.0;
+        if (lane < n_s) {
           if (wkind == 1) {
-            m = (double)lo_f(ld_coh(a.smass + (int64_t)r * n_s + k));
+            m = (double)lo_f(ld_coh(a.smass + (int64_t)r * n_s + lane));
           } else {
-            float ref, s, w;
-            load_rec(rrs, rec_off(n_s, r, k, 0), tag, ref, s, w);
-            m = s > 0.f ? (double)s * exp2_split((double)ref - (double)T.M[0]) / T.z[0] : 0.0;
+            float ref, sv, wv;
+            load_rec(rrs, rec_off(n_s, r, lane, 0), tag, ref, sv, wv);
+            m = sv > 0.f ? (double)sv * exp2_split((double)ref - (double)T.M[0]) / T.z[0] : 0.0;
             if (wkind == 2) {
               const int y = F.y;
-              if (y >= 0 && y < a.V && y / kChunk == k) m = fmax(m - F.py[F.pos], 0.0);
+              if (y >= 0 && y < a.V && y / kChunk == lane) m = fmax(m - F.py[F.pos], 0.0);
             }
           }
-          F.mass[k] = m;
         }
+        double tot;
+        pick = wave_pick(m, n_s, F.u[0], tot);
+        if (pick >= 0 || wkind == 0) break;
+        wkind = 0;
+        if (lane == 0) F.status |= kStResidualEmpty;
       }
-      __syncthreads();
-      if (t == 0) {
-        double tot = 0.0;
-        for (int k = 0; k < n_s; ++k) tot += F.mass[k];
-        int pick = -1;
-        if (tot > 0.0) {
-          const double target = F.u[0] * tot;
-          double cum = 0.0;
-          int last = -1;
-          for (int k = 0; k < n_s; ++k) {
-            cum += F.mass[k];
-            if (F.mass[k] > 0.0) last = k;
-            if (cum > target) { pick = k; break; }
-          }
-          if (pick < 0) pick = last;
-        }
-        F.kpick = pick;
-        F.pass = 2;
-        if (pick < 0 && wkind != 0) { F.status |= kStResidualEmpty; F.wkind = 0; F.pass = 1; }
-      }
-      __syncthreads();
-      if (F.pass == 2) break;
+      if (lane == 0) { F.kpick = pick; F.wkind = wkind; }
     }
+    __syncthreads();
     const int k = F.kpick;
     if (k >= 0) {
       // E. levels 2 and 3 inside chunk k.  Weights are relative within the chunk: e_p (p
-      // only) or max(e_p * r - e_q, 0) with r = alpha_p / alpha_q, exactly as streamed.
+      // only) or max(e_p r - e_q, 0) with r = alpha_p / alpha_q.
       const int wkind = F.wkind;
       float refp, sp_, wp_, refq = 0.f, rr = 0.f;
       load_rec(rrs, rec_off(n_s, r, k, 0), tag, refp, sp_, wp_);
@@ -502,24 +542,17 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       double part = 0.0;
 #pragma unroll
       for (int e = 0; e < 16; ++e) part += (double)wv[e];
-      part += __shfl_xor(part, 1, 64);
-      part += __shfl_xor(part, 2, 64);
+      // group sum over the 4 threads of a group (quad lanes), in a fixed order
+      part += dpp_d<0xb1, 0xf>(part);
+      part += dpp_d<0x4e, 0xf>(part);
       if (quarter == 0) F.gm[grp] = part;
       __syncthreads();
-      if (t == 0) {
-        const int n_in = min(kChunk, a.V - k * kChunk);
-        const int n_groups = (n_in + kGroup - 1) / kGroup;
-        double tot = 0.0;
-        for (int q = 0; q < n_groups; ++q) tot += F.gm[q];
-        const double target = F.u[1] * tot;
-        double cum = 0.0;
-        int pick = -1, last = -1;
-        for (int q = 0; q < n_groups; ++q) {
-          cum += F.gm[q];
-          if (F.gm[q] > 0.0) last = q;
-          if (cum > target) { pick = q; break; }
-        }
-        F.gpick = pick < 0 ? last : pick;
+      const int n_in = min(kChunk, a.V - k * kChunk);
+      const int n_groups = (n_in + kGroup - 1) / kGroup;
+      if (wave == 0) {
+        double tot;
+        const int gp = wave_pick(lane < n_groups ? F.gm[lane] : 0.0, n_groups, F.u[1], tot);
+        if (lane == 0) F.gpick = gp;
       }
       __syncthreads();
       if (grp == F.gpick) {
@@ -527,24 +560,17 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
         for (int e = 0; e < 16; ++e) F.wsel[quarter * 16 + e] = wv[e];
       }
       __syncthreads();
-      if (t == 0) {
+      if (wave == 0) {
         const int gsel = F.gpick;
         int pick = -1;
         if (gsel >= 0) {
           const int lo = k * kChunk + gsel * kGroup;
           const int n = min(kGroup, a.V - lo);
-          const double target = F.u[2] * F.gm[gsel];
-          double cum = 0.0;
-          int last = -1;
-          for (int e = 0; e < n; ++e) {
-            cum += (double)F.wsel[e];
-            if (F.wsel[e] > 0.f) last = e;
-            if (cum > target) { pick = e; break; }
-          }
-          if (pick < 0) pick = last;
+          double tot;
+          pick = wave_pick(lane < n ? (double)F.wsel[lane] : 0.0, n, F.u[2], tot);
           if (pick >= 0) pick += lo;
         }
-        F.xpick = pick;
+        if (lane == 0) F.xpick = pick;
       }
       __syncthreads();
       x = F.xpick;
@@ -564,7 +590,6 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
     a.out_num_accepted[b] = ok ? F.n_acc : 0;
     a.out_status[b] = F.status;
   }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------- streaming phases
@@ -580,28 +605,7 @@ struct Ticket {
 // issued after a poll stand between the poll and its use (vector memory counters retire in
 // issue order).
 constexpr int kStorer = kThreads - 64;
-
-// 64-bit DPP move of both halves (rows outside RMASK read 0).
-template <int CTRL, int RMASK>
-__device__ __forceinline__ double dpp_d(double v) {
-  const long long b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, RMASK, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, RMASK, 0xf, false);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
-}
-// fp64 sum over the wave in a fixed order (row reductions, then row broadcasts); every lane
-// gets lane 63's total.
-__device__ __forceinline__ double wave_sum_dpp_d(double v) {
-  v += dpp_d<0xb1, 0xf>(v);
-  v += dpp_d<0x4e, 0xf>(v);
-  v += dpp_d<0x124, 0xf>(v);
-  v += dpp_d<0x128, 0xf>(v);
-  v += dpp_d<0x142, 0xa>(v);
-  v += dpp_d<0x143, 0xc>(v);
-  const long long b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readlane((int)b, 63), hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
-}
+   // polls served by the XCD's L2 before device-scope polls
 
 // Bounds-checked row loads: a buffer resource over the row's bytes.  16-byte loads past the
 // end return zeros and touch no memory (num_records 0 turns every load off).
@@ -737,6 +741,9 @@ __device__ __forceinline__ void phase1(const FusedArgs& a, Lds& L, const Ticket&
     if (T.pair) {
       fold_waves(L.wp[1], ref, sm, wm);
       store_rec(rrs, rec_off(a.n_s, T.r, T.s, 1), ref, sm, wm, tag);
+      // the arrival flag goes out once both records are visible
+      wait_vmem();
+      __hip_atomic_store(a.arrive + (int64_t)T.r * a.n_s + T.s, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (!(mp > -INFINITY)) refp = -INFINITY;
@@ -756,12 +763,24 @@ __device__ __forceinline__ uint64_t phase2(const FusedArgs& a, Lds& L, int r, fl
     const bool in = lane < n_s;
     const int sl = min(lane, n_s - 1);
     const __amdgpu_buffer_rsrc_t rrs = rec_rsrc(a);
-    Rec P = load_rec_raw(rrs, rec_off(n_s, r, sl, 0)), Q = load_rec_raw(rrs, rec_off(n_s, r, sl, 1));
+    // wait until the team has had time to publish, then poll its arrival flags (one word per
+    // slice) with growing pauses, and read the records once they are all in
+    const long long t0 = wall_clock64();
+    while (wall_clock64() - t0 < a.poll_delay) __builtin_amdgcn_s_sleep(8);
+    const uint32_t* fl = a.arrive + (int64_t)r * n_s;
     bool timed_out = false;
-    if (!wave_all(rec_ok(P, tag) && rec_ok(Q, tag))) {
-      for (unsigned spins = 0;; ++spins) {
+    unsigned spins = 0;
+    for (int pause = a.poll_pause > 0 ? a.poll_pause : 4;; pause = a.poll_pause > 0 ? pause : min(2 * pause, 64)) {
+      const uint32_t f = __hip_atomic_load(fl + sl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (wave_all(f == tag)) break;
+      if (++spins > a.spin_limit) { timed_out = true; break; }
+      for (int k = 0; k < pause; ++k) __builtin_amdgcn_s_sleep(2);
+    }
+    Rec P = load_rec_raw(rrs, rec_off(n_s, r, sl, 0)), Q = load_rec_raw(rrs, rec_off(n_s, r, sl, 1));
+    if (!timed_out && !wave_all(rec_ok(P, tag) && rec_ok(Q, tag))) {
+      for (;; ++spins) {
         if (spins >= a.spin_limit) { timed_out = true; break; }
-        __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_s_sleep(4);
         P = load_rec_raw(rrs, rec_off(n_s, r, sl, 0));
         Q = load_rec_raw(rrs, rec_off(n_s, r, sl, 1));
         if (wave_all(rec_ok(P, tag) && rec_ok(Q, tag))) break;
@@ -835,75 +854,63 @@ __device__ __forceinline__ bool stage_cu(const FusedArgs& a, int* cu, int* red) 
   return block_or(bad, red) != 0;
 }
 
+// One workgroup per ticket.  Workgroup i runs on XCD i mod 8 (the dispatcher deals workgroups
+// round-robin over the XCDs), and the slices of team r go to consecutive workgroups of XCD
+// r mod 8, so a team's records meet in that XCD's L2.  A member waits only for members
+// dispatched just before or after it on the same XCD; every wait is bounded.
 template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
   __shared__ Lds L;
   const int t = threadIdx.x;
-  if (stage_cu(a, L.cu, L.i)) return;   // the finalize kernel reports it
-  for (int b = t; b < a.B; b += kThreads) {
-    const int c0 = L.cu[b], g = L.cu[b + 1] - c0;
-    for (int i = 0; i <= g; ++i) L.team_req[c0 + b + i] = (uint16_t)b;
-  }
-  __syncthreads();
-
-  const int w0 = blockIdx.x, stride = gridDim.x;
   const int n_s = a.n_s;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int tl = j / n_s;
+  Ticket T;
+  T.s = j - tl * n_s;
+  T.r = tl * 8 + xcd;
+  if (T.r >= a.n_teams) return;
+  T.pair = false;
+  T.b = 0; T.c0 = 0; T.g = 0; T.i = 0;
+  int drow = -1;
   constexpr int kEsz = DT == kDtBF16 ? 2 : 4;
-  const bool ragged = (a.V % kChunk) != 0;
-  auto decode = [&](int xt) {
-    Ticket T;
-    T.r = xt / n_s;
-    T.s = xt - T.r * n_s;
-    T.b = __builtin_amdgcn_readfirstlane((int)L.team_req[T.r]);
-    T.c0 = __builtin_amdgcn_readfirstlane(L.cu[T.b]);
-    T.g = __builtin_amdgcn_readfirstlane(L.cu[T.b + 1]) - T.c0;
-    T.i = T.r - T.c0 - T.b;
-    T.pair = (MODE == kFuSample) && (T.i < T.g);
-    return T;
-  };
-  RawSlice<DT> nxp, nxq;
-  // the ticket's loads: the draft row's always go out (no memory is touched when the ticket has
-  // no draft row), so that the number of loads after a poll does not depend on the ticket
-  auto issue = [&](const Ticket& T, bool live) {
-    if (VEC) {
-      load_raw_buf<DT>(row_rsrc(row_ptr<DT>(a.tgt, a.tgt_ld, T.r), live ? a.V * kEsz : 0), T.s * kChunk, nxp);
-      if (MODE == kFuSample)
-        load_raw_buf<DT>(row_rsrc(T.pair ? row_ptr<DT>(a.drf, a.drf_ld, T.c0 + T.i) : a.tgt,
-                                  (live && T.pair) ? a.V * kEsz : 0),
-                         T.s * kChunk, nxq);
-    } else if (live) {
-      load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, T.r), a.V, T.s * kChunk, nxp);
-      if (T.pair) load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, T.c0 + T.i), a.V, T.s * kChunk, nxq);
+  RawSlice<DT> rp, rq;
+  if (VEC) load_raw_buf<DT>(row_rsrc(row_ptr<DT>(a.tgt, a.tgt_ld, T.r), a.V * kEsz), T.s * kChunk, rp);
+  else load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, T.r), a.V, T.s * kChunk, rp);
+  if (MODE == kFuSample) {
+    // request of target row r: the largest b < B with cu[b] + b <= r (cu[b] + b grows
+    // strictly with b in a valid offset array), by a binary search through the scalar cache,
+    // which does not queue behind the row loads.  An invalid array (the finalize kernel
+    // reports it) can only give a draft row that is range-checked here.
+    int lo = 0, hi = a.B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sload_i32(a.cu + mid) + mid <= T.r) lo = mid;
+      else hi = mid;
     }
-  };
-
-  // One ticket at a time: its loads were issued one ticket earlier; after the unpack the loads
-  // of the next ticket go out, then phase 1, the team wait and phase 2.  Residual masses are
-  // stored one ticket late so that no store completion is waited for at the next unpack.
-  uint64_t* mass_ptr = nullptr;
-  uint64_t mass_word = 0;
-  if (w0 < a.n_tickets) issue(decode(w0), true);
-  for (int xt = w0; xt < a.n_tickets; xt += stride) {
-    const Ticket T = decode(xt);
-    float vp[kPerThread], vq[kPerThread];
-    float refp = 0.f, refq = 0.f;
-    unpack_raw<DT>(nxp, vp);
-    if (T.pair) unpack_raw<DT>(nxq, vq);
-    if (VEC && ragged && T.s == n_s - 1) {
-      mask_tail<DT>(a.V, T.s * kChunk, vp);
-      if (T.pair) mask_tail<DT>(a.V, T.s * kChunk, vq);
-    }
-    if (mass_ptr != nullptr && t == kStorer) st_coh(mass_ptr, mass_word);
-    mass_ptr = nullptr;
-    const bool more = xt + stride < a.n_tickets;
-    issue(decode(more ? xt + stride : xt), more);
-    phase1<DT, MODE>(a, L, T, vp, vq, refp, refq);
-    if (MODE == kFuSample && T.pair) {
-      mass_word = phase2(a, L, T.r, refp, refq, vp, vq);
-      mass_ptr = a.smass + (int64_t)T.r * n_s + T.s;
-    }
+    const int b = lo;
+    const int c0 = sload_i32(a.cu + b), c1 = sload_i32(a.cu + b + 1);
+    T.b = b; T.c0 = c0; T.g = c1 - c0; T.i = T.r - c0 - b;
+    drow = T.r - b;
+    T.pair = T.i >= 0 && T.i < T.g && drow >= 0 && drow < a.n_draft_rows;
+    if (VEC)
+      load_raw_buf<DT>(row_rsrc(T.pair ? row_ptr<DT>(a.drf, a.drf_ld, drow) : a.tgt, T.pair ? a.V * kEsz : 0),
+                       T.s * kChunk, rq);
+    else if (T.pair)
+      load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, T.s * kChunk, rq);
   }
-  if (mass_ptr != nullptr && t == kStorer) st_coh(mass_ptr, mass_word);
+  float vp[kPerThread], vq[kPerThread];
+  float refp = 0.f, refq = 0.f;
+  unpack_raw<DT>(rp, vp);
+  if (T.pair) unpack_raw<DT>(rq, vq);
+  if (VEC && (a.V % kChunk) != 0 && T.s == n_s - 1) {
+    mask_tail<DT>(a.V, T.s * kChunk, vp);
+    if (T.pair) mask_tail<DT>(a.V, T.s * kChunk, vq);
+  }
+  phase1<DT, MODE>(a, L, T, vp, vq, refp, refq);
+  if (MODE == kFuSample && T.pair) {
+    const uint64_t mass_word = phase2(a, L, T.r, refp, refq, vp, vq);
+    if (t == kStorer) st_coh(a.smass + (int64_t)T.r * n_s + T.s, mass_word);
+  }
 }
 
 // One workgroup per request, after the streaming kernel: every record is in place.
@@ -927,49 +934,32 @@ __global__ __launch_bounds__(kThreads) void k_fused_finalize(FusedArgs a) {
 // ---------------------------------------------------------------- launch
 
 template <int DT, bool VEC, int MODE>
-static hipError_t launch_fused_t(FusedArgs a, hipStream_t st) {
-  const void* fn = (const void*)k_fused<DT, VEC, MODE>;
-  static int cached_dev = -1, cached_grid = 0;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev != cached_dev) {
-    int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    if (per_cu < 1) return hipErrorInvalidConfiguration;
-    cached_grid = per_cu * cus;
-    cached_dev = dev;
-  }
-  int grid = cached_grid;
-  if (const char* g = getenv("SPEC_VERIFY_GRID")) {   // debug: a smaller resident grid
-    const int want = atoi(g);
-    if (want > 0 && want < grid) grid = want;
-  }
-  if (grid > a.n_tickets) grid = a.n_tickets;
-  if (grid < 1) return hipErrorInvalidConfiguration;
+static hipError_t launch_fused_t(FusedArgs a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  const int teams8 = (a.n_teams + 7) / 8;
+  const long long grid = 8ll * teams8 * a.n_s;
+  if (grid < 1 || grid > 0x7fffffffll) return hipErrorInvalidConfiguration;
   a.n_fin = 0;
   if (getenv("SPEC_VERIFY_DEBUG"))
-    fprintf(stderr, "[specverify] fused grid %d (resident capacity %d) tickets %d slices %d mode %d\n", grid,
-            cached_grid, a.n_tickets, a.n_s, a.mode);
-  void* args[] = {&a};
-  e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, st);
+    fprintf(stderr, "[specverify] fused grid %lld tickets %d slices %d mode %d\n", grid, a.n_tickets, a.n_s, a.mode);
+  // optional events bracket the streaming kernel alone (benchmark timing)
+  if (ev0 && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_fused<DT, VEC, MODE>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_fused_finalize<DT, VEC, MODE>), dim3(a.B), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fused(const FusedArgs& a, int dt, int vec, hipStream_t st) {
+hipError_t launch_fused(const FusedArgs& a, int dt, int vec, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (dt == kDtBF16) {
-    if (a.mode == kFuSample) return vec ? launch_fused_t<kDtBF16, true, kFuSample>(a, st) : launch_fused_t<kDtBF16, false, kFuSample>(a, st);
-    if (a.mode == kFuTokenOnly) return vec ? launch_fused_t<kDtBF16, true, kFuTokenOnly>(a, st) : launch_fused_t<kDtBF16, false, kFuTokenOnly>(a, st);
-    return vec ? launch_fused_t<kDtBF16, true, kFuGreedy>(a, st) : launch_fused_t<kDtBF16, false, kFuGreedy>(a, st);
+    if (a.mode == kFuSample) return vec ? launch_fused_t<kDtBF16, true, kFuSample>(a, st, ev0, ev1) : launch_fused_t<kDtBF16, false, kFuSample>(a, st, ev0, ev1);
+    if (a.mode == kFuTokenOnly) return vec ? launch_fused_t<kDtBF16, true, kFuTokenOnly>(a, st, ev0, ev1) : launch_fused_t<kDtBF16, false, kFuTokenOnly>(a, st, ev0, ev1);
+    return vec ? launch_fused_t<kDtBF16, true, kFuGreedy>(a, st, ev0, ev1) : launch_fused_t<kDtBF16, false, kFuGreedy>(a, st, ev0, ev1);
   }
-  if (a.mode == kFuSample) return vec ? launch_fused_t<kDtF32, true, kFuSample>(a, st) : launch_fused_t<kDtF32, false, kFuSample>(a, st);
-  if (a.mode == kFuTokenOnly) return vec ? launch_fused_t<kDtF32, true, kFuTokenOnly>(a, st) : launch_fused_t<kDtF32, false, kFuTokenOnly>(a, st);
-  return vec ? launch_fused_t<kDtF32, true, kFuGreedy>(a, st) : launch_fused_t<kDtF32, false, kFuGreedy>(a, st);
+  if (a.mode == kFuSample) return vec ? launch_fused_t<kDtF32, true, kFuSample>(a, st, ev0, ev1) : launch_fused_t<kDtF32, false, kFuSample>(a, st, ev0, ev1);
+  if (a.mode == kFuTokenOnly) return vec ? launch_fused_t<kDtF32, true, kFuTokenOnly>(a, st, ev0, ev1) : launch_fused_t<kDtF32, false, kFuTokenOnly>(a, st, ev0, ev1);
+  return vec ? launch_fused_t<kDtF32, true, kFuGreedy>(a, st, ev0, ev1) : launch_fused_t<kDtF32, false, kFuGreedy>(a, st, ev0, ev1);
 }
 
 size_t fused_record_bytes() { return 16; }

@@ -120,6 +120,9 @@ struct FusedArgs {
   uint64_t seed, step;
   uint64_t* part;       // [n_teams][n_s][2 rows][3 words] tagged slice records
   uint64_t* smass;      // [n_teams][n_s] tagged residual masses
+  uint32_t* arrive;     // [n_teams][n_s] the call's tag once a slice's records are visible
+  int poll_delay;       // wait before the first team poll, in 10 ns ticks
+  int poll_pause;       // pause between polls (0: growing)
   int32_t* out_tokens;
   int32_t* out_num_accepted;
   float* out_req_stats;
@@ -127,7 +130,7 @@ struct FusedArgs {
   PosStatsOut st;
 };
 
-hipError_t launch_fused(const FusedArgs& a, int dt, int vec, hipStream_t st);
+hipError_t launch_fused(const FusedArgs& a, int dt, int vec, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_check_cu(const int32_t* cu, int B, int G, int n_draft_rows, int* cu_bad, hipStream_t st);
 size_t fused_record_bytes();
 
