@@ -1,35 +1,36 @@
-// spec_fused.hip -- a whole verification round in one persistent, cooperatively launched kernel.
+// spec_fused.hip -- a whole verification round in two kernels: k_fused streams every needed
+// logit once; k_fused_finalize (one workgroup per request) turns the records into outputs.
 //
 // Work unit ("ticket"): one 4096-logit slice of one target row, together with the same slice
 // of its draft row when that position pairs the two (guide page "5.1 投机解码核心原理", §3.2:
 // the residual needs p and q at the same token).  The slices of one target row form a team.
-// Tickets are numbered team-major and dealt round-robin to the resident workgroups.
+// k_fused runs one workgroup per ticket; workgroup i lands on XCD i mod 8 (the dispatcher deals
+// workgroups round-robin over the XCDs) and the slices of team r are consecutive workgroups of
+// XCD r mod 8.
 //
-// Per ticket every needed logit is read from HBM exactly once:
-//   1. load the slice(s) into registers; slice max; e = exp2(l c - ref), ref = max * c;
-//      publish the slice record (ref, sum e, sum e t) of each row;
-//   2. paired positions: wait until every slice record of the team is present, combine them in
-//      a fixed order (fp64) and form the slice's residual mass sum [p - q]_+ from the
-//      registers, p = e_p alpha_p, q = e_q alpha_q (§3.2, §4.1: beta = sum [p - q]_+);
+// Per ticket:
+//   1. load the slice(s) into registers (bounds-checked buffer loads); per wave, max and
+//      e = exp2(l c - ref_w), ref_w = max * c, sums; fold the waves into one record per row
+//      (ref, sum e, sum e t) and publish it, then an arrival flag;
+//   2. paired positions: wait for the team's arrival flags, combine the team's records in
+//      fp64 (normalisers) and form the slice's residual mass sum [p - q]_+ from the e-values
+//      kept in registers, p = e_p alpha_p, q = e_q alpha_q (§3.2, §4.1: beta = sum [p - q]_+);
 //      publish it.
-// A workgroup runs phase 1 of its next ticket before phase 2 of the current one, so the team
-// wait overlaps useful work, and the loads of the ticket after that are already in flight.
-// A few finalizer workgroups take the requests round-robin as they complete: wait for every
-// record of the request, combine the team statistics (normaliser, entropy in bits and max
-// probability as in the SpecKV page's signals, beta), run the accept scan (§3.1 / §3.2, stop
+// k_fused_finalize combines the team statistics (normaliser, entropy in bits and max
+// probability as in the SpecKV page's signals, beta), runs the accept scan (§3.1 / §3.2, stop
 // at the first rejection §5.1) and the three-level sampler over the residual or p_{g+1}
-// (§5.2, one re-read chunk), and write the outputs.
+// (§5.2, one re-read chunk), and writes the outputs.
 //
-// Synchronisation without read-modify-write atomics: every record carries the call's tag (a
-// per-call sequence number, never 0) in each of its 64-bit words and travels through
-// coherent agent-scope loads and stores; a reader polls until every word it needs carries the
-// current tag.  (Same-address atomics serialise across the XCDs, and acquire / release fences
-// write back and invalidate the whole L2, so neither is used.)
-// Deadlock freedom: the launch is cooperative, so every workgroup is resident.  A workgroup
-// publishes ticket k only after the team wait of ticket k - 2, whose team is lower; so the
-// lowest team still waiting has every member published or about to be, and completes.  The
-// finalizers wait only on streaming workgroups, never the reverse.  Every wait is bounded; one that expires
-// reports SPEC_STATUS_TIMEOUT for its request.
+// Synchronisation without read-modify-write atomics: records and flags carry the call's tag (a
+// per-call sequence number, never 0) and travel through coherent agent-scope (sc1) loads and
+// stores; a 16-byte record also carries a check word mixing the tag with its contents, so a
+// stale or half-written record is never taken.  Polls are few and late: device-scope loads
+// compete with the row stream.
+// Progress: a workgroup waits only for the other slices of its own team, dispatched just before
+// or after it on the same XCD.  Workgroups of an XCD are dispatched in order, and a team has
+// far fewer members than an XCD has resident slots, so the oldest waiting team always has every
+// member resident or finished.  Every wait is also bounded: one that expires reports
+// SPEC_STATUS_TIMEOUT for its request instead of hanging.
 #include <stdio.h>
 #include <stdlib.h>
 
