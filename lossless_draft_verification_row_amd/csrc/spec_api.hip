@@ -105,6 +105,19 @@ bool fused_ok(int B, int V, int gamma_max) {
          !getenv_flag("SPEC_VERIFY_NO_FUSED");
 }
 
+// The sparse filtered path: T > 0 with top-k on (1 <= k <= 256, k < V; top-p optional), the
+// fused path's shape limits.  Top-p alone, or a larger k, is not supported.
+bool filter_supported(int B, int V, int gamma_max, const spec_sampling_params& sp) {
+  return sp.temperature > 0.f && sp.top_k >= 1 && sp.top_k < V && sp.top_k <= kFilterMaxK && B <= kMaxReqFused &&
+         (int64_t)B * (gamma_max + 1) <= kMaxTeamsFused && n_chunks(V) <= kMaxSlicesFused;
+}
+size_t filter_bytes(int64_t n_slots, int V, int k) {
+  const int64_t ns = n_chunks(V);
+  return kHeaderBytes + align_up((size_t)(n_slots * ns * filter_cap(k)) * sizeof(CandEntry)) +
+         align_up((size_t)(n_slots * ns) * sizeof(CandHead)) + align_up((size_t)n_slots * kKeepMax * sizeof(KeptEntry)) +
+         align_up((size_t)n_slots * sizeof(RowStat2));
+}
+
 float exp2_scale(const spec_sampling_params& sp) {
   return sp.temperature > 0.f ? (float)(1.4426950408889634 / (double)sp.temperature) : 0.f;
 }
@@ -146,7 +159,8 @@ int spec_set_profile_events(void* start_event, void* stop_event) {
 size_t spec_verify_workspace_bytes(int B, int V, int gamma_max, spec_dtype dt, spec_sampling_params sp) {
   (void)dt;
   if (B <= 0 || V <= 0 || gamma_max < 0) return 0;
-  if (filter_on(V, sp)) return 0;
+  if (filter_on(V, sp))
+    return filter_supported(B, V, gamma_max, sp) ? filter_bytes((int64_t)B * (2 * gamma_max + 1), V, sp.top_k) : 0;
   const size_t dense = dense_bytes((int64_t)B * (gamma_max + 1), V);
   const size_t fused = fused_bytes((int64_t)B * (gamma_max + 1), V);
   return dense > fused ? dense : fused;
@@ -184,7 +198,8 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   if (draft_logits && draft_ld < V) return SPEC_ERR_INVALID;
   if ((int64_t)B * (gamma_max + 1) * 2 > (int64_t)INT32_MAX / 2) return SPEC_ERR_INVALID;
   const bool greedy = sp.temperature == 0.f;
-  if (filter_on(V, sp)) return SPEC_ERR_UNSUPPORTED;
+  const bool filtered = filter_on(V, sp);
+  if (filtered && !filter_supported(B, V, gamma_max, sp)) return SPEC_ERR_UNSUPPORTED;
   const size_t need = spec_verify_workspace_bytes(B, V, gamma_max, dt, sp);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SPEC_ERR_WORKSPACE;
   if (((uintptr_t)workspace % kAlign) != 0) return SPEC_ERR_INVALID;
@@ -208,6 +223,49 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   char* ws = (char*)workspace;
   const int dtc = dt == SPEC_BF16 ? kDtBF16 : kDtF32;
   const bool vec = aligned16(target_logits, target_ld, dt) && aligned16(drf, draft_ld, dt);
+  if (filtered) {
+    FilterArgs f;
+    memset(&f, 0, sizeof(f));
+    f.tgt = target_logits;
+    f.tgt_ld = target_ld;
+    f.drf = drf;
+    f.drf_ld = draft_ld;
+    f.cu = cu_draft;
+    f.tokens = draft_tokens;
+    f.B = B;
+    f.G = gamma_max;
+    f.V = V;
+    f.n_s = ns;
+    f.n_draft_rows = n_draft_rows;
+    f.n_teams = n_draft_rows + B;
+    f.mode = drf ? kFuSample : kFuTokenOnly;
+    f.n_slots = f.n_teams + (drf ? n_draft_rows : 0);
+    f.k = sp.top_k;
+    f.cap = filter_cap(sp.top_k);
+    f.top_p = sp.top_p;
+    f.c = 1.4426950408889634 / (double)sp.temperature;
+    f.inv_t = 1.0 / (double)sp.temperature;
+    f.seed = seed;
+    f.step = step;
+    Carve cv{ws};
+    f.cand = cv.take<CandEntry>((size_t)f.n_slots * ns * f.cap * sizeof(CandEntry));
+    f.chead = cv.take<CandHead>((size_t)f.n_slots * ns * sizeof(CandHead));
+    f.kept = cv.take<KeptEntry>((size_t)f.n_slots * kKeepMax * sizeof(KeptEntry));
+    f.rstat = cv.take<RowStat2>((size_t)f.n_slots * sizeof(RowStat2));
+    f.out_tokens = out_tokens;
+    f.out_num_accepted = out_num_accepted;
+    f.out_req_stats = out_req_stats;
+    f.out_status = out_status;
+    f.st.p_y = pos_stats.p_y;
+    f.st.q_y = pos_stats.q_y;
+    f.st.one_minus_tv = pos_stats.one_minus_tv;
+    f.st.draft_entropy_bits = pos_stats.draft_entropy_bits;
+    f.st.draft_max_prob = pos_stats.draft_max_prob;
+    f.st.target_entropy_bits = pos_stats.target_entropy_bits;
+    f.st.target_max_prob = pos_stats.target_max_prob;
+    const hipError_t e = launch_filter(f, dtc, vec, st, g_prof_start, g_prof_stop);
+    return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
+  }
   if (fused_ok(B, V, gamma_max)) {
     FusedArgs f;
     memset(&f, 0, sizeof(f));

@@ -405,4 +405,93 @@ __device__ __forceinline__ TeamStat load_team(const TeamStat* p) {
   return v;
 }
 
+// ---------------------------------------------------------------- scalar loads
+
+// A uniform 32-bit load through the scalar data cache (read-only data of the call).
+__device__ __forceinline__ int sload_i32(const int32_t* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
+// ---------------------------------------------------------------- wave-wide fp64 helpers
+
+// 64-bit DPP move of both halves (lanes whose source is outside the row, or rows outside
+// RMASK, read 0).
+template <int CTRL, int RMASK>
+__device__ __forceinline__ double dpp_d(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, RMASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, RMASK, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, lane), hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+// fp64 sum over the wave in a fixed order (row reductions, then row broadcasts); every lane
+// gets lane 63's total.
+__device__ __forceinline__ double wave_sum_dpp_d(double v) {
+  v += dpp_d<0xb1, 0xf>(v);
+  v += dpp_d<0x4e, 0xf>(v);
+  v += dpp_d<0x124, 0xf>(v);
+  v += dpp_d<0x128, 0xf>(v);
+  v += dpp_d<0x142, 0xa>(v);
+  v += dpp_d<0x143, 0xc>(v);
+  return readlane_d(v, 63);
+}
+// Inclusive fp64 prefix sum over the wave's lanes (row shifts, then row broadcasts).
+__device__ __forceinline__ double wave_scan_dpp_d(double v) {
+  v += dpp_d<0x111, 0xf>(v);   // row_shr:1
+  v += dpp_d<0x112, 0xf>(v);   // row_shr:2
+  v += dpp_d<0x114, 0xf>(v);   // row_shr:4
+  v += dpp_d<0x118, 0xf>(v);   // row_shr:8
+  v += dpp_d<0x142, 0xa>(v);   // row_bcast:15
+  v += dpp_d<0x143, 0xc>(v);   // row_bcast:31
+  return v;
+}
+// Inverse-CDF pick over the masses held one per lane (lanes >= n hold 0): the first index
+// whose prefix sum exceeds u * total; if rounding leaves none, the last index with positive
+// mass; -1 when the total is not positive.  Returns the pick; `total` gets the sum.
+__device__ __forceinline__ int wave_pick(double m, int n, double u, double& total) {
+  const int lane = threadIdx.x & 63;
+  const bool in = lane < n;
+  const double cum = wave_scan_dpp_d(in ? m : 0.0);
+  total = readlane_d(cum, 63);
+  if (!(total > 0.0)) return -1;
+  const double target = u * total;
+  const unsigned long long over = __ballot(in && cum > target);
+  if (over) return __builtin_ctzll(over);
+  const unsigned long long pos = __ballot(in && m > 0.0);
+  return pos ? 63 - __builtin_clzll(pos) : -1;
+}
+
+// ---------------------------------------------------------------- bounds-checked row loads
+
+// Bounds-checked row loads: a buffer resource over the row's bytes.  16-byte loads past the
+// end return zeros and touch no memory (num_records 0 turns every load off).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, nbytes, 0x00020000);
+}
+template <int DT>
+__device__ __forceinline__ void load_raw_buf(__amdgpu_buffer_rsrc_t rs, int base, RawSlice<DT>& r) {
+  const int t = threadIdx.x;
+  constexpr int kEl = DT == kDtBF16 ? 8 : 4;      // elements per 16-byte vector
+  constexpr int kEsz = DT == kDtBF16 ? 2 : 4;
+#pragma unroll
+  for (int k = 0; k < kPerThread / kEl; ++k) {
+    const int e0 = base + kEl * (t + kThreads * k);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, e0 * kEsz, 0, 0);
+    r.w[4 * k + 0] = x[0]; r.w[4 * k + 1] = x[1]; r.w[4 * k + 2] = x[2]; r.w[4 * k + 3] = x[3];
+  }
+}
+// Logits at indices >= V (zeros from the bounds check) become -inf.
+template <int DT>
+__device__ __forceinline__ void mask_tail(int V, int base, float (&v)[kPerThread]) {
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    if (slice_index<DT>(base, threadIdx.x, j) >= V) v[j] = -INFINITY;
+}
+
 }  // namespace specv

@@ -1,0 +1,700 @@
+// spec_filter.hip -- verification with top-k / top-p filtered distributions.
+//
+// With top-k on (1 <= k <= 256), every filtered distribution lives on the k largest logits of
+// its row (ties at the boundary kept, reading R1 of the oracle), so after one streaming pass the
+// whole method runs on small sparse sets:
+//   k_filt_slices   one workgroup per 4096-logit slice of a target row and, for a paired
+//                   position, the same slice of its draft row: the slice's own k-th largest
+//                   value by a two- (bf16) or four-pass (fp32) radix select over order keys in
+//                   an LDS histogram, then every logit at or above it written out as a candidate
+//                   (value, index).  Each needed logit is read once; nothing waits on another
+//                   workgroup.
+//   k_filt_rows     one workgroup per row: the row's k-th largest among its slices' candidates
+//                   (the same select), the top-k set K, top-p on the renormalised K by pairwise
+//                   masses (no sort), the kept set S with p = e / Z_S in fp64, entropy in bits,
+//                   max probability, log Z (guide page "5.1 投机解码核心原理" §2.1: p and q are
+//                   the distributions after temperature, top-k, top-p; SpecKV page signals).
+//   k_filt_finalize one workgroup per request: p(y), q(y), 1 - TV = sum min(p, q) (§4.1, §4.3),
+//                   the accept scan (§3.2, §5.1) and the three-level sampler over the residual
+//                   [p - q]_+ or p_{g+1} (§3.2, §5.2) on the sparse kept sets, with the
+//                   sampler's sequential fp64 sums taken in index order.
+// A slice keeps at most `cap` candidates, those strictly above its threshold first; if it had
+// to drop ties that the row's own threshold would keep, or a row's top-k set exceeds kKeepMax,
+// the request reports SPEC_STATUS_FILTER_OVERFLOW instead of a result.
+#include "spec_device.h"
+#include "spec_internal.h"
+
+namespace specv {
+
+constexpr int kFlagBad = 1;        // a NaN or +inf logit in the row
+constexpr int kFlagOverflow = 2;   // the sparse sets could not hold the row
+constexpr int kFlagEmpty = 4;      // no finite logit in the row
+
+// Order key of a logit: unsigned, larger key = larger value; -0 and +0 share a key.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// The top 8 * NPASS bits of a key, right-aligned: for bf16 logits (NPASS = 2) they fix the
+// value, for fp32 (NPASS = 4) they are the key.
+template <int NPASS>
+__device__ __forceinline__ uint32_t key_hi(uint32_t k) {
+  return NPASS == 4 ? k : (k >> (32 - 8 * NPASS));
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
+  return v;
+}
+
+struct SelLds {
+  uint32_t hist[256];
+  int wtot[2][kWaves];
+  int digit, above, total;
+};
+
+// One pass of the block-wide radix select: `cnt(d)` for the keys whose higher digits match
+// `prefix` must already be in S.hist.  Wave 0 finds the digit d holding the kk-th largest
+// (counting from the top) and the number of keys above it.  Returns false (with the total)
+// when fewer than kk keys were counted.
+__device__ __forceinline__ void select_digit(SelLds& S, int kk) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    int c[4], s = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { c[q] = (int)S.hist[255 - 4 * lane - q]; s += c[q]; }
+    const int incl = wave_incl_scan_i(s);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    const unsigned long long hit = __ballot(incl >= kk);
+    if (lane == 0) { S.total = total; S.digit = -1; S.above = 0; }
+    if (hit && total >= kk) {
+      const int L = __builtin_ctzll(hit);
+      if (lane == L) {
+        int run = incl - s;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (run + c[q] >= kk) { S.digit = 255 - 4 * lane - q; S.above = run; break; }
+          run += c[q];
+        }
+      }
+    }
+  }
+}
+
+// Block-wide: the top 8 * NPASS bits of the k-th largest key among the valid keys (with
+// multiplicity).  for_each(cb) calls cb(key, valid) for every key this thread holds.  `all`
+// is set when fewer than k keys are valid (every valid key then qualifies).
+template <int NPASS, typename ForEach>
+__device__ uint32_t block_select(int k, SelLds& S, ForEach for_each, bool& all, int& n_valid) {
+  const int t = threadIdx.x;
+  uint32_t prefix = 0;
+  int kk = k;
+  all = false;
+  n_valid = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < NPASS; ++pass) {
+    const int sh = 8 * (NPASS - 1 - pass);   // digit position within key_hi
+    S.hist[t] = 0u;
+    __syncthreads();
+    for_each([&](uint32_t key, bool valid) {
+      const uint32_t h = key_hi<NPASS>(key);
+      if (valid && (pass == 0 || (h >> (sh + 8)) == prefix)) atomicAdd(&S.hist[(h >> sh) & 255u], 1u);
+    });
+    __syncthreads();
+    select_digit(S, kk);
+    __syncthreads();
+    const int d = S.digit;
+    if (pass == 0) n_valid = S.total;
+    __syncthreads();
+    if (d < 0) { all = true; return 0u; }
+    prefix = (prefix << 8) | (uint32_t)d;
+    kk -= S.above;
+  }
+  return prefix;
+}
+
+// Exclusive block scan of two counters; returns the totals through a and b.
+__device__ __forceinline__ void block_scan2(int& a, int& b, SelLds& S, int& ta, int& tb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ia = wave_incl_scan_i(a), ib = wave_incl_scan_i(b);
+  if (lane == 63) { S.wtot[0][wave] = ia; S.wtot[1][wave] = ib; }
+  __syncthreads();
+  int oa = 0, ob = 0;
+  ta = 0; tb = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) { oa += S.wtot[0][w]; ob += S.wtot[1][w]; }
+    ta += S.wtot[0][w];
+    tb += S.wtot[1][w];
+  }
+  a = oa + ia - a;
+  b = ob + ib - b;
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- k_filt_slices
+
+// Candidates of one row's slice: the values at or above the slice's k-th largest, the ones
+// strictly above first.  Header {stored, total, threshold digits, flags}.
+template <int DT>
+__device__ void slice_candidates(const FilterArgs& a, SelLds& S, const float (&v)[kPerThread], int slot, int s,
+                                 int base) {
+  constexpr int NP = DT == kDtBF16 ? 2 : 4;
+  const int t = threadIdx.x;
+  int bad = 0;
+  uint32_t key[kPerThread];
+  bool valid[kPerThread];
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    bad |= __builtin_amdgcn_class(v[j], 0x203) ? 1 : 0;   // NaN, +inf
+    valid[j] = v[j] > -INFINITY && v[j] < INFINITY;
+    key[j] = order_key(v[j]);
+  }
+  bad = block_or(bad, S.wtot[0]);
+  bool all;
+  int nv;
+  const uint32_t th = block_select<NP>(a.k, S,
+                                       [&](auto cb) {
+#pragma unroll
+                                         for (int j = 0; j < kPerThread; ++j) cb(key[j], valid[j]);
+                                       }, all, nv);
+  int ng = 0, ne = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    if (!valid[j]) continue;
+    const uint32_t h = key_hi<NP>(key[j]);
+    if (all || h > th) ++ng;
+    else if (h == th) ++ne;
+  }
+  int og = ng, oe = ne, tg, te;
+  block_scan2(og, oe, S, tg, te);
+  const int cap = a.cap;
+  CandEntry* out = a.cand + ((int64_t)slot * a.n_s + s) * cap;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    if (!valid[j]) continue;
+    const uint32_t h = key_hi<NP>(key[j]);
+    int pos = -1;
+    if (all || h > th) pos = og++;
+    else if (h == th) pos = tg + oe++;
+    if (pos >= 0 && pos < cap) {
+      CandEntry c;
+      c.v = v[j];
+      c.x = slice_index<DT>(base, t, j);
+      out[pos] = c;
+    }
+  }
+  if (t == 0) {
+    CandHead hd;
+    hd.total = tg + te;
+    hd.stored = min(tg + te, cap);
+    hd.th = all ? 0u : th;
+    hd.flags = (bad ? kFlagBad : 0) | (all ? 8 : 0);
+    a.chead[(int64_t)slot * a.n_s + s] = hd;
+  }
+  __syncthreads();
+}
+
+template <int DT, bool VEC, bool PAIRED>
+__global__ __launch_bounds__(kThreads) void k_filt_slices(FilterArgs a) {
+  __shared__ SelLds S;
+  const int t = threadIdx.x;
+  const int n_s = a.n_s;
+  const int r = blockIdx.x / n_s, s = blockIdx.x - (blockIdx.x / n_s) * n_s;
+  if (r >= a.n_teams) return;
+  constexpr int kEsz = DT == kDtBF16 ? 2 : 4;
+  const int base = s * kChunk;
+  RawSlice<DT> raw;
+  float v[kPerThread];
+  if (VEC) load_raw_buf<DT>(row_rsrc(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V * kEsz), base, raw);
+  else load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, base, raw);
+  // the draft row of target row r, if r is not the last row of its request
+  int drow = -1;
+  if (PAIRED) {
+    int lo = 0, hi = a.B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sload_i32(a.cu + mid) + mid <= r) lo = mid;
+      else hi = mid;
+    }
+    const int c0 = sload_i32(a.cu + lo), c1 = sload_i32(a.cu + lo + 1);
+    const int i = r - c0 - lo;
+    if (i >= 0 && i < c1 - c0 && r - lo >= 0 && r - lo < a.n_draft_rows) drow = r - lo;
+  }
+  unpack_raw<DT>(raw, v);
+  if (VEC && (a.V % kChunk) != 0 && s == n_s - 1) mask_tail<DT>(a.V, base, v);
+  slice_candidates<DT>(a, S, v, r, s, base);
+  if (PAIRED && drow >= 0) {
+    if (VEC) load_raw_buf<DT>(row_rsrc(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V * kEsz), base, raw);
+    else load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base, raw);
+    unpack_raw<DT>(raw, v);
+    if (VEC && (a.V % kChunk) != 0 && s == n_s - 1) mask_tail<DT>(a.V, base, v);
+    slice_candidates<DT>(a, S, v, a.n_teams + drow, s, base);
+  }
+  (void)t;
+}
+
+// ---------------------------------------------------------------- k_filt_rows
+
+struct RowLds {
+  SelLds sel;
+  int cnt[kMaxSlicesFused + 1];
+  int off[kMaxSlicesFused + 1];
+  float kv[kKeepMax];
+  int kx[kKeepMax];
+  double ke[kKeepMax];
+  int keep[kKeepMax];
+  double red[kWaves];
+  int flags, nk, ns;
+};
+
+__device__ __forceinline__ double block_sum_dd(double v, double* red) {
+  v = wave_sum_dpp_d(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+// One row: global top-k over the slices' candidates, top-p, the kept set with probabilities.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_filt_rows(FilterArgs a) {
+  constexpr int NP = DT == kDtBF16 ? 2 : 4;
+  __shared__ RowLds L;
+  const int t = threadIdx.x;
+  const int slot = blockIdx.x;
+  if (slot >= a.n_slots) return;
+  const int n_s = a.n_s, cap = a.cap;
+  const CandHead* hd = a.chead + (int64_t)slot * n_s;
+  const CandEntry* cd = a.cand + (int64_t)slot * n_s * cap;
+  if (t == 0) {
+    int fl = 0, off = 0;
+    for (int s = 0; s < n_s; ++s) {
+      const CandHead h = hd[s];
+      if (h.flags & kFlagBad) fl |= kFlagBad;
+      L.cnt[s] = h.stored;
+      L.off[s] = off;
+      off += h.stored;
+    }
+    L.off[n_s] = off;
+    L.flags = fl;
+  }
+  __syncthreads();
+  const int n = L.off[n_s];
+  // candidate j lives in slice s with off[s] <= j < off[s] + cnt[s]; entries of slice s sit at
+  // cd[s * cap + (j - off[s])]
+  auto at = [&](int j) -> const CandEntry& {
+    int lo = 0, hi = n_s;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (L.off[mid] <= j) lo = mid;
+      else hi = mid;
+    }
+    return cd[(int64_t)lo * cap + (j - L.off[lo])];
+  };
+  bool all;
+  int nv;
+  const uint32_t th = block_select<NP>(a.k, L.sel,
+                                       [&](auto cb) {
+                                         for (int j = t; j < n; j += kThreads) cb(order_key(at(j).v), true);
+                                       }, all, nv);
+  // dropped ties of a slice hold its threshold digits; they belong to K if those reach th
+  if (t < n_s) {
+    const CandHead h = hd[t];
+    if (h.total > h.stored && (all || h.th >= th)) atomicOr(&L.flags, kFlagOverflow);
+  }
+  // the top-k set K, compacted in candidate order
+  int mine = 0;
+  for (int j = t; j < n; j += kThreads) mine += (all || key_hi<NP>(order_key(at(j).v)) >= th) ? 1 : 0;
+  int o = mine, dummy = 0, nk, tz;
+  block_scan2(o, dummy, L.sel, nk, tz);
+  if (nk > kKeepMax) { if (t == 0) L.flags |= kFlagOverflow; }
+  else {
+    for (int j = t; j < n; j += kThreads) {
+      const CandEntry c = at(j);
+      if (all || key_hi<NP>(order_key(c.v)) >= th) { L.kv[o] = c.v; L.kx[o] = c.x; ++o; }
+    }
+  }
+  if (t == 0) L.nk = nk;
+  __syncthreads();
+  RowStat2 st;
+  st.n = 0; st.flags = L.flags; st.m = -INFINITY; st.argmax = -1;
+  st.log_z = 0.0; st.entropy = 0.0; st.max_prob = 0.0; st.z = 0.0;
+  if (nk == 0 && !(st.flags & kFlagBad)) st.flags |= kFlagEmpty;
+  if (st.flags) {
+    if (t == 0) a.rstat[slot] = st;
+    return;
+  }
+  // maximum (lowest index among equal maxima)
+  float m = -INFINITY;
+  for (int j = t; j < nk; j += kThreads) m = fmaxf(m, L.kv[j]);
+  m = block_max(m, (float*)L.red);
+  int amx = INT_MAX;
+  for (int j = t; j < nk; j += kThreads) if (L.kv[j] == m) amx = min(amx, L.kx[j]);
+  amx = block_min_i(amx, (int*)L.red);
+  // e = exp((l - m) / T) in fp64; Z_K
+  const double cd2 = (double)a.c;   // log2(e) / T
+  double zk = 0.0;
+  for (int j = t; j < nk; j += kThreads) {
+    const double e = exp2_split(((double)L.kv[j] - (double)m) * cd2);
+    L.ke[j] = e;
+    zk += e;
+  }
+  __syncthreads();
+  zk = block_sum_dd(zk, L.red);
+  // top-p: keep x iff the mass of values strictly above l_x is below top_p (the value group
+  // that first reaches top_p is kept whole; reading R1)
+  for (int j = t; j < nk; j += kThreads) {
+    int keep = 1;
+    if (a.top_p < 1.f) {
+      const float lx = L.kv[j];
+      double above = 0.0;
+      for (int y = 0; y < nk; ++y) above += (L.kv[y] > lx) ? L.ke[y] : 0.0;
+      keep = (above / zk < (double)a.top_p) ? 1 : 0;
+    }
+    L.keep[j] = keep;
+  }
+  __syncthreads();
+  // Z_S, then p, entropy, the index order of S
+  double zs = 0.0;
+  int ns_t = 0;
+  for (int j = t; j < nk; j += kThreads) if (L.keep[j]) { zs += L.ke[j]; ++ns_t; }
+  zs = block_sum_dd(zs, L.red);
+  int ns = ns_t, d2 = 0, ns_all, tz2;
+  block_scan2(ns, d2, L.sel, ns_all, tz2);
+  double ent = 0.0;
+  KeptEntry* kept = a.kept + (int64_t)slot * kKeepMax;
+  for (int j = t; j < nk; j += kThreads) {
+    if (!L.keep[j]) continue;
+    const double p = L.ke[j] / zs;
+    if (p > 0.0) ent -= p * log2_split(p);
+    const int xj = L.kx[j];
+    int rank = 0;
+    for (int y = 0; y < nk; ++y) rank += (L.keep[y] && L.kx[y] < xj) ? 1 : 0;
+    KeptEntry ke;
+    ke.x = xj;
+    ke.p = p;
+    kept[rank] = ke;
+  }
+  ent = block_sum_dd(ent, L.red);
+  if (t == 0) {
+    st.n = ns_all;
+    st.m = m;
+    st.argmax = amx;
+    st.z = zs;
+    st.log_z = (double)m * (double)a.inv_t + log2_split(zs) * 0.6931471805599453;
+    st.entropy = ent;
+    st.max_prob = 1.0 / zs;
+    a.rstat[slot] = st;
+  }
+}
+
+// ---------------------------------------------------------------- k_filt_finalize
+
+struct FinFLds {
+  double py[kMaxGamma + 1], qy[kMaxGamma + 1], u0[kMaxGamma];
+  int ytok[kMaxGamma];
+  float dh[kMaxGamma], dm[kMaxGamma];
+  double chunk[kMaxSlicesFused];
+  int flags, status, n_acc, pos, wkind, y;
+  double u[3];
+  int x;
+};
+
+// p of token x in a kept list sorted by index (0 when x is not kept).
+__device__ __forceinline__ double kept_p(const KeptEntry* ke, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (ke[mid].x < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return (lo < n && ke[lo].x == x) ? ke[lo].p : 0.0;
+}
+
+// First index whose running sum exceeds target (the last positive one if rounding leaves
+// none); sums run in the order given.
+template <typename W>
+__device__ __forceinline__ int seq_pick(int n, double target, W w) {
+  double cum = 0.0;
+  int last = -1;
+  for (int i = 0; i < n; ++i) {
+    const double wi = w(i);
+    cum += wi;
+    if (wi > 0.0) last = i;
+    if (cum > target) return i;
+  }
+  return last;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
+  __shared__ FinFLds F;
+  __shared__ int cu_s[kMaxReqFused + 1];
+  __shared__ int red_i[8];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int b = blockIdx.x;
+  const float nan = __int_as_float(0x7fc00000);
+  // the draft offsets, checked as one exclusive prefix
+  for (int k = t; k <= a.B; k += kThreads) cu_s[k] = a.cu[k];
+  __syncthreads();
+  int badc = 0;
+  for (int k = t; k < a.B; k += kThreads) {
+    const int g = cu_s[k + 1] - cu_s[k];
+    if (g < 0 || g > a.G) badc = 1;
+  }
+  if (t == 0 && (cu_s[0] != 0 || cu_s[a.B] != a.n_draft_rows)) badc = 1;
+  badc = block_or(badc, red_i);
+  if (badc) {
+    if (t <= a.G) a.out_tokens[(int64_t)b * (a.G + 1) + t] = -1;
+    if (t == 0) {
+      a.out_num_accepted[b] = 0;
+      a.out_status[b] = kStBadGamma;
+      if (a.out_req_stats)
+        for (int q = 0; q < 4; ++q) a.out_req_stats[(int64_t)b * 4 + q] = nan;
+    }
+    return;
+  }
+  const int c0 = cu_s[b], g = cu_s[b + 1] - c0;
+  if (t == 0) F.flags = 0;
+  __syncthreads();
+  // A. per position: the rows' flags and statistics, p(y), q(y), 1 - TV (one wave per position)
+  for (int i = wave; i <= g; i += kWaves) {
+    const int ps = c0 + b + i;
+    const RowStat2 P = a.rstat[ps];
+    const KeptEntry* kp = a.kept + (int64_t)ps * kKeepMax;
+    const bool okp = P.flags == 0;
+    int fl = P.flags;
+    if (i < g) {
+      const int y = a.tokens[c0 + i];
+      const bool yv = y >= 0 && y < a.V;
+      double pyd = 0.0, qyd = 1.0, ov = 0.0;
+      float py = nan, qy = nan, ovl = nan, dh = nan, dm = nan;
+      if (okp && yv) { pyd = kept_p(kp, P.n, y); py = (float)pyd; }
+      if (MODE == kFuSample) {
+        const int qs = a.n_teams + c0 + i;
+        const RowStat2 Q = a.rstat[qs];
+        fl |= Q.flags;
+        const bool okq = Q.flags == 0;
+        const KeptEntry* kq = a.kept + (int64_t)qs * kKeepMax;
+        if (okq && yv) { qyd = kept_p(kq, Q.n, y); qy = (float)qyd; }
+        if (okp && okq) {
+          double part = 0.0;
+          for (int j = lane; j < P.n; j += 64) part += fmin(kp[j].p, kept_p(kq, Q.n, kp[j].x));
+          ov = wave_sum_dpp_d(part);
+          ovl = (float)ov;
+        }
+        if (okq) { dh = (float)Q.entropy; dm = (float)Q.max_prob; }
+      } else {
+        qyd = 1.0;
+        qy = yv ? 1.f : nan;
+        ovl = okp ? (yv ? py : 0.f) : nan;
+        dh = yv ? 0.f : nan;
+        dm = yv ? 1.f : nan;
+      }
+      if (lane == 0) {
+        if (a.st.p_y) a.st.p_y[c0 + i] = py;
+        if (a.st.q_y) a.st.q_y[c0 + i] = qy;
+        if (a.st.one_minus_tv) a.st.one_minus_tv[c0 + i] = ovl;
+        if (a.st.draft_entropy_bits) a.st.draft_entropy_bits[c0 + i] = dh;
+        if (a.st.draft_max_prob) a.st.draft_max_prob[c0 + i] = dm;
+        F.dh[i] = dh;
+        F.dm[i] = dm;
+        F.py[i] = pyd;
+        F.qy[i] = qyd;
+        F.ytok[i] = y;
+        uint64_t w[4];
+        philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(i + 1), 0, 0, w);
+        F.u0[i] = u53(w[0]);
+      }
+    }
+    if (lane == 0) {
+      if (a.st.target_entropy_bits) a.st.target_entropy_bits[ps] = P.flags ? nan : (float)P.entropy;
+      if (a.st.target_max_prob) a.st.target_max_prob[ps] = P.flags ? nan : (float)P.max_prob;
+      if (fl) atomicOr(&F.flags, fl);
+    }
+  }
+  __syncthreads();
+  // B. accept scan and the row to sample (one thread)
+  if (t == 0) {
+    int status = 0, j = -1;
+    if (F.flags & kFlagOverflow) status = kStFilterOverflow;
+    else if (F.flags) status = kStNonfinite;
+    else {
+      for (int i = 0; i < g; ++i) {
+        const int y = F.ytok[i];
+        if (y < 0 || y >= a.V) { status |= kStBadToken; j = i; break; }
+        const double qy = F.qy[i];
+        if (!(qy > 0.0)) { status |= kStZeroQ; j = i; break; }
+        if (!(F.u0[i] < fmin(1.0, F.py[i] / qy))) { j = i; break; }
+      }
+    }
+    F.n_acc = j < 0 ? g : j;
+    F.pos = j < 0 ? g : j;
+    F.y = j >= 0 ? F.ytok[j] : -1;
+    F.wkind = (j < 0) ? 0 : (MODE == kFuSample ? 1 : 2);
+    uint64_t w[4];
+    philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(F.pos + 1), 0, 0, w);
+    F.u[0] = u53(w[1]);
+    F.u[1] = u53(w[2]);
+    F.u[2] = u53(w[3]);
+    F.status = status;
+    F.x = -1;
+    if (a.out_req_stats) {
+      float rq[4] = {nan, nan, nan, nan};
+      if (g > 0) {
+        double hs = 0.0, cs = 0.0;
+        float hmax = -INFINITY, cmin = INFINITY;
+        bool anynan = false;
+        for (int i = 0; i < g; ++i) {
+          const float h = F.dh[i], cm = F.dm[i];
+          if (!(h == h) || !(cm == cm)) anynan = true;
+          hs += h; cs += cm;
+          hmax = fmaxf(hmax, h); cmin = fminf(cmin, cm);
+        }
+        if (!anynan) { rq[0] = (float)(hs / g); rq[1] = (float)(cs / g); rq[2] = hmax; rq[3] = cmin; }
+      }
+      for (int q = 0; q < 4; ++q) a.out_req_stats[(int64_t)b * 4 + q] = rq[q];
+    }
+    // C. the three-level sampler on the sparse weights, sums in index order (reading R6)
+    if (!(status & (kStNonfinite | kStFilterOverflow))) {
+      const int ps = c0 + b + F.pos;
+      const RowStat2 P = a.rstat[ps];
+      const KeptEntry* kp = a.kept + (int64_t)ps * kKeepMax;
+      const KeptEntry* kq = nullptr;
+      int nq = 0;
+      if (MODE == kFuSample && F.pos < g) {
+        const int qs = a.n_teams + c0 + F.pos;
+        kq = a.kept + (int64_t)qs * kKeepMax;
+        nq = a.rstat[qs].n;
+      }
+      int wkind = F.wkind;
+      const int yx = F.y;
+      for (int pass = 0; pass < 2; ++pass) {
+        auto wgt = [&](int j) -> double {
+          const double p = kp[j].p;
+          if (wkind == 1) return fmax(p - kept_p(kq, nq, kp[j].x), 0.0);
+          if (wkind == 2) return kp[j].x == yx ? fmax(p - 1.0, 0.0) : p;
+          return p;
+        };
+        // chunk masses: group masses summed in order, chunk by chunk
+        const int n = P.n;
+        int j = 0;
+        double W = 0.0;
+        for (int k = 0; k < a.n_s; ++k) {
+          double Sk = 0.0;
+          while (j < n && (kp[j].x >> 12) == k) {
+            const int grp = kp[j].x >> 6;
+            double M = 0.0;
+            while (j < n && (kp[j].x >> 6) == grp) { M += wgt(j); ++j; }
+            Sk += M;
+          }
+          F.chunk[k] = Sk;
+          W += Sk;
+        }
+        if (!(W > 0.0)) {
+          if (wkind != 0) { status |= kStResidualEmpty; wkind = 0; continue; }
+          break;
+        }
+        const int kc = seq_pick(a.n_s, F.u[0] * W, [&](int k) { return F.chunk[k]; });
+        // entries of chunk kc and their group masses
+        int j0 = 0;
+        while (j0 < n && (kp[j0].x >> 12) < kc) ++j0;
+        int j1 = j0;
+        while (j1 < n && (kp[j1].x >> 12) == kc) ++j1;
+        double Sg = 0.0;
+        for (int jj = j0; jj < j1;) {
+          const int grp = kp[jj].x >> 6;
+          double M = 0.0;
+          while (jj < j1 && (kp[jj].x >> 6) == grp) { M += wgt(jj); ++jj; }
+          Sg += M;
+        }
+        // level 2 over the chunk's groups (empty groups add nothing)
+        const double t2 = F.u[1] * Sg;
+        double cum = 0.0;
+        int gsel = -1, glast = -1;
+        int gj0 = -1, gj1 = -1, lj0 = -1, lj1 = -1;
+        for (int jj = j0; jj < j1;) {
+          const int grp = kp[jj].x >> 6;
+          const int s0 = jj;
+          double M = 0.0;
+          while (jj < j1 && (kp[jj].x >> 6) == grp) { M += wgt(jj); ++jj; }
+          cum += M;
+          if (M > 0.0) { glast = grp; lj0 = s0; lj1 = jj; }
+          if (cum > t2) { gsel = grp; gj0 = s0; gj1 = jj; break; }
+        }
+        if (gsel < 0) { gsel = glast; gj0 = lj0; gj1 = lj1; }
+        if (gsel >= 0) {
+          double Mg = 0.0;
+          for (int jj = gj0; jj < gj1; ++jj) Mg += wgt(jj);
+          const int e = seq_pick(gj1 - gj0, F.u[2] * Mg, [&](int q) { return wgt(gj0 + q); });
+          F.x = e >= 0 ? kp[gj0 + e].x : -1;
+        }
+        break;
+      }
+      F.status = status;
+    }
+  }
+  __syncthreads();
+  const bool ok = !(F.status & (kStNonfinite | kStFilterOverflow));
+  if (t <= a.G) {
+    int tok = -1;
+    if (ok) {
+      if (t < F.n_acc) tok = F.ytok[t];
+      else if (t == F.n_acc) tok = F.x;
+    }
+    a.out_tokens[(int64_t)b * (a.G + 1) + t] = tok;
+  }
+  if (t == 0) {
+    a.out_num_accepted[b] = ok ? F.n_acc : 0;
+    a.out_status[b] = F.status;
+  }
+}
+
+// ---------------------------------------------------------------- launch
+
+hipError_t launch_filter(const FilterArgs& a, int dt, int vec, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  const long long g1 = (long long)a.n_teams * a.n_s;
+  if (g1 < 1 || g1 > 0x7fffffffll || a.B < 1) return hipErrorInvalidConfiguration;
+  if (ev0 && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
+  const bool paired = a.mode == kFuSample;
+  if (dt == kDtBF16) {
+    if (paired) {
+      if (vec) hipLaunchKernelGGL((k_filt_slices<kDtBF16, true, true>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
+      else hipLaunchKernelGGL((k_filt_slices<kDtBF16, false, true>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
+    } else {
+      if (vec) hipLaunchKernelGGL((k_filt_slices<kDtBF16, true, false>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
+      else hipLaunchKernelGGL((k_filt_slices<kDtBF16, false, false>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
+    }
+  } else {
+    if (paired) {
+      if (vec) hipLaunchKernelGGL((k_filt_slices<kDtF32, true, true>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
+      else hipLaunchKernelGGL((k_filt_slices<kDtF32, false, true>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
+    } else {
+      if (vec) hipLaunchKernelGGL((k_filt_slices<kDtF32, true, false>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
+      else hipLaunchKernelGGL((k_filt_slices<kDtF32, false, false>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
+  if (dt == kDtBF16) hipLaunchKernelGGL((k_filt_rows<kDtBF16>), dim3(a.n_slots), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((k_filt_rows<kDtF32>), dim3(a.n_slots), dim3(kThreads), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (paired) hipLaunchKernelGGL((k_filt_finalize<kFuSample>), dim3(a.B), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((k_filt_finalize<kFuTokenOnly>), dim3(a.B), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace specv

@@ -131,6 +131,57 @@ struct FusedArgs {
 };
 
 hipError_t launch_fused(const FusedArgs& a, int dt, int vec, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+
+// ---------------------------------------------------------------- filtered (top-k / top-p) path
+
+constexpr int kKeepMax = 512;          // largest top-k set (k plus boundary ties) a row may keep
+constexpr int kFilterMaxK = 256;       // largest top_k the sparse path accepts
+
+struct CandEntry {       // a candidate logit of a slice
+  float v;
+  int x;                 // token index
+};
+struct CandHead {        // one (row, slice): candidates stored / found, threshold digits, flags
+  int stored, total;
+  uint32_t th;
+  int flags;
+};
+struct KeptEntry {       // a kept token of a row, in index order
+  int x, pad;
+  double p;
+};
+struct RowStat2 {        // a row's filtered distribution
+  int n, flags;          // kept entries; kFlag* bits
+  float m;               // max logit
+  int argmax;
+  double log_z, entropy, max_prob, z;
+};
+
+struct FilterArgs {
+  const void* tgt;
+  int64_t tgt_ld;
+  const void* drf;
+  int64_t drf_ld;
+  const int32_t* cu;
+  const int32_t* tokens;
+  int B, G, V, n_s, n_draft_rows, n_teams, n_slots, mode, k, cap;
+  float top_p;
+  double c, inv_t;        // c = log2(e) / T
+  uint64_t seed, step;
+  CandEntry* cand;        // [n_slots][n_s][cap]
+  CandHead* chead;        // [n_slots][n_s]
+  KeptEntry* kept;        // [n_slots][kKeepMax]
+  RowStat2* rstat;        // [n_slots]
+  int32_t* out_tokens;
+  int32_t* out_num_accepted;
+  float* out_req_stats;
+  int32_t* out_status;
+  PosStatsOut st;
+};
+
+// Candidates kept per slice for top-k = k: the k largest plus room for boundary ties.
+inline int filter_cap(int k) { return (k + 32 + 15) / 16 * 16; }
+hipError_t launch_filter(const FilterArgs& a, int dt, int vec, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_check_cu(const int32_t* cu, int B, int G, int n_draft_rows, int* cu_bad, hipStream_t st);
 size_t fused_record_bytes();
 
