@@ -149,27 +149,22 @@ __device__ void slice_candidates(const FilterArgs& a, SelLds& S, const float (&v
   constexpr int NP = DT == kDtBF16 ? 2 : 4;
   const int t = threadIdx.x;
   int bad = 0;
-  uint32_t key[kPerThread];
-  bool valid[kPerThread];
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    bad |= __builtin_amdgcn_class(v[j], 0x203) ? 1 : 0;   // NaN, +inf
-    valid[j] = v[j] > -INFINITY && v[j] < INFINITY;
-    key[j] = order_key(v[j]);
-  }
+  for (int j = 0; j < kPerThread; ++j) bad |= __builtin_amdgcn_class(v[j], 0x203) ? 1 : 0;   // NaN, +inf
   bad = block_or(bad, S.wtot[0]);
+  auto valid = [](float x) { return x > -INFINITY && x < INFINITY; };
   bool all;
   int nv;
   const uint32_t th = block_select<NP>(a.k, S,
                                        [&](auto cb) {
 #pragma unroll
-                                         for (int j = 0; j < kPerThread; ++j) cb(key[j], valid[j]);
+                                         for (int j = 0; j < kPerThread; ++j) cb(order_key(v[j]), valid(v[j]));
                                        }, all, nv);
   int ng = 0, ne = 0;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
-    if (!valid[j]) continue;
-    const uint32_t h = key_hi<NP>(key[j]);
+    if (!valid(v[j])) continue;
+    const uint32_t h = key_hi<NP>(order_key(v[j]));
     if (all || h > th) ++ng;
     else if (h == th) ++ne;
   }
@@ -179,8 +174,8 @@ __device__ void slice_candidates(const FilterArgs& a, SelLds& S, const float (&v
   CandEntry* out = a.cand + ((int64_t)slot * a.n_s + s) * cap;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
-    if (!valid[j]) continue;
-    const uint32_t h = key_hi<NP>(key[j]);
+    if (!valid(v[j])) continue;
+    const uint32_t h = key_hi<NP>(order_key(v[j]));
     int pos = -1;
     if (all || h > th) pos = og++;
     else if (h == th) pos = tg + oe++;
@@ -202,20 +197,189 @@ __device__ void slice_candidates(const FilterArgs& a, SelLds& S, const float (&v
   __syncthreads();
 }
 
+__device__ __forceinline__ int wave_max_i(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0xb1, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x4e, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x124, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x128, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x142, 0xa, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+struct Sel2Lds {
+  uint32_t hist[2][256];   // per row: count of keys max - b, b = 0..255
+  int wmax[2][kWaves], wbad[2][kWaves];
+  int wtot[4][kWaves];
+  int tau[2], fb[2];
+  CandEntry stage[2 * (kFilterMaxK + 48)];   // candidates of both rows before the copy out
+  SelLds gen;              // the general select, for a slice whose top k spread wider
+};
+
+// Order key of a bf16-exact value (16 significant bits) and back.
+__device__ __forceinline__ int key16(float v) {
+  uint32_t b = __float_as_uint(v) >> 16;
+  if (b == 0x8000u) b = 0u;
+  return (int)((b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u));
+}
+__device__ __forceinline__ float key16_value(int k) {
+  const uint32_t b = (k & 0x8000) ? ((uint32_t)k & 0x7FFFu) : (~(uint32_t)k & 0xFFFFu);
+  return __uint_as_float(b << 16);
+}
+
+// Candidates of the target slice and (paired) the draft slice of a bf16 ticket, both rows in
+// lockstep.  The k-th largest of the 256 per-thread maxima is at most the slice's k-th largest
+// logit, so every finite logit at or above it is a valid candidate set (it holds the slice's
+// top k with all ties); for a realistic row it is barely larger than k.  That threshold comes
+// from one LDS histogram of the maxima within 256 order keys of the slice maximum (one atomic
+// per thread).  A row whose maxima spread wider, or whose candidates would not fit in `cap`,
+// takes the exact radix select instead.  Candidates are staged in LDS and copied out whole.
+__device__ void slice_candidates_bf16(const FilterArgs& a, Sel2Lds& S, const float (&vp)[kPerThread],
+                                      const float (&vq)[kPerThread], bool paired, int slot_p, int slot_q, int s,
+                                      int base) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int nrow = paired ? 2 : 1;
+  float fm[2] = {-INFINITY, -INFINITY};
+  int bad[2] = {0, 0};
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    bad[0] |= __builtin_amdgcn_class(vp[j], 0x203) ? 1 : 0;
+    fm[0] = fmaxf(fm[0], vp[j]);
+    if (paired) {
+      bad[1] |= __builtin_amdgcn_class(vq[j], 0x203) ? 1 : 0;
+      fm[1] = fmaxf(fm[1], vq[j]);
+    }
+  }
+  int tm[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) tm[r] = fm[r] > -INFINITY ? key16(fm[r]) : -1;
+  S.hist[0][t] = 0u;
+  S.hist[1][t] = 0u;
+  int mx[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    mx[r] = wave_max_i(tm[r]);
+    bad[r] = wave_or(bad[r]);
+    if (lane == 0) { S.wmax[r][wave] = mx[r]; S.wbad[r][wave] = bad[r]; }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    int m = -1, bd = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) { m = max(m, S.wmax[r][w]); bd |= S.wbad[r][w]; }
+    mx[r] = m;
+    bad[r] = bd;
+    if (tm[r] >= 0 && m - tm[r] < 256) atomicAdd(&S.hist[r][m - tm[r]], 1u);
+  }
+  __syncthreads();
+  // wave r: the k-th largest per-thread maximum of row r (bins ascend from the maximum)
+  if (wave < nrow) {
+    int c[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { c[q] = (int)S.hist[wave][4 * lane + q]; sum += c[q]; }
+    const int incl = wave_incl_scan_i(sum);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    const unsigned long long hit = __ballot(incl >= a.k);
+    if (lane == 0) { S.fb[wave] = (total < a.k) ? 1 : 0; S.tau[wave] = 0; }
+    if (hit && total >= a.k) {
+      const int Lh = __builtin_ctzll(hit);
+      if (lane == Lh) {
+        int run = incl - sum;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (run + c[q] >= a.k) { S.tau[wave] = mx[wave] - (4 * lane + q); break; }
+          run += c[q];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  float tf[2];
+  int fb[2], cnt[2] = {0, 0};
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    fb[r] = r < nrow ? S.fb[r] : 1;
+    tf[r] = fb[r] ? INFINITY : key16_value(S.tau[r]);
+  }
+  // finite logits at or above the threshold value (NaN compares false; +inf is excluded)
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    cnt[0] += (vp[j] >= tf[0] && vp[j] < INFINITY) ? 1 : 0;
+    cnt[1] += (vq[j] >= tf[1] && vq[j] < INFINITY) ? 1 : 0;
+  }
+  int off[2], tot[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int inc = wave_incl_scan_i(cnt[r]);
+    off[r] = inc - cnt[r];
+    if (lane == 63) S.wtot[r][wave] = inc;
+  }
+  __syncthreads();
+  const int cap = a.cap;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    int o = 0, tt = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) o += S.wtot[r][w];
+      tt += S.wtot[r][w];
+    }
+    off[r] += o;
+    tot[r] = tt;
+    if (tot[r] > cap) fb[r] = 1;
+  }
+  // stage in LDS (row r at stage[r * cap ..]), then one coalesced copy per row
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (fb[r]) continue;
+    const float (&v)[kPerThread] = r == 0 ? vp : vq;
+    int o = off[r];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      if (v[j] >= tf[r] && v[j] < INFINITY) {
+        S.stage[r * cap + o].v = v[j];
+        S.stage[r * cap + o].x = slice_index<kDtBF16>(base, t, j);
+        ++o;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (r >= nrow) break;
+    const int slot = r == 0 ? slot_p : slot_q;
+    if (fb[r]) {
+      // the exact select: the slice's own k-th largest, ties after the larger values
+      slice_candidates<kDtBF16>(a, S.gen, r == 0 ? vp : vq, slot, s, base);
+      continue;
+    }
+    CandEntry* out = a.cand + ((int64_t)slot * a.n_s + s) * cap;
+    for (int e = t; e < tot[r]; e += kThreads) out[e] = S.stage[r * cap + e];
+    if (t == 0) {
+      CandHead hd;
+      hd.total = tot[r];
+      hd.stored = tot[r];
+      hd.th = (uint32_t)S.tau[r];
+      hd.flags = bad[r] ? kFlagBad : 0;
+      a.chead[(int64_t)slot * a.n_s + s] = hd;
+    }
+  }
+}
+
 template <int DT, bool VEC, bool PAIRED>
 __global__ __launch_bounds__(kThreads) void k_filt_slices(FilterArgs a) {
-  __shared__ SelLds S;
-  const int t = threadIdx.x;
+  __shared__ Sel2Lds S;
   const int n_s = a.n_s;
   const int r = blockIdx.x / n_s, s = blockIdx.x - (blockIdx.x / n_s) * n_s;
   if (r >= a.n_teams) return;
   constexpr int kEsz = DT == kDtBF16 ? 2 : 4;
   const int base = s * kChunk;
-  RawSlice<DT> raw;
-  float v[kPerThread];
-  if (VEC) load_raw_buf<DT>(row_rsrc(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V * kEsz), base, raw);
-  else load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, base, raw);
-  // the draft row of target row r, if r is not the last row of its request
+  RawSlice<DT> rp, rq;
+  if (VEC) load_raw_buf<DT>(row_rsrc(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V * kEsz), base, rp);
+  else load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, base, rp);
+  // the draft row of target row r, if r is not the last row of its request (scalar-cache
+  // binary search over the offsets; the draft loads go out right after)
   int drow = -1;
   if (PAIRED) {
     int lo = 0, hi = a.B;
@@ -227,18 +391,29 @@ __global__ __launch_bounds__(kThreads) void k_filt_slices(FilterArgs a) {
     const int c0 = sload_i32(a.cu + lo), c1 = sload_i32(a.cu + lo + 1);
     const int i = r - c0 - lo;
     if (i >= 0 && i < c1 - c0 && r - lo >= 0 && r - lo < a.n_draft_rows) drow = r - lo;
+    if (VEC)
+      load_raw_buf<DT>(row_rsrc(drow >= 0 ? row_ptr<DT>(a.drf, a.drf_ld, drow) : a.tgt, drow >= 0 ? a.V * kEsz : 0),
+                       base, rq);
+    else if (drow >= 0)
+      load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base, rq);
   }
-  unpack_raw<DT>(raw, v);
-  if (VEC && (a.V % kChunk) != 0 && s == n_s - 1) mask_tail<DT>(a.V, base, v);
-  slice_candidates<DT>(a, S, v, r, s, base);
-  if (PAIRED && drow >= 0) {
-    if (VEC) load_raw_buf<DT>(row_rsrc(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V * kEsz), base, raw);
-    else load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base, raw);
-    unpack_raw<DT>(raw, v);
-    if (VEC && (a.V % kChunk) != 0 && s == n_s - 1) mask_tail<DT>(a.V, base, v);
-    slice_candidates<DT>(a, S, v, a.n_teams + drow, s, base);
+  float vp[kPerThread], vq[kPerThread];
+  unpack_raw<DT>(rp, vp);
+  if (VEC && (a.V % kChunk) != 0 && s == n_s - 1) mask_tail<DT>(a.V, base, vp);
+  const bool paired = PAIRED && drow >= 0;
+  if (paired) {
+    unpack_raw<DT>(rq, vq);
+    if (VEC && (a.V % kChunk) != 0 && s == n_s - 1) mask_tail<DT>(a.V, base, vq);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) vq[j] = -INFINITY;
   }
-  (void)t;
+  if (DT == kDtBF16) {
+    slice_candidates_bf16(a, S, vp, vq, paired, r, a.n_teams + drow, s, base);
+  } else {
+    slice_candidates<DT>(a, S.gen, vp, r, s, base);
+    if (paired) slice_candidates<DT>(a, S.gen, vq, a.n_teams + drow, s, base);
+  }
 }
 
 // ---------------------------------------------------------------- k_filt_rows
