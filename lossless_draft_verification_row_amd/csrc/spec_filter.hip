@@ -418,10 +418,13 @@ __global__ __launch_bounds__(kThreads) void k_filt_slices(FilterArgs a) {
 
 // ---------------------------------------------------------------- k_filt_rows
 
+constexpr int kRowStage = 4096;   // candidates of a row staged in LDS (more: read in place)
+
 struct RowLds {
   SelLds sel;
   int cnt[kMaxSlicesFused + 1];
   int off[kMaxSlicesFused + 1];
+  CandEntry cand[kRowStage];
   float kv[kKeepMax];
   int kx[kKeepMax];
   double ke[kKeepMax];
@@ -446,54 +449,116 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void k_filt_rows(FilterArgs a) {
   constexpr int NP = DT == kDtBF16 ? 2 : 4;
   __shared__ RowLds L;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63;
   const int slot = blockIdx.x;
   if (slot >= a.n_slots) return;
   const int n_s = a.n_s, cap = a.cap;
   const CandHead* hd = a.chead + (int64_t)slot * n_s;
   const CandEntry* cd = a.cand + (int64_t)slot * n_s * cap;
-  if (t == 0) {
-    int fl = 0, off = 0;
-    for (int s = 0; s < n_s; ++s) {
-      const CandHead h = hd[s];
-      if (h.flags & kFlagBad) fl |= kFlagBad;
-      L.cnt[s] = h.stored;
-      L.off[s] = off;
-      off += h.stored;
-    }
-    L.off[n_s] = off;
-    L.flags = fl;
+  // slice headers, one per lane of wave 0; prefix of the stored counts
+  CandHead h;
+  h.stored = 0; h.total = 0; h.th = 0u; h.flags = 0;
+  if (t < n_s) h = hd[t];
+  if (t < 64) {
+    const int inc = wave_incl_scan_i(h.stored);
+    const int fl = wave_or(h.flags & kFlagBad);
+    if (t < n_s) { L.cnt[t] = h.stored; L.off[t] = inc - h.stored; }
+    if (t == 63) { L.off[n_s] = inc; L.flags = fl; }
   }
   __syncthreads();
   const int n = L.off[n_s];
-  // candidate j lives in slice s with off[s] <= j < off[s] + cnt[s]; entries of slice s sit at
-  // cd[s * cap + (j - off[s])]
-  auto at = [&](int j) -> const CandEntry& {
+  const bool staged = n <= kRowStage;
+  // slice of candidate j: off[s] <= j < off[s + 1]
+  auto slice_of = [&](int j) {
     int lo = 0, hi = n_s;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (L.off[mid] <= j) lo = mid;
       else hi = mid;
     }
-    return cd[(int64_t)lo * cap + (j - L.off[lo])];
+    return lo;
   };
-  bool all;
-  int nv;
-  const uint32_t th = block_select<NP>(a.k, L.sel,
-                                       [&](auto cb) {
-                                         for (int j = t; j < n; j += kThreads) cb(order_key(at(j).v), true);
-                                       }, all, nv);
-  // dropped ties of a slice hold its threshold digits; they belong to K if those reach th
-  if (t < n_s) {
-    const CandHead h = hd[t];
-    if (h.total > h.stored && (all || h.th >= th)) atomicOr(&L.flags, kFlagOverflow);
+  if (staged) {
+    // copy the candidates in, 8 per thread in flight at a time
+    for (int b0 = 0; b0 < n; b0 += 8 * kThreads) {
+      CandEntry tmp[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = b0 + u * kThreads + t;
+        if (j < n) {
+          const int sl = slice_of(j);
+          tmp[u] = cd[(int64_t)sl * cap + (j - L.off[sl])];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = b0 + u * kThreads + t;
+        if (j < n) L.cand[j] = tmp[u];
+      }
+    }
+    __syncthreads();
   }
+  auto at = [&](int j) -> CandEntry {
+    if (staged) return L.cand[j];
+    const int sl = slice_of(j);
+    return cd[(int64_t)sl * cap + (j - L.off[sl])];
+  };
+  bool all = false;
+  int nv;
+  uint32_t th = 0u;
+  bool done = false;
+  if (NP == 2) {
+    // bf16: one LDS histogram of the candidate keys within 256 of the maximum (one key per
+    // bin) gives the exact k-th largest when the top k lie in that window
+    int km = -1;
+    for (int j = t; j < n; j += kThreads) km = max(km, (int)key_hi<2>(order_key(at(j).v)));
+    L.sel.hist[t] = 0u;
+    km = wave_max_i(km);
+    if (lane == 0) L.sel.wtot[0][t >> 6] = km;
+    __syncthreads();
+    km = max(max(L.sel.wtot[0][0], L.sel.wtot[0][1]), max(L.sel.wtot[0][2], L.sel.wtot[0][3]));
+    for (int j = t; j < n; j += kThreads) {
+      const int d = km - (int)key_hi<2>(order_key(at(j).v));
+      if (d < 256) atomicAdd(&L.sel.hist[d], 1u);
+    }
+    __syncthreads();
+    if (t < 64) {
+      int c[4], sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { c[q] = (int)L.sel.hist[4 * lane + q]; sum += c[q]; }
+      const int incl = wave_incl_scan_i(sum);
+      const int total = __builtin_amdgcn_readlane(incl, 63);
+      const unsigned long long hit = __ballot(incl >= a.k);
+      if (lane == 0) L.sel.digit = -1;
+      if (hit && total >= a.k) {
+        const int Lh = __builtin_ctzll(hit);
+        if (lane == Lh) {
+          int run = incl - sum;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (run + c[q] >= a.k) { L.sel.digit = km - (4 * lane + q); break; }
+            run += c[q];
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (L.sel.digit >= 0) { th = (uint32_t)L.sel.digit; done = true; }
+    __syncthreads();
+  }
+  if (!done)
+    th = block_select<NP>(a.k, L.sel,
+                          [&](auto cb) {
+                            for (int j = t; j < n; j += kThreads) cb(order_key(at(j).v), true);
+                          }, all, nv);
+  // dropped ties of a slice hold its threshold digits; they belong to K if those reach th
+  if (t < n_s && h.total > h.stored && (all || h.th >= th)) atomicOr(&L.flags, kFlagOverflow);
   // the top-k set K, compacted in candidate order
   int mine = 0;
   for (int j = t; j < n; j += kThreads) mine += (all || key_hi<NP>(order_key(at(j).v)) >= th) ? 1 : 0;
   int o = mine, dummy = 0, nk, tz;
   block_scan2(o, dummy, L.sel, nk, tz);
-  if (nk > kKeepMax) { if (t == 0) L.flags |= kFlagOverflow; }
+  if (nk > kKeepMax) { if (t == 0) atomicOr(&L.flags, kFlagOverflow); }
   else {
     for (int j = t; j < n; j += kThreads) {
       const CandEntry c = at(j);
@@ -502,6 +567,7 @@ __global__ __launch_bounds__(kThreads) void k_filt_rows(FilterArgs a) {
   }
   if (t == 0) L.nk = nk;
   __syncthreads();
+  (void)lane;
   RowStat2 st;
   st.n = 0; st.flags = L.flags; st.m = -INFINITY; st.argmax = -1;
   st.log_z = 0.0; st.entropy = 0.0; st.max_prob = 0.0; st.z = 0.0;
@@ -581,26 +647,28 @@ struct FinFLds {
   int ytok[kMaxGamma];
   float dh[kMaxGamma], dm[kMaxGamma];
   double chunk[kMaxSlicesFused];
-  int flags, status, n_acc, pos, wkind, y;
+  int pidx[kWaves][kKeepMax], qidx[kWaves][kKeepMax];   // a wave's kept token lists
+  double w[kKeepMax];                                     // sampler weights of the chosen row
+  int xs[kKeepMax];
+  int flags, status, n_acc, pos, wkind, y, n, x;
   double u[3];
-  int x;
 };
 
-// p of token x in a kept list sorted by index (0 when x is not kept).
-__device__ __forceinline__ double kept_p(const KeptEntry* ke, int n, int x) {
+// Position of token x in a sorted index list (n entries), or -1.
+__device__ __forceinline__ int find_idx(const int* ix, int n, int x) {
   int lo = 0, hi = n;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
-    if (ke[mid].x < x) lo = mid + 1;
+    if (ix[mid] < x) lo = mid + 1;
     else hi = mid;
   }
-  return (lo < n && ke[lo].x == x) ? ke[lo].p : 0.0;
+  return (lo < n && ix[lo] == x) ? lo : -1;
 }
 
 // First index whose running sum exceeds target (the last positive one if rounding leaves
 // none); sums run in the order given.
-template <typename W>
-__device__ __forceinline__ int seq_pick(int n, double target, W w) {
+template <typename Wt>
+__device__ __forceinline__ int seq_pick(int n, double target, Wt w) {
   double cum = 0.0;
   int last = -1;
   for (int i = 0; i < n; ++i) {
@@ -643,34 +711,57 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
   const int c0 = cu_s[b], g = cu_s[b + 1] - c0;
   if (t == 0) F.flags = 0;
   __syncthreads();
-  // A. per position: the rows' flags and statistics, p(y), q(y), 1 - TV (one wave per position)
+  // A. per position (one wave each): flags, statistics, p(y), q(y), 1 - TV
+  int* pix = F.pidx[wave];
+  int* qix = F.qidx[wave];
   for (int i = wave; i <= g; i += kWaves) {
     const int ps = c0 + b + i;
     const RowStat2 P = a.rstat[ps];
     const KeptEntry* kp = a.kept + (int64_t)ps * kKeepMax;
     const bool okp = P.flags == 0;
     int fl = P.flags;
+    const int np = okp ? P.n : 0;
+    for (int j = lane; j < np; j += 64) pix[j] = kp[j].x;
     if (i < g) {
       const int y = a.tokens[c0 + i];
       const bool yv = y >= 0 && y < a.V;
-      double pyd = 0.0, qyd = 1.0, ov = 0.0;
+      double pyd = 0.0, qyd = 1.0;
       float py = nan, qy = nan, ovl = nan, dh = nan, dm = nan;
-      if (okp && yv) { pyd = kept_p(kp, P.n, y); py = (float)pyd; }
       if (MODE == kFuSample) {
         const int qs = a.n_teams + c0 + i;
         const RowStat2 Q = a.rstat[qs];
         fl |= Q.flags;
         const bool okq = Q.flags == 0;
         const KeptEntry* kq = a.kept + (int64_t)qs * kKeepMax;
-        if (okq && yv) { qyd = kept_p(kq, Q.n, y); qy = (float)qyd; }
+        const int nq = okq ? Q.n : 0;
+        for (int j = lane; j < nq; j += 64) qix[j] = kq[j].x;
+        __builtin_amdgcn_wave_barrier();
+        if (okp && yv) {
+          const int m = find_idx(pix, np, y);
+          pyd = m >= 0 ? kp[m].p : 0.0;
+          py = (float)pyd;
+        }
+        if (okq && yv) {
+          const int m = find_idx(qix, nq, y);
+          qyd = m >= 0 ? kq[m].p : 0.0;
+          qy = (float)qyd;
+        }
         if (okp && okq) {
           double part = 0.0;
-          for (int j = lane; j < P.n; j += 64) part += fmin(kp[j].p, kept_p(kq, Q.n, kp[j].x));
-          ov = wave_sum_dpp_d(part);
-          ovl = (float)ov;
+          for (int j = lane; j < np; j += 64) {
+            const int m = find_idx(qix, nq, pix[j]);
+            if (m >= 0) part += fmin(kp[j].p, kq[m].p);
+          }
+          ovl = (float)wave_sum_dpp_d(part);
         }
         if (okq) { dh = (float)Q.entropy; dm = (float)Q.max_prob; }
       } else {
+        __builtin_amdgcn_wave_barrier();
+        if (okp && yv) {
+          const int m = find_idx(pix, np, y);
+          pyd = m >= 0 ? kp[m].p : 0.0;
+          py = (float)pyd;
+        }
         qyd = 1.0;
         qy = yv ? 1.f : nan;
         ovl = okp ? (yv ? py : 0.f) : nan;
@@ -698,9 +789,10 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
       if (a.st.target_max_prob) a.st.target_max_prob[ps] = P.flags ? nan : (float)P.max_prob;
       if (fl) atomicOr(&F.flags, fl);
     }
+    __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
-  // B. accept scan and the row to sample (one thread)
+  // B. accept scan, the row to sample, request statistics (one thread)
   if (t == 0) {
     int status = 0, j = -1;
     if (F.flags & kFlagOverflow) status = kStFilterOverflow;
@@ -732,92 +824,107 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
         float hmax = -INFINITY, cmin = INFINITY;
         bool anynan = false;
         for (int i = 0; i < g; ++i) {
-          const float h = F.dh[i], cm = F.dm[i];
-          if (!(h == h) || !(cm == cm)) anynan = true;
-          hs += h; cs += cm;
-          hmax = fmaxf(hmax, h); cmin = fminf(cmin, cm);
+          const float hh = F.dh[i], cm = F.dm[i];
+          if (!(hh == hh) || !(cm == cm)) anynan = true;
+          hs += hh; cs += cm;
+          hmax = fmaxf(hmax, hh); cmin = fminf(cmin, cm);
         }
         if (!anynan) { rq[0] = (float)(hs / g); rq[1] = (float)(cs / g); rq[2] = hmax; rq[3] = cmin; }
       }
       for (int q = 0; q < 4; ++q) a.out_req_stats[(int64_t)b * 4 + q] = rq[q];
     }
-    // C. the three-level sampler on the sparse weights, sums in index order (reading R6)
-    if (!(status & (kStNonfinite | kStFilterOverflow))) {
-      const int ps = c0 + b + F.pos;
-      const RowStat2 P = a.rstat[ps];
-      const KeptEntry* kp = a.kept + (int64_t)ps * kKeepMax;
-      const KeptEntry* kq = nullptr;
-      int nq = 0;
-      if (MODE == kFuSample && F.pos < g) {
-        const int qs = a.n_teams + c0 + F.pos;
-        kq = a.kept + (int64_t)qs * kKeepMax;
-        nq = a.rstat[qs].n;
-      }
-      int wkind = F.wkind;
+  }
+  __syncthreads();
+  // C. the three-level sampler on the sparse weights of the chosen row (reading R6): weights in
+  // LDS (all threads), then the level sums in index order (one thread)
+  if (!(F.status & (kStNonfinite | kStFilterOverflow))) {
+    const int ps = c0 + b + F.pos;
+    const RowStat2 P = a.rstat[ps];
+    const KeptEntry* kp = a.kept + (int64_t)ps * kKeepMax;
+    const int n = P.n;
+    const KeptEntry* kq = nullptr;
+    int nq = 0;
+    if (MODE == kFuSample && F.pos < g) {
+      const int qs = a.n_teams + c0 + F.pos;
+      kq = a.kept + (int64_t)qs * kKeepMax;
+      nq = a.rstat[qs].n;
+      for (int j = t; j < nq; j += kThreads) F.qidx[0][j] = kq[j].x;
+    }
+    for (int j = t; j < n; j += kThreads) F.xs[j] = kp[j].x;
+    __syncthreads();
+    for (int pass = 0; pass < 2; ++pass) {
+      const int wkind = pass == 0 ? F.wkind : 0;
       const int yx = F.y;
-      for (int pass = 0; pass < 2; ++pass) {
-        auto wgt = [&](int j) -> double {
-          const double p = kp[j].p;
-          if (wkind == 1) return fmax(p - kept_p(kq, nq, kp[j].x), 0.0);
-          if (wkind == 2) return kp[j].x == yx ? fmax(p - 1.0, 0.0) : p;
-          return p;
-        };
-        // chunk masses: group masses summed in order, chunk by chunk
-        const int n = P.n;
+      for (int j = t; j < n; j += kThreads) {
+        const double p = kp[j].p;
+        double w = p;
+        if (wkind == 1) {
+          const int m = find_idx(F.qidx[0], nq, F.xs[j]);
+          w = fmax(p - (m >= 0 ? kq[m].p : 0.0), 0.0);
+        } else if (wkind == 2) {
+          w = F.xs[j] == yx ? fmax(p - 1.0, 0.0) : p;
+        }
+        F.w[j] = w;
+      }
+      __syncthreads();
+      int again = 0;
+      if (t == 0) {
+        const int* xs = F.xs;
+        const double* wv = F.w;
+        // chunk masses: group masses summed in index order, chunk by chunk
         int j = 0;
         double W = 0.0;
         for (int k = 0; k < a.n_s; ++k) {
           double Sk = 0.0;
-          while (j < n && (kp[j].x >> 12) == k) {
-            const int grp = kp[j].x >> 6;
+          while (j < n && (xs[j] >> 12) == k) {
+            const int grp = xs[j] >> 6;
             double M = 0.0;
-            while (j < n && (kp[j].x >> 6) == grp) { M += wgt(j); ++j; }
+            while (j < n && (xs[j] >> 6) == grp) { M += wv[j]; ++j; }
             Sk += M;
           }
           F.chunk[k] = Sk;
           W += Sk;
         }
         if (!(W > 0.0)) {
-          if (wkind != 0) { status |= kStResidualEmpty; wkind = 0; continue; }
-          break;
+          if (wkind != 0) { F.status |= kStResidualEmpty; again = 1; }
+        } else {
+          const int kc = seq_pick(a.n_s, F.u[0] * W, [&](int k) { return F.chunk[k]; });
+          int j0 = 0;
+          while (j0 < n && (xs[j0] >> 12) < kc) ++j0;
+          int j1 = j0;
+          while (j1 < n && (xs[j1] >> 12) == kc) ++j1;
+          double Sg = 0.0;
+          for (int jj = j0; jj < j1;) {
+            const int grp = xs[jj] >> 6;
+            double M = 0.0;
+            while (jj < j1 && (xs[jj] >> 6) == grp) { M += wv[jj]; ++jj; }
+            Sg += M;
+          }
+          // level 2 over the chunk's groups (empty groups add nothing), then level 3
+          const double t2 = F.u[1] * Sg;
+          double cum = 0.0;
+          int gj0 = -1, gj1 = -1, lj0 = -1, lj1 = -1;
+          for (int jj = j0; jj < j1;) {
+            const int grp = xs[jj] >> 6;
+            const int s0 = jj;
+            double M = 0.0;
+            while (jj < j1 && (xs[jj] >> 6) == grp) { M += wv[jj]; ++jj; }
+            cum += M;
+            if (M > 0.0) { lj0 = s0; lj1 = jj; }
+            if (cum > t2) { gj0 = s0; gj1 = jj; break; }
+          }
+          if (gj0 < 0) { gj0 = lj0; gj1 = lj1; }
+          if (gj0 >= 0) {
+            double Mg = 0.0;
+            for (int jj = gj0; jj < gj1; ++jj) Mg += wv[jj];
+            const int e = seq_pick(gj1 - gj0, F.u[2] * Mg, [&](int q) { return wv[gj0 + q]; });
+            F.x = e >= 0 ? xs[gj0 + e] : -1;
+          }
         }
-        const int kc = seq_pick(a.n_s, F.u[0] * W, [&](int k) { return F.chunk[k]; });
-        // entries of chunk kc and their group masses
-        int j0 = 0;
-        while (j0 < n && (kp[j0].x >> 12) < kc) ++j0;
-        int j1 = j0;
-        while (j1 < n && (kp[j1].x >> 12) == kc) ++j1;
-        double Sg = 0.0;
-        for (int jj = j0; jj < j1;) {
-          const int grp = kp[jj].x >> 6;
-          double M = 0.0;
-          while (jj < j1 && (kp[jj].x >> 6) == grp) { M += wgt(jj); ++jj; }
-          Sg += M;
-        }
-        // level 2 over the chunk's groups (empty groups add nothing)
-        const double t2 = F.u[1] * Sg;
-        double cum = 0.0;
-        int gsel = -1, glast = -1;
-        int gj0 = -1, gj1 = -1, lj0 = -1, lj1 = -1;
-        for (int jj = j0; jj < j1;) {
-          const int grp = kp[jj].x >> 6;
-          const int s0 = jj;
-          double M = 0.0;
-          while (jj < j1 && (kp[jj].x >> 6) == grp) { M += wgt(jj); ++jj; }
-          cum += M;
-          if (M > 0.0) { glast = grp; lj0 = s0; lj1 = jj; }
-          if (cum > t2) { gsel = grp; gj0 = s0; gj1 = jj; break; }
-        }
-        if (gsel < 0) { gsel = glast; gj0 = lj0; gj1 = lj1; }
-        if (gsel >= 0) {
-          double Mg = 0.0;
-          for (int jj = gj0; jj < gj1; ++jj) Mg += wgt(jj);
-          const int e = seq_pick(gj1 - gj0, F.u[2] * Mg, [&](int q) { return wgt(gj0 + q); });
-          F.x = e >= 0 ? kp[gj0 + e].x : -1;
-        }
-        break;
+        red_i[0] = again;
       }
-      F.status = status;
+      __syncthreads();
+      if (!red_i[0]) break;
     }
   }
   __syncthreads();
