@@ -20,21 +20,20 @@ constexpr size_t kAlign = 256;
 hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
 // Bound of the fused kernel's team wait, in polls (spec_set_spin_limit).
 unsigned g_spin_limit = 1u << 18;
-// Team polling of the fused kernel: a workgroup waits poll_delay 10-ns ticks after publishing
-// before its first poll of the team's arrival flags, then pauses poll_pause x 128 cycles
-// between polls (0: doubling pauses).  Device-scope polls compete with the row stream, so
-// few and late polls are cheaper than early ones.  Tuning knobs: SPEC_VERIFY_POLL_DELAY,
-// SPEC_VERIFY_POLL_PAUSE.
+// Team polling of the streaming kernel: a workgroup waits poll_delay 10-ns ticks after
+// publishing before its first poll of the team's records, and pauses poll_pause x 128 cycles
+// after a failed poll.  Device-scope polls compete with the row stream, so few and late polls
+// are cheaper than early ones.  Tuning knobs: SPEC_VERIFY_POLL_DELAY, SPEC_VERIFY_POLL_PAUSE.
 int env_int(const char* name, int dflt) {
   const char* e = getenv(name);
   return (e && e[0]) ? atoi(e) : dflt;
 }
 int poll_delay_ticks() {
-  static const int v = env_int("SPEC_VERIFY_POLL_DELAY", 300);
+  static const int v = env_int("SPEC_VERIFY_POLL_DELAY", 400);
   return v;
 }
 int poll_pause() {
-  static const int v = env_int("SPEC_VERIFY_POLL_PAUSE", 32);
+  static const int v = env_int("SPEC_VERIFY_POLL_PAUSE", 8);
   return v;
 }
 
@@ -87,7 +86,7 @@ size_t dense_bytes(int64_t n_slots, int V) {
 size_t fused_bytes(int64_t n_teams, int V) {
   const int64_t ns = n_chunks(V);
   return kHeaderBytes + align_up((size_t)(n_teams * ns * 2) * fused_record_bytes()) +
-         align_up((size_t)(n_teams * ns) * sizeof(uint64_t)) + align_up((size_t)(n_teams * ns) * sizeof(uint32_t));
+         align_up((size_t)(n_teams * ns * 4) * sizeof(uint64_t)) + align_up((size_t)(n_teams * kMaxMembers) * 4);
 }
 
 // Tags of the fused kernel's workspace records: one per call, unique within the process,
@@ -291,8 +290,8 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
     f.tag = next_tag();
     Carve cv{ws};
     f.part = cv.take<uint64_t>((size_t)f.n_teams * ns * 2 * fused_record_bytes());
-    f.smass = cv.take<uint64_t>((size_t)f.n_teams * ns * sizeof(uint64_t));
-    f.arrive = cv.take<uint32_t>((size_t)f.n_teams * ns * sizeof(uint32_t));
+    f.smass = cv.take<uint64_t>((size_t)f.n_teams * ns * 4 * sizeof(uint64_t));
+    f.arrive = cv.take<uint32_t>((size_t)f.n_teams * kMaxMembers * sizeof(uint32_t));
     f.poll_delay = poll_delay_ticks();
     f.poll_pause = poll_pause();
     f.out_tokens = out_tokens;

@@ -414,6 +414,14 @@ __device__ __forceinline__ int sload_i32(const int32_t* p) {
   return v;
 }
 
+// Two consecutive uniform 32-bit values in one scalar load (p 4-byte aligned).
+__device__ __forceinline__ void sload2_i32(const int32_t* p, int& a, int& b) {
+  uint64_t v;
+  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  a = (int)(uint32_t)v;
+  b = (int)(uint32_t)(v >> 32);
+}
+
 // ---------------------------------------------------------------- wave-wide fp64 helpers
 
 // 64-bit DPP move of both halves (lanes whose source is outside the row, or rows outside

@@ -61,18 +61,6 @@ struct FinScratch {
   int flags, status, n_acc, pos, wkind, y, kpick, gpick, xpick;
 };
 
-struct Lds {
-  float red[8 * kWaves];
-  float f[8];
-  int i[8];
-  // one buffer per reduction of a ticket, so that consecutive reductions need no protecting
-  // barrier between them
-  float wp[2][kWaves][3];   // per-wave {ref, sum e, sum e t} of the target and draft rows
-  float rres[kWaves];
-  float cmb[4];
-  int cst;
-};
-
 struct LdsFin {
   int cu[kMaxReqFused + 1];
   int i[8];
@@ -257,15 +245,20 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
     const int r = c0 + b + ti;
     const bool pair = (MODE == kFuSample) && ti < g;
     const bool in = lane < n_s;
-    float pr = -INFINITY, ps = 0.f, pw = 0.f, qr = -INFINITY, qs = 0.f, qw = 0.f, sm = 0.f;
+    float pr = -INFINITY, ps = 0.f, pw = 0.f, qr = -INFINITY, qs = 0.f, qw = 0.f;
+    double sm = 0.0;
     bool ok = true;
     if (in) {
       ok = load_rec(rrs, rec_off(n_s, r, lane, 0), tag, pr, ps, pw);
       if (pair) {
         ok = load_rec(rrs, rec_off(n_s, r, lane, 1), tag, qr, qs, qw) && ok;
-        const uint64_t m = ld_coh(a.smass + (int64_t)r * n_s + lane);
-        sm = lo_f(m);
-        ok = ok && tag_of(m) == tag;
+        const uint64_t* mw = a.smass + ((int64_t)r * n_s + lane) * kWaves;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const uint64_t m = ld_coh(mw + w);
+          sm += (double)lo_f(m);
+          ok = ok && tag_of(m) == tag;
+        }
       }
     }
     const bool missing = !wave_all(ok);
@@ -291,7 +284,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
         if (!Q.ok) T.flags |= kTeamBadQ;
         // a slice whose team wait gave up marked its residual mass NaN
         if (!wave_all(!(in && !(sm == sm)))) T.flags |= kTeamTimeout;
-        T.beta = wave_sum_dpp_d(in ? (double)sm : 0.0);
+        T.beta = wave_sum_dpp_d(in ? sm : 0.0);
       }
     }
     if (lane == 0) F.team[ti] = T;
@@ -425,7 +418,9 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
         double m = 0.0;
         if (lane < n_s) {
           if (wkind == 1) {
-            m = (double)lo_f(ld_coh(a.smass + (int64_t)r * n_s + lane));
+            const uint64_t* mw = a.smass + ((int64_t)r * n_s + lane) * kWaves;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) m += (double)lo_f(ld_coh(mw + w));
           } else {
             float ref, sv, wv;
             load_rec(rrs, rec_off(n_s, r, lane, 0), tag, ref, sv, wv);
@@ -533,25 +528,199 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   }
 }
 
-// ---------------------------------------------------------------- streaming phases
+// ---------------------------------------------------------------- streaming kernel
 
-// One ticket; every field is uniform over the workgroup.
+// DPP wave reductions, one v_*_dpp per step (row butterflies, then row broadcasts); the
+// result is valid in lane 63.  Written out because the compiler's versions add a move and a
+// canonicalising max per step.  Values are interleaved so that each DPP read comes at least
+// two instructions after the write of its source; a block starts with s_nop 1 for the
+// instructions just before it.
+#define SPEC_DPP4(op, ctrl)                                \
+  "v_" op "_f32_dpp %0, %0, %0 " ctrl "\n\t"                \
+  "v_" op "_f32_dpp %1, %1, %1 " ctrl "\n\t"                \
+  "v_" op "_f32_dpp %2, %2, %2 " ctrl "\n\t"                \
+  "v_" op "_f32_dpp %3, %3, %3 " ctrl "\n\t"
+#define SPEC_DPP2(op, ctrl)                                \
+  "v_" op "_f32_dpp %0, %0, %0 " ctrl "\n\t"                \
+  "v_" op "_f32_dpp %1, %1, %1 " ctrl "\n\t"                \
+  "s_nop 0\n\t"
+#define SPEC_DPP_STEPS(M, op)                                             \
+  M(op, "quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf")                 \
+  M(op, "quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf")                 \
+  M(op, "row_ror:4 row_mask:0xf bank_mask:0xf")                           \
+  M(op, "row_ror:8 row_mask:0xf bank_mask:0xf")                           \
+  M(op, "row_bcast:15 row_mask:0xa bank_mask:0xf")                        \
+  M(op, "row_bcast:31 row_mask:0xc bank_mask:0xf")
+
+__device__ __forceinline__ float lane63(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ void dpp_sum4(float& a, float& b, float& c, float& d) {
+  asm volatile("s_nop 1\n\t" SPEC_DPP_STEPS(SPEC_DPP4, "add") : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+  a = lane63(a); b = lane63(b); c = lane63(c); d = lane63(d);
+}
+__device__ __forceinline__ void dpp_sum2(float& a, float& b) {
+  asm volatile("s_nop 1\n\t" SPEC_DPP_STEPS(SPEC_DPP2, "add") : "+v"(a), "+v"(b));
+  a = lane63(a); b = lane63(b);
+}
+__device__ __forceinline__ void dpp_max2(float& a, float& b) {
+  asm volatile("s_nop 1\n\t" SPEC_DPP_STEPS(SPEC_DPP2, "max") : "+v"(a), "+v"(b));
+  a = lane63(a); b = lane63(b);
+}
+
+// One ticket: a 4096-logit slice s of target row r, paired with the same slice of draft row
+// drow when position r holds a draft token.  Every field is uniform over the workgroup.
 struct Ticket {
-  int r, s, b, c0, g, i;
-  bool pair;
+  int r, s, drow;
+  bool valid, pair;
 };
 
-// The lane that publishes a workgroup's records: lane 0 of the last wave.  Wave 0 polls the
-// team records; keeping every store out of wave 0 means that, in wave 0, only the ticket loads
-// issued after a poll stand between the poll and its use (vector memory counters retire in
-// issue order).
+// Raw-word views of one thread's slice (bf16 pairs or floats): the logits are unpacked where
+// they are used, so no unpacked copy of a slice is ever held.  Element j of the slice is word
+// j / 2 (bf16: low half first) or word j (fp32).
+template <int DT>
+__device__ __forceinline__ float raw_elem(const RawSlice<DT>& r, int j) {
+  if constexpr (DT == kDtBF16) return (j & 1) ? bf16_hi(r.w[j >> 1]) : bf16_lo(r.w[j >> 1]);
+  else return __uint_as_float(r.w[j]);
+}
+// Max of a slice (quiet NaN ignored).  bf16: both halves are extracted exactly (a whole word
+// read as a float could be a signalling NaN when its high half is -inf); the extraction is
+// opaque to the compiler so that the exponent pass forms the logits again instead of keeping
+// an unpacked copy of the slice.
+template <int DT>
+__device__ __forceinline__ float max_raw(const RawSlice<DT>& r, float m) {
+  if constexpr (DT == kDtBF16) {
+#pragma unroll
+    for (int k = 0; k < RawSlice<DT>::kWords; ++k) {
+      uint32_t lo, hi;
+      asm("v_lshlrev_b32 %0, 16, %1" : "=v"(lo) : "v"(r.w[k]));
+      asm("v_and_b32 %0, 0xffff0000, %1" : "=v"(hi) : "v"(r.w[k]));
+      m = fmaxf(fmaxf(m, __uint_as_float(hi)), __uint_as_float(lo));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < RawSlice<DT>::kWords; ++k) m = fmaxf(m, __uint_as_float(r.w[k]));
+  }
+  return m;
+}
+// Logits at indices >= V (zeros from the bounds check) become -inf, on the raw words.
+template <int DT>
+__device__ __forceinline__ void mask_tail_raw(int V, int base, RawSlice<DT>& r) {
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    if (slice_index<DT>(base, threadIdx.x, j) < V) continue;
+    if constexpr (DT == kDtBF16) r.w[j >> 1] = (j & 1) ? (r.w[j >> 1] & 0xffffu) | 0xff800000u : (r.w[j >> 1] & 0xffff0000u) | 0xff80u;
+    else r.w[j] = 0xff800000u;
+  }
+}
+// e = 2^(l c - ref) of a slice given as raw words, with s = sum e and w = sum e (l c - ref).  A
+// masked logit (-inf) gives e = 0 and a NaN product in w; such a thread recomputes w from its
+// e-values, using log2(e) for l c - ref.  Words are consumed in groups of two (four logits) so
+// that the raw words die as the e-values appear.
+template <int DT>
+__device__ __forceinline__ void exp_raw(const RawSlice<DT>& r, float (&e)[kPerThread], float c, float ref, float& s,
+                                        float& w) {
+  s = 0.f;
+  w = 0.f;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const float tt = fmaf(raw_elem<DT>(r, j), c, -ref);
+    const float ej = __builtin_amdgcn_exp2f(tt);
+    s += ej;
+    w = fmaf(ej, tt, w);
+    e[j] = ej;
+    if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+  }
+  if (!(w == w)) {
+    w = 0.f;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+      if (e[j] > 0.f) w = fmaf(e[j], __builtin_amdgcn_logf(e[j]), w);
+  }
+}
+
+// e = 2^(l c - ref) in place over one slice, with s = sum e and (ENT) w = sum e (l c - ref).  A
+// masked logit (-inf) gives e = 0 and a NaN product in w; such a thread recomputes w from its
+// e-values, using log2(e) for l c - ref.
+template <bool ENT>
+__device__ __forceinline__ void exp_slice(float (&v)[kPerThread], float c, float ref, float& s, float& w) {
+  const float t0 = fmaf(v[0], c, -ref);
+  const float e0 = __builtin_amdgcn_exp2f(t0);
+  s = e0;
+  w = ENT ? e0 * t0 : 0.f;
+  v[0] = e0;
+#pragma unroll
+  for (int j = 1; j < kPerThread; ++j) {
+    const float tt = fmaf(v[j], c, -ref);
+    const float e = __builtin_amdgcn_exp2f(tt);
+    s += e;
+    if (ENT) w = fmaf(e, tt, w);
+    v[j] = e;
+  }
+  if (ENT && !(w == w)) {
+    w = 0.f;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+      if (v[j] > 0.f) w = fmaf(v[j], __builtin_amdgcn_logf(v[j]), w);
+  }
+}
+
+__device__ __forceinline__ float max_slice(const float (&v)[kPerThread], float m) {
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) m = fmaxf(m, v[j]);
+  return m;
+}
+
+// exp_raw for a slice whose e-values go straight to LDS, four at a time (stash[k][thread]).
+template <int DT>
+__device__ __forceinline__ void exp_raw_stash(const RawSlice<DT>& r, float4 (*stash)[kThreads], float c, float ref,
+                                              float& s, float& w) {
+  const int t = threadIdx.x;
+  s = 0.f;
+  w = 0.f;
+#pragma unroll
+  for (int k = 0; k < kPerThread / 4; ++k) {
+    float e4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float tt = fmaf(raw_elem<DT>(r, 4 * k + q), c, -ref);
+      e4[q] = __builtin_amdgcn_exp2f(tt);
+      s += e4[q];
+      w = fmaf(e4[q], tt, w);
+    }
+    stash[k][t] = make_float4(e4[0], e4[1], e4[2], e4[3]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (!(w == w)) {
+    w = 0.f;
+#pragma unroll
+    for (int k = 0; k < kPerThread / 4; ++k) {
+      const float4 v = stash[k][t];
+      const float e4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (e4[q] > 0.f) w = fmaf(e4[q], __builtin_amdgcn_logf(e4[q]), w);
+    }
+  }
+}
+
+struct FusedLds {
+  float4 stash[kPerThread / 4][kThreads];   // a paired ticket's target e-values of slice 1
+  float wp[2][kWaves][4];   // [row][wave] {ref, sum e over slice 0, over slice 1, sum e t}
+  float rec[2][64][2];      // the team's records {ref, s} of the target and draft rows, one per slice
+  int rst;                  // team status: 0 ok, 1 non-finite row, 2 wait gave up
+  int bad[kWaves];
+  int amax[2][kWaves];
+};
+
+// The lane that publishes a workgroup's records: lane 0 of the last wave (wave 0 polls).
 constexpr int kStorer = kThreads - 64;
-   // polls served by the XCD's L2 before device-scope polls
 
 // Fold per-wave partials {ref_w, s_w, w_w} of one row's slice (ref_w = -inf for a wave that
-// holds no finite logit) into one record relative to ref = max_w ref_w:
-// s = sum_w s_w 2^(ref_w - ref), w = sum_w 2^(ref_w - ref) (w_w + s_w (ref_w - ref)).
-__device__ __forceinline__ void fold_waves(const float (*pw)[3], float& ref, float& s, float& w) {
+// holds no finite logit; s_w = pw[w][K], w_w = pw[w][3] when W, else 0) into one record relative
+// to ref = max_w ref_w: s = sum_w s_w 2^(ref_w - ref), w = sum_w 2^(ref_w - ref) (w_w + s_w (ref_w - ref)).
+template <int K, bool W>
+__device__ __forceinline__ void fold_waves(const float (*pw)[4], float& ref, float& s, float& w) {
   float M = -INFINITY;
 #pragma unroll
   for (int k = 0; k < kWaves; ++k) M = fmaxf(M, pw[k][0]);
@@ -563,197 +732,112 @@ __device__ __forceinline__ void fold_waves(const float (*pw)[3], float& ref, flo
     if (!(pw[k][0] > -INFINITY)) continue;
     const float d = pw[k][0] - M;
     const float f = __builtin_amdgcn_exp2f(d);
-    s = fmaf(pw[k][1], f, s);
-    w = fmaf(f, fmaf(pw[k][1], d, pw[k][2]), w);
+    s = fmaf(pw[k][K], f, s);
+    w = fmaf(f, fmaf(pw[k][K], d, W ? pw[k][3] : 0.f), w);
   }
 }
 
-// Phase 1 of a ticket: per-wave maxima, e = exp2(l c - ref_w) in place, sums, one record per
-// row.  Returns each wave's references (0 for a wave with no finite logit).
-template <int DT, int MODE>
-__device__ __forceinline__ void phase1(const FusedArgs& a, Lds& L, const Ticket& T, float (&vp)[kPerThread],
-                                       float (&vq)[kPerThread], float& refp, float& refq) {
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+// Wave 0 of a paired ticket: wait until every member of the team has raised its arrival flag
+// (the team's flags share one cache line, so a poll reads one line; lanes past the last member
+// read the first flag again), then read the team's records (one slice per lane) into LDS.  A
+// flag goes out right behind its records, so a record may still be in flight when the flag is
+// seen: its check word then fails and the records are read again.  Every wait is bounded.
+__device__ __forceinline__ void team_gather(const FusedArgs& a, FusedLds& L, int r, int n_u) {
+  const int lane = threadIdx.x & 63;
+  const int n_s = a.n_s;
+  const int sl = min(lane, n_s - 1);
   const uint32_t tag = a.tag;
-  const int base = T.s * kChunk;
   const __amdgpu_buffer_rsrc_t rrs = rec_rsrc(a);
-  if (MODE == kFuGreedy) {
-    float mv[1];
-    mv[0] = vp[0];
-#pragma unroll
-    for (int j = 1; j < kPerThread; ++j) mv[0] = fmaxf(mv[0], vp[j]);
-    int badv = 0;
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) badv |= __builtin_amdgcn_class(vp[j], 0x203) ? 1 : 0;
-    block_max_f<1>(mv, L.red);
-    int idx = INT_MAX;
-    if (mv[0] > -INFINITY) {
-#pragma unroll
-      for (int j = kPerThread - 1; j >= 0; --j)
-        if (vp[j] == mv[0]) idx = slice_index<DT>(base, t, j);
-    }
-    __syncthreads();
-    idx = block_min_i(idx, L.i);
-    badv = block_or(badv, L.i);
-    if (t == kStorer)
-      store_rec(rrs, rec_off(a.n_s, T.r, T.s, 0), mv[0], __int_as_float(badv ? -2 : (idx == INT_MAX ? -1 : idx)),
-                0.f, tag);
-    return;
+  const long long t0 = wall_clock64();
+  while (wall_clock64() - t0 < a.poll_delay) __builtin_amdgcn_s_sleep(4);
+  const uint32_t* fl = a.arrive + (int64_t)r * kMaxMembers + (lane < n_u ? lane : 0);
+  unsigned spins = 0;
+  bool timed_out = false;
+  while (!wave_all(__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag)) {
+    if (++spins > a.spin_limit) { timed_out = true; break; }
+    for (int k = 0; k < a.poll_pause; ++k) __builtin_amdgcn_s_sleep(2);
   }
-  float mp = vp[0], mq = T.pair ? vq[0] : -INFINITY;
-#pragma unroll
-  for (int j = 1; j < kPerThread; ++j) mp = fmaxf(mp, vp[j]);
-  if (T.pair) {
-#pragma unroll
-    for (int j = 1; j < kPerThread; ++j) mq = fmaxf(mq, vq[j]);
+  Rec P = load_rec_raw(rrs, rec_off(n_s, r, sl, 0)), Q = load_rec_raw(rrs, rec_off(n_s, r, sl, 1));
+  while (!timed_out && !wave_all(rec_ok(P, tag) && rec_ok(Q, tag))) {
+    if (++spins > a.spin_limit) { timed_out = true; break; }
+    __builtin_amdgcn_s_sleep(4);
+    P = load_rec_raw(rrs, rec_off(n_s, r, sl, 0));
+    Q = load_rec_raw(rrs, rec_off(n_s, r, sl, 1));
   }
-  mp = wave_max_dpp(mp);
-  if (T.pair) mq = wave_max_dpp(mq);
-  refp = mp > -INFINITY ? mp * a.c : 0.f;
-  refq = mq > -INFINITY ? mq * a.c : 0.f;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  if (a.want_t_ent) {
+  L.rec[0][lane][0] = __uint_as_float(P.x);
+  L.rec[0][lane][1] = __uint_as_float(P.y);
+  L.rec[1][lane][0] = __uint_as_float(Q.x);
+  L.rec[1][lane][1] = __uint_as_float(Q.y);
+  if (lane == 0) L.rst = timed_out ? 2 : 0;
+}
+
+// Team normalisers, formed by every wave from the staged records (lane s holds slice s):
+// M = max_s ref_s and Z = sum_s s_s 2^(ref_s - M) for each row, in fp32 with a fixed-order
+// tree sum.  Returns the team status (0 ok, 1 a row non-finite or empty, 2 wait gave up).
+struct TeamNorm {
+  float Mp, Mq, izp, izq, zratio;
+};
+__device__ __forceinline__ int team_norm(const FusedLds& L, int n_s, TeamNorm& N) {
+  const int lane = threadIdx.x & 63;
+  const bool in = lane < n_s;
+  const float pr = L.rec[0][lane][0], ps = L.rec[0][lane][1];
+  const float qr = L.rec[1][lane][0], qs = L.rec[1][lane][1];
+  const bool bad = in && (!(ps == ps) || !(ps < INFINITY) || pr == INFINITY || !(qs == qs) || !(qs < INFINITY) ||
+                          qr == INFINITY);
+  float Mp = in ? pr : -INFINITY, Mq = in ? qr : -INFINITY;
+  dpp_max2(Mp, Mq);
+  float zp = (in && ps > 0.f) ? ps * __builtin_amdgcn_exp2f(pr - Mp) : 0.f;
+  float zq = (in && qs > 0.f) ? qs * __builtin_amdgcn_exp2f(qr - Mq) : 0.f;
+  dpp_sum2(zp, zq);
+  const int st = L.rst;
+  N.Mp = Mp;
+  N.Mq = Mq;
+  N.izp = __builtin_amdgcn_rcpf(zp);
+  N.izq = __builtin_amdgcn_rcpf(zq);
+  N.zratio = zq * N.izp;
+  if (st) return st;
+  return (wave_all(!bad) && zp > 0.f && zq > 0.f && Mp > -INFINITY && Mq > -INFINITY) ? 0 : 1;
+}
+
+// Residual mass of this wave's part of one paired slice, sum [p - q]_+ (guide page "5.1 投机
+// 解码核心原理", §3.2 / §4.1: beta = sum [p - q]_+), from e-values.  With
+// a_p = 2^(ref_p - M_p) / Z_p (likewise a_q) and r = a_p / a_q: if r <= 1 the mass is
+// a_q sum max(e_p r - e_q, 0), else a_p sum max(e_p - e_q / r, 0); e <= 1, so both terms stay
+// below 1 and the max with 0 is the fma's clamp modifier.
+struct ResidualScale {
+  float rr, ir, scale;
+  int form;   // 0: e_p r - e_q, 1: e_p - e_q / r, 2: e_p alone (no draft mass in this wave)
+};
+__device__ __forceinline__ ResidualScale residual_scale(const TeamNorm& N, float refp, float refq) {
+  ResidualScale R;
+  const float dp = refp - N.Mp, dq = refq - N.Mq;
+  const float ap = refp > -INFINITY ? __builtin_amdgcn_exp2f(dp) * N.izp : 0.f;
+  const float aq = refq > -INFINITY ? __builtin_amdgcn_exp2f(dq) * N.izq : 0.f;
+  R.rr = __builtin_amdgcn_exp2f(dp - dq) * N.zratio;
+  R.ir = __builtin_amdgcn_rcpf(R.rr);
+  if (!(aq > 0.f)) { R.form = 2; R.scale = ap; }
+  else if (R.rr <= 1.f) { R.form = 0; R.scale = aq; }
+  else { R.form = 1; R.scale = ap; }
+  return R;
+}
+__device__ __forceinline__ float residual_slice(const ResidualScale& R, const float (&ep)[kPerThread],
+                                                const float (&eq)[kPerThread]) {
+  float sm;
+  if (R.form == 0) {
+    sm = __builtin_amdgcn_fmed3f(fmaf(ep[0], R.rr, -eq[0]), 0.f, 1.f);
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const float tt = fmaf(vp[j], a.c, -refp);
-      const float e = __builtin_amdgcn_exp2f(tt);
-      acc[0] += e;
-      acc[1] = fmaf(e, fmaxf(tt, -200.f), acc[1]);
-      vp[j] = e;
-    }
+    for (int j = 1; j < kPerThread; ++j) sm += __builtin_amdgcn_fmed3f(fmaf(ep[j], R.rr, -eq[j]), 0.f, 1.f);
+  } else if (R.form == 1) {
+    sm = __builtin_amdgcn_fmed3f(fmaf(eq[0], -R.ir, ep[0]), 0.f, 1.f);
+#pragma unroll
+    for (int j = 1; j < kPerThread; ++j) sm += __builtin_amdgcn_fmed3f(fmaf(eq[j], -R.ir, ep[j]), 0.f, 1.f);
   } else {
+    sm = ep[0];
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(vp[j], a.c, -refp));
-      acc[0] += e;
-      vp[j] = e;
-    }
+    for (int j = 1; j < kPerThread; ++j) sm += ep[j];
   }
-  if (T.pair) {
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const float tt = fmaf(vq[j], a.c, -refq);
-      const float e = __builtin_amdgcn_exp2f(tt);
-      acc[2] += e;
-      acc[3] = fmaf(e, fmaxf(tt, -200.f), acc[3]);
-      vq[j] = e;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) acc[k] = wave_sum_dpp(acc[k]);
-  if (lane == 0) {
-    L.wp[0][wave][0] = mp > -INFINITY ? refp : -INFINITY;
-    L.wp[0][wave][1] = acc[0];
-    L.wp[0][wave][2] = acc[1];
-    L.wp[1][wave][0] = mq > -INFINITY ? refq : -INFINITY;
-    L.wp[1][wave][1] = acc[2];
-    L.wp[1][wave][2] = acc[3];
-  }
-  __syncthreads();
-  if (t == kStorer) {
-    float ref, sm, wm;
-    fold_waves(L.wp[0], ref, sm, wm);
-    store_rec(rrs, rec_off(a.n_s, T.r, T.s, 0), ref, sm, wm, tag);
-    if (T.pair) {
-      fold_waves(L.wp[1], ref, sm, wm);
-      store_rec(rrs, rec_off(a.n_s, T.r, T.s, 1), ref, sm, wm, tag);
-      // the arrival flag goes out once both records are visible
-      wait_vmem();
-      __hip_atomic_store(a.arrive + (int64_t)T.r * a.n_s + T.s, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  if (!(mp > -INFINITY)) refp = -INFINITY;
-  if (!(mq > -INFINITY)) refq = -INFINITY;
+  return sm * R.scale;
 }
-
-// Phase 2 of a paired ticket: wave 0 polls the team's records (one slice per lane; lanes past
-// the last slice read it again) and forms the normalisers; then every wave turns its kept
-// e-values into the slice's residual mass sum [p - q]_+ (guide page "5.1 投机解码核心原理",
-// §3.2 / §4.1: beta = sum [p - q]_+).  Returns the tagged mass word; the caller stores it.
-__device__ __forceinline__ uint64_t phase2(const FusedArgs& a, Lds& L, int r, float refp, float refq,
-                                           const float (&ep)[kPerThread], const float (&eq)[kPerThread]) {
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const uint32_t tag = a.tag;
-  if (wave == 0) {
-    const int n_s = a.n_s;
-    const bool in = lane < n_s;
-    const int sl = min(lane, n_s - 1);
-    const __amdgpu_buffer_rsrc_t rrs = rec_rsrc(a);
-    // wait until the team has had time to publish, then poll its arrival flags (one word per
-    // slice) with growing pauses, and read the records once they are all in
-    const long long t0 = wall_clock64();
-    while (wall_clock64() - t0 < a.poll_delay) __builtin_amdgcn_s_sleep(8);
-    const uint32_t* fl = a.arrive + (int64_t)r * n_s;
-    bool timed_out = false;
-    unsigned spins = 0;
-    for (int pause = a.poll_pause > 0 ? a.poll_pause : 4;; pause = a.poll_pause > 0 ? pause : min(2 * pause, 64)) {
-      const uint32_t f = __hip_atomic_load(fl + sl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (wave_all(f == tag)) break;
-      if (++spins > a.spin_limit) { timed_out = true; break; }
-      for (int k = 0; k < pause; ++k) __builtin_amdgcn_s_sleep(2);
-    }
-    Rec P = load_rec_raw(rrs, rec_off(n_s, r, sl, 0)), Q = load_rec_raw(rrs, rec_off(n_s, r, sl, 1));
-    if (!timed_out && !wave_all(rec_ok(P, tag) && rec_ok(Q, tag))) {
-      for (;; ++spins) {
-        if (spins >= a.spin_limit) { timed_out = true; break; }
-        __builtin_amdgcn_s_sleep(4);
-        P = load_rec_raw(rrs, rec_off(n_s, r, sl, 0));
-        Q = load_rec_raw(rrs, rec_off(n_s, r, sl, 1));
-        if (wave_all(rec_ok(P, tag) && rec_ok(Q, tag))) break;
-      }
-    }
-    const float pr = __uint_as_float(P.x), ps = __uint_as_float(P.y);
-    const float qr = __uint_as_float(Q.x), qs = __uint_as_float(Q.y);
-    const bool bad = in && (!(ps == ps) || !(ps < INFINITY) || pr == INFINITY || !(qs == qs) ||
-                            !(qs < INFINITY) || qr == INFINITY);
-    const float Mp = wave_max_dpp(in ? pr : -INFINITY), Mq = wave_max_dpp(in ? qr : -INFINITY);
-    // Z = sum_s s_s 2^(ref_s - M): the difference is exact near the maximum, the product exact
-    // in fp64, the sum fp64
-    const double zp = wave_sum_dpp_d((in && ps > 0.f) ? (double)ps * (double)__builtin_amdgcn_exp2f(pr - Mp) : 0.0);
-    const double zq = wave_sum_dpp_d((in && qs > 0.f) ? (double)qs * (double)__builtin_amdgcn_exp2f(qr - Mq) : 0.0);
-    const bool all_good = wave_all(!bad);
-    if (lane == 0) {
-      const bool ok = !timed_out && all_good && zp > 0.0 && zq > 0.0 && Mp > -INFINITY && Mq > -INFINITY;
-      L.cst = timed_out ? 2 : (ok ? 0 : 1);
-      L.cmb[0] = Mp;
-      L.cmb[1] = Mq;
-      L.cmb[2] = (float)(1.0 / zp);
-      L.cmb[3] = (float)(1.0 / zq);
-    }
-  }
-  __syncthreads();
-  const int st = L.cst;
-  float wmass = 0.f;
-  if (st == 0) {
-    // this wave's alpha = 2^(ref_w - M) / Z of each row; p = e_p alpha_p, q = e_q alpha_q
-    const float ap = refp > -INFINITY ? __builtin_amdgcn_exp2f(refp - L.cmb[0]) * L.cmb[2] : 0.f;
-    const float aq = refq > -INFINITY ? __builtin_amdgcn_exp2f(refq - L.cmb[1]) * L.cmb[3] : 0.f;
-    float sres = 0.f;
-    if (aq > 0.f) {
-      // sum_x [p - q]_+ = alpha_q sum_x max(e_p r - e_q, 0), r = alpha_p / alpha_q
-      const float rr = ap / aq;
-#pragma unroll
-      for (int j = 0; j < kPerThread; ++j) sres += fmaxf(fmaf(ep[j], rr, -eq[j]), 0.f);
-      wmass = wave_sum_dpp(sres) * aq;
-    } else {
-#pragma unroll
-      for (int j = 0; j < kPerThread; ++j) sres += ep[j];
-      wmass = wave_sum_dpp(sres) * ap;
-    }
-  }
-  if (lane == 0) L.rres[wave] = wmass;
-  __syncthreads();
-  float mass = 0.f;
-  if (t == kStorer) {
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mass += L.rres[w];
-    // NaN marks a slice whose wait gave up; 0 when a row is non-finite
-    mass = st == 2 ? __int_as_float(0x7fc00000) : (st == 1 ? 0.f : mass);
-  }
-  return tagged(mass, tag);
-}
-
-// ---------------------------------------------------------------- the kernel
 
 // Stage the draft offsets in LDS and check them as one exclusive prefix (every request is
 // refused when any offset is out of order).
@@ -770,62 +854,235 @@ __device__ __forceinline__ bool stage_cu(const FusedArgs& a, int* cu, int* red) 
   return block_or(bad, red) != 0;
 }
 
-// One workgroup per ticket.  Workgroup i runs on XCD i mod 8 (the dispatcher deals workgroups
-// round-robin over the XCDs), and the slices of team r go to consecutive workgroups of XCD
-// r mod 8, so a team's records meet in that XCD's L2.  A member waits only for members
-// dispatched just before or after it on the same XCD; every wait is bounded.
+// One workgroup per ticket: slices 2u and 2u + 1 of one target row (the second one absent at an
+// odd end), with the same slices of its draft row when the position pairs them.  Workgroup i
+// runs on XCD i mod 8 (the dispatcher deals workgroups round-robin over the XCDs), and the
+// tickets of team r go to consecutive workgroups of XCD r mod 8.  Phase 1 publishes one record
+// per row and slice, then (paired tickets) an arrival flag; a paired ticket then waits for its
+// team's flags, reads the team's records and forms its residual masses from e-values kept in
+// registers (one slice of the target's in LDS, which keeps the workgroup at 64 VGPRs).  A
+// member waits only for members dispatched just before or after it on the same XCD; every
+// wait is bounded.
 template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
-  __shared__ Lds L;
-  const int t = threadIdx.x;
-  const int n_s = a.n_s;
-  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-  const int tl = j / n_s;
-  Ticket T;
-  T.s = j - tl * n_s;
-  T.r = tl * 8 + xcd;
-  if (T.r >= a.n_teams) return;
-  T.pair = false;
-  T.b = 0; T.c0 = 0; T.g = 0; T.i = 0;
-  int drow = -1;
+  __shared__ FusedLds L;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n_s = a.n_s, n_u = (n_s + 1) >> 1;
+  const int xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
+  const int tl = jb / n_u;
+  const int u = jb - tl * n_u;
+  const int r = tl * 8 + xcd;
+  if (r >= a.n_teams) return;
+  const int s0 = 2 * u;
+  const bool has1 = s0 + 1 < n_s;
+  const uint32_t tag = a.tag;
+  const float c = a.c;
+  const __amdgpu_buffer_rsrc_t rrs = rec_rsrc(a);
   constexpr int kEsz = DT == kDtBF16 ? 2 : 4;
-  RawSlice<DT> rp, rq;
-  if (VEC) load_raw_buf<DT>(row_rsrc(row_ptr<DT>(a.tgt, a.tgt_ld, T.r), a.V * kEsz), T.s * kChunk, rp);
-  else load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, T.r), a.V, T.s * kChunk, rp);
+  const int base = s0 * kChunk;
+  const bool tail = base + 2 * kChunk > a.V;   // the row's last ticket
+  RawSlice<DT> rp[2], rq[2];
+  if (VEC) {
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V * kEsz);
+    load_raw_buf<DT>(rs, base, rp[0]);
+    load_raw_buf<DT>(rs, base + kChunk, rp[1]);
+  } else {
+    load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, base, rp[0]);
+    load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, base + kChunk, rp[1]);
+  }
+  bool pair = false;
+  int drow = -1;
   if (MODE == kFuSample) {
     // request of target row r: the largest b < B with cu[b] + b <= r (cu[b] + b grows
-    // strictly with b in a valid offset array), by a binary search through the scalar cache,
-    // which does not queue behind the row loads.  An invalid array (the finalize kernel
-    // reports it) can only give a draft row that is range-checked here.
-    int lo = 0, hi = a.B;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (sload_i32(a.cu + mid) + mid <= T.r) lo = mid;
-      else hi = mid;
+    // strictly with b in a valid offset array).  The draft loads go out at once for the guess
+    // b = r / (G + 1), exact when every request has G draft tokens; one scalar load then
+    // checks it, and a wrong guess falls back to a binary search through the scalar cache and
+    // loads again.  An invalid array (the finalize kernel reports it) can only give a draft
+    // row that is range-checked here.
+    const int lo0 = min(r / (a.G + 1), a.B - 1);
+    const bool guess_pair = r - lo0 < a.n_draft_rows && r % (a.G + 1) < a.G;
+    if (VEC) {
+      const __amdgpu_buffer_rsrc_t rs =
+          row_rsrc(guess_pair ? row_ptr<DT>(a.drf, a.drf_ld, r - lo0) : a.tgt, guess_pair ? a.V * kEsz : 0);
+      load_raw_buf<DT>(rs, base, rq[0]);
+      load_raw_buf<DT>(rs, base + kChunk, rq[1]);
     }
-    const int b = lo;
-    const int c0 = sload_i32(a.cu + b), c1 = sload_i32(a.cu + b + 1);
-    T.b = b; T.c0 = c0; T.g = c1 - c0; T.i = T.r - c0 - b;
-    drow = T.r - b;
-    T.pair = T.i >= 0 && T.i < T.g && drow >= 0 && drow < a.n_draft_rows;
-    if (VEC)
-      load_raw_buf<DT>(row_rsrc(T.pair ? row_ptr<DT>(a.drf, a.drf_ld, drow) : a.tgt, T.pair ? a.V * kEsz : 0),
-                       T.s * kChunk, rq);
-    else if (T.pair)
-      load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, T.s * kChunk, rq);
+    int lo = lo0, c0, c1;
+    sload2_i32(a.cu + lo, c0, c1);
+    if (!(c0 + lo <= r && (lo == a.B - 1 || c1 + lo + 1 > r))) {
+      lo = 0;
+      int hi = a.B;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sload_i32(a.cu + mid) + mid <= r) lo = mid;
+        else hi = mid;
+      }
+      sload2_i32(a.cu + lo, c0, c1);
+    }
+    const int i = r - c0 - lo;
+    drow = r - lo;
+    pair = i >= 0 && i < c1 - c0 && drow >= 0 && drow < a.n_draft_rows;
+    if (VEC) {
+      if (pair != guess_pair || (pair && lo != lo0)) {
+        const __amdgpu_buffer_rsrc_t rs =
+            row_rsrc(pair ? row_ptr<DT>(a.drf, a.drf_ld, drow) : a.tgt, pair ? a.V * kEsz : 0);
+        load_raw_buf<DT>(rs, base, rq[0]);
+        load_raw_buf<DT>(rs, base + kChunk, rq[1]);
+      }
+    } else if (pair) {
+      load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base, rq[0]);
+      load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base + kChunk, rq[1]);
+    }
   }
-  float vp[kPerThread], vq[kPerThread];
-  float refp = 0.f, refq = 0.f;
-  unpack_raw<DT>(rp, vp);
-  if (T.pair) unpack_raw<DT>(rq, vq);
-  if (VEC && (a.V % kChunk) != 0 && T.s == n_s - 1) {
-    mask_tail<DT>(a.V, T.s * kChunk, vp);
-    if (T.pair) mask_tail<DT>(a.V, T.s * kChunk, vq);
+  if (MODE == kFuGreedy) {
+    float vp[2][kPerThread];
+    unpack_raw<DT>(rp[0], vp[0]);
+    unpack_raw<DT>(rp[1], vp[1]);
+    if (VEC && tail) {
+      // logits past V (zeros from the bounds check) become -inf
+      mask_tail<DT>(a.V, base, vp[0]);
+      mask_tail<DT>(a.V, base + kChunk, vp[1]);
+    }
+    // greedy: per slice, the max, the lowest index of it, NaN / +inf seen
+    float m[2];
+    int idx[2], badv = 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      m[k] = max_slice(vp[k], -INFINITY);
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j) badv |= __builtin_amdgcn_class(vp[k][j], 0x203) ? 1 : 0;
+    }
+    dpp_max2(m[0], m[1]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      idx[k] = INT_MAX;
+      if (m[k] > -INFINITY) {
+#pragma unroll
+        for (int j = kPerThread - 1; j >= 0; --j)
+          if (vp[k][j] == m[k]) idx[k] = slice_index<DT>(base + k * kChunk, t, j);
+      }
+      idx[k] = wave_min_i(idx[k]);
+    }
+    badv = wave_or(badv);
+    if (lane == 0) {
+      L.wp[0][wave][0] = m[0];
+      L.wp[1][wave][0] = m[1];
+      L.amax[0][wave] = idx[0];
+      L.amax[1][wave] = idx[1];
+      L.bad[wave] = badv;
+    }
+    __syncthreads();
+    if (t == kStorer) {
+      int bb = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) bb |= L.bad[w];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (k == 1 && !has1) break;
+        float M = -INFINITY;
+        int bi = INT_MAX;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, L.wp[k][w][0]);
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+          if (L.wp[k][w][0] == M) bi = min(bi, L.amax[k][w]);
+        store_rec(rrs, rec_off(n_s, r, s0 + k, 0), M, __int_as_float(bb ? -2 : (bi == INT_MAX ? -1 : bi)), 0.f, tag);
+      }
+    }
+    return;
   }
-  phase1<DT, MODE>(a, L, T, vp, vq, refp, refq);
-  if (MODE == kFuSample && T.pair) {
-    const uint64_t mass_word = phase2(a, L, T.r, refp, refq, vp, vq);
-    if (t == kStorer) st_coh(a.smass + (int64_t)T.r * n_s + T.s, mass_word);
+  // phase 1, target row: per-wave max, e-values, sums; a paired ticket parks slice 1's
+  // e-values in LDS until its residual pass
+  if (VEC && tail) {
+    mask_tail_raw<DT>(a.V, base, rp[0]);
+    mask_tail_raw<DT>(a.V, base + kChunk, rp[1]);
+  }
+  float mp = max_raw<DT>(rp[1], max_raw<DT>(rp[0], -INFINITY));
+  float mp2 = mp;
+  dpp_max2(mp, mp2);
+  float refp = mp > -INFINITY ? mp * c : 0.f;
+  float ep[2][kPerThread];
+  float sp0, sp1, wp0, wp1;
+  exp_raw<DT>(rp[0], ep[0], c, refp, sp0, wp0);
+  // slice 1: the e-values of a paired ticket go to LDS as they are formed
+  if (pair) exp_raw_stash<DT>(rp[1], L.stash, c, refp, sp1, wp1);
+  else exp_raw<DT>(rp[1], ep[1], c, refp, sp1, wp1);
+  if (!(mp > -INFINITY)) refp = -INFINITY;
+  float sq0 = 0.f, sq1 = 0.f, wq = 0.f, refq = -INFINITY;
+  float eq[2][kPerThread];
+  if (pair) {
+    // phase 1, draft row
+    if (VEC && tail) {
+      mask_tail_raw<DT>(a.V, base, rq[0]);
+      mask_tail_raw<DT>(a.V, base + kChunk, rq[1]);
+    }
+    float mq = max_raw<DT>(rq[1], max_raw<DT>(rq[0], -INFINITY));
+    float mq2 = mq;
+    dpp_max2(mq, mq2);
+    refq = mq > -INFINITY ? mq * c : 0.f;
+    float wq0, wq1;
+    exp_raw<DT>(rq[0], eq[0], c, refq, sq0, wq0);
+    exp_raw<DT>(rq[1], eq[1], c, refq, sq1, wq1);
+    wq = wq0 + wq1;
+    if (!(mq > -INFINITY)) refq = -INFINITY;
+  }
+  float wpe = wp0 + wp1;
+  dpp_sum4(sp0, sp1, sq0, sq1);
+  dpp_sum2(wpe, wq);
+  if (lane == 0) {
+    L.wp[0][wave][0] = refp;
+    L.wp[0][wave][1] = sp0;
+    L.wp[0][wave][2] = sp1;
+    L.wp[0][wave][3] = wpe;
+    L.wp[1][wave][0] = refq;
+    L.wp[1][wave][1] = sq0;
+    L.wp[1][wave][2] = sq1;
+    L.wp[1][wave][3] = wq;
+  }
+  __syncthreads();
+  if (t == kStorer) {
+    // slice 0 carries the ticket's entropy numerator, slice 1 none (the records of a row are
+    // combined with a common reference, so the split does not matter)
+    float ref, sm, wm;
+    fold_waves<1, true>(L.wp[0], ref, sm, wm);
+    store_rec(rrs, rec_off(n_s, r, s0, 0), ref, sm, wm, tag);
+    if (has1) {
+      fold_waves<2, false>(L.wp[0], ref, sm, wm);
+      store_rec(rrs, rec_off(n_s, r, s0 + 1, 0), ref, sm, wm, tag);
+    }
+    if (pair) {
+      fold_waves<1, true>(L.wp[1], ref, sm, wm);
+      store_rec(rrs, rec_off(n_s, r, s0, 1), ref, sm, wm, tag);
+      if (has1) {
+        fold_waves<2, false>(L.wp[1], ref, sm, wm);
+        store_rec(rrs, rec_off(n_s, r, s0 + 1, 1), ref, sm, wm, tag);
+      }
+      __hip_atomic_store(a.arrive + (int64_t)r * kMaxMembers + u, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (!pair) return;
+  if (wave == 0) team_gather(a, L, r, n_u);
+  __syncthreads();
+  TeamNorm N;
+  const int st = team_norm(L, n_s, N);
+  float m0 = 0.f, m1 = 0.f;
+  if (st == 0) {
+    const ResidualScale R = residual_scale(N, refp, refq);
+    m0 = residual_slice(R, ep[0], eq[0]);
+    float ep1[kPerThread];
+#pragma unroll
+    for (int k = 0; k < kPerThread / 4; ++k) {
+      const float4 v4 = L.stash[k][t];
+      ep1[4 * k] = v4.x; ep1[4 * k + 1] = v4.y; ep1[4 * k + 2] = v4.z; ep1[4 * k + 3] = v4.w;
+    }
+    m1 = residual_slice(R, ep1, eq[1]);
+  }
+  dpp_sum2(m0, m1);
+  // NaN marks a slice whose wait gave up; 0 when a row is non-finite
+  if (st == 2) m0 = m1 = __int_as_float(0x7fc00000);
+  if (lane == 0) {
+    st_coh(a.smass + ((int64_t)r * n_s + s0) * kWaves + wave, tagged(m0, tag));
+    if (has1) st_coh(a.smass + ((int64_t)r * n_s + s0 + 1) * kWaves + wave, tagged(m1, tag));
   }
 }
 
@@ -852,9 +1109,8 @@ __global__ __launch_bounds__(kThreads) void k_fused_finalize(FusedArgs a) {
 template <int DT, bool VEC, int MODE>
 static hipError_t launch_fused_t(FusedArgs a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const int teams8 = (a.n_teams + 7) / 8;
-  const long long grid = 8ll * teams8 * a.n_s;
+  const long long grid = 8ll * teams8 * ((a.n_s + 1) / 2);
   if (grid < 1 || grid > 0x7fffffffll) return hipErrorInvalidConfiguration;
-  a.n_fin = 0;
   if (getenv("SPEC_VERIFY_DEBUG"))
     fprintf(stderr, "[specverify] fused grid %lld tickets %d slices %d mode %d\n", grid, a.n_tickets, a.n_s, a.mode);
   // optional events bracket the streaming kernel alone (benchmark timing)

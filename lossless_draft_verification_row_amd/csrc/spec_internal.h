@@ -16,6 +16,7 @@ constexpr int kMaxGamma = 64;     // gamma_max bound (one finalize thread per po
 constexpr int kMaxSlicesFused = 64;    // V <= 64 * 4096
 constexpr int kMaxTeamsFused = 4096;   // target rows
 constexpr int kMaxReqFused = 1024;     // requests
+constexpr int kMaxMembers = 32;        // streaming workgroups of one target row (two slices each)
 constexpr int kFuSample = 0;           // draft logits, temperature > 0
 constexpr int kFuTokenOnly = 1;        // token-only draft, temperature > 0
 constexpr int kFuGreedy = 2;           // temperature 0
@@ -113,16 +114,15 @@ struct FusedArgs {
   const int32_t* cu;
   const int32_t* tokens;
   int B, G, V, n_s, n_draft_rows, n_teams, n_tickets, mode, want_t_ent;
-  int n_fin;            // finalizer workgroups (set at launch)
   unsigned spin_limit;
   uint32_t tag;         // this call's record tag (never 0)
   float c;
   uint64_t seed, step;
-  uint64_t* part;       // [n_teams][n_s][2 rows][3 words] tagged slice records
-  uint64_t* smass;      // [n_teams][n_s] tagged residual masses
-  uint32_t* arrive;     // [n_teams][n_s] the call's tag once a slice's records are visible
+  uint64_t* part;       // [n_teams][2 rows][n_s] 16-byte tagged slice records
+  uint64_t* smass;      // [n_teams][n_s][4 waves] tagged residual masses
+  uint32_t* arrive;     // [n_teams][kMaxMembers] a member's flag: the call's tag once its records are out
   int poll_delay;       // wait before the first team poll, in 10 ns ticks
-  int poll_pause;       // pause between polls (0: growing)
+  int poll_pause;       // pause between team polls, in units of 128 cycles
   int32_t* out_tokens;
   int32_t* out_num_accepted;
   float* out_req_stats;
