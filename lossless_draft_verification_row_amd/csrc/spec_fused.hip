@@ -52,7 +52,8 @@ struct TeamL {      // team statistics of one position, kept in LDS by the final
 
 struct FinScratch {
   TeamL team[kMaxGamma + 1];
-  double py[kMaxGamma], qy[kMaxGamma], u0[kMaxGamma];
+  double py[kMaxGamma], qy[kMaxGamma];
+  double us[kMaxGamma + 1][3];   // sampler uniforms (Philox words 1..3) of every position
   int ytok[kMaxGamma];
   double gm[kChunk / kGroup];
   float dh[kMaxGamma], dm[kMaxGamma];
@@ -80,10 +81,7 @@ __device__ __forceinline__ uint32_t tag_of(uint64_t w) { return (uint32_t)(w >> 
 // record of an earlier call, or one read while it was being written, is never taken.
 // Layout: [team][row: 0 target, 1 draft][slice].
 __device__ __forceinline__ uint32_t rec_mix(uint32_t a, uint32_t b, uint32_t c) {
-  uint32_t h = a * 0x9E3779B1u;
-  h ^= ((b << 11) | (b >> 21)) * 0x85EBCA77u;
-  h ^= ((c << 22) | (c >> 10)) * 0xC2B2AE3Du;
-  return h ^ (h >> 15);
+  return a ^ ((b << 11) | (b >> 21)) ^ ((c << 22) | (c >> 10)) ^ 0x9E3779B9u;
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const FusedArgs& a) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)a.part, (short)0, (int)((size_t)a.n_teams * 2 * a.n_s * 16),
@@ -240,6 +238,18 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
     }
   }
 
+  // the Philox block of every position (1-based i = t + 1): word 0 is the accept draw, words
+  // 1..3 the sampler's uniforms if the emitted token is drawn there; independent of the records
+  double u_acc = 0.0;
+  if (t <= g) {
+    uint64_t w[4];
+    philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(t + 1), 0, 0, w);
+    u_acc = u53(w[0]);
+    F.us[t][0] = u53(w[1]);
+    F.us[t][1] = u53(w[2]);
+    F.us[t][2] = u53(w[3]);
+  }
+
   // A. combine each team's records (one wave per team); the streaming kernel has finished
   for (int ti = wave; ti <= g; ti += kWaves) {
     const int r = c0 + b + ti;
@@ -249,15 +259,23 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
     double sm = 0.0;
     bool ok = true;
     if (in) {
-      ok = load_rec(rrs, rec_off(n_s, r, lane, 0), tag, pr, ps, pw);
+      Rec RP = load_rec_raw(rrs, rec_off(n_s, r, lane, 0)), RQ = {0, 0, 0, 0};
+      uint64_t mw4[kWaves] = {0, 0, 0, 0};
       if (pair) {
-        ok = load_rec(rrs, rec_off(n_s, r, lane, 1), tag, qr, qs, qw) && ok;
+        RQ = load_rec_raw(rrs, rec_off(n_s, r, lane, 1));
         const uint64_t* mw = a.smass + ((int64_t)r * n_s + lane) * kWaves;
 #pragma unroll
+        for (int w = 0; w < kWaves; ++w) mw4[w] = ld_coh(mw + w);
+      }
+      ok = rec_ok(RP, tag);
+      pr = __uint_as_float(RP.x); ps = __uint_as_float(RP.y); pw = __uint_as_float(RP.z);
+      if (pair) {
+        ok = ok && rec_ok(RQ, tag);
+        qr = __uint_as_float(RQ.x); qs = __uint_as_float(RQ.y); qw = __uint_as_float(RQ.z);
+#pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-          const uint64_t m = ld_coh(mw + w);
-          sm += (double)lo_f(m);
-          ok = ok && tag_of(m) == tag;
+          sm += (double)lo_f(mw4[w]);
+          ok = ok && tag_of(mw4[w]) == tag;
         }
       }
     }
@@ -347,11 +365,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       if (!yv) { rej = true; why = kStBadToken; }
       else if (MODE == kFuGreedy) rej = y != T.amax;
       else if (!(qyd > 0.0)) { rej = true; why = kStZeroQ; }
-      else {
-        uint64_t w[4];
-        philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(t + 1), 0, 0, w);
-        rej = !(u53(w[0]) < fmin(1.0, pyd / qyd));
-      }
+      else rej = !(u_acc < fmin(1.0, pyd / qyd));
     }
   }
   // C. request flags and the first rejection (wave 0 covers positions 0..63)
@@ -375,11 +389,9 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       F.y = jj >= 0 ? F.ytok[jj] : -1;
       // wkind: 0 = p of the row, 1 = [p - q]_+, 2 = p without token y
       F.wkind = (jj < 0) ? 0 : (MODE == kFuSample ? 1 : 2);
-      uint64_t w[4];
-      philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(F.pos + 1), 0, 0, w);
-      F.u[0] = u53(w[1]);
-      F.u[1] = u53(w[2]);
-      F.u[2] = u53(w[3]);
+      F.u[0] = F.us[F.pos][0];
+      F.u[1] = F.us[F.pos][1];
+      F.u[2] = F.us[F.pos][2];
       F.status = status;
       F.kpick = -1;
       if (a.out_req_stats) {
@@ -737,6 +749,25 @@ __device__ __forceinline__ void fold_waves(const float (*pw)[4], float& ref, flo
   }
 }
 
+// fold_waves with the sum field K and the entropy flag W chosen at run time (one lane per record).
+__device__ __forceinline__ void fold_waves_rt(const float (*pw)[4], int K, bool W, float& ref, float& s, float& w) {
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) M = fmaxf(M, pw[k][0]);
+  ref = 0.f; s = 0.f; w = 0.f;
+  if (!(M > -INFINITY)) return;
+  ref = M;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    if (!(pw[k][0] > -INFINITY)) continue;
+    const float d = pw[k][0] - M;
+    const float f = __builtin_amdgcn_exp2f(d);
+    const float sk = pw[k][K];
+    s = fmaf(sk, f, s);
+    w = fmaf(f, fmaf(sk, d, W ? pw[k][3] : 0.f), w);
+  }
+}
+
 // Wave 0 of a paired ticket: wait until every member of the team has raised its arrival flag
 // (the team's flags share one cache line, so a poll reads one line; lanes past the last member
 // read the first flag again), then read the team's records (one slice per lane) into LDS.  A
@@ -1040,25 +1071,20 @@ __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
     L.wp[1][wave][3] = wq;
   }
   __syncthreads();
-  if (t == kStorer) {
-    // slice 0 carries the ticket's entropy numerator, slice 1 none (the records of a row are
-    // combined with a common reference, so the split does not matter)
-    float ref, sm, wm;
-    fold_waves<1, true>(L.wp[0], ref, sm, wm);
-    store_rec(rrs, rec_off(n_s, r, s0, 0), ref, sm, wm, tag);
-    if (has1) {
-      fold_waves<2, false>(L.wp[0], ref, sm, wm);
-      store_rec(rrs, rec_off(n_s, r, s0 + 1, 0), ref, sm, wm, tag);
+  if (wave == kWaves - 1) {
+    // lanes 0..3 of the last wave fold and store the records (row k >> 1, slice k & 1) side by
+    // side; slice 0 carries the ticket's entropy numerator, slice 1 none (the records of a row
+    // are combined with a common reference, so the split does not matter)
+    const int row = lane >> 1, sl = lane & 1;
+    if (lane < 4 && (row == 0 || pair) && (sl == 0 || has1)) {
+      float ref, sm, wm;
+      fold_waves_rt(L.wp[row], 1 + sl, sl == 0, ref, sm, wm);
+      store_rec(rrs, rec_off(n_s, r, s0 + sl, row), ref, sm, wm, tag);
     }
-    if (pair) {
-      fold_waves<1, true>(L.wp[1], ref, sm, wm);
-      store_rec(rrs, rec_off(n_s, r, s0, 1), ref, sm, wm, tag);
-      if (has1) {
-        fold_waves<2, false>(L.wp[1], ref, sm, wm);
-        store_rec(rrs, rec_off(n_s, r, s0 + 1, 1), ref, sm, wm, tag);
-      }
+    asm volatile("" ::: "memory");
+    // the arrival flag follows the records (a poller that sees it before they land re-reads)
+    if (pair && lane == 0)
       __hip_atomic_store(a.arrive + (int64_t)r * kMaxMembers + u, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
   if (!pair) return;
   if (wave == 0) team_gather(a, L, r, n_u);
