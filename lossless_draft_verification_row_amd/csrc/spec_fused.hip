@@ -238,18 +238,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
     }
   }
 
-  // the Philox block of every position (1-based i = t + 1): word 0 is the accept draw, words
-  // 1..3 the sampler's uniforms if the emitted token is drawn there; independent of the records
   double u_acc = 0.0;
-  if (t <= g) {
-    uint64_t w[4];
-    philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(t + 1), 0, 0, w);
-    u_acc = u53(w[0]);
-    F.us[t][0] = u53(w[1]);
-    F.us[t][1] = u53(w[2]);
-    F.us[t][2] = u53(w[3]);
-  }
-
   // A. combine each team's records (one wave per team); the streaming kernel has finished
   for (int ti = wave; ti <= g; ti += kWaves) {
     const int r = c0 + b + ti;
@@ -258,15 +247,29 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
     float pr = -INFINITY, ps = 0.f, pw = 0.f, qr = -INFINITY, qs = 0.f, qw = 0.f;
     double sm = 0.0;
     bool ok = true;
+    Rec RP = {0, 0, 0, 0}, RQ = {0, 0, 0, 0};
+    uint64_t mw4[kWaves] = {0, 0, 0, 0};
     if (in) {
-      Rec RP = load_rec_raw(rrs, rec_off(n_s, r, lane, 0)), RQ = {0, 0, 0, 0};
-      uint64_t mw4[kWaves] = {0, 0, 0, 0};
+      RP = load_rec_raw(rrs, rec_off(n_s, r, lane, 0));
       if (pair) {
         RQ = load_rec_raw(rrs, rec_off(n_s, r, lane, 1));
         const uint64_t* mw = a.smass + ((int64_t)r * n_s + lane) * kWaves;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) mw4[w] = ld_coh(mw + w);
       }
+    }
+    if (ti == wave && t <= g) {
+      // while the first team's records are in flight: the Philox block of position t (1-based
+      // i = t + 1), word 0 the accept draw, words 1..3 the sampler's uniforms if the emitted
+      // token is drawn there
+      uint64_t w[4];
+      philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(t + 1), 0, 0, w);
+      u_acc = u53(w[0]);
+      F.us[t][0] = u53(w[1]);
+      F.us[t][1] = u53(w[2]);
+      F.us[t][2] = u53(w[3]);
+    }
+    if (in) {
       ok = rec_ok(RP, tag);
       pr = __uint_as_float(RP.x); ps = __uint_as_float(RP.y); pw = __uint_as_float(RP.z);
       if (pair) {
@@ -788,6 +791,7 @@ __device__ __forceinline__ void team_gather(const FusedArgs& a, FusedLds& L, int
     if (++spins > a.spin_limit) { timed_out = true; break; }
     for (int k = 0; k < a.poll_pause; ++k) __builtin_amdgcn_s_sleep(2);
   }
+  // a poll that fails costs little (one line); the records are read once the flags are up
   Rec P = load_rec_raw(rrs, rec_off(n_s, r, sl, 0)), Q = load_rec_raw(rrs, rec_off(n_s, r, sl, 1));
   while (!timed_out && !wave_all(rec_ok(P, tag) && rec_ok(Q, tag))) {
     if (++spins > a.spin_limit) { timed_out = true; break; }
