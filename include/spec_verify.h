@@ -68,7 +68,10 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
  * >= V = off; otherwise every logit >= the k-th largest is kept (ties kept).  top_p >= 1 =
  * off; otherwise the smallest set of largest values whose mass over the top-k set reaches
  * top_p is kept (a boundary value is kept with all its ties).  Order: temperature, top-k,
- * top-p.  Filtering needs 1 <= top_k <= 256 in this build (top-p alone: SPEC_ERR_UNSUPPORTED). */
+ * top-p.  Every entry point filters with 1 <= top_k <= 256 (top-p optional); top-p alone
+ * returns SPEC_ERR_UNSUPPORTED in this build.  A filtered row whose top-k set (k plus boundary
+ * ties) holds more than 512 tokens cannot be represented by the sparse path: it is reported
+ * (SPEC_STATUS_FILTER_OVERFLOW, or kept_count -1 in spec_row_stats) instead of a result. */
 typedef struct {
   float temperature;
   int top_k;
@@ -135,7 +138,9 @@ size_t spec_verify_workspace_bytes(int B, int V, int gamma_max, spec_dtype dt,
  * may be NULL: max_logit, argmax (lowest index of the maximum), log_z = ln sum_kept
  * exp(l/T), entropy_bits, max_prob, kept_count (kept tokens with a finite logit).  With
  * temperature 0 the row is one-hot at the argmax: entropy 0, max_prob 1, kept 1, log_z NaN.
- * A row with a NaN / +inf logit or no finite logit gives argmax -1 and NaN statistics. */
+ * A row with a NaN / +inf logit or no finite logit gives argmax -1, NaN statistics and kept
+ * count 0; a filtered row whose top-k set overflows the sparse path gives argmax -1, NaN
+ * statistics and kept count -1. */
 int spec_row_stats(int R, int V, spec_dtype dt, const void* logits, int64_t ld,
                    spec_sampling_params sp,
                    float* max_logit, int32_t* argmax, float* log_z, float* entropy_bits,
@@ -148,7 +153,8 @@ size_t spec_row_stats_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling
  * (guide §3.2), or from p when q_logits is NULL, with the same three-level sampler.
  *  uniforms: [R, 3] fp64 in [0, 1) on the device, or NULL for Philox counter (r, 0, 1, 0),
  *  words 1..3.  Outputs [R]: out_token, out_mass (beta = sum [p - q]_+, or 1 without q; NaN
- *  for non-finite rows), out_status (NONFINITE, RESIDUAL_EMPTY: beta = 0, drawn from p). */
+ *  for non-finite rows), out_status (NONFINITE, RESIDUAL_EMPTY: beta = 0, drawn from p,
+ *  FILTER_OVERFLOW: token -1). */
 int spec_residual_sample(int R, int V, spec_dtype dt,
                          const void* p_logits, int64_t p_ld, const void* q_logits, int64_t q_ld,
                          spec_sampling_params sp, const double* uniforms,

@@ -110,6 +110,12 @@ bool filter_supported(int B, int V, int gamma_max, const spec_sampling_params& s
   return sp.temperature > 0.f && sp.top_k >= 1 && sp.top_k < V && sp.top_k <= kFilterMaxK && B <= kMaxReqFused &&
          (int64_t)B * (gamma_max + 1) <= kMaxTeamsFused && n_chunks(V) <= kMaxSlicesFused;
 }
+// The same sparse path for plain rows (spec_row_stats, spec_residual_sample): R rows, or R row
+// pairs, each one team of its own.
+bool filter_rows_supported(int R, int V, const spec_sampling_params& sp) {
+  return sp.temperature > 0.f && sp.top_k >= 1 && sp.top_k < V && sp.top_k <= kFilterMaxK &&
+         n_chunks(V) <= kMaxSlicesFused && (int64_t)R * n_chunks(V) <= 0x3fffffff;
+}
 size_t filter_bytes(int64_t n_slots, int V, int k) {
   const int64_t ns = n_chunks(V);
   return kHeaderBytes + align_up((size_t)(n_slots * ns * filter_cap(k)) * sizeof(CandEntry)) +
@@ -119,6 +125,37 @@ size_t filter_bytes(int64_t n_slots, int V, int k) {
 
 float exp2_scale(const spec_sampling_params& sp) {
   return sp.temperature > 0.f ? (float)(1.4426950408889634 / (double)sp.temperature) : 0.f;
+}
+
+// Launch descriptor of the sparse path over R plain rows (p rows as targets, q rows, if any,
+// as their draft rows), its arrays carved from the workspace.
+FilterArgs plain_filter_args(int R, int V, const void* p, int64_t p_ld, const void* q, int64_t q_ld,
+                             const spec_sampling_params& sp, void* workspace) {
+  FilterArgs f;
+  memset(&f, 0, sizeof(f));
+  const int ns = n_chunks(V);
+  f.tgt = p;
+  f.tgt_ld = p_ld;
+  f.drf = q;
+  f.drf_ld = q_ld;
+  f.B = R;
+  f.V = V;
+  f.n_s = ns;
+  f.n_teams = R;
+  f.n_draft_rows = q ? R : 0;
+  f.n_slots = q ? 2 * R : R;
+  f.k = sp.top_k;
+  f.cap = filter_cap(sp.top_k);
+  f.top_p = sp.top_p;
+  f.c = 1.4426950408889634 / (double)sp.temperature;
+  f.inv_t = 1.0 / (double)sp.temperature;
+  f.direct = 1;
+  Carve cv{(char*)workspace};
+  f.cand = cv.take<CandEntry>((size_t)f.n_slots * ns * f.cap * sizeof(CandEntry));
+  f.chead = cv.take<CandHead>((size_t)f.n_slots * ns * sizeof(CandHead));
+  f.kept = cv.take<KeptEntry>((size_t)f.n_slots * kKeepMax * sizeof(KeptEntry));
+  f.rstat = cv.take<RowStat2>((size_t)f.n_slots * sizeof(RowStat2));
+  return f;
 }
 
 }  // namespace
@@ -168,14 +205,14 @@ size_t spec_verify_workspace_bytes(int B, int V, int gamma_max, spec_dtype dt, s
 size_t spec_row_stats_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling_params sp) {
   (void)dt;
   if (R <= 0 || V <= 0) return 0;
-  if (filter_on(V, sp)) return 0;
+  if (filter_on(V, sp)) return filter_rows_supported(R, V, sp) ? filter_bytes(R, V, sp.top_k) : 0;
   return dense_bytes(R, V);
 }
 
 size_t spec_residual_sample_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling_params sp) {
   (void)dt;
   if (R <= 0 || V <= 0) return 0;
-  if (filter_on(V, sp)) return 0;
+  if (filter_on(V, sp)) return filter_rows_supported(R, V, sp) ? filter_bytes(2 * (int64_t)R, V, sp.top_k) : 0;
   return dense_bytes(R, V);
 }
 
@@ -371,12 +408,25 @@ int spec_row_stats(int R, int V, spec_dtype dt, const void* logits, int64_t ld, 
   if (R == 0) return SPEC_OK;
   if (!logits || ld < V) return SPEC_ERR_INVALID;
   if ((int64_t)R * 2 > (int64_t)INT32_MAX / 2) return SPEC_ERR_INVALID;
-  if (filter_on(V, sp)) return SPEC_ERR_UNSUPPORTED;
+  if (filter_on(V, sp) && !filter_rows_supported(R, V, sp)) return SPEC_ERR_UNSUPPORTED;
   const size_t need = spec_row_stats_workspace_bytes(R, V, dt, sp);
   if (!workspace || workspace_bytes < need) return SPEC_ERR_WORKSPACE;
   if (((uintptr_t)workspace % kAlign) != 0) return SPEC_ERR_INVALID;
   const bool greedy = sp.temperature == 0.f;
   const int ns = n_chunks(V);
+  if (filter_on(V, sp)) {
+    FilterArgs f = plain_filter_args(R, V, logits, ld, nullptr, 0, sp, workspace);
+    f.rso.enabled = 1;
+    f.rso.max_logit = max_logit;
+    f.rso.argmax = argmax;
+    f.rso.log_z = log_z;
+    f.rso.entropy_bits = entropy_bits;
+    f.rso.max_prob = max_prob;
+    f.rso.kept_count = kept_count;
+    const hipError_t e = launch_filter_rows(f, dt == SPEC_BF16 ? kDtBF16 : kDtF32, aligned16(logits, ld, dt) ? 1 : 0, 0,
+                                            (hipStream_t)hip_stream);
+    return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
+  }
 
   RowMap map;
   memset(&map, 0, sizeof(map));
@@ -422,13 +472,25 @@ int spec_residual_sample(int R, int V, spec_dtype dt, const void* p_logits, int6
   if (!p_logits || p_ld < V || !out_token || !out_status) return SPEC_ERR_INVALID;
   if (q_logits && q_ld < V) return SPEC_ERR_INVALID;
   if ((int64_t)R * 2 > (int64_t)INT32_MAX / 2) return SPEC_ERR_INVALID;
-  if (filter_on(V, sp)) return SPEC_ERR_UNSUPPORTED;
+  if (filter_on(V, sp) && !filter_rows_supported(R, V, sp)) return SPEC_ERR_UNSUPPORTED;
   const size_t need = spec_residual_sample_workspace_bytes(R, V, dt, sp);
   if (!workspace || workspace_bytes < need) return SPEC_ERR_WORKSPACE;
   if (((uintptr_t)workspace % kAlign) != 0) return SPEC_ERR_INVALID;
   const bool greedy = sp.temperature == 0.f;
   const int ns = n_chunks(V);
   const hipStream_t st = (hipStream_t)hip_stream;
+  if (filter_on(V, sp)) {
+    FilterArgs f = plain_filter_args(R, V, p_logits, p_ld, q_logits, q_ld, sp, workspace);
+    f.uniforms = uniforms;
+    f.seed = seed;
+    f.step = step;
+    f.out_tokens = out_token;
+    f.out_mass = out_mass;
+    f.out_status = out_status;
+    const int vec = aligned16(p_logits, p_ld, dt) && aligned16(q_logits, q_ld, dt);
+    const hipError_t e = launch_filter_rows(f, dt == SPEC_BF16 ? kDtBF16 : kDtF32, vec, 1, st);
+    return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
+  }
 
   RowMap map;
   memset(&map, 0, sizeof(map));

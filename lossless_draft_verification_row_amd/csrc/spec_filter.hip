@@ -381,7 +381,14 @@ __global__ __launch_bounds__(kThreads) void k_filt_slices(FilterArgs a) {
   // the draft row of target row r, if r is not the last row of its request (scalar-cache
   // binary search over the offsets; the draft loads go out right after)
   int drow = -1;
-  if (PAIRED) {
+  if (PAIRED && a.direct) {
+    if (r < a.n_draft_rows) drow = r;
+    if (VEC)
+      load_raw_buf<DT>(row_rsrc(drow >= 0 ? row_ptr<DT>(a.drf, a.drf_ld, drow) : a.tgt, drow >= 0 ? a.V * kEsz : 0),
+                       base, rq);
+    else if (drow >= 0)
+      load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base, rq);
+  } else if (PAIRED) {
     int lo = 0, hi = a.B;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -569,7 +576,7 @@ __global__ __launch_bounds__(kThreads) void k_filt_rows(FilterArgs a) {
   __syncthreads();
   (void)lane;
   RowStat2 st;
-  st.n = 0; st.flags = L.flags; st.m = -INFINITY; st.argmax = -1;
+  st.n = 0; st.flags = L.flags; st.m = -INFINITY; st.argmax = -1; st.kept_finite = 0; st.pad = 0;
   st.log_z = 0.0; st.entropy = 0.0; st.max_prob = 0.0; st.z = 0.0;
   if (nk == 0 && !(st.flags & kFlagBad)) st.flags |= kFlagEmpty;
   if (st.flags) {
@@ -608,11 +615,12 @@ __global__ __launch_bounds__(kThreads) void k_filt_rows(FilterArgs a) {
   __syncthreads();
   // Z_S, then p, entropy, the index order of S
   double zs = 0.0;
-  int ns_t = 0;
-  for (int j = t; j < nk; j += kThreads) if (L.keep[j]) { zs += L.ke[j]; ++ns_t; }
+  int ns_t = 0, nf_t = 0;
+  for (int j = t; j < nk; j += kThreads)
+    if (L.keep[j]) { zs += L.ke[j]; ++ns_t; nf_t += L.kv[j] > -INFINITY ? 1 : 0; }
   zs = block_sum_dd(zs, L.red);
-  int ns = ns_t, d2 = 0, ns_all, tz2;
-  block_scan2(ns, d2, L.sel, ns_all, tz2);
+  int ns = ns_t, nf = nf_t, ns_all, nf_all;
+  block_scan2(ns, nf, L.sel, ns_all, nf_all);
   double ent = 0.0;
   KeptEntry* kept = a.kept + (int64_t)slot * kKeepMax;
   for (int j = t; j < nk; j += kThreads) {
@@ -630,6 +638,7 @@ __global__ __launch_bounds__(kThreads) void k_filt_rows(FilterArgs a) {
   ent = block_sum_dd(ent, L.red);
   if (t == 0) {
     st.n = ns_all;
+    st.kept_finite = nf_all;
     st.m = m;
     st.argmax = amx;
     st.z = zs;
@@ -678,6 +687,60 @@ __device__ __forceinline__ int seq_pick(int n, double target, Wt w) {
     if (cum > target) return i;
   }
   return last;
+}
+
+// One thread: the three-level inverse CDF (reading R6: chunks of 4096, groups of 64, tokens)
+// over sparse weights wv[j] at increasing token indices xs[j], j < n; every mass is a
+// sequential fp64 sum in index order, empty groups add nothing.  chunk[] receives the n_s chunk
+// masses.  Returns the token (the last positive one where rounding leaves none), or -1 when the
+// total W is not positive.
+__device__ int sparse_sample(const int* xs, const double* wv, int n, int n_s, const double* u, double* chunk,
+                             double& W) {
+  int j = 0;
+  W = 0.0;
+  for (int k = 0; k < n_s; ++k) {
+    double Sk = 0.0;
+    while (j < n && (xs[j] >> 12) == k) {
+      const int grp = xs[j] >> 6;
+      double M = 0.0;
+      while (j < n && (xs[j] >> 6) == grp) { M += wv[j]; ++j; }
+      Sk += M;
+    }
+    chunk[k] = Sk;
+    W += Sk;
+  }
+  if (!(W > 0.0)) return -1;
+  const int kc = seq_pick(n_s, u[0] * W, [&](int k) { return chunk[k]; });
+  int j0 = 0;
+  while (j0 < n && (xs[j0] >> 12) < kc) ++j0;
+  int j1 = j0;
+  while (j1 < n && (xs[j1] >> 12) == kc) ++j1;
+  double Sg = 0.0;
+  for (int jj = j0; jj < j1;) {
+    const int grp = xs[jj] >> 6;
+    double M = 0.0;
+    while (jj < j1 && (xs[jj] >> 6) == grp) { M += wv[jj]; ++jj; }
+    Sg += M;
+  }
+  // level 2 over the chunk's groups, then level 3
+  const double t2 = u[1] * Sg;
+  double cum = 0.0;
+  int gj0 = -1, gj1 = -1, lj0 = -1, lj1 = -1;
+  for (int jj = j0; jj < j1;) {
+    const int grp = xs[jj] >> 6;
+    const int s0 = jj;
+    double M = 0.0;
+    while (jj < j1 && (xs[jj] >> 6) == grp) { M += wv[jj]; ++jj; }
+    cum += M;
+    if (M > 0.0) { lj0 = s0; lj1 = jj; }
+    if (cum > t2) { gj0 = s0; gj1 = jj; break; }
+  }
+  if (gj0 < 0) { gj0 = lj0; gj1 = lj1; }
+  if (gj0 < 0) return -1;
+  double Mg = 0.0;
+  for (int jj = gj0; jj < gj1; ++jj) Mg += wv[jj];
+  const int e = seq_pick(gj1 - gj0, u[2] * Mg, [&](int q) { return wv[gj0 + q]; });
+  return e >= 0 ? xs[gj0 + e] : -1;
 }
 
 template <int MODE>
@@ -869,57 +932,12 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
       __syncthreads();
       int again = 0;
       if (t == 0) {
-        const int* xs = F.xs;
-        const double* wv = F.w;
-        // chunk masses: group masses summed in index order, chunk by chunk
-        int j = 0;
-        double W = 0.0;
-        for (int k = 0; k < a.n_s; ++k) {
-          double Sk = 0.0;
-          while (j < n && (xs[j] >> 12) == k) {
-            const int grp = xs[j] >> 6;
-            double M = 0.0;
-            while (j < n && (xs[j] >> 6) == grp) { M += wv[j]; ++j; }
-            Sk += M;
-          }
-          F.chunk[k] = Sk;
-          W += Sk;
-        }
+        double W;
+        const int x = sparse_sample(F.xs, F.w, n, a.n_s, F.u, F.chunk, W);
         if (!(W > 0.0)) {
           if (wkind != 0) { F.status |= kStResidualEmpty; again = 1; }
         } else {
-          const int kc = seq_pick(a.n_s, F.u[0] * W, [&](int k) { return F.chunk[k]; });
-          int j0 = 0;
-          while (j0 < n && (xs[j0] >> 12) < kc) ++j0;
-          int j1 = j0;
-          while (j1 < n && (xs[j1] >> 12) == kc) ++j1;
-          double Sg = 0.0;
-          for (int jj = j0; jj < j1;) {
-            const int grp = xs[jj] >> 6;
-            double M = 0.0;
-            while (jj < j1 && (xs[jj] >> 6) == grp) { M += wv[jj]; ++jj; }
-            Sg += M;
-          }
-          // level 2 over the chunk's groups (empty groups add nothing), then level 3
-          const double t2 = F.u[1] * Sg;
-          double cum = 0.0;
-          int gj0 = -1, gj1 = -1, lj0 = -1, lj1 = -1;
-          for (int jj = j0; jj < j1;) {
-            const int grp = xs[jj] >> 6;
-            const int s0 = jj;
-            double M = 0.0;
-            while (jj < j1 && (xs[jj] >> 6) == grp) { M += wv[jj]; ++jj; }
-            cum += M;
-            if (M > 0.0) { lj0 = s0; lj1 = jj; }
-            if (cum > t2) { gj0 = s0; gj1 = jj; break; }
-          }
-          if (gj0 < 0) { gj0 = lj0; gj1 = lj1; }
-          if (gj0 >= 0) {
-            double Mg = 0.0;
-            for (int jj = gj0; jj < gj1; ++jj) Mg += wv[jj];
-            const int e = seq_pick(gj1 - gj0, F.u[2] * Mg, [&](int q) { return wv[gj0 + q]; });
-            F.x = e >= 0 ? xs[gj0 + e] : -1;
-          }
+          F.x = x;
         }
         red_i[0] = again;
       }
@@ -976,6 +994,137 @@ hipError_t launch_filter(const FilterArgs& a, int dt, int vec, hipStream_t st, h
   if (e != hipSuccess) return e;
   if (paired) hipLaunchKernelGGL((k_filt_finalize<kFuSample>), dim3(a.B), dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL((k_filt_finalize<kFuTokenOnly>), dim3(a.B), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- plain filtered rows
+
+// spec_row_stats: the statistics of filtered row r (SpecKV page signals on the distribution
+// actually sampled from).  A row with a NaN / +inf logit or no finite logit gives argmax -1,
+// NaN statistics and kept count 0; a row whose top-k set overflows the sparse sets, argmax -1,
+// NaN statistics and kept count -1.
+__global__ __launch_bounds__(kThreads) void k_filt_rowstats_out(FilterArgs a) {
+  const int r = blockIdx.x * kThreads + threadIdx.x;
+  if (r >= a.n_slots) return;
+  const RowStat2 st = a.rstat[r];
+  const float nan = __int_as_float(0x7fc00000);
+  const bool ok = st.flags == 0;
+  const RowStatsOut& o = a.rso;
+  if (o.max_logit) o.max_logit[r] = ok ? st.m : nan;
+  if (o.argmax) o.argmax[r] = ok ? st.argmax : -1;
+  if (o.log_z) o.log_z[r] = ok ? (float)st.log_z : nan;
+  if (o.entropy_bits) o.entropy_bits[r] = ok ? (float)st.entropy : nan;
+  if (o.max_prob) o.max_prob[r] = ok ? (float)st.max_prob : nan;
+  if (o.kept_count) o.kept_count[r] = ok ? st.kept_finite : ((st.flags & kFlagOverflow) ? -1 : 0);
+}
+
+struct ResLds {
+  int xs[kKeepMax], qx[kKeepMax];
+  double w[kKeepMax];
+  double chunk[kMaxSlicesFused];
+  double red[kWaves];
+  double u[3];
+  int x;
+};
+
+// spec_residual_sample: one draw from r(x) = [p(x) - q(x)]_+ / beta over p's kept set (guide page
+// "5.1 投机解码核心原理" §3.2, beta = sum [p - q]_+ §4.1), or from p without q rows, by the sparse
+// three-level sampler; uniforms injected, or Philox counter (r, 0, 1, 0) words 1..3.
+template <bool WITH_Q>
+__global__ __launch_bounds__(kThreads) void k_filt_residual(FilterArgs a) {
+  __shared__ ResLds S;
+  const int t = threadIdx.x, r = blockIdx.x;
+  const double dnan = __longlong_as_double(0x7ff8000000000000ll);
+  const RowStat2 P = a.rstat[r];
+  int fl = P.flags;
+  RowStat2 Q;
+  if (WITH_Q) {
+    Q = a.rstat[a.n_teams + r];
+    fl |= Q.flags;
+  }
+  if (fl) {
+    if (t == 0) {
+      a.out_tokens[r] = -1;
+      if (a.out_mass) a.out_mass[r] = dnan;
+      a.out_status[r] = (fl & kFlagOverflow) ? kStFilterOverflow : kStNonfinite;
+    }
+    return;
+  }
+  const KeptEntry* kp = a.kept + (int64_t)r * kKeepMax;
+  const int n = P.n;
+  const KeptEntry* kq = WITH_Q ? a.kept + (int64_t)(a.n_teams + r) * kKeepMax : nullptr;
+  const int nq = WITH_Q ? Q.n : 0;
+  for (int j = t; j < n; j += kThreads) S.xs[j] = kp[j].x;
+  for (int j = t; j < nq; j += kThreads) S.qx[j] = kq[j].x;
+  if (t == 0) {
+    if (a.uniforms) {
+      for (int k = 0; k < 3; ++k) S.u[k] = a.uniforms[(int64_t)r * 3 + k];
+    } else {
+      uint64_t w[4];
+      philox4x64_10(a.seed, a.step, (uint64_t)r, 0, 1, 0, w);
+      S.u[0] = u53(w[1]);
+      S.u[1] = u53(w[2]);
+      S.u[2] = u53(w[3]);
+    }
+  }
+  __syncthreads();
+  double beta = 0.0;
+  for (int j = t; j < n; j += kThreads) {
+    double w = kp[j].p;
+    if (WITH_Q) {
+      const int m = find_idx(S.qx, nq, S.xs[j]);
+      w = fmax(w - (m >= 0 ? kq[m].p : 0.0), 0.0);
+    }
+    S.w[j] = w;
+    beta += w;
+  }
+  beta = block_sum_dd(beta, S.red);
+  int status = 0;
+  if (!(beta > 0.0)) {
+    // an empty residual: drawn from p (reading R8)
+    status = kStResidualEmpty;
+    for (int j = t; j < n; j += kThreads) S.w[j] = kp[j].p;
+    __syncthreads();
+  }
+  if (t == 0) {
+    double W;
+    S.x = sparse_sample(S.xs, S.w, n, a.n_s, S.u, S.chunk, W);
+    a.out_tokens[r] = S.x;
+    if (a.out_mass) a.out_mass[r] = beta;
+    a.out_status[r] = status;
+  }
+}
+
+hipError_t launch_filter_rows(const FilterArgs& a, int dt, int vec, int what, hipStream_t st) {
+  const long long g1 = (long long)a.n_teams * a.n_s;
+  if (g1 < 1 || g1 > 0x7fffffffll || a.n_slots < 1) return hipErrorInvalidConfiguration;
+  const bool paired = what == 1 && a.drf != nullptr;
+#define SPEC_SLICES(D, P)                                                                           \
+  do {                                                                                              \
+    if (vec) hipLaunchKernelGGL((k_filt_slices<D, true, P>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);  \
+    else hipLaunchKernelGGL((k_filt_slices<D, false, P>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);     \
+  } while (0)
+  if (dt == kDtBF16) {
+    if (paired) SPEC_SLICES(kDtBF16, true);
+    else SPEC_SLICES(kDtBF16, false);
+  } else {
+    if (paired) SPEC_SLICES(kDtF32, true);
+    else SPEC_SLICES(kDtF32, false);
+  }
+#undef SPEC_SLICES
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (dt == kDtBF16) hipLaunchKernelGGL((k_filt_rows<kDtBF16>), dim3(a.n_slots), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((k_filt_rows<kDtF32>), dim3(a.n_slots), dim3(kThreads), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (what == 0) {
+    hipLaunchKernelGGL(k_filt_rowstats_out, dim3((a.n_slots + kThreads - 1) / kThreads), dim3(kThreads), 0, st, a);
+  } else if (paired) {
+    hipLaunchKernelGGL((k_filt_residual<true>), dim3(a.n_teams), dim3(kThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((k_filt_residual<false>), dim3(a.n_teams), dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

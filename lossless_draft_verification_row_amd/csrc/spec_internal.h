@@ -154,6 +154,7 @@ struct RowStat2 {        // a row's filtered distribution
   int n, flags;          // kept entries; kFlag* bits
   float m;               // max logit
   int argmax;
+  int kept_finite, pad;  // kept entries with a finite logit
   double log_z, entropy, max_prob, z;
 };
 
@@ -177,11 +178,19 @@ struct FilterArgs {
   float* out_req_stats;
   int32_t* out_status;
   PosStatsOut st;
+  // plain rows (spec_row_stats / spec_residual_sample): target row r pairs with draft row r
+  int direct;
+  const double* uniforms;   // residual draws: [rows][3] injected uniforms, or nullptr (Philox)
+  double* out_mass;
+  RowStatsOut rso;
 };
 
 // Candidates kept per slice for top-k = k: the k largest plus room for boundary ties.
 inline int filter_cap(int k) { return (k + 32 + 15) / 16 * 16; }
 hipError_t launch_filter(const FilterArgs& a, int dt, int vec, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+// Plain filtered rows: what = 0, the statistics of n_teams rows (a.rso); what = 1, one residual
+// draw per row pair (target row r, draft row r or none).
+hipError_t launch_filter_rows(const FilterArgs& a, int dt, int vec, int what, hipStream_t st);
 hipError_t launch_check_cu(const int32_t* cu, int B, int G, int n_draft_rows, int* cu_bad, hipStream_t st);
 size_t fused_record_bytes();
 

@@ -48,6 +48,12 @@ def test_workspace_sizes():
     assert L.spec_verify_workspace_bytes(0, 151936, 7, L.SPEC_BF16, 1.0) == 0
     assert L.spec_row_stats_workspace_bytes(10, 8, L.SPEC_F32, 1.0) > 0
     assert L.spec_residual_sample_workspace_bytes(10, 8, L.SPEC_F32, 0.0) > 0
+    # filtered calls: top-k (with or without top-p) is served by the sparse path; top-p alone is not
+    assert L.spec_row_stats_workspace_bytes(10, 151936, L.SPEC_BF16, 0.7, top_k=50, top_p=0.9) > 0
+    assert L.spec_residual_sample_workspace_bytes(10, 151936, L.SPEC_BF16, 0.7, top_k=50) > 0
+    assert L.spec_verify_workspace_bytes(4, 151936, 7, L.SPEC_BF16, 0.7, top_k=256) > 0
+    assert L.spec_row_stats_workspace_bytes(10, 151936, L.SPEC_BF16, 0.7, top_p=0.9) == 0
+    assert L.spec_verify_workspace_bytes(4, 151936, 7, L.SPEC_BF16, 0.7, top_k=257) == 0
 
 
 def test_argument_checks_without_gpu():

@@ -239,3 +239,105 @@ def test_filtered_full_size_sampled():
     assert rep.ok(), rep
     st = gpu["status"]
     assert not (st & (L.STATUS["NONFINITE"] | L.STATUS["FILTER_OVERFLOW"])).any()
+
+
+# ----------------------------------------------------------------------------- plain filtered rows
+
+
+def _rows(x32, dtype):
+    if dtype == "bf16":
+        bits = W.bf16_bits_from_f32(x32)
+        return torch.from_numpy(bits).view(torch.bfloat16).to(DEV), W.bf16_bits_to_f32(bits).astype(np.float64)
+    return torch.from_numpy(x32).to(DEV), x32.astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype,k,p", [("bf16", 50, 0.9), ("bf16", 7, 1.0), ("f32", 20, 0.8), ("bf16", 256, 0.95)])
+def test_filtered_row_stats(dtype, k, p):
+    """spec_row_stats with top-k / top-p: every statistic of the filtered, tempered row against
+    the oracle; rows whose top-p boundary lies within 1e-6 of a value group are excused."""
+    V = 3 * 4096 + 72
+    rng = np.random.default_rng(k)
+    x = rng.standard_normal((10, V), dtype=np.float32) * 3
+    x[2, :200] = -np.inf
+    x[5] = np.round(x[5] * 2) / 2          # ties at the boundary
+    t, xf = _rows(x, dtype)
+    sp = O.SamplingParams(0.7, k, p)
+    res = L.spec_row_stats(t, temperature=0.7, top_k=k, top_p=p)
+    torch.cuda.synchronize()
+    g = H.gpu_to_numpy(res)
+    ref = O.row_stats(xf, sp)
+    ok = ref["topp_margin"] >= H.DECISION_EPS
+    note(f"row stats dtype={dtype} k={k} p={p}: {int((~ok).sum())} rows excused")
+    assert ok.sum() >= 8
+    assert np.array_equal(g["argmax"][ok], ref["argmax"][ok])
+    assert np.array_equal(g["kept_count"][ok], ref["kept_count"][ok])
+    for key in ("max_logit", "log_z", "entropy_bits", "max_prob"):
+        assert H.close(g[key][ok], ref[key][ok]), (key, H.max_rel(g[key][ok], ref[key][ok]))
+
+
+def test_filtered_row_stats_overflow_and_nonfinite():
+    """A row whose top-k set is larger than the sparse path holds reports argmax -1, NaN
+    statistics and kept count -1; a row with a NaN reports argmax -1, NaN and kept count 0."""
+    V = 4096 + 100
+    x = np.random.default_rng(3).standard_normal((3, V), dtype=np.float32)
+    x[0] = 0.5
+    x[1, 17] = np.nan
+    t, _ = _rows(x, "bf16")
+    res = L.spec_row_stats(t, temperature=0.7, top_k=50, top_p=0.9)
+    torch.cuda.synchronize()
+    g = H.gpu_to_numpy(res)
+    assert g["argmax"][0] == -1 and g["kept_count"][0] == -1 and np.isnan(g["entropy_bits"][0])
+    assert g["argmax"][1] == -1 and g["kept_count"][1] == 0 and np.isnan(g["log_z"][1])
+    assert g["argmax"][2] >= 0 and g["kept_count"][2] > 0
+
+
+@pytest.mark.parametrize("with_q", [True, False])
+def test_filtered_residual_sample_grid(with_q):
+    """Injected uniforms on a grid over a filtered pair: every draw matches the oracle's
+    three-level sampler on [p - q]_+ (or p), decisions within 1e-6 of a boundary excused."""
+    V = 2 * 4096 + 500
+    rng = np.random.default_rng(41)
+    p = rng.standard_normal(V).astype(np.float32) * 3
+    q = p + rng.standard_normal(V).astype(np.float32)
+    n = 400
+    grid = (np.arange(n) + 0.5) / n
+    U = np.stack([grid, rng.permutation(grid), rng.permutation(grid)], axis=1)
+    P = np.tile(W.bf16_bits_from_f32(p), (n, 1))
+    Q = np.tile(W.bf16_bits_from_f32(q), (n, 1))
+    pt = torch.from_numpy(P).view(torch.bfloat16).to(DEV)
+    qt = torch.from_numpy(Q).view(torch.bfloat16).to(DEV) if with_q else None
+    res = L.spec_residual_sample(pt, qt, temperature=0.7, top_k=40, top_p=0.9,
+                                 uniforms=torch.from_numpy(U).to(DEV))
+    torch.cuda.synchronize()
+    g = H.gpu_to_numpy(res)
+    pf = W.bf16_bits_to_f32(P[:1]).astype(np.float64)
+    qf = W.bf16_bits_to_f32(Q[:1]).astype(np.float64) if with_q else None
+    ref = O.residual_sample(np.repeat(pf, n, 0), None if qf is None else np.repeat(qf, n, 0),
+                            O.SamplingParams(0.7, 40, 0.9), uniforms=U)
+    bad = (g["token"] != ref["token"]) & (ref["margin"] >= H.DECISION_EPS)
+    assert not bad.any(), np.nonzero(bad)
+    assert (g["token"] != ref["token"]).sum() <= 1
+    assert np.array_equal(g["status"], ref["status"])
+    assert H.close(g["mass"], ref["mass"])
+
+
+def test_filtered_residual_sample_philox():
+    """Philox draws (counter (r, 0, 1, 0)) on 64 filtered fp32 row pairs, one of them with
+    identical p and q (empty residual: drawn from p)."""
+    V = 4096 + 17
+    rng = np.random.default_rng(43)
+    R = 64
+    p = rng.standard_normal((R, V)).astype(np.float32) * 2
+    q = p + rng.standard_normal((R, V)).astype(np.float32)
+    q[5] = p[5]
+    res = L.spec_residual_sample(torch.from_numpy(p).to(DEV), torch.from_numpy(q).to(DEV), temperature=0.9,
+                                 top_k=30, top_p=0.85, seed=77, step=4)
+    torch.cuda.synchronize()
+    g = H.gpu_to_numpy(res)
+    ref = O.residual_sample(p.astype(np.float64), q.astype(np.float64), O.SamplingParams(0.9, 30, 0.85),
+                            seed=77, step=4)
+    bad = (g["token"] != ref["token"]) & (ref["margin"] >= H.DECISION_EPS)
+    assert not bad.any()
+    assert np.array_equal(g["status"], ref["status"])
+    assert g["status"][5] & L.STATUS["RESIDUAL_EMPTY"]
+    assert H.close(g["mass"], ref["mass"])
