@@ -216,18 +216,68 @@ __device__ __forceinline__ void load_run16(const void* row, int V, int x0, float
 // "5.1 投机解码核心原理" §3.1 / §3.2, stop at the first rejection §5.1) and the three-level
 // sampler over the residual or p_{g+1} (§5.2), and write the outputs.  Scans over chunk,
 // group and element masses are wave-wide fp64 prefix sums.
+// Stage the draft offsets in LDS and check them as one exclusive prefix (every request is
+// refused when any offset is out of order).
+__device__ __forceinline__ bool stage_cu(const FusedArgs& a, int* cu, int* red) {
+  const int t = threadIdx.x;
+  for (int k = t; k <= a.B; k += kThreads) cu[k] = a.cu[k];
+  __syncthreads();
+  int bad = 0;
+  for (int k = t; k < a.B; k += kThreads) {
+    const int g = cu[k + 1] - cu[k];
+    if (g < 0 || g > a.G) bad = 1;
+  }
+  if (t == 0 && (cu[0] != 0 || cu[a.B] != a.n_draft_rows)) bad = 1;
+  return block_or(bad, red) != 0;
+}
+
+// One team's raw workspace entries, loaded by one wave (one slice per lane).
+struct TeamRaw {
+  Rec P, Q;
+  uint64_t m[kWaves];
+};
+template <int MODE>
+__device__ __forceinline__ TeamRaw team_load(const FusedArgs& a, __amdgpu_buffer_rsrc_t rrs, int c0, int b, int g,
+                                             int ti) {
+  const int lane = threadIdx.x & 63;
+  TeamRaw R;
+  R.P = Rec{0, 0, 0, 0};
+  R.Q = Rec{0, 0, 0, 0};
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) R.m[w] = 0;
+  if (ti <= g && lane < a.n_s) {
+    const int r = c0 + b + ti;
+    R.P = load_rec_raw(rrs, rec_off(a.n_s, r, lane, 0));
+    if (MODE == kFuSample && ti < g) {
+      R.Q = load_rec_raw(rrs, rec_off(a.n_s, r, lane, 1));
+      const uint64_t* mw = a.smass + ((int64_t)r * a.n_s + lane) * kWaves;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) R.m[w] = ld_coh(mw + w);
+    }
+  }
+  return R;
+}
+
 template <int DT, bool VEC, int MODE>
 __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   FinScratch& F = L.fin;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int c0 = L.cu[b], g = L.cu[b + 1] - c0;
   const int G1 = a.G + 1;
   const int n_s = a.n_s;
   const uint32_t tag = a.tag;
   const float nan = __int_as_float(0x7fc00000);
   const double cd = (double)a.c;
   const __amdgpu_buffer_rsrc_t rrs = rec_rsrc(a);
-  // the draft tokens and their logits do not depend on any record: fetch them first
+  // this request's offsets straight from memory; the whole array is checked below, and these
+  // are clamped into the declared arrays until then (an offset pair failing this test fails
+  // the whole check too)
+  int c0, c1;
+  sload2_i32(a.cu + b, c0, c1);
+  const bool gok = c0 >= 0 && c1 >= c0 && c1 - c0 <= a.G && c1 <= a.n_draft_rows && c0 + b + (c1 - c0) < a.n_teams;
+  if (!gok) c0 = c1 = 0;
+  const int g = c1 - c0;
+  // the draft tokens, their logits, the first two teams of this wave and the Philox blocks do
+  // not depend on one another: all go out before anything waits
   float ly_p = 0.f, ly_q = 0.f;
   int ytok = -1;
   if (t < g) {
@@ -237,48 +287,51 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       if (MODE == kFuSample) ly_q = logit_at<DT>(row_ptr<DT>(a.drf, a.drf_ld, c0 + t), ytok);
     }
   }
-
+  TeamRaw pre[2];
+  pre[0] = team_load<MODE>(a, rrs, c0, b, g, wave);
+  pre[1] = team_load<MODE>(a, rrs, c0, b, g, wave + kWaves);
   double u_acc = 0.0;
+  if (t <= g) {
+    // the Philox block of position t (1-based i = t + 1): word 0 is the accept draw, words
+    // 1..3 the sampler's uniforms if the emitted token is drawn there
+    uint64_t w[4];
+    philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(t + 1), 0, 0, w);
+    u_acc = u53(w[0]);
+    F.us[t][0] = u53(w[1]);
+    F.us[t][1] = u53(w[2]);
+    F.us[t][2] = u53(w[3]);
+  }
+  // the draft offsets as one exclusive prefix: every request is refused when any is out of order
+  if (stage_cu(a, L.cu, L.i)) {
+    if (t <= a.G) a.out_tokens[(int64_t)b * G1 + t] = -1;
+    if (t == 0) {
+      a.out_num_accepted[b] = 0;
+      a.out_status[b] = kStBadGamma;
+      if (a.out_req_stats)
+        for (int q = 0; q < 4; ++q) a.out_req_stats[(int64_t)b * 4 + q] = nan;
+    }
+    return;
+  }
+
   // A. combine each team's records (one wave per team); the streaming kernel has finished
-  for (int ti = wave; ti <= g; ti += kWaves) {
+  for (int ti = wave, it = 0; ti <= g; ti += kWaves, ++it) {
     const int r = c0 + b + ti;
     const bool pair = (MODE == kFuSample) && ti < g;
     const bool in = lane < n_s;
+    const TeamRaw R = it < 2 ? pre[it] : team_load<MODE>(a, rrs, c0, b, g, ti);
     float pr = -INFINITY, ps = 0.f, pw = 0.f, qr = -INFINITY, qs = 0.f, qw = 0.f;
     double sm = 0.0;
     bool ok = true;
-    Rec RP = {0, 0, 0, 0}, RQ = {0, 0, 0, 0};
-    uint64_t mw4[kWaves] = {0, 0, 0, 0};
     if (in) {
-      RP = load_rec_raw(rrs, rec_off(n_s, r, lane, 0));
+      ok = rec_ok(R.P, tag);
+      pr = __uint_as_float(R.P.x); ps = __uint_as_float(R.P.y); pw = __uint_as_float(R.P.z);
       if (pair) {
-        RQ = load_rec_raw(rrs, rec_off(n_s, r, lane, 1));
-        const uint64_t* mw = a.smass + ((int64_t)r * n_s + lane) * kWaves;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) mw4[w] = ld_coh(mw + w);
-      }
-    }
-    if (ti == wave && t <= g) {
-      // while the first team's records are in flight: the Philox block of position t (1-based
-      // i = t + 1), word 0 the accept draw, words 1..3 the sampler's uniforms if the emitted
-      // token is drawn there
-      uint64_t w[4];
-      philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(t + 1), 0, 0, w);
-      u_acc = u53(w[0]);
-      F.us[t][0] = u53(w[1]);
-      F.us[t][1] = u53(w[2]);
-      F.us[t][2] = u53(w[3]);
-    }
-    if (in) {
-      ok = rec_ok(RP, tag);
-      pr = __uint_as_float(RP.x); ps = __uint_as_float(RP.y); pw = __uint_as_float(RP.z);
-      if (pair) {
-        ok = ok && rec_ok(RQ, tag);
-        qr = __uint_as_float(RQ.x); qs = __uint_as_float(RQ.y); qw = __uint_as_float(RQ.z);
+        ok = ok && rec_ok(R.Q, tag);
+        qr = __uint_as_float(R.Q.x); qs = __uint_as_float(R.Q.y); qw = __uint_as_float(R.Q.z);
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-          sm += (double)lo_f(mw4[w]);
-          ok = ok && tag_of(mw4[w]) == tag;
+          sm += (double)lo_f(R.m[w]);
+          ok = ok && tag_of(R.m[w]) == tag;
         }
       }
     }
@@ -874,20 +927,6 @@ __device__ __forceinline__ float residual_slice(const ResidualScale& R, const fl
   return sm * R.scale;
 }
 
-// Stage the draft offsets in LDS and check them as one exclusive prefix (every request is
-// refused when any offset is out of order).
-__device__ __forceinline__ bool stage_cu(const FusedArgs& a, int* cu, int* red) {
-  const int t = threadIdx.x;
-  for (int k = t; k <= a.B; k += kThreads) cu[k] = a.cu[k];
-  __syncthreads();
-  int bad = 0;
-  for (int k = t; k < a.B; k += kThreads) {
-    const int g = cu[k + 1] - cu[k];
-    if (g < 0 || g > a.G) bad = 1;
-  }
-  if (t == 0 && (cu[0] != 0 || cu[a.B] != a.n_draft_rows)) bad = 1;
-  return block_or(bad, red) != 0;
-}
 
 // One workgroup per ticket: slices 2u and 2u + 1 of one target row (the second one absent at an
 // odd end), with the same slices of its draft row when the position pairs them.  Workgroup i
@@ -1120,18 +1159,7 @@ __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
 template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void k_fused_finalize(FusedArgs a) {
   __shared__ LdsFin L;
-  const int t = threadIdx.x, b = blockIdx.x;
-  if (stage_cu(a, L.cu, L.i)) {
-    if (t <= a.G) a.out_tokens[(int64_t)b * (a.G + 1) + t] = -1;
-    if (t == 0) {
-      a.out_num_accepted[b] = 0;
-      a.out_status[b] = kStBadGamma;
-      if (a.out_req_stats)
-        for (int q = 0; q < 4; ++q) a.out_req_stats[(int64_t)b * 4 + q] = __int_as_float(0x7fc00000);
-    }
-    return;
-  }
-  finalize_request<DT, VEC, MODE>(a, L, b);
+  finalize_request<DT, VEC, MODE>(a, L, blockIdx.x);
 }
 
 // ---------------------------------------------------------------- launch
