@@ -131,7 +131,8 @@ def load_traffic(kernel):
             rec = json.load(f)
         import hashlib
         src = os.path.join(ROOT, "lossless_draft_verification_row_amd", "csrc",
-                           "spec_fused.hip" if kernel == "k_fused" else "spec_kernels.hip")
+                           {"k_fused": "spec_fused.hip", "k_filt_slices": "spec_filter.hip"}.get(kernel,
+                                                                                               "spec_kernels.hip"))
         h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
         if rec.get("kernel_source_sha") != h:
             return None
@@ -223,9 +224,15 @@ def main():
     kern_avg_s = float(np.mean(kernel_ms)) / 1e3
     achieved = alg_bytes / kern_avg_s / 1e9
     fused = not os.environ.get("SPEC_VERIFY_NO_FUSED")
-    kernel_name = ("k_fused (streaming kernel: every needed logit read once, both phases)" if fused
-                   else "k_pass1 (streaming pass over every needed logit)")
-    traffic = load_traffic("k_fused" if fused else "k_pass1")
+    filtered = wl.temperature > 0 and 0 < wl.top_k < wl.V
+    if filtered:
+        kernel_key, kernel_name = "k_filt_slices", ("k_filt_slices (streaming kernel: every needed logit "
+                                                    "read once, per-slice top-k candidates)")
+    elif fused:
+        kernel_key, kernel_name = "k_fused", "k_fused (streaming kernel: every needed logit read once, both phases)"
+    else:
+        kernel_key, kernel_name = "k_pass1", "k_pass1 (streaming pass over every needed logit)"
+    traffic = load_traffic(kernel_key)
     line = {
         "metric": "verified draft positions/sec (and streaming-kernel HBM GB/s vs peak), 1 MI355X",
         "value": positions / sec_per_step,

@@ -143,28 +143,35 @@ __device__ __forceinline__ void block_scan2(int& a, int& b, SelLds& S, int& ta, 
 
 // Candidates of one row's slice: the values at or above the slice's k-th largest, the ones
 // strictly above first.  Header {stored, total, threshold digits, flags}.
-template <int DT>
-__device__ void slice_candidates(const FilterArgs& a, SelLds& S, const float (&v)[kPerThread], int slot, int s,
-                                 int base) {
+// `v(j)` gives this thread's j-th logit of the slice.
+// `bad` < 0: find whether the slice holds a NaN or +inf here; else that flag, already known.
+template <int DT, typename Get>
+__device__ void slice_candidates_g(const FilterArgs& a, SelLds& S, Get v, int slot, int s, int base, int bad = -1) {
   constexpr int NP = DT == kDtBF16 ? 2 : 4;
   const int t = threadIdx.x;
-  int bad = 0;
+  if (bad < 0) {
+    bad = 0;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) bad |= __builtin_amdgcn_class(v[j], 0x203) ? 1 : 0;   // NaN, +inf
-  bad = block_or(bad, S.wtot[0]);
+    for (int j = 0; j < kPerThread; ++j) bad |= __builtin_amdgcn_class(v(j), 0x203) ? 1 : 0;   // NaN, +inf
+    bad = block_or(bad, S.wtot[0]);
+  }
   auto valid = [](float x) { return x > -INFINITY && x < INFINITY; };
   bool all;
   int nv;
   const uint32_t th = block_select<NP>(a.k, S,
                                        [&](auto cb) {
 #pragma unroll
-                                         for (int j = 0; j < kPerThread; ++j) cb(order_key(v[j]), valid(v[j]));
+                                         for (int j = 0; j < kPerThread; ++j) {
+                                           const float x = v(j);
+                                           cb(order_key(x), valid(x));
+                                         }
                                        }, all, nv);
   int ng = 0, ne = 0;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
-    if (!valid(v[j])) continue;
-    const uint32_t h = key_hi<NP>(order_key(v[j]));
+    const float x = v(j);
+    if (!valid(x)) continue;
+    const uint32_t h = key_hi<NP>(order_key(x));
     if (all || h > th) ++ng;
     else if (h == th) ++ne;
   }
@@ -174,14 +181,15 @@ __device__ void slice_candidates(const FilterArgs& a, SelLds& S, const float (&v
   CandEntry* out = a.cand + ((int64_t)slot * a.n_s + s) * cap;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
-    if (!valid(v[j])) continue;
-    const uint32_t h = key_hi<NP>(order_key(v[j]));
+    const float x = v(j);
+    if (!valid(x)) continue;
+    const uint32_t h = key_hi<NP>(order_key(x));
     int pos = -1;
     if (all || h > th) pos = og++;
     else if (h == th) pos = tg + oe++;
     if (pos >= 0 && pos < cap) {
       CandEntry c;
-      c.v = v[j];
+      c.v = x;
       c.x = slice_index<DT>(base, t, j);
       out[pos] = c;
     }
@@ -195,6 +203,12 @@ __device__ void slice_candidates(const FilterArgs& a, SelLds& S, const float (&v
     a.chead[(int64_t)slot * a.n_s + s] = hd;
   }
   __syncthreads();
+}
+
+template <int DT>
+__device__ void slice_candidates(const FilterArgs& a, SelLds& S, const float (&v)[kPerThread], int slot, int s,
+                                 int base) {
+  slice_candidates_g<DT>(a, S, [&](int j) { return v[j]; }, slot, s, base);
 }
 
 __device__ __forceinline__ int wave_max_i(int v) {
@@ -214,6 +228,7 @@ struct Sel2Lds {
   int tau[2], fb[2];
   CandEntry stage[2 * (kFilterMaxK + 48)];   // candidates of both rows before the copy out
   SelLds gen;              // the general select, for a slice whose top k spread wider
+  uint32_t raw[kPerThread / 2][kThreads];   // its raw bf16 pairs, thread t's in column t
 };
 
 // Order key of a bf16-exact value (16 significant bits) and back.
@@ -233,10 +248,13 @@ __device__ __forceinline__ float key16_value(int k) {
 // top k with all ties); for a realistic row it is barely larger than k.  That threshold comes
 // from one LDS histogram of the maxima within 256 order keys of the slice maximum (one atomic
 // per thread).  A row whose maxima spread wider, or whose candidates would not fit in `cap`,
-// takes the exact radix select instead.  Candidates are staged in LDS and copied out whole.
+// takes the exact radix select instead, on the slice read again from memory (so that the
+// register copies of both rows end with the staging and the common path keeps a small register
+// footprint).  Candidates are staged in LDS and copied out whole.
+template <bool VEC>
 __device__ void slice_candidates_bf16(const FilterArgs& a, Sel2Lds& S, const float (&vp)[kPerThread],
                                       const float (&vq)[kPerThread], bool paired, int slot_p, int slot_q, int s,
-                                      int base) {
+                                      int base, const void* row_p, const void* row_q) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int nrow = paired ? 2 : 1;
   float fm[2] = {-INFINITY, -INFINITY};
@@ -351,7 +369,23 @@ __device__ void slice_candidates_bf16(const FilterArgs& a, Sel2Lds& S, const flo
     const int slot = r == 0 ? slot_p : slot_q;
     if (fb[r]) {
       // the exact select: the slice's own k-th largest, ties after the larger values
-      slice_candidates<kDtBF16>(a, S.gen, r == 0 ? vp : vq, slot, s, base);
+      // (each thread reads back only its own words, every pass, so no values stay in registers)
+      RawSlice<kDtBF16> raw;
+      if (VEC) load_raw_buf<kDtBF16>(row_rsrc(r == 0 ? row_p : row_q, a.V * 2), base, raw);
+      else load_raw<kDtBF16, false>(r == 0 ? row_p : row_q, a.V, base, raw);
+      if (base + kChunk > a.V) {   // the tail slice: indices >= V become -inf (bf16 0xFF80)
+#pragma unroll
+        for (int k = 0; k < kPerThread / 2; ++k) {
+          const int i0 = slice_index<kDtBF16>(base, t, 2 * k);
+          if (i0 >= a.V) raw.w[k] = (raw.w[k] & 0xFFFF0000u) | 0xFF80u;
+          if (i0 + 1 >= a.V) raw.w[k] = (raw.w[k] & 0x0000FFFFu) | 0xFF800000u;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kPerThread / 2; ++k) S.raw[k][t] = raw.w[k];
+      slice_candidates_g<kDtBF16>(
+          a, S.gen, [&](int j) { return (j & 1) ? bf16_hi(S.raw[j >> 1][t]) : bf16_lo(S.raw[j >> 1][t]); }, slot, s,
+          base, bad[r]);
       continue;
     }
     CandEntry* out = a.cand + ((int64_t)slot * a.n_s + s) * cap;
@@ -389,20 +423,35 @@ __global__ __launch_bounds__(kThreads) void k_filt_slices(FilterArgs a) {
     else if (drow >= 0)
       load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base, rq);
   } else if (PAIRED) {
-    int lo = 0, hi = a.B;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (sload_i32(a.cu + mid) + mid <= r) lo = mid;
-      else hi = mid;
+    // the request guessed as b = r / (G + 1) (exact when every request has G draft tokens):
+    // its draft row is loaded at once, one scalar load checks the guess, and a wrong guess
+    // falls back to a binary search over the offsets and loads again
+    const int lo0 = min(r / (a.G + 1), a.B - 1);
+    const bool guess_pair = r - lo0 < a.n_draft_rows && r % (a.G + 1) < a.G;
+    if (VEC)
+      load_raw_buf<DT>(row_rsrc(guess_pair ? row_ptr<DT>(a.drf, a.drf_ld, r - lo0) : a.tgt, guess_pair ? a.V * kEsz : 0),
+                       base, rq);
+    int lo = lo0, c0, c1;
+    sload2_i32(a.cu + lo, c0, c1);
+    if (!(c0 + lo <= r && (lo == a.B - 1 || c1 + lo + 1 > r))) {
+      lo = 0;
+      int hi = a.B;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sload_i32(a.cu + mid) + mid <= r) lo = mid;
+        else hi = mid;
+      }
+      sload2_i32(a.cu + lo, c0, c1);
     }
-    const int c0 = sload_i32(a.cu + lo), c1 = sload_i32(a.cu + lo + 1);
     const int i = r - c0 - lo;
     if (i >= 0 && i < c1 - c0 && r - lo >= 0 && r - lo < a.n_draft_rows) drow = r - lo;
-    if (VEC)
-      load_raw_buf<DT>(row_rsrc(drow >= 0 ? row_ptr<DT>(a.drf, a.drf_ld, drow) : a.tgt, drow >= 0 ? a.V * kEsz : 0),
-                       base, rq);
-    else if (drow >= 0)
+    if (VEC) {
+      if ((drow >= 0) != guess_pair || (drow >= 0 && lo != lo0))
+        load_raw_buf<DT>(row_rsrc(drow >= 0 ? row_ptr<DT>(a.drf, a.drf_ld, drow) : a.tgt, drow >= 0 ? a.V * kEsz : 0),
+                         base, rq);
+    } else if (drow >= 0) {
       load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base, rq);
+    }
   }
   float vp[kPerThread], vq[kPerThread];
   unpack_raw<DT>(rp, vp);
@@ -416,7 +465,8 @@ __global__ __launch_bounds__(kThreads) void k_filt_slices(FilterArgs a) {
     for (int j = 0; j < kPerThread; ++j) vq[j] = -INFINITY;
   }
   if (DT == kDtBF16) {
-    slice_candidates_bf16(a, S, vp, vq, paired, r, a.n_teams + drow, s, base);
+    slice_candidates_bf16<VEC>(a, S, vp, vq, paired, r, a.n_teams + drow, s, base, row_ptr<DT>(a.tgt, a.tgt_ld, r),
+                          paired ? row_ptr<DT>(a.drf, a.drf_ld, drow) : a.tgt);
   } else {
     slice_candidates<DT>(a, S.gen, vp, r, s, base);
     if (paired) slice_candidates<DT>(a, S.gen, vq, a.n_teams + drow, s, base);
