@@ -68,10 +68,13 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
  * >= V = off; otherwise every logit >= the k-th largest is kept (ties kept).  top_p >= 1 =
  * off; otherwise the smallest set of largest values whose mass over the top-k set reaches
  * top_p is kept (a boundary value is kept with all its ties).  Order: temperature, top-k,
- * top-p.  Every entry point filters with 1 <= top_k <= 256 (top-p optional); top-p alone
- * returns SPEC_ERR_UNSUPPORTED in this build.  A filtered row whose top-k set (k plus boundary
- * ties) holds more than 512 tokens cannot be represented by the sparse path: it is reported
- * (SPEC_STATUS_FILTER_OVERFLOW, or kept_count -1 in spec_row_stats) instead of a result. */
+ * top-p.  Two paths serve filtered calls with the same results.  With 1 <= top_k <= 256 (top-p
+ * optional) the sparse path works on per-slice top-k candidates; a row whose top-k set (k plus
+ * boundary ties) holds more than 512 tokens cannot be represented there and is reported
+ * (SPEC_STATUS_FILTER_OVERFLOW, or kept_count -1 in spec_row_stats) instead of a result.
+ * Every other filter (top-p alone, top_k > 256) takes the dense path, which finds each row's
+ * kept-set threshold exactly and has no size limit; the environment variable
+ * SPEC_VERIFY_DENSE_FILTER=1 sends every filtered call there. */
 typedef struct {
   float temperature;
   int top_k;

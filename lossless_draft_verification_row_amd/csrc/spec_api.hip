@@ -79,7 +79,7 @@ size_t dense_bytes(int64_t n_slots, int V) {
   const int64_t n_lr = 2 * n_slots;
   const int64_t ns = n_chunks(V);
   return kHeaderBytes + align_up((size_t)(n_lr * ns) * slice_part_bytes()) +
-         align_up((size_t)n_lr * row_stat_bytes()) + align_up((size_t)(n_slots * ns) * sizeof(double));
+         align_up((size_t)n_lr * row_stat_bytes()) + 2 * align_up((size_t)(n_slots * ns) * sizeof(double));
 }
 
 // Workspace of the fused path for n_teams target rows, after the header.
@@ -105,17 +105,23 @@ bool fused_ok(int B, int V, int gamma_max) {
 }
 
 // The sparse filtered path: T > 0 with top-k on (1 <= k <= 256, k < V; top-p optional), the
-// fused path's shape limits.  Top-p alone, or a larger k, is not supported.
+// fused path's shape limits.  Every other filtered call (top-p alone, a larger k, larger
+// shapes) takes the dense threshold path, as does every filtered call when
+// SPEC_VERIFY_DENSE_FILTER is set.
 bool filter_supported(int B, int V, int gamma_max, const spec_sampling_params& sp) {
   return sp.temperature > 0.f && sp.top_k >= 1 && sp.top_k < V && sp.top_k <= kFilterMaxK && B <= kMaxReqFused &&
-         (int64_t)B * (gamma_max + 1) <= kMaxTeamsFused && n_chunks(V) <= kMaxSlicesFused;
+         (int64_t)B * (gamma_max + 1) <= kMaxTeamsFused && n_chunks(V) <= kMaxSlicesFused &&
+         !getenv_flag("SPEC_VERIFY_DENSE_FILTER");
 }
 // The same sparse path for plain rows (spec_row_stats, spec_residual_sample): R rows, or R row
 // pairs, each one team of its own.
 bool filter_rows_supported(int R, int V, const spec_sampling_params& sp) {
   return sp.temperature > 0.f && sp.top_k >= 1 && sp.top_k < V && sp.top_k <= kFilterMaxK &&
-         n_chunks(V) <= kMaxSlicesFused && (int64_t)R * n_chunks(V) <= 0x3fffffff;
+         n_chunks(V) <= kMaxSlicesFused && (int64_t)R * n_chunks(V) <= 0x3fffffff &&
+         !getenv_flag("SPEC_VERIFY_DENSE_FILTER");
 }
+// Thresholds of the dense filtered path: one float per logical row.
+size_t thr_bytes(int64_t n_slots) { return align_up((size_t)(2 * n_slots) * sizeof(float)); }
 size_t filter_bytes(int64_t n_slots, int V, int k) {
   const int64_t ns = n_chunks(V);
   return kHeaderBytes + align_up((size_t)(n_slots * ns * filter_cap(k)) * sizeof(CandEntry)) +
@@ -195,8 +201,10 @@ int spec_set_profile_events(void* start_event, void* stop_event) {
 size_t spec_verify_workspace_bytes(int B, int V, int gamma_max, spec_dtype dt, spec_sampling_params sp) {
   (void)dt;
   if (B <= 0 || V <= 0 || gamma_max < 0) return 0;
-  if (filter_on(V, sp))
-    return filter_supported(B, V, gamma_max, sp) ? filter_bytes((int64_t)B * (2 * gamma_max + 1), V, sp.top_k) : 0;
+  if (filter_on(V, sp)) {
+    if (filter_supported(B, V, gamma_max, sp)) return filter_bytes((int64_t)B * (2 * gamma_max + 1), V, sp.top_k);
+    return dense_bytes((int64_t)B * (gamma_max + 1), V) + thr_bytes((int64_t)B * (gamma_max + 1));
+  }
   const size_t dense = dense_bytes((int64_t)B * (gamma_max + 1), V);
   const size_t fused = fused_bytes((int64_t)B * (gamma_max + 1), V);
   return dense > fused ? dense : fused;
@@ -205,14 +213,15 @@ size_t spec_verify_workspace_bytes(int B, int V, int gamma_max, spec_dtype dt, s
 size_t spec_row_stats_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling_params sp) {
   (void)dt;
   if (R <= 0 || V <= 0) return 0;
-  if (filter_on(V, sp)) return filter_rows_supported(R, V, sp) ? filter_bytes(R, V, sp.top_k) : 0;
+  if (filter_on(V, sp)) return filter_rows_supported(R, V, sp) ? filter_bytes(R, V, sp.top_k) : dense_bytes(R, V) + thr_bytes(R);
   return dense_bytes(R, V);
 }
 
 size_t spec_residual_sample_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling_params sp) {
   (void)dt;
   if (R <= 0 || V <= 0) return 0;
-  if (filter_on(V, sp)) return filter_rows_supported(R, V, sp) ? filter_bytes(2 * (int64_t)R, V, sp.top_k) : 0;
+  if (filter_on(V, sp))
+    return filter_rows_supported(R, V, sp) ? filter_bytes(2 * (int64_t)R, V, sp.top_k) : dense_bytes(R, V) + thr_bytes(R);
   return dense_bytes(R, V);
 }
 
@@ -235,7 +244,7 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   if ((int64_t)B * (gamma_max + 1) * 2 > (int64_t)INT32_MAX / 2) return SPEC_ERR_INVALID;
   const bool greedy = sp.temperature == 0.f;
   const bool filtered = filter_on(V, sp);
-  if (filtered && !filter_supported(B, V, gamma_max, sp)) return SPEC_ERR_UNSUPPORTED;
+  const bool sparse = filtered && filter_supported(B, V, gamma_max, sp);
   const size_t need = spec_verify_workspace_bytes(B, V, gamma_max, dt, sp);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SPEC_ERR_WORKSPACE;
   if (((uintptr_t)workspace % kAlign) != 0) return SPEC_ERR_INVALID;
@@ -259,7 +268,7 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   char* ws = (char*)workspace;
   const int dtc = dt == SPEC_BF16 ? kDtBF16 : kDtF32;
   const bool vec = aligned16(target_logits, target_ld, dt) && aligned16(drf, draft_ld, dt);
-  if (filtered) {
+  if (sparse) {
     FilterArgs f;
     memset(&f, 0, sizeof(f));
     f.tgt = target_logits;
@@ -302,7 +311,7 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
     const hipError_t e = launch_filter(f, dtc, vec, st, g_prof_start, g_prof_stop);
     return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
   }
-  if (fused_ok(B, V, gamma_max)) {
+  if (!filtered && fused_ok(B, V, gamma_max)) {
     FusedArgs f;
     memset(&f, 0, sizeof(f));
     f.tgt = target_logits;
@@ -365,6 +374,15 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   L.part = cv.take<SlicePart>((size_t)(2 * n_slots) * ns * slice_part_bytes());
   L.rs = cv.take<RowStat>((size_t)(2 * n_slots) * row_stat_bytes());
   L.smass = cv.take<double>((size_t)n_slots * ns * sizeof(double));
+  L.amass = cv.take<double>((size_t)n_slots * ns * sizeof(double));
+  if (filtered) {
+    float* thr = cv.take<float>((size_t)(2 * n_slots) * sizeof(float));
+    if (launch_threshold(map, dtc, vec, V, 2 * n_slots, sp.top_k, sp.top_p, 1.4426950408889634 / (double)sp.temperature,
+                         thr, st) != hipSuccess)
+      return SPEC_ERR_LAUNCH;
+    map.thr = thr;
+    L.map = map;
+  }
   L.rso.enabled = 0;
   L.ev_start = g_prof_start;
   L.ev_stop = g_prof_stop;
@@ -383,6 +401,7 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   a.rs = L.rs;
   a.part = L.part;
   a.smass = L.smass;
+  a.amass = L.amass;
   a.out_tokens = out_tokens;
   a.out_num_accepted = out_num_accepted;
   a.out_req_stats = out_req_stats;
@@ -408,13 +427,12 @@ int spec_row_stats(int R, int V, spec_dtype dt, const void* logits, int64_t ld, 
   if (R == 0) return SPEC_OK;
   if (!logits || ld < V) return SPEC_ERR_INVALID;
   if ((int64_t)R * 2 > (int64_t)INT32_MAX / 2) return SPEC_ERR_INVALID;
-  if (filter_on(V, sp) && !filter_rows_supported(R, V, sp)) return SPEC_ERR_UNSUPPORTED;
   const size_t need = spec_row_stats_workspace_bytes(R, V, dt, sp);
   if (!workspace || workspace_bytes < need) return SPEC_ERR_WORKSPACE;
   if (((uintptr_t)workspace % kAlign) != 0) return SPEC_ERR_INVALID;
   const bool greedy = sp.temperature == 0.f;
   const int ns = n_chunks(V);
-  if (filter_on(V, sp)) {
+  if (filter_on(V, sp) && filter_rows_supported(R, V, sp)) {
     FilterArgs f = plain_filter_args(R, V, logits, ld, nullptr, 0, sp, workspace);
     f.rso.enabled = 1;
     f.rso.max_logit = max_logit;
@@ -449,6 +467,15 @@ int spec_row_stats(int R, int V, spec_dtype dt, const void* logits, int64_t ld, 
   L.part = cv.take<SlicePart>((size_t)(2 * R) * ns * slice_part_bytes());
   L.rs = cv.take<RowStat>((size_t)(2 * R) * row_stat_bytes());
   L.smass = cv.take<double>((size_t)R * ns * sizeof(double));
+  L.amass = cv.take<double>((size_t)R * ns * sizeof(double));
+  if (filter_on(V, sp)) {
+    float* thr = cv.take<float>((size_t)(2 * R) * sizeof(float));
+    if (launch_threshold(map, L.dt, L.vec, V, 2 * R, sp.top_k, sp.top_p, 1.4426950408889634 / (double)sp.temperature,
+                         thr, (hipStream_t)hip_stream) != hipSuccess)
+      return SPEC_ERR_LAUNCH;
+    map.thr = thr;
+    L.map = map;
+  }
   L.rso.enabled = 1;
   L.rso.max_logit = max_logit;
   L.rso.argmax = argmax;
@@ -472,14 +499,13 @@ int spec_residual_sample(int R, int V, spec_dtype dt, const void* p_logits, int6
   if (!p_logits || p_ld < V || !out_token || !out_status) return SPEC_ERR_INVALID;
   if (q_logits && q_ld < V) return SPEC_ERR_INVALID;
   if ((int64_t)R * 2 > (int64_t)INT32_MAX / 2) return SPEC_ERR_INVALID;
-  if (filter_on(V, sp) && !filter_rows_supported(R, V, sp)) return SPEC_ERR_UNSUPPORTED;
   const size_t need = spec_residual_sample_workspace_bytes(R, V, dt, sp);
   if (!workspace || workspace_bytes < need) return SPEC_ERR_WORKSPACE;
   if (((uintptr_t)workspace % kAlign) != 0) return SPEC_ERR_INVALID;
   const bool greedy = sp.temperature == 0.f;
   const int ns = n_chunks(V);
   const hipStream_t st = (hipStream_t)hip_stream;
-  if (filter_on(V, sp)) {
+  if (filter_on(V, sp) && filter_rows_supported(R, V, sp)) {
     FilterArgs f = plain_filter_args(R, V, p_logits, p_ld, q_logits, q_ld, sp, workspace);
     f.uniforms = uniforms;
     f.seed = seed;
@@ -515,6 +541,15 @@ int spec_residual_sample(int R, int V, spec_dtype dt, const void* p_logits, int6
   L.part = cv.take<SlicePart>((size_t)(2 * R) * ns * slice_part_bytes());
   L.rs = cv.take<RowStat>((size_t)(2 * R) * row_stat_bytes());
   L.smass = cv.take<double>((size_t)R * ns * sizeof(double));
+  L.amass = cv.take<double>((size_t)R * ns * sizeof(double));
+  if (filter_on(V, sp)) {
+    float* thr = cv.take<float>((size_t)(2 * R) * sizeof(float));
+    if (launch_threshold(map, L.dt, L.vec, V, 2 * R, sp.top_k, sp.top_p, 1.4426950408889634 / (double)sp.temperature,
+                         thr, st) != hipSuccess)
+      return SPEC_ERR_LAUNCH;
+    map.thr = thr;
+    L.map = map;
+  }
   L.rso.enabled = 0;
   if (launch_dense(L, st) != hipSuccess) return SPEC_ERR_LAUNCH;
 

@@ -502,4 +502,63 @@ __device__ __forceinline__ void mask_tail(int V, int base, float (&v)[kPerThread
     if (slice_index<DT>(base, threadIdx.x, j) >= V) v[j] = -INFINITY;
 }
 
+// ---------------------------------------------------------------- radix select helpers
+
+// Order key of a logit: unsigned, larger key = larger value; -0 and +0 share a key.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
+  return v;
+}
+
+struct SelLds {
+  uint32_t hist[256];
+  int wtot[2][kWaves];
+  int digit, above, total;
+};
+
+// One pass of the block-wide radix select: `cnt(d)` for the keys whose higher digits match
+// `prefix` must already be in S.hist.  Wave 0 finds the digit d holding the kk-th largest
+// (counting from the top) and the number of keys above it; the digit is -1 when fewer than kk
+// keys were counted (S.total holds the count).
+__device__ __forceinline__ void select_digit(SelLds& S, int kk) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    int c[4], s = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { c[q] = (int)S.hist[255 - 4 * lane - q]; s += c[q]; }
+    const int incl = wave_incl_scan_i(s);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    const unsigned long long hit = __ballot(incl >= kk);
+    if (lane == 0) { S.total = total; S.digit = -1; S.above = 0; }
+    if (hit && total >= kk) {
+      const int L = __builtin_ctzll(hit);
+      if (lane == L) {
+        int run = incl - s;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (run + c[q] >= kk) { S.digit = 255 - 4 * lane - q; S.above = run; break; }
+          run += c[q];
+        }
+      }
+    }
+  }
+}
+
+// Value of a 16-bit order key of a bf16 value (the inverse of order_key(v) >> 16).
+__device__ __forceinline__ float key16_value(int k) {
+  const uint32_t b = (k & 0x8000) ? ((uint32_t)k & 0x7FFFu) : (~(uint32_t)k & 0xFFFFu);
+  return __uint_as_float(b << 16);
+}
+
 }  // namespace specv

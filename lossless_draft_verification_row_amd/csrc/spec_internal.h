@@ -36,6 +36,8 @@ struct RowMap {
   int G;                    // gamma_max (request mode)
   int n_draft_rows;         // cu[B] as stated by the caller (request mode)
   const int* cu_bad;        // request mode: set when cu is not a valid exclusive prefix
+  const float* thr;         // per logical row: filter threshold (a logit below it is masked);
+                            // nullptr: unfiltered
 };
 
 // spec_row_stats outputs written by the combine kernel (plain-row mode).
@@ -61,7 +63,8 @@ struct DenseLaunch {
   int greedy, want_argmax, pair, vec;
   SlicePart* part;
   RowStat* rs;
-  double* smass;
+  double* smass;            // [n_slots][n_slices] sum over the slice of [p - q]_+
+  double* amass;            // [n_slots][n_slices] sum over the slice of min(p, q)
   RowStatsOut rso;
   hipEvent_t ev_start, ev_stop;   // optional: bracket the streaming pass (benchmark timing)
 };
@@ -85,6 +88,7 @@ struct FinalizeArgs {
   const RowStat* rs;
   const SlicePart* part;
   const double* smass;
+  const double* amass;
   int32_t* out_tokens;
   int32_t* out_num_accepted;
   float* out_req_stats;
@@ -195,6 +199,9 @@ hipError_t launch_check_cu(const int32_t* cu, int B, int G, int n_draft_rows, in
 size_t fused_record_bytes();
 
 hipError_t launch_dense(const DenseLaunch& L, hipStream_t st);
+// Filter thresholds of logical rows 0..n_lr-1 of `m` into thr[n_lr] (c = log2(e) / T).
+hipError_t launch_threshold(const RowMap& m, int dt, int vec, int V, int n_lr, int k, float top_p, double c,
+                            float* thr, hipStream_t st);
 hipError_t launch_finalize(const FinalizeArgs& a, int dt, hipStream_t st);
 hipError_t launch_residual_finalize(const ResidualArgs& a, int dt, hipStream_t st);
 

@@ -16,6 +16,13 @@
 //   finalize one workgroup per request: accept scan, three-level sampler (re-reads one
 //            chunk), outputs.
 // Greedy needs pass1 (argmax) + combine + finalize over the target rows only.
+//
+// Filtered rows on this path (top-p alone, or a top-k beyond the sparse path's reach): a
+// threshold kernel first finds, per row, the value tau above which the filter keeps every
+// logit (temperature, then top-k with ties, then top-p over the renormalised top-k set by value
+// groups; guide page "5.1 投机解码核心原理" §2.1).  Every later kernel treats a logit below its
+// row's tau as masked (weight 0), so the statistics, the pair pass and the sampler run on the
+// filtered distributions unchanged.
 #include "spec_device.h"
 #include "spec_internal.h"
 
@@ -70,6 +77,215 @@ __device__ __forceinline__ const void* resolve_row(const RowMap& m, int lr) {
   return (m.drf && i < g) ? row_ptr<DT>(m.drf, m.drf_ld, (int64_t)c0 + i) : nullptr;
 }
 
+// ---------------------------------------------------------------- filter threshold
+
+// Top-p masses in fixed point: e = exp2((l - m) c) in [0, 1] is held as round(e * 2^40) in a
+// u64, so every histogram sum is an exact integer whatever the order of the atomic adds
+// (V <= 2^21 keeps the row total below 2^61).
+__device__ __forceinline__ unsigned long long mass_fx(float x, float m, double c) {
+  const double t = ((double)x - (double)m) * c;   // <= 0, exact difference
+  if (!(t > -1100.0)) return 0ull;                // -inf logits and masses far below 2^-40
+  const double n = floor(t);
+  const float f = (float)(t - n);                 // [0, 1): exp2 of it to ~1 ulp in fp32
+  return (unsigned long long)rint(ldexp((double)__builtin_amdgcn_exp2f(f), (int)n + 40));
+}
+
+// f(x) for every logit of the row (16-byte loads when VEC).
+template <int DT, bool VEC, typename F>
+__device__ __forceinline__ void for_row(const void* row, int V, F f) {
+  const int t = threadIdx.x;
+  int tail = 0;
+  if constexpr (VEC) {
+    constexpr int kEl = DT == kDtBF16 ? 8 : 4;
+    const int nv = V / kEl;
+#pragma unroll 4
+    for (int i = t; i < nv; i += kThreads) {
+      const uint4 w = ((const uint4*)row)[i];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (DT == kDtBF16) {
+          f(bf16_lo(ws[q]));
+          f(bf16_hi(ws[q]));
+        } else {
+          f(__uint_as_float(ws[q]));
+        }
+      }
+    }
+    tail = nv * kEl;
+  }
+  for (int i = tail + t; i < V; i += kThreads) f(logit_at<DT>(row, i));
+}
+
+constexpr int kThrBins = 4096;   // bins of the widest digit (12 bits)
+
+struct ThrLds {
+  unsigned long long h[kThrBins];   // counts (top-k) or fixed-point masses (top-p) per digit
+  unsigned long long wsum[kWaves];
+  float redf[kWaves];
+  int redi[kWaves];
+  int digit;
+  unsigned long long above;
+};
+
+__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  unsigned long long s = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+// Walking the nb bins of S.h downwards from the top digit, the first digit d at which
+// base + (the sum of the bins >= d) satisfies reach (monotone, false at base): S.digit = d
+// (-1 if none) and S.above = base + the sum of the bins above d.  Thread t holds the bins
+// just below nb - per * t, so a block scan in thread order is a scan from the top.
+template <typename Reach>
+__device__ void thr_select(ThrLds& S, int nb, unsigned long long base, Reach reach) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int per = nb >= kThreads ? nb / kThreads : 1;
+  const bool owner = t < nb / per;
+  const int hi = nb - per * t;   // this thread's bins: hi - 1 down to hi - per
+  unsigned long long s = 0;
+  if (owner)
+    for (int q = 1; q <= per; ++q) s += S.h[hi - q];
+  unsigned long long incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) S.wsum[wave] = incl;
+  if (t == 0) S.digit = -1;
+  __syncthreads();
+  unsigned long long off = base;
+  for (int w = 0; w < wave; ++w) off += S.wsum[w];
+  incl += off;
+  const unsigned long long excl = incl - s;
+  if (owner && !reach(excl) && reach(incl)) {
+    unsigned long long run = excl;
+    for (int q = 1; q <= per; ++q) {
+      const unsigned long long h = S.h[hi - q];
+      if (reach(run + h)) { S.digit = hi - q; S.above = run; break; }
+      run += h;
+    }
+  }
+  __syncthreads();
+}
+
+// One workgroup per logical row: tau = the smallest logit the filter keeps, written to thr[lr]
+// (-inf: keep every logit; also for a row with a NaN / +inf or no finite logit, which later
+// kernels report).  top-k: the k-th largest logit with multiplicity, by a radix select over
+// order keys, one digit per pass.  top-p: walking the distinct values of the top-k set
+// downwards, the first at which the mass at or above it reaches top_p * Z_K; a mass-weighted
+// radix select over the same digits finds it exactly, one pass per digit.  The first digit is
+// 12 bits wide, so a realistic row spreads over many LDS bins and the atomics rarely collide;
+// bf16 keys (16 bits) take digits of 12 + 4 bits, fp32 keys 12 + 12 + 8.  Every pass re-reads
+// the row.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_threshold(RowMap m, int V, int k, float top_p, double c,
+                                                         float* __restrict__ thr) {
+  const int lr = blockIdx.x;
+  const void* row = resolve_row<DT>(m, lr);
+  if (row == nullptr) return;
+  __shared__ ThrLds S;
+  constexpr int KB = DT == kDtBF16 ? 16 : 32;   // key bits
+  constexpr int NL = DT == kDtBF16 ? 2 : 3;     // digits
+  const int t = threadIdx.x;
+  auto key_of = [](float x) -> uint32_t { return DT == kDtBF16 ? (order_key(x) >> 16) : order_key(x); };
+  auto width = [](int L) -> int { return DT == kDtBF16 ? (L == 0 ? 12 : 4) : (L < 2 ? 12 : 8); };
+  const bool use_k = k > 0 && k < V;
+  const bool use_p = top_p < 1.f;
+
+  // pass 1: the row max, the NaN / +inf flag and, with top-k, the first digit's counts
+  for (int i = t; i < kThrBins; i += kThreads) S.h[i] = 0ull;
+  __syncthreads();
+  float mx = -INFINITY;
+  int bad = 0;
+  for_row<DT, VEC>(row, V, [&](float x) {
+    mx = fmaxf(mx, x);
+    bad |= __builtin_amdgcn_class(x, 0x203) ? 1 : 0;   // NaN, +inf
+    if (use_k) atomicAdd(&S.h[key_of(x) >> (KB - 12)], 1ull);
+  });
+  mx = block_max(mx, S.redf);
+  bad = block_or(bad, S.redi);
+  if (bad || !(mx > -INFINITY)) {
+    if (t == 0) thr[lr] = -INFINITY;
+    return;
+  }
+
+  uint32_t key_k = 0u;   // every key at or above it is in the top-k set
+  if (use_k) {
+    unsigned long long above = 0ull;   // keys above the prefix
+    uint32_t prefix = 0u;
+    int rb = KB;                       // key bits below the prefix
+    for (int L = 0; L < NL; ++L) {
+      const int w = width(L), sh = rb - w;
+      if (L > 0) {
+        for (int i = t; i < (1 << w); i += kThreads) S.h[i] = 0ull;
+        __syncthreads();
+        for_row<DT, VEC>(row, V, [&](float x) {
+          const uint32_t key = key_of(x);
+          if ((key >> rb) == prefix) atomicAdd(&S.h[(key >> sh) & ((1u << w) - 1u)], 1ull);
+        });
+      }
+      __syncthreads();
+      thr_select(S, 1 << w, above, [&](unsigned long long n) { return n >= (unsigned long long)k; });
+      const int d = S.digit;
+      above = S.above;
+      __syncthreads();
+      prefix = (prefix << w) | (uint32_t)max(d, 0);   // d >= 0: the prefix holds the k-th key
+      rb = sh;
+    }
+    key_k = prefix;
+  }
+
+  uint32_t key_p = key_k;
+  if (use_p) {
+    unsigned long long above = 0ull;   // mass above the prefix
+    uint32_t prefix = 0u;
+    int rb = KB;
+    double target = 0.0;
+    bool found = true;
+    for (int L = 0; L < NL && found; ++L) {
+      const int w = width(L), sh = rb - w;
+      for (int i = t; i < (1 << w); i += kThreads) S.h[i] = 0ull;
+      __syncthreads();
+      unsigned long long zt = 0ull;
+      for_row<DT, VEC>(row, V, [&](float x) {
+        const uint32_t key = key_of(x);
+        if (key >= key_k && (L == 0 || (key >> rb) == prefix)) {
+          const unsigned long long fx = mass_fx(x, mx, c);
+          zt += fx;
+          if (fx) atomicAdd(&S.h[(key >> sh) & ((1u << w) - 1u)], fx);
+        }
+      });
+      if (L == 0) target = (double)top_p * (double)block_sum_u64(zt, S.wsum);   // top_p * Z_K
+      __syncthreads();
+      thr_select(S, 1 << w, above, [&](unsigned long long s) { return (double)s >= target; });
+      const int d = S.digit;
+      above = S.above;
+      __syncthreads();
+      if (d < 0) found = false;   // not reached (rounding): keep the whole top-k set
+      else prefix = (prefix << w) | (uint32_t)d;
+      rb = sh;
+    }
+    if (found) key_p = prefix;
+  }
+  if (t == 0) {
+    const uint32_t key = key_p > key_k ? key_p : key_k;
+    float v;
+    if (key == 0u) v = -INFINITY;
+    else if (DT == kDtBF16) v = key16_value((int)key);
+    else v = __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+    thr[lr] = v;
+  }
+}
+
 // ---------------------------------------------------------------- pass 1
 
 // MODE_SOFTMAX: slice max, sum of exp2((l - m) c) and the entropy numerator; argmax and kept
@@ -115,18 +331,20 @@ __global__ __launch_bounds__(kThreads) void k_pass1(RowMap m, int V, int n_slice
     bad = block_or(bad, redi);
     if (bad) out.amax = -2;
   } else {
-    // e = exp2((l - m) c) relative to the slice max; -inf logits give e = 0 and, through the
-    // clamp, a zero entropy term.  A NaN or +inf logit makes s NaN.
+    // e = exp2((l - m) c) relative to the slice max; -inf logits and logits below the row's
+    // filter threshold give e = 0 and, through the clamp, a zero entropy term.  A NaN or +inf
+    // logit (never below a threshold) makes s NaN.
     const float ref = (mw == -INFINITY) ? 0.f : mw;
+    const float th = m.thr ? m.thr[lr] : -INFINITY;
     float s = 0.f, w = 0.f;
     int cnt = 0;
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-      const float t = (v[j] - ref) * c;
+      const float t = (v[j] < th) ? -INFINITY : (v[j] - ref) * c;
       const float e = __builtin_amdgcn_exp2f(t);
       s += e;
       w = fmaf(e, fmaxf(t, -256.f), w);
-      if (want_argmax) cnt += (v[j] > -INFINITY) ? 1 : 0;
+      if (want_argmax) cnt += (v[j] > -INFINITY && !(v[j] < th)) ? 1 : 0;
     }
     out.s = (float)block_sum_d((double)s, redd);
     out.w = (float)block_sum_d((double)w, redd);
@@ -183,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(RowMap m, int n_lr, int n_
   r.m = mrow;
   r.amax = (amax == INT_MAX) ? -1 : amax;
   r.flags = (bad || !(mrow > -INFINITY)) ? kStNonfinite : 0;
-  r.tau = -INFINITY;
+  r.tau = m.thr ? m.thr[lr] : -INFINITY;
   r.kept = cnt;
   if (greedy) {
     r.z = 1.0; r.log2z = 0.0; r.inv_z = 1.f; r.h_bits = 0.f; r.maxp = 1.f; r.kept = 1;
@@ -212,12 +430,14 @@ __global__ __launch_bounds__(kThreads) void k_combine(RowMap m, int n_lr, int n_
 
 // ---------------------------------------------------------------- pair pass
 
-// Residual mass of one slice of one (target, draft) row pair: sum_x [p(x) - q(x)]_+ with
-// p(x) = exp2((l_x - m) c) / z evaluated in fp32 exactly as the finalize pass does.
+// Residual mass of one slice of one (target, draft) row pair, sum_x [p(x) - q(x)]_+, with
+// p(x) = exp2((l_x - m) c) / z evaluated in fp32 exactly as the finalize pass does; and the
+// slice's overlap sum_x min(p(x), q(x)) (each min exact), so that A = 1 - TV keeps its
+// relative precision when the two distributions barely overlap.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_pair(RowMap m, int V, int n_slices, float c,
                                                     const RowStat* __restrict__ rs,
-                                                    double* __restrict__ smass) {
+                                                    double* __restrict__ smass, double* __restrict__ amass) {
   const int slot = blockIdx.x, sl = blockIdx.y;
   const void* prow = resolve_row<DT>(m, 2 * slot);
   const void* qrow = resolve_row<DT>(m, 2 * slot + 1);
@@ -225,22 +445,30 @@ __global__ __launch_bounds__(kThreads) void k_pair(RowMap m, int V, int n_slices
   __shared__ double redd[kWaves];
   const RowStat P = rs[2 * slot], Q = rs[2 * slot + 1];
   if ((P.flags | Q.flags) != 0) {
-    if (threadIdx.x == 0) smass[(int64_t)slot * n_slices + sl] = 0.0;
+    if (threadIdx.x == 0) {
+      smass[(int64_t)slot * n_slices + sl] = 0.0;
+      amass[(int64_t)slot * n_slices + sl] = 0.0;
+    }
     return;
   }
   const int base = sl * kChunk;
   float lp[kPerThread], lq[kPerThread];
   load_slice<DT, VEC>(prow, V, base, lp);
   load_slice<DT, VEC>(qrow, V, base, lq);
-  float acc = 0.f;
+  float acc = 0.f, ovl = 0.f;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
-    const float p = __builtin_amdgcn_exp2f((lp[j] - P.m) * c) * P.inv_z;
-    const float q = __builtin_amdgcn_exp2f((lq[j] - Q.m) * c) * Q.inv_z;
+    const float p = (lp[j] < P.tau) ? 0.f : __builtin_amdgcn_exp2f((lp[j] - P.m) * c) * P.inv_z;
+    const float q = (lq[j] < Q.tau) ? 0.f : __builtin_amdgcn_exp2f((lq[j] - Q.m) * c) * Q.inv_z;
     acc += fmaxf(p - q, 0.f);
+    ovl += fminf(p, q);
   }
   const double tot = block_sum_d((double)acc, redd);
-  if (threadIdx.x == 0) smass[(int64_t)slot * n_slices + sl] = tot;
+  const double ov = block_sum_d((double)ovl, redd);
+  if (threadIdx.x == 0) {
+    smass[(int64_t)slot * n_slices + sl] = tot;
+    amass[(int64_t)slot * n_slices + sl] = ov;
+  }
 }
 
 // ---------------------------------------------------------------- sampler
@@ -275,9 +503,11 @@ __device__ int sample_in_chunk(const void* prow, const void* qrow, int V, int k,
     const int x = x0 + e;
     float w = 0.f;
     if (x < V) {
-      const float p = __builtin_amdgcn_exp2f((logit_at<DT>(prow, x) - P.m) * c) * P.inv_z;
+      const float lp = logit_at<DT>(prow, x);
+      const float p = (lp < P.tau) ? 0.f : __builtin_amdgcn_exp2f((lp - P.m) * c) * P.inv_z;
       if (wkind == 1) {
-        const float q = __builtin_amdgcn_exp2f((logit_at<DT>(qrow, x) - Q.m) * c) * Q.inv_z;
+        const float lq = logit_at<DT>(qrow, x);
+        const float q = (lq < Q.tau) ? 0.f : __builtin_amdgcn_exp2f((lq - Q.m) * c) * Q.inv_z;
         w = fmaxf(p - q, 0.f);
       } else if (wkind == 2) {
         w = (x == y) ? 0.f : p;
@@ -344,10 +574,12 @@ __device__ __forceinline__ int pick_chunk(const double* mass, int n, double u1, 
   return last;
 }
 
-// p(x) in fp64 from the row statistics: exp2((l_x - m) c) / z.
+// p(x) in fp64 from the row statistics: exp2((l_x - m) c) / z, 0 below the filter threshold.
 template <int DT>
 __device__ __forceinline__ double p_of(const void* row, int x, const RowStat& P, double cd) {
-  const double l = (double)logit_at<DT>(row, x);
+  const float lf = logit_at<DT>(row, x);
+  if (lf < P.tau) return 0.0;
+  const double l = (double)lf;
   return exp2((l - (double)P.m) * cd) / P.z;
 }
 
@@ -419,9 +651,9 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
         py = (okp && yv) ? (float)p_of<DT>(prow, y, P, cd) : nan;
         qy = (okq && yv) ? (float)p_of<DT>(qrow, y, Q, cd) : nan;
         if (okp && okq) {
-          double beta = 0.0;
-          for (int k = 0; k < a.n_slices; ++k) beta += a.smass[(int64_t)(b * G1 + t) * a.n_slices + k];
-          ovl = (float)(1.0 - beta);
+          double ov = 0.0;
+          for (int k = 0; k < a.n_slices; ++k) ov += a.amass[(int64_t)(b * G1 + t) * a.n_slices + k];
+          ovl = (float)ov;
         }
         dh = okq ? Q.h_bits : nan;
         dm = okq ? Q.maxp : nan;
@@ -665,8 +897,8 @@ static hipError_t launch_dense_t(const DenseLaunch& L, hipStream_t st) {
   if (e != hipSuccess) return e;
   if (L.pair) {
     const dim3 g3(L.n_slots, L.n_slices);
-    if (L.vec) hipLaunchKernelGGL((k_pair<DT, true>), g3, blk, 0, st, m, L.V, L.n_slices, L.c, L.rs, L.smass);
-    else hipLaunchKernelGGL((k_pair<DT, false>), g3, blk, 0, st, m, L.V, L.n_slices, L.c, L.rs, L.smass);
+    if (L.vec) hipLaunchKernelGGL((k_pair<DT, true>), g3, blk, 0, st, m, L.V, L.n_slices, L.c, L.rs, L.smass, L.amass);
+    else hipLaunchKernelGGL((k_pair<DT, false>), g3, blk, 0, st, m, L.V, L.n_slices, L.c, L.rs, L.smass, L.amass);
     e = hipGetLastError();
   }
   return e;
@@ -674,6 +906,20 @@ static hipError_t launch_dense_t(const DenseLaunch& L, hipStream_t st) {
 
 size_t slice_part_bytes() { return sizeof(SlicePart); }
 size_t row_stat_bytes() { return sizeof(RowStat); }
+
+hipError_t launch_threshold(const RowMap& m, int dt, int vec, int V, int n_lr, int k, float top_p, double c,
+                            float* thr, hipStream_t st) {
+  if (n_lr < 1) return hipSuccess;
+  const dim3 g(n_lr), blk(kThreads);
+  if (dt == kDtBF16) {
+    if (vec) hipLaunchKernelGGL((k_threshold<kDtBF16, true>), g, blk, 0, st, m, V, k, top_p, c, thr);
+    else hipLaunchKernelGGL((k_threshold<kDtBF16, false>), g, blk, 0, st, m, V, k, top_p, c, thr);
+  } else {
+    if (vec) hipLaunchKernelGGL((k_threshold<kDtF32, true>), g, blk, 0, st, m, V, k, top_p, c, thr);
+    else hipLaunchKernelGGL((k_threshold<kDtF32, false>), g, blk, 0, st, m, V, k, top_p, c, thr);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_dense(const DenseLaunch& L, hipStream_t st) {
   return L.dt == kDtBF16 ? launch_dense_t<kDtBF16>(L, st) : launch_dense_t<kDtF32>(L, st);

@@ -48,12 +48,17 @@ def test_workspace_sizes():
     assert L.spec_verify_workspace_bytes(0, 151936, 7, L.SPEC_BF16, 1.0) == 0
     assert L.spec_row_stats_workspace_bytes(10, 8, L.SPEC_F32, 1.0) > 0
     assert L.spec_residual_sample_workspace_bytes(10, 8, L.SPEC_F32, 0.0) > 0
-    # filtered calls: top-k (with or without top-p) is served by the sparse path; top-p alone is not
+    # filtered calls: top-k <= 256 (with or without top-p) takes the sparse path; top-p alone or a
+    # larger k takes the dense threshold path, whose workspace is the dense path's plus one
+    # threshold per logical row
     assert L.spec_row_stats_workspace_bytes(10, 151936, L.SPEC_BF16, 0.7, top_k=50, top_p=0.9) > 0
     assert L.spec_residual_sample_workspace_bytes(10, 151936, L.SPEC_BF16, 0.7, top_k=50) > 0
     assert L.spec_verify_workspace_bytes(4, 151936, 7, L.SPEC_BF16, 0.7, top_k=256) > 0
-    assert L.spec_row_stats_workspace_bytes(10, 151936, L.SPEC_BF16, 0.7, top_p=0.9) == 0
-    assert L.spec_verify_workspace_bytes(4, 151936, 7, L.SPEC_BF16, 0.7, top_k=257) == 0
+    dense_rows = L.spec_row_stats_workspace_bytes(10, 151936, L.SPEC_BF16, 1.0)
+    assert L.spec_row_stats_workspace_bytes(10, 151936, L.SPEC_BF16, 0.7, top_p=0.9) == dense_rows + 256
+    dense_req = L.spec_verify_workspace_bytes(4, 151936, 7, L.SPEC_BF16, 1.0)
+    assert L.spec_verify_workspace_bytes(4, 151936, 7, L.SPEC_BF16, 0.7, top_k=257) >= 256
+    assert L.spec_verify_workspace_bytes(4, 151936, 7, L.SPEC_BF16, 0.7, top_k=257) <= dense_req + 256
 
 
 def test_argument_checks_without_gpu():
@@ -73,9 +78,9 @@ def test_argument_checks_without_gpu():
     assert lib.spec_row_stats(4, 100, 1, 16, 100, bad_p, *([None] * 6), None, 0, None) == -1
     # undersized workspace is reported before any launch
     assert lib.spec_row_stats(4, 100, 1, 256, 100, sp, *([None] * 6), None, 0, None) == -3
-    # top-p without top-k is not implemented by this build
-    only_p = L.SamplingParams(1.0, 0, 0.9)
-    assert lib.spec_row_stats(4, 100, 1, 256, 100, only_p, *([None] * 6), 256, 1 << 20, None) == -2
+    # a vocabulary beyond 512 chunks of 4096 is not supported
+    big_v = 512 * 4096 + 1
+    assert lib.spec_row_stats(4, big_v, 1, 256, big_v, sp, *([None] * 6), 256, 1 << 20, None) == -2
     # B = 0 is a no-op
     assert lib.spec_verify_batch(0, 100, 3, 1, None, 100, None, 0, None, None, 0, sp, 0, 0,
                                  None, None, ps, None, None, None, 0, None) == 0

@@ -1,6 +1,7 @@
-"""GPU parity of the top-k / top-p path (spec_verify_batch with 1 <= top_k <= 256) against the
-fp64 oracle, on seeded inputs whose draft tokens are drawn from the oracle's filtered draft
-distribution (the draft model samples from its own filtered q).
+"""GPU parity of the top-k / top-p paths against the fp64 oracle, on seeded inputs whose draft
+tokens are drawn from the oracle's filtered draft distribution (the draft model samples from its
+own filtered q): the sparse path (1 <= top_k <= 256, top-p optional) and the dense threshold
+path (top-p alone, top_k > 256, or any filter with SPEC_VERIFY_DENSE_FILTER set).
 
 Sizes span several 4096-logit slices and a ragged tail; the comparison rule is in
 tests/harness.py (decisions within 1e-6 of a boundary, including the top-p boundary, are
@@ -295,6 +296,10 @@ def test_filtered_row_stats_overflow_and_nonfinite():
 def test_filtered_residual_sample_grid(with_q):
     """Injected uniforms on a grid over a filtered pair: every draw matches the oracle's
     three-level sampler on [p - q]_+ (or p), decisions within 1e-6 of a boundary excused."""
+    _residual_grid(with_q, 40, 0.9)
+
+
+def _residual_grid(with_q, k, top_p):
     V = 2 * 4096 + 500
     rng = np.random.default_rng(41)
     p = rng.standard_normal(V).astype(np.float32) * 3
@@ -306,14 +311,14 @@ def test_filtered_residual_sample_grid(with_q):
     Q = np.tile(W.bf16_bits_from_f32(q), (n, 1))
     pt = torch.from_numpy(P).view(torch.bfloat16).to(DEV)
     qt = torch.from_numpy(Q).view(torch.bfloat16).to(DEV) if with_q else None
-    res = L.spec_residual_sample(pt, qt, temperature=0.7, top_k=40, top_p=0.9,
+    res = L.spec_residual_sample(pt, qt, temperature=0.7, top_k=k, top_p=top_p,
                                  uniforms=torch.from_numpy(U).to(DEV))
     torch.cuda.synchronize()
     g = H.gpu_to_numpy(res)
     pf = W.bf16_bits_to_f32(P[:1]).astype(np.float64)
     qf = W.bf16_bits_to_f32(Q[:1]).astype(np.float64) if with_q else None
     ref = O.residual_sample(np.repeat(pf, n, 0), None if qf is None else np.repeat(qf, n, 0),
-                            O.SamplingParams(0.7, 40, 0.9), uniforms=U)
+                            O.SamplingParams(0.7, k, top_p), uniforms=U)
     bad = (g["token"] != ref["token"]) & (ref["margin"] >= H.DECISION_EPS)
     assert not bad.any(), np.nonzero(bad)
     assert (g["token"] != ref["token"]).sum() <= 1
@@ -341,3 +346,110 @@ def test_filtered_residual_sample_philox():
     assert np.array_equal(g["status"], ref["status"])
     assert g["status"][5] & L.STATUS["RESIDUAL_EMPTY"]
     assert H.close(g["mass"], ref["mass"])
+
+
+# ----------------------------------------------------------------------------- dense threshold path
+# Top-p alone and top-k beyond 256 take the dense path: a threshold kernel finds each row's
+# kept-set threshold and the dense kernels mask every logit below it.  SPEC_VERIFY_DENSE_FILTER
+# sends the top-k <= 256 cases there too, so the same oracle checks both paths on them.
+
+
+@pytest.fixture
+def dense_forced(monkeypatch):
+    monkeypatch.setenv("SPEC_VERIFY_DENSE_FILTER", "1")
+
+
+@pytest.mark.parametrize("k,p", [(0, 0.9), (0, 0.5), (0, 0.99), (1000, 1.0), (600, 0.8), (300, 0.97)])
+def test_dense_filtered_sampling(k, p):
+    sp = O.SamplingParams(0.7, k, p)
+    inp = filtered_inputs(5, V_SMALL, [7, 3, 0, 5, 2], sp, seed=300 + k + int(100 * p))
+    check(inp, sp)
+
+
+def test_dense_filtered_fp32():
+    sp = O.SamplingParams(0.9, 0, 0.8)
+    inp = filtered_inputs(3, 2 * 4096 + 36, [4, 2, 3], sp, dtype="f32", seed=8)
+    check(inp, sp)
+
+
+def test_dense_filtered_token_only():
+    sp = O.SamplingParams(0.7, 0, 0.9)
+    inp = filtered_inputs(4, V_SMALL, [5, 0, 3, 7], sp, seed=14, token_only=True)
+    check(inp, sp)
+
+
+def test_dense_forced_small_k(dense_forced):
+    test_filtered_sampling(50, 0.9)
+    test_filtered_sampling(1, 1.0)
+    test_filtered_fp32()
+
+
+def test_dense_forced_ties_and_masked(dense_forced):
+    test_filtered_ties_and_masked()
+
+
+def test_dense_forced_nonfinite(dense_forced):
+    test_filtered_nonfinite()
+
+
+def test_dense_forced_all_equal_keeps_row(dense_forced):
+    """Every logit of request 0's target rows equal: the top-k set (ties kept) is the whole row,
+    which the dense path represents (the sparse path reports FILTER_OVERFLOW)."""
+    sp = O.SamplingParams(0.7, 50, 0.9)
+    inp = filtered_inputs(2, V_SMALL, [3, 2], sp, seed=29)
+    inp.target[0:4] = W.bf16_bits_from_f32(np.full((4, V_SMALL), 0.25, np.float32))
+    gpu, _, _ = check(inp, sp)
+    assert not (gpu["status"] & L.STATUS["FILTER_OVERFLOW"]).any()
+
+
+@pytest.mark.parametrize("dtype,k,p", [("bf16", 0, 0.9), ("bf16", 2000, 1.0), ("f32", 0, 0.7), ("bf16", 500, 0.95)])
+def test_dense_filtered_row_stats(dtype, k, p):
+    test_filtered_row_stats(dtype, k, p)
+
+
+def test_dense_row_stats_all_equal_and_nonfinite(dense_forced):
+    """An all-equal row keeps every token (uniform: entropy log2 V, max prob 1 / V); a row with
+    a NaN reports argmax -1, NaN statistics and kept count 0."""
+    V = 4096 + 100
+    x = np.random.default_rng(3).standard_normal((3, V), dtype=np.float32)
+    x[0] = 0.5
+    x[1, 17] = np.nan
+    t, xf = _rows(x, "bf16")
+    res = L.spec_row_stats(t, temperature=0.7, top_k=50, top_p=0.9)
+    torch.cuda.synchronize()
+    g = H.gpu_to_numpy(res)
+    assert g["kept_count"][0] == V and g["argmax"][0] == 0
+    assert H.close(g["entropy_bits"][:1], np.array([np.log2(V)]))
+    assert H.close(g["max_prob"][:1], np.array([1.0 / V]))
+    assert g["argmax"][1] == -1 and g["kept_count"][1] == 0 and np.isnan(g["log_z"][1])
+    ref = O.row_stats(xf[2:], O.SamplingParams(0.7, 50, 0.9))
+    assert g["kept_count"][2] == ref["kept_count"][0]
+
+
+@pytest.mark.parametrize("with_q", [True, False])
+def test_dense_filtered_residual_sample_grid(with_q):
+    _residual_grid(with_q, 0, 0.9)
+
+
+def test_dense_filtered_full_size_sampled():
+    """Top-p 0.9 alone at the full filtered workload shape (B = 256, gamma = 7, V = 151,936,
+    bf16, T = 0.7): the GPU verifies the whole batch, the oracle checks a sample of requests."""
+    cfg = 5
+    wl = W.WORKLOADS[cfg]
+    sp = O.SamplingParams(wl.temperature, 0, wl.top_p)
+    inp = W.make_inputs(cfg, tokens="none")
+    rng = np.random.default_rng(56)
+    sample = [0, 2, 130, 255]
+    for b in sample:
+        c0, g = int(inp.cu_draft[b]), int(inp.gammas[b])
+        dv = W.bf16_bits_to_f32(inp.draft[c0:c0 + g]).astype(np.float64)
+        for i in range(g):
+            q = O.row_distribution(dv[i], sp).probs
+            inp.tokens[c0 + i] = int(rng.choice(wl.V, p=q / q.sum()))
+    note("full-size top-p-only batch")
+    gpu = run_gpu(inp, sp, 98, 5)
+    refs = H.oracle_requests(inp, sp, 98, 5, sample)
+    rep = H.compare_requests(gpu, refs, inp, H.Report())
+    note(repr(rep))
+    assert rep.ok(), rep
+    assert not (gpu["status"] & L.STATUS["NONFINITE"]).any()
