@@ -120,13 +120,135 @@ __device__ __forceinline__ void for_row(const void* row, int V, F f) {
 constexpr int kThrBins = 4096;   // bins of the widest digit (12 bits)
 
 struct ThrLds {
-  unsigned long long h[kThrBins];   // counts (top-k) or fixed-point masses (top-p) per digit
+  unsigned long long h[kThrBins];   // counts (top-k) or fixed-point masses (top-p) per digit;
+                                    // bf16 window: per-key counts (as uint32_t)
   unsigned long long wsum[kWaves];
+  double redd[kWaves];
+  double zwin;
   float redf[kWaves];
   int redi[kWaves];
   int digit;
   unsigned long long above;
 };
+
+// Scan over the block in thread order, in a fixed order (deterministic): excl = the sum over
+// the threads before this one, incl = excl + v, each computed so that incl of thread t - 1 and
+// excl of thread t are the same number.
+template <typename T>
+__device__ __forceinline__ void block_scan(T v, T* red, T& excl, T& incl) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  T x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  T e = __shfl_up(x, 1, 64);
+  if (lane == 0) e = 0;
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  T off = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+    if (w < wave) off += red[w];
+  __syncthreads();
+  excl = lane == 0 ? off : off + e;
+  incl = off + x;
+}
+
+// exp2((x - m) c) in fp64 to ~1 ulp of fp32 (the exponent's integer part exact).
+__device__ __forceinline__ double mass_d(float x, float m, double c) {
+  const double t = ((double)x - (double)m) * c;
+  if (!(t > -1100.0)) return 0.0;
+  const double n = floor(t);
+  return ldexp((double)__builtin_amdgcn_exp2f((float)(t - n)), (int)n);
+}
+
+// bf16 rows: the filter resolved on the window of the 4096 order keys just below the row
+// maximum, where one key is one value.  One pass counts every key of the window (and, with
+// top-k off, adds up the mass of the logits below it); the top-k and top-p selections then walk
+// the per-value counts from the top, each value group's mass count * exp2((v - m) c) taken in
+// fp64 (full-precision exp2), in a fixed order.  Returns false, leaving the row to the generic passes, when the k-th
+// largest logit or the top-p boundary lies below the window.
+template <bool VEC>
+__device__ bool window_threshold(ThrLds& S, const void* row, int V, int k, float top_p, double c, float mx,
+                                 bool use_k, bool use_p, float* thr, int lr) {
+  const int t = threadIdx.x;
+  const int key_m = (int)(order_key(mx) >> 16);
+  const int lo = max(key_m - (kThrBins - 1), 0);   // bin b holds key lo + b
+  uint32_t* cw = (uint32_t*)S.h;
+  for (int i = t; i < kThrBins; i += kThreads) cw[i] = 0u;
+  __syncthreads();
+  double bmass = 0.0;
+  for_row<kDtBF16, VEC>(row, V, [&](float x) {
+    const int key = (int)(order_key(x) >> 16);
+    if (key >= lo) atomicAdd(&cw[key - lo], 1u);
+    else if (!use_k) bmass += mass_d(x, mx, c);
+  });
+  __syncthreads();
+  constexpr int kPer = kThrBins / kThreads;
+  const int hi = kThrBins - kPer * t;   // this thread's bins: hi - 1 down to hi - kPer
+  int bk = 0;                           // lowest bin in the top-k set
+  if (use_k) {
+    int cs = 0;
+#pragma unroll
+    for (int q = 1; q <= kPer; ++q) cs += (int)cw[hi - q];
+    int excl, incl;
+    block_scan(cs, S.redi, excl, incl);
+    if (t == 0) S.digit = -1;
+    __syncthreads();
+    if (excl < k && incl >= k) {
+      int run = excl;
+      for (int q = 1; q <= kPer; ++q) {
+        run += (int)cw[hi - q];
+        if (run >= k) { S.digit = hi - q; break; }
+      }
+    }
+    __syncthreads();
+    bk = S.digit;
+    __syncthreads();
+    if (bk < 0) return false;   // fewer than k logits in the window
+  }
+  int bp = bk;
+  if (use_p) {
+    double ms = 0.0;
+#pragma unroll 4
+    for (int q = 1; q <= kPer; ++q) {
+      const int b = hi - q;
+      const uint32_t n = cw[b];
+      if (b >= bk && n) ms += (double)n * exp2(((double)key16_value(lo + b) - (double)mx) * c);
+    }
+    double excl, incl;
+    block_scan(ms, S.redd, excl, incl);
+    if (t == kThreads - 1) S.zwin = incl;   // the window's mass at or above bin bk
+    __syncthreads();
+    const double zb = use_k ? 0.0 : block_sum_d(bmass, S.redd);
+    const double target = (double)top_p * (S.zwin + zb);   // top_p * Z_K
+    if (t == 0) S.digit = -1;
+    __syncthreads();
+    if (!(excl >= target) && incl >= target) {
+      // the boundary value group is among this thread's bins (if rounding of the walk leaves
+      // it short, the last one with mass)
+      double run = excl;
+      int last = -1;
+      for (int q = 1; q <= kPer; ++q) {
+        const int b = hi - q;
+        const uint32_t n = cw[b];
+        if (b < bk || !n) continue;
+        last = b;
+        run += (double)n * exp2(((double)key16_value(lo + b) - (double)mx) * c);
+        if (run >= target) break;
+      }
+      S.digit = last;
+    }
+    __syncthreads();
+    bp = S.digit;
+    __syncthreads();
+    if (bp < 0) return false;   // the boundary lies below the window
+  }
+  if (t == 0) thr[lr] = (use_k || use_p) ? key16_value(lo + max(bk, bp)) : -INFINITY;
+  return true;
+}
 
 __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* red) {
 #pragma unroll
@@ -185,7 +307,8 @@ __device__ void thr_select(ThrLds& S, int nb, unsigned long long base, Reach rea
 // radix select over the same digits finds it exactly, one pass per digit.  The first digit is
 // 12 bits wide, so a realistic row spreads over many LDS bins and the atomics rarely collide;
 // bf16 keys (16 bits) take digits of 12 + 4 bits, fp32 keys 12 + 12 + 8.  Every pass re-reads
-// the row.
+// the row.  A bf16 row first tries the window of the 4096 values below its maximum (two passes
+// in all), which settles every realistic row.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_threshold(RowMap m, int V, int k, float top_p, double c,
                                                          float* __restrict__ thr) {
@@ -201,21 +324,21 @@ __global__ __launch_bounds__(kThreads) void k_threshold(RowMap m, int V, int k, 
   const bool use_k = k > 0 && k < V;
   const bool use_p = top_p < 1.f;
 
-  // pass 1: the row max, the NaN / +inf flag and, with top-k, the first digit's counts
-  for (int i = t; i < kThrBins; i += kThreads) S.h[i] = 0ull;
-  __syncthreads();
+  // pass 1: the row max and the NaN / +inf flag
   float mx = -INFINITY;
   int bad = 0;
   for_row<DT, VEC>(row, V, [&](float x) {
     mx = fmaxf(mx, x);
     bad |= __builtin_amdgcn_class(x, 0x203) ? 1 : 0;   // NaN, +inf
-    if (use_k) atomicAdd(&S.h[key_of(x) >> (KB - 12)], 1ull);
   });
   mx = block_max(mx, S.redf);
   bad = block_or(bad, S.redi);
   if (bad || !(mx > -INFINITY)) {
     if (t == 0) thr[lr] = -INFINITY;
     return;
+  }
+  if constexpr (DT == kDtBF16) {
+    if (window_threshold<VEC>(S, row, V, k, top_p, c, mx, use_k, use_p, thr, lr)) return;
   }
 
   uint32_t key_k = 0u;   // every key at or above it is in the top-k set
@@ -225,14 +348,12 @@ __global__ __launch_bounds__(kThreads) void k_threshold(RowMap m, int V, int k, 
     int rb = KB;                       // key bits below the prefix
     for (int L = 0; L < NL; ++L) {
       const int w = width(L), sh = rb - w;
-      if (L > 0) {
-        for (int i = t; i < (1 << w); i += kThreads) S.h[i] = 0ull;
-        __syncthreads();
-        for_row<DT, VEC>(row, V, [&](float x) {
-          const uint32_t key = key_of(x);
-          if ((key >> rb) == prefix) atomicAdd(&S.h[(key >> sh) & ((1u << w) - 1u)], 1ull);
-        });
-      }
+      for (int i = t; i < (1 << w); i += kThreads) S.h[i] = 0ull;
+      __syncthreads();
+      for_row<DT, VEC>(row, V, [&](float x) {
+        const uint32_t key = key_of(x);
+        if (L == 0 || (key >> rb) == prefix) atomicAdd(&S.h[(key >> sh) & ((1u << w) - 1u)], 1ull);
+      });
       __syncthreads();
       thr_select(S, 1 << w, above, [&](unsigned long long n) { return n >= (unsigned long long)k; });
       const int d = S.digit;

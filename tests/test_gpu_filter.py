@@ -453,3 +453,29 @@ def test_dense_filtered_full_size_sampled():
     note(repr(rep))
     assert rep.ok(), rep
     assert not (gpu["status"] & L.STATUS["NONFINITE"]).any()
+
+
+@pytest.mark.parametrize("T,k,p", [(50.0, 0, 0.99), (1.0, 12000, 1.0), (20.0, 11000, 0.95)])
+def test_dense_filtered_wide_sets(T, k, p):
+    """Kept sets reaching below the 4096 values under the row maximum (a nearly flat
+    distribution, or k close to V): bf16 rows fall back to the generic radix passes."""
+    sp = O.SamplingParams(T, k, p)
+    inp = filtered_inputs(3, V_SMALL, [4, 2, 5], sp, seed=400 + k)
+    check(inp, sp)
+
+
+@pytest.mark.parametrize("dtype,k,p,T", [("bf16", 12000, 1.0, 1.0), ("bf16", 0, 0.99, 50.0)])
+def test_dense_filtered_row_stats_wide(dtype, k, p, T):
+    V = 3 * 4096 + 72
+    rng = np.random.default_rng(k + 5)
+    x = rng.standard_normal((6, V), dtype=np.float32) * 3
+    t, xf = _rows(x, dtype)
+    res = L.spec_row_stats(t, temperature=T, top_k=k, top_p=p)
+    torch.cuda.synchronize()
+    g = H.gpu_to_numpy(res)
+    ref = O.row_stats(xf, O.SamplingParams(T, k, p))
+    ok = ref["topp_margin"] >= H.DECISION_EPS
+    assert ok.sum() >= 5
+    assert np.array_equal(g["kept_count"][ok], ref["kept_count"][ok])
+    for key in ("log_z", "entropy_bits", "max_prob"):
+        assert H.close(g[key][ok], ref[key][ok]), (key, H.max_rel(g[key][ok], ref[key][ok]))
