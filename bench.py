@@ -120,6 +120,38 @@ def cpu_baseline(inp, budget_s):
     }
 
 
+def filtered_draft_tokens(inp, seed=77):
+    """Draft tokens drawn from each draft row's filtered, tempered distribution (temperature,
+    top-k with its boundary ties, then top-p over the kept set by value groups), as a draft model
+    that samples from its own filtered q proposes them.  Plain numpy, only to synthesise the
+    inputs of a filtered workload (the unfiltered draw in the workloads module would propose
+    tokens outside the filtered support)."""
+    wl = inp.wl
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = inp.draft_f32().astype(np.float64)
+    V = rows.shape[1]
+    toks = np.empty(rows.shape[0], dtype=np.int32)
+    for r in range(rows.shape[0]):
+        x = rows[r]
+        if 0 < wl.top_k < V:
+            kth = np.partition(x, V - wl.top_k)[V - wl.top_k]
+            idx = np.nonzero(x >= kth)[0]
+        else:
+            idx = np.arange(V)
+        v = x[idx]
+        e = np.exp((v - v.max()) / wl.temperature)
+        if wl.top_p < 1.0:
+            order = np.argsort(-v, kind="stable")
+            vs, es = v[order], e[order] / e.sum()
+            starts = np.r_[0, np.nonzero(vs[1:] != vs[:-1])[0] + 1]
+            cum = np.add.reduceat(es, starts).cumsum()
+            g = int(np.searchsorted(cum, wl.top_p))   # first value group reaching top_p
+            keep = v >= vs[starts[min(g, len(starts) - 1)]]
+            idx, e = idx[keep], e[keep]
+        toks[r] = idx[rng.choice(len(idx), p=e / e.sum())]
+    return toks
+
+
 def load_traffic(kernel):
     """HBM traffic per launch from the committed rocprofv3 counter summary, if it was taken
     on the current kernel source."""
@@ -163,6 +195,8 @@ def main():
     cfg = args.config
     inp = W.make_inputs(cfg)
     wl = inp.wl
+    if wl.temperature > 0 and inp.draft is not None and (0 < wl.top_k < wl.V or wl.top_p < 1.0):
+        inp.tokens = filtered_draft_tokens(inp)
     B = len(inp.gammas)
     G = int(inp.gammas.max())
     positions = int(inp.gammas.sum())
@@ -245,8 +279,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded numpy PCG64; N(0, 3^2) target logits, draft = target + N(0, 1^2), "
-                "draft tokens drawn from the tempered draft distribution)",
+        "data": (f"synthetic (seeded numpy PCG64; N(0, {wl.sigma:g}^2) target logits, "
+                 + ("token-only draft" if inp.draft is None else
+                    f"draft = target + N(0, {wl.tau:g}^2)" if wl.tau is not None else "independent draft rows")
+                 + (", draft tokens drawn from the filtered tempered draft distribution)"
+                    if wl.temperature > 0 and (0 < wl.top_k < wl.V or wl.top_p < 1.0) else
+                    ", draft tokens drawn from the tempered draft distribution)" if wl.temperature > 0 else
+                    ", draft tokens = argmax of target + noise)")),
         "config": {"workload": wl.name, "B": B, "gamma": G, "V": wl.V, "positions_per_step": positions,
                    "temperature": wl.temperature, "top_k": wl.top_k, "top_p": wl.top_p,
                    "algorithmic_bytes_per_step": alg_bytes, "input_copies_rotated": copies,
