@@ -420,7 +420,8 @@ __global__ __launch_bounds__(kThreads) void k_filt_slices(FilterArgs a) {
 
 // ---------------------------------------------------------------- k_filt_rows
 
-constexpr int kRowStage = 4096;   // candidates of a row staged in LDS (more: read in place)
+constexpr int kRowStage = 2304;   // candidates of a row staged in LDS (more: read in place); 30 KB of
+                                  // LDS in all, so 5 rows share a CU
 
 struct RowLds {
   SelLds sel;
