@@ -268,6 +268,12 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   const float nan = __int_as_float(0x7fc00000);
   const double cd = (double)a.c;
   const __amdgpu_buffer_rsrc_t rrs = rec_rsrc(a);
+  // the draft tokens go out before this request's offsets arrive, at c0 = b G (exact when every
+  // request has G draft tokens); a wrong guess loads them again
+  const int cg = b * a.G;
+  const bool guess_in = cg + a.G <= a.n_draft_rows;
+  int ytok = -1;
+  if (guess_in && t < a.G) ytok = a.tokens[cg + t];
   // this request's offsets straight from memory; the whole array is checked below, and these
   // are clamped into the declared arrays until then (an offset pair failing this test fails
   // the whole check too)
@@ -276,16 +282,14 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   const bool gok = c0 >= 0 && c1 >= c0 && c1 - c0 <= a.G && c1 <= a.n_draft_rows && c0 + b + (c1 - c0) < a.n_teams;
   if (!gok) c0 = c1 = 0;
   const int g = c1 - c0;
-  // the draft tokens, their logits, the first two teams of this wave and the Philox blocks do
-  // not depend on one another: all go out before anything waits
+  if (!(guess_in && c0 == cg)) ytok = t < g ? a.tokens[c0 + t] : -1;
+  if (t >= g) ytok = -1;
+  // the draft tokens' logits, the first two teams of this wave and the Philox blocks do not
+  // depend on one another: all go out before anything waits
   float ly_p = 0.f, ly_q = 0.f;
-  int ytok = -1;
-  if (t < g) {
-    ytok = a.tokens[c0 + t];
-    if (ytok >= 0 && ytok < a.V) {
-      ly_p = logit_at<DT>(row_ptr<DT>(a.tgt, a.tgt_ld, c0 + b + t), ytok);
-      if (MODE == kFuSample) ly_q = logit_at<DT>(row_ptr<DT>(a.drf, a.drf_ld, c0 + t), ytok);
-    }
+  if (t < g && ytok >= 0 && ytok < a.V) {
+    ly_p = logit_at<DT>(row_ptr<DT>(a.tgt, a.tgt_ld, c0 + b + t), ytok);
+    if (MODE == kFuSample) ly_q = logit_at<DT>(row_ptr<DT>(a.drf, a.drf_ld, c0 + t), ytok);
   }
   TeamRaw pre[2];
   pre[0] = team_load<MODE>(a, rrs, c0, b, g, wave);
@@ -313,7 +317,11 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
     return;
   }
 
-  // A. combine each team's records (one wave per team); the streaming kernel has finished
+  // A. combine each team's records (one wave per team); the streaming kernel has finished.  The
+  // first two teams of each wave keep their per-slice p records and residual masses in
+  // registers for the level-1 pick.
+  float kpr[2] = {-INFINITY, -INFINITY}, kps[2] = {0.f, 0.f};
+  double ksm[2] = {0.0, 0.0};
   for (int ti = wave, it = 0; ti <= g; ti += kWaves, ++it) {
     const int r = c0 + b + ti;
     const bool pair = (MODE == kFuSample) && ti < g;
@@ -334,6 +342,11 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
           ok = ok && tag_of(R.m[w]) == tag;
         }
       }
+    }
+    if (it < 2) {
+      kpr[it & 1] = pr;
+      kps[it & 1] = ps;
+      ksm[it & 1] = sm;
     }
     const bool missing = !wave_all(ok);
     TeamL T;
@@ -478,20 +491,30 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   } else {
     const int r = c0 + b + F.pos;
     const TeamL T = F.team[F.pos];
-    // D. level 1 over the chunk masses (p's masses again if the residual turned out empty)
-    if (wave == 0) {
+    // D. level 1 over the chunk masses (p's masses again if the residual turned out empty), by
+    // the wave that combined team F.pos: its per-slice values are still in registers when the
+    // team was one of its first two, else they are read again
+    const int own = F.pos & (kWaves - 1), oit = F.pos / kWaves;
+    if (wave == own) {
+      const bool kept = oit < 2;
+      const float kr = (oit & 1) ? kpr[1] : kpr[0], ks = (oit & 1) ? kps[1] : kps[0];
+      const double km = (oit & 1) ? ksm[1] : ksm[0];
       int wkind = F.wkind;
       int pick = -1;
       for (int pass = 0; pass < 2; ++pass) {
         double m = 0.0;
         if (lane < n_s) {
           if (wkind == 1) {
-            const uint64_t* mw = a.smass + ((int64_t)r * n_s + lane) * kWaves;
+            if (kept) {
+              m = km;
+            } else {
+              const uint64_t* mw = a.smass + ((int64_t)r * n_s + lane) * kWaves;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) m += (double)lo_f(ld_coh(mw + w));
+              for (int w = 0; w < kWaves; ++w) m += (double)lo_f(ld_coh(mw + w));
+            }
           } else {
-            float ref, sv, wv;
-            load_rec(rrs, rec_off(n_s, r, lane, 0), tag, ref, sv, wv);
+            float ref = kr, sv = ks, wv;
+            if (!kept) load_rec(rrs, rec_off(n_s, r, lane, 0), tag, ref, sv, wv);
             m = sv > 0.f ? (double)sv * exp2_split((double)ref - (double)T.M[0]) / T.z[0] : 0.0;
             if (wkind == 2) {
               const int y = F.y;
