@@ -145,30 +145,72 @@ __device__ __forceinline__ void unpack_raw(const RawSlice<DT>& r, float (&v)[kPe
 
 // ---------------------------------------------------------------- reductions (wave64)
 
+// Wave-wide reductions by DPP: two quad permutations and two row rotations reduce each row
+// of 16 lanes, two row broadcasts carry the rows into lane 63, and v_readlane returns lane
+// 63's value to every lane.  Lanes a DPP step does not write keep the identity `old`.  Call
+// them with the whole wave active.
+#define SPEC_DPP_I(old, v, ctrl, rmask) __builtin_amdgcn_update_dpp((old), (v), (ctrl), (rmask), 0xf, false)
+#define SPEC_DPP_F(old, v, ctrl, rmask) \
+  __builtin_bit_cast(float, SPEC_DPP_I(__builtin_bit_cast(int, (old)), __builtin_bit_cast(int, (v)), (ctrl), (rmask)))
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  const float o = -INFINITY;
+  v = fmaxf(v, SPEC_DPP_F(o, v, 0xb1, 0xf));
+  v = fmaxf(v, SPEC_DPP_F(o, v, 0x4e, 0xf));
+  v = fmaxf(v, SPEC_DPP_F(o, v, 0x124, 0xf));
+  v = fmaxf(v, SPEC_DPP_F(o, v, 0x128, 0xf));
+  v = fmaxf(v, SPEC_DPP_F(o, v, 0x142, 0xa));
+  v = fmaxf(v, SPEC_DPP_F(o, v, 0x143, 0xc));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += SPEC_DPP_F(0.f, v, 0xb1, 0xf);
+  v += SPEC_DPP_F(0.f, v, 0x4e, 0xf);
+  v += SPEC_DPP_F(0.f, v, 0x124, 0xf);
+  v += SPEC_DPP_F(0.f, v, 0x128, 0xf);
+  v += SPEC_DPP_F(0.f, v, 0x142, 0xa);
+  v += SPEC_DPP_F(0.f, v, 0x143, 0xc);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 __device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
-  return v;
+  v = min(v, SPEC_DPP_I(INT_MAX, v, 0xb1, 0xf));
+  v = min(v, SPEC_DPP_I(INT_MAX, v, 0x4e, 0xf));
+  v = min(v, SPEC_DPP_I(INT_MAX, v, 0x124, 0xf));
+  v = min(v, SPEC_DPP_I(INT_MAX, v, 0x128, 0xf));
+  v = min(v, SPEC_DPP_I(INT_MAX, v, 0x142, 0xa));
+  v = min(v, SPEC_DPP_I(INT_MAX, v, 0x143, 0xc));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 __device__ __forceinline__ int wave_or(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
-  return v;
+  v |= SPEC_DPP_I(0, v, 0xb1, 0xf);
+  v |= SPEC_DPP_I(0, v, 0x4e, 0xf);
+  v |= SPEC_DPP_I(0, v, 0x124, 0xf);
+  v |= SPEC_DPP_I(0, v, 0x128, 0xf);
+  v |= SPEC_DPP_I(0, v, 0x142, 0xa);
+  v |= SPEC_DPP_I(0, v, 0x143, 0xc);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+// 64-bit DPP move of both halves (lanes whose source is outside the row, or rows outside
+// RMASK, read 0).
+template <int CTRL, int RMASK>
+__device__ __forceinline__ double dpp_d(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, RMASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, RMASK, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, lane), hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v += dpp_d<0xb1, 0xf>(v);
+  v += dpp_d<0x4e, 0xf>(v);
+  v += dpp_d<0x124, 0xf>(v);
+  v += dpp_d<0x128, 0xf>(v);
+  v += dpp_d<0x142, 0xa>(v);
+  v += dpp_d<0x143, 0xc>(v);
+  return readlane_d(v, 63);
 }
 
 // DPP wave reductions (gfx9 row broadcasts): the result is valid in lane 63 and is returned
@@ -424,20 +466,6 @@ __device__ __forceinline__ void sload2_i32(const int32_t* p, int& a, int& b) {
 
 // ---------------------------------------------------------------- wave-wide fp64 helpers
 
-// 64-bit DPP move of both halves (lanes whose source is outside the row, or rows outside
-// RMASK, read 0).
-template <int CTRL, int RMASK>
-__device__ __forceinline__ double dpp_d(double v) {
-  const long long b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, RMASK, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, RMASK, 0xf, false);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
-}
-__device__ __forceinline__ double readlane_d(double v, int lane) {
-  const long long b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readlane((int)b, lane), hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
-}
 // fp64 sum over the wave in a fixed order (row reductions, then row broadcasts); every lane
 // gets lane 63's total.
 __device__ __forceinline__ double wave_sum_dpp_d(double v) {

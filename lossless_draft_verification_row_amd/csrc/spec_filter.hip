@@ -160,6 +160,15 @@ __device__ void slice_candidates(const FilterArgs& a, SelLds& S, const float (&v
   slice_candidates_g<DT>(a, S, [&](int j) { return v[j]; }, slot, s, base);
 }
 
+// Mask of the wave's lanes with x >= y, straight from the compare into a scalar register pair
+// (one instruction; the wave is whole here, so it is the ballot).  Opaque to the compiler, so
+// it is formed where it is used rather than carried across a barrier.
+__device__ __forceinline__ unsigned long long wave_mask_ge(float x, float y) {
+  unsigned long long m;
+  asm volatile("v_cmp_ge_f32_e64 %0, %1, %2" : "=s"(m) : "v"(x), "v"(y));
+  return m;
+}
+
 __device__ __forceinline__ int wave_max_i(int v) {
   v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0xb1, 0xf, 0xf, false));
   v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x4e, 0xf, 0xf, false));
@@ -202,20 +211,21 @@ __device__ void slice_candidates_bf16(const FilterArgs& a, Sel2Lds& S, const flo
                                       int base, const void* row_p, const void* row_q) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int nrow = paired ? 2 : 1;
+  // per-thread maxima with NaN propagated (three-input maximum): a NaN or +inf anywhere makes
+  // the maximum NaN or +inf, which flags the row (its candidates are then never read)
   float fm[2] = {-INFINITY, -INFINITY};
-  int bad[2] = {0, 0};
+  int bad[2];
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
-    bad[0] |= __builtin_amdgcn_class(vp[j], 0x203) ? 1 : 0;
-    fm[0] = fmaxf(fm[0], vp[j]);
-    if (paired) {
-      bad[1] |= __builtin_amdgcn_class(vq[j], 0x203) ? 1 : 0;
-      fm[1] = fmaxf(fm[1], vq[j]);
-    }
+    fm[0] = __builtin_elementwise_maximum(fm[0], vp[j]);
+    if (paired) fm[1] = __builtin_elementwise_maximum(fm[1], vq[j]);
   }
   int tm[2];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) tm[r] = fm[r] > -INFINITY ? key16(fm[r]) : -1;
+  for (int r = 0; r < 2; ++r) {
+    bad[r] = fm[r] < INFINITY ? 0 : 1;
+    tm[r] = (fm[r] > -INFINITY && fm[r] < INFINITY) ? key16(fm[r]) : -1;
+  }
   S.hist[0][t] = 0u;
   S.hist[1][t] = 0u;
   int mx[2];
@@ -259,27 +269,26 @@ __device__ void slice_candidates_bf16(const FilterArgs& a, Sel2Lds& S, const flo
   }
   __syncthreads();
   float tf[2];
-  int fb[2], cnt[2] = {0, 0};
+  int fb[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     fb[r] = r < nrow ? S.fb[r] : 1;
     tf[r] = fb[r] ? INFINITY : key16_value(S.tau[r]);
   }
-  // finite logits at or above the threshold value (NaN compares false; +inf is excluded)
+  // candidates: the logits at or above the threshold value (NaN compares false; a +inf only
+  // occurs in a flagged row).  Each wave counts them per element with one ballot, so the
+  // counts are scalar; a candidate's slot is the wave's base, the element's running total and
+  // its rank among the wave's lanes (mbcnt).
+  int wc[2] = {0, 0};
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
-    cnt[0] += (vp[j] >= tf[0] && vp[j] < INFINITY) ? 1 : 0;
-    cnt[1] += (vq[j] >= tf[1] && vq[j] < INFINITY) ? 1 : 0;
+    wc[0] += __popcll(__builtin_amdgcn_ballot_w64(vp[j] >= tf[0]));
+    wc[1] += __popcll(__builtin_amdgcn_ballot_w64(vq[j] >= tf[1]));
   }
-  int off[2], tot[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int inc = wave_incl_scan_i(cnt[r]);
-    off[r] = inc - cnt[r];
-    if (lane == 63) S.wtot[r][wave] = inc;
-  }
+  if (lane == 0) { S.wtot[0][wave] = wc[0]; S.wtot[1][wave] = wc[1]; }
   __syncthreads();
   const int cap = a.cap;
+  int off[2], tot[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     int o = 0, tt = 0;
@@ -288,7 +297,7 @@ __device__ void slice_candidates_bf16(const FilterArgs& a, Sel2Lds& S, const flo
       if (w < wave) o += S.wtot[r][w];
       tt += S.wtot[r][w];
     }
-    off[r] += o;
+    off[r] = o;
     tot[r] = tt;
     if (tot[r] > cap) fb[r] = 1;
   }
@@ -297,13 +306,22 @@ __device__ void slice_candidates_bf16(const FilterArgs& a, Sel2Lds& S, const flo
   for (int r = 0; r < 2; ++r) {
     if (fb[r]) continue;
     const float (&v)[kPerThread] = r == 0 ? vp : vq;
-    int o = off[r];
+    int run = __builtin_amdgcn_readfirstlane(off[r]);   // uniform over the wave
+    CandEntry* st = S.stage + r * cap;
+    const int x0 = slice_index<kDtBF16>(base, t, 0);
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-      if (v[j] >= tf[r] && v[j] < INFINITY) {
-        S.stage[r * cap + o].v = v[j];
-        S.stage[r * cap + o].x = slice_index<kDtBF16>(base, t, j);
-        ++o;
+      const unsigned long long mk = wave_mask_ge(v[j], tf[r]);
+      if (mk) {
+        if (__builtin_amdgcn_inverse_ballot_w64(mk)) {
+          const int o = run + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(mk >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((unsigned)mk, 0u));
+          CandEntry c;
+          c.v = v[j];
+          c.x = x0 + (slice_index<kDtBF16>(base, t, j) - slice_index<kDtBF16>(base, t, 0));
+          st[o] = c;
+        }
+        run += __popcll(mk);
       }
     }
   }
