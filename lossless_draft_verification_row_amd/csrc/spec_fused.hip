@@ -798,8 +798,8 @@ __device__ __forceinline__ void exp_raw_stash(const RawSlice<DT>& r, float4 (*st
 struct FusedLds {
   float4 stash[kPerThread / 4][kThreads];   // a paired ticket's target e-values of slice 1
   float wp[2][kWaves][4];   // [row][wave] {ref, sum e over slice 0, over slice 1, sum e t}
-  float rec[2][64][2];      // the team's records {ref, s} of the target and draft rows, one per slice
-  int rst;                  // team status: 0 ok, 1 non-finite row, 2 wait gave up
+  float tn[5];              // the team's normalisers {M_p, M_q, 1 / Z_p, 1 / Z_q, Z_q / Z_p}
+  int tst;                  // team status: 0 ok, 1 non-finite row, 2 wait gave up
   int bad[kWaves];
   int amax[2][kWaves];
 };
@@ -847,11 +847,38 @@ __device__ __forceinline__ void fold_waves_rt(const float (*pw)[4], int K, bool 
   }
 }
 
+// Team normalisers from the team's records (lane s holds slice s): M = max_s ref_s and
+// Z = sum_s s_s 2^(ref_s - M) for each row, in fp32 with a fixed-order tree sum.  Status 0 ok,
+// 1 a row non-finite or empty, 2 the wait gave up.
+struct TeamNorm {
+  float Mp, Mq, izp, izq, zratio;
+};
+__device__ __forceinline__ int team_norm(float pr, float ps, float qr, float qs, int n_s, bool timed_out,
+                                         TeamNorm& N) {
+  const int lane = threadIdx.x & 63;
+  const bool in = lane < n_s;
+  const bool bad = in && (!(ps == ps) || !(ps < INFINITY) || pr == INFINITY || !(qs == qs) || !(qs < INFINITY) ||
+                          qr == INFINITY);
+  float Mp = in ? pr : -INFINITY, Mq = in ? qr : -INFINITY;
+  dpp_max2(Mp, Mq);
+  float zp = (in && ps > 0.f) ? ps * __builtin_amdgcn_exp2f(pr - Mp) : 0.f;
+  float zq = (in && qs > 0.f) ? qs * __builtin_amdgcn_exp2f(qr - Mq) : 0.f;
+  dpp_sum2(zp, zq);
+  N.Mp = Mp;
+  N.Mq = Mq;
+  N.izp = __builtin_amdgcn_rcpf(zp);
+  N.izq = __builtin_amdgcn_rcpf(zq);
+  N.zratio = zq * N.izp;
+  if (timed_out) return 2;
+  return (wave_all(!bad) && zp > 0.f && zq > 0.f && Mp > -INFINITY && Mq > -INFINITY) ? 0 : 1;
+}
+
 // Wave 0 of a paired ticket: wait until every member of the team has raised its arrival flag
 // (the team's flags share one cache line, so a poll reads one line; lanes past the last member
-// read the first flag again), then read the team's records (one slice per lane) into LDS.  A
-// flag goes out right behind its records, so a record may still be in flight when the flag is
-// seen: its check word then fails and the records are read again.  Every wait is bounded.
+// read the first flag again), then read the team's records (one slice per lane) and publish
+// the team's normalisers to the workgroup through LDS.  A flag goes out right behind its
+// records, so a record may still be in flight when the flag is seen: its check word then fails
+// and the records are read again.  Every wait is bounded.
 __device__ __forceinline__ void team_gather(const FusedArgs& a, FusedLds& L, int r, int n_u) {
   const int lane = threadIdx.x & 63;
   const int n_s = a.n_s;
@@ -875,39 +902,17 @@ __device__ __forceinline__ void team_gather(const FusedArgs& a, FusedLds& L, int
     P = load_rec_raw(rrs, rec_off(n_s, r, sl, 0));
     Q = load_rec_raw(rrs, rec_off(n_s, r, sl, 1));
   }
-  L.rec[0][lane][0] = __uint_as_float(P.x);
-  L.rec[0][lane][1] = __uint_as_float(P.y);
-  L.rec[1][lane][0] = __uint_as_float(Q.x);
-  L.rec[1][lane][1] = __uint_as_float(Q.y);
-  if (lane == 0) L.rst = timed_out ? 2 : 0;
-}
-
-// Team normalisers, formed by every wave from the staged records (lane s holds slice s):
-// M = max_s ref_s and Z = sum_s s_s 2^(ref_s - M) for each row, in fp32 with a fixed-order
-// tree sum.  Returns the team status (0 ok, 1 a row non-finite or empty, 2 wait gave up).
-struct TeamNorm {
-  float Mp, Mq, izp, izq, zratio;
-};
-__device__ __forceinline__ int team_norm(const FusedLds& L, int n_s, TeamNorm& N) {
-  const int lane = threadIdx.x & 63;
-  const bool in = lane < n_s;
-  const float pr = L.rec[0][lane][0], ps = L.rec[0][lane][1];
-  const float qr = L.rec[1][lane][0], qs = L.rec[1][lane][1];
-  const bool bad = in && (!(ps == ps) || !(ps < INFINITY) || pr == INFINITY || !(qs == qs) || !(qs < INFINITY) ||
-                          qr == INFINITY);
-  float Mp = in ? pr : -INFINITY, Mq = in ? qr : -INFINITY;
-  dpp_max2(Mp, Mq);
-  float zp = (in && ps > 0.f) ? ps * __builtin_amdgcn_exp2f(pr - Mp) : 0.f;
-  float zq = (in && qs > 0.f) ? qs * __builtin_amdgcn_exp2f(qr - Mq) : 0.f;
-  dpp_sum2(zp, zq);
-  const int st = L.rst;
-  N.Mp = Mp;
-  N.Mq = Mq;
-  N.izp = __builtin_amdgcn_rcpf(zp);
-  N.izq = __builtin_amdgcn_rcpf(zq);
-  N.zratio = zq * N.izp;
-  if (st) return st;
-  return (wave_all(!bad) && zp > 0.f && zq > 0.f && Mp > -INFINITY && Mq > -INFINITY) ? 0 : 1;
+  TeamNorm N;
+  const int st = team_norm(__uint_as_float(P.x), __uint_as_float(P.y), __uint_as_float(Q.x), __uint_as_float(Q.y),
+                           n_s, timed_out, N);
+  if (lane == 0) {
+    L.tn[0] = N.Mp;
+    L.tn[1] = N.Mq;
+    L.tn[2] = N.izp;
+    L.tn[3] = N.izq;
+    L.tn[4] = N.zratio;
+    L.tst = st;
+  }
 }
 
 // Residual mass of this wave's part of one paired slice, sum [p - q]_+ (guide page "5.1 投机
@@ -1156,7 +1161,12 @@ __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
   if (wave == 0) team_gather(a, L, r, n_u);
   __syncthreads();
   TeamNorm N;
-  const int st = team_norm(L, n_s, N);
+  N.Mp = L.tn[0];
+  N.Mq = L.tn[1];
+  N.izp = L.tn[2];
+  N.izq = L.tn[3];
+  N.zratio = L.tn[4];
+  const int st = L.tst;
   float m0 = 0.f, m1 = 0.f;
   if (st == 0) {
     const ResidualScale R = residual_scale(N, refp, refq);
