@@ -674,26 +674,34 @@ __device__ __forceinline__ float raw_elem(const RawSlice<DT>& r, int j) {
   if constexpr (DT == kDtBF16) return (j & 1) ? bf16_hi(r.w[j >> 1]) : bf16_lo(r.w[j >> 1]);
   else return __uint_as_float(r.w[j]);
 }
-// Max of a slice (quiet NaN ignored).  bf16: both halves are extracted exactly (a whole word
-// read as a float could be a signalling NaN when its high half is -inf); the extraction is
-// opaque to the compiler so that the exponent pass forms the logits again instead of keeping
-// an unpacked copy of the slice.
+// Max of two slices given as raw words.  bf16: on the packed 16-bit patterns read as signed
+// integers, non-negative values order like their patterns and negative ones (sign bit set) in
+// reverse, so per half the largest non-negative pattern, or failing any the negative pattern
+// of least magnitude (the integer minimum), is the largest value; two packed integer ops per
+// word, and no word is ever read as a float (a -inf high half would make it a signalling NaN).
+// A NaN pattern is ignored unless a half holds nothing else; a row holding one is reported
+// from its sums either way.  fp32: the plain max (quiet NaN ignored).
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 template <int DT>
-__device__ __forceinline__ float max_raw(const RawSlice<DT>& r, float m) {
+__device__ __forceinline__ float max_raw2(const RawSlice<DT>& r0, const RawSlice<DT>& r1) {
   if constexpr (DT == kDtBF16) {
+    s16x2 mx = {(short)-32768, (short)-32768}, mn = {(short)32767, (short)32767};
 #pragma unroll
     for (int k = 0; k < RawSlice<DT>::kWords; ++k) {
-      uint32_t lo, hi;
-      asm("v_lshlrev_b32 %0, 16, %1" : "=v"(lo) : "v"(r.w[k]));
-      asm("v_and_b32 %0, 0xffff0000, %1" : "=v"(hi) : "v"(r.w[k]));
-      m = fmaxf(fmaxf(m, __uint_as_float(hi)), __uint_as_float(lo));
+      const s16x2 w0 = __builtin_bit_cast(s16x2, r0.w[k]), w1 = __builtin_bit_cast(s16x2, r1.w[k]);
+      mx = __builtin_elementwise_max(mx, __builtin_elementwise_max(w0, w1));
+      mn = __builtin_elementwise_min(mn, __builtin_elementwise_min(w0, w1));
     }
+    const uint32_t h0 = (uint16_t)(mx.x >= 0 ? mx.x : mn.x), h1 = (uint16_t)(mx.y >= 0 ? mx.y : mn.y);
+    return fmaxf(__uint_as_float(h0 << 16), __uint_as_float(h1 << 16));
   } else {
+    float m = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < RawSlice<DT>::kWords; ++k) m = fmaxf(m, __uint_as_float(r.w[k]));
+    for (int k = 0; k < RawSlice<DT>::kWords; ++k) m = fmaxf(fmaxf(m, __uint_as_float(r0.w[k])), __uint_as_float(r1.w[k]));
+    return m;
   }
-  return m;
 }
+
 // Logits at indices >= V (zeros from the bounds check) become -inf, on the raw words.
 template <int DT>
 __device__ __forceinline__ void mask_tail_raw(int V, int base, RawSlice<DT>& r) {
@@ -1099,7 +1107,7 @@ __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
     mask_tail_raw<DT>(a.V, base, rp[0]);
     mask_tail_raw<DT>(a.V, base + kChunk, rp[1]);
   }
-  float mp = max_raw<DT>(rp[1], max_raw<DT>(rp[0], -INFINITY));
+  float mp = max_raw2<DT>(rp[0], rp[1]);
   float mp2 = mp;
   dpp_max2(mp, mp2);
   float refp = mp > -INFINITY ? mp * c : 0.f;
@@ -1118,7 +1126,7 @@ __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
       mask_tail_raw<DT>(a.V, base, rq[0]);
       mask_tail_raw<DT>(a.V, base + kChunk, rq[1]);
     }
-    float mq = max_raw<DT>(rq[1], max_raw<DT>(rq[0], -INFINITY));
+    float mq = max_raw2<DT>(rq[0], rq[1]);
     float mq2 = mq;
     dpp_max2(mq, mq2);
     refq = mq > -INFINITY ? mq * c : 0.f;
