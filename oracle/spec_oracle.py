@@ -48,6 +48,18 @@ Readings taken where the pages leave a step open (plainest reading the rest supp
       RESIDUAL_EMPTY and the token is drawn from p instead.
   R9  A token-only draft at T > 0 is a one-hot q at y; a bad y there leaves q = 0 (residual
       = p).
+  R10 Extra signals per position (the uncertainty features of the tree-search page's
+      selector: both KL divergences and the L1 distance, with the forward KL of the DLite
+      page's loss section, D_KL(p||q) = sum_v p(v) log(p(v)/q(v))): KL in nats (natural log,
+      as written there), 0 log 0 = 0, +inf when one side puts mass where the other has none;
+      L1 = sum_x |p - q| = 2 TV.  They use the same p_i and q_i as verification (q one-hot at
+      y_i for a token-only draft; NaN there when y_i is not a token).  Under greedy (R7) both
+      KL values are NaN.  The accept probability a_i = min(1, p_i(y_i) / q_i(y_i)) (0 when y_i
+      is not a token or q_i(y_i) = 0; greedy: 1 iff y_i is the target argmax) and, per
+      request, the expected number of tokens committed given the drafts,
+      E = 1 + sum_{k=1..gamma} prod_{i<=k} a_i: the tree-search page's variance-free block
+      efficiency (a sum over reachable nodes of products of branch transition probabilities)
+      for a single chain under the standard rule.
 
 Every function states which of the above it follows.  The decision margins recorded next
 to each result (distance of u from the accept ratio, of u*M from the sampler prefix sums,
@@ -289,9 +301,27 @@ class RequestResult:
     target_entropy_bits: np.ndarray  # [gamma + 1]
     target_max_prob: np.ndarray      # [gamma + 1]
     req_stats: np.ndarray            # [4]: mean H, mean c, max H, min c   ([SKV])
+    kl_pq: np.ndarray = None         # [gamma]: D_KL(p_i || q_i) in nats (R10)
+    kl_qp: np.ndarray = None         # [gamma]: D_KL(q_i || p_i) in nats
+    l1: np.ndarray = None            # [gamma]: sum |p_i - q_i| = 2 TV
+    accept_prob: np.ndarray = None   # [gamma]: a_i = min(1, p_i(y_i) / q_i(y_i))
+    expected_committed: float = float("nan")   # 1 + sum_k prod_{i<=k} a_i
     decisions: list = field(default_factory=list)
     target_rows: list = field(default_factory=list)
     draft_rows: list = field(default_factory=list)
+
+
+def kl_divergence(a, b):
+    """D_KL(a || b) = sum_x a(x) ln(a(x) / b(x)) in nats, terms with a(x) = 0 dropped; +inf
+    when a puts mass where b has none (R10)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if np.isnan(a).any() or np.isnan(b).any():
+        return float("nan")
+    pos = a > 0.0
+    if (b[pos] == 0.0).any():
+        return math.inf
+    return float((a[pos] * np.log(a[pos] / b[pos])).sum())
 
 
 def verify_request(target_logits, draft_logits, draft_tokens, sp: SamplingParams,
@@ -327,6 +357,8 @@ def verify_request(target_logits, draft_logits, draft_tokens, sp: SamplingParams
         target_entropy_bits=np.array([r.entropy_bits for r in P]),
         target_max_prob=np.array([r.max_prob for r in P]),
         req_stats=np.full(4, nan), target_rows=P, draft_rows=Q or [],
+        kl_pq=np.full(gamma, nan), kl_qp=np.full(gamma, nan), l1=np.full(gamma, nan),
+        accept_prob=np.full(gamma, nan),
     )
     for r in P + (Q or []):
         if r.topp_margin < math.inf:
@@ -348,15 +380,34 @@ def verify_request(target_logits, draft_logits, draft_tokens, sp: SamplingParams
         p = P[i].probs
         res.one_minus_tv[i] = float(np.minimum(p, qd).sum())
         res.tv[i] = 0.5 * float(np.abs(p - qd).sum())
-        if 0 <= ys[i] < V:
+        yv = 0 <= ys[i] < V
+        if yv:
             res.p_y[i] = float(p[ys[i]])
             res.q_y[i] = float(qd[ys[i]])
+        # extra signals (R10)
+        if Q is not None or yv:
+            res.l1[i] = float(np.abs(p - qd).sum())
+            if not greedy:
+                res.kl_pq[i] = kl_divergence(p, qd)
+                res.kl_qp[i] = kl_divergence(qd, p)
+        if greedy:
+            res.accept_prob[i] = 1.0 if (yv and ys[i] == P[i].argmax) else 0.0
+        elif not yv or qd[ys[i]] == 0.0:
+            res.accept_prob[i] = 0.0
+        else:
+            res.accept_prob[i] = min(1.0, float(p[ys[i]]) / float(qd[ys[i]]))
+    run = 1.0
+    res.expected_committed = 1.0
+    for i in range(gamma):
+        run *= res.accept_prob[i]
+        res.expected_committed += run
     if gamma > 0 and not greedy:
         h, c = res.draft_entropy_bits, res.draft_max_prob
         res.req_stats[:] = [h.mean(), c.mean(), h.max(), c.min()]
 
     if not all(r.finite for r in P + (Q or [])):
         res.status |= STATUS_NONFINITE
+        res.expected_committed = float("nan")
         return res
 
     def draws(i):

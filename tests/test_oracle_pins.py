@@ -533,3 +533,74 @@ def test_chi2_wrong_rule_rejected():
     counts, P = _chi2_trials("p", 6000)
     pv = _chi2_pvalues(counts, P)
     assert min(pv) < 1e-3, pv
+
+
+# ----------------------------------------------------------------------------- extra signals (R10)
+
+
+def test_extra_signals_worked_example():
+    """Worked example p = [0.6, 0.3, 0.1], q = [0.2, 0.5, 0.3]: both KL divergences in closed
+    form, L1 = 2 TV = 0.8, a(y) = min(1, p(y) / q(y)) = [1, 0.6, 1/3], and the expected committed
+    length averaged over y ~ q: 1 + sum_y q(y) a(y) = 1 + sum min(p, q) = 1.6."""
+    p = np.array([0.6, 0.3, 0.1])
+    q = np.array([0.2, 0.5, 0.3])
+    kl_pq = 0.6 * math.log(3.0) + 0.3 * math.log(0.6) + 0.1 * math.log(1.0 / 3.0)
+    kl_qp = 0.2 * math.log(1.0 / 3.0) + 0.5 * math.log(5.0 / 3.0) + 0.3 * math.log(3.0)
+    E = 0.0
+    for y in range(3):
+        r = O.verify_request(np.log(np.stack([p, p])), np.log(q)[None], [y], O.SamplingParams(1.0), 1, 1, 0)
+        assert abs(r.kl_pq[0] - kl_pq) < 1e-12 and abs(r.kl_qp[0] - kl_qp) < 1e-12
+        assert abs(r.l1[0] - 0.8) < 1e-12
+        assert abs(r.accept_prob[0] - [1.0, 0.6, 1.0 / 3.0][y]) < 1e-12
+        E += q[y] * r.expected_committed
+    assert abs(E - 1.6) < 1e-12
+
+
+def test_expected_committed_is_the_chain_sum():
+    """Two-token rows with y = 0 give a_i = min(1, p_i(0) / q_i(0)) in closed form; E is
+    1 + a1 + a1 a2 + a1 a2 a3.  A token outside [0, V) has a = 0 and ends the chain."""
+    pp, qq = [0.3, 0.9, 0.5, 0.7], [0.6, 0.45, 0.8]
+    tl = np.log(np.array([[x, 1.0 - x] for x in pp]))
+    dl = np.log(np.array([[z, 1.0 - z] for z in qq]))
+    a = [min(1.0, pp[i] / qq[i]) for i in range(3)]
+    r = O.verify_request(tl, dl, [0, 0, 0], O.SamplingParams(1.0), 3, 5, 0)
+    assert np.allclose(r.accept_prob, a, rtol=0, atol=1e-12)
+    assert abs(r.expected_committed - (1 + a[0] + a[0] * a[1] + a[0] * a[1] * a[2])) < 1e-12
+    r = O.verify_request(tl, dl, [0, 7, 0], O.SamplingParams(1.0), 3, 5, 0)
+    assert r.accept_prob[1] == 0.0 and abs(r.expected_committed - (1 + a[0])) < 1e-12
+
+
+def test_kl_invariants_and_support():
+    """Gibbs: KL >= 0 with equality for p = q.  Pinsker: TV <= sqrt(KL / 2).  KL = +inf in each
+    direction whose second distribution misses part of the first one's (filtered) support."""
+    rng = np.random.default_rng(17)
+    for _ in range(20):
+        tl = rng.normal(0, 2, (2, 40))
+        dl = tl[:1] + rng.normal(0, 1, (1, 40))
+        r = O.verify_request(tl, dl, [3], O.SamplingParams(0.8), 1, 1, 0)
+        assert r.kl_pq[0] >= 0 and r.kl_qp[0] >= 0
+        tv = r.l1[0] / 2
+        assert tv <= math.sqrt(r.kl_pq[0] / 2) + 1e-12 and tv <= math.sqrt(r.kl_qp[0] / 2) + 1e-12
+        assert abs(tv - r.tv[0]) < 1e-12
+    same = O.verify_request(np.stack([tl[0], tl[0]]), tl[:1], [3], O.SamplingParams(0.8), 1, 1, 0)
+    assert abs(same.kl_pq[0]) < 1e-12 and abs(same.kl_qp[0]) < 1e-12 and abs(same.l1[0]) < 1e-12
+    # top-k 3 on both rows, the draft's top 3 differing from the target's: p is not covered by q
+    t = np.array([5.0, 4.0, 3.0, 2.0, 1.0, 0.0])
+    d = np.array([5.0, 4.0, 0.0, 3.0, 1.0, 0.0])
+    r = O.verify_request(np.stack([t, t]), d[None], [0], O.SamplingParams(1.0, 3, 1.0), 1, 1, 0)
+    assert r.kl_pq[0] == math.inf and r.kl_qp[0] == math.inf
+    r = O.verify_request(np.stack([t, t]), t[None] + 0.5, [0], O.SamplingParams(1.0, 3, 1.0), 1, 1, 0)
+    assert abs(r.kl_pq[0]) < 1e-12 and abs(r.kl_qp[0]) < 1e-12   # a shifted row: the same distribution
+
+
+def test_extra_signals_token_only_and_greedy():
+    """A token-only draft is one-hot at y: KL(q || p) = -ln p(y), KL(p || q) = +inf, L1 =
+    2 (1 - p(y)), a = p(y).  Greedy: both KL values NaN, a = 1 iff y is the argmax."""
+    p = np.array([0.6, 0.3, 0.1])
+    r = O.verify_request(np.log(np.stack([p, p])), None, [1], O.SamplingParams(1.0), 1, 1, 0)
+    assert abs(r.kl_qp[0] + math.log(0.3)) < 1e-12 and r.kl_pq[0] == math.inf
+    assert abs(r.l1[0] - 1.4) < 1e-12 and abs(r.accept_prob[0] - 0.3) < 1e-12
+    g = O.verify_request(np.log(np.stack([p, p])), None, [0], O.SamplingParams(0.0), 1, 1, 0)
+    assert math.isnan(g.kl_pq[0]) and math.isnan(g.kl_qp[0]) and g.accept_prob[0] == 1.0 and g.l1[0] == 0.0
+    g = O.verify_request(np.log(np.stack([p, p])), None, [2], O.SamplingParams(0.0), 1, 1, 0)
+    assert g.accept_prob[0] == 0.0 and g.l1[0] == 2.0 and g.expected_committed == 1.0
