@@ -390,7 +390,9 @@ def verify_request(target_logits, draft_logits, draft_tokens, sp: SamplingParams
             if not greedy:
                 res.kl_pq[i] = kl_divergence(p, qd)
                 res.kl_qp[i] = kl_divergence(qd, p)
-        if greedy:
+        if not (P[i].finite and (Q is None or Q[i].finite)):
+            res.accept_prob[i] = nan   # a non-finite row has no distribution (R8)
+        elif greedy:
             res.accept_prob[i] = 1.0 if (yv and ys[i] == P[i].argmax) else 0.0
         elif not yv or qd[ys[i]] == 0.0:
             res.accept_prob[i] = 0.0
