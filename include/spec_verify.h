@@ -92,6 +92,20 @@ typedef struct {
   float* draft_max_prob;      /* max_x q_i(x); NaN when greedy                             */
   float* target_entropy_bits; /* H(p_i) in bits, i = 1..gamma_b+1; 0 when greedy           */
   float* target_max_prob;     /* max_x p_i(x); 1 when greedy                               */
+  /* Extra signals (both KL divergences and the L1 distance are the uncertainty features of
+   * the tree-search page's selector; the forward KL is the DLite page's D_KL(p||q) =
+   * sum p log(p/q)).  KL is in nats, +inf when one side puts mass where the other has none,
+   * NaN when greedy; q is one-hot at y_i for a token-only draft (then NaN if y_i is not a
+   * token).  Requesting either KL array routes the call off the single-kernel path.       */
+  float* kl_pq;               /* D_KL(p_i || q_i)                                          */
+  float* kl_qp;               /* D_KL(q_i || p_i)                                          */
+  float* l1;                  /* sum_x |p_i - q_i| = 2 TV                                  */
+  float* accept_prob;         /* a_i = min(1, p_i(y_i) / q_i(y_i)); 0 if y_i is not a token
+                                 or q_i(y_i) = 0; greedy: 1 iff y_i is the target argmax   */
+  float* expected_committed;  /* [B]: 1 + sum_{k=1..gamma_b} prod_{i<=k} a_i, the expected
+                                 tokens committed given the drafts (the tree-search page's
+                                 variance-free block efficiency for one chain); NaN for a
+                                 non-finite request                                        */
 } spec_pos_stats;
 
 /* spec_verify_batch -- verify one speculative round for B ragged requests.

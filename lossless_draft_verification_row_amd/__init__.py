@@ -35,10 +35,13 @@ class SamplingParams(ctypes.Structure):
     _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int), ("top_p", ctypes.c_float)]
 
 
+POS_STATS_FIELDS = ("p_y", "q_y", "one_minus_tv", "draft_entropy_bits", "draft_max_prob",
+                    "target_entropy_bits", "target_max_prob", "kl_pq", "kl_qp", "l1", "accept_prob",
+                    "expected_committed")
+
+
 class PosStats(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in (
-        "p_y", "q_y", "one_minus_tv", "draft_entropy_bits", "draft_max_prob",
-        "target_entropy_bits", "target_max_prob")]
+    _fields_ = [(n, ctypes.c_void_p) for n in POS_STATS_FIELDS]
 
 
 def library_path() -> str:
@@ -155,13 +158,14 @@ def spec_residual_sample_workspace_bytes(R, V, dtype, temperature, top_k=0, top_
 
 def spec_verify_batch(target_logits, draft_logits, draft_tokens, cu_draft, gamma_max, *,
                       temperature=1.0, top_k=0, top_p=1.0, seed=0, step=0, pos_stats=True,
-                      req_stats=True, workspace=None, out=None, stream=None):
+                      req_stats=True, kl=False, workspace=None, out=None, stream=None):
     """Verify one speculative round for B ragged requests (see spec_verify_batch in the header).
 
     target_logits [sum(g_b + 1), V] and draft_logits [sum g_b, V] (or None: token-only draft)
     are bf16 or fp32 CUDA tensors; draft_tokens [sum g_b] and cu_draft [B + 1] are int32 CUDA
     tensors.  Returns a dict of CUDA tensors: tokens [B, gamma_max + 1], num_accepted [B],
-    status [B], and, when requested, the per-position and per-request statistics.
+    status [B], and, when requested, the per-position and per-request statistics (pos_stats:
+    p_y ... target_max_prob, l1, accept_prob, expected_committed [B]; kl: kl_pq, kl_qp).
     """
     lib = load_library()
     dev = target_logits.device
@@ -183,15 +187,17 @@ def spec_verify_batch(target_logits, draft_logits, draft_tokens, cu_draft, gamma
         o["num_accepted"] = torch.empty(B, dtype=torch.int32, device=dev)
         o["status"] = torch.empty(B, dtype=torch.int32, device=dev)
         if pos_stats:
-            for k in ("p_y", "q_y", "one_minus_tv", "draft_entropy_bits", "draft_max_prob"):
+            for k in ("p_y", "q_y", "one_minus_tv", "draft_entropy_bits", "draft_max_prob", "l1", "accept_prob"):
                 o[k] = torch.empty(Rd, dtype=torch.float32, device=dev)
             for k in ("target_entropy_bits", "target_max_prob"):
                 o[k] = torch.empty(Rd + B, dtype=torch.float32, device=dev)
+            o["expected_committed"] = torch.empty(B, dtype=torch.float32, device=dev)
+        if kl:
+            for k in ("kl_pq", "kl_qp"):
+                o[k] = torch.empty(Rd, dtype=torch.float32, device=dev)
         if req_stats:
             o["req_stats"] = torch.empty((B, 4), dtype=torch.float32, device=dev)
-    ps = PosStats(*[_ptr(o.get(k)) for k in (
-        "p_y", "q_y", "one_minus_tv", "draft_entropy_bits", "draft_max_prob",
-        "target_entropy_bits", "target_max_prob")])
+    ps = PosStats(*[_ptr(o.get(k)) for k in POS_STATS_FIELDS])
     need = lib.spec_verify_workspace_bytes(B, V, gamma_max, dt, sp)
     wp, wn = _workspace(need, dev, workspace)
     rc = lib.spec_verify_batch(B, V, gamma_max, dt, tp, tld, dp, dld, _ptr(draft_tokens), _ptr(cu_draft), Rd,

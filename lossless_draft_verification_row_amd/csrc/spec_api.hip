@@ -79,7 +79,8 @@ size_t dense_bytes(int64_t n_slots, int V) {
   const int64_t n_lr = 2 * n_slots;
   const int64_t ns = n_chunks(V);
   return kHeaderBytes + align_up((size_t)(n_lr * ns) * slice_part_bytes()) +
-         align_up((size_t)n_lr * row_stat_bytes()) + 2 * align_up((size_t)(n_slots * ns) * sizeof(double));
+         align_up((size_t)n_lr * row_stat_bytes()) + 2 * align_up((size_t)(n_slots * ns) * sizeof(double)) +
+         align_up((size_t)(n_slots * ns * 4) * sizeof(double));
 }
 
 // Workspace of the fused path for n_teams target rows, after the header.
@@ -308,10 +309,16 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
     f.st.draft_max_prob = pos_stats.draft_max_prob;
     f.st.target_entropy_bits = pos_stats.target_entropy_bits;
     f.st.target_max_prob = pos_stats.target_max_prob;
+    f.st.kl_pq = pos_stats.kl_pq;
+    f.st.kl_qp = pos_stats.kl_qp;
+    f.st.l1 = pos_stats.l1;
+    f.st.accept_prob = pos_stats.accept_prob;
+    f.st.expected_committed = pos_stats.expected_committed;
     const hipError_t e = launch_filter(f, dtc, vec, st, g_prof_start, g_prof_stop);
     return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
   }
-  if (!filtered && fused_ok(B, V, gamma_max)) {
+  const bool want_kl = pos_stats.kl_pq != nullptr || pos_stats.kl_qp != nullptr;
+  if (!filtered && !want_kl && fused_ok(B, V, gamma_max)) {
     FusedArgs f;
     memset(&f, 0, sizeof(f));
     f.tgt = target_logits;
@@ -351,6 +358,11 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
     f.st.draft_max_prob = pos_stats.draft_max_prob;
     f.st.target_entropy_bits = pos_stats.target_entropy_bits;
     f.st.target_max_prob = pos_stats.target_max_prob;
+    f.st.kl_pq = pos_stats.kl_pq;
+    f.st.kl_qp = pos_stats.kl_qp;
+    f.st.l1 = pos_stats.l1;
+    f.st.accept_prob = pos_stats.accept_prob;
+    f.st.expected_committed = pos_stats.expected_committed;
     const hipError_t e = launch_fused(f, dtc, vec, st, g_prof_start, g_prof_stop);
     return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
   }
@@ -370,11 +382,13 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   L.greedy = greedy;
   L.want_argmax = 0;
   L.pair = (!greedy && drf != nullptr) ? 1 : 0;
+  L.want_kl = want_kl ? 1 : 0;
   L.vec = vec;
   L.part = cv.take<SlicePart>((size_t)(2 * n_slots) * ns * slice_part_bytes());
   L.rs = cv.take<RowStat>((size_t)(2 * n_slots) * row_stat_bytes());
   L.smass = cv.take<double>((size_t)n_slots * ns * sizeof(double));
   L.amass = cv.take<double>((size_t)n_slots * ns * sizeof(double));
+  L.kmass = cv.take<double>((size_t)n_slots * ns * 4 * sizeof(double));
   if (filtered) {
     float* thr = cv.take<float>((size_t)(2 * n_slots) * sizeof(float));
     if (launch_threshold(map, dtc, vec, V, 2 * n_slots, sp.top_k, sp.top_p, 1.4426950408889634 / (double)sp.temperature,
@@ -395,6 +409,7 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   a.n_slices = ns;
   a.greedy = greedy;
   a.c = L.c;
+  a.inv_t = greedy ? 0.0 : 1.0 / (double)sp.temperature;
   a.seed = seed;
   a.step = step;
   a.tokens = draft_tokens;
@@ -402,6 +417,7 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   a.part = L.part;
   a.smass = L.smass;
   a.amass = L.amass;
+  a.kmass = L.kmass;
   a.out_tokens = out_tokens;
   a.out_num_accepted = out_num_accepted;
   a.out_req_stats = out_req_stats;
@@ -413,6 +429,11 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   a.st.draft_max_prob = pos_stats.draft_max_prob;
   a.st.target_entropy_bits = pos_stats.target_entropy_bits;
   a.st.target_max_prob = pos_stats.target_max_prob;
+  a.st.kl_pq = pos_stats.kl_pq;
+  a.st.kl_qp = pos_stats.kl_qp;
+  a.st.l1 = pos_stats.l1;
+  a.st.accept_prob = pos_stats.accept_prob;
+  a.st.expected_committed = pos_stats.expected_committed;
   if (launch_finalize(a, L.dt, st) != hipSuccess) return SPEC_ERR_LAUNCH;
   return SPEC_OK;
 }
@@ -468,6 +489,7 @@ int spec_row_stats(int R, int V, spec_dtype dt, const void* logits, int64_t ld, 
   L.rs = cv.take<RowStat>((size_t)(2 * R) * row_stat_bytes());
   L.smass = cv.take<double>((size_t)R * ns * sizeof(double));
   L.amass = cv.take<double>((size_t)R * ns * sizeof(double));
+  L.kmass = cv.take<double>((size_t)R * ns * 4 * sizeof(double));
   if (filter_on(V, sp)) {
     float* thr = cv.take<float>((size_t)(2 * R) * sizeof(float));
     if (launch_threshold(map, L.dt, L.vec, V, 2 * R, sp.top_k, sp.top_p, 1.4426950408889634 / (double)sp.temperature,
@@ -542,6 +564,7 @@ int spec_residual_sample(int R, int V, spec_dtype dt, const void* p_logits, int6
   L.rs = cv.take<RowStat>((size_t)(2 * R) * row_stat_bytes());
   L.smass = cv.take<double>((size_t)R * ns * sizeof(double));
   L.amass = cv.take<double>((size_t)R * ns * sizeof(double));
+  L.kmass = cv.take<double>((size_t)R * ns * 4 * sizeof(double));
   if (filter_on(V, sp)) {
     float* thr = cv.take<float>((size_t)(2 * R) * sizeof(float));
     if (launch_threshold(map, L.dt, L.vec, V, 2 * R, sp.top_k, sp.top_p, 1.4426950408889634 / (double)sp.temperature,

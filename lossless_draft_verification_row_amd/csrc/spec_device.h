@@ -589,4 +589,15 @@ __device__ __forceinline__ float key16_value(int k) {
   return __uint_as_float(b << 16);
 }
 
+// Expected tokens committed given the drafts, 1 + sum_{k=1..g} prod_{i<=k} a_i, from the
+// per-position accept probabilities, in fp64 and position order.
+__device__ __forceinline__ float expected_committed(const double* ap, int g) {
+  double run = 1.0, e = 1.0;
+  for (int i = 0; i < g; ++i) {
+    run *= ap[i];
+    e += run;
+  }
+  return (float)e;
+}
+
 }  // namespace specv

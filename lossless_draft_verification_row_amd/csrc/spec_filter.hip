@@ -669,6 +669,7 @@ struct FinFLds {
   double py[kMaxGamma + 1], qy[kMaxGamma + 1], u0[kMaxGamma];
   int ytok[kMaxGamma];
   float dh[kMaxGamma], dm[kMaxGamma];
+  double ap[kMaxGamma];                                   // accept probability per position
   double chunk[kMaxSlicesFused];
   int pidx[kWaves][kKeepMax], qidx[kWaves][kKeepMax];   // a wave's kept token lists
   double w[kKeepMax];                                     // sampler weights of the chosen row
@@ -802,8 +803,9 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
     if (i < g) {
       const int y = a.tokens[c0 + i];
       const bool yv = y >= 0 && y < a.V;
-      double pyd = 0.0, qyd = 1.0;
-      float py = nan, qy = nan, ovl = nan, dh = nan, dm = nan;
+      double pyd = 0.0, qyd = 1.0, ap = nan;
+      float py = nan, qy = nan, ovl = nan, dh = nan, dm = nan, l1 = nan, klpq = nan, klqp = nan;
+      const bool want_kl = a.st.kl_pq || a.st.kl_qp;
       if (MODE == kFuSample) {
         const int qs = a.n_teams + c0 + i;
         const RowStat2 Q = a.rstat[qs];
@@ -824,12 +826,38 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
           qy = (float)qyd;
         }
         if (okp && okq) {
-          double part = 0.0;
+          // over p's kept set: min(p, q), [p - q]_+ (beta = TV, L1 = 2 beta) and, on request,
+          // p ln(p / q); a token of S_p missing from S_q makes D(p || q) infinite
+          double part = 0.0, beta = 0.0, kl1 = 0.0;
+          int miss = 0;
           for (int j = lane; j < np; j += 64) {
             const int m = find_idx(qix, nq, pix[j]);
-            if (m >= 0) part += fmin(kp[j].p, kq[m].p);
+            const double pv = kp[j].p, qv = m >= 0 ? kq[m].p : 0.0;
+            part += fmin(pv, qv);
+            beta += fmax(pv - qv, 0.0);
+            if (want_kl) {
+              if (m >= 0) kl1 += pv * log(pv / qv);
+              else miss = 1;
+            }
           }
           ovl = (float)wave_sum_dpp_d(part);
+          l1 = (float)(2.0 * wave_sum_dpp_d(beta));
+          ap = (yv && qyd > 0.0) ? fmin(1.0, pyd / qyd) : 0.0;
+          if (want_kl) {
+            kl1 = wave_sum_dpp_d(kl1);
+            miss = wave_or(miss);
+            klpq = miss ? INFINITY : (float)kl1;
+            double kl2 = 0.0;
+            miss = 0;
+            for (int j = lane; j < nq; j += 64) {
+              const int m = find_idx(pix, np, qix[j]);
+              if (m >= 0) kl2 += kq[j].p * log(kq[j].p / kp[m].p);
+              else miss = 1;
+            }
+            kl2 = wave_sum_dpp_d(kl2);
+            miss = wave_or(miss);
+            klqp = miss ? INFINITY : (float)kl2;
+          }
         }
         if (okq) { dh = (float)Q.entropy; dm = (float)Q.max_prob; }
       } else {
@@ -844,6 +872,13 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
         ovl = okp ? (yv ? py : 0.f) : nan;
         dh = yv ? 0.f : nan;
         dm = yv ? 1.f : nan;
+        ap = okp ? (yv ? fmin(1.0, pyd) : 0.0) : nan;
+        if (okp && yv) {
+          // q one-hot at y: D(q || p) = -ln p(y); D(p || q) is finite only for a one-hot p
+          l1 = (float)(2.0 * (1.0 - pyd));
+          klqp = (float)(-log(pyd));
+          klpq = pyd >= 1.0 ? 0.f : INFINITY;
+        }
       }
       if (lane == 0) {
         if (a.st.p_y) a.st.p_y[c0 + i] = py;
@@ -851,6 +886,11 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
         if (a.st.one_minus_tv) a.st.one_minus_tv[c0 + i] = ovl;
         if (a.st.draft_entropy_bits) a.st.draft_entropy_bits[c0 + i] = dh;
         if (a.st.draft_max_prob) a.st.draft_max_prob[c0 + i] = dm;
+        if (a.st.l1) a.st.l1[c0 + i] = l1;
+        if (a.st.accept_prob) a.st.accept_prob[c0 + i] = (float)ap;
+        if (a.st.kl_pq) a.st.kl_pq[c0 + i] = klpq;
+        if (a.st.kl_qp) a.st.kl_qp[c0 + i] = klqp;
+        F.ap[i] = ap;
         F.dh[i] = dh;
         F.dm[i] = dm;
         F.py[i] = pyd;
@@ -894,6 +934,8 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
     F.u[2] = u53(w[3]);
     F.status = status;
     F.x = -1;
+    if (a.st.expected_committed)
+      a.st.expected_committed[b] = F.flags ? nan : expected_committed(F.ap, g);
     if (a.out_req_stats) {
       float rq[4] = {nan, nan, nan, nan};
       if (g > 0) {

@@ -57,6 +57,7 @@ struct FinScratch {
   int ytok[kMaxGamma];
   double gm[kChunk / kGroup];
   float dh[kMaxGamma], dm[kMaxGamma];
+  double ap[kMaxGamma];          // accept probability of every position
   float wsel[kGroup];
   double u[3];
   int flags, status, n_acc, pos, wkind, y, kpick, gpick, xpick;
@@ -393,12 +394,14 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       const int drow = c0 + t;
       const int y = ytok;
       const bool yv = y >= 0 && y < a.V;
-      float py = nan, qy = nan, ovl = nan, dh = nan, dm = nan;
-      double pyd = 0.0, qyd = 1.0;
+      float py = nan, qy = nan, ovl = nan, dh = nan, dm = nan, l1 = nan;
+      double pyd = 0.0, qyd = 1.0, ap = nan;
       if (MODE == kFuGreedy) {
         py = (okp && yv) ? (y == T.amax ? 1.f : 0.f) : nan;
         qy = yv ? 1.f : nan;
         ovl = okp ? (yv ? py : 0.f) : nan;
+        ap = okp ? ((yv && y == T.amax) ? 1.0 : 0.0) : nan;
+        l1 = (okp && yv) ? (y == T.amax ? 0.f : 2.f) : nan;
       } else {
         if (okp && yv) {
           pyd = exp2_split((double)ly_p * cd - (double)T.M[0]) / T.z[0];
@@ -409,13 +412,19 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
           ovl = okp ? (yv ? py : 0.f) : nan;
           dh = yv ? 0.f : nan;
           dm = yv ? 1.f : nan;
+          ap = okp ? (yv ? fmin(1.0, pyd) : 0.0) : nan;
+          l1 = (okp && yv) ? (float)(2.0 * (1.0 - pyd)) : nan;
         } else {
           const bool okq = (T.flags & (kTeamBadQ | kTeamTimeout)) == 0;
           if (okq && yv) {
             qyd = exp2_split((double)ly_q * cd - (double)T.M[1]) / T.z[1];
             qy = (float)qyd;
           }
-          if (okp && okq) ovl = (float)(1.0 - T.beta);
+          if (okp && okq) {
+            ovl = (float)(1.0 - T.beta);
+            l1 = (float)(2.0 * T.beta);
+            ap = (yv && qyd > 0.0) ? fmin(1.0, pyd / qyd) : 0.0;
+          }
           dh = okq ? (float)(log2_split(T.z[1]) - T.w[1] / T.z[1]) : nan;
           dm = okq ? (float)(1.0 / T.z[1]) : nan;
         }
@@ -425,6 +434,9 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       if (a.st.one_minus_tv) a.st.one_minus_tv[drow] = ovl;
       if (a.st.draft_entropy_bits) a.st.draft_entropy_bits[drow] = dh;
       if (a.st.draft_max_prob) a.st.draft_max_prob[drow] = dm;
+      if (a.st.l1) a.st.l1[drow] = l1;
+      if (a.st.accept_prob) a.st.accept_prob[drow] = (float)ap;
+      F.ap[t] = ap;
       F.dh[t] = dh;
       F.dm[t] = dm;
       F.ytok[t] = y;
@@ -463,6 +475,8 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       F.u[2] = F.us[F.pos][2];
       F.status = status;
       F.kpick = -1;
+      if (a.st.expected_committed)
+        a.st.expected_committed[b] = fl ? nan : expected_committed(F.ap, g);
       if (a.out_req_stats) {
         float rq[4] = {nan, nan, nan, nan};
         if (g > 0 && MODE != kFuGreedy) {

@@ -61,10 +61,13 @@ struct DenseLaunch {
   int dt, V, n_slices, n_slots;
   float c;                  // log2(e) / T (0 when greedy)
   int greedy, want_argmax, pair, vec;
+  int want_kl;              // the pair pass also gathers the KL divergences' sums
   SlicePart* part;
   RowStat* rs;
   double* smass;            // [n_slots][n_slices] sum over the slice of [p - q]_+
   double* amass;            // [n_slots][n_slices] sum over the slice of min(p, q)
+  double* kmass;            // [n_slots][n_slices][4] sum p (l_p - l_q), sum q (l_q - l_p), and the
+                            // counts of p > 0 = q, q > 0 = p (the KL divergences' support)
   RowStatsOut rso;
   hipEvent_t ev_start, ev_stop;   // optional: bracket the streaming pass (benchmark timing)
 };
@@ -77,18 +80,25 @@ struct PosStatsOut {
   float* draft_max_prob;
   float* target_entropy_bits;
   float* target_max_prob;
+  float* kl_pq;
+  float* kl_qp;
+  float* l1;
+  float* accept_prob;
+  float* expected_committed;   // [B]
 };
 
 struct FinalizeArgs {
   RowMap map;
   int V, n_slices, greedy;
   float c;
+  double inv_t;             // 1 / T (T > 0)
   uint64_t seed, step;
   const int32_t* tokens;
   const RowStat* rs;
   const SlicePart* part;
   const double* smass;
   const double* amass;
+  const double* kmass;
   int32_t* out_tokens;
   int32_t* out_num_accepted;
   float* out_req_stats;

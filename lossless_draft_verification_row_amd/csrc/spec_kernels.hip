@@ -554,11 +554,15 @@ __global__ __launch_bounds__(kThreads) void k_combine(RowMap m, int n_lr, int n_
 // Residual mass of one slice of one (target, draft) row pair, sum_x [p(x) - q(x)]_+, with
 // p(x) = exp2((l_x - m) c) / z evaluated in fp32 exactly as the finalize pass does; and the
 // slice's overlap sum_x min(p(x), q(x)) (each min exact), so that A = 1 - TV keeps its
-// relative precision when the two distributions barely overlap.
+// relative precision when the two distributions barely overlap.  With want_kl, also the
+// slice's sum p (l_p - l_q) and sum q (l_q - l_p) over the tokens in both supports, and the
+// counts of tokens in one support only (membership decided on the logits: finite and not
+// below the row's filter threshold, so an underflowed probability stays in its support).
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_pair(RowMap m, int V, int n_slices, float c,
                                                     const RowStat* __restrict__ rs,
-                                                    double* __restrict__ smass, double* __restrict__ amass) {
+                                                    double* __restrict__ smass, double* __restrict__ amass,
+                                                    int want_kl, double* __restrict__ kmass) {
   const int slot = blockIdx.x, sl = blockIdx.y;
   const void* prow = resolve_row<DT>(m, 2 * slot);
   const void* qrow = resolve_row<DT>(m, 2 * slot + 1);
@@ -569,6 +573,8 @@ __global__ __launch_bounds__(kThreads) void k_pair(RowMap m, int V, int n_slices
     if (threadIdx.x == 0) {
       smass[(int64_t)slot * n_slices + sl] = 0.0;
       amass[(int64_t)slot * n_slices + sl] = 0.0;
+      if (want_kl)
+        for (int k = 0; k < 4; ++k) kmass[((int64_t)slot * n_slices + sl) * 4 + k] = 0.0;
     }
     return;
   }
@@ -589,6 +595,27 @@ __global__ __launch_bounds__(kThreads) void k_pair(RowMap m, int V, int n_slices
   if (threadIdx.x == 0) {
     smass[(int64_t)slot * n_slices + sl] = tot;
     amass[(int64_t)slot * n_slices + sl] = ov;
+  }
+  if (want_kl) {
+    float kp = 0.f, kq = 0.f;
+    int np_only = 0, nq_only = 0;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const bool inp = lp[j] > -INFINITY && !(lp[j] < P.tau), inq = lq[j] > -INFINITY && !(lq[j] < Q.tau);
+      if (inp && inq) {
+        const float d = lp[j] - lq[j];
+        kp = fmaf(__builtin_amdgcn_exp2f((lp[j] - P.m) * c) * P.inv_z, d, kp);
+        kq = fmaf(__builtin_amdgcn_exp2f((lq[j] - Q.m) * c) * Q.inv_z, -d, kq);
+      }
+      np_only += (inp && !inq) ? 1 : 0;
+      nq_only += (inq && !inp) ? 1 : 0;
+    }
+    const double skp = block_sum_d((double)kp, redd), skq = block_sum_d((double)kq, redd);
+    const double snp = block_sum_d((double)np_only, redd), snq = block_sum_d((double)nq_only, redd);
+    if (threadIdx.x == 0) {
+      double* km = kmass + ((int64_t)slot * n_slices + sl) * 4;
+      km[0] = skp; km[1] = skq; km[2] = snp; km[3] = snq;
+    }
   }
 }
 
@@ -716,6 +743,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
   __shared__ double cmass[kMaxChunks];
   __shared__ int sh_k, sh_wkind, sh_row, sh_y, sh_emit;
   __shared__ double sh_u2, sh_u3;
+  __shared__ double apos[kMaxGamma];
 
   int g, c0;
   const bool ok_req = request_rows(m, b, g, c0);
@@ -753,11 +781,14 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
       const int y = a.tokens[drow];
       const bool yv = y >= 0 && y < a.V;
       const void* prow = row_ptr<DT>(m.tgt, m.tgt_ld, trow);
-      float py = nan, qy = nan, ovl = nan, dh = nan, dm = nan;
+      float py = nan, qy = nan, ovl = nan, dh = nan, dm = nan, l1 = nan, klpq = nan, klqp = nan;
+      double ap = nan;
       if (greedy) {
         py = (okp && yv) ? (y == P.amax ? 1.f : 0.f) : nan;
         qy = yv ? 1.f : nan;
         ovl = okp ? (yv ? py : 0.f) : nan;
+        ap = okp ? ((yv && y == P.amax) ? 1.0 : 0.0) : nan;
+        l1 = (okp && yv) ? (y == P.amax ? 0.f : 2.f) : nan;
       } else if (token_only) {
         const double p = (okp && yv) ? p_of<DT>(prow, y, P, cd) : 0.0;
         py = (okp && yv) ? (float)p : nan;
@@ -765,20 +796,51 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
         ovl = okp ? (yv ? (float)p : 0.f) : nan;
         dh = yv ? 0.f : nan;
         dm = yv ? 1.f : nan;
+        ap = okp ? (yv ? fmin(1.0, p) : 0.0) : nan;
+        if (okp && yv) {
+          // q one-hot at y: D(q || p) = -ln p(y); D(p || q) is finite only for a one-hot p
+          l1 = (float)(2.0 * (1.0 - p));
+          klqp = (float)(-log(p));
+          klpq = p >= 1.0 ? 0.f : INFINITY;
+        }
       } else {
         const RowStat Q = a.rs[2 * (b * G1 + t) + 1];
         const bool okq = Q.flags == 0;
         const void* qrow = row_ptr<DT>(m.drf, m.drf_ld, drow);
-        py = (okp && yv) ? (float)p_of<DT>(prow, y, P, cd) : nan;
-        qy = (okq && yv) ? (float)p_of<DT>(qrow, y, Q, cd) : nan;
+        const double pyd = (okp && yv) ? p_of<DT>(prow, y, P, cd) : 0.0;
+        const double qyd = (okq && yv) ? p_of<DT>(qrow, y, Q, cd) : 0.0;
+        py = (okp && yv) ? (float)pyd : nan;
+        qy = (okq && yv) ? (float)qyd : nan;
         if (okp && okq) {
-          double ov = 0.0;
-          for (int k = 0; k < a.n_slices; ++k) ov += a.amass[(int64_t)(b * G1 + t) * a.n_slices + k];
+          const int64_t s0 = (int64_t)(b * G1 + t) * a.n_slices;
+          double ov = 0.0, beta = 0.0;
+          for (int k = 0; k < a.n_slices; ++k) {
+            ov += a.amass[s0 + k];
+            beta += a.smass[s0 + k];
+          }
           ovl = (float)ov;
+          l1 = (float)(2.0 * beta);
+          ap = (yv && qyd > 0.0) ? fmin(1.0, pyd / qyd) : 0.0;
+          if (a.st.kl_pq || a.st.kl_qp) {
+            // D(p || q) = sum p (l_p - l_q) / T - (LSE_p - LSE_q), LSE = m / T + ln z
+            double skp = 0.0, skq = 0.0, np_only = 0.0, nq_only = 0.0;
+            for (int k = 0; k < a.n_slices; ++k) {
+              const double* km = a.kmass + (s0 + k) * 4;
+              skp += km[0]; skq += km[1]; np_only += km[2]; nq_only += km[3];
+            }
+            const double dlse = ((double)P.m - (double)Q.m) * a.inv_t + log(P.z) - log(Q.z);
+            klpq = np_only > 0.0 ? INFINITY : (float)(skp * a.inv_t - dlse);
+            klqp = nq_only > 0.0 ? INFINITY : (float)(skq * a.inv_t + dlse);
+          }
         }
         dh = okq ? Q.h_bits : nan;
         dm = okq ? Q.maxp : nan;
       }
+      if (a.st.l1) a.st.l1[drow] = l1;
+      if (a.st.accept_prob) a.st.accept_prob[drow] = (float)ap;
+      if (a.st.kl_pq) a.st.kl_pq[drow] = klpq;
+      if (a.st.kl_qp) a.st.kl_qp[drow] = klqp;
+      apos[t] = ap;
       if (a.st.p_y) a.st.p_y[drow] = py;
       if (a.st.q_y) a.st.q_y[drow] = qy;
       if (a.st.one_minus_tv) a.st.one_minus_tv[drow] = ovl;
@@ -789,6 +851,8 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
     }
   }
   __syncthreads();
+  if (t == 0 && a.st.expected_committed)
+    a.st.expected_committed[b] = (flags & kStNonfinite) ? nan : expected_committed(apos, g);
   if (t == 0 && a.out_req_stats) {
     float r[4] = {nan, nan, nan, nan};
     if (g > 0 && !greedy) {
@@ -1018,8 +1082,12 @@ static hipError_t launch_dense_t(const DenseLaunch& L, hipStream_t st) {
   if (e != hipSuccess) return e;
   if (L.pair) {
     const dim3 g3(L.n_slots, L.n_slices);
-    if (L.vec) hipLaunchKernelGGL((k_pair<DT, true>), g3, blk, 0, st, m, L.V, L.n_slices, L.c, L.rs, L.smass, L.amass);
-    else hipLaunchKernelGGL((k_pair<DT, false>), g3, blk, 0, st, m, L.V, L.n_slices, L.c, L.rs, L.smass, L.amass);
+    if (L.vec)
+      hipLaunchKernelGGL((k_pair<DT, true>), g3, blk, 0, st, m, L.V, L.n_slices, L.c, L.rs, L.smass, L.amass, L.want_kl,
+                         L.kmass);
+    else
+      hipLaunchKernelGGL((k_pair<DT, false>), g3, blk, 0, st, m, L.V, L.n_slices, L.c, L.rs, L.smass, L.amass, L.want_kl,
+                         L.kmass);
     e = hipGetLastError();
   }
   return e;

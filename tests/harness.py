@@ -70,15 +70,16 @@ def close(gpu, ref):
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     nan_ok = np.array_equal(np.isnan(gpu), np.isnan(ref))
-    m = ~np.isnan(ref)
+    inf_ok = np.array_equal(np.isinf(gpu), np.isinf(ref)) and np.array_equal(gpu[np.isinf(ref)], ref[np.isinf(ref)])
+    m = np.isfinite(ref)
     err_ok = bool(np.all(np.abs(gpu[m] - ref[m]) <= REL_TOL * np.abs(ref[m]) + ABS_TOL))
-    return nan_ok and err_ok
+    return nan_ok and inf_ok and err_ok
 
 
 def max_rel(gpu, ref):
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    m = ~np.isnan(ref) & ~np.isnan(gpu)
+    m = np.isfinite(ref) & np.isfinite(gpu)
     if not m.any():
         return 0.0
     return float(np.max(np.abs(gpu[m] - ref[m]) / (np.abs(ref[m]) + 1e-30)))
@@ -147,6 +148,11 @@ def compare_requests(gpu, refs, inp: W.Inputs, report: Report, stats=True):
             ("draft_max_prob", gpu.get("draft_max_prob"), ref.draft_max_prob, c0, g),
             ("target_entropy_bits", gpu.get("target_entropy_bits"), ref.target_entropy_bits, c0 + b, g + 1),
             ("target_max_prob", gpu.get("target_max_prob"), ref.target_max_prob, c0 + b, g + 1),
+            ("l1", gpu.get("l1"), ref.l1, c0, g),
+            ("accept_prob", gpu.get("accept_prob"), ref.accept_prob, c0, g),
+            ("kl_pq", gpu.get("kl_pq"), ref.kl_pq, c0, g),
+            ("kl_qp", gpu.get("kl_qp"), ref.kl_qp, c0, g),
+            ("expected_committed", gpu.get("expected_committed"), np.array([ref.expected_committed]), b, 1),
         ]
         for name, garr, rarr, lo, cnt in pairs:
             if garr is None:

@@ -65,19 +65,19 @@ def filtered_inputs(B, V, gammas, sp, dtype="bf16", sigma=3.0, tau=1.0, seed=11,
     return W.Inputs(wl, gammas, cu, target, None if token_only else draft, toks, seed)
 
 
-def run_gpu(inp, sp, seed, step, gamma_max=None):
+def run_gpu(inp, sp, seed, step, gamma_max=None, kl=False):
     d = H.to_device(inp)
     G = int(inp.gammas.max()) if gamma_max is None else gamma_max
     res = L.spec_verify_batch(d["target"], d["draft"], d["tokens"], d["cu"], G, temperature=sp.temperature,
-                              top_k=sp.top_k, top_p=sp.top_p, seed=seed, step=step)
+                              top_k=sp.top_k, top_p=sp.top_p, seed=seed, step=step, kl=kl)
     torch.cuda.synchronize()
     return H.gpu_to_numpy(res)
 
 
-def check(inp, sp, seed=321, step=4, requests=None):
+def check(inp, sp, seed=321, step=4, requests=None, kl=False):
     note(f"case B={len(inp.gammas)} V={inp.target.shape[1]} dtype={inp.wl.dtype} T={sp.temperature} "
          f"k={sp.top_k} p={sp.top_p} token_only={inp.draft is None}")
-    gpu = run_gpu(inp, sp, seed, step)
+    gpu = run_gpu(inp, sp, seed, step, kl=kl)
     reqs = range(len(inp.gammas)) if requests is None else requests
     refs = H.oracle_requests(inp, sp, seed, step, reqs)
     rep = H.compare_requests(gpu, refs, inp, H.Report())
@@ -479,3 +479,19 @@ def test_dense_filtered_row_stats_wide(dtype, k, p, T):
     assert np.array_equal(g["kept_count"][ok], ref["kept_count"][ok])
     for key in ("log_z", "entropy_bits", "max_prob"):
         assert H.close(g[key][ok], ref[key][ok]), (key, H.max_rel(g[key][ok], ref[key][ok]))
+
+
+
+@pytest.mark.parametrize("k,p", [(50, 0.9), (0, 0.9), (600, 1.0)])
+def test_filtered_kl_and_signals(k, p):
+    """KL (infinite where one filtered support misses the other's tokens), L1, accept
+    probabilities and the expected committed length on both filtered paths."""
+    sp = O.SamplingParams(0.7, k, p)
+    inp = filtered_inputs(4, V_SMALL, [5, 2, 0, 7], sp, seed=500 + k)
+    gpu, refs, _ = check(inp, sp, kl=True)
+
+
+def test_filtered_kl_token_only():
+    sp = O.SamplingParams(0.7, 30, 0.9)
+    inp = filtered_inputs(3, V_SMALL, [4, 1, 6], sp, seed=61, token_only=True)
+    check(inp, sp, kl=True)

@@ -80,20 +80,21 @@ class path_env:
             os.environ["SPEC_VERIFY_NO_FUSED"] = self.old
 
 
-def run_gpu(inp, sp, seed, step, gamma_max=None, path="fused"):
+def run_gpu(inp, sp, seed, step, gamma_max=None, path="fused", kl=False):
     d = H.to_device(inp)
     G = int(inp.gammas.max()) if gamma_max is None else gamma_max
     with path_env(path):
         res = L.spec_verify_batch(d["target"], d["draft"], d["tokens"], d["cu"], G,
-                                  temperature=sp.temperature, top_k=sp.top_k, top_p=sp.top_p, seed=seed, step=step)
+                                  temperature=sp.temperature, top_k=sp.top_k, top_p=sp.top_p, seed=seed, step=step,
+                                  kl=kl)
         torch.cuda.synchronize()
     return H.gpu_to_numpy(res)
 
 
-def check(inp, sp, seed=1234, step=5, requests=None, gamma_max=None, path="fused"):
+def check(inp, sp, seed=1234, step=5, requests=None, gamma_max=None, path="fused", kl=False):
     note(f"case B={len(inp.gammas)} V={inp.target.shape[1]} dtype={inp.wl.dtype} T={sp.temperature} "
          f"k={sp.top_k} p={sp.top_p} token_only={inp.draft is None} path={path}")
-    gpu = run_gpu(inp, sp, seed, step, gamma_max, path)
+    gpu = run_gpu(inp, sp, seed, step, gamma_max, path, kl)
     reqs = range(len(inp.gammas)) if requests is None else requests
     refs = H.oracle_requests(inp, sp, seed, step, reqs)
     rep = H.compare_requests(gpu, refs, inp, H.Report())
@@ -408,3 +409,34 @@ def test_full_size_workload_sampled(cfg):
     gpu, refs, rep = check(inp, sp, seed=1000 + cfg, step=0, requests=reqs,
                            gamma_max=int(inp.gammas.max()))
     assert (gpu["status"] == 0).all()
+
+
+# ----------------------------------------------------------------------------- extra signals
+
+
+@pytest.mark.parametrize("dtype,V,T", [("bf16", 3 * 4096 + 72, 1.0), ("f32", 2 * 4096 + 5, 0.7)])
+def test_kl_and_signals(dtype, V, T):
+    """Both KL divergences (nats), L1, accept probabilities and the expected committed length
+    against the oracle; a KL request runs the multi-kernel path."""
+    inp = custom_inputs(5, V, [3, 0, 7, 1, 4], T=T, seed=V + 1, dtype=dtype)
+    gpu, refs, _ = check(inp, O.SamplingParams(T), kl=True)
+    assert np.isfinite(gpu["kl_pq"]).all() and (gpu["kl_pq"] > 0).all()
+
+
+def test_kl_token_only_and_greedy():
+    inp = custom_inputs(4, 5000, [2, 5, 0, 3], T=1.0, seed=9, token_only=True)
+    gpu, _, _ = check(inp, O.SamplingParams(1.0), kl=True)
+    assert np.isinf(gpu["kl_pq"]).all()
+    inp = custom_inputs(3, 5000, [2, 5, 3], T=0.0, seed=10, token_only=True)
+    gpu, _, _ = check(inp, O.SamplingParams(0.0), kl=True)
+    assert np.isnan(gpu["kl_pq"]).all() and np.isnan(gpu["kl_qp"]).all()
+
+
+def test_kl_draft_equals_target_is_zero():
+    inp = custom_inputs(2, 4096 + 100, [4, 3], T=1.0, seed=12)
+    for b in range(2):
+        c0, g = int(inp.cu_draft[b]), int(inp.gammas[b])
+        inp.draft[c0:c0 + g] = inp.target[c0 + b:c0 + b + g]
+    gpu, _, _ = check(inp, O.SamplingParams(1.0), kl=True)
+    assert (gpu["kl_pq"] == 0).all() and (gpu["kl_qp"] == 0).all()
+    assert np.allclose(gpu["expected_committed"], 1 + inp.gammas)
