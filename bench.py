@@ -153,8 +153,8 @@ def filtered_draft_tokens(inp, seed=77):
 
 
 def load_traffic(kernel):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel source."""
+    """The committed rocprofv3 counter summary of the kernel (HBM bytes and VALU instructions
+    per launch), if it was taken on the current kernel source."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
     if not os.path.exists(path):
         return None
@@ -168,7 +168,7 @@ def load_traffic(kernel):
         h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
         if rec.get("kernel_source_sha") != h:
             return None
-        return rec.get("bytes_per_launch")
+        return rec
     except Exception:
         return None
 
@@ -266,7 +266,13 @@ def main():
         kernel_key, kernel_name = "k_fused", "k_fused (streaming kernel: every needed logit read once, both phases)"
     else:
         kernel_key, kernel_name = "k_pass1", "k_pass1 (streaming pass over every needed logit)"
-    traffic = load_traffic(kernel_key)
+    counters = load_traffic(kernel_key) or {}
+    traffic = counters.get("bytes_per_launch")
+    # VALU issue fraction: the kernel's VALU instructions (SQ_INSTS_VALU per launch, from the
+    # same counter summary) at 4 cycles per wave64 instruction on a 16-lane SIMD, over the
+    # SIMD cycles of the measured launch (1024 SIMDs at 2.4 GHz)
+    valu = counters.get("valu_insts_per_launch")
+    valu_frac = valu * 4.0 / (kern_avg_s * 2.4e9 * 1024) if valu else None
     line = {
         "metric": "verified draft positions/sec (and streaming-kernel HBM GB/s vs peak), 1 MI355X",
         "value": positions / sec_per_step,
@@ -293,7 +299,7 @@ def main():
                    "status_nonzero_requests": int((st != 0).sum())},
         "roofline": {"bound": "hbm", "kernel": kernel_name,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "kernel_ms_avg": kern_avg_s * 1e3},
+                     "traffic": traffic, "kernel_ms_avg": kern_avg_s * 1e3, "valu_issue_frac": valu_frac},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
