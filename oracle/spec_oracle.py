@@ -61,6 +61,15 @@ Readings taken where the pages leave a step open (plainest reading the rest supp
       efficiency (a sum over reachable nodes of products of branch transition probabilities)
       for a single chain under the standard rule.
 
+  R11 Gamma selection ([SKV] "接受率预测与 gamma 选择", acceptance prediction and gamma
+      selection): context x = [H_bar, c_bar, H_max, c_min, comp] (the request statistics above
+      plus the caller's compression feature); a regressor f(x, gamma) predicts the acceptance
+      rate; the expected tokens of a step are f(x, gamma) * gamma + 1, and gamma* is the
+      argmax over {2, 4, 6, 8}.  The pages name an MLP with 16 hidden units but not its
+      layout: read as input [x, gamma] (6 values), one hidden layer of 16 ReLU units and a
+      linear output, weights supplied by the caller (the trained ones are not available).
+      Ties go to the smallest gamma; a NaN feature gives gamma* = -1.
+
 Every function states which of the above it follows.  The decision margins recorded next
 to each result (distance of u from the accept ratio, of u*M from the sampler prefix sums,
 of the top-p cumulative mass from top_p) let a comparison excuse a mismatch that sits
@@ -541,3 +550,34 @@ def residual_sample(p_logits, q_logits, sp: SamplingParams, uniforms=None, seed=
         u = uniforms[r] if uniforms is not None else residual_uniforms(seed, step, r)
         tok[r], margin[r] = sample_three_level(w, *u)
     return {"token": tok, "mass": mass, "status": status, "margin": margin}
+
+
+# ----------------------------------------------------------------------------- gamma selection
+
+
+GAMMAS = (2, 4, 6, 8)
+
+
+def select_gamma(req_stats, comp, w1, b1, w2, b2, gammas=GAMMAS):
+    """gamma* = argmax_gamma f(x, gamma) * gamma + 1 with f an MLP-16 over [x, gamma].  [SKV]
+    acceptance prediction and gamma selection, reading R11.
+
+    req_stats: [4] = H_bar, c_bar, H_max, c_min; comp: the compression feature; w1 [16, 6],
+    b1 [16], w2 [16], b2 scalar.  Returns (gamma*, expected tokens per gamma [4], margin) where
+    the margin is the gap between the best and the runner-up expectation (ties excused below
+    rounding distance).
+    """
+    x = np.asarray(list(req_stats) + [comp], dtype=np.float64)
+    w1 = np.asarray(w1, dtype=np.float64)
+    b1 = np.asarray(b1, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    if np.isnan(x).any():
+        return -1, np.full(len(gammas), np.nan), math.inf
+    E = np.empty(len(gammas))
+    for g, gamma in enumerate(gammas):
+        h = np.maximum(w1 @ np.append(x, float(gamma)) + b1, 0.0)
+        E[g] = (float(w2 @ h) + float(b2)) * gamma + 1.0
+    best = int(np.argmax(E))   # first maximum: the smallest gamma on ties
+    rest = np.delete(E, best)
+    margin = float(E[best] - rest.max()) if len(rest) else math.inf
+    return gammas[best], E, margin

@@ -604,3 +604,48 @@ def test_extra_signals_token_only_and_greedy():
     assert math.isnan(g.kl_pq[0]) and math.isnan(g.kl_qp[0]) and g.accept_prob[0] == 1.0 and g.l1[0] == 0.0
     g = O.verify_request(np.log(np.stack([p, p])), None, [2], O.SamplingParams(0.0), 1, 1, 0)
     assert g.accept_prob[0] == 0.0 and g.l1[0] == 2.0 and g.expected_committed == 1.0
+
+
+# ----------------------------------------------------------------------------- gamma selection (R11)
+
+
+def _gamma_head(alpha, beta):
+    """Weights making f(x, gamma) = alpha - beta * gamma exactly (one ReLU unit passes gamma
+    through, another carries a constant 1; the rest are dead), so E(gamma) = (alpha - beta
+    gamma) gamma + 1 peaks at gamma = alpha / (2 beta)."""
+    w1 = np.zeros((16, 6))
+    b1 = np.zeros(16)
+    w1[0, 5] = 1.0            # h0 = relu(gamma) = gamma
+    b1[1] = 1.0               # h1 = 1
+    b1[2:] = -1.0             # dead units
+    w2 = np.zeros(16)
+    w2[0] = -beta
+    w2[1] = alpha
+    return w1, b1, w2, 0.0
+
+
+def test_gamma_selection_closed_form():
+    """E(gamma) = (alpha - beta gamma) gamma + 1: the argmax over {2, 4, 6, 8} follows the
+    parabola's vertex alpha / (2 beta); ties go to the smaller gamma; NaN features give -1."""
+    stats = [3.0, 0.4, 5.0, 0.1]
+    for alpha, beta, want in [(0.8, 0.1, 4), (0.9, 0.05, 8), (0.5, 0.2, 2), (1.2, 0.1, 6)]:
+        g, E, margin = O.select_gamma(stats, 1.0, *_gamma_head(alpha, beta))
+        assert g == want, (alpha, beta, E)
+        for k, gamma in enumerate(O.GAMMAS):
+            assert abs(E[k] - ((alpha - beta * gamma) * gamma + 1.0)) < 1e-12
+    # vertex at 5 with binary-exact weights: E(4) = E(6) = 4 exactly -> the smaller gamma
+    g, E, margin = O.select_gamma(stats, 0.0, *_gamma_head(1.25, 0.125))
+    assert g == 4 and margin == 0.0
+    g, E, _ = O.select_gamma([float("nan"), 0.4, 5.0, 0.1], 0.0, *_gamma_head(0.8, 0.1))
+    assert g == -1 and np.isnan(E).all()
+
+
+def test_gamma_selection_uses_the_features():
+    """A unit reading c_min only: f = w * relu(c_min) and E = f gamma + 1 grows with gamma when
+    f > 0 (gamma* = 8) and shrinks when f < 0 (gamma* = 2)."""
+    w1 = np.zeros((16, 6)); w1[0, 3] = 1.0
+    b1 = np.zeros(16)
+    for sign, want in [(1.0, 8), (-1.0, 2)]:
+        w2 = np.zeros(16); w2[0] = sign
+        g, E, _ = O.select_gamma([3.0, 0.4, 5.0, 0.25], 1.0, w1, b1, w2, 0.0)
+        assert g == want and abs(E[0] - (sign * 0.25 * 2 + 1.0)) < 1e-12
