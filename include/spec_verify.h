@@ -181,6 +181,31 @@ int spec_residual_sample(int R, int V, spec_dtype dt,
 
 size_t spec_residual_sample_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling_params sp);
 
+/* Weights of the draft-length predictor: the SpecKV page's acceptance-rate regressor
+ * f(x, gamma), an MLP with 16 hidden units, read as h = relu(w1 [x, gamma] + b1),
+ * f = w2 . h + b2 with x = [H_bar, c_bar, H_max, c_min, comp].  Device pointers, fp32;
+ * w1 is [16][6] row-major, b1 and w2 are [16]. */
+typedef struct {
+  const float* w1;
+  const float* b1;
+  const float* w2;
+  float b2;
+} spec_gamma_mlp;
+
+/* spec_select_gamma -- each request's next draft length (SpecKV page, acceptance prediction
+ * and gamma selection): gamma* = argmax over gamma in {2, 4, 6, 8} of f(x, gamma) gamma + 1,
+ * the expected tokens of a step; ties go to the smaller gamma.
+ *  req_stats    [B, 4] fp32: H_bar, c_bar, H_max, c_min, as spec_verify_batch writes them.
+ *  comp         [B] fp32: the caller's compression feature of each request, or NULL for 0.
+ *  out_gamma    [B] int32: gamma*, or -1 when a feature is NaN (no draft tokens, greedy,
+ *               non-finite rows).
+ *  out_expected optional [B, 4] fp32: f(x, gamma) gamma + 1 for gamma = 2, 4, 6, 8.
+ * fp32 arithmetic, one wave per request, no workspace; stream-ordered after the
+ * spec_verify_batch call whose req_stats it reads.  Returns SPEC_OK, SPEC_ERR_INVALID (a
+ * required pointer is NULL, B < 0) or SPEC_ERR_LAUNCH. */
+int spec_select_gamma(int B, const float* req_stats, const float* comp, spec_gamma_mlp w, int32_t* out_gamma,
+                      float* out_expected, void* hip_stream);
+
 /* Benchmark instrumentation.  With two hipEvent_t handles set, every later spec_verify_batch
  * call records `start_event` on its stream right before its dominant streaming kernel (the
  * pass that reads every needed logit row) and `stop_event` right after it, so a benchmark can

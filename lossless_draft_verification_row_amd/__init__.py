@@ -44,6 +44,10 @@ class PosStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in POS_STATS_FIELDS]
 
 
+class GammaMLP(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p), ("b2", ctypes.c_float)]
+
+
 def library_path() -> str:
     return os.environ.get("SPEC_VERIFY_LIB", os.path.join(_HERE, "libspecverify.so"))
 
@@ -73,6 +77,8 @@ def load_library():
                                          vp, vp, vp, vp, sz, vp]
     lib.spec_residual_sample_workspace_bytes.restype = sz
     lib.spec_residual_sample_workspace_bytes.argtypes = [i32, i32, i32, SamplingParams]
+    lib.spec_select_gamma.restype = i32
+    lib.spec_select_gamma.argtypes = [i32, vp, vp, GammaMLP, vp, vp, vp]
     lib.spec_set_spin_limit.restype = i32
     lib.spec_set_spin_limit.argtypes = [ctypes.c_uint]
     lib.spec_set_profile_events.restype = i32
@@ -258,4 +264,29 @@ def spec_residual_sample(p_logits, q_logits=None, *, temperature=1.0, top_k=0, t
                                   int(step) & (2**64 - 1), _ptr(o["token"]), _ptr(o["mass"]), _ptr(o["status"]),
                                   wp, wn, _stream(stream))
     _check(rc, "spec_residual_sample")
+    return o
+
+
+def spec_select_gamma(req_stats, w1, b1, w2, b2, comp=None, stream=None):
+    """Each request's next draft length, gamma* = argmax over {2, 4, 6, 8} of
+    f(x, gamma) gamma + 1 (see spec_select_gamma in the header).  req_stats [B, 4] (as
+    spec_verify_batch returns it), w1 [16, 6], b1 [16], w2 [16] and comp [B] (or None) are
+    float32 CUDA tensors; b2 is a float.  Returns {"gamma": [B] int32, "expected": [B, 4]}."""
+    lib = load_library()
+    for t, n, shape in ((req_stats, "req_stats", None), (w1, "w1", (16, 6)), (b1, "b1", (16,)), (w2, "w2", (16,))):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous float32 CUDA tensor")
+        if shape is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{n} must have shape {shape}")
+    if req_stats.dim() != 2 or req_stats.shape[1] != 4:
+        raise ValueError("req_stats must be [B, 4]")
+    B = req_stats.shape[0]
+    if comp is not None and (comp.dtype != torch.float32 or not comp.is_cuda or comp.numel() != B):
+        raise ValueError("comp must be a float32 CUDA tensor of B values")
+    dev = req_stats.device
+    o = {"gamma": torch.empty(B, dtype=torch.int32, device=dev),
+         "expected": torch.empty((B, 4), dtype=torch.float32, device=dev)}
+    rc = lib.spec_select_gamma(B, _ptr(req_stats), _ptr(comp), GammaMLP(_ptr(w1), _ptr(b1), _ptr(w2), float(b2)),
+                               _ptr(o["gamma"]), _ptr(o["expected"]), _stream(stream))
+    _check(rc, "spec_select_gamma")
     return o

@@ -596,4 +596,14 @@ int spec_residual_sample(int R, int V, spec_dtype dt, const void* p_logits, int6
   return SPEC_OK;
 }
 
+int spec_select_gamma(int B, const float* req_stats, const float* comp, spec_gamma_mlp w, int32_t* out_gamma,
+                      float* out_expected, void* hip_stream) {
+  if (B < 0) return SPEC_ERR_INVALID;
+  if (B == 0) return SPEC_OK;
+  if (!req_stats || !w.w1 || !w.b1 || !w.w2 || !out_gamma) return SPEC_ERR_INVALID;
+  const hipError_t e = launch_select_gamma(B, req_stats, comp, w.w1, w.b1, w.w2, w.b2, out_gamma, out_expected,
+                                           (hipStream_t)hip_stream);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -213,6 +213,8 @@ hipError_t launch_dense(const DenseLaunch& L, hipStream_t st);
 hipError_t launch_threshold(const RowMap& m, int dt, int vec, int V, int n_lr, int k, float top_p, double c,
                             float* thr, hipStream_t st);
 hipError_t launch_finalize(const FinalizeArgs& a, int dt, hipStream_t st);
+hipError_t launch_select_gamma(int B, const float* req_stats, const float* comp, const float* w1, const float* b1,
+                               const float* w2, float b2, int32_t* out_gamma, float* out_expected, hipStream_t st);
 hipError_t launch_residual_finalize(const ResidualArgs& a, int dt, hipStream_t st);
 
 size_t slice_part_bytes();

@@ -1057,6 +1057,63 @@ __global__ __launch_bounds__(kThreads) void k_residual_finalize(ResidualArgs a) 
   if (t == 0) a.out_token[r] = x;
 }
 
+// ---------------------------------------------------------------- draft-length selection
+
+// One wave per request: lane 16 g + j evaluates hidden unit j of f(x, gamma_g), gamma_g =
+// 2 (g + 1), and a DPP reduction over each row of 16 lanes forms f (SpecKV page, acceptance
+// prediction and gamma selection: gamma* = argmax f(x, gamma) gamma + 1 over {2, 4, 6, 8}).
+__global__ __launch_bounds__(kThreads) void k_select_gamma(int B, const float* __restrict__ req_stats,
+                                                            const float* __restrict__ comp,
+                                                            const float* __restrict__ w1,
+                                                            const float* __restrict__ b1,
+                                                            const float* __restrict__ w2, float b2,
+                                                            int32_t* __restrict__ out_gamma,
+                                                            float* __restrict__ out_expected) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (b >= B) return;   // whole waves
+  const int g = lane >> 4, j = lane & 15;
+  const float gamma = 2.f * (float)(g + 1);
+  float x[6];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) x[k] = req_stats[(int64_t)b * 4 + k];
+  x[4] = comp ? comp[b] : 0.f;
+  x[5] = gamma;
+  bool nanx = false;
+  float h = b1[j];
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    nanx |= !(x[k] == x[k]);
+    h = fmaf(w1[j * 6 + k], x[k], h);
+  }
+  float c = w2[j] * fmaxf(h, 0.f);
+  // sum over the row's 16 lanes; every lane of the row ends with the total
+  c += SPEC_DPP_F(0.f, c, 0xb1, 0xf);    // quad_perm [1,0,3,2]
+  c += SPEC_DPP_F(0.f, c, 0x4e, 0xf);    // quad_perm [2,3,0,1]
+  c += SPEC_DPP_F(0.f, c, 0x124, 0xf);   // row_ror:4
+  c += SPEC_DPP_F(0.f, c, 0x128, 0xf);   // row_ror:8
+  const float e = fmaf(c + b2, gamma, 1.f);
+  float E[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) E[q] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), 16 * q));
+  if (lane == 0) {
+    int best = 0;
+#pragma unroll
+    for (int q = 1; q < 4; ++q)
+      if (E[q] > E[best]) best = q;
+    out_gamma[b] = nanx ? -1 : 2 * (best + 1);
+  }
+  if (out_expected && j == 0) out_expected[(int64_t)b * 4 + g] = nanx ? __int_as_float(0x7fc00000) : e;
+}
+
+hipError_t launch_select_gamma(int B, const float* req_stats, const float* comp, const float* w1, const float* b1,
+                               const float* w2, float b2, int32_t* out_gamma, float* out_expected, hipStream_t st) {
+  const int blocks = (B + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(k_select_gamma, dim3(blocks), dim3(kThreads), 0, st, B, req_stats, comp, w1, b1, w2, b2,
+                     out_gamma, out_expected);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launchers
 
 template <int DT>

@@ -84,3 +84,13 @@ def test_argument_checks_without_gpu():
     # B = 0 is a no-op
     assert lib.spec_verify_batch(0, 100, 3, 1, None, 100, None, 0, None, None, 0, sp, 0, 0,
                                  None, None, ps, None, None, None, 0, None) == 0
+
+
+def test_select_gamma_argument_checks_without_gpu():
+    lib = L.load_library()
+    w = L.GammaMLP(16, 16, 16, 0.0)
+    assert lib.spec_select_gamma(-1, 16, None, w, 16, None, None) == -1
+    assert lib.spec_select_gamma(0, None, None, w, None, None, None) == 0      # B = 0: no-op
+    assert lib.spec_select_gamma(3, None, None, w, 16, None, None) == -1      # no req_stats
+    assert lib.spec_select_gamma(3, 16, None, L.GammaMLP(16, None, 16, 0.0), 16, None, None) == -1
+    assert lib.spec_select_gamma(3, 16, None, w, None, None, None) == -1      # no out_gamma

@@ -440,3 +440,49 @@ def test_kl_draft_equals_target_is_zero():
     gpu, _, _ = check(inp, O.SamplingParams(1.0), kl=True)
     assert (gpu["kl_pq"] == 0).all() and (gpu["kl_qp"] == 0).all()
     assert np.allclose(gpu["expected_committed"], 1 + inp.gammas)
+
+
+# ----------------------------------------------------------------------------- draft-length selection
+
+
+def test_select_gamma_random_weights():
+    """Random MLP-16 weights against the oracle's fp64 MLP on the request statistics of a
+    verification call (plus made-up rows and a NaN row): gamma* exact unless the oracle's best
+    and runner-up expectations lie within fp32 rounding, expectations to an fp32 dot-product
+    rounding bound (relative error is no measure here: E(2) can cancel to near zero)."""
+    inp = custom_inputs(6, 5000, [3, 0, 7, 1, 4, 2], T=0.8, seed=21)
+    gpu = run_gpu(inp, O.SamplingParams(0.8), 5, 6)
+    rng = np.random.default_rng(99)
+    extra = np.array([[4.0, 0.3, 6.0, 0.05], [1.0, 0.8, 1.5, 0.6], [9.5, 0.05, 11.0, 0.01]], dtype=np.float32)
+    stats = np.concatenate([gpu["req_stats"], extra]).astype(np.float32)
+    B = stats.shape[0]
+    comp = rng.choice([0.0, 1.0, 2.0], size=B).astype(np.float32)
+    for trial in range(5):
+        w1 = (rng.standard_normal((16, 6)) * 0.5).astype(np.float32)
+        b1 = (rng.standard_normal(16) * 0.5).astype(np.float32)
+        w2 = (rng.standard_normal(16) * 0.3).astype(np.float32)
+        b2 = float(np.float32(rng.standard_normal() * 0.2))
+        dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+        res = L.spec_select_gamma(dv(stats), dv(w1), dv(b1), dv(w2), b2, comp=dv(comp))
+        torch.cuda.synchronize()
+        g = res["gamma"].cpu().numpy()
+        E = res["expected"].cpu().numpy()
+        for b in range(B):
+            want, Eref, margin = O.select_gamma(stats[b].astype(np.float64), float(comp[b]), w1, b1, w2, b2)
+            if want == -1:
+                assert g[b] == -1 and np.isnan(E[b]).all(), (b, g[b])
+                continue
+            # fp32 evaluation: a dot product of n terms is off by at most about n * 2^-24 times
+            # the sum of its terms' magnitudes; 32 * 2^-24 covers the 7-term hidden sums and the
+            # 16-term output sum, scaled by the magnitudes that feed each E(gamma).
+            x = np.array([*stats[b], comp[b], 0.0])
+            tol = []
+            for gam in O.GAMMAS:
+                x[5] = gam
+                hid = np.abs(w1.astype(np.float64)) @ np.abs(x) + np.abs(b1)
+                tol.append(32 * 2.0 ** -24 * (gam * (np.abs(w2) @ hid + abs(b2)) + 1))
+            tol = np.array(tol)
+            assert np.all(np.abs(E[b] - Eref) <= tol), (b, E[b], Eref, tol)
+            if margin > 2 * tol.max():
+                assert g[b] == want, (trial, b, g[b], want, Eref)
+    assert (gpu["req_stats"][1] != gpu["req_stats"][1]).all()   # request 1 has no draft: NaN row
