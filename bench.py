@@ -152,6 +152,11 @@ def filtered_draft_tokens(inp, seed=77):
     return toks
 
 
+# per-position outputs every timed call writes (the target's own entropy and max-prob are
+# optional outputs and not requested)
+OUTPUTS_PER_POSITION = ("p_y", "q_y", "one_minus_tv", "draft_entropy_bits", "draft_max_prob")
+
+
 def load_traffic(kernel):
     """The committed rocprofv3 counter summary of the kernel (HBM bytes and VALU instructions
     per launch), if it was taken on the current kernel source."""
@@ -220,7 +225,15 @@ def main():
     ws_bytes = L.spec_verify_workspace_bytes(B, wl.V, G, L.SPEC_BF16 if wl.dtype == "bf16" else L.SPEC_F32,
                                              wl.temperature, wl.top_k, wl.top_p)
     ws = L.new_workspace(ws_bytes, dev)
-    out = {}
+    # the outputs of a verification round: tokens, counts, status, the per-position draft
+    # entropy, draft max-prob, 1 - TV, p(y) and q(y), and the per-request signal aggregates
+    Rd = int(inp.cu_draft[-1])
+    out = {"tokens": torch.empty((B, G + 1), dtype=torch.int32, device=dev),
+           "num_accepted": torch.empty(B, dtype=torch.int32, device=dev),
+           "status": torch.empty(B, dtype=torch.int32, device=dev),
+           "req_stats": torch.empty((B, 4), dtype=torch.float32, device=dev)}
+    for k in OUTPUTS_PER_POSITION:
+        out[k] = torch.empty(Rd, dtype=torch.float32, device=dev)
 
     def step(k):
         return L.spec_verify_batch(tgts[k % copies], drfs[k % copies], toks, cu, G, temperature=wl.temperature,
@@ -294,6 +307,7 @@ def main():
                     ", draft tokens = argmax of target + noise)")),
         "config": {"workload": wl.name, "B": B, "gamma": G, "V": wl.V, "positions_per_step": positions,
                    "temperature": wl.temperature, "top_k": wl.top_k, "top_p": wl.top_p,
+                   "outputs": ["tokens", "num_accepted", "status", "req_stats", *OUTPUTS_PER_POSITION],
                    "algorithmic_bytes_per_step": alg_bytes, "input_copies_rotated": copies,
                    "end_to_end_GBps": alg_bytes / sec_per_step / 1e9,
                    "status_nonzero_requests": int((st != 0).sum())},

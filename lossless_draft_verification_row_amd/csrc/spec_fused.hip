@@ -645,6 +645,10 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   "v_" op "_f32_dpp %1, %1, %1 " ctrl "\n\t"                \
   "v_" op "_f32_dpp %2, %2, %2 " ctrl "\n\t"                \
   "v_" op "_f32_dpp %3, %3, %3 " ctrl "\n\t"
+#define SPEC_DPP3(op, ctrl)                                \
+  "v_" op "_f32_dpp %0, %0, %0 " ctrl "\n\t"                \
+  "v_" op "_f32_dpp %1, %1, %1 " ctrl "\n\t"                \
+  "v_" op "_f32_dpp %2, %2, %2 " ctrl "\n\t"
 #define SPEC_DPP2(op, ctrl)                                \
   "v_" op "_f32_dpp %0, %0, %0 " ctrl "\n\t"                \
   "v_" op "_f32_dpp %1, %1, %1 " ctrl "\n\t"                \
@@ -663,6 +667,10 @@ __device__ __forceinline__ float lane63(float v) {
 __device__ __forceinline__ void dpp_sum4(float& a, float& b, float& c, float& d) {
   asm volatile("s_nop 1\n\t" SPEC_DPP_STEPS(SPEC_DPP4, "add") : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
   a = lane63(a); b = lane63(b); c = lane63(c); d = lane63(d);
+}
+__device__ __forceinline__ void dpp_sum3(float& a, float& b, float& c) {
+  asm volatile("s_nop 1\n\t" SPEC_DPP_STEPS(SPEC_DPP3, "add") : "+v"(a), "+v"(b), "+v"(c));
+  a = lane63(a); b = lane63(b); c = lane63(c);
 }
 __device__ __forceinline__ void dpp_sum2(float& a, float& b) {
   asm volatile("s_nop 1\n\t" SPEC_DPP_STEPS(SPEC_DPP2, "add") : "+v"(a), "+v"(b));
@@ -690,23 +698,31 @@ __device__ __forceinline__ float raw_elem(const RawSlice<DT>& r, int j) {
 }
 // Max of two slices given as raw words.  bf16: on the packed 16-bit patterns read as signed
 // integers, non-negative values order like their patterns and negative ones (sign bit set) in
-// reverse, so per half the largest non-negative pattern, or failing any the negative pattern
-// of least magnitude (the integer minimum), is the largest value; two packed integer ops per
-// word, and no word is ever read as a float (a -inf high half would make it a signalling NaN).
-// A NaN pattern is ignored unless a half holds nothing else; a row holding one is reported
-// from its sums either way.  fp32: the plain max (quiet NaN ignored).
+// reverse, so per half the largest non-negative pattern (the integer maximum, one packed op per
+// two words), or failing any the negative pattern of least magnitude (the integer minimum,
+// taken only by a wave in which some lane holds no non-negative value in a half), is the
+// largest value.  No word is ever read as a float (a -inf high half would make it a signalling
+// NaN).  A NaN pattern is ignored unless a half holds nothing else; a row holding one is
+// reported from its sums either way.  fp32: the plain max (quiet NaN ignored).
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 template <int DT>
 __device__ __forceinline__ float max_raw2(const RawSlice<DT>& r0, const RawSlice<DT>& r1) {
   if constexpr (DT == kDtBF16) {
-    s16x2 mx = {(short)-32768, (short)-32768}, mn = {(short)32767, (short)32767};
+    s16x2 mx = __builtin_elementwise_max(__builtin_bit_cast(s16x2, r0.w[0]), __builtin_bit_cast(s16x2, r1.w[0]));
 #pragma unroll
-    for (int k = 0; k < RawSlice<DT>::kWords; ++k) {
-      const s16x2 w0 = __builtin_bit_cast(s16x2, r0.w[k]), w1 = __builtin_bit_cast(s16x2, r1.w[k]);
-      mx = __builtin_elementwise_max(mx, __builtin_elementwise_max(w0, w1));
-      mn = __builtin_elementwise_min(mn, __builtin_elementwise_min(w0, w1));
+    for (int k = 1; k < RawSlice<DT>::kWords; ++k)
+      mx = __builtin_elementwise_max(mx, __builtin_elementwise_max(__builtin_bit_cast(s16x2, r0.w[k]),
+                                                                   __builtin_bit_cast(s16x2, r1.w[k])));
+    uint32_t h0 = (uint16_t)mx.x, h1 = (uint16_t)mx.y;
+    if (__builtin_amdgcn_ballot_w64(mx.x < 0 || mx.y < 0)) {
+      s16x2 mn = __builtin_elementwise_min(__builtin_bit_cast(s16x2, r0.w[0]), __builtin_bit_cast(s16x2, r1.w[0]));
+#pragma unroll
+      for (int k = 1; k < RawSlice<DT>::kWords; ++k)
+        mn = __builtin_elementwise_min(mn, __builtin_elementwise_min(__builtin_bit_cast(s16x2, r0.w[k]),
+                                                                     __builtin_bit_cast(s16x2, r1.w[k])));
+      if (mx.x < 0) h0 = (uint16_t)mn.x;
+      if (mx.y < 0) h1 = (uint16_t)mn.y;
     }
-    const uint32_t h0 = (uint16_t)(mx.x >= 0 ? mx.x : mn.x), h1 = (uint16_t)(mx.y >= 0 ? mx.y : mn.y);
     return fmaxf(__uint_as_float(h0 << 16), __uint_as_float(h1 << 16));
   } else {
     float m = -INFINITY;
@@ -726,25 +742,24 @@ __device__ __forceinline__ void mask_tail_raw(int V, int base, RawSlice<DT>& r) 
     else r.w[j] = 0xff800000u;
   }
 }
-// e = 2^(l c - ref) of a slice given as raw words, with s = sum e and w = sum e (l c - ref).  A
-// masked logit (-inf) gives e = 0 and a NaN product in w; such a thread recomputes w from its
+// e = 2^(l c - ref) of a slice given as raw words, with s = sum e and (ENT) w = sum e (l c - ref).
+// A masked logit (-inf) gives e = 0 and a NaN product in w; such a thread recomputes w from its
 // e-values, using log2(e) for l c - ref.  Words are consumed in groups of two (four logits) so
 // that the raw words die as the e-values appear.
-template <int DT>
+template <int DT, bool ENT>
 __device__ __forceinline__ void exp_raw(const RawSlice<DT>& r, float (&e)[kPerThread], float c, float ref, float& s,
                                         float& w) {
-  s = 0.f;
   w = 0.f;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
     const float tt = fmaf(raw_elem<DT>(r, j), c, -ref);
     const float ej = __builtin_amdgcn_exp2f(tt);
-    s += ej;
-    w = fmaf(ej, tt, w);
+    s = j == 0 ? ej : s + ej;
+    if (ENT) w = j == 0 ? ej * tt : fmaf(ej, tt, w);
     e[j] = ej;
     if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
   }
-  if (!(w == w)) {
+  if (ENT && !(w == w)) {
     w = 0.f;
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j)
@@ -785,11 +800,10 @@ __device__ __forceinline__ float max_slice(const float (&v)[kPerThread], float m
 }
 
 // exp_raw for a slice whose e-values go straight to LDS, four at a time (stash[k][thread]).
-template <int DT>
+template <int DT, bool ENT>
 __device__ __forceinline__ void exp_raw_stash(const RawSlice<DT>& r, float4 (*stash)[kThreads], float c, float ref,
                                               float& s, float& w) {
   const int t = threadIdx.x;
-  s = 0.f;
   w = 0.f;
 #pragma unroll
   for (int k = 0; k < kPerThread / 4; ++k) {
@@ -798,13 +812,13 @@ __device__ __forceinline__ void exp_raw_stash(const RawSlice<DT>& r, float4 (*st
     for (int q = 0; q < 4; ++q) {
       const float tt = fmaf(raw_elem<DT>(r, 4 * k + q), c, -ref);
       e4[q] = __builtin_amdgcn_exp2f(tt);
-      s += e4[q];
-      w = fmaf(e4[q], tt, w);
+      s = (k == 0 && q == 0) ? e4[q] : s + e4[q];
+      if (ENT) w = (k == 0 && q == 0) ? e4[q] * tt : fmaf(e4[q], tt, w);
     }
     stash[k][t] = make_float4(e4[0], e4[1], e4[2], e4[3]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (!(w == w)) {
+  if (ENT && !(w == w)) {
     w = 0.f;
 #pragma unroll
     for (int k = 0; k < kPerThread / 4; ++k) {
@@ -819,6 +833,7 @@ __device__ __forceinline__ void exp_raw_stash(const RawSlice<DT>& r, float4 (*st
 
 struct FusedLds {
   float4 stash[kPerThread / 4][kThreads];   // a paired ticket's target e-values of slice 1
+  float qtail[3][kThreads];   // and the last three of its draft e-values of slice 1
   float wp[2][kWaves][4];   // [row][wave] {ref, sum e over slice 0, over slice 1, sum e t}
   float tn[5];              // the team's normalisers {M_p, M_q, 1 / Z_p, 1 / Z_q, Z_q / Z_p}
   int tst;                  // team status: 0 ok, 1 non-finite row, 2 wait gave up
@@ -981,22 +996,27 @@ __device__ __forceinline__ float residual_slice(const ResidualScale& R, const fl
 // One workgroup per ticket: slices 2u and 2u + 1 of one target row (the second one absent at an
 // odd end), with the same slices of its draft row when the position pairs them.  Workgroup i
 // runs on XCD i mod 8 (the dispatcher deals workgroups round-robin over the XCDs), and the
-// tickets of team r go to consecutive workgroups of XCD r mod 8.  Phase 1 publishes one record
-// per row and slice, then (paired tickets) an arrival flag; a paired ticket then waits for its
-// team's flags, reads the team's records and forms its residual masses from e-values kept in
-// registers (one slice of the target's in LDS, which keeps the workgroup at 64 VGPRs).  A
-// member waits only for members dispatched just before or after it on the same XCD; every
-// wait is bounded.
-template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
+// tickets of the team in dispatch place ti go to consecutive workgroups of XCD ti mod 8.
+// Phase 1 publishes one record per row and slice, then (paired tickets) an arrival flag; a
+// paired ticket then waits for its team's flags, reads the team's records and forms its
+// residual masses from e-values kept in registers (one slice of the target's and three of the
+// draft's per thread in LDS).  A member waits only for members dispatched just before or
+// after it on the same XCD; every wait is bounded.
+// Eight waves per SIMD for aligned bf16 rows (64 VGPRs: three of a thread's draft e-values
+// wait in LDS); other layouts keep the compiler's choice.
+constexpr int fused_min_waves(int dt, bool vec) { return dt == kDtBF16 && vec ? 8 : 1; }
+
+template <int DT, bool VEC, int MODE, bool TENT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_min_waves(DT, VEC)))) void k_fused(
+    FusedArgs a) {
   __shared__ FusedLds L;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int n_s = a.n_s, n_u = (n_s + 1) >> 1;
   const int xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
   const int tl = jb / n_u;
   const int u = jb - tl * n_u;
-  const int r = tl * 8 + xcd;
-  if (r >= a.n_teams) return;
+  const int ti = tl * 8 + xcd;   // the team's place in dispatch order
+  if (ti >= a.n_teams) return;
   const int s0 = 2 * u;
   const bool has1 = s0 + 1 < n_s;
   const uint32_t tag = a.tag;
@@ -1006,57 +1026,76 @@ __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
   const int base = s0 * kChunk;
   const bool tail = base + 2 * kChunk > a.V;   // the row's last ticket
   RawSlice<DT> rp[2], rq[2];
-  if (VEC) {
+  int r = ti;   // target row
+  bool pair = false;
+  int drow = -1;
+  if (MODE == kFuSample) {
+    // Dispatch order: every paired position first (draft row d = ti, target row d + b for its
+    // request b), then each request's bonus row (ti = n_draft_rows + b, target row
+    // cu[b + 1] + b).  Bonus rows have no draft row and no team wait, so the kernel's last
+    // workgroups are short ones that keep the memory busy while the paired teams before them
+    // finish.  The loads go out at once for the guess b = d / G (exact when every request has
+    // G draft tokens); scalar loads of cu then settle the request (a binary search when the
+    // guess is wrong) and a wrong target row is loaded again.  An invalid offset array (the
+    // finalize kernel reports it) can only give rows that are range-checked here.
+    const int G1 = max(a.G, 1);
+    const bool slot_pair = ti < a.n_draft_rows;
+    const int bg = slot_pair ? min(ti / G1, a.B - 1) : ti - a.n_draft_rows;
+    const int rg = min(slot_pair ? ti + bg : (bg + 1) * a.G + bg, a.n_teams - 1);
+    if (VEC) {
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc(row_ptr<DT>(a.tgt, a.tgt_ld, rg), a.V * kEsz);
+      load_raw_buf<DT>(rs, base, rp[0]);
+      load_raw_buf<DT>(rs, base + kChunk, rp[1]);
+      const __amdgpu_buffer_rsrc_t rd =
+          row_rsrc(slot_pair ? row_ptr<DT>(a.drf, a.drf_ld, ti) : a.tgt, slot_pair ? a.V * kEsz : 0);
+      load_raw_buf<DT>(rd, base, rq[0]);
+      load_raw_buf<DT>(rd, base + kChunk, rq[1]);
+    }
+    bool valid;
+    if (slot_pair) {
+      // the request of draft row d: the largest b < B with cu[b] <= d
+      int b = bg, c0, c1;
+      sload2_i32(a.cu + b, c0, c1);
+      if (!(c0 <= ti && (b == a.B - 1 || c1 > ti))) {
+        b = 0;
+        int hi = a.B;
+        while (hi - b > 1) {
+          const int mid = (b + hi) >> 1;
+          if (sload_i32(a.cu + mid) <= ti) b = mid;
+          else hi = mid;
+        }
+        sload2_i32(a.cu + b, c0, c1);
+      }
+      r = ti + b;
+      drow = ti;
+      pair = c0 <= ti && ti < c1;
+      valid = pair && r < a.n_teams;
+    } else {
+      r = sload_i32(a.cu + bg + 1) + bg;
+      valid = r >= 0 && r < a.n_teams;
+    }
+    if (!valid) return;
+    if (VEC) {
+      if (r != rg) {
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V * kEsz);
+        load_raw_buf<DT>(rs, base, rp[0]);
+        load_raw_buf<DT>(rs, base + kChunk, rp[1]);
+      }
+    } else {
+      load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, base, rp[0]);
+      load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, base + kChunk, rp[1]);
+      if (pair) {
+        load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base, rq[0]);
+        load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base + kChunk, rq[1]);
+      }
+    }
+  } else if (VEC) {
     const __amdgpu_buffer_rsrc_t rs = row_rsrc(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V * kEsz);
     load_raw_buf<DT>(rs, base, rp[0]);
     load_raw_buf<DT>(rs, base + kChunk, rp[1]);
   } else {
     load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, base, rp[0]);
     load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, base + kChunk, rp[1]);
-  }
-  bool pair = false;
-  int drow = -1;
-  if (MODE == kFuSample) {
-    // request of target row r: the largest b < B with cu[b] + b <= r (cu[b] + b grows
-    // strictly with b in a valid offset array).  The draft loads go out at once for the guess
-    // b = r / (G + 1), exact when every request has G draft tokens; one scalar load then
-    // checks it, and a wrong guess falls back to a binary search through the scalar cache and
-    // loads again.  An invalid array (the finalize kernel reports it) can only give a draft
-    // row that is range-checked here.
-    const int lo0 = min(r / (a.G + 1), a.B - 1);
-    const bool guess_pair = r - lo0 < a.n_draft_rows && r % (a.G + 1) < a.G;
-    if (VEC) {
-      const __amdgpu_buffer_rsrc_t rs =
-          row_rsrc(guess_pair ? row_ptr<DT>(a.drf, a.drf_ld, r - lo0) : a.tgt, guess_pair ? a.V * kEsz : 0);
-      load_raw_buf<DT>(rs, base, rq[0]);
-      load_raw_buf<DT>(rs, base + kChunk, rq[1]);
-    }
-    int lo = lo0, c0, c1;
-    sload2_i32(a.cu + lo, c0, c1);
-    if (!(c0 + lo <= r && (lo == a.B - 1 || c1 + lo + 1 > r))) {
-      lo = 0;
-      int hi = a.B;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (sload_i32(a.cu + mid) + mid <= r) lo = mid;
-        else hi = mid;
-      }
-      sload2_i32(a.cu + lo, c0, c1);
-    }
-    const int i = r - c0 - lo;
-    drow = r - lo;
-    pair = i >= 0 && i < c1 - c0 && drow >= 0 && drow < a.n_draft_rows;
-    if (VEC) {
-      if (pair != guess_pair || (pair && lo != lo0)) {
-        const __amdgpu_buffer_rsrc_t rs =
-            row_rsrc(pair ? row_ptr<DT>(a.drf, a.drf_ld, drow) : a.tgt, pair ? a.V * kEsz : 0);
-        load_raw_buf<DT>(rs, base, rq[0]);
-        load_raw_buf<DT>(rs, base + kChunk, rq[1]);
-      }
-    } else if (pair) {
-      load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base, rq[0]);
-      load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base + kChunk, rq[1]);
-    }
   }
   if (MODE == kFuGreedy) {
     float vp[2][kPerThread];
@@ -1127,11 +1166,23 @@ __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
   float refp = mp > -INFINITY ? mp * c : 0.f;
   float ep[2][kPerThread];
   float sp0, sp1, wp0, wp1;
-  exp_raw<DT>(rp[0], ep[0], c, refp, sp0, wp0);
-  // slice 1: the e-values of a paired ticket go to LDS as they are formed
-  if (pair) exp_raw_stash<DT>(rp[1], L.stash, c, refp, sp1, wp1);
-  else exp_raw<DT>(rp[1], ep[1], c, refp, sp1, wp1);
+  // the target's entropy numerator only when its entropy is asked for (TENT); slice 1's
+  // e-values of a paired ticket go to LDS as they are formed
+  exp_raw<DT, TENT>(rp[0], ep[0], c, refp, sp0, wp0);
+  if (pair) exp_raw_stash<DT, TENT>(rp[1], L.stash, c, refp, sp1, wp1);
+  else exp_raw<DT, TENT>(rp[1], ep[1], c, refp, sp1, wp1);
   if (!(mp > -INFINITY)) refp = -INFINITY;
+  // the target's partials are reduced before the draft row is unpacked, so that they hold no
+  // registers there
+  float wpe = wp0 + wp1;
+  if (TENT) dpp_sum3(sp0, sp1, wpe);
+  else dpp_sum2(sp0, sp1);
+  if (lane == 0) {
+    L.wp[0][wave][0] = refp;
+    L.wp[0][wave][1] = sp0;
+    L.wp[0][wave][2] = sp1;
+    L.wp[0][wave][3] = wpe;
+  }
   float sq0 = 0.f, sq1 = 0.f, wq = 0.f, refq = -INFINITY;
   float eq[2][kPerThread];
   if (pair) {
@@ -1145,23 +1196,19 @@ __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
     dpp_max2(mq, mq2);
     refq = mq > -INFINITY ? mq * c : 0.f;
     float wq0, wq1;
-    exp_raw<DT>(rq[0], eq[0], c, refq, sq0, wq0);
-    exp_raw<DT>(rq[1], eq[1], c, refq, sq1, wq1);
+    exp_raw<DT, true>(rq[0], eq[0], c, refq, sq0, wq0);
+    exp_raw<DT, true>(rq[1], eq[1], c, refq, sq1, wq1);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) L.qtail[k][t] = eq[1][kPerThread - 3 + k];
     wq = wq0 + wq1;
     if (!(mq > -INFINITY)) refq = -INFINITY;
-  }
-  float wpe = wp0 + wp1;
-  dpp_sum4(sp0, sp1, sq0, sq1);
-  dpp_sum2(wpe, wq);
-  if (lane == 0) {
-    L.wp[0][wave][0] = refp;
-    L.wp[0][wave][1] = sp0;
-    L.wp[0][wave][2] = sp1;
-    L.wp[0][wave][3] = wpe;
-    L.wp[1][wave][0] = refq;
-    L.wp[1][wave][1] = sq0;
-    L.wp[1][wave][2] = sq1;
-    L.wp[1][wave][3] = wq;
+    dpp_sum3(sq0, sq1, wq);
+    if (lane == 0) {
+      L.wp[1][wave][0] = refq;
+      L.wp[1][wave][1] = sq0;
+      L.wp[1][wave][2] = sq1;
+      L.wp[1][wave][3] = wq;
+    }
   }
   __syncthreads();
   if (wave == kWaves - 1) {
@@ -1199,6 +1246,8 @@ __global__ __launch_bounds__(kThreads) void k_fused(FusedArgs a) {
       const float4 v4 = L.stash[k][t];
       ep1[4 * k] = v4.x; ep1[4 * k + 1] = v4.y; ep1[4 * k + 2] = v4.z; ep1[4 * k + 3] = v4.w;
     }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) eq[1][kPerThread - 3 + k] = L.qtail[k][t];
     m1 = residual_slice(R, ep1, eq[1]);
   }
   dpp_sum2(m0, m1);
@@ -1228,7 +1277,10 @@ static hipError_t launch_fused_t(FusedArgs a, hipStream_t st, hipEvent_t ev0, hi
     fprintf(stderr, "[specverify] fused grid %lld tickets %d slices %d mode %d\n", grid, a.n_tickets, a.n_s, a.mode);
   // optional events bracket the streaming kernel alone (benchmark timing)
   if (ev0 && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_fused<DT, VEC, MODE>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+  if (MODE != kFuGreedy && a.want_t_ent)
+    hipLaunchKernelGGL((k_fused<DT, VEC, MODE, true>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_fused<DT, VEC, MODE, false>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
