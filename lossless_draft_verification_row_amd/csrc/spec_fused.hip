@@ -649,6 +649,9 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   "v_" op "_f32_dpp %0, %0, %0 " ctrl "\n\t"                \
   "v_" op "_f32_dpp %1, %1, %1 " ctrl "\n\t"                \
   "v_" op "_f32_dpp %2, %2, %2 " ctrl "\n\t"
+#define SPEC_DPP1(op, ctrl)                                \
+  "v_" op "_f32_dpp %0, %0, %0 " ctrl "\n\t"                \
+  "s_nop 1\n\t"
 #define SPEC_DPP2(op, ctrl)                                \
   "v_" op "_f32_dpp %0, %0, %0 " ctrl "\n\t"                \
   "v_" op "_f32_dpp %1, %1, %1 " ctrl "\n\t"                \
@@ -675,6 +678,10 @@ __device__ __forceinline__ void dpp_sum3(float& a, float& b, float& c) {
 __device__ __forceinline__ void dpp_sum2(float& a, float& b) {
   asm volatile("s_nop 1\n\t" SPEC_DPP_STEPS(SPEC_DPP2, "add") : "+v"(a), "+v"(b));
   a = lane63(a); b = lane63(b);
+}
+__device__ __forceinline__ void dpp_max1(float& a) {
+  asm volatile("s_nop 1\n\t" SPEC_DPP_STEPS(SPEC_DPP1, "max") : "+v"(a));
+  a = lane63(a);
 }
 __device__ __forceinline__ void dpp_max2(float& a, float& b) {
   asm volatile("s_nop 1\n\t" SPEC_DPP_STEPS(SPEC_DPP2, "max") : "+v"(a), "+v"(b));
@@ -713,17 +720,20 @@ __device__ __forceinline__ float max_raw2(const RawSlice<DT>& r0, const RawSlice
     for (int k = 1; k < RawSlice<DT>::kWords; ++k)
       mx = __builtin_elementwise_max(mx, __builtin_elementwise_max(__builtin_bit_cast(s16x2, r0.w[k]),
                                                                    __builtin_bit_cast(s16x2, r1.w[k])));
-    uint32_t h0 = (uint16_t)mx.x, h1 = (uint16_t)mx.y;
-    if (__builtin_amdgcn_ballot_w64(mx.x < 0 || mx.y < 0)) {
+    uint32_t mw = __builtin_bit_cast(uint32_t, mx);
+    if (__builtin_amdgcn_ballot_w64((mw & 0x80008000u) != 0u)) {
       s16x2 mn = __builtin_elementwise_min(__builtin_bit_cast(s16x2, r0.w[0]), __builtin_bit_cast(s16x2, r1.w[0]));
 #pragma unroll
       for (int k = 1; k < RawSlice<DT>::kWords; ++k)
         mn = __builtin_elementwise_min(mn, __builtin_elementwise_min(__builtin_bit_cast(s16x2, r0.w[k]),
                                                                      __builtin_bit_cast(s16x2, r1.w[k])));
-      if (mx.x < 0) h0 = (uint16_t)mn.x;
-      if (mx.y < 0) h1 = (uint16_t)mn.y;
+      const uint32_t nw = __builtin_bit_cast(uint32_t, mn);
+      if (mw & 0x8000u) mw = (mw & 0xffff0000u) | (nw & 0xffffu);
+      if (mw & 0x80000000u) mw = (mw & 0xffffu) | (nw & 0xffff0000u);
     }
-    return fmaxf(__uint_as_float(h0 << 16), __uint_as_float(h1 << 16));
+    // both halves are quiet values or NaN patterns read from memory, never signalling
+    // through arithmetic: the plain two-input maximum needs no canonicalising
+    return __builtin_elementwise_maximum(__uint_as_float(mw << 16), __uint_as_float(mw & 0xffff0000u));
   } else {
     float m = -INFINITY;
 #pragma unroll
@@ -1161,8 +1171,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_
     mask_tail_raw<DT>(a.V, base + kChunk, rp[1]);
   }
   float mp = max_raw2<DT>(rp[0], rp[1]);
-  float mp2 = mp;
-  dpp_max2(mp, mp2);
+  dpp_max1(mp);
   float refp = mp > -INFINITY ? mp * c : 0.f;
   float ep[2][kPerThread];
   float sp0, sp1, wp0, wp1;
@@ -1192,8 +1201,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_
       mask_tail_raw<DT>(a.V, base + kChunk, rq[1]);
     }
     float mq = max_raw2<DT>(rq[0], rq[1]);
-    float mq2 = mq;
-    dpp_max2(mq, mq2);
+    dpp_max1(mq);
     refq = mq > -INFINITY ? mq * c : 0.f;
     float wq0, wq1;
     exp_raw<DT, true>(rq[0], eq[0], c, refq, sq0, wq0);
