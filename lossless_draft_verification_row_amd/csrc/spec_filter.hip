@@ -1022,28 +1022,28 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
 hipError_t launch_filter(const FilterArgs& a, int dt, int vec, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const long long g1 = (long long)a.n_teams * a.n_s;
   if (g1 < 1 || g1 > 0x7fffffffll || a.B < 1) return hipErrorInvalidConfiguration;
-  if (ev0 && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
+  // optional events bracket the streaming kernel alone (benchmark timing)
   const bool paired = a.mode == kFuSample;
+  const dim3 g((unsigned)g1), b(kThreads);
   if (dt == kDtBF16) {
     if (paired) {
-      if (vec) hipLaunchKernelGGL((k_filt_slices<kDtBF16, true, true>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
-      else hipLaunchKernelGGL((k_filt_slices<kDtBF16, false, true>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
+      if (vec) launch_timed(k_filt_slices<kDtBF16, true, true>, g, b, st, ev0, ev1, a);
+      else launch_timed(k_filt_slices<kDtBF16, false, true>, g, b, st, ev0, ev1, a);
     } else {
-      if (vec) hipLaunchKernelGGL((k_filt_slices<kDtBF16, true, false>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
-      else hipLaunchKernelGGL((k_filt_slices<kDtBF16, false, false>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
+      if (vec) launch_timed(k_filt_slices<kDtBF16, true, false>, g, b, st, ev0, ev1, a);
+      else launch_timed(k_filt_slices<kDtBF16, false, false>, g, b, st, ev0, ev1, a);
     }
   } else {
     if (paired) {
-      if (vec) hipLaunchKernelGGL((k_filt_slices<kDtF32, true, true>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
-      else hipLaunchKernelGGL((k_filt_slices<kDtF32, false, true>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
+      if (vec) launch_timed(k_filt_slices<kDtF32, true, true>, g, b, st, ev0, ev1, a);
+      else launch_timed(k_filt_slices<kDtF32, false, true>, g, b, st, ev0, ev1, a);
     } else {
-      if (vec) hipLaunchKernelGGL((k_filt_slices<kDtF32, true, false>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
-      else hipLaunchKernelGGL((k_filt_slices<kDtF32, false, false>), dim3((unsigned)g1), dim3(kThreads), 0, st, a);
+      if (vec) launch_timed(k_filt_slices<kDtF32, true, false>, g, b, st, ev0, ev1, a);
+      else launch_timed(k_filt_slices<kDtF32, false, false>, g, b, st, ev0, ev1, a);
     }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
   if (dt == kDtBF16) hipLaunchKernelGGL((k_filt_rows<kDtBF16>), dim3(a.n_slots), dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL((k_filt_rows<kDtF32>), dim3(a.n_slots), dim3(kThreads), 0, st, a);
   e = hipGetLastError();

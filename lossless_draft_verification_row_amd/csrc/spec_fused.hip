@@ -1284,14 +1284,12 @@ static hipError_t launch_fused_t(FusedArgs a, hipStream_t st, hipEvent_t ev0, hi
   if (getenv("SPEC_VERIFY_DEBUG"))
     fprintf(stderr, "[specverify] fused grid %lld tickets %d slices %d mode %d\n", grid, a.n_tickets, a.n_s, a.mode);
   // optional events bracket the streaming kernel alone (benchmark timing)
-  if (ev0 && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
   if (MODE != kFuGreedy && a.want_t_ent)
-    hipLaunchKernelGGL((k_fused<DT, VEC, MODE, true>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    launch_timed(k_fused<DT, VEC, MODE, true>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
   else
-    hipLaunchKernelGGL((k_fused<DT, VEC, MODE, false>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    launch_timed(k_fused<DT, VEC, MODE, false>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_fused_finalize<DT, VEC, MODE>), dim3(a.B), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }

@@ -1,6 +1,7 @@
 // spec_internal.h -- launch descriptors shared by the C-ABI layer and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -145,6 +146,15 @@ struct FusedArgs {
 };
 
 hipError_t launch_fused(const FusedArgs& a, int dt, int vec, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+
+// Launch a kernel; with both events given they are recorded by the dispatch itself around the
+// kernel (start and end of its execution), so that their interval holds no launch gap.
+template <typename K, typename... Args>
+inline void launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1,
+                         Args... args) {
+  if (ev0 && ev1) hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev0, ev1, 0, args...);
+  else hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
 
 // ---------------------------------------------------------------- filtered (top-k / top-p) path
 

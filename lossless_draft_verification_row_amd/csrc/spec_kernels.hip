@@ -1122,17 +1122,19 @@ static hipError_t launch_dense_t(const DenseLaunch& L, hipStream_t st) {
   const RowMap& m = L.map;
   const int n_lr = 2 * L.n_slots;
   const dim3 g1(n_lr, L.n_slices);
-  if (L.ev_start && hipEventRecord(L.ev_start, st) != hipSuccess) return hipErrorInvalidValue;
+  // optional events bracket the streaming pass alone (benchmark timing)
+  const hipEvent_t e0 = L.ev_start, e1 = L.ev_stop;
   if (L.greedy) {
-    if (L.vec) hipLaunchKernelGGL((k_pass1<DT, true, kModeArgmax>), g1, blk, 0, st, m, L.V, L.n_slices, L.c, 1, L.part);
-    else hipLaunchKernelGGL((k_pass1<DT, false, kModeArgmax>), g1, blk, 0, st, m, L.V, L.n_slices, L.c, 1, L.part);
+    if (L.vec) launch_timed(k_pass1<DT, true, kModeArgmax>, g1, blk, st, e0, e1, m, L.V, L.n_slices, L.c, 1, L.part);
+    else launch_timed(k_pass1<DT, false, kModeArgmax>, g1, blk, st, e0, e1, m, L.V, L.n_slices, L.c, 1, L.part);
   } else {
-    if (L.vec) hipLaunchKernelGGL((k_pass1<DT, true, kModeSoftmax>), g1, blk, 0, st, m, L.V, L.n_slices, L.c, L.want_argmax, L.part);
-    else hipLaunchKernelGGL((k_pass1<DT, false, kModeSoftmax>), g1, blk, 0, st, m, L.V, L.n_slices, L.c, L.want_argmax, L.part);
+    if (L.vec)
+      launch_timed(k_pass1<DT, true, kModeSoftmax>, g1, blk, st, e0, e1, m, L.V, L.n_slices, L.c, L.want_argmax, L.part);
+    else
+      launch_timed(k_pass1<DT, false, kModeSoftmax>, g1, blk, st, e0, e1, m, L.V, L.n_slices, L.c, L.want_argmax, L.part);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (L.ev_stop && hipEventRecord(L.ev_stop, st) != hipSuccess) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_combine<DT>), dim3((n_lr + kWaves - 1) / kWaves), blk, 0, st, m, n_lr, L.n_slices, L.c,
                      L.greedy, L.part, L.rs, L.rso);
   e = hipGetLastError();
