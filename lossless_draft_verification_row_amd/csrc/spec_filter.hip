@@ -499,22 +499,36 @@ __global__ __launch_bounds__(kThreads) void k_filt_rows(FilterArgs a) {
     }
     return lo;
   };
+  // bf16: the largest order key among the candidates, formed while they are copied in
+  int km = -1;
   if (staged) {
-    // copy the candidates in, 8 per thread in flight at a time
-    for (int b0 = 0; b0 < n; b0 += 8 * kThreads) {
-      CandEntry tmp[8];
+    // copy the candidates in: wave w takes slices w, w + 4, ..., lane l entries l and l + 64
+    // of each; eight slices per wave (sixteen loads per thread) in flight at a time
+    const int wv = t >> 6;
+    for (int i0 = 0; i0 < cap; i0 += 128) {
+      for (int s0 = wv; s0 < n_s; s0 += kWaves * 8) {
+        CandEntry tmp[8][2];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = b0 + u * kThreads + t;
-        if (j < n) {
-          const int sl = slice_of(j);
-          tmp[u] = cd[(int64_t)sl * cap + (j - L.off[sl])];
+        for (int u = 0; u < 8; ++u) {
+          const int sl = s0 + u * kWaves;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int idx = i0 + lane + 64 * h;
+            if (sl < n_s && idx < L.cnt[sl]) tmp[u][h] = cd[(int64_t)sl * cap + idx];
+          }
         }
-      }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = b0 + u * kThreads + t;
-        if (j < n) L.cand[j] = tmp[u];
+        for (int u = 0; u < 8; ++u) {
+          const int sl = s0 + u * kWaves;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int idx = i0 + lane + 64 * h;
+            if (sl < n_s && idx < L.cnt[sl]) {
+              L.cand[L.off[sl] + idx] = tmp[u][h];
+              if (NP == 2) km = max(km, (int)key_hi<2>(order_key(tmp[u][h].v)));
+            }
+          }
+        }
       }
     }
     __syncthreads();
@@ -531,8 +545,8 @@ __global__ __launch_bounds__(kThreads) void k_filt_rows(FilterArgs a) {
   if (NP == 2) {
     // bf16: one LDS histogram of the candidate keys within 256 of the maximum (one key per
     // bin) gives the exact k-th largest when the top k lie in that window
-    int km = -1;
-    for (int j = t; j < n; j += kThreads) km = max(km, (int)key_hi<2>(order_key(at(j).v)));
+    if (!staged)
+      for (int j = t; j < n; j += kThreads) km = max(km, (int)key_hi<2>(order_key(at(j).v)));
     L.sel.hist[t] = 0u;
     km = wave_max_i(km);
     if (lane == 0) L.sel.wtot[0][t >> 6] = km;

@@ -219,9 +219,12 @@ __device__ __forceinline__ void load_run16(const void* row, int V, int x0, float
 // group and element masses are wave-wide fp64 prefix sums.
 // Stage the draft offsets in LDS and check them as one exclusive prefix (every request is
 // refused when any offset is out of order).
-__device__ __forceinline__ bool stage_cu(const FusedArgs& a, int* cu, int* red) {
+template <int N>
+__device__ __forceinline__ bool stage_cu(const FusedArgs& a, const int (&pre)[N], int* cu, int* red) {
   const int t = threadIdx.x;
-  for (int k = t; k <= a.B; k += kThreads) cu[k] = a.cu[k];
+#pragma unroll
+  for (int k = 0; k < N; ++k)
+    if (t + k * kThreads <= a.B) cu[t + k * kThreads] = pre[k];
   __syncthreads();
   int bad = 0;
   for (int k = t; k < a.B; k += kThreads) {
@@ -285,16 +288,21 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   const int g = c1 - c0;
   if (!(guess_in && c0 == cg)) ytok = t < g ? a.tokens[c0 + t] : -1;
   if (t >= g) ytok = -1;
-  // the draft tokens' logits, the first two teams of this wave and the Philox blocks do not
-  // depend on one another: all go out before anything waits
+  // the first two teams of this wave, the offset array, the draft tokens' logits and the
+  // Philox blocks do not depend on one another: all go out before anything waits (the teams
+  // first: the logits wait for the tokens)
+  TeamRaw pre[2];
+  pre[0] = team_load<MODE>(a, rrs, c0, b, g, wave);
+  pre[1] = team_load<MODE>(a, rrs, c0, b, g, wave + kWaves);
+  int cu_pre[(kMaxReqFused + 1 + kThreads - 1) / kThreads];
+#pragma unroll
+  for (int k = 0; k < (kMaxReqFused + 1 + kThreads - 1) / kThreads; ++k)
+    cu_pre[k] = t + k * kThreads <= a.B ? a.cu[t + k * kThreads] : 0;
   float ly_p = 0.f, ly_q = 0.f;
   if (t < g && ytok >= 0 && ytok < a.V) {
     ly_p = logit_at<DT>(row_ptr<DT>(a.tgt, a.tgt_ld, c0 + b + t), ytok);
     if (MODE == kFuSample) ly_q = logit_at<DT>(row_ptr<DT>(a.drf, a.drf_ld, c0 + t), ytok);
   }
-  TeamRaw pre[2];
-  pre[0] = team_load<MODE>(a, rrs, c0, b, g, wave);
-  pre[1] = team_load<MODE>(a, rrs, c0, b, g, wave + kWaves);
   double u_acc = 0.0;
   if (t <= g) {
     // the Philox block of position t (1-based i = t + 1): word 0 is the accept draw, words
@@ -307,7 +315,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
     F.us[t][2] = u53(w[3]);
   }
   // the draft offsets as one exclusive prefix: every request is refused when any is out of order
-  if (stage_cu(a, L.cu, L.i)) {
+  if (stage_cu(a, cu_pre, L.cu, L.i)) {
     if (t <= a.G) a.out_tokens[(int64_t)b * G1 + t] = -1;
     if (t == 0) {
       a.out_num_accepted[b] = 0;
@@ -550,6 +558,12 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       // E. levels 2 and 3 inside chunk k.  Weights are relative within the chunk: e_p (p
       // only) or max(e_p r - e_q, 0) with r = alpha_p / alpha_q.
       const int wkind = F.wkind;
+      // the chunk's logits and its records go out together
+      const int grp = t >> 2, quarter = t & 3;
+      const int x0 = k * kChunk + grp * kGroup + quarter * 16;
+      float wv[16], vq[16];
+      load_run16<DT, VEC>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, x0, wv);
+      if (wkind == 1) load_run16<DT, VEC>(row_ptr<DT>(a.drf, a.drf_ld, c0 + F.pos), a.V, x0, vq);
       float refp, sp_, wp_, refq = 0.f, rr = 0.f;
       load_rec(rrs, rec_off(n_s, r, k, 0), tag, refp, sp_, wp_);
       if (wkind == 1) {
@@ -559,13 +573,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
         const double alq = exp2_split((double)refq - (double)T.M[1]) / T.z[1];
         rr = (float)(alp / alq);
       }
-      const int grp = t >> 2, quarter = t & 3;
-      const int x0 = k * kChunk + grp * kGroup + quarter * 16;
-      float wv[16];
-      load_run16<DT, VEC>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, x0, wv);
       if (wkind == 1) {
-        float vq[16];
-        load_run16<DT, VEC>(row_ptr<DT>(a.drf, a.drf_ld, c0 + F.pos), a.V, x0, vq);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float ep = __builtin_amdgcn_exp2f(fmaf(wv[e], a.c, -refp));
