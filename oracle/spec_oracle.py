@@ -15,6 +15,8 @@ Pages followed (cited by page title and section):
         a one-hot q;  §4.1-4.2 q*a = min(p,q), beta = sum [p-q]_+ = 1 - A;  §4.3 A = 1 - TV;
         §5.1 stop at the first rejection;  §5.2 bonus token from p_{gamma+1};  §7 the worked
         example p = [0.6, 0.3, 0.1], q = [0.2, 0.5, 0.3].
+  [DL]  "DLite: History-free Speculative Decoding for Agentic AI", section "核心方法" (core
+        method): one projection onto the vocabulary per round.
   [SKV] "SpecKV: Adaptive Speculative Decoding with Compression-Aware Gamma Selection",
         section "草稿模型信号提取" (draft-model signals): per-position draft entropy in bits and
         max probability, their mean over the block, the maximum entropy and the minimum
@@ -69,6 +71,17 @@ Readings taken where the pages leave a step open (plainest reading the rest supp
       layout: read as input [x, gamma] (6 values), one hidden layer of 16 ReLU units and a
       linear output, weights supplied by the caller (the trained ones are not available).
       Ties go to the smallest gamma; a NaN feature gives gamma* = -1.
+
+  R12 Fused LM head ([DL] the DLite page, section "核心方法" (core method): the draft's sequential
+      head works in the hidden space and projects onto the vocabulary once).  The logits of a
+      row are l_v = sum_d h_d W_{v,d} for a hidden state h [D] and a head W [V, D], taken in
+      float64 from the exact bf16 values; the row statistics are those of spec_row_stats
+      (R1-R3, R7, R8) with no filter, and p_tok is the row's probability of a given token
+      (NaN for a token outside [0, V) or a non-finite row).  The GPU accumulates the products
+      (exact in fp32) in fp32, so its logits may differ from these by up to
+      D * 2^-24 * sum_d |h_d W_{v,d}|, the standard bound for a sum of D terms; the parity
+      tolerances follow from it, and inputs whose partial sums are all exact in fp32 pin the
+      statistics at the usual bar.
 
 Every function states which of the above it follows.  The decision margins recorded next
 to each result (distance of u from the accept ratio, of u*M from the sampler prefix sums,
@@ -581,3 +594,39 @@ def select_gamma(req_stats, comp, w1, b1, w2, b2, gammas=GAMMAS):
     rest = np.delete(E, best)
     margin = float(E[best] - rest.max()) if len(rest) else math.inf
     return gammas[best], E, margin
+
+
+# ----------------------------------------------------------------------------- fused LM head
+
+
+def lm_head_logits(hidden, weight):
+    """l = h W^T in float64 from the exact bf16 values (as float arrays).  [DL] core method,
+    reading R12."""
+    h = np.asarray(hidden, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    return h @ w.T
+
+
+def lm_head_row_stats(hidden, weight, sp: SamplingParams, tokens=None):
+    """Oracle of spec_lm_head_row_stats: the statistics of row_stats on l = h W^T, plus p_tok.
+    [DL] core method and the signals of [SKV], readings R12, R2, R3, R7, R8.
+
+    hidden [R, D] and weight [V, D] hold the bf16 values as floats; tokens [R] or None.
+    Returns row_stats's dict plus "p_tok" [R] (NaN where not defined) and "logits".
+    """
+    if sp.top_k > 0 and sp.top_k < np.asarray(weight).shape[0] or sp.top_p < 1.0:
+        raise ValueError("the fused head takes no top-k / top-p filter")
+    logits = lm_head_logits(hidden, weight)
+    out = row_stats(logits, sp)
+    R, V = logits.shape
+    p_tok = np.full(R, float("nan"))
+    if tokens is not None:
+        for r in range(R):
+            y = int(tokens[r])
+            if 0 <= y < V:
+                d = row_distribution(logits[r], sp)
+                if d.finite:
+                    p_tok[r] = float(d.probs[y])
+    out["p_tok"] = p_tok
+    out["logits"] = logits
+    return out

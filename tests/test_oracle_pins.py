@@ -649,3 +649,56 @@ def test_gamma_selection_uses_the_features():
         w2 = np.zeros(16); w2[0] = sign
         g, E, _ = O.select_gamma([3.0, 0.4, 5.0, 0.25], 1.0, w1, b1, w2, 0.0)
         assert g == want and abs(E[0] - (sign * 0.25 * 2 + 1.0)) < 1e-12
+
+
+# ----------------------------------------------------------------------------- fused LM head (R12)
+
+
+def test_lm_head_logits_brute_force():
+    """A tiny case summed by hand in Python loops: l[r][v] = sum_d h[r][d] W[v][d] (not W^T h,
+    not h W with V and D swapped)."""
+    rng = np.random.default_rng(4)
+    h = rng.integers(-3, 4, size=(2, 3)).astype(float)
+    W = rng.integers(-3, 4, size=(5, 3)).astype(float)
+    l = O.lm_head_logits(h, W)
+    assert l.shape == (2, 5)
+    for r in range(2):
+        for v in range(5):
+            assert l[r, v] == sum(h[r, d] * W[v, d] for d in range(3))
+
+
+def test_lm_head_selector_weights_give_hidden_components():
+    """A head whose row v is the unit vector of component perm[v] returns l[r, v] = h[r, perm[v]];
+    its statistics are row_stats of those values (R12 composes with R2, R3)."""
+    rng = np.random.default_rng(5)
+    D, V = 16, 40
+    perm = rng.integers(0, D, size=V)
+    W = np.zeros((V, D))
+    W[np.arange(V), perm] = 1.0
+    h = rng.standard_normal((3, D))
+    sp = O.SamplingParams(0.8)
+    got = O.lm_head_row_stats(h, W, sp, tokens=np.array([0, 39, 7]))
+    ref = O.row_stats(h[:, perm], sp)
+    for k in ("max_logit", "argmax", "log_z", "entropy_bits", "max_prob"):
+        np.testing.assert_array_equal(got[k], ref[k])
+
+
+def test_lm_head_p_tok_closed_form_and_edges():
+    """p_tok = exp(l_y / T - log Z); NaN for a token outside [0, V) and for a non-finite row."""
+    rng = np.random.default_rng(6)
+    h = rng.standard_normal((4, 8))
+    W = rng.standard_normal((30, 8))
+    sp = O.SamplingParams(1.3)
+    tok = np.array([3, -1, 30, 29])
+    got = O.lm_head_row_stats(h, W, sp, tokens=tok)
+    l = h @ W.T
+    for r, y in ((0, 3), (3, 29)):
+        want = math.exp(l[r, y] / 1.3 - got["log_z"][r])
+        assert abs(got["p_tok"][r] - want) <= 1e-12 * want
+    assert np.isnan(got["p_tok"][1]) and np.isnan(got["p_tok"][2])
+    h2 = h.copy()
+    h2[0, 0] = np.inf
+    bad = O.lm_head_row_stats(h2, W, sp, tokens=tok)
+    assert np.isnan(bad["p_tok"][0]) and bad["argmax"][0] == -1
+    greedy = O.lm_head_row_stats(h, W, O.SamplingParams(0.0), tokens=tok)
+    assert greedy["p_tok"][0] == (1.0 if np.argmax(l[0]) == 3 else 0.0)
