@@ -181,6 +181,33 @@ int spec_residual_sample(int R, int V, spec_dtype dt,
 
 size_t spec_residual_sample_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling_params sp);
 
+/* spec_lm_head_row_stats -- the statistics of spec_row_stats for logits that are never
+ * materialised: l = h W^T, the projection of hidden states onto the vocabulary (the DLite page,
+ * section "核心方法" (core method), projects onto the vocabulary once per round), computed in
+ * 256-column tiles with bf16 MFMA (fp32 accumulation) and reduced to per-row statistics in the
+ * tiles' epilogue.
+ *  hidden      [R, D] bf16 on the device, row stride h_ld elements.
+ *  weight      [V, D] bf16 on the device (one head row per vocabulary entry), row stride w_ld.
+ *              D, h_ld and w_ld must be multiples of 8 and both bases 16-byte aligned
+ *              (otherwise SPEC_ERR_UNSUPPORTED).
+ *  sp          temperature T >= 0 (0: greedy); top-k and top-p must be off (SPEC_ERR_UNSUPPORTED).
+ *  tokens      [R] int32 or NULL: a token per row for p_tok.
+ *  outputs     [R] each, or NULL: max_logit, argmax (lowest index), log_z = ln sum exp(l / T)
+ *              (NaN when greedy), entropy_bits, max_prob, p_tok = p(tokens[r]) (NaN for a
+ *              token outside [0, V); requires tokens).  A row with a NaN or +inf logit, or no
+ *              finite one, gets NaN everywhere and argmax -1; greedy rows report entropy 0,
+ *              max_prob 1 and p_tok 1 or 0.
+ *  workspace   spec_lm_head_workspace_bytes(R, V, D) bytes, 256-byte aligned.
+ * The logits carry fp32 accumulation error, at most D 2^-24 sum_d |h_d W_{v,d}| each.
+ * Returns SPEC_OK, SPEC_ERR_INVALID, SPEC_ERR_UNSUPPORTED, SPEC_ERR_WORKSPACE or
+ * SPEC_ERR_LAUNCH. */
+int spec_lm_head_row_stats(int R, int V, int D, const void* hidden, int64_t h_ld, const void* weight, int64_t w_ld,
+                           spec_sampling_params sp, const int32_t* tokens, float* max_logit, int32_t* argmax,
+                           float* log_z, float* entropy_bits, float* max_prob, float* p_tok, void* workspace,
+                           size_t workspace_bytes, void* hip_stream);
+
+size_t spec_lm_head_workspace_bytes(int R, int V, int D);
+
 /* Weights of the draft-length predictor: the SpecKV page's acceptance-rate regressor
  * f(x, gamma), an MLP with 16 hidden units, read as h = relu(w1 [x, gamma] + b1),
  * f = w2 . h + b2 with x = [H_bar, c_bar, H_max, c_min, comp].  Device pointers, fp32;

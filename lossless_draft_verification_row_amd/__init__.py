@@ -77,6 +77,11 @@ def load_library():
                                          vp, vp, vp, vp, sz, vp]
     lib.spec_residual_sample_workspace_bytes.restype = sz
     lib.spec_residual_sample_workspace_bytes.argtypes = [i32, i32, i32, SamplingParams]
+    lib.spec_lm_head_row_stats.restype = i32
+    lib.spec_lm_head_row_stats.argtypes = [i32, i32, i32, vp, i64, vp, i64, SamplingParams, vp, vp, vp, vp, vp, vp,
+                                           vp, vp, sz, vp]
+    lib.spec_lm_head_workspace_bytes.restype = sz
+    lib.spec_lm_head_workspace_bytes.argtypes = [i32, i32, i32]
     lib.spec_select_gamma.restype = i32
     lib.spec_select_gamma.argtypes = [i32, vp, vp, GammaMLP, vp, vp, vp]
     lib.spec_set_spin_limit.restype = i32
@@ -289,4 +294,40 @@ def spec_select_gamma(req_stats, w1, b1, w2, b2, comp=None, stream=None):
     rc = lib.spec_select_gamma(B, _ptr(req_stats), _ptr(comp), GammaMLP(_ptr(w1), _ptr(b1), _ptr(w2), float(b2)),
                                _ptr(o["gamma"]), _ptr(o["expected"]), _stream(stream))
     _check(rc, "spec_select_gamma")
+    return o
+
+
+HEAD_FIELDS = ("max_logit", "argmax", "log_z", "entropy_bits", "max_prob", "p_tok")
+
+
+def spec_lm_head_row_stats(hidden, weight, *, temperature=1.0, tokens=None, workspace=None, out=None, stream=None):
+    """Row statistics of l = hidden @ weight^T without materialising the logits (see
+    spec_lm_head_row_stats in the header).  hidden [R, D] and weight [V, D] are bf16 CUDA
+    tensors with unit column stride; tokens [R] int32 or None.  Returns a dict of [R] tensors:
+    max_logit, argmax, log_z, entropy_bits, max_prob and, with tokens, p_tok."""
+    lib = load_library()
+    for t, n in ((hidden, "hidden"), (weight, "weight")):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{n} must be bf16")
+    hp, hld = _rows(hidden, "hidden")
+    wp_, wld = _rows(weight, "weight")
+    R, D = hidden.shape
+    V = weight.shape[0]
+    if weight.shape[1] != D:
+        raise ValueError("hidden and weight must share D")
+    if tokens is not None and (tokens.dtype != torch.int32 or not tokens.is_cuda or tokens.numel() != R):
+        raise ValueError("tokens must be an int32 CUDA tensor of R entries")
+    dev = hidden.device
+    o = out if out is not None else {}
+    if "max_logit" not in o:
+        for k in ("max_logit", "log_z", "entropy_bits", "max_prob"):
+            o[k] = torch.empty(R, dtype=torch.float32, device=dev)
+        o["argmax"] = torch.empty(R, dtype=torch.int32, device=dev)
+        if tokens is not None:
+            o["p_tok"] = torch.empty(R, dtype=torch.float32, device=dev)
+    need = lib.spec_lm_head_workspace_bytes(R, V, D)
+    wsp, wsn = _workspace(need, dev, workspace)
+    rc = lib.spec_lm_head_row_stats(R, V, D, hp, hld, wp_, wld, _sp(temperature, 0, 1.0), _ptr(tokens),
+                                    *[_ptr(o.get(k)) for k in HEAD_FIELDS], wsp, wsn, _stream(stream))
+    _check(rc, "spec_lm_head_row_stats")
     return o

@@ -596,6 +596,57 @@ int spec_residual_sample(int R, int V, spec_dtype dt, const void* p_logits, int6
   return SPEC_OK;
 }
 
+size_t spec_lm_head_workspace_bytes(int R, int V, int D) {
+  if (R <= 0 || V <= 0 || D <= 0) return 0;
+  const int64_t n_ct = ((int64_t)V + kHeadCols - 1) / kHeadCols;
+  return kHeaderBytes + align_up((size_t)R * n_ct * sizeof(HeadRec)) + align_up((size_t)R * sizeof(float));
+}
+
+int spec_lm_head_row_stats(int R, int V, int D, const void* hidden, int64_t h_ld, const void* weight, int64_t w_ld,
+                           spec_sampling_params sp, const int32_t* tokens, float* max_logit, int32_t* argmax,
+                           float* log_z, float* entropy_bits, float* max_prob, float* p_tok, void* workspace,
+                           size_t workspace_bytes, void* hip_stream) {
+  if (R < 0 || V <= 0 || D <= 0) return SPEC_ERR_INVALID;
+  if (check_params(sp) != SPEC_OK) return SPEC_ERR_INVALID;
+  if (filter_on(V, sp)) return SPEC_ERR_UNSUPPORTED;
+  if (R == 0) return SPEC_OK;
+  if (!hidden || !weight || h_ld < D || w_ld < D) return SPEC_ERR_INVALID;
+  if (p_tok && !tokens) return SPEC_ERR_INVALID;
+  // 16-byte rows: D, the strides and the bases are whole multiples of eight bf16
+  if (D % 8 != 0 || h_ld % 8 != 0 || w_ld % 8 != 0 || ((uintptr_t)hidden % 16) != 0 || ((uintptr_t)weight % 16) != 0)
+    return SPEC_ERR_UNSUPPORTED;
+  const int64_t n_ct = ((int64_t)V + kHeadCols - 1) / kHeadCols;
+  if ((int64_t)R * n_ct > (int64_t)INT32_MAX / 2) return SPEC_ERR_INVALID;
+  const size_t need = spec_lm_head_workspace_bytes(R, V, D);
+  if (!workspace || workspace_bytes < need) return SPEC_ERR_WORKSPACE;
+  if (((uintptr_t)workspace % kAlign) != 0) return SPEC_ERR_INVALID;
+  HeadArgs a;
+  memset(&a, 0, sizeof(a));
+  a.hidden = hidden;
+  a.h_ld = h_ld;
+  a.weight = weight;
+  a.w_ld = w_ld;
+  a.R = R;
+  a.V = V;
+  a.D = D;
+  a.n_ct = (int)n_ct;
+  a.greedy = sp.temperature == 0.f ? 1 : 0;
+  a.c = exp2_scale(sp);
+  a.inv_t = a.greedy ? 0.0 : 1.0 / (double)sp.temperature;
+  a.tokens = tokens;
+  Carve cv{(char*)workspace};
+  a.rec = cv.take<HeadRec>((size_t)R * n_ct * sizeof(HeadRec));
+  a.ly = cv.take<float>((size_t)R * sizeof(float));
+  a.max_logit = max_logit;
+  a.argmax = argmax;
+  a.log_z = log_z;
+  a.entropy_bits = entropy_bits;
+  a.max_prob = max_prob;
+  a.p_tok = p_tok;
+  const hipError_t e = launch_head(a, (hipStream_t)hip_stream, g_prof_start, g_prof_stop);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
+}
+
 int spec_select_gamma(int B, const float* req_stats, const float* comp, spec_gamma_mlp w, int32_t* out_gamma,
                       float* out_expected, void* hip_stream) {
   if (B < 0) return SPEC_ERR_INVALID;

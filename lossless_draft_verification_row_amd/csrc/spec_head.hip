@@ -1,0 +1,293 @@
+// spec_head.hip -- the LM head fused with the row statistics.
+//
+// The logits of a row, l_v = sum_d h_d W_{v,d} (the projection of a hidden state onto the
+// vocabulary that the DLite page's core method does once per round), are formed tile by tile
+// with bf16 MFMA and reduced in the tile's epilogue to per-row partial statistics: the tile's
+// maximum, its lowest arg-max, sum e and sum e t with e = 2^t, t = (l - m) log2(e) / T, the
+// same partials the streaming kernels keep per slice.  The logits never reach memory.  A second
+// kernel combines a row's partials in fp64 into the statistics spec_row_stats reports (the
+// SpecKV page's signals) and the probability of a given token.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "spec_device.h"
+#include "spec_internal.h"
+
+namespace specv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kHBK = 32;         // k per stage
+constexpr int kHBV = kHeadCols;  // vocabulary columns per workgroup, 64 per wave
+constexpr int kHLd = kHBK + 8;   // LDS row stride in bf16 (80 B; 16-B aligned, staggers the banks)
+constexpr int kTLd = 65;         // epilogue transpose row stride in floats
+
+template <int RB>   // 32-row blocks per workgroup
+struct HeadLds {
+  union {
+    struct {
+      uint16_t a[2][32 * RB][kHLd];   // hidden rows x k, double-buffered
+      uint16_t b[2][kHBV][kHLd];      // head rows (vocabulary) x k
+    } k;
+    struct {
+      float t[kWaves][32][kTLd];      // one wave's 32 x 64 logits, transposed to rows
+      HeadRec part[kWaves][32 * RB];  // per wave: the partials of each row over its 64 columns
+    } e;
+  };
+};
+
+// Issue the global loads of stage kt: rows of hidden (RB * 32 x 32 k) and of the head
+// (256 x 32 k), 16 bytes each; rows or k past the end read as zero.
+template <int RB>
+__device__ __forceinline__ void head_load(const HeadArgs& a, int r0, int v0, int k0, uint4 (&ra)[RB / 2],
+                                          uint4 (&rb)[4]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < RB / 2; ++i) {
+    const int idx = t + kThreads * i, row = idx >> 2, k = k0 + 8 * (idx & 3);
+    const int r = r0 + row;
+    ra[i] = (r < a.R && k < a.D) ? *(const uint4*)((const uint16_t*)a.hidden + (int64_t)r * a.h_ld + k)
+                                 : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = t + kThreads * i, col = idx >> 2, k = k0 + 8 * (idx & 3);
+    const int v = v0 + col;
+    rb[i] = (v < a.V && k < a.D) ? *(const uint4*)((const uint16_t*)a.weight + (int64_t)v * a.w_ld + k)
+                                 : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+template <int RB>
+__device__ __forceinline__ void head_store(HeadLds<RB>& L, int buf, const uint4 (&ra)[RB / 2], const uint4 (&rb)[4]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < RB / 2; ++i) {
+    const int idx = t + kThreads * i;
+    *(uint4*)&L.k.a[buf][idx >> 2][8 * (idx & 3)] = ra[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = t + kThreads * i;
+    *(uint4*)&L.k.b[buf][idx >> 2][8 * (idx & 3)] = rb[i];
+  }
+}
+
+// One workgroup per (32 RB rows) x (256 columns) tile.  Wave w holds columns 64w .. 64w + 63
+// of every row in RB x 2 accumulators of the 32x32x16 bf16 MFMA: A[i][k] is lane i + 32 (k / 8)
+// element k % 8, B[k][j] lane j + 32 (k / 8), and C[i][j] lane j + 32 ((i / 4) % 2) element
+// 4 (i / 8) + i % 4.  Row tiles vary fastest over the grid, so the workgroups that share a head
+// tile run together.
+template <int RB>
+__global__ __launch_bounds__(kThreads) void k_head(HeadArgs a) {
+  __shared__ HeadLds<RB> L;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int rt = blockIdx.x % a.n_rt, ct = blockIdx.x / a.n_rt;
+  const int r0 = rt * 32 * RB, v0 = ct * kHBV;
+  f32x16 acc[RB][2];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  uint4 ra[RB / 2], rb[4];
+  const int n_k = (a.D + kHBK - 1) / kHBK;
+  head_load<RB>(a, r0, v0, 0, ra, rb);
+  head_store<RB>(L, 0, ra, rb);
+  __syncthreads();
+  const int fr = lane & 31, fk = 8 * (lane >> 5);
+  for (int kt = 0; kt < n_k; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_k) head_load<RB>(a, r0, v0, (kt + 1) * kHBK, ra, rb);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 fa[RB], fb[2];
+#pragma unroll
+      for (int i = 0; i < RB; ++i) fa[i] = __builtin_bit_cast(bf16x8, *(const uint4*)&L.k.a[buf][32 * i + fr][16 * h + fk]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[j] = __builtin_bit_cast(bf16x8, *(const uint4*)&L.k.b[buf][64 * wave + 32 * j + fr][16 * h + fk]);
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < n_k) head_store<RB>(L, buf ^ 1, ra, rb);
+    __syncthreads();
+  }
+
+  // Epilogue: per 32-row block, the wave's 32 x 64 logits go to LDS by row; lanes 2i and
+  // 2i + 1 take row i, 32 columns each.
+  const float c = a.c;
+  const int cw0 = v0 + 64 * wave;   // this wave's first column
+  const int hf = lane & 1, ri = lane >> 1;
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = 32 * j + (lane & 31);
+      const bool in = cw0 + col < a.V;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        L.e.t[wave][row][col] = in ? acc[i][j][e] : -INFINITY;
+      }
+    }
+    __syncthreads();
+    const float* x = &L.e.t[wave][ri][32 * hf];
+    const int r = r0 + 32 * i + ri;
+    // the token's logit, from the one lane whose columns hold it
+    if (a.tokens && r < a.R) {
+      const int y = a.tokens[r] - (cw0 + 32 * hf);
+      if (y >= 0 && y < 32 && cw0 + 32 * hf + y < a.V) a.ly[r] = x[y];
+    }
+    float m = -INFINITY;
+    int am = INT_MAX, bad = 0;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      const float v = x[q];
+      bad |= (v != v || v == INFINITY) ? 1 : 0;
+      if (v > m) { m = v; am = q; }
+    }
+    am = m > -INFINITY ? cw0 + 32 * hf + am : INT_MAX;
+    // the partner lane holds the row's other 32 columns
+    const float m2 = __shfl_xor(m, 1);
+    const int am2 = __shfl_xor(am, 1);
+    bad |= __shfl_xor(bad, 1);
+    const float M = fmaxf(m, m2);
+    int amx = INT_MAX;
+    if (m == M) amx = am;
+    if (m2 == M) amx = min(amx, am2);
+    // t = (l - M) c, exactly 0 at the maximum (e = 1); the sums in fp64
+    double s = 0.0, w = 0.0;
+    if (!a.greedy && M > -INFINITY) {
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        const float tt = (x[q] - M) * c;
+        const float ev = __builtin_amdgcn_exp2f(tt);
+        s += (double)ev;
+        if (ev > 0.f) w = fma((double)ev, (double)tt, w);
+      }
+      s += __shfl_xor(s, 1);
+      w += __shfl_xor(w, 1);
+    }
+    if (hf == 0) {
+      HeadRec pr;
+      pr.m = M;
+      pr.s = s;
+      pr.w = w;
+      pr.amax = bad ? -2 : (amx == INT_MAX ? -1 : amx);
+      L.e.part[wave][32 * i + ri] = pr;
+    }
+    __syncthreads();
+  }
+  // the four waves' partials of each row, folded in column order into the tile's record
+  if (t < 32 * RB && r0 + t < a.R) {
+    float M = -INFINITY;
+    int flag = 0;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) {
+      const HeadRec p = L.e.part[q][t];
+      M = fmaxf(M, p.m);
+      if (p.amax == -2) flag = 1;
+    }
+    HeadRec out;
+    out.m = M;
+    out.s = 0.0;
+    out.w = 0.0;
+    out.amax = -1;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) {
+      const HeadRec p = L.e.part[q][t];
+      if (out.amax < 0 && p.m == M && p.amax >= 0) out.amax = p.amax;
+      if (!a.greedy && p.m > -INFINITY && M > -INFINITY) {
+        const double d = ((double)p.m - (double)M) * (double)c;
+        const double f = exp2_split(d);
+        out.s += p.s * f;
+        out.w += f * (p.w + p.s * d);
+      }
+    }
+    if (flag) out.amax = -2;
+    a.rec[(int64_t)(r0 + t) * a.n_ct + ct] = out;
+  }
+}
+
+// One wave per row: the row's tile records in fp64 (maximum, lowest arg-max, sum e and sum e t
+// relative to the row maximum), then the statistics and p(token).  A NaN or +inf logit makes
+// every output of the row NaN and its arg-max -1.
+__global__ __launch_bounds__(kThreads) void k_head_combine(HeadArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (r >= a.R) return;
+  const HeadRec* rc = a.rec + (int64_t)r * a.n_ct;
+  float M = -INFINITY;
+  int bad = 0;
+  for (int k = lane; k < a.n_ct; k += 64) {
+    const HeadRec p = rc[k];
+    M = fmaxf(M, p.m);
+    bad |= p.amax == -2 ? 1 : 0;
+  }
+  M = wave_max_dpp(M);
+  bad = wave_or(bad);
+  int am = INT_MAX;
+  double s = 0.0, w = 0.0;
+  const double cd = (double)a.c;
+  for (int k = lane; k < a.n_ct; k += 64) {
+    const HeadRec p = rc[k];
+    if (p.m == M && p.amax >= 0) am = min(am, p.amax);
+    if (!a.greedy && p.m > -INFINITY && M > -INFINITY) {
+      const double d = ((double)p.m - (double)M) * cd;
+      const double f = exp2_split(d);
+      s += p.s * f;
+      w += f * (p.w + p.s * d);
+    }
+  }
+  am = wave_min_i(am);
+  s = wave_sum_dpp_d(s);
+  w = wave_sum_dpp_d(w);
+  if (lane != 0) return;
+  const float nan = __int_as_float(0x7fc00000);
+  const bool ok = !bad && M > -INFINITY && (a.greedy || s > 0.0);
+  const int y = a.tokens ? a.tokens[r] : -1;
+  const bool yv = y >= 0 && y < a.V;
+  float mx = nan, lz = nan, ent = nan, mp = nan, pt = nan;
+  int ax = -1;
+  if (ok) {
+    mx = M;
+    ax = am == INT_MAX ? -1 : am;
+    if (a.greedy) {
+      ent = 0.f;
+      mp = 1.f;
+      if (yv) pt = y == ax ? 1.f : 0.f;
+    } else {
+      lz = (float)((double)M * a.inv_t + log2_split(s) * 0.6931471805599453);
+      ent = (float)(log2_split(s) - w / s);
+      mp = (float)(1.0 / s);
+      if (yv) pt = (float)(exp2_split(((double)a.ly[r] - (double)M) * cd) / s);
+    }
+  }
+  if (a.max_logit) a.max_logit[r] = mx;
+  if (a.argmax) a.argmax[r] = ax;
+  if (a.log_z) a.log_z[r] = lz;
+  if (a.entropy_bits) a.entropy_bits[r] = ent;
+  if (a.max_prob) a.max_prob[r] = mp;
+  if (a.p_tok) a.p_tok[r] = pt;
+}
+
+hipError_t launch_head(const HeadArgs& a0, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  HeadArgs a = a0;
+  const bool big = a.R > 64;
+  a.n_rt = big ? (a.R + 127) / 128 : (a.R + 63) / 64;
+  const long long grid = (long long)a.n_rt * a.n_ct;
+  if (grid < 1 || grid > 0x7fffffffll) return hipErrorInvalidConfiguration;
+  if (big) launch_timed(k_head<4>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
+  else launch_timed(k_head<2>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_head_combine, dim3((unsigned)((a.R + kWaves - 1) / kWaves)), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace specv

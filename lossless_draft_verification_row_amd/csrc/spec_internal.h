@@ -227,6 +227,35 @@ hipError_t launch_select_gamma(int B, const float* req_stats, const float* comp,
                                const float* w2, float b2, int32_t* out_gamma, float* out_expected, hipStream_t st);
 hipError_t launch_residual_finalize(const ResidualArgs& a, int dt, hipStream_t st);
 
+// ---------------------------------------------------------------- fused LM head
+
+struct HeadRec {          // a row's partials over one 256-column tile of l = h W^T
+  float m;                // maximum
+  int amax;               // lowest arg-max; -1 none, -2 a NaN or +inf logit
+  double s, w;            // sum e and sum e t with e = 2^t, t = (l - m) c (fp64: a peaked row's
+                          // sum is 1 plus a little, which fp32 would round away)
+};
+struct HeadArgs {
+  const void* hidden;     // [R, D] bf16, row stride h_ld
+  int64_t h_ld;
+  const void* weight;     // [V, D] bf16, row stride w_ld
+  int64_t w_ld;
+  int R, V, D, n_rt, n_ct, greedy;
+  float c;                // log2(e) / T
+  double inv_t;
+  const int32_t* tokens;  // [R] or nullptr
+  HeadRec* rec;           // [R][n_ct]
+  float* ly;              // [R]: the logit of tokens[r]
+  float* max_logit;
+  int32_t* argmax;
+  float* log_z;
+  float* entropy_bits;
+  float* max_prob;
+  float* p_tok;
+};
+constexpr int kHeadCols = 256;   // vocabulary columns per tile
+hipError_t launch_head(const HeadArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+
 size_t slice_part_bytes();
 size_t row_stat_bytes();
 

@@ -145,3 +145,29 @@ def make_inputs(cfg, B=None, V=None, seed=None, gamma=None, tokens="gumbel") -> 
         dv = bf16_bits_to_f32(draft) if bf16 else draft
         toks = gumbel_argmax(dv, wl.temperature, rng)
     return Inputs(wl, gammas, cu, target, None if wl.token_only else draft, toks, seed)
+
+
+# ----------------------------------------------------------------------------- fused LM head inputs
+
+
+def head_inputs(R, V, D, seed, scale_h=1.0, scale_w=0.02, exact=False):
+    """Seeded hidden states [R, D] and a head [V, D] as bf16 bit patterns (uint16).  Normal by
+    default (a unit-scale hidden state, a head scaled like a trained projection so logits have
+    a standard deviation near scale_w * sqrt(D)); exact=True draws every value from
+    {-1, -1/2, 0, 1/2, 1}, so every partial sum of a dot product with D <= 2^16 terms is exact
+    in fp32.  W is generated in 8192-row blocks to bound host memory."""
+    rng = np.random.default_rng(seed)
+    if exact:
+        vals = np.array([-1.0, -0.5, 0.0, 0.5, 1.0], dtype=np.float32)
+        h = bf16_bits_from_f32(vals[rng.integers(0, 5, size=(R, D))])
+        w = np.empty((V, D), dtype=np.uint16)
+        for v0 in range(0, V, 8192):
+            n = min(8192, V - v0)
+            w[v0:v0 + n] = bf16_bits_from_f32(vals[rng.integers(0, 5, size=(n, D))])
+        return h, w
+    h = bf16_bits_from_f32(rng.standard_normal((R, D), dtype=np.float32) * np.float32(scale_h))
+    w = np.empty((V, D), dtype=np.uint16)
+    for v0 in range(0, V, 8192):
+        n = min(8192, V - v0)
+        w[v0:v0 + n] = bf16_bits_from_f32(rng.standard_normal((n, D), dtype=np.float32) * np.float32(scale_w))
+    return h, w

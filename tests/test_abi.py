@@ -94,3 +94,24 @@ def test_select_gamma_argument_checks_without_gpu():
     assert lib.spec_select_gamma(3, None, None, w, 16, None, None) == -1      # no req_stats
     assert lib.spec_select_gamma(3, 16, None, L.GammaMLP(16, None, 16, 0.0), 16, None, None) == -1
     assert lib.spec_select_gamma(3, 16, None, w, None, None, None) == -1      # no out_gamma
+
+
+def test_lm_head_argument_checks_without_gpu():
+    lib = L.load_library()
+    sp = L.SamplingParams(1.0, 0, 1.0)
+    outs = [None] * 6
+    # R = 0 is a no-op; negative sizes, null inputs, short strides are rejected
+    assert lib.spec_lm_head_row_stats(0, 100, 64, None, 64, None, 64, sp, None, *outs, None, 0, None) == 0
+    assert lib.spec_lm_head_row_stats(-1, 100, 64, 16, 64, 16, 64, sp, None, *outs, None, 0, None) == -1
+    assert lib.spec_lm_head_row_stats(4, 100, 64, None, 64, 16, 64, sp, None, *outs, None, 0, None) == -1
+    assert lib.spec_lm_head_row_stats(4, 100, 64, 16, 32, 16, 64, sp, None, *outs, None, 0, None) == -1
+    # p_tok without tokens
+    assert lib.spec_lm_head_row_stats(4, 100, 64, 16, 64, 16, 64, sp, None, None, None, None, None, None, 16,
+                                      None, 0, None) == -1
+    # filters, D or strides off the 16-byte grid: unsupported
+    assert lib.spec_lm_head_row_stats(4, 100, 64, 16, 64, 16, 64, L.SamplingParams(1.0, 10, 1.0), None, *outs,
+                                      None, 0, None) == -2
+    assert lib.spec_lm_head_row_stats(4, 100, 60, 16, 64, 16, 64, sp, None, *outs, None, 0, None) == -2
+    # undersized workspace
+    assert lib.spec_lm_head_row_stats(4, 100, 64, 16, 64, 16, 64, sp, None, *outs, 256, 16, None) == -3
+    assert lib.spec_lm_head_workspace_bytes(4, 100, 64) > 4 * 24
