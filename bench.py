@@ -20,6 +20,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of one MI355X
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -31,6 +32,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--lm-head", action="store_true",
+                    help="time the fused LM head (spec_lm_head_row_stats) on the batch-64 workload's "
+                         "target rows instead: R = 512, V = 151936, D = 4096")
     ap.add_argument("--copy-ref", action="store_true",
                     help="time plain 1 GiB copy and read kernels instead (roofline context and the "
                          "scale for HBM byte counters)")
@@ -178,6 +182,74 @@ def load_traffic(kernel):
         return None
 
 
+def lm_head_bench(args, L, W, torch):
+    """The fused LM head on the target rows of the batch-64 workload (64 requests x 8 positions
+    = 512 rows, the Qwen3 vocabulary, hidden size 4096): every row's statistics and p(token)
+    from h W^T without writing the logits.  The streaming kernel is the MFMA one, so its
+    roofline is the dense bf16 matrix-core peak (2 R V D flops per launch)."""
+    R, V, D, T = 512, 151936, 4096, 1.0
+    h_bits, w_bits = W.head_inputs(R, V, D, seed=2024)
+    dev = torch.device("cuda", 0)
+    h = torch.from_numpy(h_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    w0 = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    # two copies of the head, alternated, so that no launch finds the other's head in the cache
+    ws = [w0, w0.clone()]
+    tok = torch.from_numpy(np.random.default_rng(9).integers(0, V, size=R).astype(np.int32)).to(dev)
+    lib = L.load_library()
+    out = {}
+    work = L.new_workspace(lib.spec_lm_head_workspace_bytes(R, V, D), dev)
+
+    def step(k):
+        return L.spec_lm_head_row_stats(h, ws[k % 2], temperature=T, tokens=tok, workspace=work, out=out)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / args.steps
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    for k in range(args.steps):
+        lib.spec_set_profile_events(pairs[k][0], pairs[k][1])
+        step(k)
+    torch.cuda.synchronize()
+    lib.spec_set_profile_events(None, None)
+    kms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
+    flops = 2.0 * R * V * D
+    achieved = flops / (kms * 1e-3) / 1e12
+    line = {
+        "metric": "fused LM head rows/sec (row statistics and p(token) without materialised logits), 1 MI355X",
+        "value": R / sec, "unit": "rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": sec * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy PCG64; hidden N(0, 1), head N(0, 0.02^2), bf16)",
+        "config": {"workload": "qwen3-vocab-head-r512-d4096", "R": R, "V": V, "D": D, "temperature": T,
+                   "flops_per_step": flops, "head_bytes": V * D * 2, "head_copies_rotated": 2},
+        "roofline": {"bound": "mfma", "kernel": "k_head (bf16 MFMA tiles with the row-statistics epilogue)",
+                     "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "kernel_ms_avg": kms,
+                     "head_read_GBps": V * D * 2 / (kms * 1e-3) / 1e9},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import spec_oracle as O
+        rows = 0
+        t0 = time.perf_counter()
+        wf = W.bf16_bits_to_f32(w_bits)
+        hf = W.bf16_bits_to_f32(h_bits)
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            r = rows % R
+            O.lm_head_row_stats(hf[r:r + 4], wf, O.SamplingParams(T), tokens=tok.cpu().numpy()[r:r + 4])
+            rows += 4
+        el = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                                "sample": f"{rows} rows in blocks of 4 in {el:.1f} s (fp64 numpy matmul and "
+                                          f"row statistics, single-threaded BLAS where the host allows)"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -195,6 +267,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+    if args.lm_head:
+        lm_head_bench(args, L, W, torch)
+        return
     lib = L.load_library()
     dev = torch.device("cuda", 0)
     cfg = args.config

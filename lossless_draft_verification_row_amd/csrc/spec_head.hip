@@ -74,16 +74,24 @@ __device__ __forceinline__ void head_store(HeadLds<RB>& L, int buf, const uint4 
   }
 }
 
+// Two waves per SIMD for the tall tile (its accumulators and fragments take up to 256
+// registers).
+constexpr int head_min_waves(int rb) { return rb == 4 ? 2 : 1; }
+
 // One workgroup per (32 RB rows) x (256 columns) tile.  Wave w holds columns 64w .. 64w + 63
 // of every row in RB x 2 accumulators of the 32x32x16 bf16 MFMA: A[i][k] is lane i + 32 (k / 8)
 // element k % 8, B[k][j] lane j + 32 (k / 8), and C[i][j] lane j + 32 ((i / 4) % 2) element
-// 4 (i / 8) + i % 4.  Row tiles vary fastest over the grid, so the workgroups that share a head
-// tile run together.
+// 4 (i / 8) + i % 4.  Workgroup i runs on XCD i mod 8; the row tiles of one column tile go to
+// consecutive workgroups of one XCD, so its L2 serves the head tile they share (and the hidden
+// tiles, shared by every column tile).
 template <int RB>
-__global__ __launch_bounds__(kThreads) void k_head(HeadArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(head_min_waves(RB)))) void k_head(
+    HeadArgs a) {
   __shared__ HeadLds<RB> L;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int rt = blockIdx.x % a.n_rt, ct = blockIdx.x / a.n_rt;
+  const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+  const int rt = jx % a.n_rt, ct = (jx / a.n_rt) * 8 + xcd;
+  if (ct >= a.n_ct) return;
   const int r0 = rt * 32 * RB, v0 = ct * kHBV;
   f32x16 acc[RB][2];
 #pragma unroll
@@ -280,7 +288,7 @@ hipError_t launch_head(const HeadArgs& a0, hipStream_t st, hipEvent_t ev0, hipEv
   HeadArgs a = a0;
   const bool big = a.R > 64;
   a.n_rt = big ? (a.R + 127) / 128 : (a.R + 63) / 64;
-  const long long grid = (long long)a.n_rt * a.n_ct;
+  const long long grid = (long long)a.n_rt * ((a.n_ct + 7) / 8) * 8;
   if (grid < 1 || grid > 0x7fffffffll) return hipErrorInvalidConfiguration;
   if (big) launch_timed(k_head<4>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
   else launch_timed(k_head<2>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
