@@ -19,7 +19,7 @@ namespace specv {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kHBK = 32;         // k per stage
+constexpr int kHBK = 64;         // k per stage
 constexpr int kHBV = kHeadCols;  // vocabulary columns per workgroup, 64 per wave
 constexpr int kHLd = kHBK + 8;   // LDS row stride in bf16 (80 B; 16-B aligned, staggers the banks)
 constexpr int kTLd = 65;         // epilogue transpose row stride in floats
@@ -28,8 +28,8 @@ template <int RB>   // 32-row blocks per workgroup
 struct HeadLds {
   union {
     struct {
-      uint16_t a[2][32 * RB][kHLd];   // hidden rows x k, double-buffered
-      uint16_t b[2][kHBV][kHLd];      // head rows (vocabulary) x k
+      uint16_t a[32 * RB][kHLd];      // hidden rows x k
+      uint16_t b[kHBV][kHLd];         // head rows (vocabulary) x k
     } k;
     struct {
       float t[kWaves][32][kTLd];      // one wave's 32 x 64 logits, transposed to rows
@@ -38,39 +38,39 @@ struct HeadLds {
   };
 };
 
-// Issue the global loads of stage kt: rows of hidden (RB * 32 x 32 k) and of the head
-// (256 x 32 k), 16 bytes each; rows or k past the end read as zero.
+// Issue the global loads of one stage: rows of hidden (RB * 32 x 64 k) and of the head
+// (256 x 64 k), 16 bytes each; rows or k past the end read as zero.
 template <int RB>
-__device__ __forceinline__ void head_load(const HeadArgs& a, int r0, int v0, int k0, uint4 (&ra)[RB / 2],
-                                          uint4 (&rb)[4]) {
+__device__ __forceinline__ void head_load(const HeadArgs& a, int r0, int v0, int k0, uint4 (&ra)[RB],
+                                          uint4 (&rb)[8]) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < RB / 2; ++i) {
-    const int idx = t + kThreads * i, row = idx >> 2, k = k0 + 8 * (idx & 3);
+  for (int i = 0; i < RB; ++i) {
+    const int idx = t + kThreads * i, row = idx >> 3, k = k0 + 8 * (idx & 7);
     const int r = r0 + row;
     ra[i] = (r < a.R && k < a.D) ? *(const uint4*)((const uint16_t*)a.hidden + (int64_t)r * a.h_ld + k)
                                  : make_uint4(0u, 0u, 0u, 0u);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = t + kThreads * i, col = idx >> 2, k = k0 + 8 * (idx & 3);
+  for (int i = 0; i < 8; ++i) {
+    const int idx = t + kThreads * i, col = idx >> 3, k = k0 + 8 * (idx & 7);
     const int v = v0 + col;
     rb[i] = (v < a.V && k < a.D) ? *(const uint4*)((const uint16_t*)a.weight + (int64_t)v * a.w_ld + k)
                                  : make_uint4(0u, 0u, 0u, 0u);
   }
 }
 template <int RB>
-__device__ __forceinline__ void head_store(HeadLds<RB>& L, int buf, const uint4 (&ra)[RB / 2], const uint4 (&rb)[4]) {
+__device__ __forceinline__ void head_store(HeadLds<RB>& L, const uint4 (&ra)[RB], const uint4 (&rb)[8]) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < RB / 2; ++i) {
+  for (int i = 0; i < RB; ++i) {
     const int idx = t + kThreads * i;
-    *(uint4*)&L.k.a[buf][idx >> 2][8 * (idx & 3)] = ra[i];
+    *(uint4*)&L.k.a[idx >> 3][8 * (idx & 7)] = ra[i];
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const int idx = t + kThreads * i;
-    *(uint4*)&L.k.b[buf][idx >> 2][8 * (idx & 3)] = rb[i];
+    *(uint4*)&L.k.b[idx >> 3][8 * (idx & 7)] = rb[i];
   }
 }
 
@@ -100,30 +100,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(head_m
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  uint4 ra[RB / 2], rb[4];
+  // one LDS stage; the next stage's loads are in flight in registers while this one feeds the
+  // MFMAs, then land after a barrier
+  uint4 ra[RB], rb[8];
   const int n_k = (a.D + kHBK - 1) / kHBK;
   head_load<RB>(a, r0, v0, 0, ra, rb);
-  head_store<RB>(L, 0, ra, rb);
+  head_store<RB>(L, ra, rb);
   __syncthreads();
   const int fr = lane & 31, fk = 8 * (lane >> 5);
   for (int kt = 0; kt < n_k; ++kt) {
-    const int buf = kt & 1;
     if (kt + 1 < n_k) head_load<RB>(a, r0, v0, (kt + 1) * kHBK, ra, rb);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < kHBK / 16; ++h) {
       bf16x8 fa[RB], fb[2];
 #pragma unroll
-      for (int i = 0; i < RB; ++i) fa[i] = __builtin_bit_cast(bf16x8, *(const uint4*)&L.k.a[buf][32 * i + fr][16 * h + fk]);
+      for (int i = 0; i < RB; ++i) fa[i] = __builtin_bit_cast(bf16x8, *(const uint4*)&L.k.a[32 * i + fr][16 * h + fk]);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        fb[j] = __builtin_bit_cast(bf16x8, *(const uint4*)&L.k.b[buf][64 * wave + 32 * j + fr][16 * h + fk]);
+        fb[j] = __builtin_bit_cast(bf16x8, *(const uint4*)&L.k.b[64 * wave + 32 * j + fr][16 * h + fk]);
 #pragma unroll
       for (int i = 0; i < RB; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < n_k) head_store<RB>(L, buf ^ 1, ra, rb);
     __syncthreads();
+    if (kt + 1 < n_k) {
+      head_store<RB>(L, ra, rb);
+      __syncthreads();
+    }
   }
 
   // Epilogue: per 32-row block, the wave's 32 x 64 logits go to LDS by row; lanes 2i and
