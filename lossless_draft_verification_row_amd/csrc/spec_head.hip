@@ -28,8 +28,7 @@ template <int RB>   // 32-row blocks per workgroup
 struct HeadLds {
   union {
     struct {
-      uint16_t a[32 * RB][kHLd];      // hidden rows x k
-      uint16_t b[kHBV][kHLd];         // head rows (vocabulary) x k
+      uint16_t a[32 * RB][kHLd];      // hidden rows x k (the head goes to registers directly)
     } k;
     struct {
       float t[kWaves][32][kTLd];      // one wave's 32 x 64 logits, transposed to rows
@@ -38,11 +37,13 @@ struct HeadLds {
   };
 };
 
-// Issue the global loads of one stage: rows of hidden (RB * 32 x 64 k) and of the head
-// (256 x 64 k), 16 bytes each; rows or k past the end read as zero.
+// Issue the global loads of one stage: the workgroup's hidden rows (RB * 32 x 64 k, for LDS)
+// and this wave's B fragments of the head (its 64 columns x 64 k, straight into the MFMA
+// layout: fragment [j][h] of lane l is head row v0 + 64 wave + 32 j + l % 32, k 16 h + 8 (l / 32)
+// .. + 7), 16 bytes each; rows or k past the end read as zero.
 template <int RB>
 __device__ __forceinline__ void head_load(const HeadArgs& a, int r0, int v0, int k0, uint4 (&ra)[RB],
-                                          uint4 (&rb)[8]) {
+                                          uint4 (&fb)[2][kHBK / 16]) {
   const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
@@ -51,26 +52,25 @@ __device__ __forceinline__ void head_load(const HeadArgs& a, int r0, int v0, int
     ra[i] = (r < a.R && k < a.D) ? *(const uint4*)((const uint16_t*)a.hidden + (int64_t)r * a.h_ld + k)
                                  : make_uint4(0u, 0u, 0u, 0u);
   }
+  const int lane = t & 63, wave = t >> 6;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int idx = t + kThreads * i, col = idx >> 3, k = k0 + 8 * (idx & 7);
-    const int v = v0 + col;
-    rb[i] = (v < a.V && k < a.D) ? *(const uint4*)((const uint16_t*)a.weight + (int64_t)v * a.w_ld + k)
-                                 : make_uint4(0u, 0u, 0u, 0u);
+  for (int j = 0; j < 2; ++j) {
+    const int v = v0 + 64 * wave + 32 * j + (lane & 31);
+#pragma unroll
+    for (int h = 0; h < kHBK / 16; ++h) {
+      const int k = k0 + 16 * h + 8 * (lane >> 5);
+      fb[j][h] = (v < a.V && k < a.D) ? *(const uint4*)((const uint16_t*)a.weight + (int64_t)v * a.w_ld + k)
+                                      : make_uint4(0u, 0u, 0u, 0u);
+    }
   }
 }
 template <int RB>
-__device__ __forceinline__ void head_store(HeadLds<RB>& L, const uint4 (&ra)[RB], const uint4 (&rb)[8]) {
+__device__ __forceinline__ void head_store(HeadLds<RB>& L, const uint4 (&ra)[RB]) {
   const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
     const int idx = t + kThreads * i;
     *(uint4*)&L.k.a[idx >> 3][8 * (idx & 7)] = ra[i];
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int idx = t + kThreads * i;
-    *(uint4*)&L.k.b[idx >> 3][8 * (idx & 7)] = rb[i];
   }
 }
 
@@ -102,30 +102,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(head_m
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   // one LDS stage; the next stage's loads are in flight in registers while this one feeds the
   // MFMAs, then land after a barrier
-  uint4 ra[RB], rb[8];
+  uint4 ra[RB], fb[2][kHBK / 16], fbn[2][kHBK / 16];
   const int n_k = (a.D + kHBK - 1) / kHBK;
-  head_load<RB>(a, r0, v0, 0, ra, rb);
-  head_store<RB>(L, ra, rb);
+  head_load<RB>(a, r0, v0, 0, ra, fbn);
+  head_store<RB>(L, ra);
   __syncthreads();
   const int fr = lane & 31, fk = 8 * (lane >> 5);
   for (int kt = 0; kt < n_k; ++kt) {
-    if (kt + 1 < n_k) head_load<RB>(a, r0, v0, (kt + 1) * kHBK, ra, rb);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int h = 0; h < kHBK / 16; ++h) fb[j][h] = fbn[j][h];
+    if (kt + 1 < n_k) head_load<RB>(a, r0, v0, (kt + 1) * kHBK, ra, fbn);
 #pragma unroll
     for (int h = 0; h < kHBK / 16; ++h) {
-      bf16x8 fa[RB], fb[2];
+      bf16x8 fa[RB];
 #pragma unroll
       for (int i = 0; i < RB; ++i) fa[i] = __builtin_bit_cast(bf16x8, *(const uint4*)&L.k.a[32 * i + fr][16 * h + fk]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = __builtin_bit_cast(bf16x8, *(const uint4*)&L.k.b[64 * wave + 32 * j + fr][16 * h + fk]);
-#pragma unroll
       for (int i = 0; i < RB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], __builtin_bit_cast(bf16x8, fb[j][h]), acc[i][j],
+                                                              0, 0, 0);
     }
     __syncthreads();
     if (kt + 1 < n_k) {
-      head_store<RB>(L, ra, rb);
+      head_store<RB>(L, ra);
       __syncthreads();
     }
   }
