@@ -615,6 +615,8 @@ int spec_lm_head_row_stats(int R, int V, int D, const void* hidden, int64_t h_ld
   // 16-byte rows: D, the strides and the bases are whole multiples of eight bf16
   if (D % 8 != 0 || h_ld % 8 != 0 || w_ld % 8 != 0 || ((uintptr_t)hidden % 16) != 0 || ((uintptr_t)weight % 16) != 0)
     return SPEC_ERR_UNSUPPORTED;
+  // a tile's rows are addressed with 32-bit byte offsets (256 rows x stride x 2 B < 2^31)
+  if (h_ld > (1 << 21) || w_ld > (1 << 21)) return SPEC_ERR_UNSUPPORTED;
   const int64_t n_ct = ((int64_t)V + kHeadCols - 1) / kHeadCols;
   if ((int64_t)R * n_ct > (int64_t)INT32_MAX / 2) return SPEC_ERR_INVALID;
   const size_t need = spec_lm_head_workspace_bytes(R, V, D);

@@ -28,7 +28,8 @@ template <int RB>   // 32-row blocks per workgroup
 struct HeadLds {
   union {
     struct {
-      uint16_t a[32 * RB][kHLd];      // hidden rows x k (the head goes to registers directly)
+      alignas(16) uint16_t a[2][32 * RB][kHLd];   // hidden rows x k, double-buffered (the head
+                                                  // goes to registers directly)
     } k;
     struct {
       float t[kWaves][32][kTLd];      // one wave's 32 x 64 logits, transposed to rows
@@ -37,40 +38,44 @@ struct HeadLds {
   };
 };
 
+// 16 bytes through a buffer resource: an offset past its end reads as zero, with no branch.
+constexpr int kHeadOut = 0x7ffffff0;
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t rs, int off) {
+  const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 // Issue the global loads of one stage: the workgroup's hidden rows (RB * 32 x 64 k, for LDS)
 // and this wave's B fragments of the head (its 64 columns x 64 k, straight into the MFMA
 // layout: fragment [j][h] of lane l is head row v0 + 64 wave + 32 j + l % 32, k 16 h + 8 (l / 32)
-// .. + 7), 16 bytes each; rows or k past the end read as zero.
+// .. + 7), 16 bytes each.  The resources cover the tile's rows that exist; k past D gets an
+// offset past the end, so rows, columns and k outside the problem all read as zero.
 template <int RB>
-__device__ __forceinline__ void head_load(const HeadArgs& a, int r0, int v0, int k0, uint4 (&ra)[RB],
-                                          uint4 (&fb)[2][kHBK / 16]) {
-  const int t = threadIdx.x;
+__device__ __forceinline__ void head_load(const HeadArgs& a, __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb,
+                                          int k0, uint4 (&ra)[RB], uint4 (&fb)[2][kHBK / 16]) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
     const int idx = t + kThreads * i, row = idx >> 3, k = k0 + 8 * (idx & 7);
-    const int r = r0 + row;
-    ra[i] = (r < a.R && k < a.D) ? *(const uint4*)((const uint16_t*)a.hidden + (int64_t)r * a.h_ld + k)
-                                 : make_uint4(0u, 0u, 0u, 0u);
+    ra[i] = ld16(rsa, k < a.D ? (row * (int)a.h_ld + k) * 2 : kHeadOut);
   }
-  const int lane = t & 63, wave = t >> 6;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int v = v0 + 64 * wave + 32 * j + (lane & 31);
+    const int v = 64 * wave + 32 * j + (lane & 31);
 #pragma unroll
     for (int h = 0; h < kHBK / 16; ++h) {
       const int k = k0 + 16 * h + 8 * (lane >> 5);
-      fb[j][h] = (v < a.V && k < a.D) ? *(const uint4*)((const uint16_t*)a.weight + (int64_t)v * a.w_ld + k)
-                                      : make_uint4(0u, 0u, 0u, 0u);
+      fb[j][h] = ld16(rsb, k < a.D ? (v * (int)a.w_ld + k) * 2 : kHeadOut);
     }
   }
 }
 template <int RB>
-__device__ __forceinline__ void head_store(HeadLds<RB>& L, const uint4 (&ra)[RB]) {
+__device__ __forceinline__ void head_store(HeadLds<RB>& L, int buf, const uint4 (&ra)[RB]) {
   const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
     const int idx = t + kThreads * i;
-    *(uint4*)&L.k.a[idx >> 3][8 * (idx & 7)] = ra[i];
+    *(uint4*)&L.k.a[buf][idx >> 3][8 * (idx & 7)] = ra[i];
   }
 }
 
@@ -100,25 +105,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(head_m
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  // one LDS stage; the next stage's loads are in flight in registers while this one feeds the
-  // MFMAs, then land after a barrier
-  uint4 ra[RB], fb[2][kHBK / 16], fbn[2][kHBK / 16];
+  // two LDS stages; the next stage's loads are in flight in registers while this one feeds the
+  // MFMAs, then land in the other buffer (one barrier per stage).  The head fragments alternate
+  // between two register sets, two stages per trip.
+  const __amdgpu_buffer_rsrc_t rsa = row_rsrc((const uint16_t*)a.hidden + (int64_t)r0 * a.h_ld,
+                                             (int)(min(32 * RB, a.R - r0) * a.h_ld * 2));
+  const __amdgpu_buffer_rsrc_t rsb = row_rsrc((const uint16_t*)a.weight + (int64_t)v0 * a.w_ld,
+                                             (int)(min(kHBV, a.V - v0) * a.w_ld * 2));
+  uint4 ra[RB], fb0[2][kHBK / 16], fb1[2][kHBK / 16];
   const int n_k = (a.D + kHBK - 1) / kHBK;
-  head_load<RB>(a, r0, v0, 0, ra, fbn);
-  head_store<RB>(L, ra);
+  head_load<RB>(a, rsa, rsb, 0, ra, fb0);
+  head_store<RB>(L, 0, ra);
   __syncthreads();
   const int fr = lane & 31, fk = 8 * (lane >> 5);
-  for (int kt = 0; kt < n_k; ++kt) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int h = 0; h < kHBK / 16; ++h) fb[j][h] = fbn[j][h];
-    if (kt + 1 < n_k) head_load<RB>(a, r0, v0, (kt + 1) * kHBK, ra, fbn);
+  auto stage = [&](int kt, const uint4 (&fb)[2][kHBK / 16], uint4 (&fbn)[2][kHBK / 16]) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_k) head_load<RB>(a, rsa, rsb, (kt + 1) * kHBK, ra, fbn);
 #pragma unroll
     for (int h = 0; h < kHBK / 16; ++h) {
       bf16x8 fa[RB];
 #pragma unroll
-      for (int i = 0; i < RB; ++i) fa[i] = __builtin_bit_cast(bf16x8, *(const uint4*)&L.k.a[32 * i + fr][16 * h + fk]);
+      for (int i = 0; i < RB; ++i)
+        fa[i] = __builtin_bit_cast(bf16x8, *(const uint4*)&L.k.a[buf][32 * i + fr][16 * h + fk]);
 #pragma unroll
       for (int i = 0; i < RB; ++i)
 #pragma unroll
@@ -126,11 +134,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(head_m
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], __builtin_bit_cast(bf16x8, fb[j][h]), acc[i][j],
                                                               0, 0, 0);
     }
+    if (kt + 1 < n_k) head_store<RB>(L, buf ^ 1, ra);
     __syncthreads();
-    if (kt + 1 < n_k) {
-      head_store<RB>(L, ra);
-      __syncthreads();
-    }
+  };
+  for (int kt = 0; kt < n_k; kt += 2) {
+    stage(kt, fb0, fb1);
+    if (kt + 1 < n_k) stage(kt + 1, fb1, fb0);
   }
 
   // Epilogue: per 32-row block, the wave's 32 x 64 logits go to LDS by row; lanes 2i and
