@@ -172,8 +172,8 @@ def load_traffic(kernel):
             rec = json.load(f)
         import hashlib
         src = os.path.join(ROOT, "lossless_draft_verification_row_amd", "csrc",
-                           {"k_fused": "spec_fused.hip", "k_filt_slices": "spec_filter.hip"}.get(kernel,
-                                                                                               "spec_kernels.hip"))
+                           {"k_fused": "spec_fused.hip", "k_filt_slices": "spec_filter.hip",
+                            "k_head": "spec_head.hip"}.get(kernel, "spec_kernels.hip"))
         h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
         if rec.get("kernel_source_sha") != h:
             return None
@@ -219,6 +219,7 @@ def lm_head_bench(args, L, W, torch):
     lib.spec_set_profile_events(None, None)
     kms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
     flops = 2.0 * R * V * D
+    counters = load_traffic("k_head") or {}
     achieved = flops / (kms * 1e-3) / 1e12
     line = {
         "metric": "fused LM head rows/sec (row statistics and p(token) without materialised logits), 1 MI355X",
@@ -230,7 +231,8 @@ def lm_head_bench(args, L, W, torch):
                    "flops_per_step": flops, "head_bytes": V * D * 2, "head_copies_rotated": 2},
         "roofline": {"bound": "mfma", "kernel": "k_head (bf16 MFMA tiles with the row-statistics epilogue)",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "kernel_ms_avg": kms,
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": counters.get("bytes_per_launch"),
+                     "kernel_ms_avg": kms,
                      "head_read_GBps": V * D * 2 / (kms * 1e-3) / 1e9},
     }
     if not args.no_cpu_baseline:
