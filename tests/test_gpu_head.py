@@ -149,3 +149,34 @@ def test_head_full_vocabulary_sampled_rows():
     rows = np.array([0, 127, 128, 301, 511])
     ref, ap = oracle(h, w, 1.0, tok, rows=rows)
     check_bounded(gpu, ref, ap, D, 1.0, rows)
+
+
+@pytest.mark.parametrize("R,V,D", [(1, 5, 8), (3, 257, 24), (65, 300, 72), (2, 1, 16)])
+def test_head_small_and_ragged_shapes(R, V, D):
+    """Shapes at the edges of the tiling: a single row, fewer columns than a wave holds, one
+    column in the last tile, a single column, 65 rows (the tall tile with one row in its
+    second half), D not a multiple of the 64-deep stage."""
+    note(f"case head small R={R} V={V} D={D}")
+    h, w = W.head_inputs(R, V, D, seed=5 * R + V + D, exact=True)
+    tok = np.arange(R, dtype=np.int64) % max(V, 1)
+    for T in (1.0, 0.0):
+        gpu = run(h, w, T, tok)
+        ref, _ = oracle(h, w, T, tok)
+        check_exact(gpu, ref, np.arange(R))
+
+
+def test_head_strided_rows():
+    """Row strides larger than D (a view into wider buffers): the padding is never read."""
+    R, V, D, pad = 20, 900, 40, 24
+    h, w = W.head_inputs(R, V, D, seed=77, exact=True)
+    hb = np.full((R, D + pad), 0x7FC0, dtype=np.uint16)   # NaN padding: any read of it shows
+    wb = np.full((V, D + pad), 0x7FC0, dtype=np.uint16)
+    hb[:, :D] = h
+    wb[:, :D] = w
+    ht = torch.from_numpy(hb.view(np.int16)).view(torch.bfloat16).to(DEV)[:, :D]
+    wt = torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16).to(DEV)[:, :D]
+    res = L.spec_lm_head_row_stats(ht, wt, temperature=0.9)
+    torch.cuda.synchronize()
+    gpu = {k: v.cpu().numpy() for k, v in res.items()}
+    ref, _ = oracle(h, w, 0.9, None)
+    check_exact(gpu, ref, np.arange(R))
