@@ -21,7 +21,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kHBK = 64;         // k per stage
 constexpr int kHBV = kHeadCols;  // vocabulary columns per workgroup, 64 per wave
-constexpr int kHLd = kHBK + 8;   // LDS row stride in bf16 (80 B; 16-B aligned, staggers the banks)
+constexpr int kHLd = kHBK + 8;   // LDS row stride in bf16 (144 B: 16-B aligned, staggers the banks)
 constexpr int kTLd = 65;         // epilogue transpose row stride in floats
 
 template <int RB>   // 32-row blocks per workgroup
