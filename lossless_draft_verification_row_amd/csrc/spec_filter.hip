@@ -600,71 +600,98 @@ __global__ __launch_bounds__(kThreads) void k_filt_rows(FilterArgs a) {
       if (all || key_hi<NP>(order_key(c.v)) >= th) { L.kv[o] = c.v; L.kx[o] = c.x; ++o; }
     }
   }
-  if (t == 0) L.nk = nk;
   __syncthreads();
-  (void)lane;
+  // One wave finishes the row: the kept set (at most kKeepMax entries) is in LDS, and the steps
+  // below need only wave-wide reductions, so no barrier holds the other three waves.
+  if (t >= 64) return;
   RowStat2 st;
   st.n = 0; st.flags = L.flags; st.m = -INFINITY; st.argmax = -1; st.kept_finite = 0; st.pad = 0;
   st.log_z = 0.0; st.entropy = 0.0; st.max_prob = 0.0; st.z = 0.0;
   if (nk == 0 && !(st.flags & kFlagBad)) st.flags |= kFlagEmpty;
   if (st.flags) {
-    if (t == 0) a.rstat[slot] = st;
+    if (lane == 0) a.rstat[slot] = st;
     return;
   }
   // maximum (lowest index among equal maxima)
   float m = -INFINITY;
-  for (int j = t; j < nk; j += kThreads) m = fmaxf(m, L.kv[j]);
-  m = block_max(m, (float*)L.red);
+  for (int j = lane; j < nk; j += 64) m = fmaxf(m, L.kv[j]);
+  m = wave_max_dpp(m);
   int amx = INT_MAX;
-  for (int j = t; j < nk; j += kThreads) if (L.kv[j] == m) amx = min(amx, L.kx[j]);
-  amx = block_min_i(amx, (int*)L.red);
+  for (int j = lane; j < nk; j += 64) if (L.kv[j] == m) amx = min(amx, L.kx[j]);
+  amx = wave_min_i(amx);
   // e = exp((l - m) / T) in fp64; Z_K
   const double cd2 = (double)a.c;   // log2(e) / T
   double zk = 0.0;
-  for (int j = t; j < nk; j += kThreads) {
+  for (int j = lane; j < nk; j += 64) {
     const double e = exp2_split(((double)L.kv[j] - (double)m) * cd2);
     L.ke[j] = e;
     zk += e;
   }
-  __syncthreads();
-  zk = block_sum_dd(zk, L.red);
+  zk = wave_sum_dpp_d(zk);
+  __builtin_amdgcn_wave_barrier();
   // top-p: keep x iff the mass of values strictly above l_x is below top_p (the value group
-  // that first reaches top_p is kept whole; reading R1)
-  for (int j = t; j < nk; j += kThreads) {
+  // that first reaches top_p is kept whole; reading R1).  Up to 64 entries, one per lane, the
+  // others' values come by readlane; more, from LDS.
+  const bool small = nk <= 64;
+  if (small) {
+    const float lx = lane < nk ? L.kv[lane] : -INFINITY;
+    const double ex = lane < nk ? L.ke[lane] : 0.0;
     int keep = 1;
     if (a.top_p < 1.f) {
-      const float lx = L.kv[j];
       double above = 0.0;
-      for (int y = 0; y < nk; ++y) above += (L.kv[y] > lx) ? L.ke[y] : 0.0;
+      for (int y = 0; y < nk; ++y) {
+        const float ly = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lx), y));
+        const double ey = readlane_d(ex, y);
+        above += ly > lx ? ey : 0.0;
+      }
       keep = (above / zk < (double)a.top_p) ? 1 : 0;
     }
-    L.keep[j] = keep;
+    if (lane < nk) L.keep[lane] = keep;
+  } else {
+    for (int j = lane; j < nk; j += 64) {
+      int keep = 1;
+      if (a.top_p < 1.f) {
+        const float lx = L.kv[j];
+        double above = 0.0;
+        for (int y = 0; y < nk; ++y) above += (L.kv[y] > lx) ? L.ke[y] : 0.0;
+        keep = (above / zk < (double)a.top_p) ? 1 : 0;
+      }
+      L.keep[j] = keep;
+    }
   }
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();
   // Z_S, then p, entropy, the index order of S
   double zs = 0.0;
-  int ns_t = 0, nf_t = 0;
-  for (int j = t; j < nk; j += kThreads)
-    if (L.keep[j]) { zs += L.ke[j]; ++ns_t; nf_t += L.kv[j] > -INFINITY ? 1 : 0; }
-  zs = block_sum_dd(zs, L.red);
-  int ns = ns_t, nf = nf_t, ns_all, nf_all;
-  block_scan2(ns, nf, L.sel, ns_all, nf_all);
+  int ns_all = 0, nf_all = 0;
+  for (int j = lane; j < nk; j += 64)
+    if (L.keep[j]) { zs += L.ke[j]; ++ns_all; nf_all += L.kv[j] > -INFINITY ? 1 : 0; }
+  zs = wave_sum_dpp_d(zs);
+  ns_all = wave_sum_i(ns_all);
+  nf_all = wave_sum_i(nf_all);
   double ent = 0.0;
   KeptEntry* kept = a.kept + (int64_t)slot * kKeepMax;
-  for (int j = t; j < nk; j += kThreads) {
+  // (up to 64 entries) each lane's keep flag and index, for the rank by readlane
+  const int kp_l = small && lane < nk ? L.keep[lane] : 0;
+  const int kx_l = small && lane < nk ? L.kx[lane] : 0;
+  for (int j = lane; j < nk; j += 64) {
     if (!L.keep[j]) continue;
     const double p = L.ke[j] / zs;
     if (p > 0.0) ent -= p * log2_split(p);
     const int xj = L.kx[j];
     int rank = 0;
-    for (int y = 0; y < nk; ++y) rank += (L.keep[y] && L.kx[y] < xj) ? 1 : 0;
+    if (small) {
+      for (int y = 0; y < nk; ++y)
+        rank += (__builtin_amdgcn_readlane(kp_l, y) && __builtin_amdgcn_readlane(kx_l, y) < xj) ? 1 : 0;
+    } else {
+      for (int y = 0; y < nk; ++y) rank += (L.keep[y] && L.kx[y] < xj) ? 1 : 0;
+    }
     KeptEntry ke;
     ke.x = xj;
     ke.p = p;
     kept[rank] = ke;
   }
-  ent = block_sum_dd(ent, L.red);
-  if (t == 0) {
+  ent = wave_sum_dpp_d(ent);
+  if (lane == 0) {
     st.n = ns_all;
     st.kept_finite = nf_all;
     st.m = m;
