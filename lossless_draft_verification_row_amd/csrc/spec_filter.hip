@@ -711,7 +711,6 @@ struct FinFLds {
   int ytok[kMaxGamma];
   float dh[kMaxGamma], dm[kMaxGamma];
   double ap[kMaxGamma];                                   // accept probability per position
-  double chunk[kMaxSlicesFused];
   int pidx[kWaves][kKeepMax], qidx[kWaves][kKeepMax];   // a wave's kept token lists
   double w[kKeepMax];                                     // sampler weights of the chosen row
   int xs[kKeepMax];
@@ -730,73 +729,44 @@ __device__ __forceinline__ int find_idx(const int* ix, int n, int x) {
   return (lo < n && ix[lo] == x) ? lo : -1;
 }
 
-// First index whose running sum exceeds target (the last positive one if rounding leaves
-// none); sums run in the order given.
-template <typename Wt>
-__device__ __forceinline__ int seq_pick(int n, double target, Wt w) {
-  double cum = 0.0;
-  int last = -1;
-  for (int i = 0; i < n; ++i) {
-    const double wi = w(i);
-    cum += wi;
-    if (wi > 0.0) last = i;
-    if (cum > target) return i;
+// First position j in xs[0..n) (increasing) with xs[j] >= key.
+__device__ __forceinline__ int lower_bound_i(const int* xs, int n, int key) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (xs[mid] < key) lo = mid + 1;
+    else hi = mid;
   }
-  return last;
+  return lo;
 }
 
-// One thread: the three-level inverse CDF (reading R6: chunks of 4096, groups of 64, tokens)
-// over sparse weights wv[j] at increasing token indices xs[j], j < n; every mass is a
-// sequential fp64 sum in index order, empty groups add nothing.  chunk[] receives the n_s chunk
-// masses.  Returns the token (the last positive one where rounding leaves none), or -1 when the
-// total W is not positive.
-__device__ int sparse_sample(const int* xs, const double* wv, int n, int n_s, const double* u, double* chunk,
-                             double& W) {
-  int j = 0;
-  W = 0.0;
-  for (int k = 0; k < n_s; ++k) {
-    double Sk = 0.0;
-    while (j < n && (xs[j] >> 12) == k) {
-      const int grp = xs[j] >> 6;
-      double M = 0.0;
-      while (j < n && (xs[j] >> 6) == grp) { M += wv[j]; ++j; }
-      Sk += M;
-    }
-    chunk[k] = Sk;
-    W += Sk;
+// One wave: the three-level inverse CDF (reading R6: chunks of 4096, groups of 64, tokens) over
+// sparse weights wv[j] at increasing token indices xs[j], j < n (n_s <= 64 chunks).  Level 1:
+// lane k sums chunk k's weights in index order, then a wave-wide fp64 scan picks the chunk;
+// level 2: the same over the chunk's 64 groups; level 3: over the group's entries (at most 64).
+// Each pick takes the first running sum above u times the level's total, or the last positive
+// weight when rounding leaves none.  Every lane returns the token, or -1 with W <= 0 when the
+// total weight W is not positive.
+__device__ int sparse_sample_wave(const int* xs, const double* wv, int n, int n_s, const double* u, double& W) {
+  const int lane = threadIdx.x & 63;
+  double sk = 0.0;
+  if (lane < n_s) {
+    const int j1 = lower_bound_i(xs, n, (lane + 1) << 12);
+    for (int j = lower_bound_i(xs, n, lane << 12); j < j1; ++j) sk += wv[j];
   }
-  if (!(W > 0.0)) return -1;
-  const int kc = seq_pick(n_s, u[0] * W, [&](int k) { return chunk[k]; });
-  int j0 = 0;
-  while (j0 < n && (xs[j0] >> 12) < kc) ++j0;
-  int j1 = j0;
-  while (j1 < n && (xs[j1] >> 12) == kc) ++j1;
-  double Sg = 0.0;
-  for (int jj = j0; jj < j1;) {
-    const int grp = xs[jj] >> 6;
-    double M = 0.0;
-    while (jj < j1 && (xs[jj] >> 6) == grp) { M += wv[jj]; ++jj; }
-    Sg += M;
-  }
-  // level 2 over the chunk's groups, then level 3
-  const double t2 = u[1] * Sg;
-  double cum = 0.0;
-  int gj0 = -1, gj1 = -1, lj0 = -1, lj1 = -1;
-  for (int jj = j0; jj < j1;) {
-    const int grp = xs[jj] >> 6;
-    const int s0 = jj;
-    double M = 0.0;
-    while (jj < j1 && (xs[jj] >> 6) == grp) { M += wv[jj]; ++jj; }
-    cum += M;
-    if (M > 0.0) { lj0 = s0; lj1 = jj; }
-    if (cum > t2) { gj0 = s0; gj1 = jj; break; }
-  }
-  if (gj0 < 0) { gj0 = lj0; gj1 = lj1; }
-  if (gj0 < 0) return -1;
-  double Mg = 0.0;
-  for (int jj = gj0; jj < gj1; ++jj) Mg += wv[jj];
-  const int e = seq_pick(gj1 - gj0, u[2] * Mg, [&](int q) { return wv[gj0 + q]; });
-  return e >= 0 ? xs[gj0 + e] : -1;
+  const int kc = wave_pick(sk, n_s, u[0], W);
+  if (kc < 0) return -1;
+  const int key = ((kc << 6) + lane) << 6;
+  const int g0 = lower_bound_i(xs, n, key), g1 = lower_bound_i(xs, n, key + 64);
+  double mg = 0.0;
+  for (int j = g0; j < g1; ++j) mg += wv[j];
+  double tg;
+  const int gp = wave_pick(mg, 64, u[1], tg);
+  if (gp < 0) return -1;
+  const int a0 = __builtin_amdgcn_readlane(g0, gp), a1 = __builtin_amdgcn_readlane(g1, gp);
+  double te;
+  const int e = wave_pick(lane < a1 - a0 ? wv[a0 + lane] : 0.0, a1 - a0, u[2], te);
+  return e >= 0 ? xs[a0 + e] : -1;
 }
 
 template <int MODE>
@@ -1027,16 +997,18 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
         F.w[j] = w;
       }
       __syncthreads();
-      int again = 0;
-      if (t == 0) {
+      if (t < 64) {
         double W;
-        const int x = sparse_sample(F.xs, F.w, n, a.n_s, F.u, F.chunk, W);
-        if (!(W > 0.0)) {
-          if (wkind != 0) { F.status |= kStResidualEmpty; again = 1; }
-        } else {
-          F.x = x;
+        const int x = sparse_sample_wave(F.xs, F.w, n, a.n_s, F.u, W);
+        if (t == 0) {
+          int again = 0;
+          if (!(W > 0.0)) {
+            if (wkind != 0) { F.status |= kStResidualEmpty; again = 1; }
+          } else {
+            F.x = x;
+          }
+          red_i[0] = again;
         }
-        red_i[0] = again;
       }
       __syncthreads();
       if (!red_i[0]) break;
@@ -1118,10 +1090,8 @@ __global__ __launch_bounds__(kThreads) void k_filt_rowstats_out(FilterArgs a) {
 struct ResLds {
   int xs[kKeepMax], qx[kKeepMax];
   double w[kKeepMax];
-  double chunk[kMaxSlicesFused];
   double red[kWaves];
   double u[3];
-  int x;
 };
 
 // spec_residual_sample: one draw from r(x) = [p(x) - q(x)]_+ / beta over p's kept set (guide page
@@ -1183,12 +1153,15 @@ __global__ __launch_bounds__(kThreads) void k_filt_residual(FilterArgs a) {
     for (int j = t; j < n; j += kThreads) S.w[j] = kp[j].p;
     __syncthreads();
   }
-  if (t == 0) {
+  __syncthreads();
+  if (t < 64) {
     double W;
-    S.x = sparse_sample(S.xs, S.w, n, a.n_s, S.u, S.chunk, W);
-    a.out_tokens[r] = S.x;
-    if (a.out_mass) a.out_mass[r] = beta;
-    a.out_status[r] = status;
+    const int x = sparse_sample_wave(S.xs, S.w, n, a.n_s, S.u, W);
+    if (t == 0) {
+      a.out_tokens[r] = x;
+      if (a.out_mass) a.out_mass[r] = beta;
+      a.out_status[r] = status;
+    }
   }
 }
 
