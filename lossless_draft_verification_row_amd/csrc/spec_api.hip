@@ -87,7 +87,8 @@ size_t dense_bytes(int64_t n_slots, int V) {
 size_t fused_bytes(int64_t n_teams, int V) {
   const int64_t ns = n_chunks(V);
   return kHeaderBytes + align_up((size_t)(n_teams * ns * 2) * fused_record_bytes()) +
-         align_up((size_t)(n_teams * ns * 4) * sizeof(uint64_t)) + align_up((size_t)(n_teams * kMaxMembers) * 4);
+         align_up((size_t)(n_teams * ns * 4) * sizeof(uint64_t)) + align_up((size_t)(n_teams * kMaxMembers) * 4) +
+         align_up((size_t)n_teams * sizeof(int32_t));
 }
 
 // Tags of the fused kernel's workspace records: one per call, unique within the process,
@@ -345,6 +346,12 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
     f.part = cv.take<uint64_t>((size_t)f.n_teams * ns * 2 * fused_record_bytes());
     f.smass = cv.take<uint64_t>((size_t)f.n_teams * ns * 4 * sizeof(uint64_t));
     f.arrive = cv.take<uint32_t>((size_t)f.n_teams * kMaxMembers * sizeof(uint32_t));
+    {
+      // every request has G draft rows exactly when the rows number B G (a valid offset array
+      // has no request above G): then a team's rows follow from its place, else from a map
+      int32_t* map = cv.take<int32_t>((size_t)f.n_teams * sizeof(int32_t));
+      f.team_row = (int64_t)n_draft_rows == (int64_t)B * gamma_max ? nullptr : map;
+    }
     f.poll_delay = poll_delay_ticks();
     f.poll_pause = poll_pause();
     f.out_tokens = out_tokens;

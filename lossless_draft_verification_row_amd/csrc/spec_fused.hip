@@ -1047,7 +1047,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_
   int r = ti;   // target row
   bool pair = false;
   int drow = -1;
-  if (MODE == kFuSample) {
+  if (MODE == kFuSample && a.team_row) {
+    // a ragged batch: the row of this dispatch place comes from the map (an invalid offset
+    // array, which the finalize kernel reports, can only give rows that are range-checked here)
+    r = sload_i32(a.team_row + ti);
+    if (r < 0 || r >= a.n_teams) return;
+    pair = ti < a.n_draft_rows;
+    drow = pair ? ti : -1;
+    if (VEC) {
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V * kEsz);
+      load_raw_buf<DT>(rs, base, rp[0]);
+      load_raw_buf<DT>(rs, base + kChunk, rp[1]);
+      if (pair) {
+        const __amdgpu_buffer_rsrc_t rd = row_rsrc(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V * kEsz);
+        load_raw_buf<DT>(rd, base, rq[0]);
+        load_raw_buf<DT>(rd, base + kChunk, rq[1]);
+      }
+    } else {
+      load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, base, rp[0]);
+      load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, base + kChunk, rp[1]);
+      if (pair) {
+        load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base, rq[0]);
+        load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base + kChunk, rq[1]);
+      }
+    }
+  } else if (MODE == kFuSample) {
     // Dispatch order: every paired position first (draft row d = ti, target row d + b for its
     // request b), then each request's bonus row (ti = n_draft_rows + b, target row
     // cu[b + 1] + b).  Bonus rows have no draft row and no team wait, so the kernel's last
@@ -1275,6 +1299,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_
   }
 }
 
+// The target row of every dispatch place of a ragged batch: places 0 .. n_draft_rows - 1 are
+// the draft rows (row d of request b pairs with target row d + b), then one place per request
+// for its bonus row (cu[b + 1] + b).  An offset pair that is not a valid range writes nothing.
+__global__ __launch_bounds__(kThreads) void k_team_map(FusedArgs a) {
+  const int b = blockIdx.x * kThreads + threadIdx.x;
+  if (b >= a.B) return;
+  const int c0 = a.cu[b], c1 = a.cu[b + 1];
+  if (c0 < 0 || c1 < c0 || c1 > a.n_draft_rows || c1 - c0 > a.G) return;
+  for (int d = c0; d < c1; ++d) a.team_row[d] = d + b;
+  a.team_row[a.n_draft_rows + b] = c1 + b;
+}
+
 // One workgroup per request, after the streaming kernel: every record is in place.
 template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void k_fused_finalize(FusedArgs a) {
@@ -1291,6 +1327,11 @@ static hipError_t launch_fused_t(FusedArgs a, hipStream_t st, hipEvent_t ev0, hi
   if (grid < 1 || grid > 0x7fffffffll) return hipErrorInvalidConfiguration;
   if (getenv("SPEC_VERIFY_DEBUG"))
     fprintf(stderr, "[specverify] fused grid %lld tickets %d slices %d mode %d\n", grid, a.n_tickets, a.n_s, a.mode);
+  if (MODE == kFuSample && a.team_row) {
+    hipLaunchKernelGGL(k_team_map, dim3((unsigned)((a.B + kThreads - 1) / kThreads)), dim3(kThreads), 0, st, a);
+    const hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
   // optional events bracket the streaming kernel alone (benchmark timing)
   if (MODE != kFuGreedy && a.want_t_ent)
     launch_timed(k_fused<DT, VEC, MODE, true>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
