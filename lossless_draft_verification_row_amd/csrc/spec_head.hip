@@ -20,20 +20,23 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kHBK = 64;         // k per stage
-constexpr int kHBV = kHeadCols;  // vocabulary columns per workgroup, 64 per wave
-constexpr int kHLd = kHBK + 8;   // LDS row stride in bf16 (144 B: 16-B aligned, staggers the banks)
-constexpr int kTLd = 65;         // epilogue transpose row stride in floats
+constexpr int kHBV = kHeadCols;      // vocabulary columns per workgroup
+constexpr int kWC = kHBV / kWaves;   // columns per wave
+constexpr int kNJ = kWC / 32;        // 32-column accumulator blocks per wave
+constexpr int kHLd = kHBK + 8;       // LDS row stride in bf16 (144 B: 16-B aligned, staggers the banks)
+constexpr int kTLd = kWC + 1;        // epilogue transpose row stride in floats
+static_assert(kNJ >= 1 && kWC % 32 == 0, "each wave takes whole 32-column blocks");
 
 template <int RB>   // 32-row blocks per workgroup
 struct HeadLds {
   union {
     struct {
-      alignas(16) uint16_t a[2][32 * RB][kHLd];   // hidden rows x k, double-buffered (the head
-                                                  // goes to registers directly)
+      alignas(16) uint16_t a[32 * RB][kHLd];   // hidden rows x k of the current stage
+      alignas(16) uint16_t b[kHBV][kHLd];      // head rows (vocabulary columns) x k
     } k;
     struct {
-      float t[kWaves][32][kTLd];      // one wave's 32 x 64 logits, transposed to rows
-      HeadRec part[kWaves][32 * RB];  // per wave: the partials of each row over its 64 columns
+      float t[kWaves][32][kTLd];      // one wave's 32 x kWC logits, transposed to rows
+      HeadRec part[kWaves][32 * RB];  // per wave: the partials of each row over its columns
     } e;
   };
 };
@@ -45,47 +48,47 @@ __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t rs, int off) {
   return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
-// Issue the global loads of one stage: the workgroup's hidden rows (RB * 32 x 64 k, for LDS)
-// and this wave's B fragments of the head (its 64 columns x 64 k, straight into the MFMA
-// layout: fragment [j][h] of lane l is head row v0 + 64 wave + 32 j + l % 32, k 16 h + 8 (l / 32)
-// .. + 7), 16 bytes each.  The resources cover the tile's rows that exist; k past D gets an
+// Issue the global loads of one stage: the workgroup's hidden rows (32 RB x 64 k) and head
+// rows (256 x 64 k), eight lanes per row and 16 bytes per lane, so every row's 128 bytes come
+// in one coalesced piece.  The resources cover the tile's rows that exist; k past D gets an
 // offset past the end, so rows, columns and k outside the problem all read as zero.
 template <int RB>
 __device__ __forceinline__ void head_load(const HeadArgs& a, __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb,
-                                          int k0, uint4 (&ra)[RB], uint4 (&fb)[2][kHBK / 16]) {
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+                                          int k0, uint4 (&ra)[RB], uint4 (&rb)[kHBV / 32]) {
+  const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
     const int idx = t + kThreads * i, row = idx >> 3, k = k0 + 8 * (idx & 7);
     ra[i] = ld16(rsa, k < a.D ? (row * (int)a.h_ld + k) * 2 : kHeadOut);
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int v = 64 * wave + 32 * j + (lane & 31);
-#pragma unroll
-    for (int h = 0; h < kHBK / 16; ++h) {
-      const int k = k0 + 16 * h + 8 * (lane >> 5);
-      fb[j][h] = ld16(rsb, k < a.D ? (v * (int)a.w_ld + k) * 2 : kHeadOut);
-    }
+  for (int i = 0; i < kHBV / 32; ++i) {
+    const int idx = t + kThreads * i, row = idx >> 3, k = k0 + 8 * (idx & 7);
+    rb[i] = ld16(rsb, k < a.D ? (row * (int)a.w_ld + k) * 2 : kHeadOut);
   }
 }
 template <int RB>
-__device__ __forceinline__ void head_store(HeadLds<RB>& L, int buf, const uint4 (&ra)[RB]) {
+__device__ __forceinline__ void head_store(HeadLds<RB>& L, const uint4 (&ra)[RB], const uint4 (&rb)[kHBV / 32]) {
   const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
     const int idx = t + kThreads * i;
-    *(uint4*)&L.k.a[buf][idx >> 3][8 * (idx & 7)] = ra[i];
+    *(uint4*)&L.k.a[idx >> 3][8 * (idx & 7)] = ra[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kHBV / 32; ++i) {
+    const int idx = t + kThreads * i;
+    *(uint4*)&L.k.b[idx >> 3][8 * (idx & 7)] = rb[i];
   }
 }
 
-// Two waves per SIMD for the tall tile (its accumulators and fragments take up to 256
-// registers).
+// Two waves per SIMD for the tall tile (its accumulators, staged loads and fragments take up
+// to 256 registers; two workgroups share a CU's LDS).
 constexpr int head_min_waves(int rb) { return rb == 4 ? 2 : 1; }
 
-// One workgroup per (32 RB rows) x (256 columns) tile.  Wave w holds columns 64w .. 64w + 63
-// of every row in RB x 2 accumulators of the 32x32x16 bf16 MFMA: A[i][k] is lane i + 32 (k / 8)
-// element k % 8, B[k][j] lane j + 32 (k / 8), and C[i][j] lane j + 32 ((i / 4) % 2) element
+// One workgroup per (32 RB rows) x (kHBV columns) tile.  Wave w holds columns kWC w ..
+// kWC (w + 1) - 1 of every row in RB x kNJ accumulators of the 32x32x16 bf16 MFMA: A[i][k] is
+// lane i + 32 (k / 8) element k % 8, B[k][j] lane j + 32 (k / 8), and C[i][j] lane j + 32 ((i / 4) % 2) element
 // 4 (i / 8) + i % 4.  Workgroup i runs on XCD i mod 8; the row tiles of one column tile go to
 // consecutive workgroups of one XCD, so its L2 serves the head tile they share (and the hidden
 // tiles, shared by every column tile).
@@ -98,59 +101,64 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(head_m
   const int rt = jx % a.n_rt, ct = (jx / a.n_rt) * 8 + xcd;
   if (ct >= a.n_ct) return;
   const int r0 = rt * 32 * RB, v0 = ct * kHBV;
-  f32x16 acc[RB][2];
+  f32x16 acc[RB][kNJ];
 #pragma unroll
   for (int i = 0; i < RB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kNJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  // two LDS stages; the next stage's loads are in flight in registers while this one feeds the
-  // MFMAs, then land in the other buffer (one barrier per stage).  The head fragments alternate
-  // between two register sets, two stages per trip.
+  // One LDS stage: the next stage's loads are in flight in registers while this one feeds the
+  // MFMAs, then replace it between two barriers.  A and B fragments are read from LDS in the
+  // MFMA layout (lane l: row l % 32 of its block, k 8 (l / 32) .. + 7 of each 16).
   const __amdgpu_buffer_rsrc_t rsa = row_rsrc((const uint16_t*)a.hidden + (int64_t)r0 * a.h_ld,
                                              (int)(min(32 * RB, a.R - r0) * a.h_ld * 2));
   const __amdgpu_buffer_rsrc_t rsb = row_rsrc((const uint16_t*)a.weight + (int64_t)v0 * a.w_ld,
                                              (int)(min(kHBV, a.V - v0) * a.w_ld * 2));
-  uint4 ra[RB], fb0[2][kHBK / 16], fb1[2][kHBK / 16];
+  uint4 ra[RB], rb[kHBV / 32];
   const int n_k = (a.D + kHBK - 1) / kHBK;
-  head_load<RB>(a, rsa, rsb, 0, ra, fb0);
-  head_store<RB>(L, 0, ra);
+  head_load<RB>(a, rsa, rsb, 0, ra, rb);
+  head_store<RB>(L, ra, rb);
   __syncthreads();
   const int fr = lane & 31, fk = 8 * (lane >> 5);
-  auto stage = [&](int kt, const uint4 (&fb)[2][kHBK / 16], uint4 (&fbn)[2][kHBK / 16]) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_k) head_load<RB>(a, rsa, rsb, (kt + 1) * kHBK, ra, fbn);
+  for (int kt = 0; kt < n_k; ++kt) {
+    const bool more = kt + 1 < n_k;
+    if (more) head_load<RB>(a, rsa, rsb, (kt + 1) * kHBK, ra, rb);
+    // the MFMA stretch at raised priority: a SIMD shared with the other workgroup keeps
+    // issuing matrix work while that one is between its barriers
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int h = 0; h < kHBK / 16; ++h) {
-      bf16x8 fa[RB];
+      bf16x8 fa[RB], fv[kNJ];
 #pragma unroll
       for (int i = 0; i < RB; ++i)
-        fa[i] = __builtin_bit_cast(bf16x8, *(const uint4*)&L.k.a[buf][32 * i + fr][16 * h + fk]);
+        fa[i] = __builtin_bit_cast(bf16x8, *(const uint4*)&L.k.a[32 * i + fr][16 * h + fk]);
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j)
+        fv[j] = __builtin_bit_cast(bf16x8, *(const uint4*)&L.k.b[kWC * wave + 32 * j + fr][16 * h + fk]);
 #pragma unroll
       for (int i = 0; i < RB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], __builtin_bit_cast(bf16x8, fb[j][h]), acc[i][j],
-                                                              0, 0, 0);
+        for (int j = 0; j < kNJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fv[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < n_k) head_store<RB>(L, buf ^ 1, ra);
-    __syncthreads();
-  };
-  for (int kt = 0; kt < n_k; kt += 2) {
-    stage(kt, fb0, fb1);
-    if (kt + 1 < n_k) stage(kt + 1, fb1, fb0);
+    __builtin_amdgcn_s_setprio(0);
+    __syncthreads();   // every wave is done with this stage (and, after the last, with L.k)
+    if (more) {
+      head_store<RB>(L, ra, rb);
+      __syncthreads();
+    }
   }
 
-  // Epilogue: per 32-row block, the wave's 32 x 64 logits go to LDS by row; lanes 2i and
-  // 2i + 1 take row i, 32 columns each.
+  // Epilogue: per 32-row block, the wave's 32 x kWC logits go to LDS by row; lanes 2i and
+  // 2i + 1 take row i, kWC / 2 columns each.
   const float c = a.c;
-  const int cw0 = v0 + 64 * wave;   // this wave's first column
+  const int cw0 = v0 + kWC * wave;   // this wave's first column
   const int hf = lane & 1, ri = lane >> 1;
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kNJ; ++j) {
       const int col = 32 * j + (lane & 31);
       const bool in = cw0 + col < a.V;
 #pragma unroll
@@ -160,22 +168,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(head_m
       }
     }
     __syncthreads();
-    const float* x = &L.e.t[wave][ri][32 * hf];
+    const float* x = &L.e.t[wave][ri][kWC / 2 * hf];
     const int r = r0 + 32 * i + ri;
     // the token's logit, from the one lane whose columns hold it
     if (a.tokens && r < a.R) {
-      const int y = a.tokens[r] - (cw0 + 32 * hf);
-      if (y >= 0 && y < 32 && cw0 + 32 * hf + y < a.V) a.ly[r] = x[y];
+      const int y = a.tokens[r] - (cw0 + kWC / 2 * hf);
+      if (y >= 0 && y < kWC / 2 && cw0 + kWC / 2 * hf + y < a.V) a.ly[r] = x[y];
     }
     float m = -INFINITY;
     int am = INT_MAX, bad = 0;
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
+    for (int q = 0; q < kWC / 2; ++q) {
       const float v = x[q];
       bad |= (v != v || v == INFINITY) ? 1 : 0;
       if (v > m) { m = v; am = q; }
     }
-    am = m > -INFINITY ? cw0 + 32 * hf + am : INT_MAX;
+    am = m > -INFINITY ? cw0 + kWC / 2 * hf + am : INT_MAX;
     // the partner lane holds the row's other 32 columns
     const float m2 = __shfl_xor(m, 1);
     const int am2 = __shfl_xor(am, 1);
@@ -188,7 +196,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(head_m
     double s = 0.0, w = 0.0;
     if (!a.greedy && M > -INFINITY) {
 #pragma unroll
-      for (int q = 0; q < 32; ++q) {
+      for (int q = 0; q < kWC / 2; ++q) {
         const float tt = (x[q] - M) * c;
         const float ev = __builtin_amdgcn_exp2f(tt);
         s += (double)ev;
