@@ -62,6 +62,32 @@ def copy_reference(steps):
     print(json.dumps({"copy_reference": res, "peak_GBps": HBM_PEAK_GBS}), flush=True)
 
 
+def stream_ceiling(torch, L, lib, steps=20):
+    """Context for the roofline: the library's plain streaming-read kernel (spec_stream_read)
+    over 1 GiB on the same GPU, after the timed region, timed with HIP events around each
+    launch; GB/s and the fraction of the HBM peak."""
+    nbytes = 1 << 30
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        L.spec_stream_read(buf, sink)
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in pairs:
+        lib.spec_set_profile_events(a, b)
+        L.spec_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    lib.spec_set_profile_events(None, None)
+    ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    del buf
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "k_stream_read (spec_stream_read) over 1 GiB", "GBps": gbs, "frac": gbs / HBM_PEAK_GBS}
+
+
 class HipEvents:
     """Raw hipEvent_t pairs (the library records them on the stream its kernels run on)."""
 
@@ -390,8 +416,11 @@ def main():
                    "status_nonzero_requests": int((st != 0).sum())},
         "roofline": {"bound": "hbm", "kernel": kernel_name,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "kernel_ms_avg": kern_avg_s * 1e3, "valu_issue_frac": valu_frac},
+                     "traffic": traffic, "kernel_ms_avg": kern_avg_s * 1e3,
+                     "kernel_ms_p10_p50_p90": [float(x) for x in np.percentile(kernel_ms, [10, 50, 90])],
+                     "valu_issue_frac": valu_frac},
     }
+    line["stream_ceiling"] = stream_ceiling(torch, L, lib)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)

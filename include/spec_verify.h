@@ -240,6 +240,16 @@ int spec_select_gamma(int B, const float* req_stats, const float* comp, spec_gam
  * the events stay owned by the caller.  Returns SPEC_ERR_INVALID if only one is NULL. */
 int spec_set_profile_events(void* start_event, void* stop_event);
 
+/* Benchmark instrumentation, not a verification step: a plain streaming read of `bytes` bytes of
+ * device memory at `buf` (16-byte aligned, `bytes` a multiple of 16), the practical HBM read
+ * ceiling that a benchmark reports beside the streaming kernel's bandwidth.  `sink` is a device
+ * pointer to one uint32_t that the kernel writes only when the XOR of all words equals a fixed
+ * value (it keeps the reads from being dropped).  Profile events, when set, bracket this kernel
+ * too.  Stream-ordered; nothing is allocated.  Returns SPEC_OK (also for bytes == 0),
+ * SPEC_ERR_INVALID (bytes < 0, a NULL pointer), SPEC_ERR_UNSUPPORTED (alignment) or
+ * SPEC_ERR_LAUNCH. */
+int spec_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* hip_stream);
+
 /* Test hook: the fused kernel's bounded wait for a team gives up after `polls` polls and
  * reports SPEC_STATUS_TIMEOUT for the request (0 = give up at the first incomplete poll).
  * Process-wide; the default is 262144. */

@@ -88,6 +88,8 @@ def load_library():
     lib.spec_set_spin_limit.argtypes = [ctypes.c_uint]
     lib.spec_set_profile_events.restype = i32
     lib.spec_set_profile_events.argtypes = [vp, vp]
+    lib.spec_stream_read.restype = i32
+    lib.spec_stream_read.argtypes = [vp, i64, vp, vp]
     lib.spec_status_string.restype = ctypes.c_char_p
     lib.spec_status_string.argtypes = [i32]
     _LIB = lib
@@ -270,6 +272,16 @@ def spec_residual_sample(p_logits, q_logits=None, *, temperature=1.0, top_k=0, t
                                   wp, wn, _stream(stream))
     _check(rc, "spec_residual_sample")
     return o
+
+
+def spec_stream_read(buf, sink, stream=None):
+    """A plain streaming read of a CUDA tensor's bytes (the benchmark's HBM read ceiling); `sink`
+    is a one-element int32 CUDA tensor the kernel may write."""
+    if not (buf.is_cuda and buf.is_contiguous() and sink.is_cuda and sink.dtype == torch.int32 and sink.numel() >= 1):
+        raise ValueError("buf must be a contiguous CUDA tensor and sink a CUDA int32 tensor")
+    nbytes = buf.numel() * buf.element_size()
+    rc = load_library().spec_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream))
+    _check(rc, "spec_stream_read")
 
 
 def spec_select_gamma(req_stats, w1, b1, w2, b2, comp=None, stream=None):

@@ -666,4 +666,12 @@ int spec_select_gamma(int B, const float* req_stats, const float* comp, spec_gam
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
 }
 
+int spec_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* hip_stream) {
+  if (bytes < 0 || (bytes > 0 && !buf) || !sink) return SPEC_ERR_INVALID;
+  if (bytes % 16 != 0 || ((uintptr_t)buf & 15u) != 0) return SPEC_ERR_UNSUPPORTED;
+  if (bytes == 0) return SPEC_OK;
+  const hipError_t e = launch_stream_read(buf, bytes / 16, sink, (hipStream_t)hip_stream, g_prof_start, g_prof_stop);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -228,6 +228,8 @@ hipError_t launch_finalize(const FinalizeArgs& a, int dt, hipStream_t st);
 hipError_t launch_select_gamma(int B, const float* req_stats, const float* comp, const float* w1, const float* b1,
                                const float* w2, float b2, int32_t* out_gamma, float* out_expected, hipStream_t st);
 hipError_t launch_residual_finalize(const ResidualArgs& a, int dt, hipStream_t st);
+hipError_t launch_stream_read(const void* buf, int64_t n16, uint32_t* sink, hipStream_t st, hipEvent_t ev0,
+                              hipEvent_t ev1);
 
 // ---------------------------------------------------------------- fused LM head
 

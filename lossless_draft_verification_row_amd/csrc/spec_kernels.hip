@@ -1114,6 +1114,36 @@ hipError_t launch_select_gamma(int B, const float* req_stats, const float* comp,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- streaming-read ceiling
+
+// A plain read of n 16-byte words, for the benchmark's roofline context: workgroup g reads the
+// 64 KB chunk g, every thread 16 words 256 apart, all in flight at once, and XORs them.  The
+// XOR is stored only when it equals a fixed word, so the loads cannot be dropped while the
+// kernel writes next to nothing.
+constexpr int kStreamLoads = 16;
+constexpr int kStreamChunkWords = kStreamLoads * kThreads;   // 64 KB
+__global__ __launch_bounds__(kThreads) void k_stream_read(const uint4* __restrict__ p, int64_t n, uint32_t* sink) {
+  const int64_t base = (int64_t)blockIdx.x * kStreamChunkWords + threadIdx.x;
+  uint4 v[kStreamLoads];
+#pragma unroll
+  for (int k = 0; k < kStreamLoads; ++k) {
+    const int64_t i = base + (int64_t)k * kThreads;
+    v[k] = i < n ? p[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  uint32_t x = 0;
+#pragma unroll
+  for (int k = 0; k < kStreamLoads; ++k) x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  if (x == 0x9e3779b9u) sink[0] = x;
+}
+
+hipError_t launch_stream_read(const void* buf, int64_t n16, uint32_t* sink, hipStream_t st, hipEvent_t ev0,
+                              hipEvent_t ev1) {
+  const int64_t n_chunks = (n16 + kStreamChunkWords - 1) / kStreamChunkWords;
+  if (n_chunks > 0x7fffffffll) return hipErrorInvalidConfiguration;
+  launch_timed(k_stream_read, dim3((unsigned)n_chunks), dim3(kThreads), st, ev0, ev1, (const uint4*)buf, n16, sink);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launchers
 
 template <int DT>

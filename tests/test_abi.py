@@ -115,3 +115,13 @@ def test_lm_head_argument_checks_without_gpu():
     # undersized workspace
     assert lib.spec_lm_head_row_stats(4, 100, 64, 16, 64, 16, 64, sp, None, *outs, 256, 16, None) == -3
     assert lib.spec_lm_head_workspace_bytes(4, 100, 64) > 4 * 24
+
+
+def test_stream_read_argument_checks_without_gpu():
+    lib = L.load_library()
+    assert lib.spec_stream_read(None, 0, 16, None) == 0            # nothing to read
+    assert lib.spec_stream_read(16, -16, 16, None) == -1           # negative size
+    assert lib.spec_stream_read(None, 32, 16, None) == -1          # no buffer
+    assert lib.spec_stream_read(16, 32, None, None) == -1          # no sink
+    assert lib.spec_stream_read(16, 24, 16, None) == -2            # not whole 16-byte words
+    assert lib.spec_stream_read(8, 32, 16, None) == -2             # misaligned buffer

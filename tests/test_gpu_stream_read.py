@@ -1,0 +1,34 @@
+"""The streaming-read ceiling kernel (benchmark instrumentation): it reads every 16-byte word,
+ragged tails included, and writes its sink only when the XOR of all words is the fixed word."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import lossless_draft_verification_row_amd as L
+
+pytestmark = pytest.mark.gpu
+MAGIC = 0x9E3779B9
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("words", [1, 255, 4096, 4097, 6 * 4096 * 1024 + 17])
+@pytest.mark.parametrize("where", ["first", "last"])
+def test_stream_read_sees_every_word(words, where):
+    note(f"case stream_read words={words} where={where}")
+    host = np.zeros(words * 4, dtype=np.uint32)
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    L.spec_stream_read(buf, sink)          # all zero: the XOR is 0, the sink keeps its value
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
+    host[0 if where == "first" else 4 * words - 1] = MAGIC
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    L.spec_stream_read(buf, sink)          # one word carries the pattern: the sink is written
+    torch.cuda.synchronize()
+    assert int(sink.item()) & 0xFFFFFFFF == MAGIC
