@@ -60,8 +60,15 @@ struct FinScratch {
   double ap[kMaxGamma];          // accept probability of every position
   float wsel[kGroup];
   double u[3];
+  double red[kWaves];
+  unsigned long long lowm;       // positions whose overlap 1 - beta is below kLowOverlap
   int flags, status, n_acc, pos, wkind, y, kpick, gpick, xpick;
 };
+
+// Below this overlap A = 1 - beta, the finalize sums min(p, q) over the two rows directly: beta
+// carries an absolute error near 1e-7, which 1 - beta would turn into a relative error above
+// 1e-5 for A under about 1e-2; the direct sum keeps the relative precision of its terms.
+constexpr double kLowOverlap = 0.02;
 
 struct LdsFin {
   int cu[kMaxReqFused + 1];
@@ -388,7 +395,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   __syncthreads();
 
   // B. per position: statistics, p(y), q(y), the accept draw
-  bool rej = false;
+  bool rej = false, low = false;
   int why = 0;
   if (t <= g) {
     const int r = c0 + b + t;
@@ -430,6 +437,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
           }
           if (okp && okq) {
             ovl = (float)(1.0 - T.beta);
+            low = 1.0 - T.beta < kLowOverlap;
             l1 = (float)(2.0 * T.beta);
             ap = (yv && qyd > 0.0) ? fmin(1.0, pyd / qyd) : 0.0;
           }
@@ -439,7 +447,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       }
       if (a.st.p_y) a.st.p_y[drow] = py;
       if (a.st.q_y) a.st.q_y[drow] = qy;
-      if (a.st.one_minus_tv) a.st.one_minus_tv[drow] = ovl;
+      if (a.st.one_minus_tv && !low) a.st.one_minus_tv[drow] = ovl;
       if (a.st.draft_entropy_bits) a.st.draft_entropy_bits[drow] = dh;
       if (a.st.draft_max_prob) a.st.draft_max_prob[drow] = dm;
       if (a.st.l1) a.st.l1[drow] = l1;
@@ -464,6 +472,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
     if (lane == 0 && g >= 64) fl |= F.team[64].flags;
     fl = wave_or(fl);
     const unsigned long long rm = __ballot(rej);
+    const unsigned long long lm = __ballot(low);
     const int j = rm ? __builtin_ctzll(rm) : -1;
     const int whyj = j >= 0 ? __builtin_amdgcn_readlane(why, j) : 0;
     if (lane == 0) {
@@ -483,6 +492,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       F.u[2] = F.us[F.pos][2];
       F.status = status;
       F.kpick = -1;
+      F.lowm = lm;
       if (a.st.expected_committed)
         a.st.expected_committed[b] = fl ? nan : expected_committed(F.ap, g);
       if (a.out_req_stats) {
@@ -504,6 +514,32 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
     }
   }
   __syncthreads();
+
+  // low-overlap positions: A = sum_x min(p, q) over the two rows, re-read (guide §4.1 / §4.3:
+  // A = sum min(p, q) = 1 - TV), with p = 2^(l c - M_p) / Z_p in fp32 and the sum in fp64
+  if (MODE == kFuSample && a.st.one_minus_tv) {
+    unsigned long long lm = F.lowm;
+    while (lm) {
+      const int i = __builtin_ctzll(lm);
+      lm &= lm - 1;
+      const TeamL T = F.team[i];
+      const float ip = (float)(1.0 / T.z[0]), iq = (float)(1.0 / T.z[1]);
+      const void* prow = row_ptr<DT>(a.tgt, a.tgt_ld, c0 + b + i);
+      const void* qrow = row_ptr<DT>(a.drf, a.drf_ld, c0 + i);
+      float acc = 0.f;
+      for (int x0 = t * 16; x0 < a.V; x0 += kThreads * 16) {
+        float vp[16], vq[16];
+        load_run16<DT, VEC>(prow, a.V, x0, vp);
+        load_run16<DT, VEC>(qrow, a.V, x0, vq);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          acc += fminf(__builtin_amdgcn_exp2f(fmaf(vp[e], a.c, -T.M[0])) * ip,
+                       __builtin_amdgcn_exp2f(fmaf(vq[e], a.c, -T.M[1])) * iq);
+      }
+      const double A = block_sum_d((double)acc, F.red);
+      if (t == 0) a.st.one_minus_tv[c0 + i] = (float)A;
+    }
+  }
 
   int x = -1;
   if (F.status & (kStTimeout | kStNonfinite)) {
@@ -903,11 +939,22 @@ __device__ __forceinline__ void fold_waves_rt(const float (*pw)[4], int K, bool 
 }
 
 // Team normalisers from the team's records (lane s holds slice s): M = max_s ref_s and
-// Z = sum_s s_s 2^(ref_s - M) for each row, in fp32 with a fixed-order tree sum.  Status 0 ok,
-// 1 a row non-finite or empty, 2 the wait gave up.
+// Z = sum_s s_s 2^(ref_s - M) for each row.  The residual's scale factors depend on the ratio
+// of the two rows' normalisers, and an error in that ratio moves sum [p - q]_+ by the same
+// relative amount times the mass where p > q; the sums and the ratios are therefore formed in
+// fp64 (fixed-order DPP tree) and rounded to fp32 once.  Status 0 ok, 1 a row non-finite or
+// empty, 2 the wait gave up.
 struct TeamNorm {
-  float Mp, Mq, izp, izq, zratio;
+  float Mp, Mq;
+  float izp, izq;   // 1 / Z_p, 1 / Z_q
+  float rqp;        // Z_q / Z_p
 };
+// 1 / z for z > 0 in fp64: the fp32 reciprocal refined by one Newton step (relative error near
+// 2^-46), lighter on registers than a full fp64 division.
+__device__ __forceinline__ double recip_d(double z) {
+  const double r = (double)__builtin_amdgcn_rcpf((float)z);
+  return r * fma(-z, r, 2.0);
+}
 __device__ __forceinline__ int team_norm(float pr, float ps, float qr, float qs, int n_s, bool timed_out,
                                          TeamNorm& N) {
   const int lane = threadIdx.x & 63;
@@ -916,16 +963,41 @@ __device__ __forceinline__ int team_norm(float pr, float ps, float qr, float qs,
                           qr == INFINITY);
   float Mp = in ? pr : -INFINITY, Mq = in ? qr : -INFINITY;
   dpp_max2(Mp, Mq);
-  float zp = (in && ps > 0.f) ? ps * __builtin_amdgcn_exp2f(pr - Mp) : 0.f;
-  float zq = (in && qs > 0.f) ? qs * __builtin_amdgcn_exp2f(qr - Mq) : 0.f;
-  dpp_sum2(zp, zq);
+  const double zp = wave_sum_dpp_d((in && ps > 0.f) ? (double)ps * exp2_split((double)pr - (double)Mp) : 0.0);
+  const double zq = wave_sum_dpp_d((in && qs > 0.f) ? (double)qs * exp2_split((double)qr - (double)Mq) : 0.0);
+  const bool ok = zp > 0.0 && zq > 0.0;
+  const double izp = ok ? recip_d(zp) : 0.0;
   N.Mp = Mp;
   N.Mq = Mq;
-  N.izp = __builtin_amdgcn_rcpf(zp);
-  N.izq = __builtin_amdgcn_rcpf(zq);
-  N.zratio = zq * N.izp;
+  N.izp = (float)izp;
+  N.izq = ok ? (float)recip_d(zq) : 0.f;
+  N.rqp = (float)(zq * izp);
   if (timed_out) return 2;
-  return (wave_all(!bad) && zp > 0.f && zq > 0.f && Mp > -INFINITY && Mq > -INFINITY) ? 0 : 1;
+  return (wave_all(!bad) && ok && Mp > -INFINITY && Mq > -INFINITY) ? 0 : 1;
+}
+
+// Residual mass of a wave's part of one paired slice, sum [p - q]_+ (guide page "5.1 投机
+// 解码核心原理", §3.2 / §4.1: beta = sum [p - q]_+), from e-values e = 2^(l c - ref_w) taken
+// relative to the wave's own references.  With a_p = 2^(ref_p - M_p) / Z_p (likewise a_q) and
+// r = a_p / a_q: if r <= 1 the mass is a_q sum max(e_p r - e_q, 0), else a_p sum
+// max(e_p - e_q / r, 0); e <= 1, so both terms stay below 1 and the max with 0 is the fma's
+// clamp modifier.
+struct ResidualScale {
+  float rr, ir, scale;
+  int form;   // 0: e_p r - e_q, 1: e_p - e_q / r, 2: e_p alone (no draft mass in this wave)
+};
+__device__ __forceinline__ ResidualScale residual_scale(const TeamNorm& N, float refp, float refq) {
+  ResidualScale R = {0.f, 0.f, 0.f, 2};
+  const float dp = refp - N.Mp, dq = refq - N.Mq;
+  const float ap = refp > -INFINITY ? __builtin_amdgcn_exp2f(dp) * N.izp : 0.f;
+  if (!(refq > -INFINITY)) { R.scale = ap; return R; }
+  if (ap > 0.f) {
+    R.rr = __builtin_amdgcn_exp2f(dp - dq) * N.rqp;   // a_p / a_q = 2^(dp - dq) Z_q / Z_p
+    R.ir = 1.f / R.rr;
+  }
+  if (R.rr <= 1.f) { R.form = 0; R.scale = __builtin_amdgcn_exp2f(dq) * N.izq; }
+  else { R.form = 1; R.scale = ap; }
+  return R;
 }
 
 // Wave 0 of a paired ticket: wait until every member of the team has raised its arrival flag
@@ -965,32 +1037,11 @@ __device__ __forceinline__ void team_gather(const FusedArgs& a, FusedLds& L, int
     L.tn[1] = N.Mq;
     L.tn[2] = N.izp;
     L.tn[3] = N.izq;
-    L.tn[4] = N.zratio;
+    L.tn[4] = N.rqp;
     L.tst = st;
   }
 }
 
-// Residual mass of this wave's part of one paired slice, sum [p - q]_+ (guide page "5.1 投机
-// 解码核心原理", §3.2 / §4.1: beta = sum [p - q]_+), from e-values.  With
-// a_p = 2^(ref_p - M_p) / Z_p (likewise a_q) and r = a_p / a_q: if r <= 1 the mass is
-// a_q sum max(e_p r - e_q, 0), else a_p sum max(e_p - e_q / r, 0); e <= 1, so both terms stay
-// below 1 and the max with 0 is the fma's clamp modifier.
-struct ResidualScale {
-  float rr, ir, scale;
-  int form;   // 0: e_p r - e_q, 1: e_p - e_q / r, 2: e_p alone (no draft mass in this wave)
-};
-__device__ __forceinline__ ResidualScale residual_scale(const TeamNorm& N, float refp, float refq) {
-  ResidualScale R;
-  const float dp = refp - N.Mp, dq = refq - N.Mq;
-  const float ap = refp > -INFINITY ? __builtin_amdgcn_exp2f(dp) * N.izp : 0.f;
-  const float aq = refq > -INFINITY ? __builtin_amdgcn_exp2f(dq) * N.izq : 0.f;
-  R.rr = __builtin_amdgcn_exp2f(dp - dq) * N.zratio;
-  R.ir = __builtin_amdgcn_rcpf(R.rr);
-  if (!(aq > 0.f)) { R.form = 2; R.scale = ap; }
-  else if (R.rr <= 1.f) { R.form = 0; R.scale = aq; }
-  else { R.form = 1; R.scale = ap; }
-  return R;
-}
 __device__ __forceinline__ float residual_slice(const ResidualScale& R, const float (&ep)[kPerThread],
                                                 const float (&eq)[kPerThread]) {
   float sm;
@@ -1269,15 +1320,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_
   if (!pair) return;
   if (wave == 0) team_gather(a, L, r, n_u);
   __syncthreads();
-  TeamNorm N;
-  N.Mp = L.tn[0];
-  N.Mq = L.tn[1];
-  N.izp = L.tn[2];
-  N.izq = L.tn[3];
-  N.zratio = L.tn[4];
   const int st = L.tst;
   float m0 = 0.f, m1 = 0.f;
   if (st == 0) {
+    TeamNorm N;
+    N.Mp = L.tn[0];
+    N.Mq = L.tn[1];
+    N.izp = L.tn[2];
+    N.izq = L.tn[3];
+    N.rqp = L.tn[4];
     const ResidualScale R = residual_scale(N, refp, refq);
     m0 = residual_slice(R, ep[0], eq[0]);
     float ep1[kPerThread];

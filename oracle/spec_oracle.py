@@ -304,9 +304,19 @@ def sample_three_level(w, u1, u2, u3):
 
 @dataclass
 class Decision:
-    kind: str        # "accept" (position i) or "sample" (position i) or "topp" (row)
+    """One decision of a round and its distance from the boundary that decides it.
+
+    kind "accept": the accept test at 1-based position i, margin |u0 - a_i|.
+    kind "sample": the token drawn at position i, margin = the sampler's smallest relative
+    distance over its three levels.  kind "topp": the top-p boundary of one row, margin =
+    |cumulative mass - top_p| at the chosen value group and the one before it; ``row`` says
+    which row ("target" or "draft") and ``position`` its 1-based position.
+    """
+
+    kind: str
     position: int
     margin: float
+    row: str = ""
 
 
 @dataclass
@@ -382,9 +392,10 @@ def verify_request(target_logits, draft_logits, draft_tokens, sp: SamplingParams
         kl_pq=np.full(gamma, nan), kl_qp=np.full(gamma, nan), l1=np.full(gamma, nan),
         accept_prob=np.full(gamma, nan),
     )
-    for r in P + (Q or []):
-        if r.topp_margin < math.inf:
-            res.decisions.append(Decision("topp", -1, r.topp_margin))
+    for kind, rows in (("target", P), ("draft", Q or [])):
+        for i, r in enumerate(rows):
+            if r.topp_margin < math.inf:
+                res.decisions.append(Decision("topp", i + 1, r.topp_margin, kind))
 
     # per-position draft distributions (one-hot for token-only drafts) and pair statistics
     qdists = []

@@ -3,12 +3,17 @@ compare the two with the decision-excusal rule.
 
 Comparison rule (the tolerance the parity tests enforce):
   * accepted counts and emitted tokens are compared exactly.  A mismatch is excused only if
-    the first diverging decision lies within 1e-6 of its boundary in the oracle (accept:
-    |u - a|; sampler: the relative distance of u * mass from a prefix-sum boundary at any of
-    the three levels; top-p: |cumulative mass - top_p|).  Excused mismatches must stay below
+    the first decision where the two sides part ways lies within 1e-6 of its boundary in the
+    oracle.  That decision is the accept test at position n + 1 when the accepted counts
+    differ (n the smaller count), else the draw of the emitted token.  Its margin is |u - a|
+    for an accept test and the sampler's smallest relative distance of u * mass from a
+    prefix-sum boundary over the three levels for a draw; the top-p margin |cumulative mass -
+    top_p| of the target or draft row of that same position counts too, since those rows
+    decide it.  No other row's margin excuses anything.  Excused mismatches must stay below
     1e-4 of all draws (accept draws + sampling draws); any other mismatch fails.
   * float statistics: |gpu - ref| <= 1e-5 * |ref| + 1e-7, and NaN exactly where the oracle
-    has NaN.
+    has NaN.  A position whose target or draft row has a top-p margin below 1e-6 may keep a
+    different set on the GPU; its per-position statistics are counted as excused, not compared.
 """
 from __future__ import annotations
 
@@ -90,6 +95,7 @@ class Report:
         self.draws = 0
         self.hard = []
         self.excused = 0
+        self.excused_stats = 0
         self.stat_fail = []
         self.max_rel = {}
 
@@ -98,25 +104,34 @@ class Report:
 
     def __repr__(self):
         return (f"Report(draws={self.draws}, hard={self.hard[:5]}, excused={self.excused}, "
+                f"excused_stat_positions={self.excused_stats}, "
                 f"stat_fail={self.stat_fail[:5]}, max_rel={self.max_rel})")
+
+
+def topp_margins(ref: O.RequestResult, pos):
+    """Top-p margins of the rows of 1-based position pos (target row pos, draft row pos)."""
+    return [d.margin for d in ref.decisions if d.kind == "topp" and d.position == pos]
+
+
+def deciding_margins(ref: O.RequestResult, n_gpu):
+    """Margins of the first decision where a GPU result with n_gpu accepted tokens and the
+    oracle part ways: the accept test at the first position they decided differently, or the
+    draw of the emitted token when the counts agree; plus the top-p margins of that position's
+    rows."""
+    if n_gpu != ref.num_accepted:
+        pos = min(n_gpu, ref.num_accepted) + 1
+        margins = [d.margin for d in ref.decisions if d.kind == "accept" and d.position == pos]
+    else:
+        pos = ref.num_accepted + 1
+        margins = [d.margin for d in ref.decisions if d.kind == "sample" and d.position == pos]
+    return margins + topp_margins(ref, pos)
 
 
 def _first_divergence_excused(ref: O.RequestResult, n_gpu, toks_gpu):
     """Whether the first decision where the GPU and the oracle part ways is within
     DECISION_EPS of its boundary in the oracle."""
-    topp = [d.margin for d in ref.decisions if d.kind == "topp"]
-    if topp and min(topp) < DECISION_EPS:
-        return True
-    if n_gpu != ref.num_accepted:
-        pos = min(n_gpu, ref.num_accepted) + 1
-        for d in ref.decisions:
-            if d.kind == "accept" and d.position == pos:
-                return d.margin < DECISION_EPS
-        return False
-    for d in ref.decisions:
-        if d.kind == "sample":
-            return d.margin < DECISION_EPS
-    return False
+    m = deciding_margins(ref, n_gpu)
+    return bool(m) and min(m) < DECISION_EPS
 
 
 def compare_requests(gpu, refs, inp: W.Inputs, report: Report, stats=True):
@@ -154,14 +169,24 @@ def compare_requests(gpu, refs, inp: W.Inputs, report: Report, stats=True):
             ("kl_qp", gpu.get("kl_qp"), ref.kl_qp, c0, g),
             ("expected_committed", gpu.get("expected_committed"), np.array([ref.expected_committed]), b, 1),
         ]
+        # positions whose rows sit within DECISION_EPS of a top-p boundary (1-based)
+        near = {d.position for d in ref.decisions if d.kind == "topp" and d.margin < DECISION_EPS}
+        report.excused_stats += len(near)
         for name, garr, rarr, lo, cnt in pairs:
             if garr is None:
                 continue
-            gv = garr[lo:lo + cnt]
+            gv = np.array(garr[lo:lo + cnt], dtype=np.float64)
+            rarr = np.array(rarr, dtype=np.float64)
+            if name != "expected_committed":
+                for pos in near:
+                    if pos - 1 < cnt:
+                        gv[pos - 1] = rarr[pos - 1] = 0.0
+            elif near:
+                continue
             if not close(gv, rarr):
                 report.stat_fail.append((b, name, gv.tolist(), np.asarray(rarr).tolist()))
             report.max_rel[name] = max(report.max_rel.get(name, 0.0), max_rel(gv, rarr))
-        if "req_stats" in gpu:
+        if "req_stats" in gpu and not near:
             if not close(gpu["req_stats"][b], ref.req_stats):
                 report.stat_fail.append((b, "req_stats", gpu["req_stats"][b].tolist(), ref.req_stats.tolist()))
             report.max_rel["req_stats"] = max(report.max_rel.get("req_stats", 0.0),

@@ -155,6 +155,62 @@ def test_worked_example_v3():
     acc = gpu["num_accepted"] == 1
     # rejected draws always land on token 0 (residual [1, 0, 0])
     assert np.all(first[~acc] == 0)
+    # acceptance frequency: sum_y q(y) min(1, p(y) / q(y)) = sum min(p, q) = 0.6 (guide §4.3);
+    # 2000 Bernoulli draws, 4 standard deviations
+    freq = acc.mean()
+    note(f"acceptance frequency {freq:.4f}")
+    assert abs(freq - 0.6) < 4 * math.sqrt(0.6 * 0.4 / B)
+    # the first emitted token (accepted draft or correction) follows p (guide §4.2, §7)
+    cnt = np.bincount(first, minlength=3).astype(float)
+    pval = scipy.stats.chisquare(cnt, p * B).pvalue
+    note(f"first-token counts {cnt.tolist()} vs p * B {(p * B).tolist()}: chi2 p = {pval:.3g}")
+    assert pval > 1e-3
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_low_overlap_one_minus_tv(path):
+    """Nearly disjoint p and q (overlap near 7e-4): the target puts its mass on tokens 0..99,
+    the draft on tokens 100..199.  1 - TV = sum min(p, q) must keep 1e-5 relative precision
+    with no absolute floor (guide §4.3: A = sum min(p, q) = 1 - TV)."""
+    V = 3 * 4096 + 72
+    inp = custom_inputs(4, V, [3, 2, 1, 3], sigma=0.5, tau=0.5, seed=77)
+    t32 = W.bf16_bits_to_f32(inp.target).copy()
+    d32 = W.bf16_bits_to_f32(inp.draft).copy()
+    t32[:, :100] += 12.0
+    d32[:, 100:200] += 12.0
+    inp.target[:] = W.bf16_bits_from_f32(t32)
+    inp.draft[:] = W.bf16_bits_from_f32(d32)
+    sp = O.SamplingParams(1.0)
+    gpu, refs, rep = check(inp, sp, path=path)
+    for b, ref in refs.items():
+        c0, g = int(inp.cu_draft[b]), int(inp.gammas[b])
+        got = gpu["one_minus_tv"][c0:c0 + g].astype(np.float64)
+        assert (ref.one_minus_tv < 2e-3).all(), ref.one_minus_tv
+        rel = np.abs(got - ref.one_minus_tv) / ref.one_minus_tv
+        note(f"request {b}: 1 - TV {ref.one_minus_tv.tolist()} relative error {rel.max():.2e}")
+        assert (rel < 1e-5).all()
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_near_identical_rows_small_tv(path):
+    """Draft rows equal to the target rows except for a few hundred tokens: TV of a few 1e-3,
+    the case where the residual mass sum [p - q]_+ is a small difference of nearly equal
+    distributions (its error then comes from the normalisers' ratio)."""
+    V = 3 * 4096 + 72
+    inp = custom_inputs(5, V, [4, 3, 2, 4, 1], T=0.7, seed=78)
+    rng = np.random.default_rng(79)
+    for b in range(5):
+        g, c0 = int(inp.gammas[b]), int(inp.cu_draft[b])
+        inp.draft[c0:c0 + g] = inp.target[c0 + b:c0 + b + g]
+        d32 = W.bf16_bits_to_f32(inp.draft[c0:c0 + g]).copy()
+        idx = rng.choice(V, size=(g, 300))
+        for i in range(g):
+            d32[i, idx[i]] += rng.normal(0, 1.0, 300).astype(np.float32)
+        inp.draft[c0:c0 + g] = W.bf16_bits_from_f32(d32)
+    gpu, refs, rep = check(inp, O.SamplingParams(0.7), path=path)
+    tv = np.concatenate([r.tv for r in refs.values()])
+    note(f"TV range {tv.min():.2e} .. {tv.max():.2e}; max relative error of L1 {rep.max_rel.get('l1')}")
+    assert np.median(tv) < 0.01
 
 
 # ----------------------------------------------------------------------------- greedy / token-only

@@ -702,3 +702,138 @@ def test_lm_head_p_tok_closed_form_and_edges():
     assert np.isnan(bad["p_tok"][0]) and bad["argmax"][0] == -1
     greedy = O.lm_head_row_stats(h, W, O.SamplingParams(0.0), tokens=tok)
     assert greedy["p_tok"][0] == (1.0 if np.argmax(l[0]) == 3 else 0.0)
+
+
+# ----------------------------------------------------------------------------- decision margins
+#
+# The margins decide which GPU/oracle mismatches are excused, so each is pinned on a row whose
+# distance from its boundary is known in closed form, one case just inside 1e-6 and one just
+# outside.
+
+
+def test_accept_margin_is_distance_from_ratio():
+    """R4 accept test: the recorded margin is |u0 - a| at that position.  p = [1/2, 1/2],
+    q = [1/4, 3/4], y = 1 gives a = 2/3; u0 = 2/3 - 5e-7 accepts with margin 5e-7, u0 = 2/3 +
+    3e-6 rejects with margin 3e-6."""
+    p = np.array([0.5, 0.5])
+    q = np.array([0.25, 0.75])
+    tl = np.log(np.stack([p, p, p]))
+    dl = np.log(np.stack([q, q]))
+    sp = O.SamplingParams(1.0)
+    for d, acc in [(-5e-7, 1), (3e-6, 0)]:
+        us = {1: (2.0 / 3.0 + d, 0.5, 0.5, 0.5), 2: (0.99, 0.5, 0.5, 0.5), 3: (0.5, 0.5, 0.5, 0.5)}
+        res = O.verify_request(tl, dl, [1, 1], sp, 0, 0, 0, uniforms=us)
+        acc_dec = [x for x in res.decisions if x.kind == "accept"]
+        assert acc_dec[0].position == 1
+        assert acc_dec[0].margin == pytest.approx(abs(d), rel=1e-6)
+        assert (res.num_accepted >= 1) == bool(acc)
+        if acc:   # position 2 is tested too: u0 = 0.99 against a = 2/3
+            assert acc_dec[1].position == 2
+            assert acc_dec[1].margin == pytest.approx(0.99 - 2.0 / 3.0, rel=1e-9)
+            assert res.num_accepted == 1
+        else:
+            assert len(acc_dec) == 1 and res.num_accepted == 0
+
+
+def test_sampler_margin_level3():
+    """R6, element level: w = [1, 1, 1, 1] (one chunk, one group).  u3 = 1/2 + 1e-7 puts
+    u3 W = 2 + 4e-7 just past the prefix sum 2: token 2, margin 4e-7 / 4 = 1e-7; the other two
+    levels sit at u = 1/2 (margin 1/2)."""
+    x, m = O.sample_three_level(np.ones(4), 0.5, 0.5, 0.5 + 1e-7)
+    assert x == 2 and m == pytest.approx(1e-7, rel=1e-6)
+    x, m = O.sample_three_level(np.ones(4), 0.5, 0.5, 0.5 - 3e-6)
+    assert x == 1 and m == pytest.approx(3e-6, rel=1e-6)
+
+
+def test_sampler_margin_level1():
+    """R6, chunk level: w = 1 on two full chunks (S = [4096, 4096]).  u1 = 1/2 - 2e-7 stays in
+    chunk 0 at distance 2e-7 W from the boundary.  Inside it u2 = 0.3 picks group 19 (u2 S =
+    1228.8 between 1216 and 1280: margin 12.8 / 4096) and u3 = 0.51 element 32 (32.64 between
+    32 and 33: margin 0.36 / 64); the chunk level's 2e-7 is the smallest."""
+    w = np.ones(2 * O.CHUNK)
+    x, m = O.sample_three_level(w, 0.5 - 2e-7, 0.3, 0.51)
+    assert x == 19 * O.GROUP + 32
+    assert m == pytest.approx(2e-7, rel=1e-6)
+    x, m = O.sample_three_level(w, 0.5 + 2e-6, 0.3, 0.51)
+    assert x == O.CHUNK + 19 * O.GROUP + 32 and m == pytest.approx(2e-6, rel=1e-6)
+    _, m = O.sample_three_level(w, 0.25, 0.3, 0.51)   # chunk margin 0.25, group 12.8 / 4096
+    assert m == pytest.approx(12.8 / 4096, rel=1e-9)
+
+
+def test_sampler_margin_level2():
+    """R6, group level: one chunk of ones; u2 = 1/2 + 3e-6 lands 3e-6 S past the prefix sum
+    2048 of the first 32 groups: group 32, margin 3e-6 (u3 = 0.76 picks element 48 at margin
+    0.36 / 64)."""
+    w = np.ones(O.CHUNK)
+    x, m = O.sample_three_level(w, 0.5, 0.5 + 3e-6, 0.76)
+    assert x == 32 * O.GROUP + 48 and m == pytest.approx(3e-6, rel=1e-6)
+    x, m = O.sample_three_level(w, 0.5, 0.5 - 4e-7, 0.76)
+    assert x == 31 * O.GROUP + 48 and m == pytest.approx(4e-7, rel=1e-6)
+
+
+def test_topp_margin_is_distance_of_both_neighbouring_groups():
+    """R1 top-p boundary: p = [1/2, 3/10, 1/5].  top_p = 0.8 - 4e-7 is reached by the second
+    group (cumulative 0.8): two tokens kept, margin min(|0.8 - top_p|, |0.5 - top_p|) = 4e-7.
+    top_p = 0.8 + 2e-6 needs the third group: three kept, margin |0.8 - top_p| = 2e-6.  top_p =
+    0.3 is reached by the first group alone: margin |0.5 - 0.3| (no group before it)."""
+    l = np.log(np.array([0.5, 0.3, 0.2]))
+    for tp, kept, margin in [(0.8 - 4e-7, 2, 4e-7), (0.8 + 2e-6, 3, 2e-6), (0.3, 1, 0.2)]:
+        r = O.row_distribution(l, O.SamplingParams(1.0, 0, tp))
+        assert r.kept_count == kept
+        assert r.topp_margin == pytest.approx(margin, rel=1e-6)
+    assert O.row_distribution(l, O.SamplingParams(1.0)).topp_margin == math.inf
+
+
+def test_topp_decisions_name_their_row():
+    """Each filtered row's top-p decision carries the row kind and its 1-based position, so a
+    comparison can tell which position a near-boundary row decides."""
+    rng = np.random.default_rng(3)
+    tl = rng.normal(0, 1, (3, 50))
+    dl = rng.normal(0, 1, (2, 50))
+    res = O.verify_request(tl, dl, [1, 2], O.SamplingParams(1.0, 0, 0.7), 1, 2, 3)
+    got = sorted((d.row, d.position) for d in res.decisions if d.kind == "topp")
+    assert got == [("draft", 1), ("draft", 2), ("target", 1), ("target", 2), ("target", 3)]
+    for d in res.decisions:
+        if d.kind == "topp":
+            src = tl[d.position - 1] if d.row == "target" else dl[d.position - 1]
+            assert d.margin == O.row_distribution(src, O.SamplingParams(1.0, 0, 0.7)).topp_margin
+
+
+def test_accept_prob_of_a_nonfinite_row_is_nan():
+    """R8 / R10: a position whose draft row holds a NaN has no distribution, so its accept
+    probability is NaN while the other positions keep theirs (p = [1/2, 1/2], q = [1/4, 3/4],
+    y = 1: a = 2/3); the request is NONFINITE and its expected committed length NaN."""
+    p = np.array([0.5, 0.5])
+    q = np.array([0.25, 0.75])
+    tl = np.log(np.stack([p, p, p]))
+    dl = np.log(np.stack([q, q]))
+    dl[1, 0] = np.nan
+    res = O.verify_request(tl, dl, [1, 1], O.SamplingParams(1.0), 0, 0, 0)
+    assert res.accept_prob[0] == pytest.approx(2.0 / 3.0, rel=1e-12)
+    assert np.isnan(res.accept_prob[1])
+    assert res.status == O.STATUS_NONFINITE and res.num_accepted == 0 and res.tokens == []
+    assert np.isnan(res.expected_committed)
+
+
+def test_verify_batch_ragged_layout():
+    """The batch layout of spec_verify_batch: request b's target rows start at cu[b] + b, its
+    draft rows and tokens at cu[b].  Greedy rows with a known argmax (row i of request b peaks
+    at token 3b + i) and drafts that match up to a chosen position give outputs fixed by
+    construction."""
+    V = 16
+    gammas = [2, 0, 3]
+    cu = [0, 2, 2, 5]
+    target = np.zeros((5 + 3, V))
+    ys = np.zeros(5, dtype=np.int64)
+    agree = {0: 1, 1: 0, 2: 3}   # drafts of request b match the target argmax up to here
+    for b, g in enumerate(gammas):
+        for i in range(g + 1):
+            target[cu[b] + b + i, 3 * b + i] = 5.0
+        for i in range(g):
+            ys[cu[b] + i] = 3 * b + i if i < agree[b] else (3 * b + i + 7) % V
+    out = O.verify_batch(target, None, ys, cu, O.SamplingParams(0.0), 1, 2)
+    assert sorted(out) == [0, 1, 2]
+    assert (out[0].num_accepted, out[0].tokens) == (1, [0, 1])
+    assert (out[1].num_accepted, out[1].tokens) == (0, [3])
+    assert (out[2].num_accepted, out[2].tokens) == (3, [6, 7, 8, 9])
+    assert sorted(O.verify_batch(target, None, ys, cu, O.SamplingParams(0.0), 1, 2, requests=[2])) == [2]
