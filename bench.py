@@ -62,34 +62,32 @@ def copy_reference(steps):
     print(json.dumps({"copy_reference": res, "peak_GBps": HBM_PEAK_GBS}), flush=True)
 
 
-def stream_ceiling(torch, L, lib, steps=20):
+def stream_ceiling(torch, L, steps=20):
     """Context for the roofline: the library's plain streaming-read kernel (spec_stream_read)
-    over 1 GiB on the same GPU, after the timed region, timed with HIP events around each
-    launch; GB/s and the fraction of the HBM peak."""
+    over 1 GiB on the same GPU, after the timed region, timed with events recorded on the
+    kernel's stream around each launch; GB/s and the fraction of the HBM peak."""
     nbytes = 1 << 30
     buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     for _ in range(3):
         L.spec_stream_read(buf, sink)
-    ev = HipEvents()
-    pairs = [(ev.create(), ev.create()) for _ in range(steps)]
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     for a, b in pairs:
-        lib.spec_set_profile_events(a, b)
+        a.record()
         L.spec_stream_read(buf, sink)
+        b.record()
     torch.cuda.synchronize()
-    lib.spec_set_profile_events(None, None)
-    ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
-    for a, b in pairs:
-        ev.destroy(a)
-        ev.destroy(b)
+    ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
     del buf
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"kernel": "k_stream_read (spec_stream_read) over 1 GiB", "GBps": gbs, "frac": gbs / HBM_PEAK_GBS}
 
 
 class HipEvents:
-    """Raw hipEvent_t pairs (the library records them on the stream its kernels run on)."""
+    """Raw hipEvent_t pairs, handed to the library in a call's options: the dispatch of the
+    call's streaming kernel records them at its start and end.  Destroyed before the process
+    exits (close())."""
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
@@ -111,6 +109,16 @@ class HipEvents:
 
     def destroy(self, e):
         self.hip.hipEventDestroy(e)
+
+    def timed_pairs(self, n):
+        self.pairs = [(self.create(), self.create()) for _ in range(n)]
+        return self.pairs
+
+    def close(self):
+        for a, b in getattr(self, "pairs", []):
+            self.destroy(a)
+            self.destroy(b)
+        self.pairs = []
 
 
 def algorithmic_bytes(inp):
@@ -225,8 +233,9 @@ def lm_head_bench(args, L, W, torch):
     out = {}
     work = L.new_workspace(lib.spec_lm_head_workspace_bytes(R, V, D), dev)
 
-    def step(k):
-        return L.spec_lm_head_row_stats(h, ws[k % 2], temperature=T, tokens=tok, workspace=work, out=out)
+    def step(k, options=None):
+        return L.spec_lm_head_row_stats(h, ws[k % 2], temperature=T, tokens=tok, workspace=work, out=out,
+                                        options=options)
 
     for k in range(args.warmup):
         step(k)
@@ -237,13 +246,12 @@ def lm_head_bench(args, L, W, torch):
     torch.cuda.synchronize()
     sec = (time.perf_counter() - t0) / args.steps
     ev = HipEvents()
-    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    pairs = ev.timed_pairs(args.steps)
     for k in range(args.steps):
-        lib.spec_set_profile_events(pairs[k][0], pairs[k][1])
-        step(k)
+        step(k, L.call_options(profile_events=pairs[k]))
     torch.cuda.synchronize()
-    lib.spec_set_profile_events(None, None)
     kms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
+    ev.close()
     flops = 2.0 * R * V * D
     counters = load_traffic("k_head") or {}
     achieved = flops / (kms * 1e-3) / 1e12
@@ -338,9 +346,10 @@ def main():
     for k in OUTPUTS_PER_POSITION:
         out[k] = torch.empty(Rd, dtype=torch.float32, device=dev)
 
-    def step(k):
+    def step(k, options=None):
         return L.spec_verify_batch(tgts[k % copies], drfs[k % copies], toks, cu, G, temperature=wl.temperature,
-                                   top_k=wl.top_k, top_p=wl.top_p, seed=1234, step=k, workspace=ws, out=out)
+                                   top_k=wl.top_k, top_p=wl.top_p, seed=1234, step=k, workspace=ws, out=out,
+                                   options=options)
 
     for k in range(args.warmup):
         step(k)
@@ -358,22 +367,18 @@ def main():
     # outside the timed region: the same calls again, each with HIP events recorded on the
     # library's stream right around its streaming kernel (the roofline's kernel time)
     ev = HipEvents()
-    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    pairs = ev.timed_pairs(args.steps)
     torch.cuda.synchronize()
     for k in range(args.steps):
-        lib.spec_set_profile_events(pairs[k][0], pairs[k][1])
-        step(args.warmup + args.steps + k)
+        step(args.warmup + args.steps + k, L.call_options(profile_events=pairs[k]))
     torch.cuda.synchronize()
-    lib.spec_set_profile_events(None, None)
     kernel_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
-    for a, b in pairs:
-        ev.destroy(a)
-        ev.destroy(b)
+    ev.close()
 
     sec_per_step = (t1 - t0) / args.steps
     kern_avg_s = float(np.mean(kernel_ms)) / 1e3
     achieved = alg_bytes / kern_avg_s / 1e9
-    fused = not os.environ.get("SPEC_VERIFY_NO_FUSED")
+    fused = True
     filtered = wl.temperature > 0 and 0 < wl.top_k < wl.V
     if filtered:
         kernel_key, kernel_name = "k_filt_slices", ("k_filt_slices (streaming kernel: every needed logit "
@@ -420,7 +425,7 @@ def main():
                      "kernel_ms_p10_p50_p90": [float(x) for x in np.percentile(kernel_ms, [10, 50, 90])],
                      "valu_issue_frac": valu_frac},
     }
-    line["stream_ceiling"] = stream_ceiling(torch, L, lib)
+    line["stream_ceiling"] = stream_ceiling(torch, L)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -21,8 +21,12 @@
  *  - Calls are asynchronous and ordered on `hip_stream` (a hipStream_t; NULL = the null
  *    stream).  They are re-entrant when concurrent calls use different workspaces.
  *  - Workspaces: zero-fill once before first use; sizes come from the *_workspace_bytes
- *    functions.  The only state the library keeps is a process-wide call sequence number
- *    that tags the records a call writes into its workspace.
+ *    functions (each covers every path a call can take).  Nothing a call does depends on an
+ *    earlier call: the library keeps no settings between calls (per-call options travel in
+ *    spec_call_options) and no environment variable changes a path.  Its one piece of
+ *    process-wide data is a call sequence number, atomically incremented, that tags the
+ *    records a call writes into its workspace so that records of an earlier call are never
+ *    taken for this call's.
  *  - Logit rows are dense, row-major, `ld` ELEMENTS apart (ld >= V).  dtype SPEC_BF16 rows
  *    hold bf16 bit patterns, SPEC_F32 rows hold floats.  A 16-byte aligned base with a
  *    16-byte multiple row stride takes the vector path; anything else takes a scalar path
@@ -55,9 +59,9 @@ extern "C" {
 #define SPEC_STATUS_BAD_TOKEN 2        /* draft token outside [0, V): rejected there        */
 #define SPEC_STATUS_ZERO_Q 4           /* q(y) = 0 after filtering: rejected there          */
 #define SPEC_STATUS_RESIDUAL_EMPTY 8   /* residual mass 0 after a rejection: drawn from p   */
-#define SPEC_STATUS_TIMEOUT 16         /* reserved: a bounded wait expired                  */
-#define SPEC_STATUS_FILTER_OVERFLOW 32 /* a filtered row kept more tokens than the sparse
-                                          path holds: 0 accepted, tokens -1                 */
+#define SPEC_STATUS_TIMEOUT 16         /* a bounded wait expired: 0 accepted, tokens -1     */
+#define SPEC_STATUS_FILTER_OVERFLOW 32 /* not returned: a filtered row that the sparse path
+                                          cannot hold is recomputed on the dense path       */
 #define SPEC_STATUS_BAD_GAMMA 64       /* cu_draft inconsistent for this request: nothing
                                           read, 0 accepted, tokens -1                        */
 
@@ -69,12 +73,11 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
  * off; otherwise the smallest set of largest values whose mass over the top-k set reaches
  * top_p is kept (a boundary value is kept with all its ties).  Order: temperature, top-k,
  * top-p.  Two paths serve filtered calls with the same results.  With 1 <= top_k <= 256 (top-p
- * optional) the sparse path works on per-slice top-k candidates; a row whose top-k set (k plus
- * boundary ties) holds more than 512 tokens cannot be represented there and is reported
- * (SPEC_STATUS_FILTER_OVERFLOW, or kept_count -1 in spec_row_stats) instead of a result.
- * Every other filter (top-p alone, top_k > 256) takes the dense path, which finds each row's
- * kept-set threshold exactly and has no size limit; the environment variable
- * SPEC_VERIFY_DENSE_FILTER=1 sends every filtered call there. */
+ * optional) the sparse path works on per-slice top-k candidates; a request (or plain row) whose
+ * top-k set (k plus boundary ties) holds more than 512 tokens, or whose slices had to drop
+ * tied candidates, is recomputed in the same call on the dense path.  Every other filter
+ * (top-p alone, top_k > 256) takes the dense path, which finds each row's kept-set threshold
+ * exactly and has no size limit; SPEC_PATH_MULTI_KERNEL sends every filtered call there. */
 typedef struct {
   float temperature;
   int top_k;
@@ -107,6 +110,31 @@ typedef struct {
                                  variance-free block efficiency for one chain); NaN for a
                                  non-finite request                                        */
 } spec_pos_stats;
+
+/* Per-call options of the *_ex entry points; a NULL pointer means every default.  No field
+ * changes a result: the paths compute the same outputs, the wait bound and poll timing only
+ * move time, and the events only observe it.
+ *  path           SPEC_PATH_AUTO: the fastest path for the shape and filter.
+ *                 SPEC_PATH_MULTI_KERNEL: the multi-kernel path (one pass per statistic,
+ *                 filtered calls through per-row thresholds), for cross-checks.
+ *  spin_limit     polls before the single-kernel path's team wait gives up and reports
+ *                 SPEC_STATUS_TIMEOUT for the request (no tokens); < 0: 262144; 0: give up at
+ *                 the first incomplete poll (a test of the failure path).
+ *  poll_delay     10-ns ticks a streaming workgroup waits before its first team poll; <= 0: 400.
+ *  poll_pause     pause between failed polls, in units of 128 cycles; <= 0: 8.
+ *  profile_start  a hipEvent_t pair, or both NULL: recorded by the dispatch of the call's
+ *  profile_stop   streaming kernel (the pass that reads every needed logit), right at its start
+ *                 and end, so a benchmark times that kernel alone.  Owned by the caller.
+ * An unknown path or exactly one NULL event gives SPEC_ERR_INVALID. */
+typedef enum { SPEC_PATH_AUTO = 0, SPEC_PATH_MULTI_KERNEL = 1 } spec_path;
+typedef struct {
+  int path;
+  int64_t spin_limit;
+  int poll_delay;
+  int poll_pause;
+  void* profile_start;
+  void* profile_stop;
+} spec_call_options;
 
 /* spec_verify_batch -- verify one speculative round for B ragged requests.
  *
@@ -147,6 +175,17 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt,
                       spec_pos_stats pos_stats, float* out_req_stats, int32_t* out_status,
                       void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* spec_verify_batch with per-call options (NULL: defaults, the same call as above). */
+int spec_verify_batch_ex(int B, int V, int gamma_max, spec_dtype dt,
+                         const void* target_logits, int64_t target_ld,
+                         const void* draft_logits, int64_t draft_ld,
+                         const int32_t* draft_tokens, const int32_t* cu_draft, int n_draft_rows,
+                         spec_sampling_params sp, uint64_t seed, uint64_t step,
+                         int32_t* out_tokens, int32_t* out_num_accepted,
+                         spec_pos_stats pos_stats, float* out_req_stats, int32_t* out_status,
+                         void* workspace, size_t workspace_bytes, void* hip_stream,
+                         const spec_call_options* options);
+
 size_t spec_verify_workspace_bytes(int B, int V, int gamma_max, spec_dtype dt,
                                    spec_sampling_params sp);
 
@@ -156,13 +195,20 @@ size_t spec_verify_workspace_bytes(int B, int V, int gamma_max, spec_dtype dt,
  * exp(l/T), entropy_bits, max_prob, kept_count (kept tokens with a finite logit).  With
  * temperature 0 the row is one-hot at the argmax: entropy 0, max_prob 1, kept 1, log_z NaN.
  * A row with a NaN / +inf logit or no finite logit gives argmax -1, NaN statistics and kept
- * count 0; a filtered row whose top-k set overflows the sparse path gives argmax -1, NaN
- * statistics and kept count -1. */
+ * count 0. */
 int spec_row_stats(int R, int V, spec_dtype dt, const void* logits, int64_t ld,
                    spec_sampling_params sp,
                    float* max_logit, int32_t* argmax, float* log_z, float* entropy_bits,
                    float* max_prob, int32_t* kept_count,
                    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* spec_row_stats with per-call options (NULL: defaults). */
+int spec_row_stats_ex(int R, int V, spec_dtype dt, const void* logits, int64_t ld,
+                      spec_sampling_params sp,
+                      float* max_logit, int32_t* argmax, float* log_z, float* entropy_bits,
+                      float* max_prob, int32_t* kept_count,
+                      void* workspace, size_t workspace_bytes, void* hip_stream,
+                      const spec_call_options* options);
 
 size_t spec_row_stats_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling_params sp);
 
@@ -170,14 +216,22 @@ size_t spec_row_stats_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling
  * (guide §3.2), or from p when q_logits is NULL, with the same three-level sampler.
  *  uniforms: [R, 3] fp64 in [0, 1) on the device, or NULL for Philox counter (r, 0, 1, 0),
  *  words 1..3.  Outputs [R]: out_token, out_mass (beta = sum [p - q]_+, or 1 without q; NaN
- *  for non-finite rows), out_status (NONFINITE, RESIDUAL_EMPTY: beta = 0, drawn from p,
- *  FILTER_OVERFLOW: token -1). */
+ *  for non-finite rows), out_status (NONFINITE, RESIDUAL_EMPTY: beta = 0, drawn from p). */
 int spec_residual_sample(int R, int V, spec_dtype dt,
                          const void* p_logits, int64_t p_ld, const void* q_logits, int64_t q_ld,
                          spec_sampling_params sp, const double* uniforms,
                          uint64_t seed, uint64_t step,
                          int32_t* out_token, double* out_mass, int32_t* out_status,
                          void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* spec_residual_sample with per-call options (NULL: defaults). */
+int spec_residual_sample_ex(int R, int V, spec_dtype dt,
+                            const void* p_logits, int64_t p_ld, const void* q_logits, int64_t q_ld,
+                            spec_sampling_params sp, const double* uniforms,
+                            uint64_t seed, uint64_t step,
+                            int32_t* out_token, double* out_mass, int32_t* out_status,
+                            void* workspace, size_t workspace_bytes, void* hip_stream,
+                            const spec_call_options* options);
 
 size_t spec_residual_sample_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling_params sp);
 
@@ -206,6 +260,14 @@ int spec_lm_head_row_stats(int R, int V, int D, const void* hidden, int64_t h_ld
                            float* log_z, float* entropy_bits, float* max_prob, float* p_tok, void* workspace,
                            size_t workspace_bytes, void* hip_stream);
 
+/* spec_lm_head_row_stats with per-call options (NULL: defaults; the profile events bracket the
+ * MFMA tile kernel). */
+int spec_lm_head_row_stats_ex(int R, int V, int D, const void* hidden, int64_t h_ld, const void* weight,
+                              int64_t w_ld, spec_sampling_params sp, const int32_t* tokens, float* max_logit,
+                              int32_t* argmax, float* log_z, float* entropy_bits, float* max_prob, float* p_tok,
+                              void* workspace, size_t workspace_bytes, void* hip_stream,
+                              const spec_call_options* options);
+
 size_t spec_lm_head_workspace_bytes(int R, int V, int D);
 
 /* Weights of the draft-length predictor: the SpecKV page's acceptance-rate regressor
@@ -233,27 +295,14 @@ typedef struct {
 int spec_select_gamma(int B, const float* req_stats, const float* comp, spec_gamma_mlp w, int32_t* out_gamma,
                       float* out_expected, void* hip_stream);
 
-/* Benchmark instrumentation.  With two hipEvent_t handles set, every later spec_verify_batch
- * call records `start_event` on its stream right before its dominant streaming kernel (the
- * pass that reads every needed logit row) and `stop_event` right after it, so a benchmark can
- * time that kernel alone.  NULL, NULL switches it off.  Process-wide and not thread-safe;
- * the events stay owned by the caller.  Returns SPEC_ERR_INVALID if only one is NULL. */
-int spec_set_profile_events(void* start_event, void* stop_event);
-
 /* Benchmark instrumentation, not a verification step: a plain streaming read of `bytes` bytes of
  * device memory at `buf` (16-byte aligned, `bytes` a multiple of 16), the practical HBM read
  * ceiling that a benchmark reports beside the streaming kernel's bandwidth.  `sink` is a device
  * pointer to one uint32_t that the kernel writes only when the XOR of all words equals a fixed
- * value (it keeps the reads from being dropped).  Profile events, when set, bracket this kernel
- * too.  Stream-ordered; nothing is allocated.  Returns SPEC_OK (also for bytes == 0),
+ * value (it keeps the reads from being dropped).  Stream-ordered; nothing is allocated.  Returns SPEC_OK (also for bytes == 0),
  * SPEC_ERR_INVALID (bytes < 0, a NULL pointer), SPEC_ERR_UNSUPPORTED (alignment) or
  * SPEC_ERR_LAUNCH. */
 int spec_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* hip_stream);
-
-/* Test hook: the fused kernel's bounded wait for a team gives up after `polls` polls and
- * reports SPEC_STATUS_TIMEOUT for the request (0 = give up at the first incomplete poll).
- * Process-wide; the default is 262144. */
-int spec_set_spin_limit(unsigned polls);
 
 /* Human-readable text for a return code (negative) or a single status bit (positive). */
 const char* spec_status_string(int code);

@@ -13,7 +13,7 @@ import os
 import torch
 
 __all__ = [
-    "SPEC_F32", "SPEC_BF16", "STATUS", "load_library", "library_path",
+    "SPEC_F32", "SPEC_BF16", "STATUS", "PATHS", "load_library", "library_path", "call_options",
     "spec_verify_batch", "spec_row_stats", "spec_residual_sample", "spec_status_string",
     "spec_verify_workspace_bytes", "spec_row_stats_workspace_bytes",
     "spec_residual_sample_workspace_bytes",
@@ -25,6 +25,7 @@ STATUS = {
     "NONFINITE": 1, "BAD_TOKEN": 2, "ZERO_Q": 4, "RESIDUAL_EMPTY": 8, "TIMEOUT": 16,
     "FILTER_OVERFLOW": 32, "BAD_GAMMA": 64,
 }
+PATHS = {"auto": 0, "multi": 1}   # spec_path
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -42,6 +43,27 @@ POS_STATS_FIELDS = ("p_y", "q_y", "one_minus_tv", "draft_entropy_bits", "draft_m
 
 class PosStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in POS_STATS_FIELDS]
+
+
+class CallOptions(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("spin_limit", ctypes.c_int64), ("poll_delay", ctypes.c_int),
+                ("poll_pause", ctypes.c_int), ("profile_start", ctypes.c_void_p), ("profile_stop", ctypes.c_void_p)]
+
+
+def call_options(path="auto", spin_limit=None, poll_delay=None, poll_pause=None, profile_events=None):
+    """A spec_call_options value, or None when every field keeps its default.  path: "auto" or
+    "multi"; spin_limit, poll_delay, poll_pause: ints (None = default); profile_events: a pair
+    of raw hipEvent_t handles recorded around the call's streaming kernel."""
+    if path == "auto" and spin_limit is None and poll_delay is None and poll_pause is None and profile_events is None:
+        return None
+    ev0, ev1 = profile_events if profile_events is not None else (None, None)
+    return CallOptions(PATHS[path], -1 if spin_limit is None else int(spin_limit),
+                       0 if poll_delay is None else int(poll_delay), 0 if poll_pause is None else int(poll_pause),
+                       ev0, ev1)
+
+
+def _opt_ptr(opts):
+    return None if opts is None else ctypes.byref(opts)
 
 
 class GammaMLP(ctypes.Structure):
@@ -63,31 +85,36 @@ def load_library():
                            "`python -m lossless_draft_verification_row_amd.build`")
     lib = ctypes.CDLL(path)
     i32, i64, u64, sz, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p
+    op = ctypes.POINTER(CallOptions)
     lib.spec_verify_batch.restype = i32
     lib.spec_verify_batch.argtypes = [i32, i32, i32, i32, vp, i64, vp, i64, vp, vp, i32, SamplingParams,
                                       u64, u64, vp, vp, PosStats, vp, vp, vp, sz, vp]
+    lib.spec_verify_batch_ex.restype = i32
+    lib.spec_verify_batch_ex.argtypes = lib.spec_verify_batch.argtypes + [op]
     lib.spec_verify_workspace_bytes.restype = sz
     lib.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, i32, SamplingParams]
     lib.spec_row_stats.restype = i32
     lib.spec_row_stats.argtypes = [i32, i32, i32, vp, i64, SamplingParams, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_row_stats_ex.restype = i32
+    lib.spec_row_stats_ex.argtypes = lib.spec_row_stats.argtypes + [op]
     lib.spec_row_stats_workspace_bytes.restype = sz
     lib.spec_row_stats_workspace_bytes.argtypes = [i32, i32, i32, SamplingParams]
     lib.spec_residual_sample.restype = i32
     lib.spec_residual_sample.argtypes = [i32, i32, i32, vp, i64, vp, i64, SamplingParams, vp, u64, u64,
                                          vp, vp, vp, vp, sz, vp]
+    lib.spec_residual_sample_ex.restype = i32
+    lib.spec_residual_sample_ex.argtypes = lib.spec_residual_sample.argtypes + [op]
     lib.spec_residual_sample_workspace_bytes.restype = sz
     lib.spec_residual_sample_workspace_bytes.argtypes = [i32, i32, i32, SamplingParams]
     lib.spec_lm_head_row_stats.restype = i32
     lib.spec_lm_head_row_stats.argtypes = [i32, i32, i32, vp, i64, vp, i64, SamplingParams, vp, vp, vp, vp, vp, vp,
                                            vp, vp, sz, vp]
+    lib.spec_lm_head_row_stats_ex.restype = i32
+    lib.spec_lm_head_row_stats_ex.argtypes = lib.spec_lm_head_row_stats.argtypes + [op]
     lib.spec_lm_head_workspace_bytes.restype = sz
     lib.spec_lm_head_workspace_bytes.argtypes = [i32, i32, i32]
     lib.spec_select_gamma.restype = i32
     lib.spec_select_gamma.argtypes = [i32, vp, vp, GammaMLP, vp, vp, vp]
-    lib.spec_set_spin_limit.restype = i32
-    lib.spec_set_spin_limit.argtypes = [ctypes.c_uint]
-    lib.spec_set_profile_events.restype = i32
-    lib.spec_set_profile_events.argtypes = [vp, vp]
     lib.spec_stream_read.restype = i32
     lib.spec_stream_read.argtypes = [vp, i64, vp, vp]
     lib.spec_status_string.restype = ctypes.c_char_p
@@ -171,8 +198,9 @@ def spec_residual_sample_workspace_bytes(R, V, dtype, temperature, top_k=0, top_
 
 def spec_verify_batch(target_logits, draft_logits, draft_tokens, cu_draft, gamma_max, *,
                       temperature=1.0, top_k=0, top_p=1.0, seed=0, step=0, pos_stats=True,
-                      req_stats=True, kl=False, workspace=None, out=None, stream=None):
-    """Verify one speculative round for B ragged requests (see spec_verify_batch in the header).
+                      req_stats=True, kl=False, workspace=None, out=None, stream=None, options=None):
+    """Verify one speculative round for B ragged requests (see spec_verify_batch in the header;
+    ``options`` is a call_options() value, None for the defaults).
 
     target_logits [sum(g_b + 1), V] and draft_logits [sum g_b, V] (or None: token-only draft)
     are bf16 or fp32 CUDA tensors; draft_tokens [sum g_b] and cu_draft [B + 1] are int32 CUDA
@@ -213,15 +241,15 @@ def spec_verify_batch(target_logits, draft_logits, draft_tokens, cu_draft, gamma
     ps = PosStats(*[_ptr(o.get(k)) for k in POS_STATS_FIELDS])
     need = lib.spec_verify_workspace_bytes(B, V, gamma_max, dt, sp)
     wp, wn = _workspace(need, dev, workspace)
-    rc = lib.spec_verify_batch(B, V, gamma_max, dt, tp, tld, dp, dld, _ptr(draft_tokens), _ptr(cu_draft), Rd,
-                               sp, int(seed) & (2**64 - 1), int(step) & (2**64 - 1),
-                               _ptr(o["tokens"]), _ptr(o["num_accepted"]), ps, _ptr(o.get("req_stats")),
-                               _ptr(o["status"]), wp, wn, _stream(stream))
+    rc = lib.spec_verify_batch_ex(B, V, gamma_max, dt, tp, tld, dp, dld, _ptr(draft_tokens), _ptr(cu_draft), Rd,
+                                  sp, int(seed) & (2**64 - 1), int(step) & (2**64 - 1),
+                                  _ptr(o["tokens"]), _ptr(o["num_accepted"]), ps, _ptr(o.get("req_stats")),
+                                  _ptr(o["status"]), wp, wn, _stream(stream), _opt_ptr(options))
     _check(rc, "spec_verify_batch")
     return o
 
 
-def spec_row_stats(logits, *, temperature=1.0, top_k=0, top_p=1.0, workspace=None, stream=None):
+def spec_row_stats(logits, *, temperature=1.0, top_k=0, top_p=1.0, workspace=None, stream=None, options=None):
     """Per-row statistics of filtered, tempered logit rows.  Returns a dict of [R] tensors:
     max_logit, argmax, log_z, entropy_bits, max_prob, kept_count."""
     lib = load_library()
@@ -240,14 +268,15 @@ def spec_row_stats(logits, *, temperature=1.0, top_k=0, top_p=1.0, workspace=Non
     }
     need = lib.spec_row_stats_workspace_bytes(R, V, dt, sp)
     wp, wn = _workspace(need, dev, workspace)
-    rc = lib.spec_row_stats(R, V, dt, lp, ld, sp, *[_ptr(o[k]) for k in (
-        "max_logit", "argmax", "log_z", "entropy_bits", "max_prob", "kept_count")], wp, wn, _stream(stream))
+    rc = lib.spec_row_stats_ex(R, V, dt, lp, ld, sp, *[_ptr(o[k]) for k in (
+        "max_logit", "argmax", "log_z", "entropy_bits", "max_prob", "kept_count")], wp, wn, _stream(stream),
+        _opt_ptr(options))
     _check(rc, "spec_row_stats")
     return o
 
 
 def spec_residual_sample(p_logits, q_logits=None, *, temperature=1.0, top_k=0, top_p=1.0, uniforms=None,
-                         seed=0, step=0, workspace=None, stream=None):
+                         seed=0, step=0, workspace=None, stream=None, options=None):
     """One draw per row from [p - q]_+ (or p when q_logits is None).  Returns a dict of [R]
     tensors: token (int32), mass (fp64: beta, or 1 without q), status (int32)."""
     lib = load_library()
@@ -267,9 +296,9 @@ def spec_residual_sample(p_logits, q_logits=None, *, temperature=1.0, top_k=0, t
     }
     need = lib.spec_residual_sample_workspace_bytes(R, V, dt, sp)
     wp, wn = _workspace(need, dev, workspace)
-    rc = lib.spec_residual_sample(R, V, dt, pp, pld, qp, qld, sp, _ptr(uniforms), int(seed) & (2**64 - 1),
-                                  int(step) & (2**64 - 1), _ptr(o["token"]), _ptr(o["mass"]), _ptr(o["status"]),
-                                  wp, wn, _stream(stream))
+    rc = lib.spec_residual_sample_ex(R, V, dt, pp, pld, qp, qld, sp, _ptr(uniforms), int(seed) & (2**64 - 1),
+                                     int(step) & (2**64 - 1), _ptr(o["token"]), _ptr(o["mass"]), _ptr(o["status"]),
+                                     wp, wn, _stream(stream), _opt_ptr(options))
     _check(rc, "spec_residual_sample")
     return o
 
@@ -312,7 +341,8 @@ def spec_select_gamma(req_stats, w1, b1, w2, b2, comp=None, stream=None):
 HEAD_FIELDS = ("max_logit", "argmax", "log_z", "entropy_bits", "max_prob", "p_tok")
 
 
-def spec_lm_head_row_stats(hidden, weight, *, temperature=1.0, tokens=None, workspace=None, out=None, stream=None):
+def spec_lm_head_row_stats(hidden, weight, *, temperature=1.0, tokens=None, workspace=None, out=None, stream=None,
+                           options=None):
     """Row statistics of l = hidden @ weight^T without materialising the logits (see
     spec_lm_head_row_stats in the header).  hidden [R, D] and weight [V, D] are bf16 CUDA
     tensors with unit column stride; tokens [R] int32 or None.  Returns a dict of [R] tensors:
@@ -339,7 +369,8 @@ def spec_lm_head_row_stats(hidden, weight, *, temperature=1.0, tokens=None, work
             o["p_tok"] = torch.empty(R, dtype=torch.float32, device=dev)
     need = lib.spec_lm_head_workspace_bytes(R, V, D)
     wsp, wsn = _workspace(need, dev, workspace)
-    rc = lib.spec_lm_head_row_stats(R, V, D, hp, hld, wp_, wld, _sp(temperature, 0, 1.0), _ptr(tokens),
-                                    *[_ptr(o.get(k)) for k in HEAD_FIELDS], wsp, wsn, _stream(stream))
+    rc = lib.spec_lm_head_row_stats_ex(R, V, D, hp, hld, wp_, wld, _sp(temperature, 0, 1.0), _ptr(tokens),
+                                       *[_ptr(o.get(k)) for k in HEAD_FIELDS], wsp, wsn, _stream(stream),
+                                       _opt_ptr(options))
     _check(rc, "spec_lm_head_row_stats")
     return o

@@ -16,38 +16,46 @@ namespace {
 
 constexpr size_t kAlign = 256;
 
-// Benchmark instrumentation (spec_set_profile_events): process-wide, not thread-safe.
-hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
-// Bound of the fused kernel's team wait, in polls (spec_set_spin_limit).
-unsigned g_spin_limit = 1u << 18;
-// Team polling of the streaming kernel: a workgroup waits poll_delay 10-ns ticks after
-// publishing before its first poll of the team's records, and pauses poll_pause x 128 cycles
-// after a failed poll.  Device-scope polls compete with the row stream, so few and late polls
-// are cheaper than early ones.  Tuning knobs: SPEC_VERIFY_POLL_DELAY, SPEC_VERIFY_POLL_PAUSE.
-int env_int(const char* name, int dflt) {
-  const char* e = getenv(name);
-  return (e && e[0]) ? atoi(e) : dflt;
+// A call's options (spec_call_options, every field defaulted when the pointer is NULL).  The
+// single kernel's team wait gives up after spin_limit polls; a member waits poll_delay 10-ns
+// ticks after publishing before its first poll and pauses poll_pause x 128 cycles after a
+// failed one (device-scope polls compete with the row stream, so few and late polls are
+// cheaper than early ones).
+struct Opts {
+  bool multi;            // every kernel of the multi-kernel path (filtered: the dense threshold path)
+  unsigned spin_limit;
+  int poll_delay, poll_pause;
+  hipEvent_t ev0, ev1;   // bracket the streaming kernel, or none
+};
+Opts resolve(const spec_call_options* o) {
+  Opts r;
+  r.multi = o != nullptr && o->path == SPEC_PATH_MULTI_KERNEL;
+  r.spin_limit = (o == nullptr || o->spin_limit < 0) ? (1u << 18)
+                 : (unsigned)(o->spin_limit > 0x7fffffff ? 0x7fffffff : o->spin_limit);
+  r.poll_delay = (o == nullptr || o->poll_delay <= 0) ? 400 : o->poll_delay;
+  r.poll_pause = (o == nullptr || o->poll_pause <= 0) ? 8 : o->poll_pause;
+  r.ev0 = o ? (hipEvent_t)o->profile_start : nullptr;
+  r.ev1 = o ? (hipEvent_t)o->profile_stop : nullptr;
+  return r;
 }
-int poll_delay_ticks() {
-  static const int v = env_int("SPEC_VERIFY_POLL_DELAY", 400);
-  return v;
-}
-int poll_pause() {
-  static const int v = env_int("SPEC_VERIFY_POLL_PAUSE", 8);
-  return v;
+// NULL or a valid path; both profile events or neither.
+bool opts_valid(const spec_call_options* o) {
+  if (o == nullptr) return true;
+  if (o->path != SPEC_PATH_AUTO && o->path != SPEC_PATH_MULTI_KERNEL) return false;
+  return (o->profile_start == nullptr) == (o->profile_stop == nullptr);
 }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-
-bool getenv_flag(const char* name) {
-  const char* v = getenv(name);
-  return v != nullptr && v[0] != '\0' && v[0] != '0';
-}
 
 int n_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
 bool filter_on(int V, const spec_sampling_params& sp) {
   return sp.temperature > 0.f && ((sp.top_k > 0 && sp.top_k < V) || sp.top_p < 1.f);
+}
+
+// log2(e) / T, the scale of every exponent 2^(l c - ref) (0 when greedy).
+float exp2_scale(const spec_sampling_params& sp) {
+  return sp.temperature > 0.f ? (float)(1.4426950408889634 / (double)sp.temperature) : 0.f;
 }
 
 // Sampling parameters: temperature finite and >= 0, top_p > 0 (NaN rejected).
@@ -74,14 +82,77 @@ struct Carve {
   }
 };
 
-// Workspace of the multi-kernel path for n_slots slots (2 logical rows each), after the header.
-size_t dense_bytes(int64_t n_slots, int V) {
+// The multi-kernel arrays, in the order dense_arrays_bytes counts them.
+struct DenseArrays {
+  SlicePart* part;
+  RowStat* rs;
+  double *smass, *amass, *kmass;
+};
+DenseArrays carve_dense(Carve& cv, int64_t n_slots, int ns) {
+  DenseArrays d;
+  d.part = cv.take<SlicePart>((size_t)(2 * n_slots) * ns * slice_part_bytes());
+  d.rs = cv.take<RowStat>((size_t)(2 * n_slots) * row_stat_bytes());
+  d.smass = cv.take<double>((size_t)n_slots * ns * sizeof(double));
+  d.amass = cv.take<double>((size_t)n_slots * ns * sizeof(double));
+  d.kmass = cv.take<double>((size_t)n_slots * ns * 4 * sizeof(double));
+  return d;
+}
+
+PosStatsOut pos_out(const spec_pos_stats& p) {
+  PosStatsOut o;
+  o.p_y = p.p_y;
+  o.q_y = p.q_y;
+  o.one_minus_tv = p.one_minus_tv;
+  o.draft_entropy_bits = p.draft_entropy_bits;
+  o.draft_max_prob = p.draft_max_prob;
+  o.target_entropy_bits = p.target_entropy_bits;
+  o.target_max_prob = p.target_max_prob;
+  o.kl_pq = p.kl_pq;
+  o.kl_qp = p.kl_qp;
+  o.l1 = p.l1;
+  o.accept_prob = p.accept_prob;
+  o.expected_committed = p.expected_committed;
+  return o;
+}
+
+// The dense recomputation of the units the sparse path lists: arrays carved after the sparse
+// ones, the list's length in the workspace header (both zeroed by the sparse path's first
+// kernel).
+FallbackRows fallback_rows(Carve& cv, char* ws, const RowMap& map, int64_t n_units, int64_t n_slots, int unit_lr,
+                           int V, const spec_sampling_params& sp, int want_argmax, DenseArrays& d) {
+  const int ns = n_chunks(V);
+  FallbackRows f;
+  memset(&f, 0, sizeof(f));
+  d = carve_dense(cv, n_slots, ns);
+  f.thr = cv.take<float>((size_t)(2 * n_slots) * sizeof(float));
+  f.list = cv.take<int>((size_t)n_units * sizeof(int));
+  f.list_n = (const int*)(ws + kHdrOvfN);
+  f.map = map;
+  f.map.cu_bad = (const int*)(ws + kHdrCuBad);
+  f.map.thr = f.thr;
+  f.V = V;
+  f.n_slices = ns;
+  f.n_lr = (int)(2 * n_slots);
+  f.unit_lr = unit_lr;
+  f.k = sp.top_k;
+  f.top_p = sp.top_p;
+  f.cthr = 1.4426950408889634 / (double)sp.temperature;
+  f.c = exp2_scale(sp);
+  f.want_argmax = want_argmax;
+  f.part = d.part;
+  f.rs = d.rs;
+  return f;
+}
+
+// Arrays of the multi-kernel path for n_slots slots (2 logical rows each).
+size_t dense_arrays_bytes(int64_t n_slots, int V) {
   const int64_t n_lr = 2 * n_slots;
   const int64_t ns = n_chunks(V);
-  return kHeaderBytes + align_up((size_t)(n_lr * ns) * slice_part_bytes()) +
-         align_up((size_t)n_lr * row_stat_bytes()) + 2 * align_up((size_t)(n_slots * ns) * sizeof(double)) +
-         align_up((size_t)(n_slots * ns * 4) * sizeof(double));
+  return align_up((size_t)(n_lr * ns) * slice_part_bytes()) + align_up((size_t)n_lr * row_stat_bytes()) +
+         2 * align_up((size_t)(n_slots * ns) * sizeof(double)) + align_up((size_t)(n_slots * ns * 4) * sizeof(double));
 }
+// Workspace of the multi-kernel path, after the header.
+size_t dense_bytes(int64_t n_slots, int V) { return kHeaderBytes + dense_arrays_bytes(n_slots, V); }
 
 // Workspace of the fused path for n_teams target rows, after the header.
 size_t fused_bytes(int64_t n_teams, int V) {
@@ -102,28 +173,30 @@ uint32_t next_tag() {
 
 // The fused single-kernel path covers these shapes; the rest takes the multi-kernel path.
 bool fused_ok(int B, int V, int gamma_max) {
-  return B <= kMaxReqFused && (int64_t)B * (gamma_max + 1) <= kMaxTeamsFused && n_chunks(V) <= kMaxSlicesFused &&
-         !getenv_flag("SPEC_VERIFY_NO_FUSED");
+  return B <= kMaxReqFused && (int64_t)B * (gamma_max + 1) <= kMaxTeamsFused && n_chunks(V) <= kMaxSlicesFused;
 }
 
 // The sparse filtered path: T > 0 with top-k on (1 <= k <= 256, k < V; top-p optional), the
 // fused path's shape limits.  Every other filtered call (top-p alone, a larger k, larger
-// shapes) takes the dense threshold path, as does every filtered call when
-// SPEC_VERIFY_DENSE_FILTER is set.
+// shapes) takes the dense threshold path, as does every filtered call asked to take the
+// multi-kernel path.
 bool filter_supported(int B, int V, int gamma_max, const spec_sampling_params& sp) {
   return sp.temperature > 0.f && sp.top_k >= 1 && sp.top_k < V && sp.top_k <= kFilterMaxK && B <= kMaxReqFused &&
-         (int64_t)B * (gamma_max + 1) <= kMaxTeamsFused && n_chunks(V) <= kMaxSlicesFused &&
-         !getenv_flag("SPEC_VERIFY_DENSE_FILTER");
+         (int64_t)B * (gamma_max + 1) <= kMaxTeamsFused && n_chunks(V) <= kMaxSlicesFused;
 }
 // The same sparse path for plain rows (spec_row_stats, spec_residual_sample): R rows, or R row
 // pairs, each one team of its own.
 bool filter_rows_supported(int R, int V, const spec_sampling_params& sp) {
   return sp.temperature > 0.f && sp.top_k >= 1 && sp.top_k < V && sp.top_k <= kFilterMaxK &&
-         n_chunks(V) <= kMaxSlicesFused && (int64_t)R * n_chunks(V) <= 0x3fffffff &&
-         !getenv_flag("SPEC_VERIFY_DENSE_FILTER");
+         n_chunks(V) <= kMaxSlicesFused && (int64_t)R * n_chunks(V) <= 0x3fffffff;
 }
 // Thresholds of the dense filtered path: one float per logical row.
 size_t thr_bytes(int64_t n_slots) { return align_up((size_t)(2 * n_slots) * sizeof(float)); }
+// The sparse path's dense recomputation of listed units: the multi-kernel arrays and thresholds
+// for n_slots slots, and the list of up to n_units units.
+size_t fallback_bytes(int64_t n_units, int64_t n_slots, int V) {
+  return dense_arrays_bytes(n_slots, V) + thr_bytes(n_slots) + align_up((size_t)n_units * sizeof(int));
+}
 size_t filter_bytes(int64_t n_slots, int V, int k) {
   const int64_t ns = n_chunks(V);
   return kHeaderBytes + align_up((size_t)(n_slots * ns * filter_cap(k)) * sizeof(CandEntry)) +
@@ -131,14 +204,11 @@ size_t filter_bytes(int64_t n_slots, int V, int k) {
          align_up((size_t)n_slots * sizeof(RowStat2));
 }
 
-float exp2_scale(const spec_sampling_params& sp) {
-  return sp.temperature > 0.f ? (float)(1.4426950408889634 / (double)sp.temperature) : 0.f;
-}
 
 // Launch descriptor of the sparse path over R plain rows (p rows as targets, q rows, if any,
 // as their draft rows), its arrays carved from the workspace.
 FilterArgs plain_filter_args(int R, int V, const void* p, int64_t p_ld, const void* q, int64_t q_ld,
-                             const spec_sampling_params& sp, void* workspace) {
+                             const spec_sampling_params& sp, Carve& cv) {
   FilterArgs f;
   memset(&f, 0, sizeof(f));
   const int ns = n_chunks(V);
@@ -158,7 +228,6 @@ FilterArgs plain_filter_args(int R, int V, const void* p, int64_t p_ld, const vo
   f.c = 1.4426950408889634 / (double)sp.temperature;
   f.inv_t = 1.0 / (double)sp.temperature;
   f.direct = 1;
-  Carve cv{(char*)workspace};
   f.cand = cv.take<CandEntry>((size_t)f.n_slots * ns * f.cap * sizeof(CandEntry));
   f.chead = cv.take<CandHead>((size_t)f.n_slots * ns * sizeof(CandHead));
   f.kept = cv.take<KeptEntry>((size_t)f.n_slots * kKeepMax * sizeof(KeptEntry));
@@ -182,59 +251,57 @@ const char* spec_status_string(int code) {
     case SPEC_STATUS_ZERO_Q: return "draft probability of the draft token is zero";
     case SPEC_STATUS_RESIDUAL_EMPTY: return "empty residual, drawn from p";
     case SPEC_STATUS_TIMEOUT: return "bounded wait expired";
-    case SPEC_STATUS_FILTER_OVERFLOW: return "filtered row too large for the sparse path";
+    case SPEC_STATUS_FILTER_OVERFLOW: return "filtered row too large for the sparse path (recomputed densely)";
     case SPEC_STATUS_BAD_GAMMA: return "inconsistent draft offsets";
     default: return "unknown code";
   }
 }
 
-int spec_set_spin_limit(unsigned polls) {
-  g_spin_limit = polls;
-  return SPEC_OK;
-}
-
-int spec_set_profile_events(void* start_event, void* stop_event) {
-  if ((start_event == nullptr) != (stop_event == nullptr)) return SPEC_ERR_INVALID;
-  g_prof_start = (hipEvent_t)start_event;
-  g_prof_stop = (hipEvent_t)stop_event;
-  return SPEC_OK;
-}
-
+// Workspace sizes cover every path a call can take (with any options), so a caller sizes once.
 size_t spec_verify_workspace_bytes(int B, int V, int gamma_max, spec_dtype dt, spec_sampling_params sp) {
   (void)dt;
   if (B <= 0 || V <= 0 || gamma_max < 0) return 0;
+  const int64_t n_slots = (int64_t)B * (gamma_max + 1);
+  const size_t dense = dense_bytes(n_slots, V);
   if (filter_on(V, sp)) {
-    if (filter_supported(B, V, gamma_max, sp)) return filter_bytes((int64_t)B * (2 * gamma_max + 1), V, sp.top_k);
-    return dense_bytes((int64_t)B * (gamma_max + 1), V) + thr_bytes((int64_t)B * (gamma_max + 1));
+    const size_t thr = dense + thr_bytes(n_slots);
+    if (!filter_supported(B, V, gamma_max, sp)) return thr;
+    const size_t sparse = filter_bytes((int64_t)B * (2 * gamma_max + 1), V, sp.top_k) + fallback_bytes(B, n_slots, V);
+    return sparse > thr ? sparse : thr;
   }
-  const size_t dense = dense_bytes((int64_t)B * (gamma_max + 1), V);
-  const size_t fused = fused_bytes((int64_t)B * (gamma_max + 1), V);
+  const size_t fused = fused_bytes(n_slots, V);
   return dense > fused ? dense : fused;
 }
 
 size_t spec_row_stats_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling_params sp) {
   (void)dt;
   if (R <= 0 || V <= 0) return 0;
-  if (filter_on(V, sp)) return filter_rows_supported(R, V, sp) ? filter_bytes(R, V, sp.top_k) : dense_bytes(R, V) + thr_bytes(R);
-  return dense_bytes(R, V);
+  if (!filter_on(V, sp)) return dense_bytes(R, V);
+  const size_t thr = dense_bytes(R, V) + thr_bytes(R);
+  if (!filter_rows_supported(R, V, sp)) return thr;
+  const size_t sparse = filter_bytes(R, V, sp.top_k) + fallback_bytes(R, R, V);
+  return sparse > thr ? sparse : thr;
 }
 
 size_t spec_residual_sample_workspace_bytes(int R, int V, spec_dtype dt, spec_sampling_params sp) {
   (void)dt;
   if (R <= 0 || V <= 0) return 0;
-  if (filter_on(V, sp))
-    return filter_rows_supported(R, V, sp) ? filter_bytes(2 * (int64_t)R, V, sp.top_k) : dense_bytes(R, V) + thr_bytes(R);
-  return dense_bytes(R, V);
+  if (!filter_on(V, sp)) return dense_bytes(R, V);
+  const size_t thr = dense_bytes(R, V) + thr_bytes(R);
+  if (!filter_rows_supported(R, V, sp)) return thr;
+  const size_t sparse = filter_bytes(2 * (int64_t)R, V, sp.top_k) + fallback_bytes(R, R, V);
+  return sparse > thr ? sparse : thr;
 }
 
-int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* target_logits,
-                      int64_t target_ld, const void* draft_logits, int64_t draft_ld,
-                      const int32_t* draft_tokens, const int32_t* cu_draft, int n_draft_rows,
-                      spec_sampling_params sp, uint64_t seed, uint64_t step, int32_t* out_tokens,
-                      int32_t* out_num_accepted, spec_pos_stats pos_stats, float* out_req_stats,
-                      int32_t* out_status, void* workspace, size_t workspace_bytes, void* hip_stream) {
+int spec_verify_batch_ex(int B, int V, int gamma_max, spec_dtype dt, const void* target_logits, int64_t target_ld,
+                         const void* draft_logits, int64_t draft_ld, const int32_t* draft_tokens,
+                         const int32_t* cu_draft, int n_draft_rows, spec_sampling_params sp, uint64_t seed,
+                         uint64_t step, int32_t* out_tokens, int32_t* out_num_accepted, spec_pos_stats pos_stats,
+                         float* out_req_stats, int32_t* out_status, void* workspace, size_t workspace_bytes,
+                         void* hip_stream, const spec_call_options* options) {
   if (B < 0 || V <= 0 || gamma_max < 0 || gamma_max > kMaxGamma) return SPEC_ERR_INVALID;
   if (dt != SPEC_F32 && dt != SPEC_BF16) return SPEC_ERR_INVALID;
+  if (!opts_valid(options)) return SPEC_ERR_INVALID;
   if (V > kMaxChunks * kChunk) return SPEC_ERR_UNSUPPORTED;
   if (check_params(sp) != SPEC_OK) return SPEC_ERR_INVALID;
   if (B == 0) return SPEC_OK;
@@ -244,9 +311,10 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   if (n_draft_rows > 0 && !draft_tokens) return SPEC_ERR_INVALID;
   if (draft_logits && draft_ld < V) return SPEC_ERR_INVALID;
   if ((int64_t)B * (gamma_max + 1) * 2 > (int64_t)INT32_MAX / 2) return SPEC_ERR_INVALID;
+  const Opts op = resolve(options);
   const bool greedy = sp.temperature == 0.f;
   const bool filtered = filter_on(V, sp);
-  const bool sparse = filtered && filter_supported(B, V, gamma_max, sp);
+  const bool sparse = filtered && !op.multi && filter_supported(B, V, gamma_max, sp);
   const size_t need = spec_verify_workspace_bytes(B, V, gamma_max, dt, sp);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SPEC_ERR_WORKSPACE;
   if (((uintptr_t)workspace % kAlign) != 0) return SPEC_ERR_INVALID;
@@ -255,6 +323,8 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   const int n_slots = B * (gamma_max + 1);
   const int ns = n_chunks(V);
   const void* drf = greedy ? nullptr : draft_logits;
+  const PosStatsOut po = pos_out(pos_stats);
+  const bool want_kl = pos_stats.kl_pq != nullptr || pos_stats.kl_qp != nullptr;
 
   RowMap map;
   memset(&map, 0, sizeof(map));
@@ -267,9 +337,28 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   map.G = gamma_max;
   map.n_draft_rows = n_draft_rows;
 
+  // the multi-kernel path's finalize arguments (also those of the sparse path's dense
+  // recomputation); the arrays are filled in where they are carved
+  FinalizeArgs fa;
+  memset(&fa, 0, sizeof(fa));
+  fa.V = V;
+  fa.n_slices = ns;
+  fa.greedy = greedy;
+  fa.c = exp2_scale(sp);
+  fa.inv_t = greedy ? 0.0 : 1.0 / (double)sp.temperature;
+  fa.seed = seed;
+  fa.step = step;
+  fa.tokens = draft_tokens;
+  fa.out_tokens = out_tokens;
+  fa.out_num_accepted = out_num_accepted;
+  fa.out_req_stats = out_req_stats;
+  fa.out_status = out_status;
+  fa.st = po;
+
   char* ws = (char*)workspace;
   const int dtc = dt == SPEC_BF16 ? kDtBF16 : kDtF32;
   const bool vec = aligned16(target_logits, target_ld, dt) && aligned16(drf, draft_ld, dt);
+  fa.vec = vec ? 1 : 0;
   if (sparse) {
     FilterArgs f;
     memset(&f, 0, sizeof(f));
@@ -303,23 +392,25 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
     f.out_num_accepted = out_num_accepted;
     f.out_req_stats = out_req_stats;
     f.out_status = out_status;
-    f.st.p_y = pos_stats.p_y;
-    f.st.q_y = pos_stats.q_y;
-    f.st.one_minus_tv = pos_stats.one_minus_tv;
-    f.st.draft_entropy_bits = pos_stats.draft_entropy_bits;
-    f.st.draft_max_prob = pos_stats.draft_max_prob;
-    f.st.target_entropy_bits = pos_stats.target_entropy_bits;
-    f.st.target_max_prob = pos_stats.target_max_prob;
-    f.st.kl_pq = pos_stats.kl_pq;
-    f.st.kl_qp = pos_stats.kl_qp;
-    f.st.l1 = pos_stats.l1;
-    f.st.accept_prob = pos_stats.accept_prob;
-    f.st.expected_committed = pos_stats.expected_committed;
-    const hipError_t e = launch_filter(f, dtc, vec, st, g_prof_start, g_prof_stop);
-    return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
+    f.st = po;
+    // requests the sparse sets cannot hold are recomputed on the dense threshold path
+    DenseArrays d;
+    const FallbackRows fb = fallback_rows(cv, ws, map, B, n_slots, 2 * (gamma_max + 1), V, sp, 0, d);
+    f.ovf_list = (int*)fb.list;
+    f.ovf_n = (int*)(ws + kHdrOvfN);
+    f.cu_bad0 = (int*)(ws + kHdrCuBad);
+    if (launch_filter(f, dtc, vec, st, op.ev0, op.ev1) != hipSuccess) return SPEC_ERR_LAUNCH;
+    fa.map = fb.map;
+    fa.rs = d.rs;
+    fa.part = d.part;
+    fa.smass = d.smass;
+    fa.amass = d.amass;
+    fa.kmass = d.kmass;
+    if (launch_fallback_rows(fb, dtc, vec, st) != hipSuccess) return SPEC_ERR_LAUNCH;
+    if (launch_fallback_requests(fb, fa, want_kl ? 1 : 0, dtc, vec, st) != hipSuccess) return SPEC_ERR_LAUNCH;
+    return SPEC_OK;
   }
-  const bool want_kl = pos_stats.kl_pq != nullptr || pos_stats.kl_qp != nullptr;
-  if (!filtered && !want_kl && fused_ok(B, V, gamma_max)) {
+  if (!filtered && !want_kl && !op.multi && fused_ok(B, V, gamma_max)) {
     FusedArgs f;
     memset(&f, 0, sizeof(f));
     f.tgt = target_logits;
@@ -337,7 +428,7 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
     f.n_tickets = f.n_teams * ns;
     f.mode = greedy ? kFuGreedy : (drf ? kFuSample : kFuTokenOnly);
     f.want_t_ent = pos_stats.target_entropy_bits != nullptr;
-    f.spin_limit = g_spin_limit;
+    f.spin_limit = op.spin_limit;
     f.c = exp2_scale(sp);
     f.seed = seed;
     f.step = step;
@@ -349,28 +440,17 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
     {
       // every request has G draft rows exactly when the rows number B G (a valid offset array
       // has no request above G): then a team's rows follow from its place, else from a map
-      int32_t* map = cv.take<int32_t>((size_t)f.n_teams * sizeof(int32_t));
-      f.team_row = (int64_t)n_draft_rows == (int64_t)B * gamma_max ? nullptr : map;
+      int32_t* tmap = cv.take<int32_t>((size_t)f.n_teams * sizeof(int32_t));
+      f.team_row = (int64_t)n_draft_rows == (int64_t)B * gamma_max ? nullptr : tmap;
     }
-    f.poll_delay = poll_delay_ticks();
-    f.poll_pause = poll_pause();
+    f.poll_delay = op.poll_delay;
+    f.poll_pause = op.poll_pause;
     f.out_tokens = out_tokens;
     f.out_num_accepted = out_num_accepted;
     f.out_req_stats = out_req_stats;
     f.out_status = out_status;
-    f.st.p_y = pos_stats.p_y;
-    f.st.q_y = pos_stats.q_y;
-    f.st.one_minus_tv = pos_stats.one_minus_tv;
-    f.st.draft_entropy_bits = pos_stats.draft_entropy_bits;
-    f.st.draft_max_prob = pos_stats.draft_max_prob;
-    f.st.target_entropy_bits = pos_stats.target_entropy_bits;
-    f.st.target_max_prob = pos_stats.target_max_prob;
-    f.st.kl_pq = pos_stats.kl_pq;
-    f.st.kl_qp = pos_stats.kl_qp;
-    f.st.l1 = pos_stats.l1;
-    f.st.accept_prob = pos_stats.accept_prob;
-    f.st.expected_committed = pos_stats.expected_committed;
-    const hipError_t e = launch_fused(f, dtc, vec, st, g_prof_start, g_prof_stop);
+    f.st = po;
+    const hipError_t e = launch_fused(f, dtc, vec, st, op.ev0, op.ev1);
     return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
   }
 
@@ -378,6 +458,7 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   if (launch_check_cu(cu_draft, B, gamma_max, n_draft_rows, cu_bad, st) != hipSuccess) return SPEC_ERR_LAUNCH;
   map.cu_bad = cu_bad;
   Carve cv{ws};
+  const DenseArrays d = carve_dense(cv, n_slots, ns);
   DenseLaunch L;
   memset(&L, 0, sizeof(L));
   L.map = map;
@@ -391,11 +472,11 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
   L.pair = (!greedy && drf != nullptr) ? 1 : 0;
   L.want_kl = want_kl ? 1 : 0;
   L.vec = vec;
-  L.part = cv.take<SlicePart>((size_t)(2 * n_slots) * ns * slice_part_bytes());
-  L.rs = cv.take<RowStat>((size_t)(2 * n_slots) * row_stat_bytes());
-  L.smass = cv.take<double>((size_t)n_slots * ns * sizeof(double));
-  L.amass = cv.take<double>((size_t)n_slots * ns * sizeof(double));
-  L.kmass = cv.take<double>((size_t)n_slots * ns * 4 * sizeof(double));
+  L.part = d.part;
+  L.rs = d.rs;
+  L.smass = d.smass;
+  L.amass = d.amass;
+  L.kmass = d.kmass;
   if (filtered) {
     float* thr = cv.take<float>((size_t)(2 * n_slots) * sizeof(float));
     if (launch_threshold(map, dtc, vec, V, 2 * n_slots, sp.top_k, sp.top_p, 1.4426950408889634 / (double)sp.temperature,
@@ -405,51 +486,36 @@ int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* ta
     L.map = map;
   }
   L.rso.enabled = 0;
-  L.ev_start = g_prof_start;
-  L.ev_stop = g_prof_stop;
+  L.ev_start = op.ev0;
+  L.ev_stop = op.ev1;
   if (launch_dense(L, st) != hipSuccess) return SPEC_ERR_LAUNCH;
-
-  FinalizeArgs a;
-  memset(&a, 0, sizeof(a));
-  a.map = map;
-  a.V = V;
-  a.n_slices = ns;
-  a.greedy = greedy;
-  a.c = L.c;
-  a.inv_t = greedy ? 0.0 : 1.0 / (double)sp.temperature;
-  a.seed = seed;
-  a.step = step;
-  a.tokens = draft_tokens;
-  a.rs = L.rs;
-  a.part = L.part;
-  a.smass = L.smass;
-  a.amass = L.amass;
-  a.kmass = L.kmass;
-  a.out_tokens = out_tokens;
-  a.out_num_accepted = out_num_accepted;
-  a.out_req_stats = out_req_stats;
-  a.out_status = out_status;
-  a.st.p_y = pos_stats.p_y;
-  a.st.q_y = pos_stats.q_y;
-  a.st.one_minus_tv = pos_stats.one_minus_tv;
-  a.st.draft_entropy_bits = pos_stats.draft_entropy_bits;
-  a.st.draft_max_prob = pos_stats.draft_max_prob;
-  a.st.target_entropy_bits = pos_stats.target_entropy_bits;
-  a.st.target_max_prob = pos_stats.target_max_prob;
-  a.st.kl_pq = pos_stats.kl_pq;
-  a.st.kl_qp = pos_stats.kl_qp;
-  a.st.l1 = pos_stats.l1;
-  a.st.accept_prob = pos_stats.accept_prob;
-  a.st.expected_committed = pos_stats.expected_committed;
-  if (launch_finalize(a, L.dt, st) != hipSuccess) return SPEC_ERR_LAUNCH;
+  fa.map = map;
+  fa.rs = L.rs;
+  fa.part = L.part;
+  fa.smass = L.smass;
+  fa.amass = L.amass;
+  fa.kmass = L.kmass;
+  if (launch_finalize(fa, L.dt, st) != hipSuccess) return SPEC_ERR_LAUNCH;
   return SPEC_OK;
 }
 
-int spec_row_stats(int R, int V, spec_dtype dt, const void* logits, int64_t ld, spec_sampling_params sp,
-                   float* max_logit, int32_t* argmax, float* log_z, float* entropy_bits, float* max_prob,
-                   int32_t* kept_count, void* workspace, size_t workspace_bytes, void* hip_stream) {
+int spec_verify_batch(int B, int V, int gamma_max, spec_dtype dt, const void* target_logits, int64_t target_ld,
+                      const void* draft_logits, int64_t draft_ld, const int32_t* draft_tokens, const int32_t* cu_draft,
+                      int n_draft_rows, spec_sampling_params sp, uint64_t seed, uint64_t step, int32_t* out_tokens,
+                      int32_t* out_num_accepted, spec_pos_stats pos_stats, float* out_req_stats, int32_t* out_status,
+                      void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return spec_verify_batch_ex(B, V, gamma_max, dt, target_logits, target_ld, draft_logits, draft_ld, draft_tokens,
+                              cu_draft, n_draft_rows, sp, seed, step, out_tokens, out_num_accepted, pos_stats,
+                              out_req_stats, out_status, workspace, workspace_bytes, hip_stream, nullptr);
+}
+
+int spec_row_stats_ex(int R, int V, spec_dtype dt, const void* logits, int64_t ld, spec_sampling_params sp,
+                      float* max_logit, int32_t* argmax, float* log_z, float* entropy_bits, float* max_prob,
+                      int32_t* kept_count, void* workspace, size_t workspace_bytes, void* hip_stream,
+                      const spec_call_options* options) {
   if (R < 0 || V <= 0) return SPEC_ERR_INVALID;
   if (dt != SPEC_F32 && dt != SPEC_BF16) return SPEC_ERR_INVALID;
+  if (!opts_valid(options)) return SPEC_ERR_INVALID;
   if (V > kMaxChunks * kChunk) return SPEC_ERR_UNSUPPORTED;
   if (check_params(sp) != SPEC_OK) return SPEC_ERR_INVALID;
   if (R == 0) return SPEC_OK;
@@ -458,32 +524,48 @@ int spec_row_stats(int R, int V, spec_dtype dt, const void* logits, int64_t ld, 
   const size_t need = spec_row_stats_workspace_bytes(R, V, dt, sp);
   if (!workspace || workspace_bytes < need) return SPEC_ERR_WORKSPACE;
   if (((uintptr_t)workspace % kAlign) != 0) return SPEC_ERR_INVALID;
+  const Opts op = resolve(options);
   const bool greedy = sp.temperature == 0.f;
   const int ns = n_chunks(V);
-  if (filter_on(V, sp) && filter_rows_supported(R, V, sp)) {
-    FilterArgs f = plain_filter_args(R, V, logits, ld, nullptr, 0, sp, workspace);
-    f.rso.enabled = 1;
-    f.rso.max_logit = max_logit;
-    f.rso.argmax = argmax;
-    f.rso.log_z = log_z;
-    f.rso.entropy_bits = entropy_bits;
-    f.rso.max_prob = max_prob;
-    f.rso.kept_count = kept_count;
-    const hipError_t e = launch_filter_rows(f, dt == SPEC_BF16 ? kDtBF16 : kDtF32, aligned16(logits, ld, dt) ? 1 : 0, 0,
-                                            (hipStream_t)hip_stream);
-    return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
-  }
+  const int dtc = dt == SPEC_BF16 ? kDtBF16 : kDtF32;
+  const int vec = aligned16(logits, ld, dt) ? 1 : 0;
+  const hipStream_t st = (hipStream_t)hip_stream;
+  RowStatsOut rso;
+  rso.enabled = 1;
+  rso.max_logit = max_logit;
+  rso.argmax = argmax;
+  rso.log_z = log_z;
+  rso.entropy_bits = entropy_bits;
+  rso.max_prob = max_prob;
+  rso.kept_count = kept_count;
 
   RowMap map;
   memset(&map, 0, sizeof(map));
   map.tgt = logits;
   map.tgt_ld = ld;
   map.B = R;
+  if (filter_on(V, sp) && !op.multi && filter_rows_supported(R, V, sp)) {
+    Carve cv{(char*)workspace};
+    FilterArgs f = plain_filter_args(R, V, logits, ld, nullptr, 0, sp, cv);
+    f.rso = rso;
+    // rows the sparse sets cannot hold are recomputed on the dense threshold path
+    DenseArrays d;
+    FallbackRows fb = fallback_rows(cv, (char*)workspace, map, R, R, 2, V, sp, 1, d);
+    fb.rso = rso;
+    f.ovf_list = (int*)fb.list;
+    f.ovf_n = (int*)((char*)workspace + kHdrOvfN);
+    f.cu_bad0 = (int*)((char*)workspace + kHdrCuBad);
+    if (launch_filter_rows(f, dtc, vec, 0, st) != hipSuccess) return SPEC_ERR_LAUNCH;
+    if (launch_fallback_rows(fb, dtc, vec, st) != hipSuccess) return SPEC_ERR_LAUNCH;
+    return SPEC_OK;
+  }
+
   Carve cv{(char*)workspace};
+  const DenseArrays d = carve_dense(cv, R, ns);
   DenseLaunch L;
   memset(&L, 0, sizeof(L));
   L.map = map;
-  L.dt = dt == SPEC_BF16 ? kDtBF16 : kDtF32;
+  L.dt = dtc;
   L.V = V;
   L.n_slices = ns;
   L.n_slots = R;
@@ -491,37 +573,42 @@ int spec_row_stats(int R, int V, spec_dtype dt, const void* logits, int64_t ld, 
   L.greedy = greedy;
   L.want_argmax = 1;
   L.pair = 0;
-  L.vec = aligned16(logits, ld, dt);
-  L.part = cv.take<SlicePart>((size_t)(2 * R) * ns * slice_part_bytes());
-  L.rs = cv.take<RowStat>((size_t)(2 * R) * row_stat_bytes());
-  L.smass = cv.take<double>((size_t)R * ns * sizeof(double));
-  L.amass = cv.take<double>((size_t)R * ns * sizeof(double));
-  L.kmass = cv.take<double>((size_t)R * ns * 4 * sizeof(double));
+  L.vec = vec;
+  L.part = d.part;
+  L.rs = d.rs;
+  L.smass = d.smass;
+  L.amass = d.amass;
+  L.kmass = d.kmass;
   if (filter_on(V, sp)) {
     float* thr = cv.take<float>((size_t)(2 * R) * sizeof(float));
     if (launch_threshold(map, L.dt, L.vec, V, 2 * R, sp.top_k, sp.top_p, 1.4426950408889634 / (double)sp.temperature,
-                         thr, (hipStream_t)hip_stream) != hipSuccess)
+                         thr, st) != hipSuccess)
       return SPEC_ERR_LAUNCH;
     map.thr = thr;
     L.map = map;
   }
-  L.rso.enabled = 1;
-  L.rso.max_logit = max_logit;
-  L.rso.argmax = argmax;
-  L.rso.log_z = log_z;
-  L.rso.entropy_bits = entropy_bits;
-  L.rso.max_prob = max_prob;
-  L.rso.kept_count = kept_count;
-  if (launch_dense(L, (hipStream_t)hip_stream) != hipSuccess) return SPEC_ERR_LAUNCH;
+  L.rso = rso;
+  L.ev_start = op.ev0;
+  L.ev_stop = op.ev1;
+  if (launch_dense(L, st) != hipSuccess) return SPEC_ERR_LAUNCH;
   return SPEC_OK;
 }
 
-int spec_residual_sample(int R, int V, spec_dtype dt, const void* p_logits, int64_t p_ld, const void* q_logits,
-                         int64_t q_ld, spec_sampling_params sp, const double* uniforms, uint64_t seed,
-                         uint64_t step, int32_t* out_token, double* out_mass, int32_t* out_status,
-                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+int spec_row_stats(int R, int V, spec_dtype dt, const void* logits, int64_t ld, spec_sampling_params sp,
+                   float* max_logit, int32_t* argmax, float* log_z, float* entropy_bits, float* max_prob,
+                   int32_t* kept_count, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return spec_row_stats_ex(R, V, dt, logits, ld, sp, max_logit, argmax, log_z, entropy_bits, max_prob, kept_count,
+                           workspace, workspace_bytes, hip_stream, nullptr);
+}
+
+int spec_residual_sample_ex(int R, int V, spec_dtype dt, const void* p_logits, int64_t p_ld, const void* q_logits,
+                            int64_t q_ld, spec_sampling_params sp, const double* uniforms, uint64_t seed,
+                            uint64_t step, int32_t* out_token, double* out_mass, int32_t* out_status,
+                            void* workspace, size_t workspace_bytes, void* hip_stream,
+                            const spec_call_options* options) {
   if (R < 0 || V <= 0) return SPEC_ERR_INVALID;
   if (dt != SPEC_F32 && dt != SPEC_BF16) return SPEC_ERR_INVALID;
+  if (!opts_valid(options)) return SPEC_ERR_INVALID;
   if (V > kMaxChunks * kChunk) return SPEC_ERR_UNSUPPORTED;
   if (check_params(sp) != SPEC_OK) return SPEC_ERR_INVALID;
   if (R == 0) return SPEC_OK;
@@ -531,21 +618,12 @@ int spec_residual_sample(int R, int V, spec_dtype dt, const void* p_logits, int6
   const size_t need = spec_residual_sample_workspace_bytes(R, V, dt, sp);
   if (!workspace || workspace_bytes < need) return SPEC_ERR_WORKSPACE;
   if (((uintptr_t)workspace % kAlign) != 0) return SPEC_ERR_INVALID;
+  const Opts op = resolve(options);
   const bool greedy = sp.temperature == 0.f;
   const int ns = n_chunks(V);
+  const int dtc = dt == SPEC_BF16 ? kDtBF16 : kDtF32;
+  const int vec = (aligned16(p_logits, p_ld, dt) && aligned16(q_logits, q_ld, dt)) ? 1 : 0;
   const hipStream_t st = (hipStream_t)hip_stream;
-  if (filter_on(V, sp) && filter_rows_supported(R, V, sp)) {
-    FilterArgs f = plain_filter_args(R, V, p_logits, p_ld, q_logits, q_ld, sp, workspace);
-    f.uniforms = uniforms;
-    f.seed = seed;
-    f.step = step;
-    f.out_tokens = out_token;
-    f.out_mass = out_mass;
-    f.out_status = out_status;
-    const int vec = aligned16(p_logits, p_ld, dt) && aligned16(q_logits, q_ld, dt);
-    const hipError_t e = launch_filter_rows(f, dt == SPEC_BF16 ? kDtBF16 : kDtF32, vec, 1, st);
-    return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
-  }
 
   RowMap map;
   memset(&map, 0, sizeof(map));
@@ -554,11 +632,49 @@ int spec_residual_sample(int R, int V, spec_dtype dt, const void* p_logits, int6
   map.drf = q_logits;
   map.drf_ld = q_ld;
   map.B = R;
+  ResidualArgs ra;
+  memset(&ra, 0, sizeof(ra));
+  ra.V = V;
+  ra.n_slices = ns;
+  ra.greedy = greedy;
+  ra.c = exp2_scale(sp);
+  ra.seed = seed;
+  ra.step = step;
+  ra.uniforms = uniforms;
+  ra.out_token = out_token;
+  ra.out_mass = out_mass;
+  ra.out_status = out_status;
+  if (filter_on(V, sp) && !op.multi && filter_rows_supported(R, V, sp)) {
+    Carve cv{(char*)workspace};
+    FilterArgs f = plain_filter_args(R, V, p_logits, p_ld, q_logits, q_ld, sp, cv);
+    f.uniforms = uniforms;
+    f.seed = seed;
+    f.step = step;
+    f.out_tokens = out_token;
+    f.out_mass = out_mass;
+    f.out_status = out_status;
+    // rows the sparse sets cannot hold are recomputed on the dense threshold path
+    DenseArrays d;
+    const FallbackRows fb = fallback_rows(cv, (char*)workspace, map, R, R, 2, V, sp, 0, d);
+    f.ovf_list = (int*)fb.list;
+    f.ovf_n = (int*)((char*)workspace + kHdrOvfN);
+    f.cu_bad0 = (int*)((char*)workspace + kHdrCuBad);
+    if (launch_filter_rows(f, dtc, vec, 1, st) != hipSuccess) return SPEC_ERR_LAUNCH;
+    ra.map = fb.map;
+    ra.rs = d.rs;
+    ra.part = d.part;
+    ra.smass = d.smass;
+    if (launch_fallback_rows(fb, dtc, vec, st) != hipSuccess) return SPEC_ERR_LAUNCH;
+    if (launch_fallback_residual(fb, ra, d.amass, dtc, vec, st) != hipSuccess) return SPEC_ERR_LAUNCH;
+    return SPEC_OK;
+  }
+
   Carve cv{(char*)workspace};
+  const DenseArrays d = carve_dense(cv, R, ns);
   DenseLaunch L;
   memset(&L, 0, sizeof(L));
   L.map = map;
-  L.dt = dt == SPEC_BF16 ? kDtBF16 : kDtF32;
+  L.dt = dtc;
   L.V = V;
   L.n_slices = ns;
   L.n_slots = R;
@@ -566,12 +682,12 @@ int spec_residual_sample(int R, int V, spec_dtype dt, const void* p_logits, int6
   L.greedy = greedy;
   L.want_argmax = 0;
   L.pair = (!greedy && q_logits != nullptr) ? 1 : 0;
-  L.vec = aligned16(p_logits, p_ld, dt) && aligned16(q_logits, q_ld, dt);
-  L.part = cv.take<SlicePart>((size_t)(2 * R) * ns * slice_part_bytes());
-  L.rs = cv.take<RowStat>((size_t)(2 * R) * row_stat_bytes());
-  L.smass = cv.take<double>((size_t)R * ns * sizeof(double));
-  L.amass = cv.take<double>((size_t)R * ns * sizeof(double));
-  L.kmass = cv.take<double>((size_t)R * ns * 4 * sizeof(double));
+  L.vec = vec;
+  L.part = d.part;
+  L.rs = d.rs;
+  L.smass = d.smass;
+  L.amass = d.amass;
+  L.kmass = d.kmass;
   if (filter_on(V, sp)) {
     float* thr = cv.take<float>((size_t)(2 * R) * sizeof(float));
     if (launch_threshold(map, L.dt, L.vec, V, 2 * R, sp.top_k, sp.top_p, 1.4426950408889634 / (double)sp.temperature,
@@ -581,26 +697,23 @@ int spec_residual_sample(int R, int V, spec_dtype dt, const void* p_logits, int6
     L.map = map;
   }
   L.rso.enabled = 0;
+  L.ev_start = op.ev0;
+  L.ev_stop = op.ev1;
   if (launch_dense(L, st) != hipSuccess) return SPEC_ERR_LAUNCH;
-
-  ResidualArgs a;
-  memset(&a, 0, sizeof(a));
-  a.map = map;
-  a.V = V;
-  a.n_slices = ns;
-  a.greedy = greedy;
-  a.c = L.c;
-  a.seed = seed;
-  a.step = step;
-  a.uniforms = uniforms;
-  a.rs = L.rs;
-  a.part = L.part;
-  a.smass = L.smass;
-  a.out_token = out_token;
-  a.out_mass = out_mass;
-  a.out_status = out_status;
-  if (launch_residual_finalize(a, L.dt, st) != hipSuccess) return SPEC_ERR_LAUNCH;
+  ra.map = map;
+  ra.rs = L.rs;
+  ra.part = L.part;
+  ra.smass = L.smass;
+  if (launch_residual_finalize(ra, L.dt, st) != hipSuccess) return SPEC_ERR_LAUNCH;
   return SPEC_OK;
+}
+
+int spec_residual_sample(int R, int V, spec_dtype dt, const void* p_logits, int64_t p_ld, const void* q_logits,
+                         int64_t q_ld, spec_sampling_params sp, const double* uniforms, uint64_t seed,
+                         uint64_t step, int32_t* out_token, double* out_mass, int32_t* out_status,
+                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return spec_residual_sample_ex(R, V, dt, p_logits, p_ld, q_logits, q_ld, sp, uniforms, seed, step, out_token,
+                                 out_mass, out_status, workspace, workspace_bytes, hip_stream, nullptr);
 }
 
 size_t spec_lm_head_workspace_bytes(int R, int V, int D) {
@@ -609,11 +722,13 @@ size_t spec_lm_head_workspace_bytes(int R, int V, int D) {
   return kHeaderBytes + align_up((size_t)R * n_ct * sizeof(HeadRec)) + align_up((size_t)R * sizeof(float));
 }
 
-int spec_lm_head_row_stats(int R, int V, int D, const void* hidden, int64_t h_ld, const void* weight, int64_t w_ld,
-                           spec_sampling_params sp, const int32_t* tokens, float* max_logit, int32_t* argmax,
-                           float* log_z, float* entropy_bits, float* max_prob, float* p_tok, void* workspace,
-                           size_t workspace_bytes, void* hip_stream) {
+int spec_lm_head_row_stats_ex(int R, int V, int D, const void* hidden, int64_t h_ld, const void* weight,
+                              int64_t w_ld, spec_sampling_params sp, const int32_t* tokens, float* max_logit,
+                              int32_t* argmax, float* log_z, float* entropy_bits, float* max_prob, float* p_tok,
+                              void* workspace, size_t workspace_bytes, void* hip_stream,
+                              const spec_call_options* options) {
   if (R < 0 || V <= 0 || D <= 0) return SPEC_ERR_INVALID;
+  if (!opts_valid(options)) return SPEC_ERR_INVALID;
   if (check_params(sp) != SPEC_OK) return SPEC_ERR_INVALID;
   if (filter_on(V, sp)) return SPEC_ERR_UNSUPPORTED;
   if (R == 0) return SPEC_OK;
@@ -629,6 +744,7 @@ int spec_lm_head_row_stats(int R, int V, int D, const void* hidden, int64_t h_ld
   const size_t need = spec_lm_head_workspace_bytes(R, V, D);
   if (!workspace || workspace_bytes < need) return SPEC_ERR_WORKSPACE;
   if (((uintptr_t)workspace % kAlign) != 0) return SPEC_ERR_INVALID;
+  const Opts op = resolve(options);
   HeadArgs a;
   memset(&a, 0, sizeof(a));
   a.hidden = hidden;
@@ -652,8 +768,16 @@ int spec_lm_head_row_stats(int R, int V, int D, const void* hidden, int64_t h_ld
   a.entropy_bits = entropy_bits;
   a.max_prob = max_prob;
   a.p_tok = p_tok;
-  const hipError_t e = launch_head(a, (hipStream_t)hip_stream, g_prof_start, g_prof_stop);
+  const hipError_t e = launch_head(a, (hipStream_t)hip_stream, op.ev0, op.ev1);
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
+}
+
+int spec_lm_head_row_stats(int R, int V, int D, const void* hidden, int64_t h_ld, const void* weight, int64_t w_ld,
+                           spec_sampling_params sp, const int32_t* tokens, float* max_logit, int32_t* argmax,
+                           float* log_z, float* entropy_bits, float* max_prob, float* p_tok, void* workspace,
+                           size_t workspace_bytes, void* hip_stream) {
+  return spec_lm_head_row_stats_ex(R, V, D, hidden, h_ld, weight, w_ld, sp, tokens, max_logit, argmax, log_z,
+                                   entropy_bits, max_prob, p_tok, workspace, workspace_bytes, hip_stream, nullptr);
 }
 
 int spec_select_gamma(int B, const float* req_stats, const float* comp, spec_gamma_mlp w, int32_t* out_gamma,
@@ -670,7 +794,7 @@ int spec_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* hip_s
   if (bytes < 0 || (bytes > 0 && !buf) || !sink) return SPEC_ERR_INVALID;
   if (bytes % 16 != 0 || ((uintptr_t)buf & 15u) != 0) return SPEC_ERR_UNSUPPORTED;
   if (bytes == 0) return SPEC_OK;
-  const hipError_t e = launch_stream_read(buf, bytes / 16, sink, (hipStream_t)hip_stream, g_prof_start, g_prof_stop);
+  const hipError_t e = launch_stream_read(buf, bytes / 16, sink, (hipStream_t)hip_stream, nullptr, nullptr);
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
 }
 

@@ -589,6 +589,87 @@ __device__ __forceinline__ float key16_value(int k) {
   return __uint_as_float(b << 16);
 }
 
+// 16 consecutive logits starting at x0 (vector loads when aligned and in range).
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_run16(const void* row, int V, int x0, float (&v)[16]) {
+  if constexpr (DT == kDtBF16) {
+    const uint16_t* p = (const uint16_t*)row;
+    if (VEC && x0 + 16 <= V) {
+      const uint4 a = *(const uint4*)(p + x0), b = *(const uint4*)(p + x0 + 8);
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) { v[2 * k] = bf16_lo(w[k]); v[2 * k + 1] = bf16_hi(w[k]); }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = (x0 + e < V) ? bf16_at(p + x0 + e) : -INFINITY;
+    }
+  } else {
+    const float* p = (const float*)row;
+    if (VEC && x0 + 16 <= V) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 a = *(const float4*)(p + x0 + 4 * k);
+        v[4 * k] = a.x; v[4 * k + 1] = a.y; v[4 * k + 2] = a.z; v[4 * k + 3] = a.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = (x0 + e < V) ? p[x0 + e] : -INFINITY;
+    }
+  }
+}
+
+// Pair sums of one (target, draft) row pair with the relative precision of fp64, for the rare
+// positions where the streaming passes' fp32 sums would not keep it: A = sum min(p, q) when the
+// two distributions barely overlap (1 - beta loses A's precision), and beta = sum [p - q]_+ when
+// they nearly coincide (an error in the normalisers' ratio then moves every term the same way).
+// Two passes over both rows by the whole workgroup: Z_p and Z_q as fp64 sums of the same
+// e-values the second pass divides, then A and beta in fp64 (guide page "5.1 投机解码核心原理"
+// §4.1 / §4.3: beta = sum [p - q]_+, A = sum min(p, q) = 1 - beta).  The exponent of logit l is
+// t = (l - ref) c when SUB, else l c - ref; logits below tau are masked.  `red` holds kWaves
+// doubles of LDS.
+template <int DT, bool VEC, bool SUB>
+__device__ void pair_sums_fp64(const void* prow, const void* qrow, int V, float c, float refp, float refq, float taup,
+                               float tauq, double* red, double& A, double& beta) {
+  const int t = threadIdx.x;
+  auto ex = [&](float l, float ref, float tau) -> float {
+    if (l < tau) return 0.f;
+    return __builtin_amdgcn_exp2f(SUB ? (l - ref) * c : fmaf(l, c, -ref));
+  };
+  double zp = 0.0, zq = 0.0;
+  for (int x0 = t * 16; x0 < V; x0 += kThreads * 16) {
+    float vp[16], vq[16];
+    load_run16<DT, VEC>(prow, V, x0, vp);
+    load_run16<DT, VEC>(qrow, V, x0, vq);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      zp += (double)ex(vp[e], refp, taup);
+      zq += (double)ex(vq[e], refq, tauq);
+    }
+  }
+  zp = block_sum_d(zp, red);
+  zq = block_sum_d(zq, red);
+  const double ip = 1.0 / zp, iq = 1.0 / zq;
+  double a = 0.0, bsum = 0.0;
+  for (int x0 = t * 16; x0 < V; x0 += kThreads * 16) {
+    float vp[16], vq[16];
+    load_run16<DT, VEC>(prow, V, x0, vp);
+    load_run16<DT, VEC>(qrow, V, x0, vq);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const double pp = (double)ex(vp[e], refp, taup) * ip, qq = (double)ex(vq[e], refq, tauq) * iq;
+      a += fmin(pp, qq);
+      bsum += fmax(pp - qq, 0.0);
+    }
+  }
+  A = block_sum_d(a, red);
+  beta = block_sum_d(bsum, red);
+}
+
+// Below this overlap A, or this residual mass beta, a position's pair sums are recomputed with
+// pair_sums_fp64: the fp32 streaming sums carry an absolute error near 1e-7, which would exceed
+// 1e-5 of A (taken as 1 - beta) or of beta under about 1e-2.
+constexpr double kPairRefine = 0.02;
+
 // Expected tokens committed given the drafts, 1 + sum_{k=1..g} prod_{i<=k} a_i, from the
 // per-position accept probabilities, in fp64 and position order.
 __device__ __forceinline__ float expected_committed(const double* ap, int g) {

@@ -20,7 +20,8 @@
 //                   sampler's sequential fp64 sums taken in index order.
 // A slice keeps at most `cap` candidates, those strictly above its threshold first; if it had
 // to drop ties that the row's own threshold would keep, or a row's top-k set exceeds kKeepMax,
-// the request reports SPEC_STATUS_FILTER_OVERFLOW instead of a result.
+// the request (or plain row) is listed for the dense threshold path, which recomputes all its
+// outputs after these kernels (spec_kernels.hip, k_fb_rows and k_fb_requests / k_fb_residual).
 #include "spec_device.h"
 #include "spec_internal.h"
 
@@ -369,6 +370,11 @@ __global__ __launch_bounds__(kThreads) void k_filt_slices(FilterArgs a) {
   __shared__ Sel2Lds S;
   const int n_s = a.n_s;
   const int r = blockIdx.x / n_s, s = blockIdx.x - (blockIdx.x / n_s) * n_s;
+  // the dense recomputation's list starts empty and the offsets valid (the finalize checks them)
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (a.ovf_n) *a.ovf_n = 0;
+    if (a.cu_bad0) *a.cu_bad0 = 0;
+  }
   if (r >= a.n_teams) return;
   constexpr int kEsz = DT == kDtBF16 ? 2 : 4;
   const int base = s * kChunk;
@@ -923,7 +929,11 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
   // B. accept scan, the row to sample, request statistics (one thread)
   if (t == 0) {
     int status = 0, j = -1;
-    if (F.flags & kFlagOverflow) status = kStFilterOverflow;
+    if (F.flags & kFlagOverflow) {
+      // the dense recomputation after this kernel replaces every output of this request
+      status = kStFilterOverflow;
+      if (a.ovf_list) a.ovf_list[atomicAdd(a.ovf_n, 1)] = b;
+    }
     else if (F.flags) status = kStNonfinite;
     else {
       for (int i = 0; i < g; ++i) {
@@ -1085,6 +1095,8 @@ __global__ __launch_bounds__(kThreads) void k_filt_rowstats_out(FilterArgs a) {
   if (o.entropy_bits) o.entropy_bits[r] = ok ? (float)st.entropy : nan;
   if (o.max_prob) o.max_prob[r] = ok ? (float)st.max_prob : nan;
   if (o.kept_count) o.kept_count[r] = ok ? st.kept_finite : ((st.flags & kFlagOverflow) ? -1 : 0);
+  // the dense recomputation after this kernel replaces this row's outputs
+  if ((st.flags & kFlagOverflow) && a.ovf_list) a.ovf_list[atomicAdd(a.ovf_n, 1)] = r;
 }
 
 struct ResLds {
@@ -1114,6 +1126,8 @@ __global__ __launch_bounds__(kThreads) void k_filt_residual(FilterArgs a) {
       a.out_tokens[r] = -1;
       if (a.out_mass) a.out_mass[r] = dnan;
       a.out_status[r] = (fl & kFlagOverflow) ? kStFilterOverflow : kStNonfinite;
+      // the dense recomputation after this kernel replaces this row's outputs
+      if ((fl & kFlagOverflow) && a.ovf_list) a.ovf_list[atomicAdd(a.ovf_n, 1)] = r;
     }
     return;
   }

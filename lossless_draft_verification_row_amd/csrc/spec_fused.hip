@@ -61,14 +61,9 @@ struct FinScratch {
   float wsel[kGroup];
   double u[3];
   double red[kWaves];
-  unsigned long long lowm;       // positions whose overlap 1 - beta is below kLowOverlap
+  unsigned long long lowm;       // positions whose pair sums are recomputed (pair_sums_fp64)
   int flags, status, n_acc, pos, wkind, y, kpick, gpick, xpick;
 };
-
-// Below this overlap A = 1 - beta, the finalize sums min(p, q) over the two rows directly: beta
-// carries an absolute error near 1e-7, which 1 - beta would turn into a relative error above
-// 1e-5 for A under about 1e-2; the direct sum keeps the relative precision of its terms.
-constexpr double kLowOverlap = 0.02;
 
 struct LdsFin {
   int cu[kMaxReqFused + 1];
@@ -189,35 +184,6 @@ __device__ __forceinline__ RowComb combine_lanes(float ref, float s, float w, bo
 }
 
 // ---------------------------------------------------------------- finalize one request
-
-// 16 consecutive logits starting at x0 (vector loads when aligned and in range).
-template <int DT, bool VEC>
-__device__ __forceinline__ void load_run16(const void* row, int V, int x0, float (&v)[16]) {
-  if constexpr (DT == kDtBF16) {
-    const uint16_t* p = (const uint16_t*)row;
-    if (VEC && x0 + 16 <= V) {
-      const uint4 a = *(const uint4*)(p + x0), b = *(const uint4*)(p + x0 + 8);
-      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) { v[2 * k] = bf16_lo(w[k]); v[2 * k + 1] = bf16_hi(w[k]); }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) v[e] = (x0 + e < V) ? bf16_at(p + x0 + e) : -INFINITY;
-    }
-  } else {
-    const float* p = (const float*)row;
-    if (VEC && x0 + 16 <= V) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 a = *(const float4*)(p + x0 + 4 * k);
-        v[4 * k] = a.x; v[4 * k + 1] = a.y; v[4 * k + 2] = a.z; v[4 * k + 3] = a.w;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) v[e] = (x0 + e < V) ? p[x0 + e] : -INFINITY;
-    }
-  }
-}
 
 // One request: combine its teams' records (normaliser, entropy in bits and max probability as
 // in the SpecKV page's signals, beta = sum [p - q]_+), run the accept scan (guide page
@@ -437,7 +403,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
           }
           if (okp && okq) {
             ovl = (float)(1.0 - T.beta);
-            low = 1.0 - T.beta < kLowOverlap;
+            low = T.beta < kPairRefine || 1.0 - T.beta < kPairRefine;
             l1 = (float)(2.0 * T.beta);
             ap = (yv && qyd > 0.0) ? fmin(1.0, pyd / qyd) : 0.0;
           }
@@ -448,9 +414,9 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       if (a.st.p_y) a.st.p_y[drow] = py;
       if (a.st.q_y) a.st.q_y[drow] = qy;
       if (a.st.one_minus_tv && !low) a.st.one_minus_tv[drow] = ovl;
+      if (a.st.l1 && !low) a.st.l1[drow] = l1;
       if (a.st.draft_entropy_bits) a.st.draft_entropy_bits[drow] = dh;
       if (a.st.draft_max_prob) a.st.draft_max_prob[drow] = dm;
-      if (a.st.l1) a.st.l1[drow] = l1;
       if (a.st.accept_prob) a.st.accept_prob[drow] = (float)ap;
       F.ap[t] = ap;
       F.dh[t] = dh;
@@ -515,29 +481,21 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   }
   __syncthreads();
 
-  // low-overlap positions: A = sum_x min(p, q) over the two rows, re-read (guide §4.1 / §4.3:
-  // A = sum min(p, q) = 1 - TV), with p = 2^(l c - M_p) / Z_p in fp32 and the sum in fp64
-  if (MODE == kFuSample && a.st.one_minus_tv) {
+  // positions whose two distributions barely overlap or nearly coincide: A and beta again, with
+  // fp64 normalisers and sums (pair_sums_fp64)
+  if (MODE == kFuSample && (a.st.one_minus_tv || a.st.l1)) {
     unsigned long long lm = F.lowm;
     while (lm) {
       const int i = __builtin_ctzll(lm);
       lm &= lm - 1;
       const TeamL T = F.team[i];
-      const float ip = (float)(1.0 / T.z[0]), iq = (float)(1.0 / T.z[1]);
-      const void* prow = row_ptr<DT>(a.tgt, a.tgt_ld, c0 + b + i);
-      const void* qrow = row_ptr<DT>(a.drf, a.drf_ld, c0 + i);
-      float acc = 0.f;
-      for (int x0 = t * 16; x0 < a.V; x0 += kThreads * 16) {
-        float vp[16], vq[16];
-        load_run16<DT, VEC>(prow, a.V, x0, vp);
-        load_run16<DT, VEC>(qrow, a.V, x0, vq);
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          acc += fminf(__builtin_amdgcn_exp2f(fmaf(vp[e], a.c, -T.M[0])) * ip,
-                       __builtin_amdgcn_exp2f(fmaf(vq[e], a.c, -T.M[1])) * iq);
+      double A, beta;
+      pair_sums_fp64<DT, VEC, false>(row_ptr<DT>(a.tgt, a.tgt_ld, c0 + b + i), row_ptr<DT>(a.drf, a.drf_ld, c0 + i),
+                                     a.V, a.c, T.M[0], T.M[1], -INFINITY, -INFINITY, F.red, A, beta);
+      if (t == 0) {
+        if (a.st.one_minus_tv) a.st.one_minus_tv[c0 + i] = (float)A;
+        if (a.st.l1) a.st.l1[c0 + i] = (float)(2.0 * beta);
       }
-      const double A = block_sum_d((double)acc, F.red);
-      if (t == 0) a.st.one_minus_tv[c0 + i] = (float)A;
     }
   }
 
@@ -1376,8 +1334,6 @@ static hipError_t launch_fused_t(FusedArgs a, hipStream_t st, hipEvent_t ev0, hi
   const int teams8 = (a.n_teams + 7) / 8;
   const long long grid = 8ll * teams8 * ((a.n_s + 1) / 2);
   if (grid < 1 || grid > 0x7fffffffll) return hipErrorInvalidConfiguration;
-  if (getenv("SPEC_VERIFY_DEBUG"))
-    fprintf(stderr, "[specverify] fused grid %lld tickets %d slices %d mode %d\n", grid, a.n_tickets, a.n_s, a.mode);
   if (MODE == kFuSample && a.team_row) {
     hipLaunchKernelGGL(k_team_map, dim3((unsigned)((a.B + kThreads - 1) / kThreads)), dim3(kThreads), 0, st, a);
     const hipError_t e0 = hipGetLastError();

@@ -22,9 +22,11 @@ constexpr int kFuSample = 0;           // draft logits, temperature > 0
 constexpr int kFuTokenOnly = 1;        // token-only draft, temperature > 0
 constexpr int kFuGreedy = 2;           // temperature 0
 
-// Header at the start of every workspace (the multi-kernel path's offset-check flag).
+// Header at the start of every workspace (the multi-kernel path's offset-check flag; the
+// filtered path's count of units sent to the dense recomputation).
 constexpr size_t kHeaderBytes = 256;
 constexpr size_t kHdrCuBad = 0;                                     // i32
+constexpr size_t kHdrOvfN = 4;                                      // i32
 
 // How a logical row index maps onto the caller's arrays (see resolve_row).
 struct RowMap {
@@ -91,6 +93,7 @@ struct PosStatsOut {
 struct FinalizeArgs {
   RowMap map;
   int V, n_slices, greedy;
+  int vec;                  // rows 16-byte aligned (vector loads when rows are read again)
   float c;
   double inv_t;             // 1 / T (T > 0)
   uint64_t seed, step;
@@ -184,6 +187,28 @@ struct RowStat2 {        // a row's filtered distribution
   double log_z, entropy, max_prob, z;
 };
 
+// The dense recomputation of what the sparse filtered path cannot hold: a row whose top-k set
+// (k plus its boundary ties) exceeds kKeepMax, or a slice that had to drop tied candidates the
+// row keeps.  The sparse path's last kernel lists such units (requests, or plain rows) in
+// device memory; these kernels then run the dense threshold path on the listed units only
+// (every workgroup reads the list's length and leaves when it is zero).
+struct FallbackRows {
+  RowMap map;               // map.thr = thr
+  int V, n_slices, n_lr;    // n_lr: logical rows of the whole call
+  int unit_lr;              // logical rows per listed unit: 2 (G + 1) per request, 2 per plain row
+  int k;                    // top_k
+  float top_p;
+  double cthr;              // log2(e) / T for the threshold search
+  float c;                  // log2(e) / T
+  int want_argmax;          // argmax and kept counts in the row statistics (spec_row_stats)
+  float* thr;               // [n_lr]
+  SlicePart* part;          // [n_lr][n_slices]
+  RowStat* rs;              // [n_lr]
+  RowStatsOut rso;
+  const int* list;          // listed units
+  const int* list_n;        // their number
+};
+
 struct FilterArgs {
   const void* tgt;
   int64_t tgt_ld;
@@ -204,6 +229,10 @@ struct FilterArgs {
   float* out_req_stats;
   int32_t* out_status;
   PosStatsOut st;
+  // units the sparse sets cannot hold, for the dense recomputation (requests, or plain rows)
+  int* ovf_list;            // [B]
+  int* ovf_n;               // zeroed by the first kernel, one increment per listed unit
+  int* cu_bad0;             // the dense path's offset flag, zeroed by the first kernel
   // plain rows (spec_row_stats / spec_residual_sample): target row r pairs with draft row r
   int direct;
   const double* uniforms;   // residual draws: [rows][3] injected uniforms, or nullptr (Philox)
@@ -221,6 +250,15 @@ hipError_t launch_check_cu(const int32_t* cu, int B, int G, int n_draft_rows, in
 size_t fused_record_bytes();
 
 hipError_t launch_dense(const DenseLaunch& L, hipStream_t st);
+// The dense recomputation of listed units: per logical row the threshold, slice statistics and
+// row statistics; then per listed request the pair sums and the finalize (a.map and the arrays
+// of `a` as the dense path carves them), or per listed plain row the pair sums and the
+// residual draw.
+hipError_t launch_fallback_rows(const FallbackRows& f, int dt, int vec, hipStream_t st);
+hipError_t launch_fallback_requests(const FallbackRows& f, const FinalizeArgs& a, int want_kl, int dt, int vec,
+                                    hipStream_t st);
+hipError_t launch_fallback_residual(const FallbackRows& f, const ResidualArgs& a, double* amass, int dt, int vec,
+                                    hipStream_t st);
 // Filter thresholds of logical rows 0..n_lr-1 of `m` into thr[n_lr] (c = log2(e) / T).
 hipError_t launch_threshold(const RowMap& m, int dt, int vec, int V, int n_lr, int k, float top_p, double c,
                             float* thr, hipStream_t st);

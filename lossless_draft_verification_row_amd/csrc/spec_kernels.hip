@@ -310,9 +310,8 @@ __device__ void thr_select(ThrLds& S, int nb, unsigned long long base, Reach rea
 // the row.  A bf16 row first tries the window of the 4096 values below its maximum (two passes
 // in all), which settles every realistic row.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_threshold(RowMap m, int V, int k, float top_p, double c,
-                                                         float* __restrict__ thr) {
-  const int lr = blockIdx.x;
+__device__ void threshold_row(const RowMap& m, int V, int k, float top_p, double c, float* __restrict__ thr,
+                              int lr) {
   const void* row = resolve_row<DT>(m, lr);
   if (row == nullptr) return;
   __shared__ ThrLds S;
@@ -407,14 +406,19 @@ __global__ __launch_bounds__(kThreads) void k_threshold(RowMap m, int V, int k, 
   }
 }
 
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_threshold(RowMap m, int V, int k, float top_p, double c,
+                                                         float* __restrict__ thr) {
+  threshold_row<DT, VEC>(m, V, k, top_p, c, thr, blockIdx.x);
+}
+
 // ---------------------------------------------------------------- pass 1
 
 // MODE_SOFTMAX: slice max, sum of exp2((l - m) c) and the entropy numerator; argmax and kept
 // count on request.  MODE_ARGMAX (greedy): slice max, argmax and a NaN / +inf flag.
 template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads) void k_pass1(RowMap m, int V, int n_slices, float c,
-                                                     int want_argmax, SlicePart* __restrict__ part) {
-  const int lr = blockIdx.x, sl = blockIdx.y;
+__device__ void pass1_slice(const RowMap& m, int V, int n_slices, float c, int want_argmax,
+                            SlicePart* __restrict__ part, int lr, int sl) {
   const void* row = resolve_row<DT>(m, lr);
   if (row == nullptr) return;
   __shared__ float redf[kWaves];
@@ -474,16 +478,21 @@ __global__ __launch_bounds__(kThreads) void k_pass1(RowMap m, int V, int n_slice
   if (threadIdx.x == 0) part[(int64_t)lr * n_slices + sl] = out;
 }
 
+template <int DT, bool VEC, int MODE>
+__global__ __launch_bounds__(kThreads) void k_pass1(RowMap m, int V, int n_slices, float c,
+                                                     int want_argmax, SlicePart* __restrict__ part) {
+  pass1_slice<DT, VEC, MODE>(m, V, n_slices, c, want_argmax, part, blockIdx.x, blockIdx.y);
+}
+
 // ---------------------------------------------------------------- combine
 
 // One wave per logical row: fixed-order fp64 merge of the slice partials into RowStat.
 // Optionally writes the spec_row_stats outputs (plain-row mode, kind 0 rows only).
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_combine(RowMap m, int n_lr, int n_slices, float c,
-                                                       int greedy, const SlicePart* __restrict__ part,
-                                                       RowStat* __restrict__ rs, RowStatsOut out) {
+__device__ void combine_row(const RowMap& m, int n_lr, int n_slices, float c, int greedy,
+                            const SlicePart* __restrict__ part, RowStat* __restrict__ rs, const RowStatsOut& out,
+                            int lr) {
   const int lane = threadIdx.x & 63;
-  const int lr = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (lr >= n_lr) return;
   if (resolve_row<DT>(m, lr) == nullptr) return;
   const SlicePart* p = part + (int64_t)lr * n_slices;
@@ -549,6 +558,13 @@ __global__ __launch_bounds__(kThreads) void k_combine(RowMap m, int n_lr, int n_
   }
 }
 
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_combine(RowMap m, int n_lr, int n_slices, float c,
+                                                       int greedy, const SlicePart* __restrict__ part,
+                                                       RowStat* __restrict__ rs, RowStatsOut out) {
+  combine_row<DT>(m, n_lr, n_slices, c, greedy, part, rs, out, blockIdx.x * kWaves + (threadIdx.x >> 6));
+}
+
 // ---------------------------------------------------------------- pair pass
 
 // Residual mass of one slice of one (target, draft) row pair, sum_x [p(x) - q(x)]_+, with
@@ -559,11 +575,9 @@ __global__ __launch_bounds__(kThreads) void k_combine(RowMap m, int n_lr, int n_
 // counts of tokens in one support only (membership decided on the logits: finite and not
 // below the row's filter threshold, so an underflowed probability stays in its support).
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_pair(RowMap m, int V, int n_slices, float c,
-                                                    const RowStat* __restrict__ rs,
-                                                    double* __restrict__ smass, double* __restrict__ amass,
-                                                    int want_kl, double* __restrict__ kmass) {
-  const int slot = blockIdx.x, sl = blockIdx.y;
+__device__ void pair_slice(const RowMap& m, int V, int n_slices, float c, const RowStat* __restrict__ rs,
+                           double* __restrict__ smass, double* __restrict__ amass, int want_kl,
+                           double* __restrict__ kmass, int slot, int sl) {
   const void* prow = resolve_row<DT>(m, 2 * slot);
   const void* qrow = resolve_row<DT>(m, 2 * slot + 1);
   if (prow == nullptr || qrow == nullptr) return;
@@ -617,6 +631,14 @@ __global__ __launch_bounds__(kThreads) void k_pair(RowMap m, int V, int n_slices
       km[0] = skp; km[1] = skq; km[2] = snp; km[3] = snq;
     }
   }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_pair(RowMap m, int V, int n_slices, float c,
+                                                    const RowStat* __restrict__ rs,
+                                                    double* __restrict__ smass, double* __restrict__ amass,
+                                                    int want_kl, double* __restrict__ kmass) {
+  pair_slice<DT, VEC>(m, V, n_slices, c, rs, smass, amass, want_kl, kmass, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------- sampler
@@ -734,9 +756,8 @@ __device__ __forceinline__ double p_of(const void* row, int x, const RowStat& P,
 // ---------------------------------------------------------------- finalize (requests)
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
+__device__ void finalize_req(const FinalizeArgs& a, int b) {
   const RowMap& m = a.map;
-  const int b = blockIdx.x;
   const int G1 = m.G + 1;
   __shared__ float wbuf[kChunk];
   __shared__ double gmass[kChunk / kGroup];
@@ -744,6 +765,8 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
   __shared__ int sh_k, sh_wkind, sh_row, sh_y, sh_emit;
   __shared__ double sh_u2, sh_u3;
   __shared__ double apos[kMaxGamma];
+  __shared__ double red_d[kWaves];
+  __shared__ unsigned long long refine_m;   // positions whose pair sums are recomputed
 
   int g, c0;
   const bool ok_req = request_rows(m, b, g, c0);
@@ -765,6 +788,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
 
   // per-position statistics (one thread per position) and the non-finite check
   int flags = 0;
+  bool refine = false;
   for (int i = 0; i <= g; ++i) {
     flags |= a.rs[2 * (b * G1 + i)].flags;
     if (!token_only && i < g) flags |= a.rs[2 * (b * G1 + i) + 1].flags;
@@ -820,6 +844,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
           }
           ovl = (float)ov;
           l1 = (float)(2.0 * beta);
+          refine = beta < kPairRefine || ov < kPairRefine;
           ap = (yv && qyd > 0.0) ? fmin(1.0, pyd / qyd) : 0.0;
           if (a.st.kl_pq || a.st.kl_qp) {
             // D(p || q) = sum p (l_p - l_q) / T - (LSE_p - LSE_q), LSE = m / T + ln z
@@ -836,21 +861,48 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
         dh = okq ? Q.h_bits : nan;
         dm = okq ? Q.maxp : nan;
       }
-      if (a.st.l1) a.st.l1[drow] = l1;
+      if (a.st.l1 && !refine) a.st.l1[drow] = l1;
       if (a.st.accept_prob) a.st.accept_prob[drow] = (float)ap;
       if (a.st.kl_pq) a.st.kl_pq[drow] = klpq;
       if (a.st.kl_qp) a.st.kl_qp[drow] = klqp;
       apos[t] = ap;
       if (a.st.p_y) a.st.p_y[drow] = py;
       if (a.st.q_y) a.st.q_y[drow] = qy;
-      if (a.st.one_minus_tv) a.st.one_minus_tv[drow] = ovl;
+      if (a.st.one_minus_tv && !refine) a.st.one_minus_tv[drow] = ovl;
       if (a.st.draft_entropy_bits) a.st.draft_entropy_bits[drow] = dh;
       if (a.st.draft_max_prob) a.st.draft_max_prob[drow] = dm;
       wbuf[2 * t] = dh;
       wbuf[2 * t + 1] = dm;
     }
   }
+  {
+    const unsigned long long m = __ballot(refine);
+    if (t == 0) refine_m = m;   // wave 0 holds every position (gamma_max <= 64)
+  }
   __syncthreads();
+  // positions whose two distributions barely overlap or nearly coincide: A and beta again, with
+  // fp64 normalisers and sums (pair_sums_fp64)
+  if (!greedy && !token_only && (a.st.one_minus_tv || a.st.l1)) {
+    unsigned long long rm = refine_m;
+    while (rm) {
+      const int i = __builtin_ctzll(rm);
+      rm &= rm - 1;
+      const RowStat P = a.rs[2 * (b * G1 + i)], Q = a.rs[2 * (b * G1 + i) + 1];
+      double A, beta;
+      if (a.vec)
+        pair_sums_fp64<DT, true, true>(row_ptr<DT>(m.tgt, m.tgt_ld, (int64_t)c0 + b + i),
+                                       row_ptr<DT>(m.drf, m.drf_ld, (int64_t)c0 + i), a.V, a.c, P.m, Q.m, P.tau,
+                                       Q.tau, red_d, A, beta);
+      else
+        pair_sums_fp64<DT, false, true>(row_ptr<DT>(m.tgt, m.tgt_ld, (int64_t)c0 + b + i),
+                                        row_ptr<DT>(m.drf, m.drf_ld, (int64_t)c0 + i), a.V, a.c, P.m, Q.m, P.tau,
+                                        Q.tau, red_d, A, beta);
+      if (t == 0) {
+        if (a.st.one_minus_tv) a.st.one_minus_tv[(int64_t)c0 + i] = (float)A;
+        if (a.st.l1) a.st.l1[(int64_t)c0 + i] = (float)(2.0 * beta);
+      }
+    }
+  }
   if (t == 0 && a.st.expected_committed)
     a.st.expected_committed[b] = (flags & kStNonfinite) ? nan : expected_committed(apos, g);
   if (t == 0 && a.out_req_stats) {
@@ -976,12 +1028,16 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
   if (t == 0) a.out_num_accepted[b] = n_acc;
 }
 
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
+  finalize_req<DT>(a, blockIdx.x);
+}
+
 // ---------------------------------------------------------------- finalize (plain rows)
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_residual_finalize(ResidualArgs a) {
+__device__ void residual_row(const ResidualArgs& a, int r) {
   const RowMap& m = a.map;
-  const int r = blockIdx.x;
   __shared__ float wbuf[kChunk];
   __shared__ double gmass[kChunk / kGroup];
   __shared__ double cmass[kMaxChunks];
@@ -1055,6 +1111,11 @@ __global__ __launch_bounds__(kThreads) void k_residual_finalize(ResidualArgs a) 
     x = sample_in_chunk<DT>(prow, qrow, a.V, k, a.c, P, Q, sh_wkind, -1, sh_u2, sh_u3, wbuf, gmass);
   }
   if (t == 0) a.out_token[r] = x;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_residual_finalize(ResidualArgs a) {
+  residual_row<DT>(a, blockIdx.x);
 }
 
 // ---------------------------------------------------------------- draft-length selection
@@ -1201,6 +1262,100 @@ hipError_t launch_threshold(const RowMap& m, int dt, int vec, int V, int n_lr, i
 
 hipError_t launch_dense(const DenseLaunch& L, hipStream_t st) {
   return L.dt == kDtBF16 ? launch_dense_t<kDtBF16>(L, st) : launch_dense_t<kDtF32>(L, st);
+}
+
+// ---------------------------------------------------------------- dense recomputation of listed units
+
+// Listed units of the sparse filtered path, one workgroup per logical row in turn: the row's
+// filter threshold (the kept set is an upper set of values, so one value carries the filter),
+// its slice statistics and its row statistics, as the threshold kernel, pass 1 and the combine
+// kernel compute them.  Every workgroup reads the list's length first and leaves if it is zero.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_fb_rows(FallbackRows f) {
+  const int total = *f.list_n * f.unit_lr;
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int lr = f.list[w / f.unit_lr] * f.unit_lr + w % f.unit_lr;
+    if (resolve_row<DT>(f.map, lr) == nullptr) continue;
+    threshold_row<DT, VEC>(f.map, f.V, f.k, f.top_p, f.cthr, f.thr, lr);
+    __syncthreads();
+    for (int sl = 0; sl < f.n_slices; ++sl)
+      pass1_slice<DT, VEC, kModeSoftmax>(f.map, f.V, f.n_slices, f.c, f.want_argmax, f.part, lr, sl);
+    __syncthreads();
+    if (threadIdx.x < 64) combine_row<DT>(f.map, f.n_lr, f.n_slices, f.c, 0, f.part, f.rs, f.rso, lr);
+    __syncthreads();
+  }
+}
+
+// Listed requests after k_fb_rows: the pair sums of every position, then the finalize.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_fb_requests(FallbackRows f, FinalizeArgs a, int want_kl) {
+  const int n = *f.list_n;
+  const int G1 = f.map.G + 1;
+  for (int w = blockIdx.x; w < n; w += gridDim.x) {
+    const int b = f.list[w];
+    for (int i = 0; i < G1; ++i)
+      for (int sl = 0; sl < f.n_slices; ++sl)
+        pair_slice<DT, VEC>(f.map, f.V, f.n_slices, f.c, f.rs, (double*)a.smass, (double*)a.amass, want_kl,
+                            (double*)a.kmass, b * G1 + i, sl);
+    __syncthreads();
+    finalize_req<DT>(a, b);
+    __syncthreads();
+  }
+}
+
+// Listed plain rows after k_fb_rows: the pair sums (with q rows), then the residual draw.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_fb_residual(FallbackRows f, ResidualArgs a, double* amass) {
+  const int n = *f.list_n;
+  for (int w = blockIdx.x; w < n; w += gridDim.x) {
+    const int r = f.list[w];
+    for (int sl = 0; sl < f.n_slices; ++sl)
+      pair_slice<DT, VEC>(f.map, f.V, f.n_slices, f.c, f.rs, (double*)a.smass, amass, 0, nullptr, r, sl);
+    __syncthreads();
+    residual_row<DT>(a, r);
+    __syncthreads();
+  }
+}
+
+// Grids: enough workgroups to spread a long list, few enough that an empty one costs little.
+constexpr int kFbGrid = 256;
+
+hipError_t launch_fallback_rows(const FallbackRows& f, int dt, int vec, hipStream_t st) {
+  const dim3 g(kFbGrid), blk(kThreads);
+  if (dt == kDtBF16) {
+    if (vec) hipLaunchKernelGGL((k_fb_rows<kDtBF16, true>), g, blk, 0, st, f);
+    else hipLaunchKernelGGL((k_fb_rows<kDtBF16, false>), g, blk, 0, st, f);
+  } else {
+    if (vec) hipLaunchKernelGGL((k_fb_rows<kDtF32, true>), g, blk, 0, st, f);
+    else hipLaunchKernelGGL((k_fb_rows<kDtF32, false>), g, blk, 0, st, f);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fallback_requests(const FallbackRows& f, const FinalizeArgs& a, int want_kl, int dt, int vec,
+                                    hipStream_t st) {
+  const dim3 g(kFbGrid), blk(kThreads);
+  if (dt == kDtBF16) {
+    if (vec) hipLaunchKernelGGL((k_fb_requests<kDtBF16, true>), g, blk, 0, st, f, a, want_kl);
+    else hipLaunchKernelGGL((k_fb_requests<kDtBF16, false>), g, blk, 0, st, f, a, want_kl);
+  } else {
+    if (vec) hipLaunchKernelGGL((k_fb_requests<kDtF32, true>), g, blk, 0, st, f, a, want_kl);
+    else hipLaunchKernelGGL((k_fb_requests<kDtF32, false>), g, blk, 0, st, f, a, want_kl);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fallback_residual(const FallbackRows& f, const ResidualArgs& a, double* amass, int dt, int vec,
+                                    hipStream_t st) {
+  const dim3 g(kFbGrid), blk(kThreads);
+  if (dt == kDtBF16) {
+    if (vec) hipLaunchKernelGGL((k_fb_residual<kDtBF16, true>), g, blk, 0, st, f, a, amass);
+    else hipLaunchKernelGGL((k_fb_residual<kDtBF16, false>), g, blk, 0, st, f, a, amass);
+  } else {
+    if (vec) hipLaunchKernelGGL((k_fb_residual<kDtF32, true>), g, blk, 0, st, f, a, amass);
+    else hipLaunchKernelGGL((k_fb_residual<kDtF32, false>), g, blk, 0, st, f, a, amass);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_finalize(const FinalizeArgs& a, int dt, hipStream_t st) {

@@ -86,6 +86,26 @@ def test_argument_checks_without_gpu():
                                  None, None, ps, None, None, None, 0, None) == 0
 
 
+def test_call_options_checks_without_gpu():
+    """Per-call options: an unknown path or exactly one profile event is rejected before any
+    launch; NULL options and a valid struct pass the check (B = 0 makes the call a no-op)."""
+    lib = L.load_library()
+    sp = L.SamplingParams(1.0, 0, 1.0)
+    ps = L.PosStats()
+    args = (2, 100, 3, 1, 16, 100, None, 0, 16, 16, 0, sp, 0, 0, 16, 16, ps, None, 16, None, 0, None)
+    for bad in (L.CallOptions(7, -1, 0, 0, None, None), L.CallOptions(0, -1, 0, 0, 16, None),
+                L.CallOptions(1, -1, 0, 0, None, 16)):
+        assert lib.spec_verify_batch_ex(*args, ctypes.byref(bad)) == -1
+        assert lib.spec_row_stats_ex(4, 100, 1, 16, 100, sp, *([None] * 6), None, 0, None, ctypes.byref(bad)) == -1
+        assert lib.spec_residual_sample_ex(4, 100, 1, 16, 100, None, 0, sp, None, 0, 0, 16, None, 16, None, 0,
+                                           None, ctypes.byref(bad)) == -1
+    ok = L.call_options(path="multi", spin_limit=0, poll_delay=10)
+    zero = (0,) + args[1:]
+    assert lib.spec_verify_batch_ex(*zero, ctypes.byref(ok)) == 0
+    assert lib.spec_verify_batch_ex(*zero, None) == 0
+    assert L.call_options() is None
+
+
 def test_select_gamma_argument_checks_without_gpu():
     lib = L.load_library()
     w = L.GammaMLP(16, 16, 16, 0.0)

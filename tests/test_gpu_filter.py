@@ -1,7 +1,8 @@
 """GPU parity of the top-k / top-p paths against the fp64 oracle, on seeded inputs whose draft
 tokens are drawn from the oracle's filtered draft distribution (the draft model samples from its
 own filtered q): the sparse path (1 <= top_k <= 256, top-p optional) and the dense threshold
-path (top-p alone, top_k > 256, or any filter with SPEC_VERIFY_DENSE_FILTER set).
+path (top-p alone, top_k > 256, or any filter on the multi-kernel path), and the sparse path's
+dense recomputation of requests and rows whose top-k sets it cannot hold.
 
 Sizes span several 4096-logit slices and a ragged tail; the comparison rule is in
 tests/harness.py (decisions within 1e-6 of a boundary, including the top-p boundary, are
@@ -23,6 +24,11 @@ import harness as H
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
+_PATH = "auto"   # "multi" sends every filtered call to the dense threshold path
+
+
+def _opts():
+    return L.call_options(path=_PATH)
 
 
 def note(msg):
@@ -69,7 +75,7 @@ def run_gpu(inp, sp, seed, step, gamma_max=None, kl=False):
     d = H.to_device(inp)
     G = int(inp.gammas.max()) if gamma_max is None else gamma_max
     res = L.spec_verify_batch(d["target"], d["draft"], d["tokens"], d["cu"], G, temperature=sp.temperature,
-                              top_k=sp.top_k, top_p=sp.top_p, seed=seed, step=step, kl=kl)
+                              top_k=sp.top_k, top_p=sp.top_p, seed=seed, step=step, kl=kl, options=_opts())
     torch.cuda.synchronize()
     return H.gpu_to_numpy(res)
 
@@ -141,15 +147,43 @@ def test_filtered_ties_and_masked():
     check(inp, sp)
 
 
-def test_filtered_all_equal_overflows():
-    """Every logit equal: the top-k set is the whole row, larger than the sparse path holds; the
-    request reports FILTER_OVERFLOW with no tokens."""
+def test_filtered_all_equal_recomputed_densely():
+    """Every logit of request 0's target rows equal: the top-k set (ties kept, guide page 5.1
+    §2.1) is the whole row, more than the sparse sets hold, so the request is recomputed on
+    the dense path in the same call and matches the oracle; request 1 stays on the sparse path."""
     sp = O.SamplingParams(0.7, 50, 0.9)
     inp = filtered_inputs(2, V_SMALL, [3, 2], sp, seed=29)
     inp.target[0:4] = W.bf16_bits_from_f32(np.full((4, V_SMALL), 0.25, np.float32))   # request 0
-    gpu = run_gpu(inp, sp, 1, 1)
-    assert gpu["status"][0] & L.STATUS["FILTER_OVERFLOW"]
-    assert (gpu["tokens"][0] == -1).all() and gpu["num_accepted"][0] == 0
+    gpu, _, _ = check(inp, sp, seed=1, step=1)
+    assert not (gpu["status"] & L.STATUS["FILTER_OVERFLOW"]).any()
+
+
+@pytest.mark.parametrize("n_tied", [600, 60])
+def test_filtered_heavy_ties_at_kth_value(n_tied):
+    """n_tied equal logits at the top of some rows with top-k 50: 600 ties make the top-k set
+    larger than the sparse sets hold (dense recomputation); 60 ties stay sparse.  Requests with
+    and without ties are mixed in one call; every request matches the oracle."""
+    sp = O.SamplingParams(0.7, 50, 0.9)
+    V = V_SMALL
+    inp = filtered_inputs(5, V, [4, 3, 5, 2, 4], sp, seed=40 + n_tied)
+    rng = np.random.default_rng(n_tied)
+    for b in (1, 3):
+        c0, g = int(inp.cu_draft[b]), int(inp.gammas[b])
+        for arr, rows in ((inp.target, range(c0 + b, c0 + b + g + 1)), (inp.draft, range(c0, c0 + g))):
+            for r in rows:
+                f = W.bf16_bits_to_f32(arr[r]).copy()
+                f[rng.choice(V, n_tied, replace=False)] = 12.0
+                arr[r] = W.bf16_bits_from_f32(f)
+    dv = W.bf16_bits_to_f32(inp.draft).astype(np.float64)
+    rng2 = np.random.default_rng(7)
+    for r in range(inp.draft.shape[0]):
+        q = O.row_distribution(dv[r], sp).probs
+        inp.tokens[r] = int(rng2.choice(V, p=q / q.sum()))
+    gpu, refs, _ = check(inp, sp)
+    assert not (gpu["status"] & L.STATUS["FILTER_OVERFLOW"]).any()
+    kept = [refs[1].target_rows[0].kept_count, refs[0].target_rows[0].kept_count]
+    note(f"kept tokens with and without ties: {kept}")
+    assert kept[0] >= n_tied
 
 
 def test_filtered_nonfinite():
@@ -263,7 +297,7 @@ def test_filtered_row_stats(dtype, k, p):
     x[5] = np.round(x[5] * 2) / 2          # ties at the boundary
     t, xf = _rows(x, dtype)
     sp = O.SamplingParams(0.7, k, p)
-    res = L.spec_row_stats(t, temperature=0.7, top_k=k, top_p=p)
+    res = L.spec_row_stats(t, temperature=0.7, top_k=k, top_p=p, options=_opts())
     torch.cuda.synchronize()
     g = H.gpu_to_numpy(res)
     ref = O.row_stats(xf, sp)
@@ -277,19 +311,24 @@ def test_filtered_row_stats(dtype, k, p):
 
 
 def test_filtered_row_stats_overflow_and_nonfinite():
-    """A row whose top-k set is larger than the sparse path holds reports argmax -1, NaN
-    statistics and kept count -1; a row with a NaN reports argmax -1, NaN and kept count 0."""
+    """A row whose top-k set is larger than the sparse sets hold (every logit equal) is
+    recomputed densely: it keeps every token (uniform: entropy log2 V, max prob 1 / V); a row
+    with a NaN reports argmax -1, NaN and kept count 0; an ordinary row matches the oracle."""
     V = 4096 + 100
     x = np.random.default_rng(3).standard_normal((3, V), dtype=np.float32)
     x[0] = 0.5
     x[1, 17] = np.nan
-    t, _ = _rows(x, "bf16")
-    res = L.spec_row_stats(t, temperature=0.7, top_k=50, top_p=0.9)
+    t, xf = _rows(x, "bf16")
+    res = L.spec_row_stats(t, temperature=0.7, top_k=50, top_p=0.9, options=_opts())
     torch.cuda.synchronize()
     g = H.gpu_to_numpy(res)
-    assert g["argmax"][0] == -1 and g["kept_count"][0] == -1 and np.isnan(g["entropy_bits"][0])
+    assert g["kept_count"][0] == V and g["argmax"][0] == 0
+    assert H.close(g["entropy_bits"][:1], np.array([np.log2(V)]))
+    assert H.close(g["max_prob"][:1], np.array([1.0 / V]))
     assert g["argmax"][1] == -1 and g["kept_count"][1] == 0 and np.isnan(g["log_z"][1])
-    assert g["argmax"][2] >= 0 and g["kept_count"][2] > 0
+    ref = O.row_stats(xf[2:], O.SamplingParams(0.7, 50, 0.9))
+    assert g["kept_count"][2] == ref["kept_count"][0] and g["argmax"][2] == ref["argmax"][0]
+    assert H.close(g["entropy_bits"][2:], ref["entropy_bits"])
 
 
 @pytest.mark.parametrize("with_q", [True, False])
@@ -312,7 +351,7 @@ def _residual_grid(with_q, k, top_p):
     pt = torch.from_numpy(P).view(torch.bfloat16).to(DEV)
     qt = torch.from_numpy(Q).view(torch.bfloat16).to(DEV) if with_q else None
     res = L.spec_residual_sample(pt, qt, temperature=0.7, top_k=k, top_p=top_p,
-                                 uniforms=torch.from_numpy(U).to(DEV))
+                                 uniforms=torch.from_numpy(U).to(DEV), options=_opts())
     torch.cuda.synchronize()
     g = H.gpu_to_numpy(res)
     pf = W.bf16_bits_to_f32(P[:1]).astype(np.float64)
@@ -326,6 +365,36 @@ def _residual_grid(with_q, k, top_p):
     assert H.close(g["mass"], ref["mass"])
 
 
+@pytest.mark.parametrize("with_q", [True, False])
+def test_filtered_residual_sample_overflow_rows(with_q):
+    """Plain rows with 600 equal top logits (top-k 50): the sparse sets cannot hold them, so
+    they are recomputed densely in the same call; mixed with ordinary rows, every draw, mass
+    and status matches the oracle (decisions within 1e-6 of a boundary excused)."""
+    V = 2 * 4096 + 500
+    R = 24
+    rng = np.random.default_rng(43)
+    p = rng.standard_normal((R, V)).astype(np.float32) * 3
+    q = p + rng.standard_normal((R, V)).astype(np.float32)
+    for r in range(0, R, 2):
+        p[r, rng.choice(V, 600, replace=False)] = 12.0
+        q[r, rng.choice(V, 600, replace=False)] = 12.0
+    U = rng.random((R, 3))
+    P, Q = W.bf16_bits_from_f32(p), W.bf16_bits_from_f32(q)
+    pt = torch.from_numpy(P).view(torch.bfloat16).to(DEV)
+    qt = torch.from_numpy(Q).view(torch.bfloat16).to(DEV) if with_q else None
+    res = L.spec_residual_sample(pt, qt, temperature=0.7, top_k=50, top_p=0.9,
+                                 uniforms=torch.from_numpy(U).to(DEV), options=_opts())
+    torch.cuda.synchronize()
+    g = H.gpu_to_numpy(res)
+    pf = W.bf16_bits_to_f32(P).astype(np.float64)
+    qf = W.bf16_bits_to_f32(Q).astype(np.float64) if with_q else None
+    ref = O.residual_sample(pf, qf, O.SamplingParams(0.7, 50, 0.9), uniforms=U)
+    bad = (g["token"] != ref["token"]) & (ref["margin"] >= H.DECISION_EPS)
+    assert not bad.any(), (np.nonzero(bad), g["token"], ref["token"])
+    assert np.array_equal(g["status"], ref["status"]), (g["status"], ref["status"])
+    assert H.close(g["mass"], ref["mass"])
+
+
 def test_filtered_residual_sample_philox():
     """Philox draws (counter (r, 0, 1, 0)) on 64 filtered fp32 row pairs, one of them with
     identical p and q (empty residual: drawn from p)."""
@@ -335,7 +404,8 @@ def test_filtered_residual_sample_philox():
     p = rng.standard_normal((R, V)).astype(np.float32) * 2
     q = p + rng.standard_normal((R, V)).astype(np.float32)
     q[5] = p[5]
-    res = L.spec_residual_sample(torch.from_numpy(p).to(DEV), torch.from_numpy(q).to(DEV), temperature=0.9,
+    res = L.spec_residual_sample(torch.from_numpy(p).to(DEV), torch.from_numpy(q).to(DEV), options=_opts(),
+                                 temperature=0.9,
                                  top_k=30, top_p=0.85, seed=77, step=4)
     torch.cuda.synchronize()
     g = H.gpu_to_numpy(res)
@@ -350,13 +420,13 @@ def test_filtered_residual_sample_philox():
 
 # ----------------------------------------------------------------------------- dense threshold path
 # Top-p alone and top-k beyond 256 take the dense path: a threshold kernel finds each row's
-# kept-set threshold and the dense kernels mask every logit below it.  SPEC_VERIFY_DENSE_FILTER
-# sends the top-k <= 256 cases there too, so the same oracle checks both paths on them.
+# kept-set threshold and the dense kernels mask every logit below it.  The multi-kernel path
+# option sends the top-k <= 256 cases there too, so the same oracle checks both paths on them.
 
 
 @pytest.fixture
 def dense_forced(monkeypatch):
-    monkeypatch.setenv("SPEC_VERIFY_DENSE_FILTER", "1")
+    monkeypatch.setattr(sys.modules[__name__], "_PATH", "multi")
 
 
 @pytest.mark.parametrize("k,p", [(0, 0.9), (0, 0.5), (0, 0.99), (1000, 1.0), (600, 0.8), (300, 0.97)])
@@ -408,6 +478,10 @@ def test_dense_filtered_row_stats(dtype, k, p):
 
 
 def test_dense_row_stats_all_equal_and_nonfinite(dense_forced):
+    test_filtered_row_stats_overflow_and_nonfinite()
+
+
+def _unused_dense_row_stats_all_equal_and_nonfinite():
     """An all-equal row keeps every token (uniform: entropy log2 V, max prob 1 / V); a row with
     a NaN reports argmax -1, NaN statistics and kept count 0."""
     V = 4096 + 100
@@ -415,7 +489,7 @@ def test_dense_row_stats_all_equal_and_nonfinite(dense_forced):
     x[0] = 0.5
     x[1, 17] = np.nan
     t, xf = _rows(x, "bf16")
-    res = L.spec_row_stats(t, temperature=0.7, top_k=50, top_p=0.9)
+    res = L.spec_row_stats(t, temperature=0.7, top_k=50, top_p=0.9, options=_opts())
     torch.cuda.synchronize()
     g = H.gpu_to_numpy(res)
     assert g["kept_count"][0] == V and g["argmax"][0] == 0

@@ -60,34 +60,18 @@ def custom_inputs(B, V, gammas, dtype="bf16", sigma=3.0, tau=1.0, T=1.0, seed=7,
     return W.Inputs(wl, gammas, cu, target, None if token_only else draft, toks.astype(np.int32), seed)
 
 
-class path_env:
-    """Select the single-kernel (fused) or the multi-kernel path of spec_verify_batch."""
-
-    def __init__(self, path):
-        self.path = path
-
-    def __enter__(self):
-        self.old = os.environ.get("SPEC_VERIFY_NO_FUSED")
-        if self.path == "multi":
-            os.environ["SPEC_VERIFY_NO_FUSED"] = "1"
-        else:
-            os.environ.pop("SPEC_VERIFY_NO_FUSED", None)
-
-    def __exit__(self, *exc):
-        if self.old is None:
-            os.environ.pop("SPEC_VERIFY_NO_FUSED", None)
-        else:
-            os.environ["SPEC_VERIFY_NO_FUSED"] = self.old
+def path_options(path):
+    """Call options selecting the single-kernel (fused) or the multi-kernel path."""
+    return L.call_options(path="multi" if path == "multi" else "auto")
 
 
 def run_gpu(inp, sp, seed, step, gamma_max=None, path="fused", kl=False):
     d = H.to_device(inp)
     G = int(inp.gammas.max()) if gamma_max is None else gamma_max
-    with path_env(path):
-        res = L.spec_verify_batch(d["target"], d["draft"], d["tokens"], d["cu"], G,
-                                  temperature=sp.temperature, top_k=sp.top_k, top_p=sp.top_p, seed=seed, step=step,
-                                  kl=kl)
-        torch.cuda.synchronize()
+    res = L.spec_verify_batch(d["target"], d["draft"], d["tokens"], d["cu"], G,
+                              temperature=sp.temperature, top_k=sp.top_k, top_p=sp.top_p, seed=seed, step=step,
+                              kl=kl, options=path_options(path))
+    torch.cuda.synchronize()
     return H.gpu_to_numpy(res)
 
 
@@ -283,9 +267,9 @@ def test_bad_offsets_are_reported_not_read(path):
     d = H.to_device(inp)
     for cu_bad in ([0, 2, 9, 6], [1, 3, 6, 7], [0, 2, 5, 5]):   # gamma > max, cu[0] != 0, cu[B] != rows
         cu = torch.tensor(cu_bad, dtype=torch.int32, device=DEV)
-        with path_env(path):
-            res = L.spec_verify_batch(d["target"], d["draft"], d["tokens"], cu, 3, temperature=1.0, seed=1)
-            torch.cuda.synchronize()
+        res = L.spec_verify_batch(d["target"], d["draft"], d["tokens"], cu, 3, temperature=1.0, seed=1,
+                                  options=path_options(path))
+        torch.cuda.synchronize()
         st = res["status"].cpu().numpy()
         assert (st == L.STATUS["BAD_GAMMA"]).all(), (cu_bad, st)
         assert (res["tokens"].cpu().numpy() == -1).all()
@@ -295,16 +279,16 @@ def test_bad_offsets_are_reported_not_read(path):
 
 
 def test_forced_timeout_then_clean_call():
-    """A zero wait bound forces the team wait to give up: the affected requests report TIMEOUT
-    with no tokens, the others still match the oracle, and the next call is exact again."""
+    """A zero wait bound (a per-call option) forces the team wait to give up: the affected
+    requests report TIMEOUT with no tokens, the others still match the oracle, and the next
+    call, with the default bound, is exact again."""
     inp = custom_inputs(6, 6 * 4096 + 10, [5, 4, 3, 5, 2, 6], seed=29)
     sp = O.SamplingParams(1.0)
-    lib = L.load_library()
-    lib.spec_set_spin_limit(0)
-    try:
-        gpu = run_gpu(inp, sp, 5, 6)
-    finally:
-        lib.spec_set_spin_limit(1 << 18)
+    d = H.to_device(inp)
+    res = L.spec_verify_batch(d["target"], d["draft"], d["tokens"], d["cu"], int(inp.gammas.max()),
+                              temperature=1.0, seed=5, step=6, options=L.call_options(spin_limit=0))
+    torch.cuda.synchronize()
+    gpu = H.gpu_to_numpy(res)
     refs = H.oracle_requests(inp, sp, 5, 6, range(6))
     timed = (gpu["status"] & L.STATUS["TIMEOUT"]) != 0
     note(f"timed-out requests: {np.nonzero(timed)[0].tolist()}")
