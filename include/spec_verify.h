@@ -52,6 +52,8 @@ extern "C" {
 #define SPEC_ERR_UNSUPPORTED (-2) /* a valid combination this build does not implement     */
 #define SPEC_ERR_WORKSPACE (-3)   /* workspace smaller than the *_workspace_bytes figure    */
 #define SPEC_ERR_LAUNCH (-4)      /* a HIP launch failed                                    */
+#define SPEC_ERR_SCRATCH_LIMIT (-5) /* spec_verify_batch_noalloc: the call needs more workspace
+                                       than SPEC_NOALLOC_SCRATCH_BYTES                        */
 
 /* per-request / per-row status bits written to out_status on the device */
 #define SPEC_STATUS_NONFINITE 1        /* NaN or +inf logit, or a row with no finite logit:
@@ -188,6 +190,27 @@ int spec_verify_batch_ex(int B, int V, int gamma_max, spec_dtype dt,
 
 size_t spec_verify_workspace_bytes(int B, int V, int gamma_max, spec_dtype dt,
                                    spec_sampling_params sp);
+
+/* spec_verify_batch_noalloc -- spec_verify_batch for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments and results without the workspace.  The workspace is a static device array of the
+ * library, SPEC_NOALLOC_SCRATCH_BYTES on each GPU it runs on, held until the process ends; its
+ * address is looked up once per device on the first call there, which also clears it with one
+ * kernel on `hip_stream`.  The call allocates nothing (no hipMalloc, no library allocation).
+ * Every call on one GPU shares that GPU's array and it keeps the last call's contents: calls
+ * that overlap in time on one GPU (different streams, threads or processes' graphs) race; order
+ * them, for example on one stream.  A call whose spec_verify_workspace_bytes exceeds the array
+ * returns SPEC_ERR_SCRATCH_LIMIT before any launch (the batch-64 and batch-256 unfiltered
+ * workloads need a few MB; top-k filtered batches of 256 requests need more than the array). */
+#define SPEC_NOALLOC_SCRATCH_BYTES (32u << 20)
+int spec_verify_batch_noalloc(int B, int V, int gamma_max, spec_dtype dt,
+                              const void* target_logits, int64_t target_ld,
+                              const void* draft_logits, int64_t draft_ld,
+                              const int32_t* draft_tokens, const int32_t* cu_draft, int n_draft_rows,
+                              spec_sampling_params sp, uint64_t seed, uint64_t step,
+                              int32_t* out_tokens, int32_t* out_num_accepted,
+                              spec_pos_stats pos_stats, float* out_req_stats, int32_t* out_status,
+                              void* hip_stream);
 
 /* spec_row_stats -- per-row statistics of R filtered, tempered logit rows (the signals of the
  * SpecKV page, computed on the distribution actually sampled from).  Each output is [R] and

@@ -14,7 +14,7 @@ import torch
 
 __all__ = [
     "SPEC_F32", "SPEC_BF16", "STATUS", "PATHS", "load_library", "library_path", "call_options",
-    "spec_verify_batch", "spec_row_stats", "spec_residual_sample", "spec_status_string",
+    "spec_verify_batch", "spec_verify_batch_noalloc", "spec_row_stats", "spec_residual_sample", "spec_status_string",
     "spec_verify_workspace_bytes", "spec_row_stats_workspace_bytes",
     "spec_residual_sample_workspace_bytes",
 ]
@@ -91,6 +91,9 @@ def load_library():
                                       u64, u64, vp, vp, PosStats, vp, vp, vp, sz, vp]
     lib.spec_verify_batch_ex.restype = i32
     lib.spec_verify_batch_ex.argtypes = lib.spec_verify_batch.argtypes + [op]
+    lib.spec_verify_batch_noalloc.restype = i32
+    lib.spec_verify_batch_noalloc.argtypes = [i32, i32, i32, i32, vp, i64, vp, i64, vp, vp, i32, SamplingParams,
+                                              u64, u64, vp, vp, PosStats, vp, vp, vp]
     lib.spec_verify_workspace_bytes.restype = sz
     lib.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, i32, SamplingParams]
     lib.spec_row_stats.restype = i32
@@ -247,6 +250,32 @@ def spec_verify_batch(target_logits, draft_logits, draft_tokens, cu_draft, gamma
                                   _ptr(o["status"]), wp, wn, _stream(stream), _opt_ptr(options))
     _check(rc, "spec_verify_batch")
     return o
+
+
+def spec_verify_batch_noalloc(target_logits, draft_logits, draft_tokens, cu_draft, gamma_max, *, out,
+                              temperature=1.0, top_k=0, top_p=1.0, seed=0, step=0, stream=None):
+    """spec_verify_batch without a workspace, for callers that cannot allocate device memory:
+    the library's static per-GPU scratch serves as the workspace (see the header).  ``out``
+    holds the caller's output tensors (the keys spec_verify_batch returns; tokens, num_accepted
+    and status are required, the statistics optional).  Raises when the call needs more than
+    the scratch holds."""
+    lib = load_library()
+    B = cu_draft.numel() - 1
+    V = target_logits.shape[1]
+    dt = _dtype_code(target_logits)
+    tp, tld = _rows(target_logits, "target_logits")
+    dp, dld = (None, 0) if draft_logits is None else _rows(draft_logits, "draft_logits")
+    for t, n in ((draft_tokens, "draft_tokens"), (cu_draft, "cu_draft")):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 CUDA tensor")
+    ps = PosStats(*[_ptr(out.get(k)) for k in POS_STATS_FIELDS])
+    rc = lib.spec_verify_batch_noalloc(B, V, gamma_max, dt, tp, tld, dp, dld, _ptr(draft_tokens), _ptr(cu_draft),
+                                       draft_tokens.numel(), _sp(temperature, top_k, top_p),
+                                       int(seed) & (2**64 - 1), int(step) & (2**64 - 1), _ptr(out["tokens"]),
+                                       _ptr(out["num_accepted"]), ps, _ptr(out.get("req_stats")),
+                                       _ptr(out["status"]), _stream(stream))
+    _check(rc, "spec_verify_batch_noalloc")
+    return out
 
 
 def spec_row_stats(logits, *, temperature=1.0, top_k=0, top_p=1.0, workspace=None, stream=None, options=None):

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libspecverify.so"
-SOURCES = ["spec_api.hip", "spec_kernels.hip", "spec_fused.hip", "spec_filter.hip", "spec_head.hip"]
+SOURCES = ["spec_api.hip", "spec_kernels.hip", "spec_fused.hip", "spec_filter.hip", "spec_head.hip",
+           "spec_noalloc.hip"]
 ARCH = os.environ.get("SPEC_OFFLOAD_ARCH", "gfx950")
 
 

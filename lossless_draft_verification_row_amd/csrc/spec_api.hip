@@ -246,6 +246,7 @@ const char* spec_status_string(int code) {
     case SPEC_ERR_UNSUPPORTED: return "unsupported combination";
     case SPEC_ERR_WORKSPACE: return "workspace too small";
     case SPEC_ERR_LAUNCH: return "HIP launch failed";
+    case SPEC_ERR_SCRATCH_LIMIT: return "call needs more workspace than the no-allocation scratch holds";
     case SPEC_STATUS_NONFINITE: return "non-finite logits";
     case SPEC_STATUS_BAD_TOKEN: return "draft token out of range";
     case SPEC_STATUS_ZERO_Q: return "draft probability of the draft token is zero";
