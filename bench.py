@@ -1,11 +1,14 @@
 """Benchmark: batched speculative-sampling verification on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-per-config] [--no-cpu-baseline]
 
 A step is one spec_verify_batch call over one batch of the workload (every row read, accept
 scan, correction / bonus sampling, signals).  Inputs are synthetic, seeded, resident in HBM
 before the timed region; several copies of the batch are rotated so the 256 MB last-level
-cache cannot serve a later step from an earlier one.  Prints one JSON line.
+cache cannot serve a later step from an earlier one.  Prints one JSON line: the headline
+workload (config 2 by default), then `per_config` with the other workloads (B=128 ragged
+Llama-3 vocabulary, greedy B=256, filtered B=256), the streaming-read ceiling of the same GPU
+and the fp64 oracle timed over the host's cores.
 """
 from __future__ import annotations
 
@@ -31,6 +34,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="measure only --config (by default configs 3, 4 and 5 follow in per_config)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--lm-head", action="store_true",
                     help="time the fused LM head (spec_lm_head_row_stats) on the batch-64 workload's "
@@ -130,31 +135,64 @@ def algorithmic_bytes(inp):
     return rows * V * esz
 
 
-def cpu_baseline(inp, budget_s):
-    """The fp64 oracle as it stands, on a bounded sample of requests of the same workload."""
+def _oracle_request(args):
+    """One request through the fp64 oracle (a worker-process task of the CPU baseline)."""
     from oracle import spec_oracle as O
-    import importlib
+    tl, dl, ys, dtype, sp, b = args
+    widen = ((lambda a: (np.asarray(a, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+              .astype(np.float64)) if dtype == "bf16" else (lambda a: np.asarray(a, np.float64)))
+    O.verify_request(widen(tl), None if dl is None else widen(dl), ys, sp, 1, 0, b)
+    return len(ys)
+
+
+def cpu_workers():
+    """Worker count of the CPU baseline: every host core the process may use."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(inp, budget_s, pool, n_workers):
+    """The fp64 oracle as it stands (never tuned for this), over a pool of worker processes, one
+    request per task, on repeated passes over the workload's batch: three runs of about a third
+    of the budget each, the median reported as verified positions per second."""
+    from oracle import spec_oracle as O
     sp = O.SamplingParams(inp.wl.temperature, inp.wl.top_k, inp.wl.top_p)
-    W = importlib.import_module("lossless_draft_verification_row_amd.workloads")
-    t0 = time.perf_counter()
-    done, positions = 0, 0
     B = len(inp.gammas)
-    while time.perf_counter() - t0 < budget_s:
-        b = done % B   # the same requests again once the batch is exhausted
-        g = int(inp.gammas[b])
-        c0 = int(inp.cu_draft[b])
-        conv = (lambda a: W.bf16_bits_to_f32(a).astype(np.float64)) if inp.wl.dtype == "bf16" else \
-            (lambda a: np.asarray(a, np.float64))
-        tl = conv(inp.target[c0 + b:c0 + b + g + 1])
-        dl = None if (inp.draft is None or sp.temperature == 0) else conv(inp.draft[c0:c0 + g])
-        O.verify_request(tl, dl, [int(y) for y in inp.tokens[c0:c0 + g]], sp, 1, 0, b)
-        done += 1
-        positions += g
-    el = time.perf_counter() - t0
+    tasks = []
+    for b in range(B):
+        g, c0 = int(inp.gammas[b]), int(inp.cu_draft[b])
+        tl = np.ascontiguousarray(inp.target[c0 + b:c0 + b + g + 1])
+        dl = None if (inp.draft is None or sp.temperature == 0) else np.ascontiguousarray(inp.draft[c0:c0 + g])
+        tasks.append((tl, dl, [int(y) for y in inp.tokens[c0:c0 + g]], inp.wl.dtype, sp, b))
+    rates, total_req, total_pos = [], 0, 0
+    for _ in range(3):
+        t0 = time.perf_counter()
+        pos = req = 0
+        while time.perf_counter() - t0 < budget_s / 3:
+            pos += sum(pool.map(_oracle_request, tasks, chunksize=1))
+            req += B
+        el = time.perf_counter() - t0
+        rates.append(pos / el)
+        total_req += req
+        total_pos += pos
     return {
-        "value": positions / el, "unit": "positions/s", "cores": 1, "kind": "oracle",
-        "sample": f"{done} request verifications (batch of {B} cycled; {positions} verified positions) in {el:.1f} s, "
-                  f"single-threaded numpy fp64 on {platform.processor() or platform.machine()}",
+        "value": float(np.median(rates)), "unit": "positions/s", "cores": n_workers, "kind": "oracle",
+        "sample": f"{total_req} request verifications ({total_pos} verified positions; the workload's batch of "
+                  f"{B} requests repeated) in three runs of about {budget_s / 3:.0f} s, median of the three rates; "
+                  f"fp64 numpy oracle, one request per task over {n_workers} worker processes on {cpu_model()}",
     }
 
 
@@ -286,29 +324,12 @@ def lm_head_bench(args, L, W, torch):
     print(json.dumps(line), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: one GPU's share of the "
-                                   "request batch is the unit measured; --gpus must be 1"}))
-        sys.exit(2)
-    import torch
-    import lossless_draft_verification_row_amd as L
-    from lossless_draft_verification_row_amd import workloads as W
-
-    if args.copy_ref:
-        copy_reference(args.steps)
-        return
-
-    if not torch.cuda.is_available():
-        print(json.dumps({"error": "no GPU visible"}))
-        sys.exit(1)
-    if args.lm_head:
-        lm_head_bench(args, L, W, torch)
-        return
-    lib = L.load_library()
+def measure(cfg, args, torch, L, W, steps, warmup):
+    """One workload: seeded inputs resident in HBM (rotated copies beyond the 256 MB last-level
+    cache), `warmup` untimed calls, `steps` calls timed on the host clock between two
+    synchronisations, then `steps` more with events recorded by the streaming kernel's own
+    dispatch.  Returns the inputs and the measured figures."""
     dev = torch.device("cuda", 0)
-    cfg = args.config
     inp = W.make_inputs(cfg)
     wl = inp.wl
     if wl.temperature > 0 and inp.draft is not None and (0 < wl.top_k < wl.V or wl.top_p < 1.0):
@@ -351,42 +372,87 @@ def main():
                                    top_k=wl.top_k, top_p=wl.top_p, seed=1234, step=k, workspace=ws, out=out,
                                    options=options)
 
-    for k in range(args.warmup):
+    for k in range(warmup):
         step(k)
     torch.cuda.synchronize()
 
     # the timed region: exactly `steps` calls, nothing else on the stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(args.warmup + k)
+    for k in range(steps):
+        step(warmup + k)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     st = out["status"].cpu().numpy()
 
-    # outside the timed region: the same calls again, each with HIP events recorded on the
-    # library's stream right around its streaming kernel (the roofline's kernel time)
+    # outside the timed region: the same calls again, each with events recorded by the dispatch
+    # of its streaming kernel (the roofline's kernel time)
     ev = HipEvents()
-    pairs = ev.timed_pairs(args.steps)
+    pairs = ev.timed_pairs(steps)
     torch.cuda.synchronize()
-    for k in range(args.steps):
-        step(args.warmup + args.steps + k, L.call_options(profile_events=pairs[k]))
+    for k in range(steps):
+        step(warmup + steps + k, L.call_options(profile_events=pairs[k]))
     torch.cuda.synchronize()
     kernel_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
     ev.close()
+    del tgts, drfs, ws
+    torch.cuda.empty_cache()
 
-    sec_per_step = (t1 - t0) / args.steps
-    kern_avg_s = float(np.mean(kernel_ms)) / 1e3
-    achieved = alg_bytes / kern_avg_s / 1e9
-    fused = True
+    sec = (t1 - t0) / steps
+    kern_s = float(np.mean(kernel_ms)) / 1e3
     filtered = wl.temperature > 0 and 0 < wl.top_k < wl.V
-    if filtered:
-        kernel_key, kernel_name = "k_filt_slices", ("k_filt_slices (streaming kernel: every needed logit "
-                                                    "read once, per-slice top-k candidates)")
-    elif fused:
-        kernel_key, kernel_name = "k_fused", "k_fused (streaming kernel: every needed logit read once, both phases)"
-    else:
-        kernel_key, kernel_name = "k_pass1", "k_pass1 (streaming pass over every needed logit)"
+    return {
+        "inp": inp, "B": B, "G": G, "positions": positions, "alg_bytes": alg_bytes, "copies": copies,
+        "sec": sec, "kern_s": kern_s, "kernel_ms": kernel_ms, "status_nonzero": int((st != 0).sum()),
+        "kernel_key": "k_filt_slices" if filtered else "k_fused",
+    }
+
+
+def summary(m):
+    """The per-config figures of a measurement."""
+    return {
+        "workload": m["inp"].wl.name, "call_us": m["sec"] * 1e6, "positions_per_s": m["positions"] / m["sec"],
+        "kernel": m["kernel_key"], "kernel_us": m["kern_s"] * 1e6,
+        "kernel_frac": m["alg_bytes"] / m["kern_s"] / 1e9 / HBM_PEAK_GBS,
+        "end_to_end_frac": m["alg_bytes"] / m["sec"] / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_bytes": m["alg_bytes"], "status_nonzero_requests": m["status_nonzero"],
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: one GPU's share of the "
+                                   "request batch is the unit measured; --gpus must be 1"}))
+        sys.exit(2)
+    # the CPU baseline's worker processes start before anything touches the GPU
+    pool, n_workers = None, 0
+    if not args.no_cpu_baseline and not args.copy_ref and not args.lm_head:
+        import multiprocessing as mp
+        n_workers = cpu_workers()
+        pool = mp.get_context("spawn").Pool(n_workers)
+    import torch
+    import lossless_draft_verification_row_amd as L
+    from lossless_draft_verification_row_amd import workloads as W
+
+    if args.copy_ref:
+        copy_reference(args.steps)
+        return
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    if args.lm_head:
+        lm_head_bench(args, L, W, torch)
+        return
+    m = measure(args.config, args, torch, L, W, args.steps, args.warmup)
+    inp, wl = m["inp"], m["inp"].wl
+    alg_bytes, kern_avg_s, sec_per_step = m["alg_bytes"], m["kern_s"], m["sec"]
+    achieved = alg_bytes / kern_avg_s / 1e9
+    kernel_key = m["kernel_key"]
+    kernel_name = (("k_filt_slices (streaming kernel: every needed logit read once, per-slice top-k candidates)")
+                   if kernel_key == "k_filt_slices" else
+                   "k_fused (streaming kernel: every needed logit read once, both phases)")
     counters = load_traffic(kernel_key) or {}
     traffic = counters.get("bytes_per_launch")
     # VALU issue fraction: the kernel's VALU instructions (SQ_INSTS_VALU per launch, from the
@@ -396,7 +462,7 @@ def main():
     valu_frac = valu * 4.0 / (kern_avg_s * 2.4e9 * 1024) if valu else None
     line = {
         "metric": "verified draft positions/sec (and streaming-kernel HBM GB/s vs peak), 1 MI355X",
-        "value": positions / sec_per_step,
+        "value": m["positions"] / sec_per_step,
         "unit": "positions/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -413,21 +479,31 @@ def main():
                     if wl.temperature > 0 and (0 < wl.top_k < wl.V or wl.top_p < 1.0) else
                     ", draft tokens drawn from the tempered draft distribution)" if wl.temperature > 0 else
                     ", draft tokens = argmax of target + noise)")),
-        "config": {"workload": wl.name, "B": B, "gamma": G, "V": wl.V, "positions_per_step": positions,
+        "config": {"workload": wl.name, "B": m["B"], "gamma": m["G"], "V": wl.V, "positions_per_step": m["positions"],
                    "temperature": wl.temperature, "top_k": wl.top_k, "top_p": wl.top_p,
                    "outputs": ["tokens", "num_accepted", "status", "req_stats", *OUTPUTS_PER_POSITION],
-                   "algorithmic_bytes_per_step": alg_bytes, "input_copies_rotated": copies,
+                   "algorithmic_bytes_per_step": alg_bytes, "input_copies_rotated": m["copies"],
                    "end_to_end_GBps": alg_bytes / sec_per_step / 1e9,
-                   "status_nonzero_requests": int((st != 0).sum())},
+                   "status_nonzero_requests": m["status_nonzero"]},
         "roofline": {"bound": "hbm", "kernel": kernel_name,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "end_to_end_frac": alg_bytes / sec_per_step / 1e9 / HBM_PEAK_GBS,
                      "traffic": traffic, "kernel_ms_avg": kern_avg_s * 1e3,
-                     "kernel_ms_p10_p50_p90": [float(x) for x in np.percentile(kernel_ms, [10, 50, 90])],
+                     "kernel_ms_p10_p50_p90": [float(x) for x in np.percentile(m["kernel_ms"], [10, 50, 90])],
                      "valu_issue_frac": valu_frac},
     }
+    if not args.no_per_config:
+        line["per_config"] = {}
+        for c in (3, 4, 5):
+            if c == args.config:
+                continue
+            line["per_config"][str(c)] = summary(measure(c, args, torch, L, W, max(10, args.steps // 2),
+                                                         args.warmup))
     line["stream_ceiling"] = stream_ceiling(torch, L)
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    if pool is not None:
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, pool, n_workers)
+        pool.terminate()
+        pool.join()
     print(json.dumps(line), flush=True)
 
 
