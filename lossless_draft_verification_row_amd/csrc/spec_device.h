@@ -449,17 +449,27 @@ __device__ __forceinline__ TeamStat load_team(const TeamStat* p) {
 
 // ---------------------------------------------------------------- scalar loads
 
+// The wave's (uniform) pointer in scalar registers: callers pass wave-uniform addresses, and
+// taking the first lane's copy lets the scalar load below take it even where the compiler cannot
+// prove the uniformity itself.
+__device__ __forceinline__ const int32_t* uniform_ptr(const int32_t* p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const int32_t*)(((uint64_t)hi << 32) | lo);
+}
+
 // A uniform 32-bit load through the scalar data cache (read-only data of the call).
 __device__ __forceinline__ int sload_i32(const int32_t* p) {
   int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_ptr(p)) : "memory");
   return v;
 }
 
 // Two consecutive uniform 32-bit values in one scalar load (p 4-byte aligned).
 __device__ __forceinline__ void sload2_i32(const int32_t* p, int& a, int& b) {
   uint64_t v;
-  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_ptr(p)) : "memory");
   a = (int)(uint32_t)v;
   b = (int)(uint32_t)(v >> 32);
 }
