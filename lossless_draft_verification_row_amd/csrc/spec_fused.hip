@@ -56,13 +56,13 @@ struct FinScratch {
   double us[kMaxGamma + 1][3];   // sampler uniforms (Philox words 1..3) of every position
   int ytok[kMaxGamma];
   double gm[kChunk / kGroup];
-  float dh[kMaxGamma], dm[kMaxGamma];
+  int spick[kMaxGamma + 1];      // level-1 pick of each position taken early (-1: none)
   double ap[kMaxGamma];          // accept probability of every position
-  float wsel[kGroup];
+  alignas(16) float wall[kChunk];   // the picked chunk's sampler weights
   double u[3];
   double red[kWaves];
   unsigned long long lowm;       // positions whose pair sums are recomputed (pair_sums_fp64)
-  int flags, status, n_acc, pos, wkind, y, kpick, gpick, xpick;
+  int flags, status, n_acc, pos, wkind, y, kpick, xpick;
 };
 
 struct LdsFin {
@@ -160,27 +160,68 @@ __device__ __forceinline__ void block_max_f(float (&v)[N], float* red) {
 
 // Fixed-order fp64 combine of one row's slice records held one per lane (lanes >= n_s hold
 // ref = -inf, s = 0): M = max ref, z = sum s 2^(ref - M), w = sum 2^(ref - M) (w_s + s_s (ref - M)).
-struct RowComb {
-  double z, w;
-  float M;
-  bool ok;
-};
-__device__ __forceinline__ RowComb combine_lanes(float ref, float s, float w, bool in_range) {
-  RowComb rc;
-  const bool bad = in_range && (!(s == s) || !(s < INFINITY) || ref == INFINITY);
-  const float M = wave_max_dpp(in_range ? ref : -INFINITY);
-  double z = 0.0, ww = 0.0;
-  if (in_range && s > 0.f) {
-    const double d = (double)ref - (double)M;
-    const double f = exp2_split(d);
-    z = (double)s * f;
-    ww = f * ((double)w + (double)s * d);
+// Several wave reductions at once, step by step in the fixed order of wave_sum_dpp_d /
+// wave_max_dpp for every value, so that their DPP latencies overlap; every lane gets the
+// results.
+template <int N>
+__device__ __forceinline__ void wave_sums_dpp_d(double (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_d<0xb1, 0xf>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_d<0x4e, 0xf>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_d<0x124, 0xf>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_d<0x128, 0xf>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_d<0x142, 0xa>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_d<0x143, 0xc>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = readlane_d(v[i], 63);
+}
+template <int N>
+__device__ __forceinline__ void wave_maxs_dpp(float (&v)[N]) {
+  const float ninf = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], SPEC_DPP(ninf, v[i], 0xb1, 0xf));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], SPEC_DPP(ninf, v[i], 0x4e, 0xf));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], SPEC_DPP(ninf, v[i], 0x124, 0xf));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], SPEC_DPP(ninf, v[i], 0x128, 0xf));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], SPEC_DPP(ninf, v[i], 0x142, 0xa));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], SPEC_DPP(ninf, v[i], 0x143, 0xc));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[i]), 63));
+}
+// Two inverse-CDF picks (wave_pick) side by side.
+__device__ __forceinline__ void wave_pick2(const double (&m)[2], int n, const double (&u)[2], int (&pick)[2]) {
+  const int lane = threadIdx.x & 63;
+  const bool in = lane < n;
+  double cum[2] = {in ? m[0] : 0.0, in ? m[1] : 0.0};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) cum[i] += dpp_d<0x111, 0xf>(cum[i]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) cum[i] += dpp_d<0x112, 0xf>(cum[i]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) cum[i] += dpp_d<0x114, 0xf>(cum[i]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) cum[i] += dpp_d<0x118, 0xf>(cum[i]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) cum[i] += dpp_d<0x142, 0xa>(cum[i]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) cum[i] += dpp_d<0x143, 0xc>(cum[i]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const double total = readlane_d(cum[i], 63);
+    const unsigned long long over = __ballot(in && cum[i] > u[i] * total);
+    const unsigned long long pos = __ballot(in && m[i] > 0.0);
+    pick[i] = !(total > 0.0) ? -1 : (over ? __builtin_ctzll(over) : (pos ? 63 - __builtin_clzll(pos) : -1));
   }
-  rc.z = wave_sum_dpp_d(z);
-  rc.w = wave_sum_dpp_d(ww);
-  rc.M = M;
-  rc.ok = wave_all(!bad) && rc.z > 0.0 && M > -INFINITY;
-  return rc;
 }
 
 // ---------------------------------------------------------------- finalize one request
@@ -238,46 +279,38 @@ __device__ __forceinline__ TeamRaw team_load(const FusedArgs& a, __amdgpu_buffer
 template <int DT, bool VEC, int MODE>
 __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   FinScratch& F = L.fin;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // the wave index in a scalar register, so that per-team values derived from it stay scalar
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int G1 = a.G + 1;
   const int n_s = a.n_s;
   const uint32_t tag = a.tag;
   const float nan = __int_as_float(0x7fc00000);
   const double cd = (double)a.c;
   const __amdgpu_buffer_rsrc_t rrs = rec_rsrc(a);
-  // the draft tokens go out before this request's offsets arrive, at c0 = b G (exact when every
-  // request has G draft tokens); a wrong guess loads them again
+  // Every load of the request goes out before anything waits, at the guess c0 = b G, g = G
+  // (exact when every request has G draft tokens): the first two teams of each wave, the draft
+  // tokens and (sampling) their logits kept by the streaming kernel, the request's offsets and
+  // the whole offset array.  A wrong guess loads the request's part again.
   const int cg = b * a.G;
   const bool guess_in = cg + a.G <= a.n_draft_rows;
-  int ytok = -1;
-  if (guess_in && t < a.G) ytok = a.tokens[cg + t];
-  // this request's offsets straight from memory; the whole array is checked below, and these
-  // are clamped into the declared arrays until then (an offset pair failing this test fails
-  // the whole check too)
-  int c0, c1;
-  sload2_i32(a.cu + b, c0, c1);
-  const bool gok = c0 >= 0 && c1 >= c0 && c1 - c0 <= a.G && c1 <= a.n_draft_rows && c0 + b + (c1 - c0) < a.n_teams;
-  if (!gok) c0 = c1 = 0;
-  const int g = c1 - c0;
-  if (!(guess_in && c0 == cg)) ytok = t < g ? a.tokens[c0 + t] : -1;
-  if (t >= g) ytok = -1;
-  // the first two teams of this wave, the offset array, the draft tokens' logits and the
-  // Philox blocks do not depend on one another: all go out before anything waits (the teams
-  // first: the logits wait for the tokens)
   TeamRaw pre[2];
-  pre[0] = team_load<MODE>(a, rrs, c0, b, g, wave);
-  pre[1] = team_load<MODE>(a, rrs, c0, b, g, wave + kWaves);
+  int ytok = -1;
+  float ly_p = 0.f, ly_q = 0.f;
+  if (guess_in) {
+    pre[0] = team_load<MODE>(a, rrs, cg, b, a.G, wave);
+    pre[1] = team_load<MODE>(a, rrs, cg, b, a.G, wave + kWaves);
+    if (t < a.G) {
+      ytok = a.tokens[cg + t];
+      if (MODE == kFuSample) { ly_p = a.ylog[2 * (cg + t)]; ly_q = a.ylog[2 * (cg + t) + 1]; }
+    }
+  }
+  int c0 = a.cu[b], c1 = a.cu[b + 1];
   int cu_pre[(kMaxReqFused + 1 + kThreads - 1) / kThreads];
 #pragma unroll
   for (int k = 0; k < (kMaxReqFused + 1 + kThreads - 1) / kThreads; ++k)
     cu_pre[k] = t + k * kThreads <= a.B ? a.cu[t + k * kThreads] : 0;
-  float ly_p = 0.f, ly_q = 0.f;
-  if (t < g && ytok >= 0 && ytok < a.V) {
-    ly_p = logit_at<DT>(row_ptr<DT>(a.tgt, a.tgt_ld, c0 + b + t), ytok);
-    if (MODE == kFuSample) ly_q = logit_at<DT>(row_ptr<DT>(a.drf, a.drf_ld, c0 + t), ytok);
-  }
   double u_acc = 0.0;
-  if (t <= g) {
+  if (t <= a.G) {
     // the Philox block of position t (1-based i = t + 1): word 0 is the accept draw, words
     // 1..3 the sampler's uniforms if the emitted token is drawn there
     uint64_t w[4];
@@ -287,6 +320,19 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
     F.us[t][1] = u53(w[2]);
     F.us[t][2] = u53(w[3]);
   }
+  // this request's offsets are clamped into the declared arrays until the whole array is
+  // checked below (an offset pair failing this test fails that check too)
+  const bool gok = c0 >= 0 && c1 >= c0 && c1 - c0 <= a.G && c1 <= a.n_draft_rows && c0 + b + (c1 - c0) < a.n_teams;
+  if (!gok) c0 = c1 = 0;
+  const int g = c1 - c0;
+  if (!(guess_in && c0 == cg && g == a.G)) {
+    pre[0] = team_load<MODE>(a, rrs, c0, b, g, wave);
+    pre[1] = team_load<MODE>(a, rrs, c0, b, g, wave + kWaves);
+    ytok = t < g ? a.tokens[c0 + t] : -1;
+    if (MODE == kFuSample && t < g) { ly_p = a.ylog[2 * (c0 + t)]; ly_q = a.ylog[2 * (c0 + t) + 1]; }
+  }
+  if (t >= g) ytok = -1;
+  if (MODE == kFuTokenOnly && ytok >= 0 && ytok < a.V) ly_p = logit_at<DT>(row_ptr<DT>(a.tgt, a.tgt_ld, c0 + b + t), ytok);
   // the draft offsets as one exclusive prefix: every request is refused when any is out of order
   if (stage_cu(a, cu_pre, L.cu, L.i)) {
     if (t <= a.G) a.out_tokens[(int64_t)b * G1 + t] = -1;
@@ -299,137 +345,182 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
     return;
   }
 
-  // A. combine each team's records (one wave per team); the streaming kernel has finished.  The
-  // first two teams of each wave keep their per-slice p records and residual masses in
-  // registers for the level-1 pick.
+  // A. combine each team's records (one wave per team, two teams per pass side by side); the
+  // streaming kernel has finished.  The first two teams of each wave keep their per-slice p
+  // records and residual masses in registers for the level-1 pick.  Sampling: for those teams
+  // the level-1 pick of the token their position would emit (over [p - q]_+ for a paired
+  // position, over p for the bonus position) is taken at once, and the picked chunk is touched
+  // so that it sits in L2 when the sampler reads it (the touched words are only consumed at the
+  // end, so that nothing waits for them).
   float kpr[2] = {-INFINITY, -INFINITY}, kps[2] = {0.f, 0.f};
   double ksm[2] = {0.0, 0.0};
-  for (int ti = wave, it = 0; ti <= g; ti += kWaves, ++it) {
-    const int r = c0 + b + ti;
-    const bool pair = (MODE == kFuSample) && ti < g;
-    const bool in = lane < n_s;
-    const TeamRaw R = it < 2 ? pre[it] : team_load<MODE>(a, rrs, c0, b, g, ti);
-    float pr = -INFINITY, ps = 0.f, pw = 0.f, qr = -INFINITY, qs = 0.f, qw = 0.f;
-    double sm = 0.0;
-    bool ok = true;
-    if (in) {
-      ok = rec_ok(R.P, tag);
-      pr = __uint_as_float(R.P.x); ps = __uint_as_float(R.P.y); pw = __uint_as_float(R.P.z);
-      if (pair) {
-        ok = ok && rec_ok(R.Q, tag);
-        qr = __uint_as_float(R.Q.x); qs = __uint_as_float(R.Q.y); qw = __uint_as_float(R.Q.z);
+  constexpr int kEsz = DT == kDtBF16 ? 2 : 4;
+  constexpr int kTouch = kEsz / 2;   // 128-byte lines of a chunk row per lane
+  uint32_t tch[2][2][kTouch];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          sm += (double)lo_f(R.m[w]);
-          ok = ok && tag_of(R.m[w]) == tag;
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int h = 0; h < kTouch; ++h) tch[j][0][h] = tch[j][1][h] = 0u;
+  const bool in = lane < n_s;
+  for (int ti = wave, it = 0; ti <= g; ti += 2 * kWaves, it += 2) {
+    const int tt[2] = {ti, ti + kWaves};
+    TeamRaw R[2];
+    R[0] = it == 0 ? pre[0] : team_load<MODE>(a, rrs, c0, b, g, tt[0]);
+    R[1] = it == 0 ? pre[1] : team_load<MODE>(a, rrs, c0, b, g, tt[1]);
+    // rows 2j (p) and 2j + 1 (q) of team j
+    float ref[4], s[4], w[4];
+    double sm[2];
+    bool ok[2], pair[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      pair[j] = (MODE == kFuSample) && tt[j] < g;
+      ref[2 * j] = ref[2 * j + 1] = -INFINITY;
+      s[2 * j] = s[2 * j + 1] = w[2 * j] = w[2 * j + 1] = 0.f;
+      sm[j] = 0.0;
+      ok[j] = true;
+      if (in) {
+        ok[j] = rec_ok(R[j].P, tag);
+        ref[2 * j] = __uint_as_float(R[j].P.x); s[2 * j] = __uint_as_float(R[j].P.y); w[2 * j] = __uint_as_float(R[j].P.z);
+        if (pair[j]) {
+          ok[j] = ok[j] && rec_ok(R[j].Q, tag);
+          ref[2 * j + 1] = __uint_as_float(R[j].Q.x); s[2 * j + 1] = __uint_as_float(R[j].Q.y);
+          w[2 * j + 1] = __uint_as_float(R[j].Q.z);
+#pragma unroll
+          for (int q = 0; q < kWaves; ++q) {
+            sm[j] += (double)lo_f(R[j].m[q]);
+            ok[j] = ok[j] && tag_of(R[j].m[q]) == tag;
+          }
         }
       }
     }
-    if (it < 2) {
-      kpr[it & 1] = pr;
-      kps[it & 1] = ps;
-      ksm[it & 1] = sm;
+    if (it == 0) {
+      kpr[0] = ref[0]; kps[0] = s[0]; ksm[0] = sm[0];
+      kpr[1] = ref[2]; kps[1] = s[2]; ksm[1] = sm[1];
     }
-    const bool missing = !wave_all(ok);
-    TeamL T;
-    T.z[0] = T.z[1] = 1.0; T.w[0] = T.w[1] = 0.0; T.beta = 0.0; T.M[0] = T.M[1] = 0.f;
-    T.amax = -1;
-    T.flags = missing ? kTeamTimeout : 0;
+    TeamL T[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      T[j].z[0] = T[j].z[1] = 1.0; T[j].w[0] = T[j].w[1] = 0.0; T[j].beta = 0.0; T[j].M[0] = T[j].M[1] = 0.f;
+      T[j].amax = -1;
+      T[j].flags = wave_all(ok[j]) ? 0 : kTeamTimeout;
+    }
     if (MODE == kFuGreedy) {
-      const int qa = __float_as_int(ps);
-      const bool bad = in && (qa == -2 || pr == INFINITY);
-      const float M = wave_max_dpp(in ? pr : -INFINITY);
-      const int idx = wave_min_i((in && pr == M && qa >= 0) ? qa : INT_MAX);
-      T.M[0] = M;
-      T.amax = idx == INT_MAX ? -1 : idx;
-      if (!wave_all(!bad) || !(M > -INFINITY)) { T.flags |= kTeamBadP; T.amax = -1; }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int qa = __float_as_int(s[2 * j]);
+        const bool bad = in && (qa == -2 || ref[2 * j] == INFINITY);
+        const float M = wave_max_dpp(in ? ref[2 * j] : -INFINITY);
+        const int idx = wave_min_i((in && ref[2 * j] == M && qa >= 0) ? qa : INT_MAX);
+        T[j].M[0] = M;
+        T[j].amax = idx == INT_MAX ? -1 : idx;
+        if (!wave_all(!bad) || !(M > -INFINITY)) { T[j].flags |= kTeamBadP; T[j].amax = -1; }
+      }
     } else {
-      const RowComb P = combine_lanes(pr, ps, pw, in);
-      T.z[0] = P.z; T.w[0] = P.w; T.M[0] = P.M;
-      if (!P.ok) T.flags |= kTeamBadP;
-      if (pair) {
-        const RowComb Q = combine_lanes(qr, qs, qw, in);
-        T.z[1] = Q.z; T.w[1] = Q.w; T.M[1] = Q.M;
-        if (!Q.ok) T.flags |= kTeamBadQ;
-        // a slice whose team wait gave up marked its residual mass NaN
-        if (!wave_all(!(in && !(sm == sm)))) T.flags |= kTeamTimeout;
-        T.beta = wave_sum_dpp_d(in ? sm : 0.0);
+      // per row: M = max over slices, Z = sum s 2^(ref - M), W = sum 2^(ref - M) (w + s (ref - M))
+      bool use[4], bad[4];
+      float M[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        use[k] = in && ((k & 1) == 0 || pair[k >> 1]);
+        bad[k] = use[k] && (!(s[k] == s[k]) || !(s[k] < INFINITY) || ref[k] == INFINITY);
+        M[k] = use[k] ? ref[k] : -INFINITY;
+      }
+      wave_maxs_dpp(M);
+      double sums[10];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const double d = (double)ref[k] - (double)M[k];
+        const double e = exp2_split(d);
+        const bool on = use[k] && s[k] > 0.f;
+        sums[2 * k] = on ? (double)s[k] * e : 0.0;
+        sums[2 * k + 1] = on ? e * ((double)w[k] + (double)s[k] * d) : 0.0;
+      }
+      sums[8] = in ? sm[0] : 0.0;
+      sums[9] = in ? sm[1] : 0.0;
+      wave_sums_dpp_d(sums);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        T[j].z[0] = sums[4 * j]; T[j].w[0] = sums[4 * j + 1]; T[j].M[0] = M[2 * j];
+        if (!(wave_all(!bad[2 * j]) && sums[4 * j] > 0.0 && M[2 * j] > -INFINITY)) T[j].flags |= kTeamBadP;
+        if (pair[j]) {
+          T[j].z[1] = sums[4 * j + 2]; T[j].w[1] = sums[4 * j + 3]; T[j].M[1] = M[2 * j + 1];
+          if (!(wave_all(!bad[2 * j + 1]) && sums[4 * j + 2] > 0.0 && M[2 * j + 1] > -INFINITY)) T[j].flags |= kTeamBadQ;
+          // a slice whose team wait gave up marked its residual mass NaN
+          if (!wave_all(!(in && !(sm[j] == sm[j])))) T[j].flags |= kTeamTimeout;
+          T[j].beta = sums[8 + j];
+        }
       }
     }
-    if (lane == 0) F.team[ti] = T;
+    int spick[2] = {-1, -1};
+    if (MODE == kFuSample && it == 0) {
+      // the masses the level-1 pick takes for each team's position (wkind 1 paired, 0 bonus)
+      double m[2], u[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bool on = in && tt[j] <= g && T[j].flags == 0;
+        const double mp = s[2 * j] > 0.f ? (double)s[2 * j] * exp2_split((double)ref[2 * j] - (double)T[j].M[0]) / T[j].z[0] : 0.0;
+        m[j] = on ? (pair[j] ? sm[j] : mp) : 0.0;
+        u[j] = F.us[min(tt[j], g)][0];
+      }
+      wave_pick2(m, n_s, u, spick);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = c0 + b + min(tt[j], g);
+        const __amdgpu_buffer_rsrc_t rt = row_rsrc(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V * kEsz);
+        const __amdgpu_buffer_rsrc_t rd = row_rsrc(row_ptr<DT>(a.drf, a.drf_ld, c0 + min(tt[j], g)), a.V * kEsz);
+#pragma unroll
+        for (int h = 0; h < kTouch; ++h) {
+          const int line = spick[j] * kChunk * kEsz + (h * 64 + lane) * 128;
+          // a team without a pick (or without a draft row) reads past the resource: no access
+          tch[j][0][h] = __builtin_amdgcn_raw_buffer_load_b32(rt, spick[j] >= 0 ? line : 0x40000000, 0, 0);
+          tch[j][1][h] = __builtin_amdgcn_raw_buffer_load_b32(rd, spick[j] >= 0 && pair[j] ? line : 0x40000000, 0, 0);
+        }
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (tt[j] <= g) {
+          F.team[tt[j]] = T[j];
+          F.spick[tt[j]] = spick[j];
+        }
+    }
   }
   __syncthreads();
 
-  // B. per position: statistics, p(y), q(y), the accept draw
+  // B. the accept test of every position: p(y), q(y) and the accept draw
   bool rej = false, low = false;
   int why = 0;
-  if (t <= g) {
-    const int r = c0 + b + t;
+  if (t < g) {
     const TeamL T = F.team[t];
     const bool okp = (T.flags & (kTeamBadP | kTeamTimeout)) == 0;
-    const float hp = (float)(log2_split(T.z[0]) - T.w[0] / T.z[0]);
-    if (a.st.target_entropy_bits) a.st.target_entropy_bits[r] = okp ? (MODE == kFuGreedy ? 0.f : hp) : nan;
-    if (a.st.target_max_prob)
-      a.st.target_max_prob[r] = okp ? (MODE == kFuGreedy ? 1.f : (float)(1.0 / T.z[0])) : nan;
-    if (t < g) {
-      const int drow = c0 + t;
-      const int y = ytok;
-      const bool yv = y >= 0 && y < a.V;
-      float py = nan, qy = nan, ovl = nan, dh = nan, dm = nan, l1 = nan;
-      double pyd = 0.0, qyd = 1.0, ap = nan;
-      if (MODE == kFuGreedy) {
-        py = (okp && yv) ? (y == T.amax ? 1.f : 0.f) : nan;
-        qy = yv ? 1.f : nan;
-        ovl = okp ? (yv ? py : 0.f) : nan;
-        ap = okp ? ((yv && y == T.amax) ? 1.0 : 0.0) : nan;
-        l1 = (okp && yv) ? (y == T.amax ? 0.f : 2.f) : nan;
+    const int y = ytok;
+    const bool yv = y >= 0 && y < a.V;
+    double pyd = 0.0, qyd = 1.0, ap = nan;
+    if (MODE == kFuGreedy) {
+      ap = okp ? ((yv && y == T.amax) ? 1.0 : 0.0) : nan;
+    } else {
+      if (okp && yv) pyd = exp2_split((double)ly_p * cd - (double)T.M[0]) / T.z[0];
+      if (MODE == kFuTokenOnly) {
+        ap = okp ? (yv ? fmin(1.0, pyd) : 0.0) : nan;
       } else {
-        if (okp && yv) {
-          pyd = exp2_split((double)ly_p * cd - (double)T.M[0]) / T.z[0];
-          py = (float)pyd;
-        }
-        if (MODE == kFuTokenOnly) {
-          qy = yv ? 1.f : nan;
-          ovl = okp ? (yv ? py : 0.f) : nan;
-          dh = yv ? 0.f : nan;
-          dm = yv ? 1.f : nan;
-          ap = okp ? (yv ? fmin(1.0, pyd) : 0.0) : nan;
-          l1 = (okp && yv) ? (float)(2.0 * (1.0 - pyd)) : nan;
-        } else {
-          const bool okq = (T.flags & (kTeamBadQ | kTeamTimeout)) == 0;
-          if (okq && yv) {
-            qyd = exp2_split((double)ly_q * cd - (double)T.M[1]) / T.z[1];
-            qy = (float)qyd;
-          }
-          if (okp && okq) {
-            ovl = (float)(1.0 - T.beta);
-            low = T.beta < kPairRefine || 1.0 - T.beta < kPairRefine;
-            l1 = (float)(2.0 * T.beta);
-            ap = (yv && qyd > 0.0) ? fmin(1.0, pyd / qyd) : 0.0;
-          }
-          dh = okq ? (float)(log2_split(T.z[1]) - T.w[1] / T.z[1]) : nan;
-          dm = okq ? (float)(1.0 / T.z[1]) : nan;
+        const bool okq = (T.flags & (kTeamBadQ | kTeamTimeout)) == 0;
+        if (okq && yv) qyd = exp2_split((double)ly_q * cd - (double)T.M[1]) / T.z[1];
+        if (okp && okq) {
+          low = T.beta < kPairRefine || 1.0 - T.beta < kPairRefine;
+          ap = (yv && qyd > 0.0) ? fmin(1.0, pyd / qyd) : 0.0;
         }
       }
-      if (a.st.p_y) a.st.p_y[drow] = py;
-      if (a.st.q_y) a.st.q_y[drow] = qy;
-      if (a.st.one_minus_tv && !low) a.st.one_minus_tv[drow] = ovl;
-      if (a.st.l1 && !low) a.st.l1[drow] = l1;
-      if (a.st.draft_entropy_bits) a.st.draft_entropy_bits[drow] = dh;
-      if (a.st.draft_max_prob) a.st.draft_max_prob[drow] = dm;
-      if (a.st.accept_prob) a.st.accept_prob[drow] = (float)ap;
-      F.ap[t] = ap;
-      F.dh[t] = dh;
-      F.dm[t] = dm;
-      F.ytok[t] = y;
-      F.py[t] = pyd;
-      F.qy[t] = qyd;
-      // the accept test of position t (evaluated for every position; the scan takes the first)
-      if (!yv) { rej = true; why = kStBadToken; }
-      else if (MODE == kFuGreedy) rej = y != T.amax;
-      else if (!(qyd > 0.0)) { rej = true; why = kStZeroQ; }
-      else rej = !(u_acc < fmin(1.0, pyd / qyd));
     }
+    F.ap[t] = ap;
+    F.ytok[t] = y;
+    F.py[t] = pyd;
+    F.qy[t] = qyd;
+    // the accept test of position t (evaluated for every position; the scan takes the first)
+    if (!yv) { rej = true; why = kStBadToken; }
+    else if (MODE == kFuGreedy) rej = y != T.amax;
+    else if (!(qyd > 0.0)) { rej = true; why = kStZeroQ; }
+    else rej = !(u_acc < fmin(1.0, pyd / qyd));
   }
   // C. request flags and the first rejection (wave 0 covers positions 0..63)
   if (wave == 0) {
@@ -458,28 +549,221 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       F.u[2] = F.us[F.pos][2];
       F.status = status;
       F.kpick = -1;
+      F.flags = fl;
       F.lowm = lm;
-      if (a.st.expected_committed)
-        a.st.expected_committed[b] = fl ? nan : expected_committed(F.ap, g);
-      if (a.out_req_stats) {
-        float rq[4] = {nan, nan, nan, nan};
-        if (g > 0 && MODE != kFuGreedy) {
-          double hs = 0.0, cs = 0.0;
-          float hmax = -INFINITY, cmin = INFINITY;
-          bool anynan = false;
-          for (int i = 0; i < g; ++i) {
-            const float h = F.dh[i], cm = F.dm[i];
-            if (!(h == h) || !(cm == cm)) anynan = true;
-            hs += h; cs += cm;
-            hmax = fmaxf(hmax, h); cmin = fminf(cmin, cm);
-          }
-          if (!anynan) { rq[0] = (float)(hs / g); rq[1] = (float)(cs / g); rq[2] = hmax; rq[3] = cmin; }
-        }
-        for (int q = 0; q < 4; ++q) a.out_req_stats[(int64_t)b * 4 + q] = rq[q];
-      }
     }
   }
   __syncthreads();
+
+  int x = -1;
+  const bool sampled = MODE != kFuGreedy && !(F.status & (kStTimeout | kStNonfinite));
+  const int rpos = c0 + b + F.pos;
+  const TeamL TP = F.team[F.pos];
+  if (sampled) {
+    // D. level 1 over the chunk masses (p's masses again if the residual turned out empty), by
+    // the wave that combined team F.pos: taken already in A when that team was one of its
+    // first two; otherwise its per-slice values are still in registers (or read again)
+    const int own = F.pos & (kWaves - 1), oit = F.pos / kWaves;
+    if (wave == own) {
+      const bool kept = oit < 2;
+      const float kr = (oit & 1) ? kpr[1] : kpr[0], ks = (oit & 1) ? kps[1] : kps[0];
+      const double km = (oit & 1) ? ksm[1] : ksm[0];
+      int wkind = F.wkind;
+      int pick = MODE == kFuSample ? F.spick[F.pos] : -1;
+      for (int pass = 0; pass < 2 && pick < 0; ++pass) {
+        double m = 0.0;
+        if (lane < n_s) {
+          if (wkind == 1) {
+            if (kept) {
+              m = km;
+            } else {
+              const uint64_t* mw = a.smass + ((int64_t)rpos * n_s + lane) * kWaves;
+#pragma unroll
+              for (int w = 0; w < kWaves; ++w) m += (double)lo_f(ld_coh(mw + w));
+            }
+          } else {
+            float ref = kr, sv = ks, wv;
+            if (!kept) load_rec(rrs, rec_off(n_s, rpos, lane, 0), tag, ref, sv, wv);
+            m = sv > 0.f ? (double)sv * exp2_split((double)ref - (double)TP.M[0]) / TP.z[0] : 0.0;
+            if (wkind == 2) {
+              const int y = F.y;
+              if (y >= 0 && y < a.V && y / kChunk == lane) m = fmax(m - F.py[F.pos], 0.0);
+            }
+          }
+        }
+        double tot;
+        pick = wave_pick(m, n_s, F.u[0], tot);
+        if (pick >= 0 || wkind == 0) break;
+        wkind = 0;
+        if (lane == 0) F.status |= kStResidualEmpty;
+      }
+      if (lane == 0) { F.kpick = pick; F.wkind = wkind; }
+    }
+    __syncthreads();
+  }
+  // E1. the picked chunk's logits and its records go out; the statistics below are formed while
+  // they travel
+  const int k = sampled ? F.kpick : -1;
+  const int wkind = F.wkind;
+  const int grp = t >> 2, quarter = t & 3;
+  const int x0 = k * kChunk + grp * kGroup + quarter * 16;
+  float wv[16], vq[16];
+  float refp = 0.f, refq = 0.f, rr = 0.f;
+  if (k >= 0) {
+    load_run16<DT, VEC>(row_ptr<DT>(a.tgt, a.tgt_ld, rpos), a.V, x0, wv);
+    if (wkind == 1) load_run16<DT, VEC>(row_ptr<DT>(a.drf, a.drf_ld, c0 + F.pos), a.V, x0, vq);
+    float sp_, wp_;
+    load_rec(rrs, rec_off(n_s, rpos, k, 0), tag, refp, sp_, wp_);
+    if (wkind == 1) {
+      float sq_, wq_;
+      load_rec(rrs, rec_off(n_s, rpos, k, 1), tag, refq, sq_, wq_);
+    }
+  }
+
+  // B2. per-position statistics (the SpecKV page's signals, 1 - TV, p(y), q(y), accept
+  // probability) and the request's aggregates
+  if (t <= g) {
+    const int r = c0 + b + t;
+    const TeamL T = F.team[t];
+    const bool okp = (T.flags & (kTeamBadP | kTeamTimeout)) == 0;
+    const float hp = (float)(log2_split(T.z[0]) - T.w[0] / T.z[0]);
+    if (a.st.target_entropy_bits) a.st.target_entropy_bits[r] = okp ? (MODE == kFuGreedy ? 0.f : hp) : nan;
+    if (a.st.target_max_prob)
+      a.st.target_max_prob[r] = okp ? (MODE == kFuGreedy ? 1.f : (float)(1.0 / T.z[0])) : nan;
+  }
+  float dh = nan, dm = nan;
+  if (t < g) {
+    const int drow = c0 + t;
+    const TeamL T = F.team[t];
+    const bool okp = (T.flags & (kTeamBadP | kTeamTimeout)) == 0;
+    const int y = F.ytok[t];
+    const bool yv = y >= 0 && y < a.V;
+    const double pyd = F.py[t], qyd = F.qy[t];
+    float py = nan, qy = nan, ovl = nan, l1 = nan;
+    if (MODE == kFuGreedy) {
+      py = (okp && yv) ? (y == T.amax ? 1.f : 0.f) : nan;
+      qy = yv ? 1.f : nan;
+      ovl = okp ? (yv ? py : 0.f) : nan;
+      l1 = (okp && yv) ? (y == T.amax ? 0.f : 2.f) : nan;
+    } else {
+      if (okp && yv) py = (float)pyd;
+      if (MODE == kFuTokenOnly) {
+        qy = yv ? 1.f : nan;
+        ovl = okp ? (yv ? py : 0.f) : nan;
+        dh = yv ? 0.f : nan;
+        dm = yv ? 1.f : nan;
+        l1 = (okp && yv) ? (float)(2.0 * (1.0 - pyd)) : nan;
+      } else {
+        const bool okq = (T.flags & (kTeamBadQ | kTeamTimeout)) == 0;
+        if (okq && yv) qy = (float)qyd;
+        if (okp && okq) {
+          ovl = (float)(1.0 - T.beta);
+          l1 = (float)(2.0 * T.beta);
+        }
+        dh = okq ? (float)(log2_split(T.z[1]) - T.w[1] / T.z[1]) : nan;
+        dm = okq ? (float)(1.0 / T.z[1]) : nan;
+      }
+    }
+    const bool lw = (F.lowm >> t) & 1ull;
+    if (a.st.p_y) a.st.p_y[drow] = py;
+    if (a.st.q_y) a.st.q_y[drow] = qy;
+    if (a.st.one_minus_tv && !lw) a.st.one_minus_tv[drow] = ovl;
+    if (a.st.l1 && !lw) a.st.l1[drow] = l1;
+    if (a.st.draft_entropy_bits) a.st.draft_entropy_bits[drow] = dh;
+    if (a.st.draft_max_prob) a.st.draft_max_prob[drow] = dm;
+    if (a.st.accept_prob) a.st.accept_prob[drow] = (float)F.ap[t];
+  }
+  if (wave == 0) {
+    // the request's draft-signal aggregates in position order (positions 0..g-1 are lanes of
+    // this wave)
+    if (a.out_req_stats) {
+      float rq[4] = {nan, nan, nan, nan};
+      if (g > 0 && MODE != kFuGreedy) {
+        double hs = 0.0, cs = 0.0;
+        float hmax = -INFINITY, cmin = INFINITY;
+        bool anynan = false;
+        for (int i = 0; i < g; ++i) {
+          const float h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dh), i));
+          const float cm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dm), i));
+          if (!(h == h) || !(cm == cm)) anynan = true;
+          hs += h; cs += cm;
+          hmax = fmaxf(hmax, h); cmin = fminf(cmin, cm);
+        }
+        if (!anynan) { rq[0] = (float)(hs / g); rq[1] = (float)(cs / g); rq[2] = hmax; rq[3] = cmin; }
+      }
+      if (lane == 0)
+        for (int q = 0; q < 4; ++q) a.out_req_stats[(int64_t)b * 4 + q] = rq[q];
+    }
+    if (lane == 0 && a.st.expected_committed)
+      a.st.expected_committed[b] = F.flags ? nan : expected_committed(F.ap, g);
+  }
+
+  if (k >= 0) {
+    // E2. levels 2 and 3 inside chunk k.  Weights are relative within the chunk: e_p (p only)
+    // or max(e_p r - e_q, 0) with r = alpha_p / alpha_q.
+    if (wkind == 1) {
+      const double alp = exp2_split((double)refp - (double)TP.M[0]) / TP.z[0];
+      const double alq = exp2_split((double)refq - (double)TP.M[1]) / TP.z[1];
+      rr = (float)(alp / alq);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float ep = __builtin_amdgcn_exp2f(fmaf(wv[e], a.c, -refp));
+        const float eq = __builtin_amdgcn_exp2f(fmaf(vq[e], a.c, -refq));
+        wv[e] = fmaxf(fmaf(ep, rr, -eq), 0.f);
+      }
+    } else {
+      const int yx = F.y;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float ep = __builtin_amdgcn_exp2f(fmaf(wv[e], a.c, -refp));
+        wv[e] = (wkind == 2 && x0 + e == yx) ? 0.f : ep;
+      }
+    }
+    double part = 0.0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) part += (double)wv[e];
+    // group sum over the 4 threads of a group (quad lanes), in a fixed order
+    part += dpp_d<0xb1, 0xf>(part);
+    part += dpp_d<0x4e, 0xf>(part);
+    if (quarter == 0) F.gm[grp] = part;
+#pragma unroll
+    for (int e = 0; e < 16; e += 4)
+      *(float4*)&F.wall[grp * kGroup + quarter * 16 + e] = make_float4(wv[e], wv[e + 1], wv[e + 2], wv[e + 3]);
+    __syncthreads();
+    if (wave == 0) {
+      // level 2 over the chunk's groups, level 3 inside the picked group
+      const int n_in = min(kChunk, a.V - k * kChunk);
+      const int n_groups = (n_in + kGroup - 1) / kGroup;
+      double tot;
+      const int gsel = wave_pick(lane < n_groups ? F.gm[lane] : 0.0, n_groups, F.u[1], tot);
+      int pick = -1;
+      if (gsel >= 0) {
+        const int lo = k * kChunk + gsel * kGroup;
+        const int n = min(kGroup, a.V - lo);
+        pick = wave_pick(lane < n ? (double)F.wall[gsel * kGroup + lane] : 0.0, n, F.u[2], tot);
+        if (pick >= 0) pick += lo;
+      }
+      if (lane == 0) F.xpick = pick;
+    }
+    __syncthreads();
+    x = F.xpick;
+  } else if (MODE == kFuGreedy && !(F.status & (kStTimeout | kStNonfinite))) {
+    x = TP.amax;
+  }
+  // F. outputs
+  const bool ok = !(F.status & (kStTimeout | kStNonfinite));
+  if (t <= a.G) {
+    int tok = -1;
+    if (ok) {
+      if (t < F.n_acc) tok = F.ytok[t];
+      else if (t == F.n_acc) tok = x;
+    }
+    a.out_tokens[(int64_t)b * G1 + t] = tok;
+  }
+  if (t == 0) {
+    a.out_num_accepted[b] = ok ? F.n_acc : 0;
+    a.out_status[b] = F.status;
+  }
 
   // positions whose two distributions barely overlap or nearly coincide: A and beta again, with
   // fp64 normalisers and sums (pair_sums_fp64)
@@ -498,141 +782,11 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       }
     }
   }
-
-  int x = -1;
-  if (F.status & (kStTimeout | kStNonfinite)) {
-    x = -1;
-  } else if (MODE == kFuGreedy) {
-    x = F.team[F.pos].amax;
-  } else {
-    const int r = c0 + b + F.pos;
-    const TeamL T = F.team[F.pos];
-    // D. level 1 over the chunk masses (p's masses again if the residual turned out empty), by
-    // the wave that combined team F.pos: its per-slice values are still in registers when the
-    // team was one of its first two, else they are read again
-    const int own = F.pos & (kWaves - 1), oit = F.pos / kWaves;
-    if (wave == own) {
-      const bool kept = oit < 2;
-      const float kr = (oit & 1) ? kpr[1] : kpr[0], ks = (oit & 1) ? kps[1] : kps[0];
-      const double km = (oit & 1) ? ksm[1] : ksm[0];
-      int wkind = F.wkind;
-      int pick = -1;
-      for (int pass = 0; pass < 2; ++pass) {
-        double m = 0.0;
-        if (lane < n_s) {
-          if (wkind == 1) {
-            if (kept) {
-              m = km;
-            } else {
-              const uint64_t* mw = a.smass + ((int64_t)r * n_s + lane) * kWaves;
+  // the touched words are kept alive (their loads have long completed)
 #pragma unroll
-              for (int w = 0; w < kWaves; ++w) m += (double)lo_f(ld_coh(mw + w));
-            }
-          } else {
-            float ref = kr, sv = ks, wv;
-            if (!kept) load_rec(rrs, rec_off(n_s, r, lane, 0), tag, ref, sv, wv);
-            m = sv > 0.f ? (double)sv * exp2_split((double)ref - (double)T.M[0]) / T.z[0] : 0.0;
-            if (wkind == 2) {
-              const int y = F.y;
-              if (y >= 0 && y < a.V && y / kChunk == lane) m = fmax(m - F.py[F.pos], 0.0);
-            }
-          }
-        }
-        double tot;
-        pick = wave_pick(m, n_s, F.u[0], tot);
-        if (pick >= 0 || wkind == 0) break;
-        wkind = 0;
-        if (lane == 0) F.status |= kStResidualEmpty;
-      }
-      if (lane == 0) { F.kpick = pick; F.wkind = wkind; }
-    }
-    __syncthreads();
-    const int k = F.kpick;
-    if (k >= 0) {
-      // E. levels 2 and 3 inside chunk k.  Weights are relative within the chunk: e_p (p
-      // only) or max(e_p r - e_q, 0) with r = alpha_p / alpha_q.
-      const int wkind = F.wkind;
-      // the chunk's logits and its records go out together
-      const int grp = t >> 2, quarter = t & 3;
-      const int x0 = k * kChunk + grp * kGroup + quarter * 16;
-      float wv[16], vq[16];
-      load_run16<DT, VEC>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, x0, wv);
-      if (wkind == 1) load_run16<DT, VEC>(row_ptr<DT>(a.drf, a.drf_ld, c0 + F.pos), a.V, x0, vq);
-      float refp, sp_, wp_, refq = 0.f, rr = 0.f;
-      load_rec(rrs, rec_off(n_s, r, k, 0), tag, refp, sp_, wp_);
-      if (wkind == 1) {
-        float sq_, wq_;
-        load_rec(rrs, rec_off(n_s, r, k, 1), tag, refq, sq_, wq_);
-        const double alp = exp2_split((double)refp - (double)T.M[0]) / T.z[0];
-        const double alq = exp2_split((double)refq - (double)T.M[1]) / T.z[1];
-        rr = (float)(alp / alq);
-      }
-      if (wkind == 1) {
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float ep = __builtin_amdgcn_exp2f(fmaf(wv[e], a.c, -refp));
-          const float eq = __builtin_amdgcn_exp2f(fmaf(vq[e], a.c, -refq));
-          wv[e] = fmaxf(fmaf(ep, rr, -eq), 0.f);
-        }
-      } else {
-        const int yx = F.y;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float ep = __builtin_amdgcn_exp2f(fmaf(wv[e], a.c, -refp));
-          wv[e] = (wkind == 2 && x0 + e == yx) ? 0.f : ep;
-        }
-      }
-      double part = 0.0;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) part += (double)wv[e];
-      // group sum over the 4 threads of a group (quad lanes), in a fixed order
-      part += dpp_d<0xb1, 0xf>(part);
-      part += dpp_d<0x4e, 0xf>(part);
-      if (quarter == 0) F.gm[grp] = part;
-      __syncthreads();
-      const int n_in = min(kChunk, a.V - k * kChunk);
-      const int n_groups = (n_in + kGroup - 1) / kGroup;
-      if (wave == 0) {
-        double tot;
-        const int gp = wave_pick(lane < n_groups ? F.gm[lane] : 0.0, n_groups, F.u[1], tot);
-        if (lane == 0) F.gpick = gp;
-      }
-      __syncthreads();
-      if (grp == F.gpick) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) F.wsel[quarter * 16 + e] = wv[e];
-      }
-      __syncthreads();
-      if (wave == 0) {
-        const int gsel = F.gpick;
-        int pick = -1;
-        if (gsel >= 0) {
-          const int lo = k * kChunk + gsel * kGroup;
-          const int n = min(kGroup, a.V - lo);
-          double tot;
-          pick = wave_pick(lane < n ? (double)F.wsel[lane] : 0.0, n, F.u[2], tot);
-          if (pick >= 0) pick += lo;
-        }
-        if (lane == 0) F.xpick = pick;
-      }
-      __syncthreads();
-      x = F.xpick;
-    }
-  }
-  // F. outputs
-  const bool ok = !(F.status & (kStTimeout | kStNonfinite));
-  if (t <= a.G) {
-    int tok = -1;
-    if (ok) {
-      if (t < F.n_acc) tok = F.ytok[t];
-      else if (t == F.n_acc) tok = x;
-    }
-    a.out_tokens[(int64_t)b * G1 + t] = tok;
-  }
-  if (t == 0) {
-    a.out_num_accepted[b] = ok ? F.n_acc : 0;
-    a.out_status[b] = F.status;
-  }
+    for (int h = 0; h < kTouch; ++h) asm volatile("" ::"v"(tch[j][0][h]), "v"(tch[j][1][h]));
 }
 
 // ---------------------------------------------------------------- streaming kernel
@@ -1000,6 +1154,19 @@ __device__ __forceinline__ void team_gather(const FusedArgs& a, FusedLds& L, int
   }
 }
 
+// The logits of a paired position's draft token y in its target and draft rows, kept for the
+// finalize kernel's accept test (p(y) and q(y)): written by the one ticket whose slices hold y,
+// by a wave that would otherwise idle while wave 0 waits for the team.
+template <int DT>
+__device__ __forceinline__ void record_token_logits(const FusedArgs& a, int r, int drow, int base) {
+  const int y = sload_i32(a.tokens + drow);
+  if (y < base || y >= base + 2 * kChunk || y >= a.V) return;
+  if ((threadIdx.x & 63) == 0) {
+    a.ylog[2 * drow] = logit_at<DT>(row_ptr<DT>(a.tgt, a.tgt_ld, r), y);
+    a.ylog[2 * drow + 1] = logit_at<DT>(row_ptr<DT>(a.drf, a.drf_ld, drow), y);
+  }
+}
+
 __device__ __forceinline__ float residual_slice(const ResidualScale& R, const float (&ep)[kPerThread],
                                                 const float (&eq)[kPerThread]) {
   float sm;
@@ -1277,6 +1444,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_
   }
   if (!pair) return;
   if (wave == 0) team_gather(a, L, r, n_u);
+  else if (MODE == kFuSample && wave == 1) record_token_logits<DT>(a, r, drow, base);
   __syncthreads();
   const int st = L.tst;
   float m0 = 0.f, m1 = 0.f;

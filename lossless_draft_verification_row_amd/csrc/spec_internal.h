@@ -139,6 +139,7 @@ struct FusedArgs {
   uint64_t* part;       // [n_teams][2 rows][n_s] 16-byte tagged slice records
   uint64_t* smass;      // [n_teams][n_s][4 waves] tagged residual masses
   uint32_t* arrive;     // [n_teams][kMaxMembers] a member's flag: the call's tag once its records are out
+  float* ylog;          // [n_draft_rows][2]: each draft token's logit in its target and draft row
   int32_t* team_row;    // [n_teams]: the target row of the team in each dispatch place, for ragged
                         // batches (written by k_team_map); nullptr when every request has G drafts
   int poll_delay;       // wait before the first team poll, in 10 ns ticks
