@@ -93,16 +93,16 @@ __device__ __forceinline__ void block_scan2(int& a, int& b, SelLds& S, int& ta, 
 
 // Candidates of one row's slice: the values at or above the slice's k-th largest, the ones
 // strictly above first.  Header {stored, total, threshold digits, flags}.
-// `v(j)` gives this thread's j-th logit of the slice.
-// `bad` < 0: find whether the slice holds a NaN or +inf here; else that flag, already known.
-template <int DT, typename Get>
-__device__ void slice_candidates_g(const FilterArgs& a, SelLds& S, Get v, int slot, int s, int base, int bad = -1) {
+// `v(j)` gives this thread's j-th logit of the list (j < N), `idx(j)` its token index.
+// `bad` < 0: find whether the list holds a NaN or +inf here; else that flag, already known.
+template <int DT, int N, int U, typename Get, typename Idx>
+__device__ void slice_candidates_g(const FilterArgs& a, SelLds& S, Get v, Idx idx, int slot, int l, int bad = -1) {
   constexpr int NP = DT == kDtBF16 ? 2 : 4;
   const int t = threadIdx.x;
   if (bad < 0) {
     bad = 0;
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) bad |= __builtin_amdgcn_class(v(j), 0x203) ? 1 : 0;   // NaN, +inf
+#pragma unroll U
+    for (int j = 0; j < N; ++j) bad |= __builtin_amdgcn_class(v(j), 0x203) ? 1 : 0;   // NaN, +inf
     bad = block_or(bad, S.wtot[0]);
   }
   auto valid = [](float x) { return x > -INFINITY && x < INFINITY; };
@@ -110,15 +110,15 @@ __device__ void slice_candidates_g(const FilterArgs& a, SelLds& S, Get v, int sl
   int nv;
   const uint32_t th = block_select<NP>(a.k, S,
                                        [&](auto cb) {
-#pragma unroll
-                                         for (int j = 0; j < kPerThread; ++j) {
+#pragma unroll U
+                                         for (int j = 0; j < N; ++j) {
                                            const float x = v(j);
                                            cb(order_key(x), valid(x));
                                          }
                                        }, all, nv);
   int ng = 0, ne = 0;
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
+#pragma unroll U
+  for (int j = 0; j < N; ++j) {
     const float x = v(j);
     if (!valid(x)) continue;
     const uint32_t h = key_hi<NP>(order_key(x));
@@ -128,9 +128,9 @@ __device__ void slice_candidates_g(const FilterArgs& a, SelLds& S, Get v, int sl
   int og = ng, oe = ne, tg, te;
   block_scan2(og, oe, S, tg, te);
   const int cap = a.cap;
-  CandEntry* out = a.cand + ((int64_t)slot * a.n_s + s) * cap;
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
+  CandEntry* out = a.cand + ((int64_t)slot * a.n_l + l) * cap;
+#pragma unroll U
+  for (int j = 0; j < N; ++j) {
     const float x = v(j);
     if (!valid(x)) continue;
     const uint32_t h = key_hi<NP>(order_key(x));
@@ -140,7 +140,7 @@ __device__ void slice_candidates_g(const FilterArgs& a, SelLds& S, Get v, int sl
     if (pos >= 0 && pos < cap) {
       CandEntry c;
       c.v = x;
-      c.x = slice_index<DT>(base, t, j);
+      c.x = idx(j);
       out[pos] = c;
     }
   }
@@ -150,7 +150,7 @@ __device__ void slice_candidates_g(const FilterArgs& a, SelLds& S, Get v, int sl
     hd.stored = min(tg + te, cap);
     hd.th = all ? 0u : th;
     hd.flags = (bad ? kFlagBad : 0) | (all ? 8 : 0);
-    a.chead[(int64_t)slot * a.n_s + s] = hd;
+    a.chead[(int64_t)slot * a.n_l + l] = hd;
   }
   __syncthreads();
 }
@@ -158,7 +158,9 @@ __device__ void slice_candidates_g(const FilterArgs& a, SelLds& S, Get v, int sl
 template <int DT>
 __device__ void slice_candidates(const FilterArgs& a, SelLds& S, const float (&v)[kPerThread], int slot, int s,
                                  int base) {
-  slice_candidates_g<DT>(a, S, [&](int j) { return v[j]; }, slot, s, base);
+  const int t = threadIdx.x;
+  slice_candidates_g<DT, kPerThread, kPerThread>(a, S, [&](int j) { return v[j]; },
+                                     [&](int j) { return slice_index<DT>(base, t, j); }, slot, s);
 }
 
 // Mask of the wave's lanes with x >= y, straight from the compare into a scalar register pair
@@ -180,14 +182,18 @@ __device__ __forceinline__ int wave_max_i(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
-struct Sel2Lds {
-  uint32_t hist[2][256];   // per row: count of keys max - b, b = 0..255
+constexpr int kStageW = 128;   // candidates one wave may stage per row of a list
+
+struct ListLds {
+  uint32_t hist[2][256];   // per row: count of per-thread maxima at order key max - b, b = 0..255
   int wmax[2][kWaves], wbad[2][kWaves];
-  int wtot[4][kWaves];
+  int wcnt[2][kWaves];
   int tau[2], fb[2];
-  CandEntry stage[2 * (kFilterMaxK + 48)];   // candidates of both rows before the copy out
-  SelLds gen;              // the general select, for a slice whose top k spread wider
-  uint32_t raw[kPerThread / 2][kThreads];   // its raw bf16 pairs, thread t's in column t
+  SelLds gen;              // the general select, for a list whose top k spread wider
+  union {
+    CandEntry stage[2][kWaves][kStageW];      // each wave's candidates of each row, before the copy out
+    uint32_t raw[kPerThread][kThreads];       // the exact select's raw bf16 pairs, thread t's in column t
+  };
 };
 
 // Order key of a bf16-exact value (16 significant bits) and back.
@@ -197,29 +203,62 @@ __device__ __forceinline__ int key16(float v) {
   return (int)((b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u));
 }
 
-// Candidates of the target slice and (paired) the draft slice of a bf16 ticket, both rows in
-// lockstep.  The k-th largest of the 256 per-thread maxima is at most the slice's k-th largest
-// logit, so every finite logit at or above it is a valid candidate set (it holds the slice's
-// top k with all ties); for a realistic row it is barely larger than k.  That threshold comes
-// from one LDS histogram of the maxima within 256 order keys of the slice maximum (one atomic
-// per thread).  A row whose maxima spread wider, or whose candidates would not fit in `cap`,
-// takes the exact radix select instead, on the slice read again from memory (so that the
-// register copies of both rows end with the staging and the common path keeps a small register
-// footprint).  Candidates are staged in LDS and copied out whole.
+// Logit j (< 2 kPerThread) of a thread's bf16 list of two 4096-logit chunks held as raw words,
+// and its token index.
+__device__ __forceinline__ float list_elem(const RawSlice<kDtBF16> (&r)[2], int j) {
+  const uint32_t w = r[j / kPerThread].w[(j % kPerThread) >> 1];
+  return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+// The same logit unpacked by an opaque move, so that the compiler does not keep the unpacked
+// values of an earlier pass alive (the raw words take half the registers).
+__device__ __forceinline__ float list_elem_fresh(const RawSlice<kDtBF16> (&r)[2], int j) {
+  const uint32_t w = r[j / kPerThread].w[(j % kPerThread) >> 1];
+  uint32_t x;
+  if (j & 1) asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(x) : "v"(w));
+  else asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(x) : "v"(w));
+  return __uint_as_float(x);
+}
+__device__ __forceinline__ int list_index(int base, int t, int j) {
+  return slice_index<kDtBF16>(base + (j / kPerThread) * kChunk, t, j % kPerThread);
+}
+// Raw bf16 halves at indices >= V become -inf (0xFF80): a bounds-checked vector load returns
+// zeros past the row.
+__device__ __forceinline__ void mask_tail_words(int V, int base, RawSlice<kDtBF16>& r) {
+  const int t = threadIdx.x;
+  if (base + kChunk <= V) return;
+#pragma unroll
+  for (int k = 0; k < kPerThread / 2; ++k) {
+    const int i0 = slice_index<kDtBF16>(base, t, 2 * k);
+    if (i0 >= V) r.w[k] = (r.w[k] & 0xFFFF0000u) | 0xFF80u;
+    if (i0 + 1 >= V) r.w[k] = (r.w[k] & 0x0000FFFFu) | 0xFF800000u;
+  }
+}
+
+// Candidates of one list of a bf16 target row and (paired) the same list of its draft row: two
+// 4096-logit chunks, 32 logits per thread per row, both rows in lockstep.  The k-th largest of
+// the 256 per-thread maxima is at most the list's k-th largest logit, so every finite logit at
+// or above it is a valid candidate set (it holds the list's top k with all ties); for a
+// realistic row it is barely larger than k.  That threshold comes from one LDS histogram of the
+// maxima within 256 order keys of the list maximum (one atomic per thread).  Each wave then
+// stages its candidates in its own LDS region in one compare pass (wave counts by popcount,
+// slots by mbcnt, elements no lane keeps skipped), and the regions are copied out whole.  A row
+// whose maxima spread wider, or whose candidates fill a region or the list's `cap`, takes the
+// exact radix select instead, on the list read again from memory.
 template <bool VEC>
-__device__ void slice_candidates_bf16(const FilterArgs& a, Sel2Lds& S, const float (&vp)[kPerThread],
-                                      const float (&vq)[kPerThread], bool paired, int slot_p, int slot_q, int s,
-                                      int base, const void* row_p, const void* row_q) {
+__device__ void list_candidates_bf16(const FilterArgs& a, ListLds& S, const RawSlice<kDtBF16> (&rp)[2],
+                                     const RawSlice<kDtBF16> (&rq)[2], bool paired, int slot_p, int slot_q, int l,
+                                     int base, const void* row_p, const void* row_q) {
+  constexpr int NE = 2 * kPerThread;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int nrow = paired ? 2 : 1;
-  // per-thread maxima with NaN propagated (three-input maximum): a NaN or +inf anywhere makes
-  // the maximum NaN or +inf, which flags the row (its candidates are then never read)
+  // per-thread maxima with NaN propagated: a NaN or +inf anywhere makes the maximum NaN or
+  // +inf, which flags the row (its candidates are then never read)
   float fm[2] = {-INFINITY, -INFINITY};
   int bad[2];
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    fm[0] = __builtin_elementwise_maximum(fm[0], vp[j]);
-    if (paired) fm[1] = __builtin_elementwise_maximum(fm[1], vq[j]);
+  for (int j = 0; j < NE; ++j) {
+    fm[0] = __builtin_elementwise_maximum(fm[0], list_elem(rp, j));
+    if (paired) fm[1] = __builtin_elementwise_maximum(fm[1], list_elem(rq, j));
   }
   int tm[2];
 #pragma unroll
@@ -277,99 +316,101 @@ __device__ void slice_candidates_bf16(const FilterArgs& a, Sel2Lds& S, const flo
     tf[r] = fb[r] ? INFINITY : key16_value(S.tau[r]);
   }
   // candidates: the logits at or above the threshold value (NaN compares false; a +inf only
-  // occurs in a flagged row).  Each wave counts them per element with one ballot, so the
-  // counts are scalar; a candidate's slot is the wave's base, the element's running total and
-  // its rank among the wave's lanes (mbcnt).
-  int wc[2] = {0, 0};
+  // occurs in a flagged row), staged by each wave in its own region in one pass
+  auto stage_row = [&](const RawSlice<kDtBF16> (&rw)[2], int r) {
+    CandEntry* st = S.stage[r][wave];
+    int run = 0;   // uniform over the wave
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    wc[0] += __popcll(__builtin_amdgcn_ballot_w64(vp[j] >= tf[0]));
-    wc[1] += __popcll(__builtin_amdgcn_ballot_w64(vq[j] >= tf[1]));
-  }
-  if (lane == 0) { S.wtot[0][wave] = wc[0]; S.wtot[1][wave] = wc[1]; }
-  __syncthreads();
-  const int cap = a.cap;
-  int off[2], tot[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    int o = 0, tt = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      if (w < wave) o += S.wtot[r][w];
-      tt += S.wtot[r][w];
-    }
-    off[r] = o;
-    tot[r] = tt;
-    if (tot[r] > cap) fb[r] = 1;
-  }
-  // stage in LDS (row r at stage[r * cap ..]), then one coalesced copy per row
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    if (fb[r]) continue;
-    const float (&v)[kPerThread] = r == 0 ? vp : vq;
-    int run = __builtin_amdgcn_readfirstlane(off[r]);   // uniform over the wave
-    CandEntry* st = S.stage + r * cap;
-    const int x0 = slice_index<kDtBF16>(base, t, 0);
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const unsigned long long mk = wave_mask_ge(v[j], tf[r]);
+    for (int j = 0; j < NE; ++j) {
+      const float v = list_elem_fresh(rw, j);
+      const unsigned long long mk = wave_mask_ge(v, tf[r]);
       if (mk) {
         if (__builtin_amdgcn_inverse_ballot_w64(mk)) {
           const int o = run + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(mk >> 32),
                                                             __builtin_amdgcn_mbcnt_lo((unsigned)mk, 0u));
-          CandEntry c;
-          c.v = v[j];
-          c.x = x0 + (slice_index<kDtBF16>(base, t, j) - slice_index<kDtBF16>(base, t, 0));
-          st[o] = c;
+          if (o < kStageW) {
+            CandEntry c;
+            c.v = v;
+            c.x = list_index(base, t, j);
+            st[o] = c;
+          }
         }
         run += __popcll(mk);
       }
     }
-  }
+    return run;
+  };
+  int wc0 = 0, wc1 = 0;
+  if (!fb[0]) wc0 = stage_row(rp, 0);
+  if (!fb[1]) wc1 = stage_row(rq, 1);
+  if (lane == 0) { S.wcnt[0][wave] = wc0; S.wcnt[1][wave] = wc1; }
   __syncthreads();
+  const int cap = a.cap;
+  int tot[2], o1[2], o2[2], o3[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    if (r >= nrow) break;
+    const int c0 = S.wcnt[r][0], c1 = S.wcnt[r][1], c2 = S.wcnt[r][2], c3 = S.wcnt[r][3];
+    o1[r] = c0;
+    o2[r] = c0 + c1;
+    o3[r] = c0 + c1 + c2;
+    tot[r] = o3[r] + c3;
+    if (tot[r] > cap || max(max(c0, c1), max(c2, c3)) > kStageW) fb[r] = 1;
+  }
+  // the staged rows go out whole
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (r >= nrow || fb[r]) continue;
     const int slot = r == 0 ? slot_p : slot_q;
-    if (fb[r]) {
-      // the exact select: the slice's own k-th largest, ties after the larger values
-      // (each thread reads back only its own words, every pass, so no values stay in registers)
-      RawSlice<kDtBF16> raw;
-      if (VEC) load_raw_buf<kDtBF16>(row_rsrc(r == 0 ? row_p : row_q, a.V * 2), base, raw);
-      else load_raw<kDtBF16, false>(r == 0 ? row_p : row_q, a.V, base, raw);
-      if (base + kChunk > a.V) {   // the tail slice: indices >= V become -inf (bf16 0xFF80)
-#pragma unroll
-        for (int k = 0; k < kPerThread / 2; ++k) {
-          const int i0 = slice_index<kDtBF16>(base, t, 2 * k);
-          if (i0 >= a.V) raw.w[k] = (raw.w[k] & 0xFFFF0000u) | 0xFF80u;
-          if (i0 + 1 >= a.V) raw.w[k] = (raw.w[k] & 0x0000FFFFu) | 0xFF800000u;
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < kPerThread / 2; ++k) S.raw[k][t] = raw.w[k];
-      slice_candidates_g<kDtBF16>(
-          a, S.gen, [&](int j) { return (j & 1) ? bf16_hi(S.raw[j >> 1][t]) : bf16_lo(S.raw[j >> 1][t]); }, slot, s,
-          base, bad[r]);
-      continue;
+    CandEntry* out = a.cand + ((int64_t)slot * a.n_l + l) * cap;
+    for (int e = t; e < tot[r]; e += kThreads) {
+      const int w = (e >= o1[r]) + (e >= o2[r]) + (e >= o3[r]);
+      const int wo = w == 0 ? 0 : (w == 1 ? o1[r] : (w == 2 ? o2[r] : o3[r]));
+      out[e] = S.stage[r][w][e - wo];
     }
-    CandEntry* out = a.cand + ((int64_t)slot * a.n_s + s) * cap;
-    for (int e = t; e < tot[r]; e += kThreads) out[e] = S.stage[r * cap + e];
     if (t == 0) {
       CandHead hd;
       hd.total = tot[r];
       hd.stored = tot[r];
       hd.th = (uint32_t)S.tau[r];
       hd.flags = bad[r] ? kFlagBad : 0;
-      a.chead[(int64_t)slot * a.n_s + s] = hd;
+      a.chead[(int64_t)slot * a.n_l + l] = hd;
     }
+  }
+  if (!fb[0] && (nrow < 2 || !fb[1])) return;
+  // the exact select for the other rows: the list's own k-th largest, ties after the larger
+  // values, on the list read again (its raw words go to LDS over the staging area, once every
+  // copy out has read it; each thread reads back only its own words)
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (r >= nrow || !fb[r]) continue;
+    const int slot = r == 0 ? slot_p : slot_q;
+    RawSlice<kDtBF16> raw[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (VEC) load_raw_buf<kDtBF16>(row_rsrc(r == 0 ? row_p : row_q, a.V * 2), base + h * kChunk, raw[h]);
+      else load_raw<kDtBF16, false>(r == 0 ? row_p : row_q, a.V, base + h * kChunk, raw[h]);
+      mask_tail_words(a.V, base + h * kChunk, raw[h]);
+    }
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) S.raw[k][t] = raw[k / (kPerThread / 2)].w[k % (kPerThread / 2)];
+    slice_candidates_g<kDtBF16, NE, 2>(
+        a, S.gen,
+        [&](int j) {
+          const uint32_t w = *(volatile uint32_t*)&S.raw[j >> 1][t];   // read at each use
+          return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+        },
+        [&](int j) { return list_index(base, t, j); }, slot, l, bad[r]);
   }
 }
 
 template <int DT, bool VEC, bool PAIRED>
 __global__ __launch_bounds__(kThreads) void k_filt_slices(FilterArgs a) {
-  __shared__ Sel2Lds S;
-  const int n_s = a.n_s;
-  const int r = blockIdx.x / n_s, s = blockIdx.x - (blockIdx.x / n_s) * n_s;
+  __shared__ ListLds S;
+  // one workgroup per candidate list: two 4096-logit chunks (bf16) or one (fp32)
+  constexpr int kSpan = DT == kDtBF16 ? 2 : 1;
+  const int n_l = a.n_l;
+  const int r = blockIdx.x / n_l, l = blockIdx.x - (blockIdx.x / n_l) * n_l;
   // the dense recomputation's list starts empty and the offsets valid (the finalize checks them)
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     if (a.ovf_n) *a.ovf_n = 0;
@@ -377,29 +418,37 @@ __global__ __launch_bounds__(kThreads) void k_filt_slices(FilterArgs a) {
   }
   if (r >= a.n_teams) return;
   constexpr int kEsz = DT == kDtBF16 ? 2 : 4;
-  const int base = s * kChunk;
-  RawSlice<DT> rp, rq;
-  if (VEC) load_raw_buf<DT>(row_rsrc(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V * kEsz), base, rp);
-  else load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, base, rp);
+  const int base = l * kSpan * kChunk;
+  RawSlice<DT> rp[kSpan], rq[kSpan];
+  {
+    const void* row = row_ptr<DT>(a.tgt, a.tgt_ld, r);
+#pragma unroll
+    for (int h = 0; h < kSpan; ++h) {
+      if (VEC) load_raw_buf<DT>(row_rsrc(row, a.V * kEsz), base + h * kChunk, rp[h]);
+      else load_raw<DT, false>(row, a.V, base + h * kChunk, rp[h]);
+    }
+  }
+  auto load_q = [&](int drow) {
+    const void* row = drow >= 0 ? row_ptr<DT>(a.drf, a.drf_ld, drow) : a.tgt;
+#pragma unroll
+    for (int h = 0; h < kSpan; ++h) {
+      if (VEC) load_raw_buf<DT>(row_rsrc(row, drow >= 0 ? a.V * kEsz : 0), base + h * kChunk, rq[h]);
+      else if (drow >= 0) load_raw<DT, false>(row, a.V, base + h * kChunk, rq[h]);
+    }
+  };
   // the draft row of target row r, if r is not the last row of its request (scalar-cache
   // binary search over the offsets; the draft loads go out right after)
   int drow = -1;
   if (PAIRED && a.direct) {
     if (r < a.n_draft_rows) drow = r;
-    if (VEC)
-      load_raw_buf<DT>(row_rsrc(drow >= 0 ? row_ptr<DT>(a.drf, a.drf_ld, drow) : a.tgt, drow >= 0 ? a.V * kEsz : 0),
-                       base, rq);
-    else if (drow >= 0)
-      load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base, rq);
+    load_q(drow);
   } else if (PAIRED) {
     // the request guessed as b = r / (G + 1) (exact when every request has G draft tokens):
     // its draft row is loaded at once, one scalar load checks the guess, and a wrong guess
     // falls back to a binary search over the offsets and loads again
     const int lo0 = min(r / (a.G + 1), a.B - 1);
     const bool guess_pair = r - lo0 < a.n_draft_rows && r % (a.G + 1) < a.G;
-    if (VEC)
-      load_raw_buf<DT>(row_rsrc(guess_pair ? row_ptr<DT>(a.drf, a.drf_ld, r - lo0) : a.tgt, guess_pair ? a.V * kEsz : 0),
-                       base, rq);
+    if (VEC) load_q(guess_pair ? r - lo0 : -1);
     int lo = lo0, c0, c1;
     sload2_i32(a.cu + lo, c0, c1);
     if (!(c0 + lo <= r && (lo == a.B - 1 || c1 + lo + 1 > r))) {
@@ -415,30 +464,38 @@ __global__ __launch_bounds__(kThreads) void k_filt_slices(FilterArgs a) {
     const int i = r - c0 - lo;
     if (i >= 0 && i < c1 - c0 && r - lo >= 0 && r - lo < a.n_draft_rows) drow = r - lo;
     if (VEC) {
-      if ((drow >= 0) != guess_pair || (drow >= 0 && lo != lo0))
-        load_raw_buf<DT>(row_rsrc(drow >= 0 ? row_ptr<DT>(a.drf, a.drf_ld, drow) : a.tgt, drow >= 0 ? a.V * kEsz : 0),
-                         base, rq);
+      if ((drow >= 0) != guess_pair || (drow >= 0 && lo != lo0)) load_q(drow);
     } else if (drow >= 0) {
-      load_raw<DT, false>(row_ptr<DT>(a.drf, a.drf_ld, drow), a.V, base, rq);
+      load_q(drow);
     }
   }
-  float vp[kPerThread], vq[kPerThread];
-  unpack_raw<DT>(rp, vp);
-  if (VEC && (a.V % kChunk) != 0 && s == n_s - 1) mask_tail<DT>(a.V, base, vp);
   const bool paired = PAIRED && drow >= 0;
-  if (paired) {
-    unpack_raw<DT>(rq, vq);
-    if (VEC && (a.V % kChunk) != 0 && s == n_s - 1) mask_tail<DT>(a.V, base, vq);
-  } else {
+  if constexpr (DT == kDtBF16) {
+    if (VEC) {
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) vq[j] = -INFINITY;
-  }
-  if (DT == kDtBF16) {
-    slice_candidates_bf16<VEC>(a, S, vp, vq, paired, r, a.n_teams + drow, s, base, row_ptr<DT>(a.tgt, a.tgt_ld, r),
-                          paired ? row_ptr<DT>(a.drf, a.drf_ld, drow) : a.tgt);
+      for (int h = 0; h < kSpan; ++h) {
+        mask_tail_words(a.V, base + h * kChunk, rp[h]);
+        if (paired) mask_tail_words(a.V, base + h * kChunk, rq[h]);
+      }
+    }
+    if (!paired) {
+#pragma unroll
+      for (int h = 0; h < kSpan; ++h)
+#pragma unroll
+        for (int k = 0; k < kPerThread / 2; ++k) rq[h].w[k] = 0xFF80FF80u;
+    }
+    list_candidates_bf16<VEC>(a, S, rp, rq, paired, r, a.n_teams + drow, l, base, row_ptr<DT>(a.tgt, a.tgt_ld, r),
+                              paired ? row_ptr<DT>(a.drf, a.drf_ld, drow) : a.tgt);
   } else {
-    slice_candidates<DT>(a, S.gen, vp, r, s, base);
-    if (paired) slice_candidates<DT>(a, S.gen, vq, a.n_teams + drow, s, base);
+    float vp[kPerThread], vq[kPerThread];
+    unpack_raw<DT>(rp[0], vp);
+    if (VEC && (a.V % kChunk) != 0 && l == n_l - 1) mask_tail<DT>(a.V, base, vp);
+    slice_candidates<DT>(a, S.gen, vp, r, l, base);
+    if (paired) {
+      unpack_raw<DT>(rq[0], vq);
+      if (VEC && (a.V % kChunk) != 0 && l == n_l - 1) mask_tail<DT>(a.V, base, vq);
+      slice_candidates<DT>(a, S.gen, vq, a.n_teams + drow, l, base);
+    }
   }
 }
 
@@ -479,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void k_filt_rows(FilterArgs a) {
   const int t = threadIdx.x, lane = t & 63;
   const int slot = blockIdx.x;
   if (slot >= a.n_slots) return;
-  const int n_s = a.n_s, cap = a.cap;
+  const int n_s = a.n_l, cap = a.cap;   // candidate lists of the row
   const CandHead* hd = a.chead + (int64_t)slot * n_s;
   const CandEntry* cd = a.cand + (int64_t)slot * n_s * cap;
   // slice headers, one per lane of wave 0; prefix of the stored counts
@@ -1042,8 +1099,17 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
 
 // ---------------------------------------------------------------- launch
 
-hipError_t launch_filter(const FilterArgs& a, int dt, int vec, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  const long long g1 = (long long)a.n_teams * a.n_s;
+// The candidate lists of a row: one per two 4096-logit chunks for bf16 rows, one per chunk for
+// fp32 rows (the workspace holds one per chunk).
+FilterArgs with_lists(const FilterArgs& a0, int dt) {
+  FilterArgs a = a0;
+  a.n_l = dt == kDtBF16 ? (a.n_s + 1) / 2 : a.n_s;
+  return a;
+}
+
+hipError_t launch_filter(const FilterArgs& a0, int dt, int vec, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  const FilterArgs a = with_lists(a0, dt);
+  const long long g1 = (long long)a.n_teams * a.n_l;
   if (g1 < 1 || g1 > 0x7fffffffll || a.B < 1) return hipErrorInvalidConfiguration;
   // optional events bracket the streaming kernel alone (benchmark timing)
   const bool paired = a.mode == kFuSample;
@@ -1179,8 +1245,9 @@ __global__ __launch_bounds__(kThreads) void k_filt_residual(FilterArgs a) {
   }
 }
 
-hipError_t launch_filter_rows(const FilterArgs& a, int dt, int vec, int what, hipStream_t st) {
-  const long long g1 = (long long)a.n_teams * a.n_s;
+hipError_t launch_filter_rows(const FilterArgs& a0, int dt, int vec, int what, hipStream_t st) {
+  const FilterArgs a = with_lists(a0, dt);
+  const long long g1 = (long long)a.n_teams * a.n_l;
   if (g1 < 1 || g1 > 0x7fffffffll || a.n_slots < 1) return hipErrorInvalidConfiguration;
   const bool paired = what == 1 && a.drf != nullptr;
 #define SPEC_SLICES(D, P)                                                                           \

@@ -218,11 +218,12 @@ struct FilterArgs {
   const int32_t* cu;
   const int32_t* tokens;
   int B, G, V, n_s, n_draft_rows, n_teams, n_slots, mode, k, cap;
+  int n_l;                // candidate lists per row (set by the launchers; n_l <= n_s)
   float top_p;
   double c, inv_t;        // c = log2(e) / T
   uint64_t seed, step;
-  CandEntry* cand;        // [n_slots][n_s][cap]
-  CandHead* chead;        // [n_slots][n_s]
+  CandEntry* cand;        // [n_slots][n_l][cap] (sized for n_s lists)
+  CandHead* chead;        // [n_slots][n_l] (sized for n_s)
   KeptEntry* kept;        // [n_slots][kKeepMax]
   RowStat2* rstat;        // [n_slots]
   int32_t* out_tokens;
