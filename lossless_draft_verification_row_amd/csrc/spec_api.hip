@@ -407,7 +407,6 @@ int spec_verify_batch_ex(int B, int V, int gamma_max, spec_dtype dt, const void*
     fa.smass = d.smass;
     fa.amass = d.amass;
     fa.kmass = d.kmass;
-    if (launch_fallback_rows(fb, dtc, vec, st) != hipSuccess) return SPEC_ERR_LAUNCH;
     if (launch_fallback_requests(fb, fa, want_kl ? 1 : 0, dtc, vec, st) != hipSuccess) return SPEC_ERR_LAUNCH;
     return SPEC_OK;
   }
@@ -666,7 +665,6 @@ int spec_residual_sample_ex(int R, int V, spec_dtype dt, const void* p_logits, i
     ra.rs = d.rs;
     ra.part = d.part;
     ra.smass = d.smass;
-    if (launch_fallback_rows(fb, dtc, vec, st) != hipSuccess) return SPEC_ERR_LAUNCH;
     if (launch_fallback_residual(fb, ra, d.amass, dtc, vec, st) != hipSuccess) return SPEC_ERR_LAUNCH;
     return SPEC_OK;
   }

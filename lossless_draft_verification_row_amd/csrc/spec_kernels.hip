@@ -1286,13 +1286,32 @@ __global__ __launch_bounds__(kThreads) void k_fb_rows(FallbackRows f) {
   }
 }
 
-// Listed requests after k_fb_rows: the pair sums of every position, then the finalize.
+// The dense recomputation of every row of listed unit u (a request's 2 (G + 1) rows, or a plain
+// row pair) by one workgroup: threshold, per-slice partials, row statistics.
+template <int DT, bool VEC>
+__device__ void fb_unit_rows(const FallbackRows& f, int u) {
+  for (int i = 0; i < f.unit_lr; ++i) {
+    const int lr = u * f.unit_lr + i;
+    if (resolve_row<DT>(f.map, lr) == nullptr) continue;
+    threshold_row<DT, VEC>(f.map, f.V, f.k, f.top_p, f.cthr, f.thr, lr);
+    __syncthreads();
+    for (int sl = 0; sl < f.n_slices; ++sl)
+      pass1_slice<DT, VEC, kModeSoftmax>(f.map, f.V, f.n_slices, f.c, f.want_argmax, f.part, lr, sl);
+    __syncthreads();
+    if (threadIdx.x < 64) combine_row<DT>(f.map, f.n_lr, f.n_slices, f.c, 0, f.part, f.rs, f.rso, lr);
+    __syncthreads();
+  }
+}
+
+// Listed requests, one workgroup each: their rows, the pair sums of every position, then the
+// finalize (a batch with nothing listed costs one launch).
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_fb_requests(FallbackRows f, FinalizeArgs a, int want_kl) {
   const int n = *f.list_n;
   const int G1 = f.map.G + 1;
   for (int w = blockIdx.x; w < n; w += gridDim.x) {
     const int b = f.list[w];
+    fb_unit_rows<DT, VEC>(f, b);
     for (int i = 0; i < G1; ++i)
       for (int sl = 0; sl < f.n_slices; ++sl)
         pair_slice<DT, VEC>(f.map, f.V, f.n_slices, f.c, f.rs, (double*)a.smass, (double*)a.amass, want_kl,
@@ -1303,12 +1322,14 @@ __global__ __launch_bounds__(kThreads) void k_fb_requests(FallbackRows f, Finali
   }
 }
 
-// Listed plain rows after k_fb_rows: the pair sums (with q rows), then the residual draw.
+// Listed plain row pairs, one workgroup each: their rows, the pair sums (with q rows), then the
+// residual draw.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_fb_residual(FallbackRows f, ResidualArgs a, double* amass) {
   const int n = *f.list_n;
   for (int w = blockIdx.x; w < n; w += gridDim.x) {
     const int r = f.list[w];
+    fb_unit_rows<DT, VEC>(f, r);
     for (int sl = 0; sl < f.n_slices; ++sl)
       pair_slice<DT, VEC>(f.map, f.V, f.n_slices, f.c, f.rs, (double*)a.smass, amass, 0, nullptr, r, sl);
     __syncthreads();
@@ -1318,7 +1339,7 @@ __global__ __launch_bounds__(kThreads) void k_fb_residual(FallbackRows f, Residu
 }
 
 // Grids: enough workgroups to spread a long list, few enough that an empty one costs little.
-constexpr int kFbGrid = 256;
+constexpr int kFbGrid = 128;
 
 hipError_t launch_fallback_rows(const FallbackRows& f, int dt, int vec, hipStream_t st) {
   const dim3 g(kFbGrid), blk(kThreads);
