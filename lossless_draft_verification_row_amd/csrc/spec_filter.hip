@@ -501,8 +501,8 @@ __global__ __launch_bounds__(kThreads) void k_filt_slices(FilterArgs a) {
 
 // ---------------------------------------------------------------- k_filt_rows
 
-constexpr int kRowStage = 2304;   // candidates of a row staged in LDS (more: read in place); 30 KB of
-                                  // LDS in all, so 5 rows share a CU
+constexpr int kRowStage = 1280;   // candidates of a row staged in LDS (more: read in place); 22 KB of
+                                  // LDS in all, so 6 rows (the register limit) share a CU
 
 struct RowLds {
   SelLds sel;
@@ -530,7 +530,7 @@ __device__ __forceinline__ double block_sum_dd(double v, double* red) {
 
 // One row: global top-k over the slices' candidates, top-p, the kept set with probabilities.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_filt_rows(FilterArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) void k_filt_rows(FilterArgs a) {
   constexpr int NP = DT == kDtBF16 ? 2 : 4;
   __shared__ RowLds L;
   const int t = threadIdx.x, lane = t & 63;
@@ -565,14 +565,14 @@ __global__ __launch_bounds__(kThreads) void k_filt_rows(FilterArgs a) {
   // bf16: the largest order key among the candidates, formed while they are copied in
   int km = -1;
   if (staged) {
-    // copy the candidates in: wave w takes slices w, w + 4, ..., lane l entries l and l + 64
-    // of each; eight slices per wave (sixteen loads per thread) in flight at a time
+    // copy the candidates in: wave w takes lists w, w + 4, ..., lane l entries l and l + 64
+    // of each; four lists per wave (eight loads per thread) in flight at a time
     const int wv = t >> 6;
     for (int i0 = 0; i0 < cap; i0 += 128) {
-      for (int s0 = wv; s0 < n_s; s0 += kWaves * 8) {
-        CandEntry tmp[8][2];
+      for (int s0 = wv; s0 < n_s; s0 += kWaves * 4) {
+        CandEntry tmp[4][2];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 4; ++u) {
           const int sl = s0 + u * kWaves;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void k_filt_rows(FilterArgs a) {
           }
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 4; ++u) {
           const int sl = s0 + u * kWaves;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
