@@ -508,7 +508,7 @@ struct RowLds {
   SelLds sel;
   int cnt[kMaxSlicesFused + 1];
   int off[kMaxSlicesFused + 1];
-  CandEntry cand[kRowStage];
+  alignas(16) CandEntry cand[kRowStage];   // also the partial sums of the kept-set steps
   float kv[kKeepMax];
   int kx[kKeepMax];
   double ke[kKeepMax];
@@ -664,66 +664,86 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) v
     }
   }
   __syncthreads();
-  // One wave finishes the row: the kept set (at most kKeepMax entries) is in LDS, and the steps
-  // below need only wave-wide reductions, so no barrier holds the other three waves.
-  if (t >= 64) return;
+  // The kept set (at most kKeepMax entries) is in LDS.  Wave 0 takes the maximum and the
+  // e-values; the quadratic top-p and rank sums are spread over the four waves (wave w takes
+  // every fourth entry y), their partials meeting in the staging area, free again; wave 0 then
+  // forms Z_S, p, entropy and writes the kept set in index order.
+  const int wave = t >> 6;
   RowStat2 st;
   st.n = 0; st.flags = L.flags; st.m = -INFINITY; st.argmax = -1; st.kept_finite = 0; st.pad = 0;
   st.log_z = 0.0; st.entropy = 0.0; st.max_prob = 0.0; st.z = 0.0;
   if (nk == 0 && !(st.flags & kFlagBad)) st.flags |= kFlagEmpty;
   if (st.flags) {
-    if (lane == 0) a.rstat[slot] = st;
+    if (t == 0) a.rstat[slot] = st;
     return;
   }
-  // maximum (lowest index among equal maxima)
   float m = -INFINITY;
-  for (int j = lane; j < nk; j += 64) m = fmaxf(m, L.kv[j]);
-  m = wave_max_dpp(m);
   int amx = INT_MAX;
-  for (int j = lane; j < nk; j += 64) if (L.kv[j] == m) amx = min(amx, L.kx[j]);
-  amx = wave_min_i(amx);
-  // e = exp((l - m) / T) in fp64; Z_K
-  const double cd2 = (double)a.c;   // log2(e) / T
-  double zk = 0.0;
-  for (int j = lane; j < nk; j += 64) {
-    const double e = exp2_split(((double)L.kv[j] - (double)m) * cd2);
-    L.ke[j] = e;
-    zk += e;
-  }
-  zk = wave_sum_dpp_d(zk);
-  __builtin_amdgcn_wave_barrier();
-  // top-p: keep x iff the mass of values strictly above l_x is below top_p (the value group
-  // that first reaches top_p is kept whole; reading R1).  Up to 64 entries, one per lane, the
-  // others' values come by readlane; more, from LDS.
-  const bool small = nk <= 64;
-  if (small) {
-    const float lx = lane < nk ? L.kv[lane] : -INFINITY;
-    const double ex = lane < nk ? L.ke[lane] : 0.0;
-    int keep = 1;
-    if (a.top_p < 1.f) {
-      double above = 0.0;
-      for (int y = 0; y < nk; ++y) {
-        const float ly = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lx), y));
-        const double ey = readlane_d(ex, y);
-        above += ly > lx ? ey : 0.0;
-      }
-      keep = (above / zk < (double)a.top_p) ? 1 : 0;
-    }
-    if (lane < nk) L.keep[lane] = keep;
-  } else {
+  if (wave == 0) {
+    // maximum (lowest index among equal maxima)
+    for (int j = lane; j < nk; j += 64) m = fmaxf(m, L.kv[j]);
+    m = wave_max_dpp(m);
+    for (int j = lane; j < nk; j += 64) if (L.kv[j] == m) amx = min(amx, L.kx[j]);
+    amx = wave_min_i(amx);
+    // e = exp((l - m) / T) in fp64; Z_K
+    const double cd2 = (double)a.c;   // log2(e) / T
+    double zk = 0.0;
     for (int j = lane; j < nk; j += 64) {
-      int keep = 1;
-      if (a.top_p < 1.f) {
+      const double e = exp2_split(((double)L.kv[j] - (double)m) * cd2);
+      L.ke[j] = e;
+      zk += e;
+    }
+    zk = wave_sum_dpp_d(zk);
+    if (lane == 0) L.red[0] = zk;
+  }
+  __syncthreads();
+  const double zk = L.red[0];
+  constexpr int kPartJ = kRowStage * (int)sizeof(CandEntry) / (kWaves * (int)sizeof(double));
+  double* part = (double*)L.cand;
+  int* ipart = (int*)L.cand;
+  // top-p: keep x iff the mass of values strictly above l_x is below top_p (the value group
+  // that first reaches top_p is kept whole; reading R1); keep[j] = 1 for a kept entry
+  for (int j0 = 0; j0 < nk; j0 += kPartJ) {
+    const int j1 = min(nk, j0 + kPartJ);
+    if (a.top_p < 1.f) {
+      for (int j = j0 + lane; j < j1; j += 64) {
         const float lx = L.kv[j];
-        double above = 0.0;
-        for (int y = 0; y < nk; ++y) above += (L.kv[y] > lx) ? L.ke[y] : 0.0;
-        keep = (above / zk < (double)a.top_p) ? 1 : 0;
+        double ab = 0.0;
+        for (int y = wave; y < nk; y += kWaves) ab += (L.kv[y] > lx) ? L.ke[y] : 0.0;
+        part[wave * kPartJ + (j - j0)] = ab;
       }
-      L.keep[j] = keep;
+      __syncthreads();
+      for (int j = j0 + t; j < j1; j += kThreads) {
+        const int i = j - j0;
+        const double above = ((part[i] + part[kPartJ + i]) + part[2 * kPartJ + i]) + part[3 * kPartJ + i];
+        L.keep[j] = (above / zk < (double)a.top_p) ? 1 : 0;
+      }
+      __syncthreads();
+    } else {
+      for (int j = j0 + t; j < j1; j += kThreads) L.keep[j] = 1;
     }
   }
-  __builtin_amdgcn_wave_barrier();
-  // Z_S, then p, entropy, the index order of S
+  __syncthreads();
+  // rank of every kept entry among the kept ones by index: keep[j] becomes rank + 1
+  for (int j0 = 0; j0 < nk; j0 += kPartJ) {
+    const int j1 = min(nk, j0 + kPartJ);
+    for (int j = j0 + lane; j < j1; j += 64) {
+      int c = 0;
+      if (L.keep[j]) {
+        const int xj = L.kx[j];
+        for (int y = wave; y < nk; y += kWaves) c += (L.keep[y] && L.kx[y] < xj) ? 1 : 0;
+      }
+      ipart[wave * kPartJ + (j - j0)] = c;
+    }
+    __syncthreads();
+    for (int j = j0 + t; j < j1; j += kThreads) {
+      const int i = j - j0;
+      if (L.keep[j]) L.keep[j] = 1 + ipart[i] + ipart[kPartJ + i] + ipart[2 * kPartJ + i] + ipart[3 * kPartJ + i];
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+  // Z_S, then p, entropy, the kept set in index order
   double zs = 0.0;
   int ns_all = 0, nf_all = 0;
   for (int j = lane; j < nk; j += 64)
@@ -733,25 +753,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) v
   nf_all = wave_sum_i(nf_all);
   double ent = 0.0;
   KeptEntry* kept = a.kept + (int64_t)slot * kKeepMax;
-  // (up to 64 entries) each lane's keep flag and index, for the rank by readlane
-  const int kp_l = small && lane < nk ? L.keep[lane] : 0;
-  const int kx_l = small && lane < nk ? L.kx[lane] : 0;
   for (int j = lane; j < nk; j += 64) {
     if (!L.keep[j]) continue;
     const double p = L.ke[j] / zs;
     if (p > 0.0) ent -= p * log2_split(p);
-    const int xj = L.kx[j];
-    int rank = 0;
-    if (small) {
-      for (int y = 0; y < nk; ++y)
-        rank += (__builtin_amdgcn_readlane(kp_l, y) && __builtin_amdgcn_readlane(kx_l, y) < xj) ? 1 : 0;
-    } else {
-      for (int y = 0; y < nk; ++y) rank += (L.keep[y] && L.kx[y] < xj) ? 1 : 0;
-    }
     KeptEntry ke;
-    ke.x = xj;
+    ke.x = L.kx[j];
     ke.p = p;
-    kept[rank] = ke;
+    kept[L.keep[j] - 1] = ke;
   }
   ent = wave_sum_dpp_d(ent);
   if (lane == 0) {
