@@ -780,15 +780,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) v
 
 struct FinFLds {
   double py[kMaxGamma + 1], qy[kMaxGamma + 1], u0[kMaxGamma];
+  double us[kMaxGamma + 1][3];                            // sampler uniforms of every position
   int ytok[kMaxGamma];
+  int np[kMaxGamma + 1], nq[kMaxGamma + 1];               // kept counts of every position's rows
   float dh[kMaxGamma], dm[kMaxGamma];
   double ap[kMaxGamma];                                   // accept probability per position
   int pidx[kWaves][kKeepMax], qidx[kWaves][kKeepMax];   // a wave's kept token lists
+  double ppv[kWaves][kKeepMax], qpv[kWaves][kKeepMax];  // and their probabilities
   double w[kKeepMax];                                     // sampler weights of the chosen row
   int xs[kKeepMax];
   int flags, status, n_acc, pos, wkind, y, n, x;
   double u[3];
 };
+
+// A row's kept set into LDS (indices and probabilities): the first 64 entries are read before
+// the count is known (the kept array always holds kKeepMax entries), the rest after it.
+__device__ __forceinline__ void stage_kept(const KeptEntry* k, int n, int* ix, double* pv, const KeptEntry& first) {
+  const int lane = threadIdx.x & 63;
+  if (lane < n) { ix[lane] = first.x; pv[lane] = first.p; }
+  for (int j = 64 + lane; j < n; j += 64) { const KeptEntry e = k[j]; ix[j] = e.x; pv[j] = e.p; }
+}
 
 // Position of token x in a sorted index list (n entries), or -1.
 __device__ __forceinline__ int find_idx(const int* ix, int n, int x) {
@@ -872,40 +883,63 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
   const int c0 = cu_s[b], g = cu_s[b + 1] - c0;
   if (t == 0) F.flags = 0;
   __syncthreads();
-  // A. per position (one wave each): flags, statistics, p(y), q(y), 1 - TV
+  // A. per position (one wave each): flags, statistics, p(y), q(y), 1 - TV.  A position's row
+  // statistics, token and first 64 kept entries of both rows are read at once; every later
+  // lookup is in LDS.
   int* pix = F.pidx[wave];
   int* qix = F.qidx[wave];
+  double* ppv = F.ppv[wave];
+  double* qpv = F.qpv[wave];
   for (int i = wave; i <= g; i += kWaves) {
     const int ps = c0 + b + i;
-    const RowStat2 P = a.rstat[ps];
+    const int qs = a.n_teams + c0 + i;
+    const bool has_q = MODE == kFuSample && i < g;
     const KeptEntry* kp = a.kept + (int64_t)ps * kKeepMax;
+    const KeptEntry* kq = a.kept + (int64_t)qs * kKeepMax;
+    const RowStat2 P = a.rstat[ps];
+    RowStat2 Q;
+    Q.n = 0; Q.flags = 0; Q.entropy = 0.0; Q.max_prob = 0.0;
+    if (has_q) Q = a.rstat[qs];
+    const KeptEntry kp0 = kp[lane];
+    KeptEntry kq0;
+    kq0.x = 0; kq0.p = 0.0;
+    if (has_q) kq0 = kq[lane];
+    const int y = i < g ? a.tokens[c0 + i] : -1;
     const bool okp = P.flags == 0;
     int fl = P.flags;
     const int np = okp ? P.n : 0;
-    for (int j = lane; j < np; j += 64) pix[j] = kp[j].x;
+    stage_kept(kp, np, pix, ppv, kp0);
+    if (lane == 0) {
+      // the Philox block of position i (1-based i + 1): word 0 is the accept draw, words 1..3
+      // the sampler's uniforms if the emitted token is drawn there
+      uint64_t w[4];
+      philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(i + 1), 0, 0, w);
+      if (i < g) F.u0[i] = u53(w[0]);
+      F.us[i][0] = u53(w[1]);
+      F.us[i][1] = u53(w[2]);
+      F.us[i][2] = u53(w[3]);
+      F.np[i] = np;
+    }
     if (i < g) {
-      const int y = a.tokens[c0 + i];
       const bool yv = y >= 0 && y < a.V;
       double pyd = 0.0, qyd = 1.0, ap = nan;
       float py = nan, qy = nan, ovl = nan, dh = nan, dm = nan, l1 = nan, klpq = nan, klqp = nan;
       const bool want_kl = a.st.kl_pq || a.st.kl_qp;
       if (MODE == kFuSample) {
-        const int qs = a.n_teams + c0 + i;
-        const RowStat2 Q = a.rstat[qs];
         fl |= Q.flags;
         const bool okq = Q.flags == 0;
-        const KeptEntry* kq = a.kept + (int64_t)qs * kKeepMax;
         const int nq = okq ? Q.n : 0;
-        for (int j = lane; j < nq; j += 64) qix[j] = kq[j].x;
+        stage_kept(kq, nq, qix, qpv, kq0);
+        if (lane == 0) F.nq[i] = nq;
         __builtin_amdgcn_wave_barrier();
         if (okp && yv) {
           const int m = find_idx(pix, np, y);
-          pyd = m >= 0 ? kp[m].p : 0.0;
+          pyd = m >= 0 ? ppv[m] : 0.0;
           py = (float)pyd;
         }
         if (okq && yv) {
           const int m = find_idx(qix, nq, y);
-          qyd = m >= 0 ? kq[m].p : 0.0;
+          qyd = m >= 0 ? qpv[m] : 0.0;
           qy = (float)qyd;
         }
         if (okp && okq) {
@@ -915,7 +949,7 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
           int miss = 0;
           for (int j = lane; j < np; j += 64) {
             const int m = find_idx(qix, nq, pix[j]);
-            const double pv = kp[j].p, qv = m >= 0 ? kq[m].p : 0.0;
+            const double pv = ppv[j], qv = m >= 0 ? qpv[m] : 0.0;
             part += fmin(pv, qv);
             beta += fmax(pv - qv, 0.0);
             if (want_kl) {
@@ -934,7 +968,7 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
             miss = 0;
             for (int j = lane; j < nq; j += 64) {
               const int m = find_idx(pix, np, qix[j]);
-              if (m >= 0) kl2 += kq[j].p * log(kq[j].p / kp[m].p);
+              if (m >= 0) kl2 += qpv[j] * log(qpv[j] / ppv[m]);
               else miss = 1;
             }
             kl2 = wave_sum_dpp_d(kl2);
@@ -947,7 +981,7 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
         __builtin_amdgcn_wave_barrier();
         if (okp && yv) {
           const int m = find_idx(pix, np, y);
-          pyd = m >= 0 ? kp[m].p : 0.0;
+          pyd = m >= 0 ? ppv[m] : 0.0;
           py = (float)pyd;
         }
         qyd = 1.0;
@@ -979,9 +1013,6 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
         F.py[i] = pyd;
         F.qy[i] = qyd;
         F.ytok[i] = y;
-        uint64_t w[4];
-        philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(i + 1), 0, 0, w);
-        F.u0[i] = u53(w[0]);
       }
     }
     if (lane == 0) {
@@ -1014,11 +1045,9 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
     F.pos = j < 0 ? g : j;
     F.y = j >= 0 ? F.ytok[j] : -1;
     F.wkind = (j < 0) ? 0 : (MODE == kFuSample ? 1 : 2);
-    uint64_t w[4];
-    philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(F.pos + 1), 0, 0, w);
-    F.u[0] = u53(w[1]);
-    F.u[1] = u53(w[2]);
-    F.u[2] = u53(w[3]);
+    F.u[0] = F.us[F.pos][0];
+    F.u[1] = F.us[F.pos][1];
+    F.u[2] = F.us[F.pos][2];
     F.status = status;
     F.x = -1;
     if (a.st.expected_committed)
@@ -1044,29 +1073,31 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
   // C. the three-level sampler on the sparse weights of the chosen row (reading R6): weights in
   // LDS (all threads), then the level sums in index order (one thread)
   if (!(F.status & (kStNonfinite | kStFilterOverflow))) {
+    // the chosen row's kept set (indices into xs, probabilities into w) and, for the residual,
+    // its draft row's (into wave 0's lists), in one pass
     const int ps = c0 + b + F.pos;
-    const RowStat2 P = a.rstat[ps];
     const KeptEntry* kp = a.kept + (int64_t)ps * kKeepMax;
-    const int n = P.n;
+    const int n = F.np[F.pos];
     const KeptEntry* kq = nullptr;
     int nq = 0;
     if (MODE == kFuSample && F.pos < g) {
       const int qs = a.n_teams + c0 + F.pos;
       kq = a.kept + (int64_t)qs * kKeepMax;
-      nq = a.rstat[qs].n;
-      for (int j = t; j < nq; j += kThreads) F.qidx[0][j] = kq[j].x;
+      nq = F.nq[F.pos];
     }
-    for (int j = t; j < n; j += kThreads) F.xs[j] = kp[j].x;
+    __syncthreads();   // every wave is done with its lists
+    for (int j = t; j < nq; j += kThreads) { const KeptEntry e = kq[j]; F.qidx[0][j] = e.x; F.qpv[0][j] = e.p; }
+    for (int j = t; j < n; j += kThreads) { const KeptEntry e = kp[j]; F.xs[j] = e.x; F.ppv[0][j] = e.p; }
     __syncthreads();
     for (int pass = 0; pass < 2; ++pass) {
       const int wkind = pass == 0 ? F.wkind : 0;
       const int yx = F.y;
       for (int j = t; j < n; j += kThreads) {
-        const double p = kp[j].p;
+        const double p = F.ppv[0][j];
         double w = p;
         if (wkind == 1) {
           const int m = find_idx(F.qidx[0], nq, F.xs[j]);
-          w = fmax(p - (m >= 0 ? kq[m].p : 0.0), 0.0);
+          w = fmax(p - (m >= 0 ? F.qpv[0][m] : 0.0), 0.0);
         } else if (wkind == 2) {
           w = F.xs[j] == yx ? fmax(p - 1.0, 0.0) : p;
         }
