@@ -860,8 +860,18 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int b = blockIdx.x;
   const float nan = __int_as_float(0x7fc00000);
-  // the draft offsets, checked as one exclusive prefix
+  // the draft offsets, checked as one exclusive prefix; meanwhile thread t draws the Philox block
+  // of position t (1-based t + 1): word 0 is the accept draw, words 1..3 the sampler's uniforms
+  // if the emitted token is drawn there
   for (int k = t; k <= a.B; k += kThreads) cu_s[k] = a.cu[k];
+  if (t <= a.G) {
+    uint64_t w[4];
+    philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(t + 1), 0, 0, w);
+    if (t < a.G) F.u0[t] = u53(w[0]);
+    F.us[t][0] = u53(w[1]);
+    F.us[t][1] = u53(w[2]);
+    F.us[t][2] = u53(w[3]);
+  }
   __syncthreads();
   int badc = 0;
   for (int k = t; k < a.B; k += kThreads) {
@@ -890,36 +900,47 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
   int* qix = F.qidx[wave];
   double* ppv = F.ppv[wave];
   double* qpv = F.qpv[wave];
+  // the reads of position i; the wave's next position is read while this one is worked on
+  struct PosIn {
+    RowStat2 P, Q;
+    KeptEntry kp0, kq0;
+    int y;
+  };
+  auto read_pos = [&](int i) {
+    PosIn r;
+    r.Q.n = 0; r.Q.flags = 0; r.Q.entropy = 0.0; r.Q.max_prob = 0.0;
+    r.kq0.x = 0; r.kq0.p = 0.0;
+    r.y = -1;
+    r.P = r.Q;
+    r.kp0 = r.kq0;
+    if (i > g) return r;
+    const int ps = c0 + b + i, qs = a.n_teams + c0 + i;
+    r.P = a.rstat[ps];
+    r.kp0 = a.kept[(int64_t)ps * kKeepMax + lane];
+    if (MODE == kFuSample && i < g) {
+      r.Q = a.rstat[qs];
+      r.kq0 = a.kept[(int64_t)qs * kKeepMax + lane];
+    }
+    if (i < g) r.y = a.tokens[c0 + i];
+    return r;
+  };
+  PosIn nxt = read_pos(wave);
   for (int i = wave; i <= g; i += kWaves) {
+    const PosIn cur = nxt;
+    nxt = read_pos(i + kWaves);
     const int ps = c0 + b + i;
     const int qs = a.n_teams + c0 + i;
-    const bool has_q = MODE == kFuSample && i < g;
     const KeptEntry* kp = a.kept + (int64_t)ps * kKeepMax;
     const KeptEntry* kq = a.kept + (int64_t)qs * kKeepMax;
-    const RowStat2 P = a.rstat[ps];
-    RowStat2 Q;
-    Q.n = 0; Q.flags = 0; Q.entropy = 0.0; Q.max_prob = 0.0;
-    if (has_q) Q = a.rstat[qs];
-    const KeptEntry kp0 = kp[lane];
-    KeptEntry kq0;
-    kq0.x = 0; kq0.p = 0.0;
-    if (has_q) kq0 = kq[lane];
-    const int y = i < g ? a.tokens[c0 + i] : -1;
+    const RowStat2 P = cur.P;
+    const RowStat2 Q = cur.Q;
+    const KeptEntry kp0 = cur.kp0, kq0 = cur.kq0;
+    const int y = cur.y;
     const bool okp = P.flags == 0;
     int fl = P.flags;
     const int np = okp ? P.n : 0;
     stage_kept(kp, np, pix, ppv, kp0);
-    if (lane == 0) {
-      // the Philox block of position i (1-based i + 1): word 0 is the accept draw, words 1..3
-      // the sampler's uniforms if the emitted token is drawn there
-      uint64_t w[4];
-      philox4x64_10(a.seed, a.step, (uint64_t)b, (uint64_t)(i + 1), 0, 0, w);
-      if (i < g) F.u0[i] = u53(w[0]);
-      F.us[i][0] = u53(w[1]);
-      F.us[i][1] = u53(w[2]);
-      F.us[i][2] = u53(w[3]);
-      F.np[i] = np;
-    }
+    if (lane == 0) F.np[i] = np;
     if (i < g) {
       const bool yv = y >= 0 && y < a.V;
       double pyd = 0.0, qyd = 1.0, ap = nan;
