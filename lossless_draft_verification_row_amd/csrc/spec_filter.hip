@@ -539,7 +539,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) v
   const int n_s = a.n_l, cap = a.cap;   // candidate lists of the row
   const CandHead* hd = a.chead + (int64_t)slot * n_s;
   const CandEntry* cd = a.cand + (int64_t)slot * n_s * cap;
-  // slice headers, one per lane of wave 0; prefix of the stored counts
+  // the first 64 candidates of each wave's first four lists go out with the headers (every
+  // list has cap slots; entries past its count are never used)
+  const int wv = t >> 6;
+  CandEntry pre[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int sl = wv + u * kWaves;
+    if (sl < n_s && lane < cap) pre[u] = cd[(int64_t)sl * cap + lane];
+  }
+  // list headers, one per lane of wave 0; prefix of the stored counts
   CandHead h;
   h.stored = 0; h.total = 0; h.th = 0u; h.flags = 0;
   if (t < n_s) h = hd[t];
@@ -566,18 +575,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) v
   int km = -1;
   if (staged) {
     // copy the candidates in: wave w takes lists w, w + 4, ..., lane l entries l and l + 64
-    // of each; four lists per wave (eight loads per thread) in flight at a time
-    const int wv = t >> 6;
+    // of each; four lists per wave (eight loads per thread) in flight at a time, the first
+    // four already read
     for (int i0 = 0; i0 < cap; i0 += 128) {
       for (int s0 = wv; s0 < n_s; s0 += kWaves * 4) {
         CandEntry tmp[4][2];
+        const bool first = i0 == 0 && s0 == wv;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int sl = s0 + u * kWaves;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int idx = i0 + lane + 64 * h;
-            if (sl < n_s && idx < L.cnt[sl]) tmp[u][h] = cd[(int64_t)sl * cap + idx];
+            if (first && h == 0) tmp[u][h] = pre[u];
+            else if (sl < n_s && idx < L.cnt[sl]) tmp[u][h] = cd[(int64_t)sl * cap + idx];
           }
         }
 #pragma unroll
