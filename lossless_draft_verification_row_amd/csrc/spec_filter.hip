@@ -871,6 +871,35 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int b = blockIdx.x;
   const float nan = __int_as_float(0x7fc00000);
+  // the reads of position i; the wave's next position is read while this one is worked on
+  struct PosIn {
+    RowStat2 P, Q;
+    KeptEntry kp0, kq0;
+    int y;
+  };
+  auto read_pos = [&](int i, int c0, int g) {
+    PosIn r;
+    r.Q.n = 0; r.Q.flags = 0; r.Q.entropy = 0.0; r.Q.max_prob = 0.0;
+    r.kq0.x = 0; r.kq0.p = 0.0;
+    r.y = -1;
+    r.P = r.Q;
+    r.kp0 = r.kq0;
+    if (i > g) return r;
+    const int ps = c0 + b + i, qs = a.n_teams + c0 + i;
+    r.P = a.rstat[ps];
+    r.kp0 = a.kept[(int64_t)ps * kKeepMax + lane];
+    if (MODE == kFuSample && i < g) {
+      r.Q = a.rstat[qs];
+      r.kq0 = a.kept[(int64_t)qs * kKeepMax + lane];
+    }
+    if (i < g) r.y = a.tokens[c0 + i];
+    return r;
+  };
+  // the wave's first position goes out at once, at the guess c0 = b G (exact when every request
+  // has G draft tokens); a wrong guess reads it again once the offsets are known
+  const int cg = b * a.G;
+  const bool guess_in = cg + a.G <= a.n_draft_rows;
+  PosIn nxt = read_pos(guess_in ? wave : a.G + 1, cg, a.G);
   // the draft offsets, checked as one exclusive prefix; meanwhile thread t draws the Philox block
   // of position t (1-based t + 1): word 0 is the accept draw, words 1..3 the sampler's uniforms
   // if the emitted token is drawn there
@@ -902,6 +931,7 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
     return;
   }
   const int c0 = cu_s[b], g = cu_s[b + 1] - c0;
+  if (!(guess_in && c0 == cg && g == a.G)) nxt = read_pos(wave, c0, g);
   if (t == 0) F.flags = 0;
   __syncthreads();
   // A. per position (one wave each): flags, statistics, p(y), q(y), 1 - TV.  A position's row
@@ -911,34 +941,9 @@ __global__ __launch_bounds__(kThreads) void k_filt_finalize(FilterArgs a) {
   int* qix = F.qidx[wave];
   double* ppv = F.ppv[wave];
   double* qpv = F.qpv[wave];
-  // the reads of position i; the wave's next position is read while this one is worked on
-  struct PosIn {
-    RowStat2 P, Q;
-    KeptEntry kp0, kq0;
-    int y;
-  };
-  auto read_pos = [&](int i) {
-    PosIn r;
-    r.Q.n = 0; r.Q.flags = 0; r.Q.entropy = 0.0; r.Q.max_prob = 0.0;
-    r.kq0.x = 0; r.kq0.p = 0.0;
-    r.y = -1;
-    r.P = r.Q;
-    r.kp0 = r.kq0;
-    if (i > g) return r;
-    const int ps = c0 + b + i, qs = a.n_teams + c0 + i;
-    r.P = a.rstat[ps];
-    r.kp0 = a.kept[(int64_t)ps * kKeepMax + lane];
-    if (MODE == kFuSample && i < g) {
-      r.Q = a.rstat[qs];
-      r.kq0 = a.kept[(int64_t)qs * kKeepMax + lane];
-    }
-    if (i < g) r.y = a.tokens[c0 + i];
-    return r;
-  };
-  PosIn nxt = read_pos(wave);
   for (int i = wave; i <= g; i += kWaves) {
     const PosIn cur = nxt;
-    nxt = read_pos(i + kWaves);
+    nxt = read_pos(i + kWaves, c0, g);
     const int ps = c0 + b + i;
     const int qs = a.n_teams + c0 + i;
     const KeptEntry* kp = a.kept + (int64_t)ps * kKeepMax;
