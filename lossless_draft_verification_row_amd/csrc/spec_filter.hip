@@ -501,21 +501,30 @@ __global__ __launch_bounds__(kThreads) void k_filt_slices(FilterArgs a) {
 
 // ---------------------------------------------------------------- k_filt_rows
 
-constexpr int kRowStage = 1280;   // candidates of a row staged in LDS (more: read in place); 22 KB of
-                                  // LDS in all, so 6 rows (the register limit) share a CU
+constexpr int kRowStage = 1280;   // candidates of a row staged in LDS (more: read in place); 16 KB of
+                                  // LDS in all, so eight rows share a CU
+
+// Partial sums per wave of the kept-set steps, in the staging area beside e and keep.
+constexpr int kPartJ = (kRowStage * 8 - kKeepMax * 12) / (kWaves * 8);
 
 struct RowLds {
   SelLds sel;
   int cnt[kMaxSlicesFused + 1];
   int off[kMaxSlicesFused + 1];
-  alignas(16) CandEntry cand[kRowStage];   // also the partial sums of the kept-set steps
+  union {
+    alignas(16) CandEntry cand[kRowStage];   // the staged candidates, until the kept set is compacted
+    struct {
+      double ke[kKeepMax];                   // then the kept set's e-values,
+      int keep[kKeepMax];                    // keep flags / ranks
+      double part[kWaves][kPartJ];           // and the waves' partial sums
+    } k;
+  };
   float kv[kKeepMax];
   int kx[kKeepMax];
-  double ke[kKeepMax];
-  int keep[kKeepMax];
   double red[kWaves];
   int flags, nk, ns;
 };
+static_assert(sizeof(CandEntry) == 8 && kPartJ >= 64, "the kept-set scratch fits the staging area");
 
 __device__ __forceinline__ double block_sum_dd(double v, double* red) {
   v = wave_sum_dpp_d(v);
@@ -530,7 +539,7 @@ __device__ __forceinline__ double block_sum_dd(double v, double* red) {
 
 // One row: global top-k over the slices' candidates, top-p, the kept set with probabilities.
 template <int DT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) void k_filt_rows(FilterArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_filt_rows(FilterArgs a) {
   constexpr int NP = DT == kDtBF16 ? 2 : 4;
   __shared__ RowLds L;
   const int t = threadIdx.x, lane = t & 63;
@@ -539,12 +548,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) v
   const int n_s = a.n_l, cap = a.cap;   // candidate lists of the row
   const CandHead* hd = a.chead + (int64_t)slot * n_s;
   const CandEntry* cd = a.cand + (int64_t)slot * n_s * cap;
-  // the first 64 candidates of each wave's first four lists go out with the headers (every
+  // the first 64 candidates of each wave's first two lists go out with the headers (every
   // list has cap slots; entries past its count are never used)
   const int wv = t >> 6;
-  CandEntry pre[4];
+  CandEntry pre[2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < 2; ++u) {
     const int sl = wv + u * kWaves;
     if (sl < n_s && lane < cap) pre[u] = cd[(int64_t)sl * cap + lane];
   }
@@ -576,7 +585,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) v
   if (staged) {
     // copy the candidates in: wave w takes lists w, w + 4, ..., lane l entries l and l + 64
     // of each; four lists per wave (eight loads per thread) in flight at a time, the first
-    // four already read
+    // two already read
     for (int i0 = 0; i0 < cap; i0 += 128) {
       for (int s0 = wv; s0 < n_s; s0 += kWaves * 4) {
         CandEntry tmp[4][2];
@@ -587,7 +596,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) v
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int idx = i0 + lane + 64 * h;
-            if (first && h == 0) tmp[u][h] = pre[u];
+            if (first && h == 0 && u < 2) tmp[u][h] = pre[u];
             else if (sl < n_s && idx < L.cnt[sl]) tmp[u][h] = cd[(int64_t)sl * cap + idx];
           }
         }
@@ -677,8 +686,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) v
   __syncthreads();
   // The kept set (at most kKeepMax entries) is in LDS.  Wave 0 takes the maximum and the
   // e-values; the quadratic top-p and rank sums are spread over the four waves (wave w takes
-  // every fourth entry y), their partials meeting in the staging area, free again; wave 0 then
-  // forms Z_S, p, entropy and writes the kept set in index order.
+  // every fourth entry y), their partials meeting in LDS (the e-values, flags and partials use
+  // the staging area, free again); wave 0 then forms Z_S, p, entropy and writes the kept set in
+  // index order.
   const int wave = t >> 6;
   RowStat2 st;
   st.n = 0; st.flags = L.flags; st.m = -INFINITY; st.argmax = -1; st.kept_finite = 0; st.pad = 0;
@@ -701,7 +711,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) v
     double zk = 0.0;
     for (int j = lane; j < nk; j += 64) {
       const double e = exp2_split(((double)L.kv[j] - (double)m) * cd2);
-      L.ke[j] = e;
+      L.k.ke[j] = e;
       zk += e;
     }
     zk = wave_sum_dpp_d(zk);
@@ -709,9 +719,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) v
   }
   __syncthreads();
   const double zk = L.red[0];
-  constexpr int kPartJ = kRowStage * (int)sizeof(CandEntry) / (kWaves * (int)sizeof(double));
-  double* part = (double*)L.cand;
-  int* ipart = (int*)L.cand;
+  double* part = &L.k.part[0][0];
+  int* ipart = (int*)&L.k.part[0][0];
   // top-p: keep x iff the mass of values strictly above l_x is below top_p (the value group
   // that first reaches top_p is kept whole; reading R1); keep[j] = 1 for a kept entry
   for (int j0 = 0; j0 < nk; j0 += kPartJ) {
@@ -720,18 +729,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) v
       for (int j = j0 + lane; j < j1; j += 64) {
         const float lx = L.kv[j];
         double ab = 0.0;
-        for (int y = wave; y < nk; y += kWaves) ab += (L.kv[y] > lx) ? L.ke[y] : 0.0;
+        for (int y = wave; y < nk; y += kWaves) ab += (L.kv[y] > lx) ? L.k.ke[y] : 0.0;
         part[wave * kPartJ + (j - j0)] = ab;
       }
       __syncthreads();
       for (int j = j0 + t; j < j1; j += kThreads) {
         const int i = j - j0;
         const double above = ((part[i] + part[kPartJ + i]) + part[2 * kPartJ + i]) + part[3 * kPartJ + i];
-        L.keep[j] = (above / zk < (double)a.top_p) ? 1 : 0;
+        L.k.keep[j] = (above / zk < (double)a.top_p) ? 1 : 0;
       }
       __syncthreads();
     } else {
-      for (int j = j0 + t; j < j1; j += kThreads) L.keep[j] = 1;
+      for (int j = j0 + t; j < j1; j += kThreads) L.k.keep[j] = 1;
     }
   }
   __syncthreads();
@@ -740,16 +749,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) v
     const int j1 = min(nk, j0 + kPartJ);
     for (int j = j0 + lane; j < j1; j += 64) {
       int c = 0;
-      if (L.keep[j]) {
+      if (L.k.keep[j]) {
         const int xj = L.kx[j];
-        for (int y = wave; y < nk; y += kWaves) c += (L.keep[y] && L.kx[y] < xj) ? 1 : 0;
+        for (int y = wave; y < nk; y += kWaves) c += (L.k.keep[y] && L.kx[y] < xj) ? 1 : 0;
       }
       ipart[wave * kPartJ + (j - j0)] = c;
     }
     __syncthreads();
     for (int j = j0 + t; j < j1; j += kThreads) {
       const int i = j - j0;
-      if (L.keep[j]) L.keep[j] = 1 + ipart[i] + ipart[kPartJ + i] + ipart[2 * kPartJ + i] + ipart[3 * kPartJ + i];
+      if (L.k.keep[j]) L.k.keep[j] = 1 + ipart[i] + ipart[kPartJ + i] + ipart[2 * kPartJ + i] + ipart[3 * kPartJ + i];
     }
     __syncthreads();
   }
@@ -758,20 +767,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) v
   double zs = 0.0;
   int ns_all = 0, nf_all = 0;
   for (int j = lane; j < nk; j += 64)
-    if (L.keep[j]) { zs += L.ke[j]; ++ns_all; nf_all += L.kv[j] > -INFINITY ? 1 : 0; }
+    if (L.k.keep[j]) { zs += L.k.ke[j]; ++ns_all; nf_all += L.kv[j] > -INFINITY ? 1 : 0; }
   zs = wave_sum_dpp_d(zs);
   ns_all = wave_sum_i(ns_all);
   nf_all = wave_sum_i(nf_all);
   double ent = 0.0;
   KeptEntry* kept = a.kept + (int64_t)slot * kKeepMax;
   for (int j = lane; j < nk; j += 64) {
-    if (!L.keep[j]) continue;
-    const double p = L.ke[j] / zs;
+    if (!L.k.keep[j]) continue;
+    const double p = L.k.ke[j] / zs;
     if (p > 0.0) ent -= p * log2_split(p);
     KeptEntry ke;
     ke.x = L.kx[j];
     ke.p = p;
-    kept[L.keep[j] - 1] = ke;
+    kept[L.k.keep[j] - 1] = ke;
   }
   ent = wave_sum_dpp_d(ent);
   if (lane == 0) {
