@@ -445,6 +445,11 @@ int spec_verify_batch_ex(int B, int V, int gamma_max, spec_dtype dt, const void*
     }
     f.ylog = cv.take<float>((size_t)f.n_teams * 2 * sizeof(float));
     f.poll_delay = op.poll_delay;
+    {
+      int dev = 0, cus = 0;
+      if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+      f.tail_wgs = cus * kFusedWgsPerCu;
+    }
     f.poll_pause = op.poll_pause;
     f.out_tokens = out_tokens;
     f.out_num_accepted = out_num_accepted;

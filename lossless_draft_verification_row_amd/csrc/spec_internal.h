@@ -17,6 +17,7 @@ constexpr int kMaxGamma = 64;     // gamma_max bound (one finalize thread per po
 constexpr int kMaxSlicesFused = 64;    // V <= 64 * 4096
 constexpr int kMaxTeamsFused = 4096;   // target rows
 constexpr int kMaxReqFused = 1024;     // requests
+constexpr int kFusedWgsPerCu = 8;       // resident streaming workgroups per CU (64 VGPRs, 19.7 KB LDS)
 constexpr int kMaxMembers = 32;        // streaming workgroups of one target row (two slices each)
 constexpr int kFuSample = 0;           // draft logits, temperature > 0
 constexpr int kFuTokenOnly = 1;        // token-only draft, temperature > 0
@@ -143,6 +144,8 @@ struct FusedArgs {
   int32_t* team_row;    // [n_teams]: the target row of the team in each dispatch place, for ragged
                         // batches (written by k_team_map); nullptr when every request has G drafts
   int poll_delay;       // wait before the first team poll, in 10 ns ticks
+  int tail_wgs;         // the launch's last generation (one workgroup per resident slot), which
+                        // waits half the poll delay
   int poll_pause;       // pause between team polls, in units of 128 cycles
   int32_t* out_tokens;
   int32_t* out_num_accepted;
