@@ -299,6 +299,33 @@ def test_forced_timeout_then_clean_call():
     check(inp, sp, seed=5, step=6)
 
 
+def test_co_running_kernel_changes_nothing():
+    """A team's members wait only for one another, dispatched side by side on one XCD.  With
+    another kernel streaming on a second stream at the same time (its workgroups taking CU slots
+    and memory bandwidth among the teams'), every wait still ends: no request reports TIMEOUT and
+    every output is bit-equal to the same call run alone."""
+    inp = custom_inputs(48, 16 * 4096 + 77, [7] * 48, seed=41)
+    sp = O.SamplingParams(1.0)
+    solo = run_gpu(inp, sp, 21, 4)
+    assert (solo["status"] == 0).all()
+    d = H.to_device(inp)
+    buf = torch.empty(512 << 20, dtype=torch.uint8, device=DEV)
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        note(f"co-running call {rep}")
+        torch.cuda.synchronize()
+        L.spec_stream_read(buf, sink, stream=side)
+        res = L.spec_verify_batch(d["target"], d["draft"], d["tokens"], d["cu"], 7, temperature=1.0, seed=21,
+                                  step=4)
+        L.spec_stream_read(buf, sink, stream=side)
+        torch.cuda.synchronize()
+        got = H.gpu_to_numpy(res)
+        assert ((got["status"] & L.STATUS["TIMEOUT"]) == 0).all()
+        for k in solo:
+            assert np.array_equal(got[k], solo[k], equal_nan=True), k
+
+
 def test_repeated_calls_identical():
     """Back-to-back calls on one workspace give bitwise equal outputs (counters reset)."""
     inp = custom_inputs(5, 3 * 4096 + 8, [7, 7, 7, 7, 7], seed=37)
