@@ -796,6 +796,353 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   }
 }
 
+// ---------------------------------------------------------------- k_filt_rows_w (bf16 rows)
+
+// One wave per bf16 row, no workgroup barrier.  Entry `lane` of every candidate list (one list
+// per 8192 logits, at most 32) is read in one go into a register holding the entry's 16-bit
+// order key and its offset in the list; entries past 64 of a longer list are read from memory
+// at each pass.  The threshold is the same k-th largest key as in k_filt_rows.  When it lies
+// within 256 keys of the row maximum (the usual case), the per-key counts that found it carry
+// the rest: equal keys are equal values with equal e-values, so the mass above a key (top-p),
+// Z, the entropy and every kept probability come from at most 256 keys, four per lane.  A
+// top-k set spread wider, or fewer candidates than k, keeps its e-values in LDS and sums the
+// masses above each entry directly.  The kept set goes out in index order: a list covers one
+// index range, so an entry's place is the kept entries of the lists before its own plus those
+// of its own list below it.
+constexpr int kWLists = kMaxSlicesFused / 2;
+
+struct RowWLds {
+  union {
+    uint32_t hist[256];    // candidates per order key km - d (or per radix digit)
+    double pd[256];        // window case: p of the kept key km - d
+    double ke[kKeepMax];   // spread case: e-values of the top-k set
+  };
+  uint16_t kk[kKeepMax];   // the top-k set in list order: order keys
+  int kx[kKeepMax];        // and token indices
+  int kb[kWLists + 1];     // list s holds entries kb[s] .. kb[s + 1] - 1
+  int kc[kWLists];         // kept entries per list, then their exclusive prefix
+};
+
+// A bf16-exact candidate as one word: its order key in the high half, bit 15 set, and its
+// offset within its list in the low 13 bits.  Zero is no candidate.
+__device__ __forceinline__ uint32_t cand_word(uint32_t vbits, uint32_t x) {
+  uint32_t b = vbits >> 16;
+  if (b == 0x8000u) b = 0u;
+  const uint32_t key = (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+  uint32_t w = (key << 16) | 0x8000u | (x & 0x1FFFu);
+  asm volatile("" : "+v"(w));   // one register per candidate, not its two halves
+  return w;
+}
+
+template <int NL>
+__global__ __launch_bounds__(64) void k_filt_rows_w(FilterArgs a) {
+  static_assert(NL <= kWLists, "a bf16 row has at most kWLists lists");
+  __shared__ RowWLds L;
+  const int lane = threadIdx.x;
+  const int slot = blockIdx.x;
+  if (slot >= a.n_slots) return;
+  const int n_l = a.n_l, cap = a.cap, k = a.k;
+  RowStat2 st;
+  st.n = 0; st.flags = 0; st.m = -INFINITY; st.argmax = -1; st.kept_finite = 0; st.pad = 0;
+  st.log_z = 0.0; st.entropy = 0.0; st.max_prob = 0.0; st.z = 0.0;
+  if (n_l > NL) {   // not a bf16 row's lists: leave the row to the dense recomputation
+    st.flags = kFlagOverflow;
+    if (lane == 0) a.rstat[slot] = st;
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<CandEntry*>(a.cand + (int64_t)slot * n_l * cap), (short)0, n_l * cap * (int)sizeof(CandEntry),
+      0x00020000);
+  // every load at once, unconditionally (past the row's lists the bounds check returns zeros
+  // and reads nothing): list headers (lane s: list s) and entry `lane` of every list
+  const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<CandHead*>(a.chead + (int64_t)slot * n_l), (short)0, n_l * (int)sizeof(CandHead), 0x00020000);
+  const auto hv = __builtin_amdgcn_raw_buffer_load_b128(rh, lane * (int)sizeof(CandHead), 0, 0);
+  using u32x2 = decltype(__builtin_amdgcn_raw_buffer_load_b64(rs, 0, 0, 0));
+  u32x2 raw[NL];
+#pragma unroll
+  for (int s = 0; s < NL; ++s) raw[s] = __builtin_amdgcn_raw_buffer_load_b64(rs, (s * cap + lane) * 8, 0, 0);
+  CandHead h;   // zeros past the row's lists
+  h.stored = (int)hv[0]; h.total = (int)hv[1]; h.th = hv[2]; h.flags = (int)hv[3];
+  uint32_t w[NL];
+#pragma unroll
+  for (int s = 0; s < NL; ++s) {
+    const uint32_t cw = cand_word(raw[s][0], raw[s][1]);
+    w[s] = lane < __builtin_amdgcn_readlane(h.stored, s) ? cw : 0u;
+  }
+  const int bad = wave_or(h.flags & kFlagBad);
+  const bool extra = wave_or(h.stored > 64 ? 1 : 0) != 0;
+  // cb(word, valid, list) for every candidate; entries past 64 of a list in uniform rounds
+  auto for_each = [&](auto cb) {
+#pragma unroll
+    for (int s = 0; s < NL; ++s) {
+      if (s < n_l) {
+        cb(w[s], w[s] != 0u, s);
+        if (extra) {
+          const int cs = __builtin_amdgcn_readlane(h.stored, s);
+          for (int e0 = 64; e0 < cs; e0 += 64) {
+            const auto e = __builtin_amdgcn_raw_buffer_load_b64(rs, (s * cap + e0 + lane) * 8, 0, 0);
+            cb(cand_word(e[0], e[1]), e0 + lane < cs, s);
+          }
+        }
+      }
+    }
+  };
+  // the largest key, then the candidates per key within 256 below it
+  int km = -1;
+  for_each([&](uint32_t wd, bool ok, int) {
+    if (ok) km = max(km, (int)(wd >> 16));
+  });
+  km = wave_max_i(km);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) L.hist[lane + 64 * q] = 0u;
+  __builtin_amdgcn_wave_barrier();
+  for_each([&](uint32_t wd, bool ok, int) {
+    const int d = km - (int)(wd >> 16);
+    if (ok && d < 256) atomicAdd(&L.hist[d], 1u);
+  });
+  __builtin_amdgcn_wave_barrier();
+  int cq[4], csum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) { cq[q] = (int)L.hist[4 * lane + q]; csum += cq[q]; }
+  const int cinc = wave_incl_scan_i(csum);
+  const bool window = __builtin_amdgcn_readlane(cinc, 63) >= k;
+  bool all = false;
+  uint32_t th = 0u;
+  if (window) {
+    int dg = -1, run = cinc - csum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (dg < 0 && run + cq[q] >= k) dg = 4 * lane + q;
+      run += cq[q];
+    }
+    dg = __builtin_amdgcn_readlane(dg, __builtin_ctzll(__ballot(cinc >= k)));
+    th = (uint32_t)(km - dg);
+  } else {
+    // exact radix select, high then low byte of the key, over every candidate
+    uint32_t prefix = 0u;
+    int kk = k;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) L.hist[lane + 64 * q] = 0u;
+      __builtin_amdgcn_wave_barrier();
+      for_each([&](uint32_t wd, bool ok, int) {
+        const uint32_t key = wd >> 16;
+        if (ok && (pass == 0 || (key >> 8) == prefix)) atomicAdd(&L.hist[pass == 0 ? (key >> 8) : (key & 255u)], 1u);
+      });
+      __builtin_amdgcn_wave_barrier();
+      int c[4], s = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { c[q] = (int)L.hist[255 - 4 * lane - q]; s += c[q]; }
+      const int inc = wave_incl_scan_i(s);
+      if (__builtin_amdgcn_readlane(inc, 63) < kk) { all = true; break; }
+      int dg = -1, ab = 0, run = inc - s;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (dg < 0 && run + c[q] >= kk) { dg = 255 - 4 * lane - q; ab = run; }
+        run += c[q];
+      }
+      const int lh = __builtin_ctzll(__ballot(inc >= kk));
+      dg = __builtin_amdgcn_readlane(dg, lh);
+      ab = __builtin_amdgcn_readlane(ab, lh);
+      prefix = (prefix << 8) | (uint32_t)dg;
+      kk -= ab;
+    }
+    th = all ? 0u : prefix;
+  }
+  // dropped ties of a list hold its threshold key; they belong to the top-k set if it reaches th
+  int fl = bad;
+  if (lane < n_l && h.total > h.stored && (all || h.th >= th)) fl |= kFlagOverflow;
+  fl = wave_or(fl);
+  // the top-k set, compacted list by list
+  const uint32_t thw = all ? 0u : (th << 16);
+  int nk = 0, amx = INT_MAX, cur = -1;
+  for_each([&](uint32_t wd, bool ok, int s) {
+    if (s != cur) {   // uniform: the first entries of list s
+      cur = s;
+      if (lane == 0) L.kb[s] = nk;
+    }
+    const bool in = ok && wd >= thw;
+    const unsigned long long mk = __ballot(in);
+    if (in) {
+      const int o = nk + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(mk >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mk, 0u));
+      const int x = (s << 13) | (int)(wd & 0x1FFFu);
+      if (o < kKeepMax) { L.kk[o] = (uint16_t)(wd >> 16); L.kx[o] = x; }
+      if ((int)(wd >> 16) == km) amx = min(amx, x);
+    }
+    nk += __popcll(mk);
+  });
+  if (lane == 0) L.kb[n_l] = nk;
+  amx = wave_min_i(amx);
+  if (nk > kKeepMax) fl |= kFlagOverflow;
+  if (nk == 0 && !(fl & kFlagBad)) fl |= kFlagEmpty;
+  if (fl) {
+    st.flags = fl;
+    if (lane == 0) a.rstat[slot] = st;
+    return;
+  }
+  __builtin_amdgcn_wave_barrier();
+  const float m = key16_value(km);
+  const double md = (double)m, cd2 = a.c;
+  const int nq8 = (nk + 63) >> 6;   // the top-k set's entries per lane
+  int key_cut;
+  double zs, ent = 0.0;
+  int nkept = 0, nfin = 0;
+  if (window) {
+    // key km - d, d = 4 lane + q: its count in the top-k set, e-value and mass
+    const int dth = km - (int)th;
+    int nq[4];
+    double eq[4], mq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = 4 * lane + q;
+      nq[q] = d <= dth ? cq[q] : 0;
+      eq[q] = nq[q] > 0 ? exp2_split(((double)key16_value(km - d) - md) * cd2) : 0.0;
+      mq[q] = (double)nq[q] * eq[q];
+    }
+    const double inc = wave_scan_dpp_d(((mq[0] + mq[1]) + mq[2]) + mq[3]);
+    const double zk = readlane_d(inc, 63);
+    // mass strictly above key km - d: the lanes below, then this lane's keys before d
+    const long long ib = __double_as_longlong(inc);
+    const int src = (lane == 0 ? 0 : lane - 1) * 4;
+    const int plo = __builtin_amdgcn_ds_bpermute(src, (int)ib), phi = __builtin_amdgcn_ds_bpermute(src, (int)(ib >> 32));
+    double ab = lane == 0 ? 0.0 : __longlong_as_double(((long long)phi << 32) | (unsigned)plo);
+    int dcut = -1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (nq[q] > 0 && (!(a.top_p < 1.f) || ab / zk < (double)a.top_p)) dcut = 4 * lane + q;
+      ab += mq[q];
+    }
+    dcut = wave_max_i(dcut);
+    key_cut = km - dcut;   // dcut < 0 keeps nothing
+    double zl = 0.0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = 4 * lane + q;
+      if (d <= dcut) {
+        zl += mq[q];
+        nkept += nq[q];
+        if (km - d >= 128) nfin += nq[q];   // keys below 128 are -inf
+      }
+    }
+    zs = wave_sum_dpp_d(zl);
+    double el = 0.0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = 4 * lane + q;
+      if (d <= dcut && nq[q] > 0) {
+        const double p = eq[q] / zs;
+        if (p > 0.0) el -= (double)nq[q] * (p * log2_split(p));
+        L.pd[d] = p;
+      }
+    }
+    ent = wave_sum_dpp_d(el);
+  } else {
+    double zl = 0.0;
+    for (int q = 0; q < nq8; ++q) {
+      const int j = lane + 64 * q;
+      if (j < nk) {
+        const double e = exp2_split(((double)key16_value(L.kk[j]) - md) * cd2);
+        L.ke[j] = e;
+        zl += e;
+      }
+    }
+    const double zk = wave_sum_dpp_d(zl);
+    __builtin_amdgcn_wave_barrier();
+    if (a.top_p < 1.f) {
+      // keep x iff the mass of the strictly larger values is below top_p (an upper set of keys)
+      int kmin = INT_MAX;
+      for (int q = 0; q < nq8; ++q) {
+        const int j = lane + 64 * q;
+        const int kj = j < nk ? (int)L.kk[j] : 0x10000;
+        double ab = 0.0;
+        for (int y = 0; y < nk; ++y) ab += ((int)L.kk[y] > kj) ? L.ke[y] : 0.0;
+        if (j < nk && ab / zk < (double)a.top_p) kmin = min(kmin, kj);
+      }
+      kmin = wave_min_i(kmin);
+      key_cut = kmin == INT_MAX ? 0x10000 : kmin;
+    } else {
+      key_cut = 0;
+    }
+    double zl2 = 0.0;
+    for (int q = 0; q < nq8; ++q) {
+      const int j = lane + 64 * q;
+      if (j < nk && (int)L.kk[j] >= key_cut) {
+        zl2 += L.ke[j];
+        ++nkept;
+        if (L.kk[j] >= 128) ++nfin;
+      }
+    }
+    zs = wave_sum_dpp_d(zl2);
+    double el = 0.0;
+    for (int q = 0; q < nq8; ++q) {
+      const int j = lane + 64 * q;
+      if (j < nk && (int)L.kk[j] >= key_cut) {
+        const double p = L.ke[j] / zs;
+        if (p > 0.0) el -= p * log2_split(p);
+      }
+    }
+    ent = wave_sum_dpp_d(el);
+  }
+  nkept = wave_sum_i(nkept);
+  nfin = wave_sum_i(nfin);
+  // the kept set in index order: kept entries of the lists before, then of its own list below it
+  if (lane < n_l) L.kc[lane] = 0;
+  __builtin_amdgcn_wave_barrier();
+  for (int q = 0; q < nq8; ++q) {
+    const int j = lane + 64 * q;
+    if (j < nk && (int)L.kk[j] >= key_cut) atomicAdd(&L.kc[L.kx[j] >> 13], 1);
+  }
+  __builtin_amdgcn_wave_barrier();
+  {
+    const int c = lane < n_l ? L.kc[lane] : 0;
+    const int inc = wave_incl_scan_i(c);
+    __builtin_amdgcn_wave_barrier();
+    if (lane < n_l) L.kc[lane] = inc - c;
+  }
+  __builtin_amdgcn_wave_barrier();
+  KeptEntry* kept = a.kept + (int64_t)slot * kKeepMax;
+  for (int q = 0; q < nq8; ++q) {
+    const int j = lane + 64 * q;
+    if (j < nk) {
+      const int kj = L.kk[j];
+      if (kj >= key_cut) {
+        const int x = L.kx[j], l = x >> 13;
+        int r = L.kc[l];
+        const int y1 = L.kb[l + 1];
+        for (int y = L.kb[l]; y < y1; ++y) r += ((int)L.kk[y] >= key_cut && L.kx[y] < x) ? 1 : 0;
+        KeptEntry e;
+        e.x = x;
+        e.pad = 0;
+        e.p = window ? L.pd[km - kj] : L.ke[j] / zs;
+        kept[r] = e;
+      }
+    }
+  }
+  if (lane == 0) {
+    st.n = nkept;
+    st.kept_finite = nfin;
+    st.m = m;
+    st.argmax = amx;
+    st.z = zs;
+    st.log_z = md * a.inv_t + log2_split(zs) * 0.6931471805599453;
+    st.entropy = ent;
+    st.max_prob = 1.0 / zs;
+    a.rstat[slot] = st;
+  }
+}
+
+// The wave-per-row kernel with room for the row's lists (a bf16 row has at most kWLists).
+void launch_rows_w(const FilterArgs& a, hipStream_t st) {
+  const dim3 g(a.n_slots), b(64);
+  if (a.n_l <= 8) hipLaunchKernelGGL(k_filt_rows_w<8>, g, b, 0, st, a);
+  else if (a.n_l <= 16) hipLaunchKernelGGL(k_filt_rows_w<16>, g, b, 0, st, a);
+  else if (a.n_l <= 24) hipLaunchKernelGGL(k_filt_rows_w<24>, g, b, 0, st, a);
+  else hipLaunchKernelGGL(k_filt_rows_w<kWLists>, g, b, 0, st, a);
+}
+
 // ---------------------------------------------------------------- k_filt_finalize
 
 struct FinFLds {
@@ -1219,7 +1566,7 @@ hipError_t launch_filter(const FilterArgs& a0, int dt, int vec, hipStream_t st, 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (dt == kDtBF16) hipLaunchKernelGGL((k_filt_rows<kDtBF16>), dim3(a.n_slots), dim3(kThreads), 0, st, a);
+  if (dt == kDtBF16) launch_rows_w(a, st);
   else hipLaunchKernelGGL((k_filt_rows<kDtF32>), dim3(a.n_slots), dim3(kThreads), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1351,7 +1698,7 @@ hipError_t launch_filter_rows(const FilterArgs& a0, int dt, int vec, int what, h
 #undef SPEC_SLICES
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (dt == kDtBF16) hipLaunchKernelGGL((k_filt_rows<kDtBF16>), dim3(a.n_slots), dim3(kThreads), 0, st, a);
+  if (dt == kDtBF16) launch_rows_w(a, st);
   else hipLaunchKernelGGL((k_filt_rows<kDtF32>), dim3(a.n_slots), dim3(kThreads), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
