@@ -186,6 +186,58 @@ def test_filtered_heavy_ties_at_kth_value(n_tied):
     assert kept[0] >= n_tied
 
 
+def _redraw_tokens(inp, sp, seed):
+    """Draft tokens drawn again from the oracle's filtered q of the (edited) draft rows."""
+    dv = W.bf16_bits_to_f32(inp.draft).astype(np.float64)
+    rng = np.random.default_rng(seed)
+    V = inp.target.shape[1]
+    for r in range(inp.draft.shape[0]):
+        q = O.row_distribution(dv[r], sp).probs
+        inp.tokens[r] = int(rng.choice(V, p=q / q.sum()))
+
+
+@pytest.mark.parametrize("k,p", [(50, 0.9), (50, 1.0), (256, 1.0), (256, 0.95)])
+def test_filtered_spread_top_k_sets(k, p):
+    """Top-k sets whose values span more than 256 bf16 order keys (several octaves, or both
+    signs): the row kernel finds the threshold by the exact radix select and sums the masses
+    above each kept entry directly.  Requests 1 and 3 get a block of large logits (24-40) over
+    the N(0, 3^2) background; request 4's rows are all negative apart from ten at +2; with
+    k = 256 the top-k set holds more than 64 entries per row and each list more than 64
+    candidates.  Requests 0 and 2 keep ordinary rows; every request matches the oracle."""
+    sp = O.SamplingParams(0.7, k, p)
+    V = V_SMALL
+    inp = filtered_inputs(5, V, [4, 3, 5, 2, 4], sp, seed=60 + k)
+    rng = np.random.default_rng(k + int(p * 100))
+    n_big = 12 if k == 50 else 100
+    big = np.array([40.0, 36.0, 32.0, 28.0, 24.0], np.float32)
+
+    def rows_of(b):
+        c0, g = int(inp.cu_draft[b]), int(inp.gammas[b])
+        return ((inp.target, range(c0 + b, c0 + b + g + 1)), (inp.draft, range(c0, c0 + g)))
+
+    for b in (1, 3):
+        for arr, rows in rows_of(b):
+            for r in rows:
+                f = W.bf16_bits_to_f32(arr[r]).copy()
+                f[rng.choice(V, n_big, replace=False)] = rng.choice(big, n_big)
+                arr[r] = W.bf16_bits_from_f32(f)
+    for arr, rows in rows_of(4):
+        for r in rows:
+            f = -np.abs(W.bf16_bits_to_f32(arr[r]))
+            f[rng.choice(V, 10, replace=False)] = 2.0
+            arr[r] = W.bf16_bits_from_f32(f)
+    _redraw_tokens(inp, sp, 3)
+    gpu, _, _ = check(inp, sp)
+    assert not (gpu["status"] & L.STATUS["FILTER_OVERFLOW"]).any()
+
+
+def test_filtered_sampling_wide_vocabulary():
+    """V = 250,000: 31 candidate lists per bf16 row, the widest the row kernel holds."""
+    sp = O.SamplingParams(0.7, 50, 0.9)
+    inp = filtered_inputs(3, 250000, [2, 3, 1], sp, seed=71)
+    check(inp, sp)
+
+
 def test_filtered_nonfinite():
     sp = O.SamplingParams(0.7, 50, 0.9)
     inp = filtered_inputs(3, V_SMALL, [3, 3, 3], sp, seed=31)
@@ -304,6 +356,30 @@ def test_filtered_row_stats(dtype, k, p):
     ok = ref["topp_margin"] >= H.DECISION_EPS
     note(f"row stats dtype={dtype} k={k} p={p}: {int((~ok).sum())} rows excused")
     assert ok.sum() >= 8
+    assert np.array_equal(g["argmax"][ok], ref["argmax"][ok])
+    assert np.array_equal(g["kept_count"][ok], ref["kept_count"][ok])
+    for key in ("max_logit", "log_z", "entropy_bits", "max_prob"):
+        assert H.close(g[key][ok], ref[key][ok]), (key, H.max_rel(g[key][ok], ref[key][ok]))
+
+
+@pytest.mark.parametrize("V", [70000, 250000])
+def test_filtered_row_stats_list_counts(V):
+    """spec_row_stats on bf16 rows of 9 and 31 candidate lists (the row kernel's 16- and
+    32-list variants), ordinary rows and one whose top-k set spans both signs."""
+    rng = np.random.default_rng(V)
+    x = rng.standard_normal((5, V), dtype=np.float32) * 3
+    x[3] = -np.abs(x[3])
+    x[3, rng.choice(V, 10, replace=False)] = 2.0
+    x[4] = np.round(x[4] * 2) / 2
+    t, xf = _rows(x, "bf16")
+    sp = O.SamplingParams(0.7, 50, 0.9)
+    res = L.spec_row_stats(t, temperature=0.7, top_k=50, top_p=0.9, options=_opts())
+    torch.cuda.synchronize()
+    g = H.gpu_to_numpy(res)
+    ref = O.row_stats(xf, sp)
+    ok = ref["topp_margin"] >= H.DECISION_EPS
+    note(f"row stats V={V}: {int((~ok).sum())} rows excused")
+    assert ok.sum() >= 4
     assert np.array_equal(g["argmax"][ok], ref["argmax"][ok])
     assert np.array_equal(g["kept_count"][ok], ref["kept_count"][ok])
     for key in ("max_logit", "log_z", "entropy_bits", "max_prob"):
