@@ -91,6 +91,17 @@ __device__ __forceinline__ void block_scan2(int& a, int& b, SelLds& S, int& ta, 
 
 // ---------------------------------------------------------------- k_filt_slices
 
+// A bf16 list's candidate as one 32-bit word: the 16-bit order key of its value in the high
+// half (larger key, larger value; -0 and +0 share a key), bit 15 set, and its offset within the
+// list's 8192 logits (lists start at multiples of 8192) in the low 13 bits.
+__device__ __forceinline__ uint32_t list_word(float v, int x) {
+  uint32_t b = __float_as_uint(v) >> 16;
+  if (b == 0x8000u) b = 0u;
+  const uint32_t key = (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+  return (key << 16) | 0x8000u | ((uint32_t)x & 0x1FFFu);
+}
+
+
 // Candidates of one row's slice: the values at or above the slice's k-th largest, the ones
 // strictly above first.  Header {stored, total, threshold digits, flags}.
 // `v(j)` gives this thread's j-th logit of the list (j < N), `idx(j)` its token index.
@@ -128,7 +139,7 @@ __device__ void slice_candidates_g(const FilterArgs& a, SelLds& S, Get v, Idx id
   int og = ng, oe = ne, tg, te;
   block_scan2(og, oe, S, tg, te);
   const int cap = a.cap;
-  CandEntry* out = a.cand + ((int64_t)slot * a.n_l + l) * cap;
+  const int64_t lo = ((int64_t)slot * a.n_l + l) * cap;
 #pragma unroll U
   for (int j = 0; j < N; ++j) {
     const float x = v(j);
@@ -138,10 +149,14 @@ __device__ void slice_candidates_g(const FilterArgs& a, SelLds& S, Get v, Idx id
     if (all || h > th) pos = og++;
     else if (h == th) pos = tg + oe++;
     if (pos >= 0 && pos < cap) {
-      CandEntry c;
-      c.v = x;
-      c.x = idx(j);
-      out[pos] = c;
+      if constexpr (DT == kDtBF16) {
+        ((uint32_t*)a.cand)[lo + pos] = list_word(x, idx(j));
+      } else {
+        CandEntry c;
+        c.v = x;
+        c.x = idx(j);
+        a.cand[lo + pos] = c;
+      }
     }
   }
   if (t == 0) {
@@ -191,7 +206,7 @@ struct ListLds {
   int tau[2], fb[2];
   SelLds gen;              // the general select, for a list whose top k spread wider
   union {
-    CandEntry stage[2][kWaves][kStageW];      // each wave's candidates of each row, before the copy out
+    uint32_t stage[2][kWaves][kStageW];       // each wave's candidates of each row, before the copy out
     uint32_t raw[kPerThread][kThreads];       // the exact select's raw bf16 pairs, thread t's in column t
   };
 };
@@ -318,7 +333,7 @@ __device__ void list_candidates_bf16(const FilterArgs& a, ListLds& S, const RawS
   // candidates: the logits at or above the threshold value (NaN compares false; a +inf only
   // occurs in a flagged row), staged by each wave in its own region in one pass
   auto stage_row = [&](const RawSlice<kDtBF16> (&rw)[2], int r) {
-    CandEntry* st = S.stage[r][wave];
+    uint32_t* st = S.stage[r][wave];
     int run = 0;   // uniform over the wave
 #pragma unroll
     for (int j = 0; j < NE; ++j) {
@@ -328,12 +343,7 @@ __device__ void list_candidates_bf16(const FilterArgs& a, ListLds& S, const RawS
         if (__builtin_amdgcn_inverse_ballot_w64(mk)) {
           const int o = run + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(mk >> 32),
                                                             __builtin_amdgcn_mbcnt_lo((unsigned)mk, 0u));
-          if (o < kStageW) {
-            CandEntry c;
-            c.v = v;
-            c.x = list_index(base, t, j);
-            st[o] = c;
-          }
+          if (o < kStageW) st[o] = list_word(v, list_index(base, t, j));
         }
         run += __popcll(mk);
       }
@@ -361,7 +371,7 @@ __device__ void list_candidates_bf16(const FilterArgs& a, ListLds& S, const RawS
   for (int r = 0; r < 2; ++r) {
     if (r >= nrow || fb[r]) continue;
     const int slot = r == 0 ? slot_p : slot_q;
-    CandEntry* out = a.cand + ((int64_t)slot * a.n_l + l) * cap;
+    uint32_t* out = (uint32_t*)a.cand + ((int64_t)slot * a.n_l + l) * cap;
     for (int e = t; e < tot[r]; e += kThreads) {
       const int w = (e >= o1[r]) + (e >= o2[r]) + (e >= o3[r]);
       const int wo = w == 0 ? 0 : (w == 1 ? o1[r] : (w == 2 ? o2[r] : o3[r]));
@@ -540,6 +550,7 @@ __device__ __forceinline__ double block_sum_dd(double v, double* red) {
 // One row: global top-k over the slices' candidates, top-p, the kept set with probabilities.
 template <int DT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_filt_rows(FilterArgs a) {
+  static_assert(DT == kDtF32, "bf16 rows go to k_filt_rows_w (their lists hold 32-bit words)");
   constexpr int NP = DT == kDtBF16 ? 2 : 4;
   __shared__ RowLds L;
   const int t = threadIdx.x, lane = t & 63;
@@ -799,9 +810,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
 // ---------------------------------------------------------------- k_filt_rows_w (bf16 rows)
 
 // One wave per bf16 row, no workgroup barrier.  Entry `lane` of every candidate list (one list
-// per 8192 logits, at most 32) is read in one go into a register holding the entry's 16-bit
-// order key and its offset in the list; entries past 64 of a longer list are read from memory
-// at each pass.  The threshold is the same k-th largest key as in k_filt_rows.  When it lies
+// per 8192 logits, at most 32; one word per candidate: 16-bit order key, valid bit, offset in
+// the list) is read in one go into a register; entries past 64 of a longer list are read from
+// memory at each pass.  The threshold is the same k-th largest key as in k_filt_rows.  When it lies
 // within 256 keys of the row maximum (the usual case), the per-key counts that found it carry
 // the rest: equal keys are equal values with equal e-values, so the mass above a key (top-p),
 // Z, the entropy and every kept probability come from at most 256 keys, four per lane.  A
@@ -823,17 +834,6 @@ struct RowWLds {
   int kc[kWLists];         // kept entries per list, then their exclusive prefix
 };
 
-// A bf16-exact candidate as one word: its order key in the high half, bit 15 set, and its
-// offset within its list in the low 13 bits.  Zero is no candidate.
-__device__ __forceinline__ uint32_t cand_word(uint32_t vbits, uint32_t x) {
-  uint32_t b = vbits >> 16;
-  if (b == 0x8000u) b = 0u;
-  const uint32_t key = (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
-  uint32_t w = (key << 16) | 0x8000u | (x & 0x1FFFu);
-  asm volatile("" : "+v"(w));   // one register per candidate, not its two halves
-  return w;
-}
-
 template <int NL>
 __global__ __launch_bounds__(64) void k_filt_rows_w(FilterArgs a) {
   static_assert(NL <= kWLists, "a bf16 row has at most kWLists lists");
@@ -851,24 +851,25 @@ __global__ __launch_bounds__(64) void k_filt_rows_w(FilterArgs a) {
     return;
   }
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<CandEntry*>(a.cand + (int64_t)slot * n_l * cap), (short)0, n_l * cap * (int)sizeof(CandEntry),
-      0x00020000);
+      (uint32_t*)a.cand + (int64_t)slot * n_l * cap, (short)0, n_l * cap * 4, 0x00020000);
   // every load at once, unconditionally (past the row's lists the bounds check returns zeros
   // and reads nothing): list headers (lane s: list s) and entry `lane` of every list
   const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<CandHead*>(a.chead + (int64_t)slot * n_l), (short)0, n_l * (int)sizeof(CandHead), 0x00020000);
   const auto hv = __builtin_amdgcn_raw_buffer_load_b128(rh, lane * (int)sizeof(CandHead), 0, 0);
-  using u32x2 = decltype(__builtin_amdgcn_raw_buffer_load_b64(rs, 0, 0, 0));
-  u32x2 raw[NL];
-#pragma unroll
-  for (int s = 0; s < NL; ++s) raw[s] = __builtin_amdgcn_raw_buffer_load_b64(rs, (s * cap + lane) * 8, 0, 0);
-  CandHead h;   // zeros past the row's lists
-  h.stored = (int)hv[0]; h.total = (int)hv[1]; h.th = hv[2]; h.flags = (int)hv[3];
   uint32_t w[NL];
 #pragma unroll
+  for (int s = 0; s < NL; ++s) w[s] = __builtin_amdgcn_raw_buffer_load_b32(rs, (s * cap + lane) * 4, 0, 0);
+  CandHead h;   // zeros past the row's lists
+  h.stored = (int)hv[0]; h.total = (int)hv[1]; h.th = hv[2]; h.flags = (int)hv[3];
+  // opaque moves: every load is issued unconditionally before the first wait, and each word
+  // stays one register rather than its key and offset apart
+#pragma unroll
+  for (int s = 0; s < NL; ++s) asm volatile("" : "+v"(w[s]));
+#pragma unroll
   for (int s = 0; s < NL; ++s) {
-    const uint32_t cw = cand_word(raw[s][0], raw[s][1]);
-    w[s] = lane < __builtin_amdgcn_readlane(h.stored, s) ? cw : 0u;
+    w[s] = lane < __builtin_amdgcn_readlane(h.stored, s) ? w[s] : 0u;
+    asm volatile("" : "+v"(w[s]));
   }
   const int bad = wave_or(h.flags & kFlagBad);
   const bool extra = wave_or(h.stored > 64 ? 1 : 0) != 0;
@@ -881,8 +882,7 @@ __global__ __launch_bounds__(64) void k_filt_rows_w(FilterArgs a) {
         if (extra) {
           const int cs = __builtin_amdgcn_readlane(h.stored, s);
           for (int e0 = 64; e0 < cs; e0 += 64) {
-            const auto e = __builtin_amdgcn_raw_buffer_load_b64(rs, (s * cap + e0 + lane) * 8, 0, 0);
-            cb(cand_word(e[0], e[1]), e0 + lane < cs, s);
+            cb(__builtin_amdgcn_raw_buffer_load_b32(rs, (s * cap + e0 + lane) * 4, 0, 0), e0 + lane < cs, s);
           }
         }
       }

@@ -225,7 +225,7 @@ struct FilterArgs {
   float top_p;
   double c, inv_t;        // c = log2(e) / T
   uint64_t seed, step;
-  CandEntry* cand;        // [n_slots][n_l][cap] (sized for n_s lists)
+  CandEntry* cand;        // [n_slots][n_l][cap] (sized for n_s lists); a bf16 list holds one 32-bit word per entry
   CandHead* chead;        // [n_slots][n_l] (sized for n_s)
   KeptEntry* kept;        // [n_slots][kKeepMax]
   RowStat2* rstat;        // [n_slots]
