@@ -159,7 +159,7 @@ size_t fused_bytes(int64_t n_teams, int V) {
   const int64_t ns = n_chunks(V);
   return kHeaderBytes + align_up((size_t)(n_teams * ns * 2) * fused_record_bytes()) +
          align_up((size_t)(n_teams * ns * 4) * sizeof(uint64_t)) + align_up((size_t)(n_teams * kMaxMembers) * 4) +
-         align_up((size_t)n_teams * sizeof(int32_t)) + align_up((size_t)n_teams * 2 * sizeof(float));
+         align_up((size_t)n_teams * 2 * sizeof(float));
 }
 
 // Tags of the fused kernel's workspace records: one per call, unique within the process,
@@ -437,12 +437,9 @@ int spec_verify_batch_ex(int B, int V, int gamma_max, spec_dtype dt, const void*
     f.part = cv.take<uint64_t>((size_t)f.n_teams * ns * 2 * fused_record_bytes());
     f.smass = cv.take<uint64_t>((size_t)f.n_teams * ns * 4 * sizeof(uint64_t));
     f.arrive = cv.take<uint32_t>((size_t)f.n_teams * kMaxMembers * sizeof(uint32_t));
-    {
-      // every request has G draft rows exactly when the rows number B G (a valid offset array
-      // has no request above G): then a team's rows follow from its place, else from a map
-      int32_t* tmap = cv.take<int32_t>((size_t)f.n_teams * sizeof(int32_t));
-      f.team_row = (int64_t)n_draft_rows == (int64_t)B * gamma_max ? nullptr : tmap;
-    }
+    // every request has G draft rows exactly when the rows number B G (a valid offset array
+    // has no request above G): then a team's rows follow from its place
+    f.ragged = (int64_t)n_draft_rows == (int64_t)B * gamma_max ? 0 : 1;
     f.ylog = cv.take<float>((size_t)f.n_teams * 2 * sizeof(float));
     f.poll_delay = op.poll_delay;
     {

@@ -1005,6 +1005,7 @@ struct FusedLds {
   int tst;                  // team status: 0 ok, 1 non-finite row, 2 wait gave up
   int bad[kWaves];
   int amax[2][kWaves];
+  int req;                  // ragged batches: the request of this place's draft row
 };
 
 // The lane that publishes a workgroup's records: lane 0 of the last wave (wave 0 polls).
@@ -1203,7 +1204,7 @@ __device__ __forceinline__ float residual_slice(const ResidualScale& R, const fl
 // wait in LDS); other layouts keep the compiler's choice.
 constexpr int fused_min_waves(int dt, bool vec) { return dt == kDtBF16 && vec ? 8 : 1; }
 
-template <int DT, bool VEC, int MODE, bool TENT>
+template <int DT, bool VEC, int MODE, bool TENT, bool RAG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_min_waves(DT, VEC)))) void k_fused(
     FusedArgs a) {
   __shared__ FusedLds L;
@@ -1226,13 +1227,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_
   int r = ti;   // target row
   bool pair = false;
   int drow = -1;
-  if (MODE == kFuSample && a.team_row) {
-    // a ragged batch: the row of this dispatch place comes from the map (an invalid offset
-    // array, which the finalize kernel reports, can only give rows that are range-checked here)
-    r = sload_i32(a.team_row + ti);
-    if (r < 0 || r >= a.n_teams) return;
+  if (MODE == kFuSample && RAG) {
+    // a ragged batch: draft row d belongs to request b = #{b' in 1..B : cu[b'] <= d} (the offsets
+    // ascend), counted by ballots over bounds-checked loads of the whole offset array, all at
+    // once; a bonus place reads its request's end offset.  An invalid offset array (the finalize
+    // kernel reports it) can only give rows that are range-checked here.
     pair = ti < a.n_draft_rows;
     drow = pair ? ti : -1;
+    if (pair) {
+      // wave 0 counts (the loads the batch needs, all at once); the others take its count
+      if (wave == 0) {
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.cu), (short)0,
+                                                                           (a.B + 1) * 4, 0x00020000);
+        int cnt = 0;
+#pragma unroll 1
+        for (int k0 = 0; k0 < a.B; k0 += 256) {   // 256 offsets per round (one round up to B = 256)
+          int cv[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) cv[k] = (int)__builtin_amdgcn_raw_buffer_load_b32(rc, (1 + k0 + 64 * k + lane) * 4, 0, 0);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) cnt += __popcll(__ballot(1 + k0 + 64 * k + lane <= a.B && cv[k] <= ti));
+        }
+        if (lane == 0) L.req = min(cnt, a.B - 1);
+      }
+      __syncthreads();
+      r = ti + __builtin_amdgcn_readfirstlane(L.req);
+    } else {
+      const int b = ti - a.n_draft_rows;
+      r = sload_i32(a.cu + b + 1) + b;
+    }
+    if (r < 0 || r >= a.n_teams) return;
     if (VEC) {
       const __amdgpu_buffer_rsrc_t rs = row_rsrc(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V * kEsz);
       load_raw_buf<DT>(rs, base, rp[0]);
@@ -1479,18 +1503,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_
   }
 }
 
-// The target row of every dispatch place of a ragged batch: places 0 .. n_draft_rows - 1 are
-// the draft rows (row d of request b pairs with target row d + b), then one place per request
-// for its bonus row (cu[b + 1] + b).  An offset pair that is not a valid range writes nothing.
-__global__ __launch_bounds__(kThreads) void k_team_map(FusedArgs a) {
-  const int b = blockIdx.x * kThreads + threadIdx.x;
-  if (b >= a.B) return;
-  const int c0 = a.cu[b], c1 = a.cu[b + 1];
-  if (c0 < 0 || c1 < c0 || c1 > a.n_draft_rows || c1 - c0 > a.G) return;
-  for (int d = c0; d < c1; ++d) a.team_row[d] = d + b;
-  a.team_row[a.n_draft_rows + b] = c1 + b;
-}
-
 // One workgroup per request, after the streaming kernel: every record is in place.
 template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void k_fused_finalize(FusedArgs a) {
@@ -1505,16 +1517,17 @@ static hipError_t launch_fused_t(FusedArgs a, hipStream_t st, hipEvent_t ev0, hi
   const int teams8 = (a.n_teams + 7) / 8;
   const long long grid = 8ll * teams8 * ((a.n_s + 1) / 2);
   if (grid < 1 || grid > 0x7fffffffll) return hipErrorInvalidConfiguration;
-  if (MODE == kFuSample && a.team_row) {
-    hipLaunchKernelGGL(k_team_map, dim3((unsigned)((a.B + kThreads - 1) / kThreads)), dim3(kThreads), 0, st, a);
-    const hipError_t e0 = hipGetLastError();
-    if (e0 != hipSuccess) return e0;
-  }
   // optional events bracket the streaming kernel alone (benchmark timing)
-  if (MODE != kFuGreedy && a.want_t_ent)
-    launch_timed(k_fused<DT, VEC, MODE, true>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
-  else
-    launch_timed(k_fused<DT, VEC, MODE, false>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
+  // ragged sampling batches find each place's request among the offsets (a kernel of their own,
+  // so that the uniform kernel keeps its registers)
+  const bool rag = MODE == kFuSample && a.ragged;
+  if (MODE != kFuGreedy && a.want_t_ent) {
+    if (rag) launch_timed(k_fused<DT, VEC, MODE, true, true>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
+    else launch_timed(k_fused<DT, VEC, MODE, true, false>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
+  } else {
+    if (rag) launch_timed(k_fused<DT, VEC, MODE, false, true>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
+    else launch_timed(k_fused<DT, VEC, MODE, false, false>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_fused_finalize<DT, VEC, MODE>), dim3(a.B), dim3(kThreads), 0, st, a);

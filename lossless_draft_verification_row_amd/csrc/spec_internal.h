@@ -141,8 +141,8 @@ struct FusedArgs {
   uint64_t* smass;      // [n_teams][n_s][4 waves] tagged residual masses
   uint32_t* arrive;     // [n_teams][kMaxMembers] a member's flag: the call's tag once its records are out
   float* ylog;          // [n_draft_rows][2]: each draft token's logit in its target and draft row
-  int32_t* team_row;    // [n_teams]: the target row of the team in each dispatch place, for ragged
-                        // batches (written by k_team_map); nullptr when every request has G drafts
+  int ragged;           // 1 unless every request has G draft rows: a dispatch place then finds its
+                        // request among the offsets instead of from its place
   int poll_delay;       // wait before the first team poll, in 10 ns ticks
   int tail_wgs;         // the launch's last generation (one workgroup per resident slot), which
                         // waits half the poll delay

@@ -74,7 +74,6 @@ hipError_t launch_fused(const FusedArgs& a, int, int, hipStream_t, hipEvent_t, h
   carved("fused records", a.part, (size_t)a.n_teams * a.n_s * 2 * 16);
   carved("fused residual masses", a.smass, (size_t)a.n_teams * a.n_s * 4 * sizeof(uint64_t));
   carved("fused arrival flags", a.arrive, (size_t)a.n_teams * kMaxMembers * sizeof(uint32_t));
-  if (a.team_row) carved("fused team map", a.team_row, (size_t)a.n_teams * sizeof(int32_t));
   carved("fused token logits", a.ylog, (size_t)a.n_teams * 2 * sizeof(float));
   return hipSuccess;
 }
