@@ -288,17 +288,18 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   const double cd = (double)a.c;
   const __amdgpu_buffer_rsrc_t rrs = rec_rsrc(a);
   // Every load of the request goes out before anything waits, at the guess c0 = b G, g = G
-  // (exact when every request has G draft tokens): the first two teams of each wave, the draft
+  // (exact when every request has G draft tokens): the first three teams of each wave, the draft
   // tokens and (sampling) their logits kept by the streaming kernel, the request's offsets and
   // the whole offset array.  A wrong guess loads the request's part again.
   const int cg = b * a.G;
   const bool guess_in = cg + a.G <= a.n_draft_rows;
-  TeamRaw pre[2];
+  TeamRaw pre[3];   // teams wave, wave + 4 and (gamma >= 8) wave + 8
   int ytok = -1;
   float ly_p = 0.f, ly_q = 0.f;
   if (guess_in) {
     pre[0] = team_load<MODE>(a, rrs, cg, b, a.G, wave);
     pre[1] = team_load<MODE>(a, rrs, cg, b, a.G, wave + kWaves);
+    pre[2] = team_load<MODE>(a, rrs, cg, b, a.G, wave + 2 * kWaves);
     if (t < a.G) {
       ytok = a.tokens[cg + t];
       if (MODE == kFuSample) { ly_p = a.ylog[2 * (cg + t)]; ly_q = a.ylog[2 * (cg + t) + 1]; }
@@ -328,6 +329,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   if (!(guess_in && c0 == cg && g == a.G)) {
     pre[0] = team_load<MODE>(a, rrs, c0, b, g, wave);
     pre[1] = team_load<MODE>(a, rrs, c0, b, g, wave + kWaves);
+    pre[2] = team_load<MODE>(a, rrs, c0, b, g, wave + 2 * kWaves);
     ytok = t < g ? a.tokens[c0 + t] : -1;
     if (MODE == kFuSample && t < g) { ly_p = a.ylog[2 * (c0 + t)]; ly_q = a.ylog[2 * (c0 + t) + 1]; }
   }
@@ -365,7 +367,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   for (int ti = wave, it = 0; ti <= g; ti += 2 * kWaves, it += 2) {
     const int tt[2] = {ti, ti + kWaves};
     TeamRaw R[2];
-    R[0] = it == 0 ? pre[0] : team_load<MODE>(a, rrs, c0, b, g, tt[0]);
+    R[0] = it == 0 ? pre[0] : (it == 2 ? pre[2] : team_load<MODE>(a, rrs, c0, b, g, tt[0]));
     R[1] = it == 0 ? pre[1] : team_load<MODE>(a, rrs, c0, b, g, tt[1]);
     // rows 2j (p) and 2j + 1 (q) of team j
     float ref[4], s[4], w[4];
