@@ -235,6 +235,20 @@ def filtered_draft_tokens(inp, seed=77):
 OUTPUTS_PER_POSITION = ("p_y", "q_y", "one_minus_tv", "draft_entropy_bits", "draft_max_prob")
 
 
+def kernel_source_digest(kernel):
+    """First 16 hex digits of the sha256 over the kernel's source file and the two headers every
+    kernel includes, in that order: a profile is current only while all three are unchanged."""
+    import hashlib
+    csrc = os.path.join(ROOT, "lossless_draft_verification_row_amd", "csrc")
+    src = {"k_fused": "spec_fused.hip", "k_filt_slices": "spec_filter.hip",
+           "k_head": "spec_head.hip"}.get(kernel, "spec_kernels.hip")
+    h = hashlib.sha256()
+    for name in (src, "spec_device.h", "spec_internal.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def load_traffic(kernel):
     """The committed rocprofv3 counter summary of the kernel (HBM bytes and VALU instructions
     per launch), if it was taken on the current kernel source."""
@@ -244,12 +258,7 @@ def load_traffic(kernel):
     try:
         with open(path) as f:
             rec = json.load(f)
-        import hashlib
-        src = os.path.join(ROOT, "lossless_draft_verification_row_amd", "csrc",
-                           {"k_fused": "spec_fused.hip", "k_filt_slices": "spec_filter.hip",
-                            "k_head": "spec_head.hip"}.get(kernel, "spec_kernels.hip"))
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-        if rec.get("kernel_source_sha") != h:
+        if rec.get("kernel_source_sha") != kernel_source_digest(kernel):
             return None
         return rec
     except Exception:

@@ -51,6 +51,13 @@ __device__ __forceinline__ int slice_index(int base, int t, int j) {
   else return base + 4 * (t + kThreads * (j >> 2)) + (j & 3);
 }
 
+// 16 bytes of a logit row read once: a non-temporal load (the streaming passes' policy).
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 w = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Load this thread's 16 logits of one slice; indices >= V read as -inf.
 template <int DT, bool VEC>
 __device__ __forceinline__ void load_slice(const void* row, int V, int base, float (&v)[kPerThread]) {
@@ -61,7 +68,7 @@ __device__ __forceinline__ void load_slice(const void* row, int V, int base, flo
     for (int k = 0; k < 2; ++k) {
       const int e0 = base + 8 * (t + kThreads * k);
       if (VEC && e0 + 8 <= V) {
-        const uint4 x = *(const uint4*)(r + e0);
+        const uint4 x = ld_nt16(r + e0);
         v[8 * k + 0] = bf16_lo(x.x); v[8 * k + 1] = bf16_hi(x.x);
         v[8 * k + 2] = bf16_lo(x.y); v[8 * k + 3] = bf16_hi(x.y);
         v[8 * k + 4] = bf16_lo(x.z); v[8 * k + 5] = bf16_hi(x.z);
@@ -77,7 +84,8 @@ __device__ __forceinline__ void load_slice(const void* row, int V, int base, flo
     for (int k = 0; k < 4; ++k) {
       const int e0 = base + 4 * (t + kThreads * k);
       if (VEC && e0 + 4 <= V) {
-        const float4 x = *(const float4*)(r + e0);
+        const uint4 xw = ld_nt16(r + e0);
+        const float4 x = make_float4(__uint_as_float(xw.x), __uint_as_float(xw.y), __uint_as_float(xw.z), __uint_as_float(xw.w));
         v[4 * k + 0] = x.x; v[4 * k + 1] = x.y; v[4 * k + 2] = x.z; v[4 * k + 3] = x.w;
       } else {
 #pragma unroll
@@ -105,7 +113,7 @@ __device__ __forceinline__ void load_raw(const void* row, int V, int base, RawSl
     for (int k = 0; k < 2; ++k) {
       const int e0 = base + 8 * (t + kThreads * k);
       if (VEC && e0 + 8 <= V) {
-        const uint4 x = *(const uint4*)(p + e0);
+        const uint4 x = ld_nt16(p + e0);
         r.w[4 * k + 0] = x.x; r.w[4 * k + 1] = x.y; r.w[4 * k + 2] = x.z; r.w[4 * k + 3] = x.w;
       } else {
 #pragma unroll
@@ -122,7 +130,7 @@ __device__ __forceinline__ void load_raw(const void* row, int V, int base, RawSl
     for (int k = 0; k < 4; ++k) {
       const int e0 = base + 4 * (t + kThreads * k);
       if (VEC && e0 + 4 <= V) {
-        const uint4 x = *(const uint4*)(p + e0);
+        const uint4 x = ld_nt16(p + e0);
         r.w[4 * k + 0] = x.x; r.w[4 * k + 1] = x.y; r.w[4 * k + 2] = x.z; r.w[4 * k + 3] = x.w;
       } else {
 #pragma unroll
@@ -516,7 +524,10 @@ __device__ __forceinline__ int wave_pick(double m, int n, double u, double& tota
 // ---------------------------------------------------------------- bounds-checked row loads
 
 // Bounds-checked row loads: a buffer resource over the row's bytes.  16-byte loads past the
-// end return zeros and touch no memory (num_records 0 turns every load off).
+// end return zeros and touch no memory (num_records 0 turns every load off).  The streaming
+// loads are non-temporal (the nt cache policy): each logit is read once, and marking the lines
+// for early eviction raises the read rate the HBM sustains (a plain 1 GiB read: 5.8 -> 6.6 TB/s).
+constexpr int kCpolNt = 2;   // cache-policy bits of a buffer load: non-temporal
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, int nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, nbytes, 0x00020000);
 }
@@ -528,7 +539,7 @@ __device__ __forceinline__ void load_raw_buf(__amdgpu_buffer_rsrc_t rs, int base
 #pragma unroll
   for (int k = 0; k < kPerThread / kEl; ++k) {
     const int e0 = base + kEl * (t + kThreads * k);
-    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, e0 * kEsz, 0, 0);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, e0 * kEsz, 0, kCpolNt);
     r.w[4 * k + 0] = x[0]; r.w[4 * k + 1] = x[1]; r.w[4 * k + 2] = x[2]; r.w[4 * k + 3] = x[3];
   }
 }

@@ -100,7 +100,7 @@ __device__ __forceinline__ void for_row(const void* row, int V, F f) {
     const int nv = V / kEl;
 #pragma unroll 4
     for (int i = t; i < nv; i += kThreads) {
-      const uint4 w = ((const uint4*)row)[i];
+      const uint4 w = ld_nt16((const uint4*)row + i);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -1178,9 +1178,9 @@ hipError_t launch_select_gamma(int B, const float* req_stats, const float* comp,
 // ---------------------------------------------------------------- streaming-read ceiling
 
 // A plain read of n 16-byte words, for the benchmark's roofline context: workgroup g reads the
-// 64 KB chunk g, every thread 16 words 256 apart, all in flight at once, and XORs them.  The
-// XOR is stored only when it equals a fixed word, so the loads cannot be dropped while the
-// kernel writes next to nothing.
+// 64 KB chunk g, every thread 16 words 256 apart, all in flight at once (non-temporal, like the
+// streaming kernels' logit loads), and XORs them.  The XOR is stored only when it equals a fixed
+// word, so the loads cannot be dropped while the kernel writes next to nothing.
 constexpr int kStreamLoads = 16;
 constexpr int kStreamChunkWords = kStreamLoads * kThreads;   // 64 KB
 __global__ __launch_bounds__(kThreads) void k_stream_read(const uint4* __restrict__ p, int64_t n, uint32_t* sink) {
@@ -1189,7 +1189,10 @@ __global__ __launch_bounds__(kThreads) void k_stream_read(const uint4* __restric
 #pragma unroll
   for (int k = 0; k < kStreamLoads; ++k) {
     const int64_t i = base + (int64_t)k * kThreads;
-    v[k] = i < n ? p[i] : make_uint4(0u, 0u, 0u, 0u);
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (i < n) w = __builtin_nontemporal_load((const u32x4*)&p[i]);
+    v[k] = make_uint4(w[0], w[1], w[2], w[3]);
   }
   uint32_t x = 0;
 #pragma unroll
