@@ -100,6 +100,16 @@ def test_dense_bf16_ragged(V, path):
     check(inp, O.SamplingParams(1.0), path=path)
 
 
+def test_ragged_batch_of_many_requests():
+    """A ragged batch of 600 requests (drafts 0..8 each): the streaming kernel finds each draft
+    row's request among the 601 offsets in three rounds of 256; every request against the
+    oracle."""
+    rng = np.random.default_rng(600)
+    gammas = rng.integers(0, 9, 600).tolist()
+    inp = custom_inputs(600, 2 * 4096 + 40, gammas, T=1.0, seed=601)
+    check(inp, O.SamplingParams(1.0))
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_dense_bf16_temperature(path):
     inp = custom_inputs(6, 3 * 4096 + 300, [2, 4, 6, 8, 1, 3], tau=1.5, T=0.7, seed=3)
