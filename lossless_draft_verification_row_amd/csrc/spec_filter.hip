@@ -91,14 +91,12 @@ __device__ __forceinline__ void block_scan2(int& a, int& b, SelLds& S, int& ta, 
 
 // ---------------------------------------------------------------- k_filt_slices
 
-// A bf16 list's candidate as one 32-bit word: the 16-bit order key of its value in the high
-// half (larger key, larger value; -0 and +0 share a key), bit 15 set, and its offset within the
-// list's 8192 logits (lists start at multiples of 8192) in the low 13 bits.
+// A bf16 list's candidate as one 32-bit word: the raw bf16 bits of its value in the high half,
+// bit 15 set, and its offset within the list's 8192 logits (lists start at multiples of 8192)
+// in the low 13 bits.  The row kernel turns the bits into an order key; the streaming kernel,
+// where a candidate's word takes whole issue slots for a few lanes, only ORs the parts.
 __device__ __forceinline__ uint32_t list_word(float v, int x) {
-  uint32_t b = __float_as_uint(v) >> 16;
-  if (b == 0x8000u) b = 0u;
-  const uint32_t key = (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
-  return (key << 16) | 0x8000u | ((uint32_t)x & 0x1FFFu);
+  return __float_as_uint(v) | 0x8000u | ((uint32_t)x & 0x1FFFu);
 }
 
 
@@ -343,7 +341,7 @@ __device__ void list_candidates_bf16(const FilterArgs& a, ListLds& S, const RawS
         if (__builtin_amdgcn_inverse_ballot_w64(mk)) {
           const int o = run + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(mk >> 32),
                                                             __builtin_amdgcn_mbcnt_lo((unsigned)mk, 0u));
-          if (o < kStageW) st[o] = list_word(v, list_index(base, t, j));
+          if (o < kStageW) st[o] = __float_as_uint(v) | 0x8000u | (uint32_t)list_index(0, t, j);   // list_word
         }
         run += __popcll(mk);
       }
@@ -810,9 +808,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
 // ---------------------------------------------------------------- k_filt_rows_w (bf16 rows)
 
 // One wave per bf16 row, no workgroup barrier.  Entry `lane` of every candidate list (one list
-// per 8192 logits, at most 32; one word per candidate: 16-bit order key, valid bit, offset in
-// the list) is read in one go into a register; entries past 64 of a longer list are read from
-// memory at each pass.  The threshold is the same k-th largest key as in k_filt_rows.  When it lies
+// per 8192 logits, at most 32; one word per candidate: raw bf16 bits, valid bit, offset in the
+// list) is read in one go into a register, its bits turned into their order key; entries past
+// 64 of a longer list are read from memory at each pass.  The threshold is the same k-th largest key as in k_filt_rows.  When it lies
 // within 256 keys of the row maximum (the usual case), the per-key counts that found it carry
 // the rest: equal keys are equal values with equal e-values, so the mass above a key (top-p),
 // Z, the entropy and every kept probability come from at most 256 keys, four per lane.  A
@@ -821,6 +819,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
 // index range, so an entry's place is the kept entries of the lists before its own plus those
 // of its own list below it.
 constexpr int kWLists = kMaxSlicesFused / 2;
+
+// A list word with its raw bf16 bits replaced by their 16-bit order key (larger key, larger
+// value; -0 and +0 share a key); offset and valid bit unchanged.
+__device__ __forceinline__ uint32_t key_word(uint32_t w) {
+  uint32_t b = w >> 16;
+  if (b == 0x8000u) b = 0u;
+  const uint32_t key = (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+  return (key << 16) | (w & 0xFFFFu);
+}
 
 struct RowWLds {
   union {
@@ -868,7 +875,7 @@ __global__ __launch_bounds__(64) void k_filt_rows_w(FilterArgs a) {
   for (int s = 0; s < NL; ++s) asm volatile("" : "+v"(w[s]));
 #pragma unroll
   for (int s = 0; s < NL; ++s) {
-    w[s] = lane < __builtin_amdgcn_readlane(h.stored, s) ? w[s] : 0u;
+    w[s] = lane < __builtin_amdgcn_readlane(h.stored, s) ? key_word(w[s]) : 0u;
     asm volatile("" : "+v"(w[s]));
   }
   const int bad = wave_or(h.flags & kFlagBad);
@@ -882,7 +889,7 @@ __global__ __launch_bounds__(64) void k_filt_rows_w(FilterArgs a) {
         if (extra) {
           const int cs = __builtin_amdgcn_readlane(h.stored, s);
           for (int e0 = 64; e0 < cs; e0 += 64) {
-            cb(__builtin_amdgcn_raw_buffer_load_b32(rs, (s * cap + e0 + lane) * 4, 0, 0), e0 + lane < cs, s);
+            cb(key_word(__builtin_amdgcn_raw_buffer_load_b32(rs, (s * cap + e0 + lane) * 4, 0, 0)), e0 + lane < cs, s);
           }
         }
       }
