@@ -3,22 +3,26 @@
 // With top-k on (1 <= k <= 256), every filtered distribution lives on the k largest logits of
 // its row (ties at the boundary kept, reading R1 of the oracle), so after one streaming pass the
 // whole method runs on small sparse sets:
-//   k_filt_slices   one workgroup per 4096-logit slice of a target row and, for a paired
-//                   position, the same slice of its draft row: the slice's own k-th largest
-//                   value by a two- (bf16) or four-pass (fp32) radix select over order keys in
-//                   an LDS histogram, then every logit at or above it written out as a candidate
-//                   (value, index).  Each needed logit is read once; nothing waits on another
-//                   workgroup.
-//   k_filt_rows     one workgroup per row: the row's k-th largest among its slices' candidates
-//                   (the same select), the top-k set K, top-p on the renormalised K by pairwise
-//                   masses (no sort), the kept set S with p = e / Z_S in fp64, entropy in bits,
-//                   max probability, log Z (guide page "5.1 投机解码核心原理" §2.1: p and q are
-//                   the distributions after temperature, top-k, top-p; SpecKV page signals).
+//   k_filt_slices   one workgroup per candidate list: two 4096-logit chunks of a bf16 target row
+//                   (one chunk of an fp32 row) and, for a paired position, the same chunks of its
+//                   draft row.  The list's threshold is the k-th largest of its 256 per-thread
+//                   maxima (an LDS histogram; an exact radix select over the list when they
+//                   spread wider); every logit at or above it is a candidate, written as one
+//                   32-bit word (bf16: raw bits, valid bit, offset in the list) or a
+//                   {value, index} pair (fp32).  Each needed logit is read once; nothing waits
+//                   on another workgroup.
+//   k_filt_rows_w   bf16 rows, one wave per row: the row's k-th largest among its lists'
+//                   candidates, the top-k set K, top-p on the renormalised K from per-key counts
+//                   (or pairwise masses when K spreads wider), the kept set S with p = e / Z_S in
+//                   fp64 in index order, entropy in bits, max probability, log Z (guide page
+//                   "5.1 投机解码核心原理" §2.1: p and q are the distributions after temperature,
+//                   top-k, top-p; SpecKV page signals).  k_filt_rows does the same for fp32
+//                   rows, one workgroup per row.
 //   k_filt_finalize one workgroup per request: p(y), q(y), 1 - TV = sum min(p, q) (§4.1, §4.3),
 //                   the accept scan (§3.2, §5.1) and the three-level sampler over the residual
 //                   [p - q]_+ or p_{g+1} (§3.2, §5.2) on the sparse kept sets, with the
 //                   sampler's sequential fp64 sums taken in index order.
-// A slice keeps at most `cap` candidates, those strictly above its threshold first; if it had
+// A list keeps at most `cap` candidates, those strictly above its threshold first; if it had
 // to drop ties that the row's own threshold would keep, or a row's top-k set exceeds kKeepMax,
 // the request (or plain row) is listed for the dense threshold path, which recomputes all its
 // outputs after these kernels (spec_kernels.hip, k_fb_rows and k_fb_requests / k_fb_residual).

@@ -1,15 +1,17 @@
 // spec_fused.hip -- a whole verification round in two kernels: k_fused streams every needed
 // logit once; k_fused_finalize (one workgroup per request) turns the records into outputs.
 //
-// Work unit ("ticket"): one 4096-logit slice of one target row, together with the same slice
-// of its draft row when that position pairs the two (guide page "5.1 投机解码核心原理", §3.2:
-// the residual needs p and q at the same token).  The slices of one target row form a team.
-// k_fused runs one workgroup per ticket; workgroup i lands on XCD i mod 8 (the dispatcher deals
-// workgroups round-robin over the XCDs) and the slices of team r are consecutive workgroups of
-// XCD r mod 8.
+// Work unit ("ticket"): two consecutive 4096-logit slices of one target row, together with the
+// same slices of its draft row when that position pairs the two (guide page "5.1 投机解码核心
+// 原理", §3.2: the residual needs p and q at the same token).  The tickets of one target row
+// form a team.  k_fused runs one workgroup per ticket; workgroup i lands on XCD i mod 8 (the
+// dispatcher deals workgroups round-robin over the XCDs) and the tickets of the team in
+// dispatch place ti are consecutive workgroups of XCD ti mod 8.  A place's rows follow from
+// the place in a uniform batch and from the draft offsets (one search per workgroup) in a
+// ragged one.
 //
 // Per ticket:
-//   1. load the slice(s) into registers (bounds-checked buffer loads); per wave, max and
+//   1. load the slices into registers (bounds-checked, non-temporal buffer loads); per wave, max and
 //      e = exp2(l c - ref_w), ref_w = max * c, sums; fold the waves into one record per row
 //      (ref, sum e, sum e t) and publish it, then an arrival flag;
 //   2. paired positions: wait for the team's arrival flags, combine the team's records in
