@@ -91,6 +91,32 @@ def stream_ceiling(torch, L, steps=20):
     return {"kernel": "k_stream_read (spec_stream_read) over 1 GiB", "GBps": gbs, "frac": gbs / HBM_PEAK_GBS}
 
 
+def mfma_ceiling(torch, L, reps=5):
+    """Context for the matrix roofline: the library's register-operand MFMA kernel
+    (spec_mfma_rate) on the head's 4 x 4 accumulator pattern, 1280 workgroups x 4 waves x 2048
+    steps x 16 MFMAs, with constant operands and with random operands that change every step;
+    TFLOP/s and the fraction of the dense bf16 peak, timed with events on the kernel's stream."""
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    wgs, iters = 1280, 2048
+    flops = wgs * 4 * iters * 16 * 2.0 * 32 * 32 * 16
+    out = {"kernel": "k_mfma_rate (spec_mfma_rate), 16 independent 32x32x16 bf16 MFMAs per step, "
+                     "register operands, no memory traffic"}
+    for mode, name in ((0, "constant_operands"), (2, "random_operands")):
+        for _ in range(2):
+            L.spec_mfma_rate(mode, iters, wgs, sink)
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in pairs:
+            a.record()
+            L.spec_mfma_rate(mode, iters, wgs, sink)
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in pairs]))
+        tf = flops / (ms * 1e-3) / 1e12
+        out[name] = {"TFLOPs": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS}
+    return out
+
+
 class HipEvents:
     """Raw hipEvent_t pairs, handed to the library in a call's options: the dispatch of the
     call's streaming kernel records them at its start and end.  Destroyed before the process
@@ -317,7 +343,10 @@ def lm_head_bench(args, L, W, torch):
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": counters.get("bytes_per_launch"),
                      "kernel_ms_avg": kms,
                      "head_read_GBps": V * D * 2 / (kms * 1e-3) / 1e9},
+        "mfma_ceiling": mfma_ceiling(torch, L),
     }
+    ceil = line["mfma_ceiling"]["random_operands"]["TFLOPs"]
+    line["roofline"]["frac_of_random_operand_ceiling"] = achieved / ceil
     if not args.no_cpu_baseline:
         from oracle import spec_oracle as O
         rows = 0

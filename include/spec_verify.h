@@ -327,6 +327,19 @@ int spec_select_gamma(int B, const float* req_stats, const float* comp, spec_gam
  * SPEC_ERR_LAUNCH. */
 int spec_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* hip_stream);
 
+/* Benchmark instrumentation, not a verification step: the matrix cores' sustained bf16 rate on
+ * the fused LM head's pattern, the practical counterpart of the dense MFMA peak that a benchmark
+ * reports beside the head's rate.  `workgroups` workgroups of four waves (one wave per SIMD)
+ * each issue `iters` steps of 16 independent 32x32x16 bf16 MFMAs (2^19 flop each) on register
+ * operands, with no memory traffic: mode 0 all operands 1.0; mode 1 random bf16 operands of
+ * normal magnitude, the same every step; mode 2 the random operands with mantissa bits flipped
+ * every step.  Modes 1 and 2 show how the rate depends on the data the multipliers see.
+ * `sink` is a device pointer to one float, written only if the accumulated sum is exactly
+ * 2^127 (it keeps the work from being dropped).  Stream-ordered; nothing is allocated.  Returns
+ * SPEC_OK (also for iters == 0 or workgroups == 0), SPEC_ERR_INVALID (mode outside 0..2,
+ * iters outside 0..2^20, workgroups outside 0..65536, a NULL sink) or SPEC_ERR_LAUNCH. */
+int spec_mfma_rate(int mode, int iters, int workgroups, float* sink, void* hip_stream);
+
 /* Human-readable text for a return code (negative) or a single status bit (positive). */
 const char* spec_status_string(int code);
 

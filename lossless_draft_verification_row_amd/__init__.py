@@ -120,6 +120,8 @@ def load_library():
     lib.spec_select_gamma.argtypes = [i32, vp, vp, GammaMLP, vp, vp, vp]
     lib.spec_stream_read.restype = i32
     lib.spec_stream_read.argtypes = [vp, i64, vp, vp]
+    lib.spec_mfma_rate.restype = i32
+    lib.spec_mfma_rate.argtypes = [i32, i32, i32, vp, vp]
     lib.spec_status_string.restype = ctypes.c_char_p
     lib.spec_status_string.argtypes = [i32]
     _LIB = lib
@@ -340,6 +342,16 @@ def spec_stream_read(buf, sink, stream=None):
     nbytes = buf.numel() * buf.element_size()
     rc = load_library().spec_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream))
     _check(rc, "spec_stream_read")
+
+
+def spec_mfma_rate(mode, iters, workgroups, sink, stream=None):
+    """Benchmark instrumentation (see spec_mfma_rate in the header): `workgroups` x 4 waves of
+    `iters` steps of 16 bf16 32x32x16 MFMAs on register operands; mode 0 constant, 1 random
+    fixed, 2 random changing every step.  sink: a float32 CUDA tensor of at least one element."""
+    if sink.dtype != torch.float32 or sink.numel() < 1 or not sink.is_cuda:
+        raise ValueError("sink must be a float32 CUDA tensor")
+    rc = load_library().spec_mfma_rate(int(mode), int(iters), int(workgroups), _ptr(sink), _stream(stream))
+    _check(rc, "spec_mfma_rate")
 
 
 def spec_select_gamma(req_stats, w1, b1, w2, b2, comp=None, stream=None):

@@ -237,6 +237,12 @@ FilterArgs plain_filter_args(int R, int V, const void* p, int64_t p_ld, const vo
 
 }  // namespace
 
+namespace specv {
+// The matrix-rate kernel's launcher (spec_head.hip), used only by spec_mfma_rate.
+hipError_t launch_mfma_rate(int mode, int iters, int workgroups, float* sink, hipStream_t st, hipEvent_t ev0,
+                            hipEvent_t ev1);
+}  // namespace specv
+
 extern "C" {
 
 const char* spec_status_string(int code) {
@@ -797,6 +803,14 @@ int spec_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* hip_s
   if (bytes % 16 != 0 || ((uintptr_t)buf & 15u) != 0) return SPEC_ERR_UNSUPPORTED;
   if (bytes == 0) return SPEC_OK;
   const hipError_t e = launch_stream_read(buf, bytes / 16, sink, (hipStream_t)hip_stream, nullptr, nullptr);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
+}
+
+int spec_mfma_rate(int mode, int iters, int workgroups, float* sink, void* hip_stream) {
+  if (mode < 0 || mode > 2 || iters < 0 || iters > (1 << 20) || workgroups < 0 || workgroups > (1 << 16) || !sink)
+    return SPEC_ERR_INVALID;
+  if (iters == 0 || workgroups == 0) return SPEC_OK;
+  const hipError_t e = launch_mfma_rate(mode, iters, workgroups, sink, (hipStream_t)hip_stream, nullptr, nullptr);
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
 }
 

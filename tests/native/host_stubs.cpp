@@ -173,6 +173,11 @@ hipError_t launch_stream_read(const void*, int64_t, uint32_t*, hipStream_t, hipE
   return hipSuccess;
 }
 
+hipError_t launch_mfma_rate(int, int, int, float*, hipStream_t, hipEvent_t, hipEvent_t) {
+  ++hoststub::g_launches;
+  return hipSuccess;
+}
+
 hipError_t launch_head(const HeadArgs& a, hipStream_t, hipEvent_t, hipEvent_t) {
   ++hoststub::g_launches;
   carved("head records", a.rec, (size_t)a.R * a.n_ct * sizeof(HeadRec));

@@ -145,3 +145,15 @@ def test_stream_read_argument_checks_without_gpu():
     assert lib.spec_stream_read(16, 32, None, None) == -1          # no sink
     assert lib.spec_stream_read(16, 24, 16, None) == -2            # not whole 16-byte words
     assert lib.spec_stream_read(8, 32, 16, None) == -2             # misaligned buffer
+
+
+def test_mfma_rate_argument_checks_without_gpu():
+    lib = L.load_library()
+    assert lib.spec_mfma_rate(0, 0, 8, 16, None) == 0             # no steps: nothing launched
+    assert lib.spec_mfma_rate(2, 8, 0, 16, None) == 0             # no workgroups
+    assert lib.spec_mfma_rate(3, 8, 8, 16, None) == -1            # mode outside 0..2
+    assert lib.spec_mfma_rate(-1, 8, 8, 16, None) == -1
+    assert lib.spec_mfma_rate(0, -1, 8, 16, None) == -1           # negative steps
+    assert lib.spec_mfma_rate(0, (1 << 20) + 1, 8, 16, None) == -1
+    assert lib.spec_mfma_rate(0, 8, (1 << 16) + 1, 16, None) == -1
+    assert lib.spec_mfma_rate(0, 8, 8, None, None) == -1          # no sink

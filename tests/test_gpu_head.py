@@ -181,3 +181,40 @@ def test_head_strided_rows(R):
     gpu = {k: v.cpu().numpy() for k, v in res.items()}
     ref, _ = oracle(h, w, 0.9, None)
     check_exact(gpu, ref, np.arange(R))
+
+
+@pytest.mark.parametrize("R,V,D", [(129, 1000, 64), (300, 4096 + 77, 192), (257, 513, 128), (512, 300, 256)])
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_head_square_tiles_exact(R, V, D, T):
+    """More than 128 rows and D a whole number of 64-deep stages: the 256 x 256 tiles fed by
+    direct-to-LDS loads.  Ragged row and column tails (one row in a second row tile, 77 columns
+    in the last column tile, fewer columns than one tile), dyadic values so the logits are exact."""
+    note(f"case head square exact R={R} V={V} D={D} T={T}")
+    h, w = W.head_inputs(R, V, D, seed=3 * R + V + D, exact=True)
+    tok = np.random.default_rng(4).integers(-1, V + 1, size=R)
+    gpu = run(h, w, T, tok)
+    ref, _ = oracle(h, w, T, tok)
+    check_exact(gpu, ref, np.arange(R))
+
+
+def test_head_square_tiles_nonfinite_and_strided():
+    """The square tiles with row strides wider than D (NaN padding that must never be read)
+    and a NaN and an infinity in two hidden rows of the second row tile."""
+    R, V, D, pad = 300, 700, 64, 24
+    h, w = W.head_inputs(R, V, D, seed=91, exact=True)
+    h[260, 3] = 0x7FC0            # NaN
+    h[299, 63] = 0xFF80           # -inf
+    hb = np.full((R, D + pad), 0x7FC0, dtype=np.uint16)
+    wb = np.full((V, D + pad), 0x7FC0, dtype=np.uint16)
+    hb[:, :D] = h
+    wb[:, :D] = w
+    ht = torch.from_numpy(hb.view(np.int16)).view(torch.bfloat16).to(DEV)[:, :D]
+    wt = torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16).to(DEV)[:, :D]
+    tok = np.arange(R, dtype=np.int64) % V
+    res = L.spec_lm_head_row_stats(ht, wt, temperature=0.8,
+                                   tokens=torch.from_numpy(tok.astype(np.int32)).to(DEV))
+    torch.cuda.synchronize()
+    gpu = {k: v.cpu().numpy() for k, v in res.items()}
+    ref, _ = oracle(h, w, 0.8, tok)
+    check_exact(gpu, ref, np.arange(R))
+    assert gpu["argmax"][260] == -1 and np.isnan(gpu["log_z"][299])

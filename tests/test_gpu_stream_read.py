@@ -1,5 +1,6 @@
-"""The streaming-read ceiling kernel (benchmark instrumentation): it reads every 16-byte word,
-ragged tails included, and writes its sink only when the XOR of all words is the fixed word."""
+"""The ceiling kernels (benchmark instrumentation).  The streaming read reads every 16-byte
+word, ragged tails included, and writes its sink only when the XOR of all words is the fixed
+word; the matrix-rate kernel runs in each operand mode without touching its sink."""
 import sys
 
 import numpy as np
@@ -32,3 +33,14 @@ def test_stream_read_sees_every_word(words, where):
     L.spec_stream_read(buf, sink)          # one word carries the pattern: the sink is written
     torch.cuda.synchronize()
     assert int(sink.item()) & 0xFFFFFFFF == MAGIC
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_mfma_rate_runs_and_leaves_the_sink(mode):
+    """The matrix-rate kernel runs in every operand mode; its sum is never exactly 2^127, so the
+    sink keeps the value it had."""
+    note(f"case mfma_rate mode={mode}")
+    sink = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+    L.spec_mfma_rate(mode, 16, 8, sink)
+    torch.cuda.synchronize()
+    assert sink.item() == 7.0
