@@ -7,6 +7,14 @@
 // same partials the streaming kernels keep per slice.  The logits never reach memory.  A second
 // kernel combines a row's partials in fp64 into the statistics spec_row_stats reports (the
 // SpecKV page's signals) and the probability of a given token.
+//
+//   k_head_sq       more than 128 rows, D a multiple of 64: 256 x 256 tiles, one wave per
+//                   SIMD with 4 x 4 accumulators, stages loaded straight into LDS
+//   k_head          otherwise: 128 x 256 (or 64 x 256) tiles, two waves per SIMD, stages
+//                   staged through registers
+//   k_head_combine  one wave per row: the row's tile records, then the statistics
+//   k_mfma_rate     benchmark instrumentation: the matrix cores' rate on the same MFMA
+//                   pattern with register operands
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -280,7 +288,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Loads i0 .. i0 + 3 of one stage: wave w fills granule positions 64 (8 w + i) + lane of both
 // operands (row 64 w + 8 i + lane / 8, slot lane % 8, holding k granule slot ^ swz(row)); the
-// lane's byte offset within the tile is vo[i], the stage's k is the scalar offset.
+// lane's byte offsets within the tiles are va[i] and vb[i], the stage's k is the scalar offset.
 __device__ __forceinline__ void dma_quarter(HeadDmaLds& L, int buf, int i0, __amdgpu_buffer_rsrc_t rsa,
                                             __amdgpu_buffer_rsrc_t rsb, const int (&va)[kDKS],
                                             const int (&vb)[kDKS], int koff, int wave_u) {
