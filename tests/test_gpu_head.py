@@ -218,3 +218,17 @@ def test_head_square_tiles_nonfinite_and_strided():
     ref, _ = oracle(h, w, 0.8, tok)
     check_exact(gpu, ref, np.arange(R))
     assert gpu["argmax"][260] == -1 and np.isnan(gpu["log_z"][299])
+
+
+@pytest.mark.parametrize("T", [1.0, 0.6, 0.0])
+def test_head_square_tiles_normal_values_bounded(T):
+    """Normal values on the 256 x 256 tiles (more than 128 rows, D a multiple of 64): the
+    statistics within the bounds the fp32 accumulation allows, rows in both row tiles."""
+    R, V, D = 300, 3000, 320
+    note(f"case head square normal R={R} V={V} D={D} T={T}")
+    h, w = W.head_inputs(R, V, D, seed=29, scale_w=0.2)
+    tok = np.random.default_rng(5).integers(0, V, size=R)
+    gpu = run(h, w, T, tok)
+    rows = np.array([0, 77, 255, 256, 299])
+    ref, ap = oracle(h, w, T, tok, rows=rows)
+    check_bounded(gpu, ref, ap, D, T, rows)
