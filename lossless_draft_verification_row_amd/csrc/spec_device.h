@@ -639,15 +639,61 @@ __device__ __forceinline__ void load_run16(const void* row, int V, int x0, float
   }
 }
 
+// 16 consecutive logits of a row as raw 16-byte words (two for bf16, four for fp32), loaded
+// when the run is aligned and in range; raw_run_unpack turns them into floats, reading the
+// elements one by one itself for a run that is not (masked: -inf past V).
+template <int DT>
+struct RawRun16 {
+  uint4 w[DT == kDtBF16 ? 2 : 4];
+};
+template <int DT, bool VEC>
+__device__ __forceinline__ RawRun16<DT> raw_run_load(const void* row, int V, int x0) {
+  RawRun16<DT> r;
+  constexpr int n = DT == kDtBF16 ? 2 : 4;
+  if (VEC && x0 + 16 <= V) {
+    const uint4* p = (const uint4*)((const char*)row + (size_t)x0 * (DT == kDtBF16 ? 2 : 4));
+#pragma unroll
+    for (int k = 0; k < n; ++k) r.w[k] = p[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < n; ++k) r.w[k] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  return r;
+}
+template <int DT, bool VEC>
+__device__ __forceinline__ void raw_run_unpack(const RawRun16<DT>& r, const void* row, int V, int x0, float (&v)[16]) {
+  if (VEC && x0 + 16 <= V) {
+    if constexpr (DT == kDtBF16) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t w[4] = {r.w[k].x, r.w[k].y, r.w[k].z, r.w[k].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { v[8 * k + 2 * q] = bf16_lo(w[q]); v[8 * k + 2 * q + 1] = bf16_hi(w[q]); }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[4 * k] = __uint_as_float(r.w[k].x); v[4 * k + 1] = __uint_as_float(r.w[k].y);
+        v[4 * k + 2] = __uint_as_float(r.w[k].z); v[4 * k + 3] = __uint_as_float(r.w[k].w);
+      }
+    }
+  } else {
+    load_run16<DT, VEC>(row, V, x0, v);
+  }
+}
+
 // Pair sums of one (target, draft) row pair with the relative precision of fp64, for the rare
 // positions where the streaming passes' fp32 sums would not keep it: A = sum min(p, q) when the
 // two distributions barely overlap (1 - beta loses A's precision), and beta = sum [p - q]_+ when
 // they nearly coincide (an error in the normalisers' ratio then moves every term the same way).
 // Two passes over both rows by the whole workgroup: Z_p and Z_q as fp64 sums of the same
 // e-values the second pass divides, then A and beta in fp64 (guide page "5.1 投机解码核心原理"
-// §4.1 / §4.3: beta = sum [p - q]_+, A = sum min(p, q) = 1 - beta).  The exponent of logit l is
-// t = (l - ref) c when SUB, else l c - ref; logits below tau are masked.  `red` holds kWaves
-// doubles of LDS.
+// §4.1 / §4.3: beta = sum [p - q]_+, A = sum min(p, q) = 1 - beta).  One workgroup reads the
+// rows, so each thread keeps kPairRuns runs of 16 logits of both rows in flight before it works
+// on any of them (a run at a time would leave the pass at the latency of one load per thread).
+// The exponent of logit l is t = (l - ref) c when SUB, else l c - ref; logits below tau are
+// masked.  `red` holds kWaves doubles of LDS.
+constexpr int kPairRuns = 4;
 template <int DT, bool VEC, bool SUB>
 __device__ void pair_sums_fp64(const void* prow, const void* qrow, int V, float c, float refp, float refq, float taup,
                                float tauq, double* red, double& A, double& beta) {
@@ -656,34 +702,94 @@ __device__ void pair_sums_fp64(const void* prow, const void* qrow, int V, float 
     if (l < tau) return 0.f;
     return __builtin_amdgcn_exp2f(SUB ? (l - ref) * c : fmaf(l, c, -ref));
   };
+  constexpr int kStep = kThreads * 16;
   double zp = 0.0, zq = 0.0;
-  for (int x0 = t * 16; x0 < V; x0 += kThreads * 16) {
-    float vp[16], vq[16];
-    load_run16<DT, VEC>(prow, V, x0, vp);
-    load_run16<DT, VEC>(qrow, V, x0, vq);
+  for (int x0 = t * 16; x0 < V; x0 += kPairRuns * kStep) {
+    RawRun16<DT> rp[kPairRuns], rq[kPairRuns];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      zp += (double)ex(vp[e], refp, taup);
-      zq += (double)ex(vq[e], refq, tauq);
+    for (int u = 0; u < kPairRuns; ++u) {
+      rp[u] = raw_run_load<DT, VEC>(prow, V, x0 + u * kStep);
+      rq[u] = raw_run_load<DT, VEC>(qrow, V, x0 + u * kStep);
+    }
+#pragma unroll
+    for (int u = 0; u < kPairRuns; ++u) {
+      const int xu = x0 + u * kStep;
+      if (xu >= V) break;
+      float vp[16], vq[16];
+      raw_run_unpack<DT, VEC>(rp[u], prow, V, xu, vp);
+      raw_run_unpack<DT, VEC>(rq[u], qrow, V, xu, vq);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        zp += (double)ex(vp[e], refp, taup);
+        zq += (double)ex(vq[e], refq, tauq);
+      }
     }
   }
   zp = block_sum_d(zp, red);
   zq = block_sum_d(zq, red);
   const double ip = 1.0 / zp, iq = 1.0 / zq;
   double a = 0.0, bsum = 0.0;
-  for (int x0 = t * 16; x0 < V; x0 += kThreads * 16) {
-    float vp[16], vq[16];
-    load_run16<DT, VEC>(prow, V, x0, vp);
-    load_run16<DT, VEC>(qrow, V, x0, vq);
+  for (int x0 = t * 16; x0 < V; x0 += kPairRuns * kStep) {
+    RawRun16<DT> rp[kPairRuns], rq[kPairRuns];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const double pp = (double)ex(vp[e], refp, taup) * ip, qq = (double)ex(vq[e], refq, tauq) * iq;
-      a += fmin(pp, qq);
-      bsum += fmax(pp - qq, 0.0);
+    for (int u = 0; u < kPairRuns; ++u) {
+      rp[u] = raw_run_load<DT, VEC>(prow, V, x0 + u * kStep);
+      rq[u] = raw_run_load<DT, VEC>(qrow, V, x0 + u * kStep);
+    }
+#pragma unroll
+    for (int u = 0; u < kPairRuns; ++u) {
+      const int xu = x0 + u * kStep;
+      if (xu >= V) break;
+      float vp[16], vq[16];
+      raw_run_unpack<DT, VEC>(rp[u], prow, V, xu, vp);
+      raw_run_unpack<DT, VEC>(rq[u], qrow, V, xu, vq);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const double pp = (double)ex(vp[e], refp, taup) * ip, qq = (double)ex(vq[e], refq, tauq) * iq;
+        a += fmin(pp, qq);
+        bsum += fmax(pp - qq, 0.0);
+      }
     }
   }
   A = block_sum_d(a, red);
   beta = block_sum_d(bsum, red);
+}
+
+// 1 - TV = A = sum min(p, q) of one (target, draft) row pair in one pass over both rows, for
+// positions whose two distributions barely overlap, with the rows' own normalisers: p =
+// 2^(l c - refp) / zp (refp and zp as the streaming passes formed them), q alike.  Every term is
+// positive, so the sum keeps the relative precision of its terms (fp32 each, about 1e-6 at
+// worst from the exponent's rounding) however small A is; 16 terms are added in fp32, the runs
+// in fp64 (guide page "5.1 投机解码核心原理" §4.3).  `red` holds kWaves doubles of LDS.
+template <int DT, bool VEC>
+__device__ double pair_overlap(const void* prow, const void* qrow, int V, float c, float refp, float refq, double zp,
+                               double zq, double* red) {
+  const int t = threadIdx.x;
+  const float ip = (float)(1.0 / zp), iq = (float)(1.0 / zq);
+  constexpr int kStep = kThreads * 16;
+  double a = 0.0;
+  for (int x0 = t * 16; x0 < V; x0 += kPairRuns * kStep) {
+    RawRun16<DT> rp[kPairRuns], rq[kPairRuns];
+#pragma unroll
+    for (int u = 0; u < kPairRuns; ++u) {
+      rp[u] = raw_run_load<DT, VEC>(prow, V, x0 + u * kStep);
+      rq[u] = raw_run_load<DT, VEC>(qrow, V, x0 + u * kStep);
+    }
+#pragma unroll
+    for (int u = 0; u < kPairRuns; ++u) {
+      const int xu = x0 + u * kStep;
+      if (xu >= V) break;
+      float vp[16], vq[16];
+      raw_run_unpack<DT, VEC>(rp[u], prow, V, xu, vp);
+      raw_run_unpack<DT, VEC>(rq[u], qrow, V, xu, vq);
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        s += fminf(__builtin_amdgcn_exp2f(fmaf(vp[e], c, -refp)) * ip, __builtin_amdgcn_exp2f(fmaf(vq[e], c, -refq)) * iq);
+      a += (double)s;
+    }
+  }
+  return block_sum_d(a, red);
 }
 
 // Below this overlap A, or this residual mass beta, a position's pair sums are recomputed with

@@ -63,7 +63,8 @@ struct FinScratch {
   alignas(16) float wall[kChunk];   // the picked chunk's sampler weights
   double u[3];
   double red[kWaves];
-  unsigned long long lowm;       // positions whose pair sums are recomputed (pair_sums_fp64)
+  unsigned long long lowm;       // positions whose 1 - TV or L1 is recomputed from the rows
+  unsigned long long lowbm;      // of those, the ones whose beta needs fp64 normalisers
   int flags, status, n_acc, pos, wkind, y, kpick, xpick;
 };
 
@@ -493,7 +494,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   __syncthreads();
 
   // B. the accept test of every position: p(y), q(y) and the accept draw
-  bool rej = false, low = false;
+  bool rej = false, low = false, lowb = false;
   int why = 0;
   if (t < g) {
     const TeamL T = F.team[t];
@@ -511,7 +512,10 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
         const bool okq = (T.flags & (kTeamBadQ | kTeamTimeout)) == 0;
         if (okq && yv) qyd = exp2_split((double)ly_q * cd - (double)T.M[1]) / T.z[1];
         if (okp && okq) {
-          low = T.beta < kPairRefine || 1.0 - T.beta < kPairRefine;
+          // a requested output whose fp32 streaming sum would lose its relative precision:
+          // L1 = 2 beta when the distributions nearly coincide, 1 - TV when they barely overlap
+          lowb = a.st.l1 && T.beta < kPairRefine;
+          low = lowb || (a.st.one_minus_tv && 1.0 - T.beta < kPairRefine);
           ap = (yv && qyd > 0.0) ? fmin(1.0, pyd / qyd) : 0.0;
         }
       }
@@ -534,6 +538,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
     fl = wave_or(fl);
     const unsigned long long rm = __ballot(rej);
     const unsigned long long lm = __ballot(low);
+    const unsigned long long lbm = __ballot(lowb);
     const int j = rm ? __builtin_ctzll(rm) : -1;
     const int whyj = j >= 0 ? __builtin_amdgcn_readlane(why, j) : 0;
     if (lane == 0) {
@@ -555,6 +560,7 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       F.kpick = -1;
       F.flags = fl;
       F.lowm = lm;
+      F.lowbm = lbm;
     }
   }
   __syncthreads();
@@ -769,17 +775,26 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
     a.out_status[b] = F.status;
   }
 
-  // positions whose two distributions barely overlap or nearly coincide: A and beta again, with
-  // fp64 normalisers and sums (pair_sums_fp64)
+  // positions whose requested 1 - TV or L1 the fp32 streaming sums cannot give: when beta is
+  // small, A and beta again with fp64 normalisers (pair_sums_fp64, two passes); when only the
+  // overlap is small, A directly as a sum of positive terms with the team's normalisers
+  // (pair_overlap, one pass), beta as streamed
   if (MODE == kFuSample && (a.st.one_minus_tv || a.st.l1)) {
     unsigned long long lm = F.lowm;
+    const unsigned long long lbm = F.lowbm;
     while (lm) {
       const int i = __builtin_ctzll(lm);
       lm &= lm - 1;
       const TeamL T = F.team[i];
+      const void* prow = row_ptr<DT>(a.tgt, a.tgt_ld, c0 + b + i);
+      const void* qrow = row_ptr<DT>(a.drf, a.drf_ld, c0 + i);
       double A, beta;
-      pair_sums_fp64<DT, VEC, false>(row_ptr<DT>(a.tgt, a.tgt_ld, c0 + b + i), row_ptr<DT>(a.drf, a.drf_ld, c0 + i),
-                                     a.V, a.c, T.M[0], T.M[1], -INFINITY, -INFINITY, F.red, A, beta);
+      if ((lbm >> i) & 1ull) {
+        pair_sums_fp64<DT, VEC, false>(prow, qrow, a.V, a.c, T.M[0], T.M[1], -INFINITY, -INFINITY, F.red, A, beta);
+      } else {
+        A = pair_overlap<DT, VEC>(prow, qrow, a.V, a.c, T.M[0], T.M[1], T.z[0], T.z[1], F.red);
+        beta = T.beta;
+      }
       if (t == 0) {
         if (a.st.one_minus_tv) a.st.one_minus_tv[c0 + i] = (float)A;
         if (a.st.l1) a.st.l1[c0 + i] = (float)(2.0 * beta);

@@ -162,11 +162,13 @@ def test_worked_example_v3():
 
 
 @pytest.mark.parametrize("path", PATHS)
-def test_low_overlap_one_minus_tv(path):
-    """Nearly disjoint p and q (overlap near 7e-4): the target puts its mass on tokens 0..99,
-    the draft on tokens 100..199.  1 - TV = sum min(p, q) must keep 1e-5 relative precision
-    with no absolute floor (guide §4.3: A = sum min(p, q) = 1 - TV)."""
-    V = 3 * 4096 + 72
+@pytest.mark.parametrize("V", [3 * 4096 + 72, 151936])
+def test_low_overlap_one_minus_tv(path, V):
+    """Nearly disjoint p and q (overlap near 7e-4 at the small vocabulary, 7e-3 at the full
+    one): the target puts its mass on tokens 0..99, the draft on tokens 100..199.
+    1 - TV = sum min(p, q) must keep 1e-5 relative precision with no absolute floor (guide
+    §4.3: A = sum min(p, q) = 1 - TV).  The full vocabulary takes the fp64 recomputation over
+    several groups of runs per thread."""
     inp = custom_inputs(4, V, [3, 2, 1, 3], sigma=0.5, tau=0.5, seed=77)
     t32 = W.bf16_bits_to_f32(inp.target).copy()
     d32 = W.bf16_bits_to_f32(inp.draft).copy()
@@ -179,18 +181,18 @@ def test_low_overlap_one_minus_tv(path):
     for b, ref in refs.items():
         c0, g = int(inp.cu_draft[b]), int(inp.gammas[b])
         got = gpu["one_minus_tv"][c0:c0 + g].astype(np.float64)
-        assert (ref.one_minus_tv < 2e-3).all(), ref.one_minus_tv
+        assert (ref.one_minus_tv < 1e-2).all(), ref.one_minus_tv
         rel = np.abs(got - ref.one_minus_tv) / ref.one_minus_tv
         note(f"request {b}: 1 - TV {ref.one_minus_tv.tolist()} relative error {rel.max():.2e}")
         assert (rel < 1e-5).all()
 
 
 @pytest.mark.parametrize("path", PATHS)
-def test_near_identical_rows_small_tv(path):
+@pytest.mark.parametrize("V", [3 * 4096 + 72, 151936])
+def test_near_identical_rows_small_tv(path, V):
     """Draft rows equal to the target rows except for a few hundred tokens: TV of a few 1e-3,
     the case where the residual mass sum [p - q]_+ is a small difference of nearly equal
     distributions (its error then comes from the normalisers' ratio)."""
-    V = 3 * 4096 + 72
     inp = custom_inputs(5, V, [4, 3, 2, 4, 1], T=0.7, seed=78)
     rng = np.random.default_rng(79)
     for b in range(5):
@@ -205,6 +207,38 @@ def test_near_identical_rows_small_tv(path):
     tv = np.concatenate([r.tv for r in refs.values()])
     note(f"TV range {tv.min():.2e} .. {tv.max():.2e}; max relative error of L1 {rep.max_rel.get('l1')}")
     assert np.median(tv) < 0.01
+
+
+def test_near_identical_rows_one_minus_tv_without_l1():
+    """The benchmark's outputs (1 - TV but no L1) on near-identical rows: 1 - TV = 1 - beta is
+    then close to 1 and precise from the streaming sums, so the finalize recomputes nothing;
+    the value still meets the relative bar against the oracle."""
+    V = 151936
+    inp = custom_inputs(4, V, [4, 3, 2, 4], T=0.7, seed=81)
+    rng = np.random.default_rng(82)
+    for b in range(4):
+        g, c0 = int(inp.gammas[b]), int(inp.cu_draft[b])
+        d32 = W.bf16_bits_to_f32(inp.target[c0 + b:c0 + b + g]).copy()
+        idx = rng.choice(V, size=(g, 300))
+        for i in range(g):
+            d32[i, idx[i]] += rng.normal(0, 1.0, 300).astype(np.float32)
+        inp.draft[c0:c0 + g] = W.bf16_bits_from_f32(d32)
+    d = H.to_device(inp)
+    B, G, Rd = 4, int(inp.gammas.max()), int(inp.cu_draft[-1])
+    out = {"tokens": torch.empty((B, G + 1), dtype=torch.int32, device=DEV),
+           "num_accepted": torch.empty(B, dtype=torch.int32, device=DEV),
+           "status": torch.empty(B, dtype=torch.int32, device=DEV),
+           "one_minus_tv": torch.empty(Rd, dtype=torch.float32, device=DEV)}
+    L.spec_verify_batch(d["target"], d["draft"], d["tokens"], d["cu"], G, temperature=0.7, seed=3, step=1, out=out)
+    torch.cuda.synchronize()
+    got = out["one_minus_tv"].cpu().numpy().astype(np.float64)
+    refs = H.oracle_requests(inp, O.SamplingParams(0.7), 3, 1, range(B))
+    tv = np.concatenate([r.tv for r in refs.values()])
+    assert (tv < 0.02).sum() >= len(tv) // 2, tv
+    for b, ref in refs.items():
+        c0, g = int(inp.cu_draft[b]), int(inp.gammas[b])
+        rel = np.abs(got[c0:c0 + g] - ref.one_minus_tv) / ref.one_minus_tv
+        assert (rel < 1e-5).all(), (b, rel)
 
 
 # ----------------------------------------------------------------------------- greedy / token-only
