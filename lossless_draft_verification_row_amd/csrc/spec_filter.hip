@@ -199,7 +199,7 @@ __device__ __forceinline__ int wave_max_i(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
-constexpr int kStageW = 128;   // candidates one wave may stage per row of a list
+constexpr int kStageW = 512;   // candidates one wave may stage per row of a list (shares LDS with raw)
 
 struct ListLds {
   uint32_t hist[2][256];   // per row: count of per-thread maxima at order key max - b, b = 0..255

@@ -3,6 +3,7 @@
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -245,8 +246,19 @@ struct FilterArgs {
   RowStatsOut rso;
 };
 
-// Candidates kept per slice for top-k = k: the k largest plus room for boundary ties.
-inline int filter_cap(int k) { return (k + 32 + 15) / 16 * 16; }
+// Candidate slots of one list for top-k = k.  A list's candidates are its logits at or above
+// the k-th largest of its 256 per-thread maxima (32 logits per thread), so for a row of i.i.d.
+// values their expected count is 8192 (1 - q^(1/32)) with q = (256.5 - k) / 257, the expected
+// quantile of that order statistic: 56 at k = 50, 175 at k = 128, about 1450 at k = 256.  The
+// slots hold that count plus five standard deviations of it (and never fewer than k + 32), so
+// that a list rarely takes the exact select, which reads the list again.
+inline int filter_cap(int k) {
+  const double q = (256.5 - (double)k) / 257.0;
+  const double c = 8192.0 * (1.0 - pow(q > 0.0 ? q : 1e-9, 1.0 / 32.0));
+  const int need = (int)ceil(c + 5.0 * sqrt(c));
+  const int cap = need > k + 32 ? need : k + 32;
+  return (cap < 8192 ? cap : 8192) + 15 & ~15;
+}
 hipError_t launch_filter(const FilterArgs& a, int dt, int vec, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 // Plain filtered rows: what = 0, the statistics of n_teams rows (a.rso); what = 1, one residual
 // draw per row pair (target row r, draft row r or none).

@@ -231,6 +231,18 @@ def test_filtered_spread_top_k_sets(k, p):
     assert not (gpu["status"] & L.STATUS["FILTER_OVERFLOW"]).any()
 
 
+@pytest.mark.parametrize("k,p", [(128, 1.0), (200, 0.9)])
+def test_filtered_large_k_full_vocabulary(k, p):
+    """Top-k 128 and 200 over the full Qwen3 vocabulary: a list keeps a few hundred candidates
+    (its slots grow with k), a row several thousand over its 19 lists; every request matches
+    the oracle and none is refused."""
+    sp = O.SamplingParams(0.7, k, p)
+    V = 151936
+    inp = filtered_inputs(4, V, [3, 2, 4, 1], sp, seed=90 + k)
+    gpu, _, _ = check(inp, sp)
+    assert not (gpu["status"] & L.STATUS["FILTER_OVERFLOW"]).any()
+
+
 def test_filtered_sampling_wide_vocabulary():
     """V = 250,000: 31 candidate lists per bf16 row, the widest the row kernel holds."""
     sp = O.SamplingParams(0.7, 50, 0.9)
