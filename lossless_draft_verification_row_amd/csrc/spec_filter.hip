@@ -199,6 +199,7 @@ __device__ __forceinline__ int wave_max_i(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
+constexpr int kTop2K = 128;    // above this k a list's threshold counts each thread's two largest values
 constexpr int kStageW = 512;   // candidates one wave may stage per row of a list (shares LDS with raw)
 
 struct ListLds {
@@ -253,10 +254,11 @@ __device__ __forceinline__ void mask_tail_words(int V, int base, RawSlice<kDtBF1
 
 // Candidates of one list of a bf16 target row and (paired) the same list of its draft row: two
 // 4096-logit chunks, 32 logits per thread per row, both rows in lockstep.  The k-th largest of
-// the 256 per-thread maxima is at most the list's k-th largest logit, so every finite logit at
-// or above it is a valid candidate set (it holds the list's top k with all ties); for a
-// realistic row it is barely larger than k.  That threshold comes from one LDS histogram of the
-// maxima within 256 order keys of the list maximum (one atomic per thread).  Each wave then
+// the 256 per-thread maxima (for k above kTop2K, of the 512 values that are each thread's two
+// largest) is at most the list's k-th largest logit, so every finite logit at or above it is a
+// valid candidate set (it holds the list's top k with all ties); for a realistic row it is
+// not much larger than k.  That threshold comes from one LDS histogram of the
+// maxima within 256 order keys of the list maximum (one or two atomics per thread).  Each wave then
 // stages its candidates in its own LDS region in one compare pass (wave counts by popcount,
 // slots by mbcnt, elements no lane keeps skipped), and the regions are copied out whole.  A row
 // whose maxima spread wider, or whose candidates fill a region or the list's `cap`, takes the
@@ -271,17 +273,37 @@ __device__ void list_candidates_bf16(const FilterArgs& a, ListLds& S, const RawS
   // per-thread maxima with NaN propagated: a NaN or +inf anywhere makes the maximum NaN or
   // +inf, which flags the row (its candidates are then never read)
   float fm[2] = {-INFINITY, -INFINITY};
+  // above kTop2K each thread also gives its second largest, so that k counts against 512
+  // values: the k-th largest of the 256 maxima alone is their smallest at k = 256, far down the
+  // list, and its candidates would overflow the list's slots
+  float f2[2] = {-INFINITY, -INFINITY};
+  const bool top2 = a.k > kTop2K;
   int bad[2];
+  if (top2) {
 #pragma unroll
-  for (int j = 0; j < NE; ++j) {
-    fm[0] = __builtin_elementwise_maximum(fm[0], list_elem(rp, j));
-    if (paired) fm[1] = __builtin_elementwise_maximum(fm[1], list_elem(rq, j));
+    for (int j = 0; j < NE; ++j) {
+      const float v = list_elem(rp, j);
+      f2[0] = fmaxf(f2[0], fminf(fm[0], v));
+      fm[0] = __builtin_elementwise_maximum(fm[0], v);
+      if (paired) {
+        const float w = list_elem(rq, j);
+        f2[1] = fmaxf(f2[1], fminf(fm[1], w));
+        fm[1] = __builtin_elementwise_maximum(fm[1], w);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+      fm[0] = __builtin_elementwise_maximum(fm[0], list_elem(rp, j));
+      if (paired) fm[1] = __builtin_elementwise_maximum(fm[1], list_elem(rq, j));
+    }
   }
-  int tm[2];
+  int tm[2], t2[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     bad[r] = fm[r] < INFINITY ? 0 : 1;
     tm[r] = (fm[r] > -INFINITY && fm[r] < INFINITY) ? key16(fm[r]) : -1;
+    t2[r] = (top2 && f2[r] > -INFINITY && f2[r] < INFINITY) ? key16(f2[r]) : -1;
   }
   S.hist[0][t] = 0u;
   S.hist[1][t] = 0u;
@@ -301,6 +323,7 @@ __device__ void list_candidates_bf16(const FilterArgs& a, ListLds& S, const RawS
     mx[r] = m;
     bad[r] = bd;
     if (tm[r] >= 0 && m - tm[r] < 256) atomicAdd(&S.hist[r][m - tm[r]], 1u);
+    if (t2[r] >= 0 && m - t2[r] < 256) atomicAdd(&S.hist[r][m - t2[r]], 1u);
   }
   __syncthreads();
   // wave r: the k-th largest per-thread maximum of row r (bins ascend from the maximum)
