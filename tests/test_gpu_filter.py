@@ -158,15 +158,17 @@ def test_filtered_all_equal_recomputed_densely():
     assert not (gpu["status"] & L.STATUS["FILTER_OVERFLOW"]).any()
 
 
-@pytest.mark.parametrize("n_tied", [600, 60])
-def test_filtered_heavy_ties_at_kth_value(n_tied):
-    """n_tied equal logits at the top of some rows with top-k 50: 600 ties make the top-k set
-    larger than the sparse sets hold (dense recomputation); 60 ties stay sparse.  Requests with
-    and without ties are mixed in one call; every request matches the oracle."""
-    sp = O.SamplingParams(0.7, 50, 0.9)
+@pytest.mark.parametrize("n_tied,k", [(600, 50), (60, 50), (300, 200), (700, 200), (40, 256)])
+def test_filtered_heavy_ties_at_kth_value(n_tied, k):
+    """n_tied equal logits at the top of some rows: 600 ties with top-k 50, or 700 with top-k
+    200, make the top-k set larger than the sparse sets hold (dense recomputation); fewer stay
+    sparse, at top-k 200 and 256 through lists whose threshold counts each thread's two
+    largest values.  Requests with and without ties are mixed in one call; every request
+    matches the oracle."""
+    sp = O.SamplingParams(0.7, k, 0.9)
     V = V_SMALL
-    inp = filtered_inputs(5, V, [4, 3, 5, 2, 4], sp, seed=40 + n_tied)
-    rng = np.random.default_rng(n_tied)
+    inp = filtered_inputs(5, V, [4, 3, 5, 2, 4], sp, seed=40 + n_tied + k)
+    rng = np.random.default_rng(n_tied + k)
     for b in (1, 3):
         c0, g = int(inp.cu_draft[b]), int(inp.gammas[b])
         for arr, rows in ((inp.target, range(c0 + b, c0 + b + g + 1)), (inp.draft, range(c0, c0 + g))):
