@@ -272,9 +272,12 @@ size_t spec_verify_workspace_bytes(int B, int V, int gamma_max, spec_dtype dt, s
   const size_t dense = dense_bytes(n_slots, V);
   if (filter_on(V, sp)) {
     const size_t thr = dense + thr_bytes(n_slots);
-    if (!filter_supported(B, V, gamma_max, sp)) return thr;
+    // the fused path with thresholds (uniform bf16 batches) needs the thresholds ahead of its arrays
+    const size_t fthr = fused_bytes(n_slots, V) + thr_bytes(n_slots);
+    const size_t off_sparse = thr > fthr ? thr : fthr;
+    if (!filter_supported(B, V, gamma_max, sp)) return off_sparse;
     const size_t sparse = filter_bytes((int64_t)B * (2 * gamma_max + 1), V, sp.top_k) + fallback_bytes(B, n_slots, V);
-    return sparse > thr ? sparse : thr;
+    return sparse > off_sparse ? sparse : off_sparse;
   }
   const size_t fused = fused_bytes(n_slots, V);
   return dense > fused ? dense : fused;
@@ -416,9 +419,26 @@ int spec_verify_batch_ex(int B, int V, int gamma_max, spec_dtype dt, const void*
     if (launch_fallback_requests(fb, fa, want_kl ? 1 : 0, dtc, vec, st) != hipSuccess) return SPEC_ERR_LAUNCH;
     return SPEC_OK;
   }
-  if (!filtered && !want_kl && !op.multi && fused_ok(B, V, gamma_max)) {
+  // filtered calls off the sparse path (top-p alone, a larger k) on a uniform bf16 batch: one
+  // threshold per logical row, then the fused path with every logit below its row's threshold
+  // masked (a ragged or fp32 batch takes the dense threshold path below)
+  const bool masked = filtered && dt == SPEC_BF16 && vec && (int64_t)n_draft_rows == (int64_t)B * gamma_max;
+  if ((!filtered || masked) && !want_kl && !op.multi && fused_ok(B, V, gamma_max)) {
+    Carve cv{ws};
+    const float* thr = nullptr;
+    if (masked) {
+      int* cu_bad = (int*)(ws + kHdrCuBad);
+      if (launch_check_cu(cu_draft, B, gamma_max, n_draft_rows, cu_bad, st) != hipSuccess) return SPEC_ERR_LAUNCH;
+      map.cu_bad = cu_bad;
+      float* t = cv.take<float>((size_t)(2 * n_slots) * sizeof(float));
+      if (launch_threshold(map, dtc, vec, V, 2 * n_slots, sp.top_k, sp.top_p,
+                           1.4426950408889634 / (double)sp.temperature, t, st) != hipSuccess)
+        return SPEC_ERR_LAUNCH;
+      thr = t;
+    }
     FusedArgs f;
     memset(&f, 0, sizeof(f));
+    f.thr = thr;
     f.tgt = target_logits;
     f.tgt_ld = target_ld;
     f.drf = drf;
@@ -439,7 +459,6 @@ int spec_verify_batch_ex(int B, int V, int gamma_max, spec_dtype dt, const void*
     f.seed = seed;
     f.step = step;
     f.tag = next_tag();
-    Carve cv{ws};
     f.part = cv.take<uint64_t>((size_t)f.n_teams * ns * 2 * fused_record_bytes());
     f.smass = cv.take<uint64_t>((size_t)f.n_teams * ns * 4 * sizeof(uint64_t));
     f.arrive = cv.take<uint32_t>((size_t)f.n_teams * kMaxMembers * sizeof(uint32_t));

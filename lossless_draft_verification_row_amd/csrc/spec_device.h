@@ -760,10 +760,11 @@ __device__ void pair_sums_fp64(const void* prow, const void* qrow, int V, float 
 // 2^(l c - refp) / zp (refp and zp as the streaming passes formed them), q alike.  Every term is
 // positive, so the sum keeps the relative precision of its terms (fp32 each, about 1e-6 at
 // worst from the exponent's rounding) however small A is; 16 terms are added in fp32, the runs
-// in fp64 (guide page "5.1 投机解码核心原理" §4.3).  `red` holds kWaves doubles of LDS.
+// in fp64 (guide page "5.1 投机解码核心原理" §4.3).  Logits below taup / tauq are masked.  `red`
+// holds kWaves doubles of LDS.
 template <int DT, bool VEC>
 __device__ double pair_overlap(const void* prow, const void* qrow, int V, float c, float refp, float refq, double zp,
-                               double zq, double* red) {
+                               double zq, float taup, float tauq, double* red) {
   const int t = threadIdx.x;
   const float ip = (float)(1.0 / zp), iq = (float)(1.0 / zq);
   constexpr int kStep = kThreads * 16;
@@ -784,8 +785,11 @@ __device__ double pair_overlap(const void* prow, const void* qrow, int V, float 
       raw_run_unpack<DT, VEC>(rq[u], qrow, V, xu, vq);
       float s = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        s += fminf(__builtin_amdgcn_exp2f(fmaf(vp[e], c, -refp)) * ip, __builtin_amdgcn_exp2f(fmaf(vq[e], c, -refq)) * iq);
+      for (int e = 0; e < 16; ++e) {
+        const float pe = vp[e] < taup ? 0.f : __builtin_amdgcn_exp2f(fmaf(vp[e], c, -refp)) * ip;
+        const float qe = vq[e] < tauq ? 0.f : __builtin_amdgcn_exp2f(fmaf(vq[e], c, -refq)) * iq;
+        s += fminf(pe, qe);
+      }
       a += (double)s;
     }
   }

@@ -299,6 +299,12 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   TeamRaw pre[3];   // teams wave, wave + 4 and (gamma >= 8) wave + 8
   int ytok = -1;
   float ly_p = 0.f, ly_q = 0.f;
+  // filtered off the sparse path (uniform batches): position t's thresholds, target and draft
+  float thp = -INFINITY, thq = -INFINITY;
+  if (a.thr && guess_in && t <= a.G) {
+    thp = a.thr[2 * (cg + b + t)];
+    if (t < a.G) thq = a.thr[2 * (cg + b + t) + 1];
+  }
   if (guess_in) {
     pre[0] = team_load<MODE>(a, rrs, cg, b, a.G, wave);
     pre[1] = team_load<MODE>(a, rrs, cg, b, a.G, wave + kWaves);
@@ -338,6 +344,9 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   }
   if (t >= g) ytok = -1;
   if (MODE == kFuTokenOnly && ytok >= 0 && ytok < a.V) ly_p = logit_at<DT>(row_ptr<DT>(a.tgt, a.tgt_ld, c0 + b + t), ytok);
+  // a token below its row's threshold has probability 0 there (no threshold: -inf, nothing below)
+  if (ly_p < thp) ly_p = -INFINITY;
+  if (ly_q < thq) ly_q = -INFINITY;
   // the draft offsets as one exclusive prefix: every request is refused when any is out of order
   if (stage_cu(a, cu_pre, L.cu, L.i)) {
     if (t <= a.G) a.out_tokens[(int64_t)b * G1 + t] = -1;
@@ -438,7 +447,10 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
         const double e = exp2_split(d);
         const bool on = use[k] && s[k] > 0.f;
         sums[2 * k] = on ? (double)s[k] * e : 0.0;
-        sums[2 * k + 1] = on ? e * ((double)w[k] + (double)s[k] * d) : 0.0;
+        // a ticket's entropy numerator rides on its slice-0 record, whose own sum is 0 when every
+        // logit of that slice is masked while the other slice's are not: the numerator counts
+        // whenever the record has a reference
+        sums[2 * k + 1] = (use[k] && ref[k] > -INFINITY) ? e * ((double)w[k] + (double)s[k] * d) : 0.0;
       }
       sums[8] = in ? sm[0] : 0.0;
       sums[9] = in ? sm[1] : 0.0;
@@ -619,7 +631,12 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
   const int x0 = k * kChunk + grp * kGroup + quarter * 16;
   float wv[16], vq[16];
   float refp = 0.f, refq = 0.f, rr = 0.f;
+  float ctp = -INFINITY, ctq = -INFINITY;   // the picked position's thresholds (filtered, uniform)
   if (k >= 0) {
+    if (a.thr) {
+      ctp = a.thr[2 * rpos];
+      if (wkind == 1) ctq = a.thr[2 * rpos + 1];
+    }
     load_run16<DT, VEC>(row_ptr<DT>(a.tgt, a.tgt_ld, rpos), a.V, x0, wv);
     if (wkind == 1) load_run16<DT, VEC>(row_ptr<DT>(a.drf, a.drf_ld, c0 + F.pos), a.V, x0, vq);
     float sp_, wp_;
@@ -710,16 +727,30 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
 
   if (k >= 0) {
     // E2. levels 2 and 3 inside chunk k.  Weights are relative within the chunk: e_p (p only)
-    // or max(e_p r - e_q, 0) with r = alpha_p / alpha_q.
+    // or max(e_p r - e_q, 0) with r = alpha_p / alpha_q.  Logits below a row's threshold weigh 0.
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if (wv[e] < ctp) wv[e] = -INFINITY;
+      if (vq[e] < ctq) vq[e] = -INFINITY;
+    }
     if (wkind == 1) {
-      const double alp = exp2_split((double)refp - (double)TP.M[0]) / TP.z[0];
-      const double alq = exp2_split((double)refq - (double)TP.M[1]) / TP.z[1];
-      rr = (float)(alp / alq);
+      // a chunk where q keeps nothing (its reference is -inf: every draft logit masked) has
+      // [p - q]_+ = p there, so its weights are e_p alone
+      const bool hq = refq > -INFINITY;
+      if (hq) {
+        const double alp = exp2_split((double)refp - (double)TP.M[0]) / TP.z[0];
+        const double alq = exp2_split((double)refq - (double)TP.M[1]) / TP.z[1];
+        rr = (float)(alp / alq);
+      }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float ep = __builtin_amdgcn_exp2f(fmaf(wv[e], a.c, -refp));
-        const float eq = __builtin_amdgcn_exp2f(fmaf(vq[e], a.c, -refq));
-        wv[e] = fmaxf(fmaf(ep, rr, -eq), 0.f);
+        if (hq) {
+          const float eq = __builtin_amdgcn_exp2f(fmaf(vq[e], a.c, -refq));
+          wv[e] = fmaxf(fmaf(ep, rr, -eq), 0.f);
+        } else {
+          wv[e] = ep;
+        }
       }
     } else {
       const int yx = F.y;
@@ -788,11 +819,13 @@ __device__ void finalize_request(const FusedArgs& a, LdsFin& L, int b) {
       const TeamL T = F.team[i];
       const void* prow = row_ptr<DT>(a.tgt, a.tgt_ld, c0 + b + i);
       const void* qrow = row_ptr<DT>(a.drf, a.drf_ld, c0 + i);
+      const float tp = a.thr ? a.thr[2 * (c0 + b + i)] : -INFINITY;
+      const float tq = a.thr ? a.thr[2 * (c0 + b + i) + 1] : -INFINITY;
       double A, beta;
       if ((lbm >> i) & 1ull) {
-        pair_sums_fp64<DT, VEC, false>(prow, qrow, a.V, a.c, T.M[0], T.M[1], -INFINITY, -INFINITY, F.red, A, beta);
+        pair_sums_fp64<DT, VEC, false>(prow, qrow, a.V, a.c, T.M[0], T.M[1], tp, tq, F.red, A, beta);
       } else {
-        A = pair_overlap<DT, VEC>(prow, qrow, a.V, a.c, T.M[0], T.M[1], T.z[0], T.z[1], F.red);
+        A = pair_overlap<DT, VEC>(prow, qrow, a.V, a.c, T.M[0], T.M[1], T.z[0], T.z[1], tp, tq, F.red);
         beta = T.beta;
       }
       if (t == 0) {
@@ -927,6 +960,24 @@ __device__ __forceinline__ void mask_tail_raw(int V, int base, RawSlice<DT>& r) 
     else r.w[j] = 0xff800000u;
   }
 }
+// Filtering off the sparse path: every logit of a raw slice below the row's threshold becomes
+// -inf (weight 0 from here on, as the logits past V); NaN compares false and stays, so a
+// non-finite row is still reported.
+template <int DT>
+__device__ __forceinline__ void mask_below_raw(RawSlice<DT>& r, float tau) {
+#pragma unroll
+  for (int k = 0; k < RawSlice<DT>::kWords; ++k) {
+    const uint32_t w = r.w[k];
+    if constexpr (DT == kDtBF16) {
+      const uint32_t lo = __uint_as_float(w << 16) < tau ? 0xff80u : (w & 0xffffu);
+      const uint32_t hi = __uint_as_float(w & 0xffff0000u) < tau ? 0xff800000u : (w & 0xffff0000u);
+      r.w[k] = hi | lo;
+    } else {
+      r.w[k] = __uint_as_float(w) < tau ? 0xff800000u : w;
+    }
+  }
+}
+
 // e = 2^(l c - ref) of a slice given as raw words, with s = sum e and (ENT) w = sum e (l c - ref).
 // A masked logit (-inf) gives e = 0 and a NaN product in w; such a thread recomputes w from its
 // e-values, using log2(e) for l c - ref.  Words are consumed in groups of two (four logits) so
@@ -1038,7 +1089,7 @@ __device__ __forceinline__ void fold_waves(const float (*pw)[4], float& ref, flo
   float M = -INFINITY;
 #pragma unroll
   for (int k = 0; k < kWaves; ++k) M = fmaxf(M, pw[k][0]);
-  ref = 0.f; s = 0.f; w = 0.f;
+  ref = -INFINITY; s = 0.f; w = 0.f;   // a slice with no finite logit: no reference either
   if (!(M > -INFINITY)) return;
   ref = M;
 #pragma unroll
@@ -1056,7 +1107,7 @@ __device__ __forceinline__ void fold_waves_rt(const float (*pw)[4], int K, bool 
   float M = -INFINITY;
 #pragma unroll
   for (int k = 0; k < kWaves; ++k) M = fmaxf(M, pw[k][0]);
-  ref = 0.f; s = 0.f; w = 0.f;
+  ref = -INFINITY; s = 0.f; w = 0.f;   // a slice with no finite logit: no reference either
   if (!(M > -INFINITY)) return;
   ref = M;
 #pragma unroll
@@ -1221,10 +1272,12 @@ __device__ __forceinline__ float residual_slice(const ResidualScale& R, const fl
 // after it on the same XCD; every wait is bounded.
 // Eight waves per SIMD for aligned bf16 rows (64 VGPRs: three of a thread's draft e-values
 // wait in LDS); other layouts keep the compiler's choice.
-constexpr int fused_min_waves(int dt, bool vec) { return dt == kDtBF16 && vec ? 8 : 1; }
+// Eight waves per SIMD (64 registers) for aligned bf16 rows; the masked variant's extra
+// compares need more, six waves per SIMD (80 registers), so that nothing spills.
+constexpr int fused_min_waves(int dt, bool vec, bool mask) { return dt == kDtBF16 && vec ? (mask ? 6 : 8) : 1; }
 
-template <int DT, bool VEC, int MODE, bool TENT, bool RAG>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_min_waves(DT, VEC)))) void k_fused(
+template <int DT, bool VEC, int MODE, bool TENT, bool RAG, bool MASK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_min_waves(DT, VEC, MASK)))) void k_fused(
     FusedArgs a) {
   __shared__ FusedLds L;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -1361,6 +1414,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_
     load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, base, rp[0]);
     load_raw<DT, false>(row_ptr<DT>(a.tgt, a.tgt_ld, r), a.V, base + kChunk, rp[1]);
   }
+  // filtering off the sparse path (uniform batches only): this team's thresholds, at logical
+  // rows 2 r and 2 r + 1 (a uniform batch's target row r is its slot b (G + 1) + i)
+  float tau_p = -INFINITY, tau_q = -INFINITY;
+  if constexpr (MASK) {
+    tau_p = __int_as_float(sload_i32((const int32_t*)a.thr + 2 * r));
+    if (pair) tau_q = __int_as_float(sload_i32((const int32_t*)a.thr + 2 * r + 1));
+  }
   if (MODE == kFuGreedy) {
     float vp[2][kPerThread];
     unpack_raw<DT>(rp[0], vp[0]);
@@ -1424,6 +1484,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_
     mask_tail_raw<DT>(a.V, base, rp[0]);
     mask_tail_raw<DT>(a.V, base + kChunk, rp[1]);
   }
+  if constexpr (MASK) {
+    mask_below_raw<DT>(rp[0], tau_p);
+    mask_below_raw<DT>(rp[1], tau_p);
+  }
   float mp = max_raw2<DT>(rp[0], rp[1]);
   dpp_max1(mp);
   float refp = mp > -INFINITY ? mp * c : 0.f;
@@ -1453,6 +1517,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_
     if (VEC && tail) {
       mask_tail_raw<DT>(a.V, base, rq[0]);
       mask_tail_raw<DT>(a.V, base + kChunk, rq[1]);
+    }
+    if constexpr (MASK) {
+      mask_below_raw<DT>(rq[0], tau_q);
+      mask_below_raw<DT>(rq[1], tau_q);
     }
     float mq = max_raw2<DT>(rq[0], rq[1]);
     dpp_max1(mq);
@@ -1540,12 +1608,25 @@ static hipError_t launch_fused_t(FusedArgs a, hipStream_t st, hipEvent_t ev0, hi
   // ragged sampling batches find each place's request among the offsets (a kernel of their own,
   // so that the uniform kernel keeps its registers)
   const bool rag = MODE == kFuSample && a.ragged;
+  if constexpr (DT == kDtBF16 && VEC && MODE != kFuGreedy) {
+    // filtered off the sparse path: the thresholds mask the logits (uniform batches)
+    if (a.thr) {
+      if (rag) return hipErrorInvalidValue;
+      if (a.want_t_ent) launch_timed(k_fused<DT, VEC, MODE, true, false, true>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
+      else launch_timed(k_fused<DT, VEC, MODE, false, false, true>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((k_fused_finalize<DT, VEC, MODE>), dim3(a.B), dim3(kThreads), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  if (a.thr) return hipErrorInvalidValue;
   if (MODE != kFuGreedy && a.want_t_ent) {
-    if (rag) launch_timed(k_fused<DT, VEC, MODE, true, true>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
-    else launch_timed(k_fused<DT, VEC, MODE, true, false>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
+    if (rag) launch_timed(k_fused<DT, VEC, MODE, true, true, false>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
+    else launch_timed(k_fused<DT, VEC, MODE, true, false, false>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
   } else {
-    if (rag) launch_timed(k_fused<DT, VEC, MODE, false, true>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
-    else launch_timed(k_fused<DT, VEC, MODE, false, false>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
+    if (rag) launch_timed(k_fused<DT, VEC, MODE, false, true, false>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
+    else launch_timed(k_fused<DT, VEC, MODE, false, false, false>, dim3((unsigned)grid), dim3(kThreads), st, ev0, ev1, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

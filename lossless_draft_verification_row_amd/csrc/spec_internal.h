@@ -142,6 +142,9 @@ struct FusedArgs {
   uint64_t* smass;      // [n_teams][n_s][4 waves] tagged residual masses
   uint32_t* arrive;     // [n_teams][kMaxMembers] a member's flag: the call's tag once its records are out
   float* ylog;          // [n_draft_rows][2]: each draft token's logit in its target and draft row
+  const float* thr;     // filtered calls off the sparse path, uniform batches only: per logical row
+                        // 2 (b (G + 1) + i) + kind (kind 0 target, 1 draft) the filter threshold,
+                        // a logit below it masked; nullptr: unfiltered
   int ragged;           // 1 unless every request has G draft rows: a dispatch place then finds its
                         // request among the offsets instead of from its place
   int poll_delay;       // wait before the first team poll, in 10 ns ticks

@@ -526,6 +526,18 @@ def test_dense_filtered_sampling(k, p):
     check(inp, sp)
 
 
+@pytest.mark.parametrize("k,p,token_only", [(0, 0.9, False), (0, 0.5, False), (0, 0.99, False), (1000, 1.0, False),
+                                             (300, 0.95, False), (0, 0.9, True)])
+def test_filtered_uniform_batch_masked_fused(k, p, token_only):
+    """Filters off the sparse path (top-p alone, top-k above 256) on a uniform bf16 batch, every
+    request with gamma drafts: per-row thresholds, then the fused streaming kernel with every
+    logit below its row's threshold masked.  Two vocabularies, one with a ragged last chunk."""
+    sp = O.SamplingParams(0.7, k, p)
+    for V in (V_SMALL, 3 * 4096):
+        inp = filtered_inputs(5, V, [4, 4, 4, 4, 4], sp, seed=400 + k + int(100 * p) + V, token_only=token_only)
+        check(inp, sp)
+
+
 def test_dense_filtered_fp32():
     sp = O.SamplingParams(0.9, 0, 0.8)
     inp = filtered_inputs(3, 2 * 4096 + 36, [4, 2, 3], sp, dtype="f32", seed=8)

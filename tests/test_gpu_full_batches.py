@@ -88,7 +88,8 @@ def test_full_batch_filtered_every_request():
 
 
 def test_full_batch_top_p_only_every_request():
-    """The filtered workload's shape with top-p 0.9 alone (the dense threshold path): every
+    """The filtered workload's shape with top-p 0.9 alone (a uniform bf16 batch: per-row
+    thresholds, then the fused streaming kernel with the logits below them masked): every
     request."""
     wl = W.WORKLOADS[5]
     sp = O.SamplingParams(wl.temperature, 0, wl.top_p)

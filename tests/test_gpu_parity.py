@@ -209,6 +209,26 @@ def test_near_identical_rows_small_tv(path, V):
     assert np.median(tv) < 0.01
 
 
+@pytest.mark.parametrize("path", PATHS)
+def test_masked_leading_slice_entropy(path):
+    """Rows whose first 8192 logits are -inf (a caller's masked vocabulary block): a streaming
+    ticket's first slice then holds no finite logit while its second does, and the entropy
+    numerator the ticket files with its first slice must still count.  Target and draft
+    entropies, max-probabilities and 1 - TV against the oracle."""
+    V = 3 * 4096 + 72
+    inp = custom_inputs(4, V, [3, 3, 3, 3], T=0.8, seed=83)
+    for arr in (inp.target, inp.draft):
+        f = W.bf16_bits_to_f32(arr).copy()
+        f[1::2, :8192] = -np.inf
+        arr[:] = W.bf16_bits_from_f32(f)
+    rng = np.random.default_rng(84)
+    dv = W.bf16_bits_to_f32(inp.draft).astype(np.float64)
+    for r in range(inp.draft.shape[0]):
+        q = O.row_distribution(dv[r], O.SamplingParams(0.8)).probs
+        inp.tokens[r] = int(rng.choice(V, p=q / q.sum()))
+    check(inp, O.SamplingParams(0.8), path=path)
+
+
 def test_near_identical_rows_one_minus_tv_without_l1():
     """The benchmark's outputs (1 - TV but no L1) on near-identical rows: 1 - TV = 1 - beta is
     then close to 1 and precise from the streaming sums, so the finalize recomputes nothing;
