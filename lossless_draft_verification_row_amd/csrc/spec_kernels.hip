@@ -310,11 +310,8 @@ __device__ void thr_select(ThrLds& S, int nb, unsigned long long base, Reach rea
 // the row.  A bf16 row first tries the window of the 4096 values below its maximum (two passes
 // in all), which settles every realistic row.
 template <int DT, bool VEC>
-__device__ void threshold_row(const RowMap& m, int V, int k, float top_p, double c, float* __restrict__ thr,
-                              int lr) {
-  const void* row = resolve_row<DT>(m, lr);
-  if (row == nullptr) return;
-  __shared__ ThrLds S;
+__device__ void threshold_row_s(ThrLds& S, const void* row, int V, int k, float top_p, double c,
+                                float* __restrict__ thr, int lr) {
   constexpr int KB = DT == kDtBF16 ? 16 : 32;   // key bits
   constexpr int NL = DT == kDtBF16 ? 2 : 3;     // digits
   const int t = threadIdx.x;
@@ -407,9 +404,229 @@ __device__ void threshold_row(const RowMap& m, int V, int k, float top_p, double
 }
 
 template <int DT, bool VEC>
+__device__ void threshold_row(const RowMap& m, int V, int k, float top_p, double c, float* __restrict__ thr,
+                              int lr) {
+  const void* row = resolve_row<DT>(m, lr);
+  if (row == nullptr) return;
+  __shared__ ThrLds S;
+  threshold_row_s<DT, VEC>(S, row, V, k, top_p, c, thr, lr);
+}
+
+template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_threshold(RowMap m, int V, int k, float top_p, double c,
                                                          float* __restrict__ thr) {
   threshold_row<DT, VEC>(m, V, k, top_p, c, thr, blockIdx.x);
+}
+
+// ---------------------------------------------------------------- one-pass bf16 threshold
+
+// bf16 rows in one pass: an exact per-value histogram.  A bf16 logit of magnitude in
+// [2^-24, 2^24) has one of 48 * 128 bit patterns per sign, so one LDS bin per pattern counts
+// every value group of such a row exactly.  The filter is then read off the bins as
+// threshold_row reads it off its window, walking the value groups from the top (rank 0 = the
+// largest value): top-k walks the counts, top-p walks the masses n exp2((v - m) c), in fp64,
+// against top_p times their sum over the top-k set; m is the largest populated value.  The bin
+// of a pair of logits is formed with packed 16-bit arithmetic (two logits per instruction, no
+// branch): logits outside the covered range land in one overflow bin per sign.  A row with
+// overflow is read again and its overflow sorted out: +-0 (a value group of its own), -inf (no
+// mass; top-k counts only finite logits, and fewer than k of them keep the whole row), anything
+// else (NaN, +inf, a magnitude below 2^-24 or from 2^24 up) leaves the row to threshold_row_s,
+// run by the same workgroup on the same LDS.  A row without overflow is read once (twice or more
+// in threshold_row), and no exp is taken per logit.
+constexpr int kHE0 = 127 - 24;                 // lowest biased exponent covered
+constexpr int kHSide = 48 * 128;               // value bins per sign
+constexpr int kHRanks = 2 * kHSide + 1;        // value groups, from the top (+-0 in the middle)
+constexpr int kHBins = 2 * kHSide + 2;         // positives [0, kHSide), overflow kHSide, negatives
+                                               // [kHSide + 1, 2 kHSide + 1), overflow 2 kHSide + 1
+constexpr int kHPer = (kHRanks + kThreads - 1) / kThreads;   // ranks per thread in a walk
+
+typedef unsigned short hu16x2 __attribute__((ext_vector_type(2)));
+
+struct HistLds {
+  union {
+    ThrLds t;                  // threshold_row_s, for rows the histogram does not cover
+    uint32_t n[kHBins];
+  } u;
+  double redd[kWaves];
+  int redi[kWaves];
+  int digit;
+  uint32_t zeros;
+  double zt;
+};
+
+// Count of value rank r (0: the largest covered value; kHSide: +-0).
+__device__ __forceinline__ uint32_t hist_count(const HistLds& S, int r) {
+  if (r < kHSide) return S.u.n[kHSide - 1 - r];
+  return r == kHSide ? S.zeros : S.u.n[r];
+}
+// Value of value rank r.
+__device__ __forceinline__ float hist_value(int r) {
+  if (r == kHSide) return 0.f;
+  const uint32_t h = r < kHSide ? (uint32_t)(kHSide - 1 - r) : (0x8000u | (uint32_t)(r - kHSide - 1));
+  return __uint_as_float((h + (uint32_t)(kHE0 << 7)) << 16);
+}
+
+// The bins of the two bf16 logits of word w: per half, min(|h| - base, kHSide) + sign * (kHSide + 1).
+__device__ __forceinline__ uint32_t hist_bin2(uint32_t w) {
+  const hu16x2 h = __builtin_bit_cast(hu16x2, w);
+  const hu16x2 base = {(unsigned short)(kHE0 << 7), (unsigned short)(kHE0 << 7)};
+  const hu16x2 side = {(unsigned short)kHSide, (unsigned short)kHSide};
+  const hu16x2 step = {(unsigned short)(kHSide + 1), (unsigned short)(kHSide + 1)};
+  const hu16x2 mag = {0x7fff, 0x7fff};
+  const hu16x2 idx = __builtin_elementwise_min((hu16x2)((h & mag) - base), side);
+  return __builtin_bit_cast(uint32_t, (hu16x2)((h >> (hu16x2){15, 15}) * step + idx));
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void k_threshold_hist(RowMap m, int V, int k, float top_p, double c,
+                                                              float* __restrict__ thr) {
+  const int lr = blockIdx.x;
+  const void* row = resolve_row<kDtBF16>(m, lr);
+  if (row == nullptr) return;
+  __shared__ HistLds S;
+  uint32_t* H = S.u.n;
+  const int t = threadIdx.x;
+  for (int i = t; i < kHBins; i += kThreads) H[i] = 0u;
+  if (t == 0) S.zeros = 0u;
+  __syncthreads();
+
+  // the pass: each logit's pattern into its bin, kHLoads 16-byte words in flight per thread
+  // (three workgroups per CU: the loads, not the bins, set the pace)
+  constexpr int kHLoads = 8;
+  int tail = 0;
+  if constexpr (VEC) {
+    const int nv = V >> 3;
+    for (int i0 = 0; i0 < nv; i0 += kHLoads * kThreads) {
+      uint4 w[kHLoads];
+#pragma unroll
+      for (int j = 0; j < kHLoads; ++j) {   // unconditional (past the end: the last word again)
+        const int i = min(i0 + j * kThreads + t, nv - 1);
+        w[j] = ld_nt16((const uint4*)row + i);
+      }
+#pragma unroll
+      for (int j = 0; j < kHLoads; ++j) {
+        if (i0 + j * kThreads + t < nv) {
+          const uint32_t ws[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t b = hist_bin2(ws[q]);
+            atomicAdd(&H[b & 0xffffu], 1u);
+            atomicAdd(&H[b >> 16], 1u);
+          }
+        }
+      }
+    }
+    tail = nv << 3;
+  }
+  for (int i = tail + t; i < V; i += kThreads) atomicAdd(&H[hist_bin2(((const uint16_t*)row)[i]) & 0xffffu], 1u);
+  __syncthreads();
+  if (H[kHSide] | H[2 * kHSide + 1]) {
+    // overflow: read the row again and sort it out (+-0 counted, -inf skipped, anything else
+    // sends the row to the search from memory)
+    uint32_t zc = 0u;
+    int other = 0;
+    auto sort_out = [&](uint32_t h) {
+      const uint32_t a = h & 0x7fffu;
+      const uint32_t idx = a - (uint32_t)(kHE0 << 7);
+      if (idx >= (uint32_t)kHSide) {
+        if (a == 0u) ++zc;
+        else if (h != 0xff80u) other = 1;
+      }
+    };
+    if constexpr (VEC) {
+      const int nv = V >> 3;
+      for (int i = t; i < nv; i += kThreads) {
+        const uint4 w = ld_nt16((const uint4*)row + i);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { sort_out(ws[q] & 0xffffu); sort_out(ws[q] >> 16); }
+      }
+    }
+    for (int i = tail + t; i < V; i += kThreads) sort_out(((const uint16_t*)row)[i]);
+    if (block_or(other, S.redi)) {
+      threshold_row_s<kDtBF16, VEC>(S.u.t, row, V, k, top_p, c, thr, lr);
+      return;
+    }
+    const double z = block_sum_d((double)zc, S.redd);
+    if (t == 0) S.zeros = (uint32_t)z;
+    __syncthreads();
+  }
+  const bool use_k = k > 0 && k < V;
+  const bool use_p = top_p < 1.f;
+  const int r0 = kHPer * t;   // this thread's ranks: r0 .. r0 + kHPer - 1
+  // the largest populated value group: the row max
+  int first = INT_MAX;
+  for (int q = kHPer - 1; q >= 0; --q) {
+    const int r = r0 + q;
+    if (r < kHRanks && hist_count(S, r)) first = r;
+  }
+  first = block_min_i(first, S.redi);
+  if (first == INT_MAX || !(use_k || use_p)) {   // no finite logit, or nothing to filter
+    if (t == 0) thr[lr] = -INFINITY;
+    return;
+  }
+  const float mx = hist_value(first);
+  int rk = kHRanks - 1;   // last rank of the top-k set
+  if (use_k) {
+    int cs = 0;
+    for (int q = 0; q < kHPer; ++q) {
+      const int r = r0 + q;
+      if (r < kHRanks) cs += (int)hist_count(S, r);
+    }
+    int excl, incl;
+    block_scan(cs, S.redi, excl, incl);
+    if (t == 0) S.digit = kHRanks - 1;   // fewer than k finite logits: the k-th largest is -inf
+    __syncthreads();
+    if (excl < k && incl >= k) {
+      int run = excl;
+      for (int q = 0; q < kHPer && r0 + q < kHRanks; ++q) {
+        run += (int)hist_count(S, r0 + q);
+        if (run >= k) { S.digit = r0 + q; break; }
+      }
+    }
+    __syncthreads();
+    rk = S.digit;
+    __syncthreads();
+  }
+  int rp = rk;
+  if (use_p) {
+    double ms = 0.0;
+    for (int q = 0; q < kHPer; ++q) {
+      const int r = r0 + q;
+      if (r > rk) break;
+      const uint32_t n = hist_count(S, r);
+      if (n) ms += (double)n * exp2(((double)hist_value(r) - (double)mx) * c);
+    }
+    double excl, incl;
+    block_scan(ms, S.redd, excl, incl);
+    if (t == kThreads - 1) S.zt = incl;   // the mass of the top-k set
+    if (t == 0) S.digit = -1;
+    __syncthreads();
+    const double target = (double)top_p * S.zt;
+    if (!(excl >= target) && incl >= target) {
+      // the boundary value group is among this thread's ranks (if rounding of the walk leaves
+      // it short, the last one with mass)
+      double run = excl;
+      int last = -1;
+      for (int q = 0; q < kHPer; ++q) {
+        const int r = r0 + q;
+        if (r > rk) break;
+        const uint32_t n = hist_count(S, r);
+        if (!n) continue;
+        last = r;
+        run += (double)n * exp2(((double)hist_value(r) - (double)mx) * c);
+        if (run >= target) break;
+      }
+      S.digit = last;
+    }
+    __syncthreads();
+    if (S.digit >= 0) rp = S.digit;   // -1 only if no thread saw the crossing: keep the top-k set
+  }
+  if (t == 0) {
+    // the lowest rank keeps every finite logit: -inf then (-inf logits weigh nothing either way)
+    const int r = min(rk, rp);
+    thr[lr] = r >= kHRanks - 1 ? -INFINITY : hist_value(r);
+  }
 }
 
 // ---------------------------------------------------------------- pass 1
@@ -1254,8 +1471,8 @@ hipError_t launch_threshold(const RowMap& m, int dt, int vec, int V, int n_lr, i
   if (n_lr < 1) return hipSuccess;
   const dim3 g(n_lr), blk(kThreads);
   if (dt == kDtBF16) {
-    if (vec) hipLaunchKernelGGL((k_threshold<kDtBF16, true>), g, blk, 0, st, m, V, k, top_p, c, thr);
-    else hipLaunchKernelGGL((k_threshold<kDtBF16, false>), g, blk, 0, st, m, V, k, top_p, c, thr);
+    if (vec) hipLaunchKernelGGL((k_threshold_hist<true>), g, blk, 0, st, m, V, k, top_p, c, thr);
+    else hipLaunchKernelGGL((k_threshold_hist<false>), g, blk, 0, st, m, V, k, top_p, c, thr);
   } else {
     if (vec) hipLaunchKernelGGL((k_threshold<kDtF32, true>), g, blk, 0, st, m, V, k, top_p, c, thr);
     else hipLaunchKernelGGL((k_threshold<kDtF32, false>), g, blk, 0, st, m, V, k, top_p, c, thr);

@@ -538,6 +538,31 @@ def test_filtered_uniform_batch_masked_fused(k, p, token_only):
         check(inp, sp)
 
 
+@pytest.mark.parametrize("k,p", [(0, 0.9), (1000, 1.0), (300, 0.95)])
+def test_threshold_value_bins_edges(k, p, monkeypatch):
+    """Rows at the edges of the one-pass bf16 threshold (a bin per bf16 value of magnitude in
+    [2^-24, 2^24), one for +-0), in a uniform batch (the masked fused path) and again on the
+    multi-kernel path: a coarse value grid (ties, a zero value group), a long run of -0, a long
+    -inf run, and rows holding a magnitude outside the binned range (tiny, huge negative), which
+    the kernel hands to the search from memory."""
+    sp = O.SamplingParams(0.7, k, p)
+    V = V_SMALL
+    inp = filtered_inputs(5, V, [4, 4, 4, 4, 4], sp, seed=500 + k + int(100 * p))
+    rng = np.random.default_rng(7)
+    for arr in (inp.target, inp.draft):
+        f = W.bf16_bits_to_f32(arr)
+        f[0::3] = np.round(f[0::3] * 2.0) / 2.0
+        f[0::6, :V // 8] = -0.0
+        f[1::3, 4096:4096 + 3000] = -np.inf
+        f[2::3, rng.integers(0, V, 20)] = 3e-9
+        f[2::6, rng.integers(0, V, 5)] = -4e7
+        arr[...] = W.bf16_bits_from_f32(f)
+    _redraw_tokens(inp, sp, 901)
+    check(inp, sp)
+    monkeypatch.setattr(sys.modules[__name__], "_PATH", "multi")
+    check(inp, sp)
+
+
 def test_dense_filtered_fp32():
     sp = O.SamplingParams(0.9, 0, 0.8)
     inp = filtered_inputs(3, 2 * 4096 + 36, [4, 2, 3], sp, dtype="f32", seed=8)
