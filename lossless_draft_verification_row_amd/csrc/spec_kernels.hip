@@ -466,6 +466,52 @@ __device__ __forceinline__ float hist_value(int r) {
   return __uint_as_float((h + (uint32_t)(kHE0 << 7)) << 16);
 }
 
+// Masses exp2((v_r - m) c) of the value ranks r0, r0 + 1, ... in turn: exp2 afresh at the first
+// rank and wherever a rank opens a new binade (or is the +-0 group), else one multiply by the
+// binade's step factor exp2(-u c), u the spacing of bf16 values in it (the next rank lies one
+// spacing lower on either sign).  Both walks over a thread's ranks take the same sequence.
+struct RankMass {
+  double e = 0.0, rho = 0.0;
+  int seg = -2;
+  __device__ __forceinline__ double at(int r, float mx, double c) {
+    int sg = -1;
+    if (r != kHSide) {
+      const uint32_t h = (r < kHSide ? (uint32_t)(kHSide - 1 - r) : (0x8000u | (uint32_t)(r - kHSide - 1))) +
+                         (uint32_t)(kHE0 << 7);
+      sg = (int)(h >> 7);   // sign and exponent field
+    }
+    if (sg >= 0 && sg == seg) {
+      e *= rho;
+    } else {
+      e = exp2(((double)hist_value(r) - (double)mx) * c);
+      if (sg >= 0) rho = exp2(-ldexp(1.0, (sg & 0xff) - 134) * c);
+      seg = sg;
+    }
+    return e;
+  }
+};
+
+// f(r, n) for this thread's value ranks r = r0, r0 + 1, ... up to r0 + kHPer - 1 and rmax, in
+// order, n the rank's count, until f returns false.  The counts are read from LDS eight at a
+// time ahead of their use.
+template <typename F>
+__device__ __forceinline__ void walk_ranks(const HistLds& S, int r0, int rmax, F f) {
+  for (int q0 = 0; q0 < kHPer; q0 += 8) {
+    uint32_t c8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = r0 + q0 + j;
+      c8[j] = (q0 + j < kHPer && r <= rmax) ? hist_count(S, r) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = r0 + q0 + j;
+      if (q0 + j >= kHPer || r > rmax) return;
+      if (!f(r, c8[j])) return;
+    }
+  }
+}
+
 // The bins of the two bf16 logits of word w: per half, min(|h| - base, kHSide) + sign * (kHSide + 1).
 __device__ __forceinline__ uint32_t hist_bin2(uint32_t w) {
   const hu16x2 h = __builtin_bit_cast(hu16x2, w);
@@ -492,7 +538,7 @@ __global__ __launch_bounds__(kThreads) void k_threshold_hist(RowMap m, int V, in
 
   // the pass: each logit's pattern into its bin, kHLoads 16-byte words in flight per thread
   // (three workgroups per CU: the loads, not the bins, set the pace)
-  constexpr int kHLoads = 8;
+  constexpr int kHLoads = 16;
   int tail = 0;
   if constexpr (VEC) {
     const int nv = V >> 3;
@@ -556,10 +602,10 @@ __global__ __launch_bounds__(kThreads) void k_threshold_hist(RowMap m, int V, in
   const int r0 = kHPer * t;   // this thread's ranks: r0 .. r0 + kHPer - 1
   // the largest populated value group: the row max
   int first = INT_MAX;
-  for (int q = kHPer - 1; q >= 0; --q) {
-    const int r = r0 + q;
-    if (r < kHRanks && hist_count(S, r)) first = r;
-  }
+  walk_ranks(S, r0, kHRanks - 1, [&](int r, uint32_t n) {
+    if (n) first = r;
+    return n == 0u;
+  });
   first = block_min_i(first, S.redi);
   if (first == INT_MAX || !(use_k || use_p)) {   // no finite logit, or nothing to filter
     if (t == 0) thr[lr] = -INFINITY;
@@ -569,20 +615,21 @@ __global__ __launch_bounds__(kThreads) void k_threshold_hist(RowMap m, int V, in
   int rk = kHRanks - 1;   // last rank of the top-k set
   if (use_k) {
     int cs = 0;
-    for (int q = 0; q < kHPer; ++q) {
-      const int r = r0 + q;
-      if (r < kHRanks) cs += (int)hist_count(S, r);
-    }
+    walk_ranks(S, r0, kHRanks - 1, [&](int, uint32_t n) {
+      cs += (int)n;
+      return true;
+    });
     int excl, incl;
     block_scan(cs, S.redi, excl, incl);
     if (t == 0) S.digit = kHRanks - 1;   // fewer than k finite logits: the k-th largest is -inf
     __syncthreads();
     if (excl < k && incl >= k) {
       int run = excl;
-      for (int q = 0; q < kHPer && r0 + q < kHRanks; ++q) {
-        run += (int)hist_count(S, r0 + q);
-        if (run >= k) { S.digit = r0 + q; break; }
-      }
+      walk_ranks(S, r0, kHRanks - 1, [&](int r, uint32_t n) {
+        run += (int)n;
+        if (run >= k) S.digit = r;
+        return run < k;
+      });
     }
     __syncthreads();
     rk = S.digit;
@@ -591,12 +638,12 @@ __global__ __launch_bounds__(kThreads) void k_threshold_hist(RowMap m, int V, in
   int rp = rk;
   if (use_p) {
     double ms = 0.0;
-    for (int q = 0; q < kHPer; ++q) {
-      const int r = r0 + q;
-      if (r > rk) break;
-      const uint32_t n = hist_count(S, r);
-      if (n) ms += (double)n * exp2(((double)hist_value(r) - (double)mx) * c);
-    }
+    RankMass rm;
+    walk_ranks(S, r0, rk, [&](int r, uint32_t n) {
+      const double e = rm.at(r, mx, c);
+      if (n) ms += (double)n * e;
+      return true;
+    });
     double excl, incl;
     block_scan(ms, S.redd, excl, incl);
     if (t == kThreads - 1) S.zt = incl;   // the mass of the top-k set
@@ -608,15 +655,14 @@ __global__ __launch_bounds__(kThreads) void k_threshold_hist(RowMap m, int V, in
       // it short, the last one with mass)
       double run = excl;
       int last = -1;
-      for (int q = 0; q < kHPer; ++q) {
-        const int r = r0 + q;
-        if (r > rk) break;
-        const uint32_t n = hist_count(S, r);
-        if (!n) continue;
+      RankMass rm;
+      walk_ranks(S, r0, rk, [&](int r, uint32_t n) {
+        const double e = rm.at(r, mx, c);
+        if (!n) return true;
         last = r;
-        run += (double)n * exp2(((double)hist_value(r) - (double)mx) * c);
-        if (run >= target) break;
-      }
+        run += (double)n * e;
+        return !(run >= target);
+      });
       S.digit = last;
     }
     __syncthreads();
