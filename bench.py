@@ -13,6 +13,7 @@ and the fp64 oracle timed over the host's cores.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import ctypes
 import json
 import os
@@ -38,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true",
                     help="measure only --config (by default configs 3, 4 and 5 follow in per_config)")
+    ap.add_argument("--filter", type=lambda v: (int(v.split(",")[0]), float(v.split(",")[1])), default=None,
+                    metavar="K,P", help="the workload of --config with top-k K and top-p P instead of its own "
+                                        "(the filtered paths: e.g. 0,0.9 for top-p alone); use with --no-per-config")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--lm-head", action="store_true",
                     help="time the fused LM head (spec_lm_head_row_stats) on the batch-64 workload's "
@@ -371,6 +375,10 @@ def measure(cfg, args, torch, L, W, steps, warmup):
     dispatch.  Returns the inputs and the measured figures."""
     dev = torch.device("cuda", 0)
     inp = W.make_inputs(cfg)
+    if args.filter is not None:
+        k, p = args.filter
+        base = inp.wl.name.split("-topk")[0]
+        inp.wl = dataclasses.replace(inp.wl, name=f"{base}-topk{k}-topp{p:g}", top_k=k, top_p=p)
     wl = inp.wl
     if wl.temperature > 0 and inp.draft is not None and (0 < wl.top_k < wl.V or wl.top_p < 1.0):
         inp.tokens = filtered_draft_tokens(inp)
