@@ -1271,10 +1271,10 @@ __device__ __forceinline__ float residual_slice(const ResidualScale& R, const fl
 // draft's per thread in LDS).  A member waits only for members dispatched just before or
 // after it on the same XCD; every wait is bounded.
 // Eight waves per SIMD for aligned bf16 rows (64 VGPRs: three of a thread's draft e-values
-// wait in LDS); other layouts keep the compiler's choice.
-// Eight waves per SIMD (64 registers) for aligned bf16 rows; the masked variant's extra
-// compares need more, six waves per SIMD (80 registers), so that nothing spills.
-constexpr int fused_min_waves(int dt, bool vec, bool mask) { return dt == kDtBF16 && vec ? (mask ? 6 : 8) : 1; }
+// wait in LDS); other layouts keep the compiler's choice.  The masked variant's compares need
+// 72 VGPRs: seven waves per SIMD, nothing spilled (at eight it spills 12-15 registers and runs
+// slower; at six it has one workgroup per CU fewer).
+constexpr int fused_min_waves(int dt, bool vec, bool mask) { return dt == kDtBF16 && vec ? (mask ? 7 : 8) : 1; }
 
 template <int DT, bool VEC, int MODE, bool TENT, bool RAG, bool MASK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fused_min_waves(DT, VEC, MASK)))) void k_fused(
