@@ -23,6 +23,12 @@
 // at the first rejection §5.1) and the three-level sampler over the residual or p_{g+1}
 // (§5.2, one re-read chunk), and writes the outputs.
 //
+// Filtered uniform bf16 batches off the sparse path (top-p alone, top-k above 256; §2.1: p and
+// q are the distributions after temperature, top-k and top-p): the MASK variant takes one
+// threshold per row from the threshold kernel and turns every logit below it into -inf as the
+// raw words arrive, so the records, residual masses and outputs are those of the filtered
+// rows; the finalize masks the logits it reads again against the same thresholds.
+//
 // Synchronisation without read-modify-write atomics: records and flags carry the call's tag (a
 // per-call sequence number, never 0) and travel through coherent agent-scope (sc1) loads and
 // stores; a 16-byte record also carries a check word mixing the tag with its contents, so a
