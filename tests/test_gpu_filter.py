@@ -271,26 +271,35 @@ def test_filtered_repeated_calls_identical():
             assert np.array_equal(o[k], outs[0][k], equal_nan=True), k
 
 
-def test_filtered_chi2_lossless():
-    """V = 8, gamma = 3, top-k 5 then top-p 0.85 at T = 1: over 100 launches of 1024 replicated
-    requests (distinct Philox steps), the emitted token at position k, conditioned on reaching
-    k, follows the filtered p_k (alpha 1e-3).  The rows keep 3-4 tokens each and overlap
-    partly, so accepts, residual draws and bonus draws all occur."""
+@pytest.mark.parametrize("dtype,k,p", [("f32", 5, 0.85), ("bf16", 0, 0.8)])
+def test_filtered_chi2_lossless(dtype, k, p):
+    """V = 8, gamma = 3 at T = 1: over 100 launches of 1024 replicated requests (distinct
+    Philox steps), the emitted token at position k, conditioned on reaching k, follows the
+    filtered p_k (alpha 1e-3).  fp32 rows with top-k 5 then top-p 0.85 (the sparse path), and
+    bf16 rows with top-p 0.8 alone (a uniform batch: the per-row thresholds and the masked fused
+    kernel).  The rows keep 3-4 tokens each and overlap partly, so accepts, residual draws and
+    bonus draws all occur."""
     V, g, nb, nl = 8, 3, 1024, 100
     rng = np.random.default_rng(4240)
-    sp = O.SamplingParams(1.0, 5, 0.85)
+    sp = O.SamplingParams(1.0, k, p)
     tl = (rng.standard_normal((g + 1, V)) * 1.0).astype(np.float32)
     dl = (tl[:g] + rng.standard_normal((g, V)) * 0.7).astype(np.float32)
+    if dtype == "bf16":
+        tb, db = W.bf16_bits_from_f32(tl), W.bf16_bits_from_f32(dl)
+        tl, dl = W.bf16_bits_to_f32(tb), W.bf16_bits_to_f32(db)
+        target = torch.from_numpy(np.tile(tb, (nb, 1))).view(torch.bfloat16).to(DEV)
+        draft = torch.from_numpy(np.tile(db, (nb, 1))).view(torch.bfloat16).to(DEV)
+    else:
+        target = torch.from_numpy(np.tile(tl, (nb, 1))).to(DEV)
+        draft = torch.from_numpy(np.tile(dl, (nb, 1))).to(DEV)
     P = [O.row_distribution(r.astype(np.float64), sp).probs for r in tl]
     Qd = [O.row_distribution(r.astype(np.float64), sp).probs for r in dl]
-    target = torch.from_numpy(np.tile(tl, (nb, 1))).to(DEV)
-    draft = torch.from_numpy(np.tile(dl, (nb, 1))).to(DEV)
     cu = torch.arange(0, g * (nb + 1), g, dtype=torch.int32, device=DEV)
     outs, naccs = [], []
     for step in range(nl):
         toks = np.stack([rng.choice(V, size=nb, p=Qd[i]) for i in range(g)], axis=1).astype(np.int32)
         res = L.spec_verify_batch(target, draft, torch.from_numpy(toks.reshape(-1)).to(DEV), cu, g,
-                                  temperature=1.0, top_k=5, top_p=0.85, seed=77, step=step,
+                                  temperature=1.0, top_k=k, top_p=p, seed=77, step=step,
                                   pos_stats=False, req_stats=False)
         torch.cuda.synchronize()
         assert (res["status"].cpu().numpy() == 0).all()
