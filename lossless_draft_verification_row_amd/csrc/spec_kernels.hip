@@ -448,6 +448,7 @@ struct HistLds {
     uint32_t n[kHBins];
   } u;
   double redd[kWaves];
+  double rho[48];              // step factor exp2(-u c) of each covered binade
   int redi[kWaves];
   int digit;
   uint32_t zeros;
@@ -466,27 +467,34 @@ __device__ __forceinline__ float hist_value(int r) {
   return __uint_as_float((h + (uint32_t)(kHE0 << 7)) << 16);
 }
 
-// Masses exp2((v_r - m) c) of the value ranks r0, r0 + 1, ... in turn: exp2 afresh at the first
-// rank and wherever a rank opens a new binade (or is the +-0 group), else one multiply by the
-// binade's step factor exp2(-u c), u the spacing of bf16 values in it (the next rank lies one
-// spacing lower on either sign).  Both walks over a thread's ranks take the same sequence.
+// Masses exp2((v_r - m) c) of the value ranks r0, r0 + 1, ... in turn.  The next rank always
+// lies one spacing lower: the spacing of the binade it enters for a positive value, of the
+// binade it leaves for a negative one (the same binade inside one), so its mass is the last one
+// times that binade's step factor rho = exp2(-u c), u = 2^(E - 134) for exponent field E, taken
+// from a per-workgroup table.  exp2 afresh only at the first rank at or below the row max (the
+// ranks above it are empty, and their masses could overflow) and next to the +-0 group (checked
+// against a direct exp2 per rank: 8e-14 relative at most).  Both walks over a thread's ranks
+// take the same sequence.
 struct RankMass {
-  double e = 0.0, rho = 0.0;
-  int seg = -2;
-  __device__ __forceinline__ double at(int r, float mx, double c) {
+  double e = 0.0;
+  int prev = -2;   // the last rank's sign and exponent field (-1: the +-0 group, -2: none)
+  __device__ __forceinline__ double at(int r, int rfirst, float mx, double c, const double* rho) {
+    if (r < rfirst) {
+      prev = -2;
+      return 0.0;
+    }
     int sg = -1;
     if (r != kHSide) {
       const uint32_t h = (r < kHSide ? (uint32_t)(kHSide - 1 - r) : (0x8000u | (uint32_t)(r - kHSide - 1))) +
                          (uint32_t)(kHE0 << 7);
-      sg = (int)(h >> 7);   // sign and exponent field
+      sg = (int)(h >> 7);
     }
-    if (sg >= 0 && sg == seg) {
-      e *= rho;
+    if (prev >= 0 && sg >= 0 && (sg >> 8) == (prev >> 8)) {
+      e *= rho[(((sg >> 8) ? prev : sg) & 0xff) - kHE0];
     } else {
       e = exp2(((double)hist_value(r) - (double)mx) * c);
-      if (sg >= 0) rho = exp2(-ldexp(1.0, (sg & 0xff) - 134) * c);
-      seg = sg;
     }
+    prev = sg;
     return e;
   }
 };
@@ -534,6 +542,7 @@ __global__ __launch_bounds__(kThreads) void k_threshold_hist(RowMap m, int V, in
   const int t = threadIdx.x;
   for (int i = t; i < kHBins; i += kThreads) H[i] = 0u;
   if (t == 0) S.zeros = 0u;
+  if (t < 48) S.rho[t] = exp2(-ldexp(1.0, kHE0 + t - 134) * c);
   __syncthreads();
 
   // the pass: each logit's pattern into its bin, kHLoads 16-byte words in flight per thread
@@ -641,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void k_threshold_hist(RowMap m, int V, in
     double ms = 0.0;
     RankMass rm;
     walk_ranks(S, r0, rk, [&](int r, uint32_t n) {
-      const double e = rm.at(r, mx, c);
+      const double e = rm.at(r, first, mx, c, S.rho);
       if (n) ms += (double)n * e;
       return true;
     });
@@ -658,7 +667,7 @@ __global__ __launch_bounds__(kThreads) void k_threshold_hist(RowMap m, int V, in
       int last = -1;
       RankMass rm;
       walk_ranks(S, r0, rk, [&](int r, uint32_t n) {
-        const double e = rm.at(r, mx, c);
+        const double e = rm.at(r, first, mx, c, S.rho);
         if (!n) return true;
         last = r;
         run += (double)n * e;
